@@ -1,0 +1,138 @@
+"""Seeded synthetic workloads for DualKV shared-prompt attention.
+
+This module only draws inputs.  It holds none of the attention arithmetic, so both
+the CPU oracle (``oracle/``) and the HIP path may use it without sharing method code.
+
+Shapes follow the workloads in "DualKV: Shared-Prompt Flash Attention for Efficient
+RL Training with Large Rollouts and Long Contexts" (arXiv 2605.15422): Qwen3-8B
+attention dimensions (H=32 query heads, 8 KV heads, d=128, §4.1 / Table 1),
+GRPO/DAPO rollout sizes (§4.2), and the Gemma-4 head-dim-512 global and
+sliding-window layers (§3 "Head dimensions and sliding-window support").  No
+dataset is read: every tensor is drawn from a seeded CPU generator.
+
+Single-prompt packing (§2.2, eq. 5): the prompt is stored once as rows [0, P) and
+response i occupies rows P + cu[i] ... P + cu[i+1] - 1.  Tensors are token-major
+``[tokens, heads, d]``.  The HIP path receives the prompt and response parts as
+separate tensors (q_p/k_p/v_p and q_r/k_r/v_r).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    P: int                      # shared prompt tokens
+    N: int                      # responses
+    R: Optional[int]            # fixed response length (None -> drawn)
+    R_range: Optional[tuple]    # (lo, hi) inclusive when drawn uniformly
+    Hq: int
+    Hkv: int
+    d: int
+    dtype: str                  # "fp32" or "bf16"
+    window_left: int = -1       # -1 = global causal
+    seed: int = 0
+    scaled: bool = True         # values ~ N(0,1)/sqrt(d) (else N(0,1))
+
+    def resp_lens(self) -> list:
+        if self.R is not None:
+            return [self.R] * self.N
+        g = torch.Generator().manual_seed(10_000 + self.seed)
+        lo, hi = self.R_range
+        return torch.randint(lo, hi + 1, (self.N,), generator=g).tolist()
+
+
+# The five workloads (the d=512 "layer pair" is two layers: global and windowed).
+# Sliding window (1024) is read as 1024 visible keys including the query itself,
+# i.e. window_left = 1023.
+WORKLOADS = {
+    "tiny": Workload("tiny", P=64, N=4, R=32, R_range=None, Hq=2, Hkv=2, d=64,
+                     dtype="fp32", seed=1, scaled=False),
+    "qwen3_8b": Workload("qwen3_8b", P=4096, N=32, R=4096, R_range=None, Hq=32, Hkv=8,
+                         d=128, dtype="bf16", seed=2),
+    "dapo_varlen": Workload("dapo_varlen", P=8192, N=16, R=None, R_range=(512, 4096),
+                            Hq=32, Hkv=8, d=128, dtype="bf16", seed=3),
+    "large_rollout": Workload("large_rollout", P=16384, N=64, R=1024, R_range=None,
+                              Hq=32, Hkv=8, d=128, dtype="bf16", seed=4),
+    "d512_global": Workload("d512_global", P=57344, N=8, R=8192, R_range=None, Hq=16,
+                            Hkv=4, d=512, dtype="bf16", seed=5),
+    "d512_swa": Workload("d512_swa", P=57344, N=8, R=8192, R_range=None, Hq=16, Hkv=4,
+                         d=512, dtype="bf16", window_left=1023, seed=6),
+}
+
+
+def torch_dtype(name: str) -> torch.dtype:
+    return {"fp32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+def cu_seqlens(lens) -> torch.Tensor:
+    cu = [0]
+    for r in lens:
+        cu.append(cu[-1] + int(r))
+    return torch.tensor(cu, dtype=torch.int32)
+
+
+def _draw(g: torch.Generator, shape, dtype: str, scale: float) -> torch.Tensor:
+    """fp32 tensor whose values are exactly representable in ``dtype``."""
+    x = torch.randn(shape, generator=g, dtype=torch.float32) * scale
+    if dtype == "bf16":
+        x = x.to(torch.bfloat16).to(torch.float32)
+    return x
+
+
+def make_inputs(P: int, lens, Hq: int, Hkv: int, d: int, dtype: str = "fp32",
+                seed: int = 0, scaled: bool = False, dout: bool = True) -> dict:
+    """Single-prompt packed inputs (fp32 tensors holding ``dtype``-exact values).
+
+    Returns q_p [P,Hq,d], k_p/v_p [P,Hkv,d], q_r [T,Hq,d], k_r/v_r [T,Hkv,d],
+    do_p [P,Hq,d] (the prompt-row upstream gradient seen by the single prompt
+    copy), do_r [T,Hq,d] and cu (int32 [N+1]).
+    """
+    g = torch.Generator().manual_seed(seed)
+    T = int(sum(lens))
+    s = 1.0 / math.sqrt(d) if scaled else 1.0
+    out = {
+        "q_p": _draw(g, (P, Hq, d), dtype, s),
+        "k_p": _draw(g, (P, Hkv, d), dtype, s),
+        "v_p": _draw(g, (P, Hkv, d), dtype, s),
+        "q_r": _draw(g, (T, Hq, d), dtype, s),
+        "k_r": _draw(g, (T, Hkv, d), dtype, s),
+        "v_r": _draw(g, (T, Hkv, d), dtype, s),
+        "cu": cu_seqlens(lens),
+    }
+    if dout:
+        out["do_p"] = _draw(g, (P, Hq, d), dtype, 1.0)
+        out["do_r"] = _draw(g, (T, Hq, d), dtype, 1.0)
+    return out
+
+
+def split_prompt_grad(do_p: torch.Tensor, N: int, seed: int) -> torch.Tensor:
+    """Per-copy prompt-row upstream gradients dO_P^(i), i = 1..N, in float64.
+
+    In the N-copy packing each copy's prompt rows receive their own upstream
+    gradient; in the single-prompt packing the one prompt copy receives their sum
+    (the paper's Appendix A.5: the residual stream aggregates the N branches).
+    dO_P^(i) = do_p / N + e_i, where the e_i are multiples of 1/256 that sum to
+    exactly zero, so sum_i dO_P^(i) equals do_p to within float64 rounding.
+    """
+    g = torch.Generator().manual_seed(20_000 + seed)
+    base = do_p.to(torch.float64) / N
+    if N == 1:
+        return base.unsqueeze(0).clone()
+    e = torch.randint(-64, 65, (N - 1,) + tuple(do_p.shape), generator=g).to(torch.float64) / 256.0
+    last = -e.sum(0)
+    parts = torch.cat([e, last.unsqueeze(0)], 0) + base.unsqueeze(0)
+    return parts
+
+
+def workload_inputs(w: Workload, dout: bool = True) -> dict:
+    lens = w.resp_lens()
+    x = make_inputs(w.P, lens, w.Hq, w.Hkv, w.d, w.dtype, seed=w.seed, scaled=w.scaled,
+                    dout=dout)
+    x["lens"] = lens
+    return x
