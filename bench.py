@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of DualKV shared-prompt attention, forward + backward, on one MI355X.
+
+One step is the whole hot path on one batch: Call 1 forward (dkv_ctx_fwd), Call 2
+forward (dkv_fwd), Call 1 backward (dkv_ctx_bwd, clearing the shared fp32
+accumulator) and Call 2 backward (dkv_bwd, adding the responses' terms and casting
+dK_P/dV_P once).  Inputs are seeded synthetic tensors already resident in HBM.
+
+Reported value: useful TFLOP/s = 14 * d * Hq * (visible pairs of both calls) / step
+time (4*d per pair forward, 10*d backward; masked work is not counted).  Also
+reported: the fraction of the bf16 MFMA peak, the speedup over the same library's
+causal kernel run on the N-copy packing (eq. (1)/(2) of the DualKV paper), the
+roofline of the dominant kernel (timed live with HIP events on its stream), and the
+CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3_8b")
+    ap.add_argument("--no-ncopy", action="store_true", help="skip the N-copy comparator")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(args, *a):
+    if not args.quiet:
+        print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_algo_work(w, lens, pairs):
+    """Algorithmic work per kernel class for one step: (amount, unit, bound)."""
+    d, Hq, Hkv, P = w.d, w.Hq, w.Hkv, w.P
+    T = P + sum(lens)                   # query rows over both calls
+    eb = 2 if w.dtype == "bf16" else 4
+    return {
+        # forward: Q K^T and P V on every visible pair
+        "attn_fwd": (4 * d * Hq * pairs, "flop", "mfma"),
+        # dQ kernel: recomputes S and dP, then dS K
+        "bwd_dq": (6 * d * Hq * pairs, "flop", "mfma"),
+        # dK/dV kernel: recomputes S and dP, then P^T dO and dS^T Q
+        "bwd_dkdv": (8 * d * Hq * pairs, "flop", "mfma"),
+        # D = rowsum(dO * O): read O and dO, write one fp32 per row
+        "bwd_pre": (T * Hq * (2 * d * eb + 4), "byte", "hbm"),
+        # clear the two fp32 accumulators
+        "acc_zero": (2 * P * Hkv * d * 4, "byte", "hbm"),
+        # read the two fp32 accumulators, write dK_P, dV_P
+        "acc_cast": (2 * P * Hkv * d * (4 + eb), "byte", "hbm"),
+    }
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they were
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec.get("sources", []):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec.get("sources_sha256"):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    from shared_prompt_exact_dkv_amd import accounting, _lib
+    import shared_prompt_exact_dkv_amd as dkv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    w = workloads.WORKLOADS[args.workload]
+    lens = w.resp_lens()
+    N, P, Hq, Hkv, d, wl = w.N, w.P, w.Hq, w.Hkv, w.d, w.window_left
+    tdt = workloads.torch_dtype(w.dtype)
+    log(args, "workload", w)
+
+    x = workloads.make_inputs(P, lens, Hq, Hkv, d, w.dtype, seed=w.seed, scaled=w.scaled,
+                              device=dev)
+    x = {k: (v.to(tdt).contiguous() if k != "cu" else v) for k, v in x.items()}
+    cu_host = [int(c) for c in x["cu"]]
+    cu = x["cu"].to(dev)
+    cu_p_host = [0, P]
+    cu_p = torch.tensor(cu_p_host, dtype=torch.int32, device=dev)
+    T = cu_host[-1]
+
+    # Preallocated outputs, accumulator and one workspace for every call.
+    o_p = torch.empty_like(x["q_p"])
+    o_r = torch.empty_like(x["q_r"])
+    lse_p = torch.empty((Hq, P), dtype=torch.float32, device=dev)
+    lse_r = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    dq_p = torch.empty_like(x["q_p"])
+    dq_r = torch.empty_like(x["q_r"])
+    dk_r = torch.empty_like(x["k_r"])
+    dv_r = torch.empty_like(x["v_r"])
+    dk_p = torch.empty_like(x["k_p"])
+    dv_p = torch.empty_like(x["v_p"])
+    acc = torch.empty((2, P, Hkv, d), dtype=torch.float32, device=dev)
+    wsz = max(dkv.dkv_workspace_size(c, x["q_r"], x["k_r"], cu, cu_host=cu_host, ctx_len=P,
+                                     window_left=wl) for c in (1, 3))
+    wsz = max(wsz, max(dkv.dkv_workspace_size(c, x["q_p"], x["k_p"], cu_p, cu_host=cu_p_host,
+                                              window_left=wl) for c in (0, 2)))
+    ws = torch.empty(max(wsz, 256), dtype=torch.uint8, device=dev)
+
+    def dk_step():
+        dkv.dkv_ctx_fwd(x["q_p"], x["k_p"], x["v_p"], cu_p, cu_host=cu_p_host, window_left=wl,
+                        out=o_p, lse=lse_p, workspace=ws)
+        dkv.dkv_fwd(x["q_r"], x["k_p"], x["v_p"], x["k_r"], x["v_r"], cu, cu_host=cu_host,
+                    window_left=wl, out=o_r, lse=lse_r, workspace=ws)
+        dkv.dkv_ctx_bwd(x["q_p"], x["k_p"], x["v_p"], o_p, lse_p, x["do_p"], cu_p,
+                        cu_host=cu_p_host, window_left=wl, dq=dq_p, acc_dk=acc[0],
+                        acc_dv=acc[1], acc_flags=dkv.DKV_ACC_ZERO, workspace=ws)
+        dkv.dkv_bwd(x["q_r"], x["k_p"], x["v_p"], x["k_r"], x["v_r"], o_r, lse_r, x["do_r"], cu,
+                    acc_dk_p=acc[0], acc_dv_p=acc[1], acc_flags=dkv.DKV_ACC_FINALIZE,
+                    cu_host=cu_host, window_left=wl, dq_r=dq_r, dk_r=dk_r, dv_r=dv_r,
+                    dk_p=dk_p, dv_p=dv_p, workspace=ws)
+
+    def timed(step, k):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(k):
+            step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / k
+
+    for _ in range(args.warmup):
+        dk_step()
+    torch.cuda.synchronize()
+    _lib.lib().dkv_timing_reset()
+    _lib.lib().dkv_timing_enable(1)
+    ms = timed(dk_step, args.steps)
+    _lib.lib().dkv_timing_enable(0)
+    ktimes = _lib.timing_read()
+    _lib.lib().dkv_timing_reset()
+    log(args, "dualkv ms/step %.3f" % ms, ktimes)
+
+    pairs = accounting.pairs_dualkv(P, lens, wl)
+    flops = accounting.useful_flops(pairs, Hq, d)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+
+    # Fwd/bwd split of the step (per call classes), from the live kernel times.
+    fwd_ms = ktimes.get("attn_fwd", (0.0, 0))[0] / args.steps
+    bwd_ms = sum(v[0] for k, v in ktimes.items() if k != "attn_fwd") / args.steps
+
+    # Roofline of the dominant kernel class.
+    algo = kernel_algo_work(w, lens, pairs)
+    dom = max(ktimes, key=lambda k: ktimes[k][0]) if ktimes else None
+    roof = None
+    if dom is not None:
+        tot_ms, launches = ktimes[dom]
+        amount, unit, bound = algo[dom]
+        per_launch = amount * args.steps / launches
+        avg_s = tot_ms * 1e-3 / launches
+        if unit == "flop":
+            achieved = per_launch / avg_s / 1e12
+            pk, un = peak, "TFLOP/s"
+        else:
+            achieved = per_launch / avg_s / 1e9
+            pk, un = PEAK_HBM_GBS, "GB/s"
+        roof = {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": pk,
+                "unit": un, "frac": round(achieved / pk, 4),
+                "traffic": traffic_for(dom, w.name), "avg_launch_ms": round(tot_ms / launches, 4),
+                "launches_per_step": launches // args.steps}
+    kernels = {k: {"ms_per_step": round(v[0] / args.steps, 4), "launches_per_step": v[1] // args.steps}
+               for k, v in ktimes.items()}
+
+    # N-copy comparator: the same library's causal kernel over N sequences [P, R_i].
+    ncopy_ms = None
+    if not args.no_ncopy:
+        qn = torch.cat([t for i in range(N) for t in (x["q_p"], x["q_r"][cu_host[i]:cu_host[i + 1]])])
+        kn = torch.cat([t for i in range(N) for t in (x["k_p"], x["k_r"][cu_host[i]:cu_host[i + 1]])])
+        vn = torch.cat([t for i in range(N) for t in (x["v_p"], x["v_r"][cu_host[i]:cu_host[i + 1]])])
+        don = torch.cat([t for i in range(N) for t in (x["do_p"], x["do_r"][cu_host[i]:cu_host[i + 1]])])
+        cun_host = [0]
+        for r in lens:
+            cun_host.append(cun_host[-1] + P + r)
+        cun = torch.tensor(cun_host, dtype=torch.int32, device=dev)
+        on = torch.empty_like(qn)
+        lsen = torch.empty((Hq, cun_host[-1]), dtype=torch.float32, device=dev)
+        dqn = torch.empty_like(qn)
+        dkn = torch.empty_like(kn)
+        dvn = torch.empty_like(vn)
+        wsn_sz = max(dkv.dkv_workspace_size(c, qn, kn, cun, cu_host=cun_host, window_left=wl)
+                     for c in (0, 2))
+        wsn = torch.empty(max(wsn_sz, 256), dtype=torch.uint8, device=dev)
+
+        def nc_step():
+            dkv.dkv_ctx_fwd(qn, kn, vn, cun, cu_host=cun_host, window_left=wl, out=on, lse=lsen,
+                            workspace=wsn)
+            dkv.dkv_ctx_bwd(qn, kn, vn, on, lsen, don, cun, cu_host=cun_host, window_left=wl,
+                            dq=dqn, dk=dkn, dv=dvn, workspace=wsn)
+
+        for _ in range(max(1, args.warmup // 2)):
+            nc_step()
+        ncopy_ms = timed(nc_step, max(2, args.steps // 2))
+        log(args, "ncopy ms/step %.3f" % ncopy_ms)
+        del qn, kn, vn, don, on, dqn, dkn, dvn, wsn
+        torch.cuda.empty_cache()
+
+    # CPU oracle on a bounded sample: the N-copy fwd+bwd of sequence 1 for one kv-head
+    # group, extrapolated to the whole workload by visible-pair count.
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        S0 = P + lens[0]
+        G = Hq // Hkv
+        xs = workloads.make_inputs(P, [lens[0]], G, 1, d, w.dtype, seed=w.seed + 100,
+                                   scaled=w.scaled)
+        q0, k0, v0 = oracle.copy_of(xs, 0)
+        do0 = torch.cat([xs["do_p"], xs["do_r"]]).double().numpy()
+        t0 = time.perf_counter()
+        oracle.seq_fwd(q0, k0, v0, window_left=wl)
+        oracle.seq_bwd(q0, k0, v0, do0, window_left=wl)
+        cpu_s = time.perf_counter() - t0
+        full_pairs = accounting.pairs_ncopy(P, lens, wl)
+        full_s = cpu_s * full_pairs / accounting.causal_pairs(S0, wl) * Hkv
+        cpu = {"value": round(flops / full_s / 1e12, 6), "unit": "TFLOP/s",
+               "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": "N-copy fwd+bwd (eq. 2, fp64) of sequence 1 (%d tokens) for 1 of %d "
+                         "kv-head groups (%d q-heads); %.1f s, extrapolated by visible-pair "
+                         "count to the full N-copy workload (%.0f s)" % (S0, Hkv, G, cpu_s, full_s)}
+        log(args, "cpu oracle sample %.2f s" % cpu_s)
+
+    speedup = (ncopy_ms / ms) if ncopy_ms else None
+    out = {
+        "metric": "DualKV fwd+bwd TFLOP/s (% MFMA peak); speedup vs N-copy causal attn",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "P": P, "N": N,
+                   "R": w.R if w.R is not None else "U%s" % (list(w.R_range),),
+                   "Hq": Hq, "Hkv": Hkv, "d": d, "window_left": wl,
+                   "parallelism": "single-gpu"},
+        "pct_mfma_peak": round(100.0 * tflops / peak, 2),
+        "speedup_vs_ncopy": round(speedup, 3) if speedup else None,
+        "ideal_speedup": round(accounting.ideal_speedup(P, lens, wl), 3),
+        "ncopy_ms_per_step": round(ncopy_ms, 4) if ncopy_ms else None,
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "useful_tflop_per_step": round(flops / 1e12, 4),
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+/*
+ * dkv.h -- C ABI of libdkv: DualKV shared-prompt attention on AMD MI355X (gfx950).
+ *
+ * The method ("DualKV: Shared-Prompt Flash Attention for Efficient RL Training with
+ * Large Rollouts and Long Contexts", arXiv 2605.15422) computes exact causal
+ * attention for N responses that share one P-token prompt.  The batch is packed
+ * with a single prompt copy (§2.2, eq. (5)): prompt rows, then response 1..N.  The
+ * work splits into two calls (§2.2 "two-call decomposition"):
+ *
+ *   Call 1  dkv_ctx_fwd / dkv_ctx_bwd  causal self-attention over the single prompt
+ *                                     copy (eq. (3)).  With several sequences it is
+ *                                     plain varlen causal attention, which is also
+ *                                     how the N-copy packing of §2.1 (eq. (2)) runs.
+ *   Call 2  dkv_fwd / dkv_bwd          every response attends to the shared K_P,V_P
+ *                                     and to its own K_Ri,V_Ri under the causal mask
+ *                                     shifted by P (eq. (4), §3.1).
+ *
+ * The gradient of the shared prompt K_P,V_P is the Call-1 term plus the sum of the
+ * N Call-2 terms (eq. (6)); both calls add into one caller-owned fp32 accumulator,
+ * which is cast to the tensor dtype exactly once (§3.2 "fp32 atomic accumulation").
+ *
+ * Conventions (all entry points)
+ *   - Tensors are caller-owned, contiguous, token-major device buffers:
+ *       queries / outputs / output grads  [tokens, Hq,  d]
+ *       keys / values / their grads       [tokens, Hkv, d]
+ *       LSE                               [Hq, tokens] fp32, natural log
+ *     in the dtype named by dkv_params.dtype (bf16 or fp32).  Device pointers must
+ *     be 16-byte aligned.
+ *   - The library never allocates or frees device memory.  Scratch space comes from
+ *     `ws` (device memory, `ws_bytes` long, 256-byte aligned), sized by
+ *     dkv_workspace_size() for the same parameters and call.
+ *   - Calls only enqueue work on `stream` and return; they never synchronize.  The
+ *     returned status reports argument validation and launch errors; a fault inside
+ *     a kernel surfaces at the caller's next synchronization.
+ *   - A non-OK status leaves a message retrievable with dkv_last_error() (per host
+ *     thread).  Validation happens before any device work is enqueued, so an
+ *     invalid call enqueues nothing.
+ *   - Concurrent calls on different streams must not share a workspace.
+ */
+#ifndef DKV_H
+#define DKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DKV_OK = 0,
+    DKV_ERR_INVALID_ARG = 1,   /* inconsistent shapes, bad cu_seqlens, null pointers */
+    DKV_ERR_UNSUPPORTED = 2,   /* valid but not implemented (e.g. head_dim) */
+    DKV_ERR_WORKSPACE = 3,     /* ws too small or misaligned */
+    DKV_ERR_HIP = 4            /* a HIP runtime call failed */
+} dkv_status;
+
+typedef enum { DKV_BF16 = 0, DKV_FP32 = 1 } dkv_dtype;
+
+/* Which call a workspace is sized for. */
+typedef enum {
+    DKV_CALL_CTX_FWD = 0,
+    DKV_CALL_FWD = 1,
+    DKV_CALL_CTX_BWD = 2,
+    DKV_CALL_BWD = 3
+} dkv_call;
+
+/* Flags of the shared-prompt gradient accumulator (dkv_ctx_bwd / dkv_bwd). */
+enum {
+    DKV_ACC_ZERO = 1,      /* clear acc_dk_p / acc_dv_p before adding this call's terms */
+    DKV_ACC_FINALIZE = 2,  /* after adding, cast the accumulator into dk_p / dv_p once */
+    DKV_ACC_SPLIT = 4      /* dkv_bwd only: per-chunk slices + fixed-order reduction
+                              instead of fp32 atomics (bitwise reproducible) */
+};
+
+typedef struct {
+    /* Number of sequences.  dkv_fwd/dkv_bwd: N responses.  dkv_ctx_*: number of
+       independent causal sequences (1 for Call 1 over the prompt; N for the N-copy
+       packing of eq. (2)). */
+    int32_t num_seqs;
+    /* P, the shared prompt length (context_seqlen of §3).  dkv_fwd/dkv_bwd only:
+       response row r sits at logical position P + r.  Must be 0 for dkv_ctx_*. */
+    int32_t ctx_len;
+    int32_t num_heads_q;       /* Hq, a multiple of Hkv (grouped-query attention) */
+    int32_t num_heads_kv;      /* Hkv; q-head h reads kv-head h / (Hq / Hkv) */
+    int32_t head_dim;          /* d: 64, 128 or 512 */
+    /* -1: global causal.  w >= 0: key at logical position j is visible from the query
+       at logical position t iff t - w <= j <= t (applies to the prompt region too). */
+    int32_t window_left;
+    float softmax_scale;       /* <= 0 selects 1/sqrt(head_dim) (eqs. (2)-(4)) */
+    int32_t dtype;             /* dkv_dtype of every tensor except LSE/accumulators */
+    /* Prefix sums of the per-sequence query lengths, int32 [num_seqs + 1] with
+       cu[0] = 0, non-decreasing (zero-length sequences allowed).  The host copy is
+       read during the call (validation and tile scheduling); the device copy, which
+       must hold the same values, is read by the kernels. */
+    const int32_t *cu_seqlens_host;
+    const int32_t *cu_seqlens_dev;
+} dkv_params;
+
+/* Bytes of device workspace the given call needs for these parameters (0 means
+   none; a valid pointer is still fine).  Returns (size_t)-1 for invalid params. */
+size_t dkv_workspace_size(const dkv_params *p, int which_call);
+
+/*
+ * Call 1 forward, eq. (3) -- causal self-attention of each sequence of
+ * cu_seqlens (varlen).  q [T, Hq, d], k/v [T, Hkv, d], T = cu[num_seqs];
+ * writes o [T, Hq, d] and lse [Hq, T].
+ */
+dkv_status dkv_ctx_fwd(const dkv_params *p, const void *q, const void *k, const void *v,
+                       void *o, float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Call 2 forward, eq. (4) and §3.1 -- response rows of sequence i attend to the
+ * shared prompt keys [0, P) and to their own preceding response keys, as one
+ * online softmax over both regions.  q_resp [T_R, Hq, d]; k_p/v_p [P, Hkv, d];
+ * k_r/v_r [T_R, Hkv, d]; T_R = cu[num_seqs].  Writes o_r [T_R, Hq, d] and
+ * lse_r [Hq, T_R].
+ */
+dkv_status dkv_fwd(const dkv_params *p, const void *q_resp, const void *k_p,
+                   const void *v_p, const void *k_r, const void *v_r, void *o_r,
+                   float *lse_r, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Call 1 backward -- gradients of eq. (3) for upstream gradient dout (for the
+ * single prompt copy: the sum of the N copies' prompt-row gradients, Appendix A.5).
+ * Inputs as in dkv_ctx_fwd plus o, lse (from the forward) and dout [T, Hq, d].
+ * Writes dq [T, Hq, d].  Key/value gradients:
+ *   - acc_dk / acc_dv non-NULL (fp32 [T, Hkv, d]): added into the accumulator
+ *     (cleared first with DKV_ACC_ZERO; cast into dk/dv with DKV_ACC_FINALIZE).
+ *     With one sequence over the prompt this is the Call-1 term of eq. (6).
+ *   - acc_dk / acc_dv NULL: written directly to dk / dv [T, Hkv, d] (plain varlen
+ *     causal backward, e.g. the N-copy packing).
+ */
+dkv_status dkv_ctx_bwd(const dkv_params *p, const void *q, const void *k, const void *v,
+                       const void *o, const float *lse, const void *dout, void *dq,
+                       void *dk, void *dv, float *acc_dk, float *acc_dv, int acc_flags,
+                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Call 2 backward, §3.2 -- gradients of eq. (4).  Inputs as in dkv_fwd plus o_r,
+ * lse_r and dout_r [T_R, Hq, d].  Writes dq_r [T_R, Hq, d] and dk_r/dv_r
+ * [T_R, Hkv, d] directly; adds the N responses' prompt-key terms into
+ * acc_dk_p / acc_dv_p (fp32 [P, Hkv, d], required when P > 0).  With
+ * DKV_ACC_FINALIZE, casts the accumulator into dk_p / dv_p [P, Hkv, d] once all
+ * terms are in.
+ */
+dkv_status dkv_bwd(const dkv_params *p, const void *q_resp, const void *k_p,
+                   const void *v_p, const void *k_r, const void *v_r, const void *o_r,
+                   const float *lse_r, const void *dout_r, void *dq_r, void *dk_r,
+                   void *dv_r, float *acc_dk_p, float *acc_dv_p, int acc_flags,
+                   void *dk_p, void *dv_p, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The single cast of §3.2 (Stage 2) on its own: acc_dk/acc_dv fp32 [rows, Hkv, d]
+ * -> dk/dv [rows, Hkv, d] in p->dtype, round-to-nearest-even (a copy for fp32).
+ */
+dkv_status dkv_cast_acc(const dkv_params *p, int32_t rows, const float *acc_dk,
+                        const float *acc_dv, void *dk, void *dv, hipStream_t stream);
+
+/*
+ * Per-kernel timing, a profiling aid.  While enabled, every kernel the library
+ * launches is bracketed by two HIP events recorded on its own stream.
+ * dkv_timing_read() waits for those events and reports, per kernel class, the
+ * summed milliseconds and the launch count since the last reset; it returns the
+ * number of classes written (at most max_entries).  Names are static strings.
+ * Not thread-safe against concurrent launches from other host threads.
+ */
+void dkv_timing_enable(int on);
+void dkv_timing_reset(void);
+int dkv_timing_read(const char **names, double *ms, int *launches, int max_entries);
+
+/* Message for the last non-OK status on this host thread ("" if none). */
+const char *dkv_last_error(void);
+
+/* Library version string. */
+const char *dkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DKV_H */

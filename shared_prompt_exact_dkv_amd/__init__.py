@@ -1,0 +1,179 @@
+"""DualKV shared-prompt attention for AMD MI355X (gfx950).
+
+Thin torch binding of libdkv's C ABI (include/dkv.h).  The functions below only
+marshal arguments: torch tensors supply device memory and the current stream, and
+every step of the attention runs in libdkv's HIP kernels.
+
+Method: "DualKV: Shared-Prompt Flash Attention for Efficient RL Training with Large
+Rollouts and Long Contexts" (arXiv 2605.15422).  Call 1 (``dkv_ctx_fwd`` /
+``dkv_ctx_bwd``) is causal self-attention over the single prompt copy, eq. (3);
+Call 2 (``dkv_fwd`` / ``dkv_bwd``) is the shared-prompt attention of the responses,
+eq. (4); the shared prompt K/V gradient is the sum of eq. (6).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+from ._lib import DKV_ACC_FINALIZE, DKV_ACC_SPLIT, DKV_ACC_ZERO, DkvError  # noqa: F401
+
+__all__ = ["dkv_workspace_size", "dkv_ctx_fwd", "dkv_fwd", "dkv_ctx_bwd", "dkv_bwd",
+           "dkv_cast_acc", "dualkv_forward", "dualkv_backward", "DkvError", "DKV_ACC_ZERO", "DKV_ACC_FINALIZE", "DKV_ACC_SPLIT"]
+
+_DT = {torch.bfloat16: L.DKV_BF16, torch.float32: L.DKV_FP32}
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _host_cu(cu_seqlens, cu_host):
+    if cu_host is not None:
+        return [int(c) for c in cu_host]
+    return [int(c) for c in cu_seqlens.cpu().tolist()]
+
+
+def _params(q, k, cu_seqlens, cu_host, ctx_len, window_left, softmax_scale):
+    if q.dtype not in _DT:
+        raise TypeError("unsupported dtype %s" % q.dtype)
+    cu = _host_cu(cu_seqlens, cu_host)
+    return L.make_params(num_seqs=len(cu) - 1, ctx_len=ctx_len, num_heads_q=q.shape[1],
+                         num_heads_kv=k.shape[1], head_dim=q.shape[2],
+                         window_left=window_left, softmax_scale=softmax_scale,
+                         dtype=_DT[q.dtype], cu_host=cu, cu_dev=_p(cu_seqlens))
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ws(params, call, device, workspace):
+    n = L.lib().dkv_workspace_size(params, call)
+    if n == (1 << 64) - 1:
+        L.check(L.DKV_ERR_INVALID_ARG)
+    if n == 0:
+        return None, 0
+    if workspace is not None and workspace.numel() * workspace.element_size() >= n:
+        return workspace, workspace.numel() * workspace.element_size()
+    return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+def dkv_workspace_size(call: int, q, k, cu_seqlens, *, cu_host=None, ctx_len=0,
+                       window_left=-1, softmax_scale=0.0) -> int:
+    p, keep = _params(q, k, cu_seqlens, cu_host, ctx_len, window_left, softmax_scale)
+    return int(L.lib().dkv_workspace_size(p, call))
+
+
+def dkv_ctx_fwd(q, k, v, cu_seqlens, *, cu_host=None, window_left=-1, softmax_scale=0.0,
+                out=None, lse=None, workspace=None):
+    """Causal self-attention of each sequence of ``cu_seqlens`` (Call 1, eq. (3)).
+    q [T,Hq,d], k/v [T,Hkv,d] -> (o [T,Hq,d], lse [Hq,T] fp32)."""
+    p, keep = _params(q, k, cu_seqlens, cu_host, 0, window_left, softmax_scale)
+    T, Hq, _ = q.shape
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    ws, nws = _ws(p, L.DKV_CALL_CTX_FWD, q.device, workspace)
+    L.check(L.lib().dkv_ctx_fwd(p, _p(q), _p(k), _p(v), _p(o), _p(lse), _p(ws), nws,
+                                _stream(q.device)))
+    return o, lse
+
+
+def dkv_fwd(q_resp, k_p, v_p, k_r, v_r, cu_seqlens, *, cu_host=None, window_left=-1,
+            softmax_scale=0.0, out=None, lse=None, workspace=None):
+    """Shared-prompt attention of the responses (Call 2, eq. (4)); P = k_p.shape[0].
+    -> (o_r [T_R,Hq,d], lse_r [Hq,T_R] fp32)."""
+    p, keep = _params(q_resp, k_r, cu_seqlens, cu_host, k_p.shape[0], window_left,
+                      softmax_scale)
+    T, Hq, _ = q_resp.shape
+    o = torch.empty_like(q_resp) if out is None else out
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=q_resp.device) if lse is None else lse
+    ws, nws = _ws(p, L.DKV_CALL_FWD, q_resp.device, workspace)
+    L.check(L.lib().dkv_fwd(p, _p(q_resp), _p(k_p), _p(v_p), _p(k_r), _p(v_r), _p(o), _p(lse),
+                            _p(ws), nws, _stream(q_resp.device)))
+    return o, lse
+
+
+def dkv_ctx_bwd(q, k, v, o, lse, dout, cu_seqlens, *, cu_host=None, window_left=-1,
+                softmax_scale=0.0, dq=None, dk=None, dv=None, acc_dk=None, acc_dv=None,
+                acc_flags=0, workspace=None):
+    """Backward of Call 1 (eq. (3)).  Without accumulators dk/dv are written directly;
+    with acc_dk/acc_dv (fp32 [T,Hkv,d]) the key/value gradients are added into them
+    (cleared first with DKV_ACC_ZERO, cast into dk/dv with DKV_ACC_FINALIZE).
+    -> (dq, dk, dv)."""
+    p, keep = _params(q, k, cu_seqlens, cu_host, 0, window_left, softmax_scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    if acc_dk is None or (acc_flags & L.DKV_ACC_FINALIZE):
+        dk = torch.empty_like(k) if dk is None else dk
+        dv = torch.empty_like(v) if dv is None else dv
+    ws, nws = _ws(p, L.DKV_CALL_CTX_BWD, q.device, workspace)
+    L.check(L.lib().dkv_ctx_bwd(p, _p(q), _p(k), _p(v), _p(o), _p(lse), _p(dout), _p(dq),
+                                _p(dk), _p(dv), _p(acc_dk), _p(acc_dv), int(acc_flags), _p(ws),
+                                nws, _stream(q.device)))
+    return dq, dk, dv
+
+
+def dkv_bwd(q_resp, k_p, v_p, k_r, v_r, o_r, lse_r, dout_r, cu_seqlens, *, acc_dk_p, acc_dv_p,
+            acc_flags=0, cu_host=None, window_left=-1, softmax_scale=0.0, dq_r=None, dk_r=None,
+            dv_r=None, dk_p=None, dv_p=None, workspace=None):
+    """Backward of Call 2 (eq. (4), §3.2).  Adds the responses' prompt-key gradients
+    into acc_dk_p/acc_dv_p (fp32 [P,Hkv,d]); with DKV_ACC_FINALIZE also casts the
+    accumulator into dk_p/dv_p.  -> (dq_r, dk_r, dv_r, dk_p, dv_p)."""
+    p, keep = _params(q_resp, k_r, cu_seqlens, cu_host, k_p.shape[0], window_left,
+                      softmax_scale)
+    dq_r = torch.empty_like(q_resp) if dq_r is None else dq_r
+    dk_r = torch.empty_like(k_r) if dk_r is None else dk_r
+    dv_r = torch.empty_like(v_r) if dv_r is None else dv_r
+    if acc_flags & L.DKV_ACC_FINALIZE:
+        dk_p = torch.empty_like(k_p) if dk_p is None else dk_p
+        dv_p = torch.empty_like(v_p) if dv_p is None else dv_p
+    ws, nws = _ws(p, L.DKV_CALL_BWD, q_resp.device, workspace)
+    L.check(L.lib().dkv_bwd(p, _p(q_resp), _p(k_p), _p(v_p), _p(k_r), _p(v_r), _p(o_r),
+                            _p(lse_r), _p(dout_r), _p(dq_r), _p(dk_r), _p(dv_r), _p(acc_dk_p),
+                            _p(acc_dv_p), int(acc_flags), _p(dk_p), _p(dv_p), _p(ws), nws,
+                            _stream(q_resp.device)))
+    return dq_r, dk_r, dv_r, dk_p, dv_p
+
+
+def dkv_cast_acc(acc_dk, acc_dv, dk, dv):
+    """Cast the fp32 accumulators into dk/dv (their dtype), once."""
+    rows, Hkv, d = acc_dk.shape
+    p, keep = L.make_params(num_seqs=0, ctx_len=0, num_heads_q=Hkv, num_heads_kv=Hkv,
+                            head_dim=d, dtype=_DT[dk.dtype], cu_host=[0])
+    L.check(L.lib().dkv_cast_acc(p, rows, _p(acc_dk), _p(acc_dv), _p(dk), _p(dv),
+                                 _stream(dk.device)))
+    return dk, dv
+
+
+def dualkv_forward(q_p, k_p, v_p, q_r, k_r, v_r, cu_seqlens, *, cu_host=None, window_left=-1,
+                   softmax_scale=0.0):
+    """The two calls of the forward: Call 1 over the prompt, Call 2 over the responses.
+    -> (o_p, lse_p, o_r, lse_r)."""
+    P = q_p.shape[0]
+    cu_p = torch.tensor([0, P], dtype=torch.int32, device=q_p.device)
+    o_p, lse_p = dkv_ctx_fwd(q_p, k_p, v_p, cu_p, cu_host=[0, P], window_left=window_left,
+                             softmax_scale=softmax_scale)
+    o_r, lse_r = dkv_fwd(q_r, k_p, v_p, k_r, v_r, cu_seqlens, cu_host=cu_host,
+                         window_left=window_left, softmax_scale=softmax_scale)
+    return o_p, lse_p, o_r, lse_r
+
+
+def dualkv_backward(q_p, k_p, v_p, q_r, k_r, v_r, o_p, lse_p, o_r, lse_r, do_p, do_r,
+                    cu_seqlens, *, cu_host=None, window_left=-1, softmax_scale=0.0,
+                    acc=None):
+    """The two calls of the backward sharing one fp32 accumulator for dK_P/dV_P
+    (eq. (6)): Call 1 clears it and adds the prompt self-attention term, Call 2 adds
+    the N responses' terms and casts once.  -> dict of dq_p, dk_p, dv_p, dq_r, dk_r,
+    dv_r."""
+    P = q_p.shape[0]
+    if acc is None:
+        acc = torch.empty((2,) + tuple(k_p.shape), dtype=torch.float32, device=k_p.device)
+    cu_p = torch.tensor([0, P], dtype=torch.int32, device=q_p.device)
+    dq_p, _, _ = dkv_ctx_bwd(q_p, k_p, v_p, o_p, lse_p, do_p, cu_p, cu_host=[0, P],
+                             window_left=window_left, softmax_scale=softmax_scale,
+                             acc_dk=acc[0], acc_dv=acc[1], acc_flags=DKV_ACC_ZERO)
+    dq_r, dk_r, dv_r, dk_p, dv_p = dkv_bwd(q_r, k_p, v_p, k_r, v_r, o_r, lse_r, do_r,
+                                           cu_seqlens, acc_dk_p=acc[0], acc_dv_p=acc[1],
+                                           acc_flags=DKV_ACC_FINALIZE, cu_host=cu_host,
+                                           window_left=window_left,
+                                           softmax_scale=softmax_scale)
+    return {"dq_p": dq_p, "dk_p": dk_p, "dv_p": dv_p, "dq_r": dq_r, "dk_r": dk_r, "dv_r": dv_r}

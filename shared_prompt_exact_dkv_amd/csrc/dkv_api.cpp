@@ -1,0 +1,648 @@
+// dkv_api.cpp -- the C ABI of libdkv (include/dkv.h): argument validation, tile
+// scheduling and kernel launches.  No device memory is allocated here; scratch
+// lives in the caller's workspace.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/dkv.h"
+#include "dkv_launch.h"
+
+using namespace dkv;
+
+namespace {
+
+thread_local std::string g_err;
+
+dkv_status fail(dkv_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+dkv_status hip_fail(hipError_t e, const char *what) {
+  return fail(DKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(int dtype) { return dtype == DKV_BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------- validation --
+
+struct Shape {
+  int N, P, Hq, Hkv, G, d, wl, dtype;
+  float scale;
+  long T;                   // cu[N]
+  std::vector<int> cu;
+  int bm_tok;               // query tokens per forward / dQ workgroup
+};
+
+dkv_status check_params(const dkv_params *p, bool is_ctx, Shape *s) {
+  if (!p) return fail(DKV_ERR_INVALID_ARG, "params is NULL");
+  if (p->num_seqs < 0) return fail(DKV_ERR_INVALID_ARG, "num_seqs < 0 (%d)", p->num_seqs);
+  if (p->ctx_len < 0) return fail(DKV_ERR_INVALID_ARG, "ctx_len < 0 (%d)", p->ctx_len);
+  if (is_ctx && p->ctx_len != 0)
+    return fail(DKV_ERR_INVALID_ARG, "ctx_len must be 0 for dkv_ctx_* calls (got %d)", p->ctx_len);
+  if (p->num_heads_q <= 0 || p->num_heads_kv <= 0)
+    return fail(DKV_ERR_INVALID_ARG, "head counts must be positive (Hq=%d, Hkv=%d)",
+                p->num_heads_q, p->num_heads_kv);
+  if (p->num_heads_q % p->num_heads_kv != 0)
+    return fail(DKV_ERR_INVALID_ARG, "Hq (%d) is not a multiple of Hkv (%d)", p->num_heads_q,
+                p->num_heads_kv);
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 512)
+    return fail(DKV_ERR_INVALID_ARG, "head_dim must be 64, 128 or 512 (got %d)", p->head_dim);
+  if (p->window_left < -1)
+    return fail(DKV_ERR_INVALID_ARG, "window_left must be -1 or >= 0 (got %d)", p->window_left);
+  if (p->dtype != DKV_BF16 && p->dtype != DKV_FP32)
+    return fail(DKV_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
+  if (!(std::isfinite(p->softmax_scale)))
+    return fail(DKV_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (!p->cu_seqlens_host) return fail(DKV_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
+  const int G = p->num_heads_q / p->num_heads_kv;
+  if (G > kRowsPerWG)
+    return fail(DKV_ERR_UNSUPPORTED, "Hq/Hkv = %d exceeds %d", G, kRowsPerWG);
+  s->N = p->num_seqs;
+  s->P = p->ctx_len;
+  s->Hq = p->num_heads_q;
+  s->Hkv = p->num_heads_kv;
+  s->G = G;
+  s->d = p->head_dim;
+  s->wl = p->window_left;
+  s->dtype = p->dtype;
+  s->scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
+  s->cu.assign(p->cu_seqlens_host, p->cu_seqlens_host + p->num_seqs + 1);
+  if (s->cu[0] != 0) return fail(DKV_ERR_INVALID_ARG, "cu_seqlens[0] must be 0 (got %d)", s->cu[0]);
+  for (int i = 0; i < s->N; ++i)
+    if (s->cu[i + 1] < s->cu[i])
+      return fail(DKV_ERR_INVALID_ARG, "cu_seqlens decreases at %d (%d -> %d)", i, s->cu[i],
+                  s->cu[i + 1]);
+  s->T = s->cu[s->N];
+  if (s->T > 0 && !p->cu_seqlens_dev)
+    return fail(DKV_ERR_INVALID_ARG, "cu_seqlens_dev is NULL");
+  s->bm_tok = kRowsPerWG / G;
+  if (s->d == 512) return fail(DKV_ERR_UNSUPPORTED, "head_dim 512 is not available in this build");
+  return DKV_OK;
+}
+
+dkv_status check_ptr(const void *ptr, const char *name, bool needed) {
+  if (!needed) return DKV_OK;
+  if (!ptr) return fail(DKV_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(ptr)) return fail(DKV_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return DKV_OK;
+}
+
+// ---------------------------------------------------------------- scheduling --
+//
+// Query-parallel work items (forward, dQ): one per (kv head, sequence, query tile).
+// Items are ordered longest-first (the visible key range grows with the tile index
+// under the causal mask) and, within a work level, interleaved over kv heads so that
+// workgroup b -- which the dispatcher places on XCD b % 8 -- keeps one kv head per
+// XCD where Hkv divides 8, letting that XCD's L2 hold the head's K_P/V_P.
+
+long q_item_work(const Shape &s, int tile, int seqlen, int BN) {
+  long t0 = (long)tile * s.bm_tok;
+  long t1 = std::min<long>(seqlen, t0 + s.bm_tok);
+  long qmin = s.P + t0, qmax = s.P + t1 - 1;
+  long lo = (s.wl >= 0) ? std::max<long>(0, qmin - s.wl) : 0;
+  long keys = qmax + 1 - lo;
+  return (keys + BN - 1) / BN;
+}
+
+std::vector<QItem> build_q_items(const Shape &s, int BN) {
+  struct Rec { long work; int seq, tile; };
+  std::vector<Rec> recs;
+  for (int i = 0; i < s.N; ++i) {
+    int len = s.cu[i + 1] - s.cu[i];
+    int nt = (len + s.bm_tok - 1) / s.bm_tok;
+    for (int m = 0; m < nt; ++m) recs.push_back({q_item_work(s, m, len, BN), i, m});
+  }
+  std::stable_sort(recs.begin(), recs.end(),
+                   [](const Rec &a, const Rec &b) { return a.work > b.work; });
+  std::vector<QItem> items;
+  items.reserve(recs.size() * s.Hkv);
+  for (const Rec &r : recs)
+    for (int g = 0; g < s.Hkv; ++g)
+      items.push_back({g, r.tile, s.cu[r.seq], s.cu[r.seq + 1] - s.cu[r.seq]});
+  return items;
+}
+
+// ----------------------------------------------------- pinned staging of lists --
+//
+// Work lists are built on the host and copied into the workspace on the caller's
+// stream.  Each copy reads from a pinned host slot that is not reused before an
+// event recorded after the copy has completed.
+
+struct StagingRing {
+  struct Slot {
+    void *host = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+    bool pending = false;
+  };
+  std::mutex mu;
+  std::map<int, std::vector<Slot>> per_device;
+  size_t next = 0;
+};
+
+StagingRing &ring() {
+  static StagingRing r;
+  return r;
+}
+
+dkv_status upload(const void *src, size_t bytes, void *dst, hipStream_t stream) {
+  if (bytes == 0) return DKV_OK;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  StagingRing &r = ring();
+  std::lock_guard<std::mutex> lock(r.mu);
+  auto &slots = r.per_device[dev];
+  if (slots.empty()) slots.resize(8);
+  StagingRing::Slot &sl = slots[r.next++ % slots.size()];
+  if (sl.pending) {
+    e = hipEventSynchronize(sl.ev);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(staging)");
+    sl.pending = false;
+  }
+  if (!sl.ev) {
+    e = hipEventCreateWithFlags(&sl.ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  }
+  if (sl.cap < bytes) {
+    if (sl.host) (void)hipHostFree(sl.host);
+    sl.host = nullptr;
+    sl.cap = 0;
+    size_t cap = std::max<size_t>(bytes, 64 * 1024);
+    e = hipHostMalloc(&sl.host, cap, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(staging)");
+    sl.cap = cap;
+  }
+  std::memcpy(sl.host, src, bytes);
+  e = hipMemcpyAsync(dst, sl.host, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work list)");
+  e = hipEventRecord(sl.ev, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(staging)");
+  sl.pending = true;
+  return DKV_OK;
+}
+
+// -------------------------------------------------------------- kernel timing --
+
+enum KernelClass { kKFwd = 0, kKPre, kKDq, kKDkdv, kKZero, kKCast, kKClasses };
+const char *const kKernelNames[kKClasses] = {"attn_fwd", "bwd_pre", "bwd_dq", "bwd_dkdv",
+                                             "acc_zero", "acc_cast"};
+
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  struct Rec { int cls; hipEvent_t a, b; };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+};
+
+Timing &timing() {
+  static Timing t;
+  return t;
+}
+
+hipEvent_t get_event(Timing &t) {
+  if (!t.pool.empty()) {
+    hipEvent_t e = t.pool.back();
+    t.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Launch `fn` (returning hipError_t) on `stream`, bracketed by events when enabled.
+template <typename F> hipError_t timed(int cls, hipStream_t stream, F &&fn) {
+  Timing &t = timing();
+  if (!t.on) return fn();
+  std::lock_guard<std::mutex> lock(t.mu);
+  hipEvent_t a = get_event(t), b = get_event(t);
+  if (!a || !b) return fn();
+  hipEventRecord(a, stream);
+  hipError_t e = fn();
+  hipEventRecord(b, stream);
+  t.recs.push_back({cls, a, b});
+  return e;
+}
+
+// ------------------------------------------------------------ workspace plans --
+
+struct FwdPlan {
+  size_t items_off = 0, bytes = 0;
+  size_t n_items = 0;
+};
+
+FwdPlan plan_fwd(const Shape &s) {
+  FwdPlan pl;
+  size_t n = 0;
+  for (int i = 0; i < s.N; ++i) {
+    int len = s.cu[i + 1] - s.cu[i];
+    n += (size_t)((len + s.bm_tok - 1) / s.bm_tok) * s.Hkv;
+  }
+  pl.n_items = n;
+  pl.items_off = 0;
+  pl.bytes = align_up(n * sizeof(QItem));
+  return pl;
+}
+
+dkv_status check_ws(void *ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return DKV_OK;
+  if (!ws) return fail(DKV_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+  if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+    return fail(DKV_ERR_WORKSPACE, "workspace is not %zu-byte aligned", kAlign);
+  if (ws_bytes < need)
+    return fail(DKV_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  return DKV_OK;
+}
+
+dkv_status run_fwd(const Shape &s, const void *q, const void *kc, const void *vc,
+                   const void *ko, const void *vo, void *o, float *lse, void *ws,
+                   size_t ws_bytes, hipStream_t stream) {
+  FwdPlan pl = plan_fwd(s);
+  dkv_status st = check_ws(ws, ws_bytes, pl.bytes);
+  if (st != DKV_OK) return st;
+  if (pl.n_items == 0) return DKV_OK;
+  std::vector<QItem> items = build_q_items(s, kFwdBN);
+  char *wsb = static_cast<char *>(ws);
+  st = upload(items.data(), items.size() * sizeof(QItem), wsb + pl.items_off, stream);
+  if (st != DKV_OK) return st;
+  FwdArgs a{};
+  a.q = q;
+  a.k_ctx = kc;
+  a.v_ctx = vc;
+  a.k_own = ko;
+  a.v_own = vo;
+  a.o = o;
+  a.lse = lse;
+  a.items = reinterpret_cast<const QItem *>(wsb + pl.items_off);
+  a.Hq = s.Hq;
+  a.Hkv = s.Hkv;
+  a.G = s.G;
+  a.bm_tok = s.bm_tok;
+  a.ctx_len = s.P;
+  a.window_left = s.wl;
+  a.lse_ld = (int)s.T;
+  a.scale = s.scale;
+  hipError_t e = timed(kKFwd, stream, [&] { return launch_fwd(s.dtype, s.d, a, (int)items.size(), stream); });
+  if (e != hipSuccess) return hip_fail(e, "fwd kernel launch");
+  return DKV_OK;
+}
+
+// Key-parallel work items (dK/dV): one per (kv head, key tile) of each sequence's own
+// keys, and per (kv head, prompt key tile, chunk of sequences) of the shared prompt.
+// The chunk size sets how many sequences' partial dK_P/dV_P a workgroup sums in
+// registers before one atomic add per element.
+
+int ctx_chunk(const Shape &s) {
+  static int env = [] {
+    const char *e = getenv("DKV_CTX_CHUNK");
+    return e ? atoi(e) : 0;
+  }();
+  if (env > 0) return std::min(env, std::max(1, s.N));
+  return 1;
+}
+
+long kv_rows_visible(const Shape &s, bool ctx, int key_start, int nk, int len) {
+  long lo, hi;
+  if (ctx) {
+    lo = 0;
+    hi = len;
+    if (s.wl >= 0) hi = std::min<long>(len, (long)key_start + nk - 1 + s.wl - s.P + 1);
+  } else {
+    lo = key_start;
+    hi = len;
+    if (s.wl >= 0) hi = std::min<long>(len, (long)key_start + nk - 1 + s.wl + 1);
+  }
+  return std::max<long>(0, hi - lo);
+}
+
+std::vector<KVItem> build_kv_items(const Shape &s, bool with_ctx) {
+  struct Rec { long work; int region, key_start, lo, hi; };
+  std::vector<Rec> recs;
+  for (int i = 0; i < s.N; ++i) {
+    int len = s.cu[i + 1] - s.cu[i];
+    for (int k0 = 0; k0 < len; k0 += kBwdBN) {
+      int nk = std::min(kBwdBN, len - k0);
+      recs.push_back({kv_rows_visible(s, false, k0, nk, len), kRegionOwn, k0, i, i + 1});
+    }
+  }
+  if (with_ctx && s.P > 0 && s.N > 0) {
+    int cs = ctx_chunk(s);
+    for (int k0 = 0; k0 < s.P; k0 += kBwdBN) {
+      int nk = std::min(kBwdBN, s.P - k0);
+      for (int lo = 0; lo < s.N; lo += cs) {
+        int hi = std::min(s.N, lo + cs);
+        long w = 0;
+        for (int i = lo; i < hi; ++i) w += kv_rows_visible(s, true, k0, nk, s.cu[i + 1] - s.cu[i]);
+        if (w > 0) recs.push_back({w, kRegionCtx, k0, lo, hi});
+      }
+    }
+  }
+  std::stable_sort(recs.begin(), recs.end(),
+                   [](const Rec &a, const Rec &b) { return a.work > b.work; });
+  std::vector<KVItem> items;
+  items.reserve(recs.size() * s.Hkv);
+  for (const Rec &r : recs)
+    for (int g = 0; g < s.Hkv; ++g) items.push_back({g, r.region, r.key_start, r.lo, r.hi, {0, 0, 0}});
+  return items;
+}
+
+struct BwdPlan {
+  size_t d_off = 0, q_off = 0, kv_off = 0, bytes = 0;
+  size_t n_q = 0, n_kv = 0;
+};
+
+BwdPlan plan_bwd(const Shape &s, bool with_ctx) {
+  BwdPlan pl;
+  FwdPlan fq = plan_fwd(s);
+  pl.n_q = fq.n_items;
+  size_t nkv = 0;
+  for (int i = 0; i < s.N; ++i) {
+    int len = s.cu[i + 1] - s.cu[i];
+    nkv += (size_t)((len + kBwdBN - 1) / kBwdBN);
+  }
+  if (with_ctx && s.P > 0 && s.N > 0) {
+    int cs = ctx_chunk(s);
+    nkv += (size_t)((s.P + kBwdBN - 1) / kBwdBN) * ((s.N + cs - 1) / cs);
+  }
+  pl.n_kv = nkv * s.Hkv;   // upper bound (empty windowed items are dropped)
+  pl.d_off = 0;
+  pl.q_off = align_up((size_t)s.Hq * s.T * sizeof(float));
+  pl.kv_off = pl.q_off + align_up(pl.n_q * sizeof(QItem));
+  pl.bytes = pl.kv_off + align_up(pl.n_kv * sizeof(KVItem));
+  if (s.T == 0) pl.bytes = 0;
+  return pl;
+}
+
+struct BwdIO {
+  const int32_t *cu_dev;
+  const void *q, *kc, *vc, *ko, *vo, *o, *dout;
+  const float *lse;
+  void *dq, *dk_own, *dv_own;
+  float *acc_dk, *acc_dv;
+  long acc_rows;      // rows of the accumulator (P for the shared prompt)
+  int flags;
+  void *dk_fin, *dv_fin;
+  bool with_ctx, own_to_acc;
+};
+
+dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
+                   hipStream_t stream) {
+  BwdPlan pl = plan_bwd(s, io.with_ctx);
+  dkv_status st = check_ws(ws, ws_bytes, pl.bytes);
+  if (st != DKV_OK) return st;
+  char *wsb = static_cast<char *>(ws);
+  const long acc_elems = io.acc_rows * s.Hkv * s.d;
+  hipError_t e;
+  if ((io.flags & DKV_ACC_ZERO) && io.acc_dk) {
+    e = timed(kKZero, stream, [&] {
+      hipError_t r = launch_fill_zero(io.acc_dk, acc_elems, stream);
+      return r != hipSuccess ? r : launch_fill_zero(io.acc_dv, acc_elems, stream);
+    });
+    if (e != hipSuccess) return hip_fail(e, "zero acc");
+  }
+  if (s.T > 0) {
+    float *D = reinterpret_cast<float *>(wsb + pl.d_off);
+    e = timed(kKPre, stream, [&] { return launch_bwd_pre(s.dtype, s.d, io.o, io.dout, D, s.T, s.Hq, stream); });
+    if (e != hipSuccess) return hip_fail(e, "bwd preprocess launch");
+    std::vector<QItem> qi = build_q_items(s, kFwdBN);
+    std::vector<KVItem> kv = build_kv_items(s, io.with_ctx);
+    if ((st = upload(qi.data(), qi.size() * sizeof(QItem), wsb + pl.q_off, stream)) != DKV_OK) return st;
+    if ((st = upload(kv.data(), kv.size() * sizeof(KVItem), wsb + pl.kv_off, stream)) != DKV_OK) return st;
+    BwdQArgs qa{};
+    qa.q = io.q; qa.k_ctx = io.kc; qa.v_ctx = io.vc; qa.k_own = io.ko; qa.v_own = io.vo;
+    qa.dout = io.dout; qa.lse = io.lse; qa.D = D; qa.dq = io.dq;
+    qa.items = reinterpret_cast<const QItem *>(wsb + pl.q_off);
+    qa.Hq = s.Hq; qa.Hkv = s.Hkv; qa.G = s.G; qa.bm_tok = s.bm_tok; qa.ctx_len = s.P;
+    qa.window_left = s.wl; qa.lse_ld = (int)s.T; qa.scale = s.scale;
+    e = timed(kKDq, stream, [&] { return launch_bwd_dq(s.dtype, s.d, qa, (int)qi.size(), stream); });
+    if (e != hipSuccess) return hip_fail(e, "dq kernel launch");
+    BwdKVArgs ka{};
+    ka.q = io.q; ka.dout = io.dout; ka.k_ctx = io.kc; ka.v_ctx = io.vc; ka.k_own = io.ko;
+    ka.v_own = io.vo; ka.lse = io.lse; ka.D = D; ka.cu = io.cu_dev;
+    ka.dk_own = io.dk_own; ka.dv_own = io.dv_own; ka.acc_dk = io.acc_dk; ka.acc_dv = io.acc_dv;
+    ka.items = reinterpret_cast<const KVItem *>(wsb + pl.kv_off);
+    ka.Hq = s.Hq; ka.Hkv = s.Hkv; ka.G = s.G; ka.ctx_len = s.P; ka.window_left = s.wl;
+    ka.lse_ld = (int)s.T; ka.own_to_acc = io.own_to_acc ? 1 : 0;
+    ka.scale = s.scale;
+    e = timed(kKDkdv, stream, [&] { return launch_bwd_dkdv(s.dtype, s.d, ka, (int)kv.size(), stream); });
+    if (e != hipSuccess) return hip_fail(e, "dkdv kernel launch");
+  }
+  if ((io.flags & DKV_ACC_FINALIZE) && io.acc_dk) {
+    e = timed(kKCast, stream, [&] {
+      hipError_t r = launch_cast(s.dtype, io.acc_dk, io.dk_fin, acc_elems, stream);
+      return r != hipSuccess ? r : launch_cast(s.dtype, io.acc_dv, io.dv_fin, acc_elems, stream);
+    });
+    if (e != hipSuccess) return hip_fail(e, "cast launch");
+  }
+  return DKV_OK;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI ==
+
+extern "C" {
+
+const char *dkv_last_error(void) { return g_err.c_str(); }
+
+const char *dkv_version(void) { return "dkv 0.1 (gfx950)"; }
+
+void dkv_timing_enable(int on) {
+  Timing &t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  t.on = on != 0;
+}
+
+void dkv_timing_reset(void) {
+  Timing &t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  for (auto &r : t.recs) {
+    hipEventSynchronize(r.b);
+    t.pool.push_back(r.a);
+    t.pool.push_back(r.b);
+  }
+  t.recs.clear();
+}
+
+int dkv_timing_read(const char **names, double *ms, int *launches, int max_entries) {
+  Timing &t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  double sum[kKClasses] = {0};
+  int cnt[kKClasses] = {0};
+  for (auto &r : t.recs) {
+    float x = 0.f;
+    if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&x, r.a, r.b) == hipSuccess) {
+      sum[r.cls] += x;
+      cnt[r.cls] += 1;
+    }
+  }
+  int n = 0;
+  for (int c = 0; c < kKClasses && n < max_entries; ++c) {
+    if (!cnt[c]) continue;
+    if (names) names[n] = kKernelNames[c];
+    if (ms) ms[n] = sum[c];
+    if (launches) launches[n] = cnt[c];
+    ++n;
+  }
+  return n;
+}
+
+size_t dkv_workspace_size(const dkv_params *p, int which_call) {
+  Shape s;
+  bool is_ctx = which_call == DKV_CALL_CTX_FWD || which_call == DKV_CALL_CTX_BWD;
+  if (which_call < DKV_CALL_CTX_FWD || which_call > DKV_CALL_BWD) {
+    fail(DKV_ERR_INVALID_ARG, "unknown call %d", which_call);
+    return (size_t)-1;
+  }
+  if (check_params(p, is_ctx, &s) != DKV_OK) return (size_t)-1;
+  if (which_call == DKV_CALL_CTX_FWD || which_call == DKV_CALL_FWD) return plan_fwd(s).bytes;
+  return plan_bwd(s, which_call == DKV_CALL_BWD).bytes;
+}
+
+dkv_status dkv_ctx_fwd(const dkv_params *p, const void *q, const void *k, const void *v,
+                       void *o, float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  dkv_status st = check_params(p, true, &s);
+  if (st != DKV_OK) return st;
+  bool need = s.T > 0;
+  if ((st = check_ptr(q, "q", need)) || (st = check_ptr(k, "k", need)) ||
+      (st = check_ptr(v, "v", need)) || (st = check_ptr(o, "o", need)) ||
+      (st = check_ptr(lse, "lse", need)))
+    return st;
+  return run_fwd(s, q, k, v, k, v, o, lse, ws, ws_bytes, stream);
+}
+
+dkv_status dkv_fwd(const dkv_params *p, const void *q_resp, const void *k_p, const void *v_p,
+                   const void *k_r, const void *v_r, void *o_r, float *lse_r, void *ws,
+                   size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  dkv_status st = check_params(p, false, &s);
+  if (st != DKV_OK) return st;
+  bool need = s.T > 0;
+  if ((st = check_ptr(q_resp, "q_resp", need)) || (st = check_ptr(k_p, "k_p", need && s.P > 0)) ||
+      (st = check_ptr(v_p, "v_p", need && s.P > 0)) || (st = check_ptr(k_r, "k_r", need)) ||
+      (st = check_ptr(v_r, "v_r", need)) || (st = check_ptr(o_r, "o_r", need)) ||
+      (st = check_ptr(lse_r, "lse_r", need)))
+    return st;
+  return run_fwd(s, q_resp, k_p, v_p, k_r, v_r, o_r, lse_r, ws, ws_bytes, stream);
+}
+
+dkv_status dkv_ctx_bwd(const dkv_params *p, const void *q, const void *k, const void *v,
+                       const void *o, const float *lse, const void *dout, void *dq, void *dk,
+                       void *dv, float *acc_dk, float *acc_dv, int acc_flags, void *ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  dkv_status st = check_params(p, true, &s);
+  if (st != DKV_OK) return st;
+  if (acc_flags & ~(DKV_ACC_ZERO | DKV_ACC_FINALIZE))
+    return fail(DKV_ERR_INVALID_ARG, "dkv_ctx_bwd accepts DKV_ACC_ZERO | DKV_ACC_FINALIZE only");
+  if (s.T == 0) return DKV_OK;   // nothing to compute, clear or cast
+  const bool use_acc = acc_dk != nullptr || acc_dv != nullptr;
+  bool need = true;
+  if ((st = check_ptr(q, "q", need)) || (st = check_ptr(k, "k", need)) ||
+      (st = check_ptr(v, "v", need)) || (st = check_ptr(o, "o", need)) ||
+      (st = check_ptr(lse, "lse", need)) || (st = check_ptr(dout, "dout", need)) ||
+      (st = check_ptr(dq, "dq", need)))
+    return st;
+  if (use_acc) {
+    if ((st = check_ptr(acc_dk, "acc_dk", true)) || (st = check_ptr(acc_dv, "acc_dv", true)))
+      return st;
+    if ((acc_flags & DKV_ACC_FINALIZE) &&
+        ((st = check_ptr(dk, "dk", need)) || (st = check_ptr(dv, "dv", need))))
+      return st;
+  } else {
+    if (acc_flags)
+      return fail(DKV_ERR_INVALID_ARG, "accumulator flags given without accumulator buffers");
+    if ((st = check_ptr(dk, "dk", need)) || (st = check_ptr(dv, "dv", need))) return st;
+  }
+  BwdIO io{};
+  io.cu_dev = p->cu_seqlens_dev;
+  io.q = q; io.kc = k; io.vc = v; io.ko = k; io.vo = v; io.o = o; io.dout = dout; io.lse = lse;
+  io.dq = dq; io.dk_own = dk; io.dv_own = dv; io.acc_dk = acc_dk; io.acc_dv = acc_dv;
+  io.acc_rows = s.T; io.flags = acc_flags; io.dk_fin = dk; io.dv_fin = dv;
+  io.with_ctx = false; io.own_to_acc = use_acc;
+  return run_bwd(s, io, ws, ws_bytes, stream);
+}
+
+dkv_status dkv_bwd(const dkv_params *p, const void *q_resp, const void *k_p, const void *v_p,
+                   const void *k_r, const void *v_r, const void *o_r, const float *lse_r,
+                   const void *dout_r, void *dq_r, void *dk_r, void *dv_r, float *acc_dk_p,
+                   float *acc_dv_p, int acc_flags, void *dk_p, void *dv_p, void *ws,
+                   size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  dkv_status st = check_params(p, false, &s);
+  if (st != DKV_OK) return st;
+  if (acc_flags & DKV_ACC_SPLIT)
+    return fail(DKV_ERR_UNSUPPORTED, "DKV_ACC_SPLIT is not available in this build");
+  if (acc_flags & ~(DKV_ACC_ZERO | DKV_ACC_FINALIZE))
+    return fail(DKV_ERR_INVALID_ARG, "unknown accumulator flags 0x%x", acc_flags);
+  bool need = s.T > 0;
+  bool needp = s.P > 0;
+  if ((st = check_ptr(q_resp, "q_resp", need)) || (st = check_ptr(k_p, "k_p", need && needp)) ||
+      (st = check_ptr(v_p, "v_p", need && needp)) || (st = check_ptr(k_r, "k_r", need)) ||
+      (st = check_ptr(v_r, "v_r", need)) || (st = check_ptr(o_r, "o_r", need)) ||
+      (st = check_ptr(lse_r, "lse_r", need)) || (st = check_ptr(dout_r, "dout_r", need)) ||
+      (st = check_ptr(dq_r, "dq_r", need)) || (st = check_ptr(dk_r, "dk_r", need)) ||
+      (st = check_ptr(dv_r, "dv_r", need)) ||
+      (st = check_ptr(acc_dk_p, "acc_dk_p", needp)) ||
+      (st = check_ptr(acc_dv_p, "acc_dv_p", needp)))
+    return st;
+  if ((acc_flags & DKV_ACC_FINALIZE) &&
+      ((st = check_ptr(dk_p, "dk_p", needp)) || (st = check_ptr(dv_p, "dv_p", needp))))
+    return st;
+  BwdIO io{};
+  io.cu_dev = p->cu_seqlens_dev;
+  io.q = q_resp; io.kc = k_p; io.vc = v_p; io.ko = k_r; io.vo = v_r; io.o = o_r;
+  io.dout = dout_r; io.lse = lse_r; io.dq = dq_r; io.dk_own = dk_r; io.dv_own = dv_r;
+  io.acc_dk = needp ? acc_dk_p : nullptr; io.acc_dv = needp ? acc_dv_p : nullptr;
+  io.acc_rows = s.P; io.flags = acc_flags; io.dk_fin = dk_p; io.dv_fin = dv_p;
+  io.with_ctx = true; io.own_to_acc = false;
+  return run_bwd(s, io, ws, ws_bytes, stream);
+}
+
+dkv_status dkv_cast_acc(const dkv_params *p, int32_t rows, const float *acc_dk,
+                        const float *acc_dv, void *dk, void *dv, hipStream_t stream) {
+  if (!p) return fail(DKV_ERR_INVALID_ARG, "params is NULL");
+  if (rows < 0) return fail(DKV_ERR_INVALID_ARG, "rows < 0");
+  if (p->dtype != DKV_BF16 && p->dtype != DKV_FP32)
+    return fail(DKV_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
+  if (p->num_heads_kv <= 0 || p->head_dim <= 0)
+    return fail(DKV_ERR_INVALID_ARG, "bad head shape");
+  dkv_status st;
+  bool need = rows > 0;
+  if ((st = check_ptr(acc_dk, "acc_dk", need)) || (st = check_ptr(acc_dv, "acc_dv", need)) ||
+      (st = check_ptr(dk, "dk", need)) || (st = check_ptr(dv, "dv", need)))
+    return st;
+  long n = (long)rows * p->num_heads_kv * p->head_dim;
+  hipError_t e;
+  e = timed(kKCast, stream, [&] {
+    hipError_t r = launch_cast(p->dtype, acc_dk, dk, n, stream);
+    return r != hipSuccess ? r : launch_cast(p->dtype, acc_dv, dv, n, stream);
+  });
+  if (e != hipSuccess) return hip_fail(e, "cast");
+  return DKV_OK;
+}
+
+}  // extern "C"

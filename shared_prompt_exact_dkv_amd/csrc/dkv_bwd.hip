@@ -1,0 +1,602 @@
+// dkv_bwd.hip -- backward kernels ("DualKV", arXiv 2605.15422, §3.2 and App. A.4).
+//
+// For each visible (query row t, key j) pair of one q-head:
+//   p  = exp(scale * <q_t, k_j> - lse_t)        (recomputed from the forward's LSE)
+//   dP = <dO_t, v_j>,   dS = p * (dP - D_t),    D_t = <dO_t, O_t>
+//   dQ_t += scale * dS * k_j,   dK_j += scale * dS * q_t,   dV_j += p * dO_t
+// Kernels:
+//   bwd_pre   D = rowsum(dO * O) in fp32 (the auxiliary preprocessing launch)
+//   bwd_dq    query-parallel: a workgroup keeps 128 query rows in registers and
+//             walks the shared-prompt key tiles, then its own sequence's tiles,
+//             exactly like the forward; dQ is written once, no atomics.
+//   bwd_dkdv  key-parallel: a workgroup keeps 128 keys (K, V and the dK, dV
+//             accumulators) in registers and walks the query rows that see them.
+//             Response keys are written directly; shared-prompt keys are visited
+//             once per chunk of sequences and their partial dK_P, dV_P summed into
+//             the caller's fp32 accumulator with atomic adds (§3.2 "fp32 atomic
+//             accumulation", eq. (6)).
+//   cast      the accumulator is rounded to the tensor dtype once (§3.2 Stage 2).
+// Transposed operands (contractions over query rows or key rows) are read from the
+// same row-layout LDS tiles with the gfx950 transpose read.
+#include "dkv_device.h"
+#include "dkv_launch.h"
+#include "dkv_tiles.h"
+
+namespace dkv {
+
+// ------------------------------------------------------------------ bwd_pre --
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const T *o, const T *dout, float *D,
+                                                      long T_tok, int Hq) {
+  constexpr int E = 16 / sizeof(T);          // elements per 16-byte chunk
+  constexpr int TPR = HD / E;                // threads per (token, head) row
+  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  const long row = gid / TPR;                // token-major: row = t * Hq + h
+  const int ch = gid % TPR;
+  float acc = 0.f;
+  if (row < T_tok * Hq) {
+    uint4 a = *reinterpret_cast<const uint4 *>(o + row * HD + ch * E);
+    uint4 b = *reinterpret_cast<const uint4 *>(dout + row * HD + ch * E);
+    const T *x = reinterpret_cast<const T *>(&a);
+    const T *y = reinterpret_cast<const T *>(&b);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc += to_f32(x[e]) * to_f32(y[e]);
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < T_tok * Hq && ch == 0) {
+    long t = row / Hq;
+    int h = row - t * Hq;
+    D[(long)h * T_tok + t] = acc;
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float *p, long n) {
+  long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i + 3 < n) {
+    *reinterpret_cast<float4 *>(p + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+  } else {
+    for (; i < n; ++i) p[i] = 0.f;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void cast_kernel(const float *src, T *dst, long n) {
+  long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i + 3 < n) {
+    float4 v = *reinterpret_cast<const float4 *>(src + i);
+    dst[i] = from_f32<T>(v.x);
+    dst[i + 1] = from_f32<T>(v.y);
+    dst[i + 2] = from_f32<T>(v.z);
+    dst[i + 3] = from_f32<T>(v.w);
+  } else {
+    for (; i < n; ++i) dst[i] = from_f32<T>(src[i]);
+  }
+}
+
+// ------------------------------------------------------------------- bwd_dq --
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdQArgs a) {
+  constexpr int BN = kFwdBN;
+  using TC = TileCfg<T, HD, BN>;
+  using M = Mfma<T>;
+  constexpr int NKC = HD / M::K;
+  constexpr int NDB = HD / 32;
+  constexpr int NKB = BN / 32;
+  __shared__ __attribute__((aligned(16))) char smem[2 * TC::kRowBytes];
+  char *ks = smem;
+  char *vs = smem + TC::kRowBytes;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const QItem it = a.items[blockIdx.x];
+  const int g = it.g, seq0 = it.seq_start, seqlen = it.seq_len;
+  const int t0 = it.tile * a.bm_tok;
+  const int nt = min(a.bm_tok, seqlen - t0);
+  const int qr = wave * 32 + col;
+  int tok = qr / a.G;
+  const int hj = qr - tok * a.G;
+  const bool row_valid = tok < nt;
+  if (!row_valid) tok = nt - 1;
+  const int h = g * a.G + hj;
+  const int P = a.ctx_len, wl = a.window_left;
+  const int qpos = P + t0 + tok;
+  const int qmin = P + t0, qmax = P + t0 + nt - 1;
+  const long qld = (long)a.Hq * HD;
+  const long kld = (long)a.Hkv * HD;
+  const long qrow = (long)(seq0 + t0 + tok);
+
+  const T *qptr = reinterpret_cast<const T *>(a.q) + qrow * qld + (long)h * HD;
+  const T *dptr = reinterpret_cast<const T *>(a.dout) + qrow * qld + (long)h * HD;
+  typename M::frag qf[NKC], df[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    if constexpr (sizeof(T) == 2) {
+      qf[kc] = as_bf16x8(*reinterpret_cast<const uint4 *>(qptr + kc * 16 + half * 8));
+      df[kc] = as_bf16x8(*reinterpret_cast<const uint4 *>(dptr + kc * 16 + half * 8));
+    } else {
+      qf[kc] = qptr[kc * 2 + half];
+      df[kc] = dptr[kc * 2 + half];
+    }
+  }
+  using SM = Softmax<T>;
+  const float sf = SM::factor(a.scale);
+  const float lse2 = SM::lse_in(a.lse[(long)h * a.lse_ld + qrow]);
+  const float Dq = a.D[(long)h * a.lse_ld + qrow];
+
+  f32x16 acc[NDB];
+  f32x16 comp[sizeof(T) == 4 ? NDB : 1];   // Kahan terms (fp32 path only)
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = zero16();
+#pragma unroll
+  for (int db = 0; db < (sizeof(T) == 4 ? NDB : 1); ++db) comp[db] = zero16();
+
+  const int ctx_lo = (wl >= 0) ? max(0, qmin - wl) : 0;
+  const int ctx_t0 = (ctx_lo / BN) * BN;
+  const int n_ctx = (P > ctx_lo) ? (P - ctx_t0 + BN - 1) / BN : 0;
+  const int own_lo = (wl >= 0) ? max(0, t0 - wl) : 0;
+  const int own_t0 = (own_lo / BN) * BN;
+  const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
+  const int n_tiles = n_ctx + n_own;
+
+  const T *kc_base = reinterpret_cast<const T *>(a.k_ctx) + (long)g * HD;
+  const T *vc_base = reinterpret_cast<const T *>(a.v_ctx) + (long)g * HD;
+  const T *ko_base = reinterpret_cast<const T *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
+  const T *vo_base = reinterpret_cast<const T *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
+
+  RowRegs<T, HD, BN> kregs, vregs;
+  auto issue = [&](int i) {
+    if (i < n_ctx) {
+      int s = ctx_t0 + i * BN;
+      kregs.load(kc_base + (long)s * kld, kld, P - s, tid);
+      vregs.load(vc_base + (long)s * kld, kld, P - s, tid);
+    } else {
+      int s = own_t0 + (i - n_ctx) * BN;
+      kregs.load(ko_base + (long)s * kld, kld, seqlen - s, tid);
+      vregs.load(vo_base + (long)s * kld, kld, seqlen - s, tid);
+    }
+  };
+  if (n_tiles > 0) issue(0);
+
+  for (int i = 0; i < n_tiles; ++i) {
+    int nrows, kpos0;
+    if (i < n_ctx) {
+      int s = ctx_t0 + i * BN;
+      nrows = P - s;
+      kpos0 = s;
+    } else {
+      int s = own_t0 + (i - n_ctx) * BN;
+      nrows = seqlen - s;
+      kpos0 = P + s;
+    }
+    __syncthreads();
+    kregs.store(ks, tid);
+    vregs.store(vs, tid);
+    __syncthreads();
+    if (i + 1 < n_tiles) issue(i + 1);
+
+    f32x16 s[NKB], dp[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = zero16();
+      dp[kb] = zero16();
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        s[kb] = mfma(row_frag<T, HD, BN>(ks, kb * 32 + col, kc, half), qf[kc], s[kb]);
+        dp[kb] = mfma(row_frag<T, HD, BN>(vs, kb * 32 + col, kc, half), df[kc], dp[kb]);
+      }
+    }
+    const bool need_mask = (nrows < BN) || (kpos0 + BN - 1 > qmin) ||
+                           (wl >= 0 && kpos0 < qmax - wl);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float p = SM::ex(fmaf(s[kb][v], sf, -lse2));
+        if (need_mask) {
+          int kk = kb * 32 + c_row(v, half);
+          int kp = kpos0 + kk;
+          bool vis = (kk < nrows) && (kp <= qpos) && (wl < 0 || kp >= qpos - wl);
+          if (!vis) p = 0.f;
+        }
+        s[kb][v] = p * (dp[kb][v] - Dq);   // dS^T
+      }
+
+    // dQ^T += K^T dS^T.
+    if constexpr (sizeof(T) == 2) {
+      bf16x8 sf[2 * NKB];
+#pragma unroll
+      for (int u = 0; u < 2 * NKB; ++u) {
+        float t[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = s[u >> 1][8 * (u & 1) + e];
+        sf[u] = pack8(t);
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int u = 0; u < 2 * NKB; ++u)
+          acc[db] = mfma(tr_frag<TC::kRowStride>(ks, 16 * u, db * 32, lane), sf[u], acc[db]);
+    } else {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        f32x16 part = zero16();
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            part = mfma(row_elem<HD, BN>(ks, kb * 32 + c_row(v, half), db * 32 + col),
+                        s[kb][v], part);
+        kahan_add(acc[db], comp[db], part);
+      }
+    }
+  }
+
+  if (row_valid) {
+    T *optr = reinterpret_cast<T *>(a.dq) + qrow * qld + (long)h * HD;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int dim = db * 32 + 8 * i + 4 * half;
+        if constexpr (sizeof(T) == 2) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * i + e] * a.scale);
+          *reinterpret_cast<bf16x4 *>(optr + dim) = w;
+        } else {
+          float4 w = make_float4(acc[db][4 * i] * a.scale, acc[db][4 * i + 1] * a.scale,
+                                 acc[db][4 * i + 2] * a.scale, acc[db][4 * i + 3] * a.scale);
+          *reinterpret_cast<float4 *>(optr + dim) = w;
+        }
+      }
+  }
+}
+
+// ----------------------------------------------------------------- bwd_dkdv --
+
+// Query-step rows: 32 flattened (token, head) rows of one kv head's G q-heads.
+template <typename T, int HD> struct QStepRegs : RowRegs<T, HD, kBwdBM> {
+  using C = TileCfg<T, HD, kBwdBM>;
+  // base: row 0 of the sequence, first q-head of the group; rows f0 .. f0+31 of the
+  // flattened (token, head) index, valid below fend.
+  __device__ __forceinline__ void load_flat(const T *base, long qld, int G, int f0, int fend,
+                                            int tid) {
+    constexpr int per_row = (sizeof(T) == 2) ? HD / 8 : HD / 4;
+#pragma unroll
+    for (int p = 0; p < C::kRowPasses; ++p) {
+      int id = p * 256 + tid;
+      int row = id / per_row, ch = id % per_row;
+      int f = f0 + row;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (id < C::kChunks && f < fend) {
+        int t = f / G, j = f - t * G;
+        v = *reinterpret_cast<const uint4 *>(base + (long)t * qld + (long)j * HD +
+                                             ch * (16 / sizeof(T)));
+      }
+      this->r[p] = v;
+    }
+  }
+};
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
+  constexpr int BM = kBwdBM;          // query rows per step
+  constexpr int BNW = kBwdBN;         // keys per workgroup (4 waves x 32)
+  using TC = TileCfg<T, HD, BM>;
+  using M = Mfma<T>;
+  constexpr int NKC = HD / M::K;
+  constexpr int NDB = HD / 32;
+  __shared__ __attribute__((aligned(16))) char smem[2 * TC::kRowBytes + 2 * BM * 4];
+  char *qs = smem;
+  char *dos = smem + TC::kRowBytes;
+  float *lse_s = reinterpret_cast<float *>(smem + 2 * TC::kRowBytes);
+  float *d_s = lse_s + BM;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const KVItem it = a.items[blockIdx.x];
+  const int g = it.g, G = a.G, P = a.ctx_len, wl = a.window_left;
+  const bool ctx = it.region == kRegionCtx;
+  const long qld = (long)a.Hq * HD;
+  const long kld = (long)a.Hkv * HD;
+  const int own0 = ctx ? 0 : a.cu[it.seq_lo];                  // row of the own sequence
+  const int nkeys = ctx ? P - it.key_start : a.cu[it.seq_lo + 1] - own0 - it.key_start;
+  const int kbase = ctx ? 0 : P;                               // logical position offset
+  const int nk_tile = min(BNW, nkeys);
+
+  // This lane's key (one column of the S tile) and its K, V fragments.
+  const int kw0 = 32 * wave;                                   // wave's first key in tile
+  const int key = kw0 + col;
+  const bool key_valid = key < nkeys;
+  using SM = Softmax<T>;
+  const float sf = SM::factor(a.scale);
+  const T *kp = reinterpret_cast<const T *>(ctx ? a.k_ctx : a.k_own) +
+                (long)(own0 + it.key_start + (key_valid ? key : 0)) * kld + (long)g * HD;
+  const T *vp = reinterpret_cast<const T *>(ctx ? a.v_ctx : a.v_own) +
+                (long)(own0 + it.key_start + (key_valid ? key : 0)) * kld + (long)g * HD;
+  typename M::frag kf[NKC], vf[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    if constexpr (sizeof(T) == 2) {
+      uint4 z = make_uint4(0, 0, 0, 0);
+      kf[kc] = as_bf16x8(key_valid ? *reinterpret_cast<const uint4 *>(kp + kc * 16 + half * 8) : z);
+      vf[kc] = as_bf16x8(key_valid ? *reinterpret_cast<const uint4 *>(vp + kc * 16 + half * 8) : z);
+    } else {
+      kf[kc] = key_valid ? kp[kc * 2 + half] : 0.f;
+      vf[kc] = key_valid ? vp[kc * 2 + half] : 0.f;
+    }
+  }
+  const bool wave_active = kw0 < nkeys;
+
+  f32x16 dk[NDB], dv[NDB];
+  constexpr int NC = sizeof(T) == 4 ? NDB : 1;   // Kahan terms (fp32 path only)
+  f32x16 ck[NC], cv[NC];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dk[db] = zero16();
+    dv[db] = zero16();
+  }
+#pragma unroll
+  for (int db = 0; db < NC; ++db) {
+    ck[db] = zero16();
+    cv[db] = zero16();
+  }
+
+  // Query rows that can see this key tile, per sequence, in flattened units.
+  auto seq_range = [&](int s, int &fa, int &fb) {
+    int len = a.cu[s + 1] - a.cu[s];
+    int r_lo, r_hi;
+    if (ctx) {
+      r_lo = 0;
+      r_hi = len;
+      if (wl >= 0) r_hi = min(len, it.key_start + nk_tile - 1 + wl - P + 1);
+    } else {
+      r_lo = it.key_start;
+      r_hi = len;
+      if (wl >= 0) r_hi = min(len, it.key_start + nk_tile - 1 + wl + 1);
+    }
+    fa = r_lo * G;
+    fb = r_hi > r_lo ? r_hi * G : fa;
+  };
+
+  // Cursor over (sequence, 32-row step).
+  int cs = it.seq_lo, cf = 0, cfe = 0;
+  bool done = false;
+  auto seek = [&]() {   // from sequence cs onward, find a non-empty range
+    while (cs < it.seq_hi) {
+      int fa, fb;
+      seq_range(cs, fa, fb);
+      if (fb > fa) {
+        cf = fa;
+        cfe = fb;
+        return;
+      }
+      ++cs;
+    }
+    done = true;
+  };
+  seek();
+
+  QStepRegs<T, HD> qregs, dregs;
+  float lse_r = INFINITY, d_r = 0.f;
+  auto issue = [&]() {
+    const int s0 = a.cu[cs];
+    const T *qb = reinterpret_cast<const T *>(a.q) + (long)s0 * qld + (long)g * G * HD;
+    const T *db_ = reinterpret_cast<const T *>(a.dout) + (long)s0 * qld + (long)g * G * HD;
+    qregs.load_flat(qb, qld, G, cf, cfe, tid);
+    dregs.load_flat(db_, qld, G, cf, cfe, tid);
+    if (tid < BM) {
+      int f = cf + tid;
+      if (f < cfe) {
+        int t = f / G, j = f - t * G;
+        long idx = (long)(g * G + j) * a.lse_ld + s0 + t;
+        lse_r = SM::lse_in(a.lse[idx]);
+        d_r = a.D[idx];
+      } else {
+        lse_r = INFINITY;
+        d_r = 0.f;
+      }
+    }
+  };
+  if (!done) issue();
+
+  while (!done) {
+    const int s_cur = cs, f0 = cf, fend = cfe;
+    __syncthreads();
+    qregs.store(qs, tid);
+    dregs.store(dos, tid);
+    if (tid < BM) {
+      lse_s[tid] = lse_r;
+      d_s[tid] = d_r;
+    }
+    __syncthreads();
+    cf += BM;
+    if (cf >= cfe) {
+      ++cs;
+      seek();
+    }
+    if (!done) issue();
+
+    if (wave_active) {
+      // S = Q K^T and dP = dO V^T for 32 query rows x this wave's 32 keys.
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        s = mfma(row_frag<T, HD, BM>(qs, col, kc, half), kf[kc], s);
+        dp = mfma(row_frag<T, HD, BM>(dos, col, kc, half), vf[kc], dp);
+      }
+      const int ta = f0 / G;
+      const int tb = (min(f0 + BM, fend) - 1) / G;
+      const int qpa = P + ta, qpb = P + tb;
+      const int kpa = kbase + it.key_start + kw0;
+      const int kpb = kbase + it.key_start + min(kw0 + 32, nkeys) - 1;
+      const bool full = (f0 + BM <= fend) && (kw0 + 32 <= nkeys) && (kpb <= qpa) &&
+                        (wl < 0 || kpa >= qpb - wl);
+      const int kpos = kbase + it.key_start + key;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float4 l4 = *reinterpret_cast<const float4 *>(lse_s + 8 * i + 4 * half);
+        float4 d4 = *reinterpret_cast<const float4 *>(d_s + 8 * i + 4 * half);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = 4 * i + e;
+          float p = SM::ex(fmaf(s[v], sf, -lv[e]));
+          if (!full) {
+            int f = f0 + c_row(v, half);
+            int qp = P + f / G;
+            bool vis = (f < fend) && key_valid && (kpos <= qp) && (wl < 0 || kpos >= qp - wl);
+            if (!vis) p = 0.f;
+          }
+          s[v] = p;                          // P
+          dp[v] = p * (dp[v] - dv4[e]);      // dS
+        }
+      }
+      // dV += P^T dO and dK += dS^T Q (contractions over the step's query rows).
+      if constexpr (sizeof(T) == 2) {
+        bf16x8 pf[2], sf[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float t1[8], t2[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            t1[e] = s[8 * u + e];
+            t2[e] = dp[8 * u + e];
+          }
+          pf[u] = pack8(t1);
+          sf[u] = pack8(t2);
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            dv[db] = mfma(pf[u], tr_frag<TC::kRowStride>(dos, 16 * u, db * 32, lane), dv[db]);
+            dk[db] = mfma(sf[u], tr_frag<TC::kRowStride>(qs, 16 * u, db * 32, lane), dk[db]);
+          }
+      } else {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          f32x16 pv = zero16(), pk = zero16();
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = c_row(v, half);
+            pv = mfma(s[v], row_elem<HD, BM>(dos, r, db * 32 + col), pv);
+            pk = mfma(dp[v], row_elem<HD, BM>(qs, r, db * 32 + col), pk);
+          }
+          kahan_add(dv[db], cv[db], pv);
+          kahan_add(dk[db], ck[db], pk);
+        }
+      }
+    }
+    (void)s_cur;
+  }
+
+  // Epilogue: lane holds dims db*32 + col of keys kw0 + c_row(v, half).
+  if (!wave_active) return;
+  const bool to_acc = ctx || a.own_to_acc;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int k = kw0 + c_row(v, half);
+      if (k >= nkeys) continue;
+      const long off = (long)(own0 + it.key_start + k) * kld + (long)g * HD + db * 32 + col;
+      const float gk = dk[db][v] * a.scale;
+      const float gv = dv[db][v];
+      if (to_acc) {
+        atomicAdd(a.acc_dk + off, gk);
+        atomicAdd(a.acc_dv + off, gv);
+      } else {
+        reinterpret_cast<T *>(a.dk_own)[off] = from_f32<T>(gk);
+        reinterpret_cast<T *>(a.dv_own)[off] = from_f32<T>(gv);
+      }
+    }
+}
+
+// ---------------------------------------------------------------- launchers --
+
+template <typename T, int HD>
+static hipError_t pre_t(const void *o, const void *dout, float *D, long T_tok, int Hq,
+                        hipStream_t s) {
+  constexpr int TPR = HD / (16 / sizeof(T));
+  long threads = T_tok * Hq * TPR;
+  long blocks = (threads + 255) / 256;
+  hipLaunchKernelGGL((bwd_pre_kernel<T, HD>), dim3(blocks), dim3(256), 0, s,
+                     reinterpret_cast<const T *>(o), reinterpret_cast<const T *>(dout), D, T_tok,
+                     Hq);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pre(int dtype, int hd, const void *o, const void *dout, float *D, long T,
+                          int Hq, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (dtype == 0) {
+    if (hd == 64) return pre_t<bf16, 64>(o, dout, D, T, Hq, s);
+    if (hd == 128) return pre_t<bf16, 128>(o, dout, D, T, Hq, s);
+  } else {
+    if (hd == 64) return pre_t<float, 64>(o, dout, D, T, Hq, s);
+    if (hd == 128) return pre_t<float, 128>(o, dout, D, T, Hq, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fill_zero(float *p, long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  long blocks = (n + 1023) / 1024;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast(int dtype, const float *src, void *dst, long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  long blocks = (n + 1023) / 1024;
+  if (dtype == 0)
+    hipLaunchKernelGGL(cast_kernel<bf16>, dim3(blocks), dim3(256), 0, s, src,
+                       reinterpret_cast<bf16 *>(dst), n);
+  else
+    hipLaunchKernelGGL(cast_kernel<float>, dim3(blocks), dim3(256), 0, s, src,
+                       reinterpret_cast<float *>(dst), n);
+  return hipGetLastError();
+}
+
+template <typename T, int HD>
+static hipError_t dq_t(const BwdQArgs &a, int n, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_dq_kernel<T, HD>), dim3(n), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(int dtype, int hd, const BwdQArgs &a, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (dtype == 0) {
+    if (hd == 64) return dq_t<bf16, 64>(a, n, s);
+    if (hd == 128) return dq_t<bf16, 128>(a, n, s);
+  } else {
+    if (hd == 64) return dq_t<float, 64>(a, n, s);
+    if (hd == 128) return dq_t<float, 128>(a, n, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int HD>
+static hipError_t dkdv_t(const BwdKVArgs &a, int n, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, HD>), dim3(n), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(int dtype, int hd, const BwdKVArgs &a, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (dtype == 0) {
+    if (hd == 64) return dkdv_t<bf16, 64>(a, n, s);
+    if (hd == 128) return dkdv_t<bf16, 128>(a, n, s);
+  } else {
+    if (hd == 64) return dkdv_t<float, 64>(a, n, s);
+    if (hd == 128) return dkdv_t<float, 128>(a, n, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dkv

@@ -1,0 +1,123 @@
+// dkv_device.h -- device-side building blocks shared by the DualKV kernels (gfx950).
+//
+// Matrix products use the CDNA4 32x32 MFMA forms:
+//   bf16: v_mfma_f32_32x32x16_bf16  A[32x16] * B[16x32] -> C[32x32] fp32
+//   fp32: v_mfma_f32_32x32x2_f32    A[32x2]  * B[2x32]  -> C[32x32] fp32
+// Lane layout (wave64, lane l, col = l % 32, half = l / 32):
+//   A operand: row = col, k = half * KL + [0, KL)      (KL = 8 bf16 / 1 fp32)
+//   B operand: column = col, same k split
+//   C: column = col; element v (0..15) is row 8*(v/4) + 4*half + (v%4)
+// So a C tile read back per lane is "one column, 16 rows"; the kernels compute
+// transposed score tiles (keys x queries) so that each lane owns one query row of
+// the softmax, and feed the C tile straight back as the B operand of the next
+// product.  A C tile used as a k-operand pairs lane-half `half`, element e with row
+//   kappa(half, e) = 8*(e/4) + 4*half + (e%4)     (within a 16-row slice)
+// and the other operand is read in that same order from an LDS layout that keeps
+// four consecutive rows of each column together ("T4": [row/4][col][row%4]).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dkv {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+static constexpr float kLog2e = 1.4426950408889634f;
+static constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+template <typename T> struct Mfma;
+template <> struct Mfma<bf16> {
+  using frag = bf16x8;
+  static constexpr int K = 16;   // contraction depth of one MFMA
+  static constexpr int KL = 8;   // k values per lane
+};
+template <> struct Mfma<float> {
+  using frag = float;
+  static constexpr int K = 2;
+  static constexpr int KL = 1;
+};
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Row index (within a 32-row C tile) of element v held by lane-half `half`.
+__device__ __forceinline__ int c_row(int v, int half) { return 8 * (v >> 2) + 4 * half + (v & 3); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// Pack eight fp32 values into a bf16 fragment (round to nearest even).
+__device__ __forceinline__ bf16x8 pack8(const float *x) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)x[i];
+  return r;
+}
+
+// Low/high 16-bit halves of two words interleaved: (lo(a), lo(b)) and (hi(a), hi(b)).
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Compensated (Kahan) add of a partial tile sum into a running fp32 accumulator.
+// Used on the fp32 path, whose gradients are summed over thousands of terms and
+// checked at 1e-5 absolute.
+__device__ __forceinline__ void kahan_add(f32x16 &sum, f32x16 &comp, const f32x16 &x) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float y = x[i] - comp[i];
+    float t = sum[i] + y;
+    comp[i] = (t - sum[i]) - y;
+    sum[i] = t;
+  }
+}
+
+// Exponent domain of the softmax.  bf16 runs in base 2 with the hardware exp2
+// (logits pre-multiplied by scale*log2(e)); the fp32 path, whose results are
+// checked at 1e-5, runs in base e with the accurate expf/logf so that neither the
+// logits nor the stored natural-log LSE pass through a rounded log2(e) factor.
+template <typename T> struct Softmax {
+  // factor applied to raw scores; LSE (natural log) -> kernel domain
+  __device__ static float factor(float scale) { return scale * kLog2e; }
+  __device__ static float lse_in(float lse) { return lse * kLog2e; }
+  __device__ static float ex(float x) { return fast_exp2(x); }
+  __device__ static float lse_out(float m, float l) { return (m + fast_log2(l)) * kLn2; }
+};
+template <> struct Softmax<float> {
+  __device__ static float factor(float scale) { return scale; }
+  __device__ static float lse_in(float lse) { return lse; }
+  __device__ static float ex(float x) { return expf(x); }
+  __device__ static float lse_out(float m, float l) { return m + logf(l); }
+};
+
+}  // namespace dkv

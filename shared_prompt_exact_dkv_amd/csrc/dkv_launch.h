@@ -1,0 +1,84 @@
+// dkv_launch.h -- host-visible kernel argument blocks and launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dkv {
+
+// Key/value tile height of the forward and dQ kernels; query rows per workgroup
+// (4 waves x 32 rows).  A workgroup's query rows are bm_tok tokens x G heads of one
+// kv head, token-major, so each 32-row wave block mixes tokens and heads.
+static constexpr int kFwdBN = 64;
+static constexpr int kRowsPerWG = 128;
+// Key rows per dK/dV workgroup (4 waves x 32 keys) and query rows per step.
+static constexpr int kBwdBN = 128;
+static constexpr int kBwdBM = 32;
+
+// Work item of the query-parallel kernels (forward, dQ).
+struct QItem {
+  int32_t g;          // kv head
+  int32_t tile;       // query tile index within the sequence
+  int32_t seq_start;  // first row of the sequence in the query / own-key tensors
+  int32_t seq_len;    // rows of the sequence
+};
+
+struct FwdArgs {
+  const void *q, *k_ctx, *v_ctx, *k_own, *v_own;
+  void *o;
+  float *lse;
+  const QItem *items;
+  int Hq, Hkv, G, bm_tok;
+  int ctx_len;        // P: logical offset of the own region (0 = no shared region)
+  int window_left;    // -1 global
+  int lse_ld;         // tokens per LSE row
+  float scale;        // softmax scale
+};
+
+hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs &a, int n_items, hipStream_t s);
+
+// ---- backward ----
+
+// D[h][t] = sum_c dO[t][h][c] * O[t][h][c] (fp32), rows = T tokens x Hq heads.
+hipError_t launch_bwd_pre(int dtype, int head_dim, const void *o, const void *dout, float *D,
+                          long T, int Hq, hipStream_t s);
+hipError_t launch_fill_zero(float *p, long n, hipStream_t s);
+// dst[i] = round(src[i]) in dtype (a copy for fp32).
+hipError_t launch_cast(int dtype, const float *src, void *dst, long n, hipStream_t s);
+
+struct BwdQArgs {
+  const void *q, *k_ctx, *v_ctx, *k_own, *v_own, *dout;
+  const float *lse, *D;
+  void *dq;
+  const QItem *items;
+  int Hq, Hkv, G, bm_tok, ctx_len, window_left, lse_ld;
+  float scale;
+};
+hipError_t launch_bwd_dq(int dtype, int head_dim, const BwdQArgs &a, int n_items, hipStream_t s);
+
+// Work item of the key-parallel dK/dV kernel: one key tile of one region of one kv
+// head, against the query rows of sequences [seq_lo, seq_hi).
+enum { kRegionCtx = 0, kRegionOwn = 1 };
+struct KVItem {
+  int32_t g;
+  int32_t region;     // kRegionCtx: keys of the shared prompt; kRegionOwn: of seq_lo
+  int32_t key_start;  // first key of the tile within its region
+  int32_t seq_lo, seq_hi;
+  int32_t pad[3];
+};
+
+struct BwdKVArgs {
+  const void *q, *dout, *k_ctx, *v_ctx, *k_own, *v_own;
+  const float *lse, *D;
+  const int32_t *cu;           // device prefix sums of the query sequences
+  void *dk_own, *dv_own;       // direct outputs of own-region keys
+  float *acc_dk, *acc_dv;      // fp32 accumulators: ctx-region keys, and own keys if own_to_acc
+  const KVItem *items;
+  int Hq, Hkv, G, ctx_len, window_left, lse_ld;
+  int own_to_acc;
+  float scale;
+};
+hipError_t launch_bwd_dkdv(int dtype, int head_dim, const BwdKVArgs &a, int n_items,
+                           hipStream_t s);
+
+}  // namespace dkv

@@ -1,0 +1,86 @@
+"""The C ABI library loads, exports every function include/dkv.h declares, and
+rejects invalid arguments on the host (no GPU needed: validation runs before any
+HIP call)."""
+import ctypes
+
+import pytest
+
+from shared_prompt_exact_dkv_amd import _lib as L
+
+
+def test_exports_every_header_function():
+    names = L.header_functions()
+    assert {"dkv_ctx_fwd", "dkv_fwd", "dkv_ctx_bwd", "dkv_bwd", "dkv_cast_acc",
+            "dkv_workspace_size", "dkv_last_error"} <= set(names)
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert b"gfx950" in lib.dkv_version()
+
+
+def _params(**kw):
+    base = dict(num_seqs=2, ctx_len=16, num_heads_q=8, num_heads_kv=2, head_dim=128,
+                window_left=-1, softmax_scale=0.0, dtype=L.DKV_BF16, cu_host=[0, 5, 9],
+                cu_dev=0x1000)
+    base.update(kw)
+    return L.make_params(**base)
+
+
+FAKE = 0x10000   # 16-byte aligned, never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("kw,status,frag", [
+    (dict(num_heads_q=6, num_heads_kv=4), L.DKV_ERR_INVALID_ARG, "multiple"),
+    (dict(head_dim=96), L.DKV_ERR_INVALID_ARG, "head_dim"),
+    (dict(window_left=-2), L.DKV_ERR_INVALID_ARG, "window_left"),
+    (dict(cu_host=[1, 5, 9]), L.DKV_ERR_INVALID_ARG, "cu_seqlens[0]"),
+    (dict(cu_host=[0, 5, 4]), L.DKV_ERR_INVALID_ARG, "decreases"),
+    (dict(dtype=7), L.DKV_ERR_INVALID_ARG, "dtype"),
+    (dict(ctx_len=-1), L.DKV_ERR_INVALID_ARG, "ctx_len"),
+    (dict(cu_dev=0), L.DKV_ERR_INVALID_ARG, "cu_seqlens_dev"),
+    (dict(softmax_scale=float("nan")), L.DKV_ERR_INVALID_ARG, "scale"),
+])
+def test_fwd_rejects_invalid_params(kw, status, frag):
+    p, keep = _params(**kw)
+    lib = L.lib()
+    st = lib.dkv_fwd(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None)
+    assert st == status
+    assert frag in L.last_error()
+
+
+def test_ctx_calls_require_zero_ctx_len():
+    p, keep = _params(ctx_len=4)
+    st = L.lib().dkv_ctx_fwd(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None)
+    assert st == L.DKV_ERR_INVALID_ARG and "ctx_len" in L.last_error()
+
+
+def test_null_and_misaligned_pointers():
+    p, keep = _params()
+    lib = L.lib()
+    st = lib.dkv_fwd(p, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None)
+    assert st == L.DKV_ERR_INVALID_ARG and "q_resp" in L.last_error()
+    st = lib.dkv_fwd(p, FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None)
+    assert st == L.DKV_ERR_INVALID_ARG and "aligned" in L.last_error()
+
+
+def test_workspace_checks():
+    p, keep = _params()
+    lib = L.lib()
+    need = lib.dkv_workspace_size(p, L.DKV_CALL_FWD)
+    assert 0 < need < (1 << 20)
+    st = lib.dkv_fwd(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None)
+    assert st == L.DKV_ERR_WORKSPACE
+    st = lib.dkv_fwd(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16, need, None)
+    assert st == L.DKV_ERR_WORKSPACE and "aligned" in L.last_error()
+    st = lib.dkv_fwd(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None)
+    assert st == L.DKV_ERR_WORKSPACE
+    bad, keep2 = _params(head_dim=3)
+    assert lib.dkv_workspace_size(bad, L.DKV_CALL_FWD) == ctypes.c_size_t(-1).value
+    assert lib.dkv_workspace_size(p, 99) == ctypes.c_size_t(-1).value
+
+
+def test_empty_batch_is_a_no_op():
+    p, keep = _params(cu_host=[0, 0, 0], cu_dev=0)
+    lib = L.lib()
+    assert lib.dkv_workspace_size(p, L.DKV_CALL_FWD) == 0
+    assert lib.dkv_fwd(p, None, None, None, None, None, None, None, None, 0, None) == L.DKV_OK

@@ -1,0 +1,132 @@
+"""GPU parity of the backward against the CPU oracle.
+
+The oracle runs the N-copy packing (eq. (2)) where each copy's prompt rows get their
+own upstream gradient dO_P^(i); the GPU sees the single prompt copy with their sum
+(Appendix A.5), and sums the shared prompt's K/V gradient over both calls and all N
+responses in one fp32 accumulator (eq. (6)), cast once.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import shared_prompt_exact_dkv_amd as dkv
+from tests._gpu import DEV, check, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dq_p", "dk_p", "dv_p", "dq_r", "dk_r", "dv_r")
+
+CASES = [
+    # P, lens, Hq, Hkv, d, window_left, dtype, scaled
+    (64, [32, 32, 32, 32], 2, 2, 64, -1, "fp32", False),        # the tiny workload
+    (100, [37, 0, 1, 130], 4, 1, 64, -1, "fp32", False),
+    (70, [65, 3], 8, 2, 128, -1, "fp32", False),
+    (150, [100, 60], 8, 1, 128, 127, "fp32", False),
+    (130, [77, 64, 129], 8, 2, 128, -1, "bf16", True),
+    (130, [77, 64, 129], 8, 2, 128, -1, "bf16", False),
+    (0, [50, 90], 4, 4, 64, -1, "bf16", False),
+    (33, [200], 32, 8, 128, -1, "bf16", False),
+    (191, [45, 150, 7], 16, 2, 64, 40, "bf16", False),
+    (97, [120, 33], 4, 2, 128, 0, "bf16", False),
+    (300, [140, 260, 1], 8, 2, 128, 200, "bf16", False),
+    (5, [3, 2, 1], 1, 1, 64, -1, "bf16", False),
+]
+
+
+def _run(P, lens, Hq, Hkv, d, wl, dtype, scaled, seed):
+    x = workloads.make_inputs(P, lens, Hq, Hkv, d, dtype, seed=seed, scaled=scaled)
+    N = len(lens)
+    do_copies = workloads.split_prompt_grad(x["do_p"], N, seed=seed)
+    ref = oracle.ncopy_reference(x, do_copies=do_copies, window_left=wl)
+    t = to_dev(x, dtype)
+    o_p, lse_p, o_r, lse_r = dkv.dualkv_forward(t["q_p"], t["k_p"], t["v_p"], t["q_r"],
+                                                t["k_r"], t["v_r"], t["cu"],
+                                                cu_host=t["cu_host"], window_left=wl)
+    g = dkv.dualkv_backward(t["q_p"], t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], o_p,
+                            lse_p, o_r, lse_r, t["do_p"], t["do_r"], t["cu"],
+                            cu_host=t["cu_host"], window_left=wl)
+    torch.cuda.synchronize()
+    return x, t, ref, g, (o_p, lse_p, o_r, lse_r)
+
+
+@pytest.mark.parametrize("P,lens,Hq,Hkv,d,wl,dtype,scaled", CASES)
+def test_dualkv_backward_matches_oracle(P, lens, Hq, Hkv, d, wl, dtype, scaled):
+    x, t, ref, g, fwd = _run(P, lens, Hq, Hkv, d, wl, dtype, scaled, seed=P + 3 * len(lens))
+    for k in GRADS:
+        if g[k] is None:
+            assert ref[k].size == 0, k
+            continue
+        check(k, g[k], ref[k], dtype)
+
+
+def test_accumulator_order_is_free():
+    # Call 2 first (clearing) then Call 1 (finalizing) gives the same dK_P / dV_P.
+    P, lens, Hq, Hkv, d, dtype = 96, [50, 70, 20], 8, 2, 128, "bf16"
+    x, t, ref, g, (o_p, lse_p, o_r, lse_r) = _run(P, lens, Hq, Hkv, d, -1, dtype, False, 4)
+    acc = torch.empty((2, P, Hkv, d), dtype=torch.float32, device=DEV)
+    dkv.dkv_bwd(t["q_r"], t["k_p"], t["v_p"], t["k_r"], t["v_r"], o_r, lse_r, t["do_r"],
+                t["cu"], acc_dk_p=acc[0], acc_dv_p=acc[1], acc_flags=dkv.DKV_ACC_ZERO,
+                cu_host=t["cu_host"])
+    cu_p = torch.tensor([0, P], dtype=torch.int32, device=DEV)
+    _, dk_p, dv_p = dkv.dkv_ctx_bwd(t["q_p"], t["k_p"], t["v_p"], o_p, lse_p, t["do_p"], cu_p,
+                                    cu_host=[0, P], acc_dk=acc[0], acc_dv=acc[1],
+                                    acc_flags=dkv.DKV_ACC_FINALIZE)
+    torch.cuda.synchronize()
+    check("dk_p", dk_p, ref["dk_p"], dtype)
+    check("dv_p", dv_p, ref["dv_p"], dtype)
+    # both orders agree to fp32 reassociation before the single bf16 cast
+    assert (dk_p.float() - g["dk_p"].float()).abs().max().item() <= \
+        2e-2 * g["dk_p"].float().abs().max().item()
+
+
+@pytest.mark.parametrize("dtype,d", [("fp32", 64), ("bf16", 128)])
+def test_ncopy_backward_through_causal_kernel(dtype, d):
+    # The N-copy packing of eq. (1) through dkv_ctx_bwd with direct dK/dV writes: each
+    # copy's gradients must match that copy's oracle gradients.
+    P, lens, Hq, Hkv = 70, [40, 0, 95], 8, 2
+    x = workloads.make_inputs(P, lens, Hq, Hkv, d, dtype, seed=9)
+    N = len(lens)
+    do_copies = workloads.split_prompt_grad(x["do_p"], N, seed=9)
+    ref = oracle.ncopy_reference(x, do_copies=do_copies, keep_copies=True)
+    qs, ks, vs, dos, cu = [], [], [], [], [0]
+    for i in range(N):
+        q, k, v = oracle.copy_of(x, i)
+        a, b = int(x["cu"][i]), int(x["cu"][i + 1])
+        qs.append(q), ks.append(k), vs.append(v)
+        dos.append(np.concatenate([do_copies[i].numpy(), x["do_r"][a:b].numpy()]))
+        cu.append(cu[-1] + q.shape[0])
+    f = lambda z: torch.from_numpy(np.concatenate(z)).to(torch.float32)
+    dd = to_dev({"q": f(qs), "k": f(ks), "v": f(vs), "do": f(dos),
+                 "cu": torch.tensor(cu, dtype=torch.int32)}, dtype)
+    o, lse = dkv.dkv_ctx_fwd(dd["q"], dd["k"], dd["v"], dd["cu"], cu_host=dd["cu_host"])
+    dq, dk, dv = dkv.dkv_ctx_bwd(dd["q"], dd["k"], dd["v"], o, lse, dd["do"], dd["cu"],
+                                 cu_host=dd["cu_host"])
+    torch.cuda.synchronize()
+    for i in range(N):
+        c = ref["copies"][i]
+        a, b = cu[i], cu[i + 1]
+        bound = None
+        if dtype == "bf16":
+            # per-copy do_p^(i) is not bf16-representable; its bf16 rounding is an input
+            # perturbation of ~2^-9 relative, well inside the tolerance used here
+            bound = None
+        check("dq copy %d" % i, dq[a:b], c["dq"], dtype, bound)
+        check("dk copy %d" % i, dk[a:b], c["dk"], dtype, bound)
+        check("dv copy %d" % i, dv[a:b], c["dv"], dtype, bound)
+
+
+def test_repeated_backward_consistent():
+    # fp32 atomics may reorder the shared-prompt sums; every run must stay within the
+    # tolerance of the oracle and of each other.
+    P, lens, Hq, Hkv, d = 200, [64] * 8, 8, 2, 64
+    x, t, ref, g, fwd = _run(P, lens, Hq, Hkv, d, -1, "fp32", False, 21)
+    o_p, lse_p, o_r, lse_r = fwd
+    for _ in range(3):
+        g2 = dkv.dualkv_backward(t["q_p"], t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"],
+                                 o_p, lse_p, o_r, lse_r, t["do_p"], t["do_r"], t["cu"],
+                                 cu_host=t["cu_host"])
+        torch.cuda.synchronize()
+        for k in GRADS:
+            check(k, g2[k], ref[k], "fp32")

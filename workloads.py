@@ -77,37 +77,43 @@ def cu_seqlens(lens) -> torch.Tensor:
     return torch.tensor(cu, dtype=torch.int32)
 
 
-def _draw(g: torch.Generator, shape, dtype: str, scale: float) -> torch.Tensor:
-    """fp32 tensor whose values are exactly representable in ``dtype``."""
-    x = torch.randn(shape, generator=g, dtype=torch.float32) * scale
+def _draw(g: torch.Generator, shape, dtype: str, scale: float, keep: bool = False) -> torch.Tensor:
+    """Values exactly representable in ``dtype``: fp32 tensors, or (``keep``) tensors
+    already in ``dtype``."""
+    x = torch.randn(shape, generator=g, dtype=torch.float32, device=g.device) * scale
     if dtype == "bf16":
-        x = x.to(torch.bfloat16).to(torch.float32)
+        x = x.to(torch.bfloat16)
+        if not keep:
+            x = x.to(torch.float32)
     return x
 
 
 def make_inputs(P: int, lens, Hq: int, Hkv: int, d: int, dtype: str = "fp32",
-                seed: int = 0, scaled: bool = False, dout: bool = True) -> dict:
-    """Single-prompt packed inputs (fp32 tensors holding ``dtype``-exact values).
+                seed: int = 0, scaled: bool = False, dout: bool = True,
+                device: str = "cpu") -> dict:
+    """Single-prompt packed inputs (fp32 tensors holding ``dtype``-exact values; on a
+    non-CPU ``device`` the tensors are drawn there and kept in ``dtype``).
 
     Returns q_p [P,Hq,d], k_p/v_p [P,Hkv,d], q_r [T,Hq,d], k_r/v_r [T,Hkv,d],
     do_p [P,Hq,d] (the prompt-row upstream gradient seen by the single prompt
     copy), do_r [T,Hq,d] and cu (int32 [N+1]).
     """
-    g = torch.Generator().manual_seed(seed)
+    g = torch.Generator(device=device).manual_seed(seed)
+    keep = device != "cpu"
     T = int(sum(lens))
     s = 1.0 / math.sqrt(d) if scaled else 1.0
     out = {
-        "q_p": _draw(g, (P, Hq, d), dtype, s),
-        "k_p": _draw(g, (P, Hkv, d), dtype, s),
-        "v_p": _draw(g, (P, Hkv, d), dtype, s),
-        "q_r": _draw(g, (T, Hq, d), dtype, s),
-        "k_r": _draw(g, (T, Hkv, d), dtype, s),
-        "v_r": _draw(g, (T, Hkv, d), dtype, s),
+        "q_p": _draw(g, (P, Hq, d), dtype, s, keep),
+        "k_p": _draw(g, (P, Hkv, d), dtype, s, keep),
+        "v_p": _draw(g, (P, Hkv, d), dtype, s, keep),
+        "q_r": _draw(g, (T, Hq, d), dtype, s, keep),
+        "k_r": _draw(g, (T, Hkv, d), dtype, s, keep),
+        "v_r": _draw(g, (T, Hkv, d), dtype, s, keep),
         "cu": cu_seqlens(lens),
     }
     if dout:
-        out["do_p"] = _draw(g, (P, Hq, d), dtype, 1.0)
-        out["do_r"] = _draw(g, (T, Hq, d), dtype, 1.0)
+        out["do_p"] = _draw(g, (P, Hq, d), dtype, 1.0, keep)
+        out["do_r"] = _draw(g, (T, Hq, d), dtype, 1.0, keep)
     return out
 
 
@@ -130,9 +136,9 @@ def split_prompt_grad(do_p: torch.Tensor, N: int, seed: int) -> torch.Tensor:
     return parts
 
 
-def workload_inputs(w: Workload, dout: bool = True) -> dict:
+def workload_inputs(w: Workload, dout: bool = True, device: str = "cpu") -> dict:
     lens = w.resp_lens()
     x = make_inputs(w.P, lens, w.Hq, w.Hkv, w.d, w.dtype, seed=w.seed, scaled=w.scaled,
-                    dout=dout)
+                    dout=dout, device=device)
     x["lens"] = lens
     return x
