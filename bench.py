@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-ncopy", action="store_true", help="skip the N-copy comparator")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (torch), the reference "
+                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     return ap.parse_args()
 
 
@@ -252,6 +255,17 @@ def main():
                          "kv-head groups (%d q-heads); %.1f s, extrapolated by visible-pair "
                          "count to the full N-copy workload (%.0f s)" % (S0, Hkv, G, cpu_s, full_s)}
         log(args, "cpu oracle sample %.2f s" % cpu_s)
+
+    if args.copy_calibration:
+        # A plain copy of known size: 1 GiB read, 1 GiB written.  Under rocprofv3 --pmc
+        # its FETCH_SIZE / WRITE_SIZE readings give the counters' scale factor.
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(args, "copy calibration: %d bytes read, %d bytes written" % (4 << 28, 4 << 28))
+        del src, dst
 
     speedup = (ncopy_ms / ms) if ncopy_ms else None
     out = {

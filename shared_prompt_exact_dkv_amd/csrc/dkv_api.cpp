@@ -109,11 +109,40 @@ dkv_status check_ptr(const void *ptr, const char *name, bool needed) {
 
 // ---------------------------------------------------------------- scheduling --
 //
-// Query-parallel work items (forward, dQ): one per (kv head, sequence, query tile).
-// Items are ordered longest-first (the visible key range grows with the tile index
-// under the causal mask) and, within a work level, interleaved over kv heads so that
-// workgroup b -- which the dispatcher places on XCD b % 8 -- keeps one kv head per
-// XCD where Hkv divides 8, letting that XCD's L2 hold the head's K_P/V_P.
+// MI355X dispatches workgroup b of a launch to XCD b % 8, and each XCD has its own
+// L2.  The work lists are therefore built per XCD and interleaved: XCD x serves the
+// kv heads g with g % 8 == x (a head with fewer than 8 heads in total is spread over
+// 8 / Hkv XCDs, by sequence).  On each XCD the items of one (kv head, sequence)
+// group run together, so that the group's keys and values (forward, dQ) or query
+// rows (dK/dV) are fetched from HBM once and re-read from L2.  Groups are taken
+// longest first and, inside a group, items longest first (the visible key range of
+// a query tile grows with its index under the causal mask), so the end of the grid
+// fills with short items.
+
+constexpr int kXcds = 8;
+
+// The XCD that serves part `part` (a sequence group, or a tile) of kv head g: a head
+// owns XCDs g, g + Hkv, ... when Hkv divides 8, else XCD g % 8.
+struct HeadXcds {
+  int Hkv, span;
+  explicit HeadXcds(int hkv) : Hkv(hkv), span((hkv < kXcds && kXcds % hkv == 0) ? kXcds / hkv : 1) {}
+  int xcd(int g, int part) const { return (g + (part % span) * Hkv) % kXcds; }
+};
+
+template <typename Item>
+std::vector<Item> interleave_xcds(std::vector<std::vector<Item>> &lists) {
+  size_t total = 0, longest = 0;
+  for (auto &l : lists) {
+    total += l.size();
+    longest = std::max(longest, l.size());
+  }
+  std::vector<Item> out;
+  out.reserve(total);
+  for (size_t k = 0; k < longest; ++k)
+    for (auto &l : lists)
+      if (k < l.size()) out.push_back(l[k]);
+  return out;
+}
 
 long q_item_work(const Shape &s, int tile, int seqlen, int BN) {
   long t0 = (long)tile * s.bm_tok;
@@ -125,21 +154,37 @@ long q_item_work(const Shape &s, int tile, int seqlen, int BN) {
 }
 
 std::vector<QItem> build_q_items(const Shape &s, int BN) {
-  struct Rec { long work; int seq, tile; };
-  std::vector<Rec> recs;
+  struct Rec { long work; int tile; };
+  struct Group { long work; int seq; std::vector<Rec> recs; };
+  std::vector<Group> groups;
   for (int i = 0; i < s.N; ++i) {
     int len = s.cu[i + 1] - s.cu[i];
     int nt = (len + s.bm_tok - 1) / s.bm_tok;
-    for (int m = 0; m < nt; ++m) recs.push_back({q_item_work(s, m, len, BN), i, m});
+    if (nt == 0) continue;
+    Group gr{0, i, {}};
+    for (int m = 0; m < nt; ++m) {
+      long w = q_item_work(s, m, len, BN);
+      gr.recs.push_back({w, m});
+      gr.work += w;
+    }
+    std::stable_sort(gr.recs.begin(), gr.recs.end(),
+                     [](const Rec &a, const Rec &b) { return a.work > b.work; });
+    groups.push_back(std::move(gr));
   }
-  std::stable_sort(recs.begin(), recs.end(),
-                   [](const Rec &a, const Rec &b) { return a.work > b.work; });
-  std::vector<QItem> items;
-  items.reserve(recs.size() * s.Hkv);
-  for (const Rec &r : recs)
+  std::stable_sort(groups.begin(), groups.end(),
+                   [](const Group &a, const Group &b) { return a.work > b.work; });
+  HeadXcds hx(s.Hkv);
+  std::vector<std::vector<QItem>> lists(kXcds);
+  // One sequence alone (Call 1) is spread over a head's XCDs tile by tile.
+  const bool by_tile = groups.size() < (size_t)hx.span;
+  for (size_t gi = 0; gi < groups.size(); ++gi) {
+    const Group &gr = groups[gi];
+    const int start = s.cu[gr.seq], len = s.cu[gr.seq + 1] - start;
     for (int g = 0; g < s.Hkv; ++g)
-      items.push_back({g, r.tile, s.cu[r.seq], s.cu[r.seq + 1] - s.cu[r.seq]});
-  return items;
+      for (size_t r = 0; r < gr.recs.size(); ++r)
+        lists[hx.xcd(g, (int)(by_tile ? r : gi))].push_back({g, gr.recs[r].tile, start, len});
+  }
+  return interleave_xcds(lists);
 }
 
 // ----------------------------------------------------- pinned staging of lists --
@@ -338,34 +383,50 @@ long kv_rows_visible(const Shape &s, bool ctx, int key_start, int nk, int len) {
 }
 
 std::vector<KVItem> build_kv_items(const Shape &s, bool with_ctx) {
+  // One group per (chunk of sequences): the prompt key tiles that add this chunk's
+  // terms to the shared accumulator, and the chunk's own response key tiles.  All of
+  // them stream the chunk's query rows.
   struct Rec { long work; int region, key_start, lo, hi; };
-  std::vector<Rec> recs;
-  for (int i = 0; i < s.N; ++i) {
-    int len = s.cu[i + 1] - s.cu[i];
-    for (int k0 = 0; k0 < len; k0 += kBwdBN) {
-      int nk = std::min(kBwdBN, len - k0);
-      recs.push_back({kv_rows_visible(s, false, k0, nk, len), kRegionOwn, k0, i, i + 1});
-    }
-  }
-  if (with_ctx && s.P > 0 && s.N > 0) {
-    int cs = ctx_chunk(s);
-    for (int k0 = 0; k0 < s.P; k0 += kBwdBN) {
-      int nk = std::min(kBwdBN, s.P - k0);
-      for (int lo = 0; lo < s.N; lo += cs) {
-        int hi = std::min(s.N, lo + cs);
+  struct Group { long work; std::vector<Rec> recs; };
+  const int cs = (with_ctx && s.P > 0) ? ctx_chunk(s) : 1;
+  std::vector<Group> groups;
+  for (int lo = 0; lo < s.N; lo += cs) {
+    const int hi = std::min(s.N, lo + cs);
+    Group gr{0, {}};
+    if (with_ctx && s.P > 0) {
+      for (int k0 = 0; k0 < s.P; k0 += kBwdBN) {
+        int nk = std::min(kBwdBN, s.P - k0);
         long w = 0;
         for (int i = lo; i < hi; ++i) w += kv_rows_visible(s, true, k0, nk, s.cu[i + 1] - s.cu[i]);
-        if (w > 0) recs.push_back({w, kRegionCtx, k0, lo, hi});
+        if (w > 0) gr.recs.push_back({w, kRegionCtx, k0, lo, hi});
       }
     }
+    for (int i = lo; i < hi; ++i) {
+      int len = s.cu[i + 1] - s.cu[i];
+      for (int k0 = 0; k0 < len; k0 += kBwdBN) {
+        int nk = std::min(kBwdBN, len - k0);
+        gr.recs.push_back({kv_rows_visible(s, false, k0, nk, len), kRegionOwn, k0, i, i + 1});
+      }
+    }
+    if (gr.recs.empty()) continue;
+    for (const Rec &r : gr.recs) gr.work += r.work;
+    std::stable_sort(gr.recs.begin(), gr.recs.end(),
+                     [](const Rec &a, const Rec &b) { return a.work > b.work; });
+    groups.push_back(std::move(gr));
   }
-  std::stable_sort(recs.begin(), recs.end(),
-                   [](const Rec &a, const Rec &b) { return a.work > b.work; });
-  std::vector<KVItem> items;
-  items.reserve(recs.size() * s.Hkv);
-  for (const Rec &r : recs)
-    for (int g = 0; g < s.Hkv; ++g) items.push_back({g, r.region, r.key_start, r.lo, r.hi, {0, 0, 0}});
-  return items;
+  std::stable_sort(groups.begin(), groups.end(),
+                   [](const Group &a, const Group &b) { return a.work > b.work; });
+  HeadXcds hx(s.Hkv);
+  std::vector<std::vector<KVItem>> lists(kXcds);
+  const bool by_tile = groups.size() < (size_t)hx.span;
+  for (size_t gi = 0; gi < groups.size(); ++gi)
+    for (int g = 0; g < s.Hkv; ++g)
+      for (size_t r = 0; r < groups[gi].recs.size(); ++r) {
+        const Rec &x = groups[gi].recs[r];
+        lists[hx.xcd(g, (int)(by_tile ? r : gi))].push_back(
+            {g, x.region, x.key_start, x.lo, x.hi, {0, 0, 0}});
+      }
+  return interleave_xcds(lists);
 }
 
 struct BwdPlan {

@@ -261,9 +261,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdQArgs a) {
 template <typename T, int HD> struct QStepRegs : RowRegs<T, HD, kBwdBM> {
   using C = TileCfg<T, HD, kBwdBM>;
   // base: row 0 of the sequence, first q-head of the group; rows f0 .. f0+31 of the
-  // flattened (token, head) index, valid below fend.
-  __device__ __forceinline__ void load_flat(const T *base, long qld, int G, int f0, int fend,
-                                            int tid) {
+  // flattened (token, head) index, loaded where flo <= row < fend (else zero).
+  __device__ __forceinline__ void load_flat(const T *base, long qld, int G, int f0, int flo,
+                                            int fend, int tid) {
     constexpr int per_row = (sizeof(T) == 2) ? HD / 8 : HD / 4;
 #pragma unroll
     for (int p = 0; p < C::kRowPasses; ++p) {
@@ -271,7 +271,7 @@ template <typename T, int HD> struct QStepRegs : RowRegs<T, HD, kBwdBM> {
       int row = id / per_row, ch = id % per_row;
       int f = f0 + row;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (id < C::kChunks && f < fend) {
+      if (id < C::kChunks && f >= flo && f < fend) {
         int t = f / G, j = f - t * G;
         v = *reinterpret_cast<const uint4 *>(base + (long)t * qld + (long)j * HD +
                                              ch * (16 / sizeof(T)));
@@ -362,19 +362,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
     fb = r_hi > r_lo ? r_hi * G : fa;
   };
 
-  // Cursor over (sequence, 32-row step).
-  int cs = it.seq_lo, cf = 0, cfe = 0;
+  // Cursor over (sequence, 32-row step), walked from the last visible row of the
+  // last sequence backward.  Steps sit on multiples of 32 flattened rows, so every
+  // key tile of one sequence starts on the same block: the workgroups that share a
+  // sequence stream the same query rows at the same time and hit in L2.
+  int cs = it.seq_hi - 1, cf = 0, cfa = 0, cfb = 0;
   bool done = false;
-  auto seek = [&]() {   // from sequence cs onward, find a non-empty range
-    while (cs < it.seq_hi) {
+  auto seek = [&]() {   // from sequence cs downward, find a non-empty range
+    while (cs >= it.seq_lo) {
       int fa, fb;
       seq_range(cs, fa, fb);
       if (fb > fa) {
-        cf = fa;
-        cfe = fb;
+        cfa = fa;
+        cfb = fb;
+        cf = ((fb - 1) / BM) * BM;
         return;
       }
-      ++cs;
+      --cs;
     }
     done = true;
   };
@@ -384,13 +388,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
   float lse_r = INFINITY, d_r = 0.f;
   auto issue = [&]() {
     const int s0 = a.cu[cs];
+    const int lo = max(cf, cfa), hi = min(cf + BM, cfb);
     const T *qb = reinterpret_cast<const T *>(a.q) + (long)s0 * qld + (long)g * G * HD;
     const T *db_ = reinterpret_cast<const T *>(a.dout) + (long)s0 * qld + (long)g * G * HD;
-    qregs.load_flat(qb, qld, G, cf, cfe, tid);
-    dregs.load_flat(db_, qld, G, cf, cfe, tid);
+    qregs.load_flat(qb, qld, G, cf, lo, hi, tid);
+    dregs.load_flat(db_, qld, G, cf, lo, hi, tid);
     if (tid < BM) {
       int f = cf + tid;
-      if (f < cfe) {
+      if (f >= lo && f < hi) {
         int t = f / G, j = f - t * G;
         long idx = (long)(g * G + j) * a.lse_ld + s0 + t;
         lse_r = SM::lse_in(a.lse[idx]);
@@ -404,7 +409,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
   if (!done) issue();
 
   while (!done) {
-    const int s_cur = cs, f0 = cf, fend = cfe;
+    const int f0 = cf, flo = max(cf, cfa), fend = min(cf + BM, cfb);
     __syncthreads();
     qregs.store(qs, tid);
     dregs.store(dos, tid);
@@ -413,9 +418,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
       d_s[tid] = d_r;
     }
     __syncthreads();
-    cf += BM;
-    if (cf >= cfe) {
-      ++cs;
+    cf -= BM;
+    if (cf + BM <= cfa) {
+      --cs;
       seek();
     }
     if (!done) issue();
@@ -428,12 +433,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
         s = mfma(row_frag<T, HD, BM>(qs, col, kc, half), kf[kc], s);
         dp = mfma(row_frag<T, HD, BM>(dos, col, kc, half), vf[kc], dp);
       }
-      const int ta = f0 / G;
-      const int tb = (min(f0 + BM, fend) - 1) / G;
+      const int ta = flo / G;
+      const int tb = (fend - 1) / G;
       const int qpa = P + ta, qpb = P + tb;
       const int kpa = kbase + it.key_start + kw0;
       const int kpb = kbase + it.key_start + min(kw0 + 32, nkeys) - 1;
-      const bool full = (f0 + BM <= fend) && (kw0 + 32 <= nkeys) && (kpb <= qpa) &&
+      const bool full = (flo == f0) && (f0 + BM <= fend) && (kw0 + 32 <= nkeys) && (kpb <= qpa) &&
                         (wl < 0 || kpa >= qpb - wl);
       const int kpos = kbase + it.key_start + key;
 #pragma unroll
@@ -449,7 +454,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
           if (!full) {
             int f = f0 + c_row(v, half);
             int qp = P + f / G;
-            bool vis = (f < fend) && key_valid && (kpos <= qp) && (wl < 0 || kpos >= qp - wl);
+            bool vis = (f >= flo) && (f < fend) && key_valid && (kpos <= qp) &&
+                       (wl < 0 || kpos >= qp - wl);
             if (!vis) p = 0.f;
           }
           s[v] = p;                          // P
@@ -492,7 +498,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
         }
       }
     }
-    (void)s_cur;
   }
 
   // Epilogue: lane holds dims db*32 + col of keys kw0 + c_row(v, half).
