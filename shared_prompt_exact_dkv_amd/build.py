@@ -2,7 +2,10 @@
 
 Every HIP source is compiled with the packed-fp32 target feature turned off; the
 host-only translation unit gets the same flags (hipcc's host pass ignores the
-feature with a warning).  Objects go to _build/ at the repository root, the shared
+feature with a warning).  MFMA results are kept in architectural VGPRs
+(-amdgpu-mfma-vgpr-form): the softmax and the scaling work on the score tiles with
+VALU instructions, which cannot read accumulation registers, so accumulators placed
+there would be copied out and back on every tile.  Objects go to _build/ at the repository root, the shared
 library next to this file.
 """
 from __future__ import annotations
@@ -22,6 +25,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["dkv_api.cpp", "dkv_fwd.hip", "dkv_bwd.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I", os.path.join(ROOT, "include")]
 
 

@@ -255,6 +255,152 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdQArgs a) {
   }
 }
 
+// bf16 dQ kernel with two waves per SIMD: K and V tiles double-buffered in LDS
+// through buffer loads (one barrier per 64-key tile), each tile taken as two 32-key
+// halves so that Sᵀ, dPᵀ and dSᵀ of one half are live at a time.
+template <int HD>
+__global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
+  constexpr int BN = kFwdBN;
+  using TC = TileCfg<bf16, HD, BN>;
+  constexpr int TILE = TC::kRowBytes;
+  constexpr int NKC = HD / 16;
+  constexpr int NDB = HD / 32;
+  __shared__ __attribute__((aligned(16))) char smem[2][2 * TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const QItem it = a.items[blockIdx.x];
+  const int g = it.g, seq0 = it.seq_start, seqlen = it.seq_len;
+  const int t0 = it.tile * a.bm_tok;
+  const int nt = min(a.bm_tok, seqlen - t0);
+  const int qr = wave * 32 + col;
+  int tok = qr / a.G;
+  const int hj = qr - tok * a.G;
+  const bool row_valid = tok < nt;
+  if (!row_valid) tok = nt - 1;
+  const int h = g * a.G + hj;
+  const int P = a.ctx_len, wl = a.window_left;
+  const int qpos = P + t0 + tok;
+  const int qmin = P + t0, qmax = P + t0 + nt - 1;
+  const long qld = (long)a.Hq * HD;
+  const long kld = (long)a.Hkv * HD;
+  const long qrow = (long)(seq0 + t0 + tok);
+
+  const bf16 *qptr = reinterpret_cast<const bf16 *>(a.q) + qrow * qld + (long)h * HD;
+  const bf16 *dptr = reinterpret_cast<const bf16 *>(a.dout) + qrow * qld + (long)h * HD;
+  bf16x8 qf[NKC], df[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    qf[kc] = as_bf16x8(*reinterpret_cast<const uint4 *>(qptr + kc * 16 + half * 8));
+    df[kc] = as_bf16x8(*reinterpret_cast<const uint4 *>(dptr + kc * 16 + half * 8));
+  }
+  const float sf = a.scale * kLog2e;
+  const float lse2 = a.lse[(long)h * a.lse_ld + qrow] * kLog2e;
+  const float Dq = a.D[(long)h * a.lse_ld + qrow];
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = zero16();
+
+  const int ctx_lo = (wl >= 0) ? max(0, qmin - wl) : 0;
+  const int ctx_t0 = (ctx_lo / BN) * BN;
+  const int n_ctx = (P > ctx_lo) ? (P - ctx_t0 + BN - 1) / BN : 0;
+  const int own_lo = (wl >= 0) ? max(0, t0 - wl) : 0;
+  const int own_t0 = (own_lo / BN) * BN;
+  const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
+  const int n_tiles = n_ctx + n_own;
+
+  const bf16 *kc_base = reinterpret_cast<const bf16 *>(a.k_ctx) + (long)g * HD;
+  const bf16 *vc_base = reinterpret_cast<const bf16 *>(a.v_ctx) + (long)g * HD;
+  const bf16 *ko_base = reinterpret_cast<const bf16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
+  const bf16 *vo_base = reinterpret_cast<const bf16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
+  const int kld_b = (int)(kld * 2);
+  BufRows<HD, BN> kregs, vregs;
+  auto issue = [&](int i) {
+    if (i < n_ctx) {
+      int s = ctx_t0 + i * BN;
+      kregs.load(kc_base + (long)s * kld, kld_b, P - s, tid);
+      vregs.load(vc_base + (long)s * kld, kld_b, P - s, tid);
+    } else {
+      int s = own_t0 + (i - n_ctx) * BN;
+      kregs.load(ko_base + (long)s * kld, kld_b, seqlen - s, tid);
+      vregs.load(vo_base + (long)s * kld, kld_b, seqlen - s, tid);
+    }
+  };
+  if (n_tiles > 0) {
+    issue(0);
+    kregs.store(smem[0], tid);
+    vregs.store(smem[0] + TILE, tid);
+    if (n_tiles > 1) issue(1);
+  }
+
+  for (int i = 0; i < n_tiles; ++i) {
+    int nrows, kpos0;
+    if (i < n_ctx) {
+      int s = ctx_t0 + i * BN;
+      nrows = P - s;
+      kpos0 = s;
+    } else {
+      int s = own_t0 + (i - n_ctx) * BN;
+      nrows = seqlen - s;
+      kpos0 = P + s;
+    }
+    __syncthreads();
+    if (i + 1 < n_tiles) {
+      kregs.store(smem[(i + 1) & 1], tid);
+      vregs.store(smem[(i + 1) & 1] + TILE, tid);
+      if (i + 2 < n_tiles) issue(i + 2);
+    }
+    const char *ks = smem[i & 1];
+    const char *vs = smem[i & 1] + TILE;
+    const bool need_mask = (nrows < BN) || (kpos0 + BN - 1 > qmin) ||
+                           (wl >= 0 && kpos0 < qmax - wl);
+
+#pragma unroll
+    for (int hb = 0; hb < BN / 32; ++hb) {
+      f32x16 st = zero16(), dpt = zero16();
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        st = mfma(row_frag<bf16, HD, BN>(ks, hb * 32 + col, kc, half), qf[kc], st);
+        dpt = mfma(row_frag<bf16, HD, BN>(vs, hb * 32 + col, kc, half), df[kc], dpt);
+      }
+      float ds[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float p = fast_exp2(fmaf(st[v], sf, -lse2));
+        if (need_mask) {
+          int kk = hb * 32 + c_row(v, half);
+          int kp = kpos0 + kk;
+          bool vis = (kk < nrows) && (kp <= qpos) && (wl < 0 || kp >= qpos - wl);
+          if (!vis) p = 0.f;
+        }
+        ds[v] = p * (dpt[v] - Dq);
+      }
+      const bf16x8 d0 = pack8(ds), d1 = pack8(ds + 8);
+      // dQᵀ += Kᵀ dSᵀ.
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        acc[db] = mfma(tr_frag<TC::kRowStride>(ks, hb * 32, db * 32, lane), d0, acc[db]);
+        acc[db] = mfma(tr_frag<TC::kRowStride>(ks, hb * 32 + 16, db * 32, lane), d1, acc[db]);
+      }
+    }
+  }
+
+  if (row_valid) {
+    bf16 *optr = reinterpret_cast<bf16 *>(a.dq) + qrow * qld + (long)h * HD;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int dim = db * 32 + 8 * i + 4 * half;
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * i + e] * a.scale);
+        *reinterpret_cast<bf16x4 *>(optr + dim) = w;
+      }
+  }
+}
+
 // ----------------------------------------------------------------- bwd_dkdv --
 
 // Query-step rows: 32 flattened (token, head) rows of one kv head's G q-heads.
@@ -522,6 +668,275 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
     }
 }
 
+// bf16 dK/dV kernel.  A workgroup owns 128 keys of one region and kv head (32 per
+// wave: K, V fragments and the dK, dV accumulators in registers) and streams the
+// query rows that see them in 64-row steps (two 32-row blocks), from the last step
+// backward.  Q, dO, LSE and D of the next step are loaded with buffer loads while
+// the current one is computed, and double-buffered in LDS (one barrier per step).
+// The rows of a step are flattened (token, head-of-group) pairs; a thread's rows
+// within the step are fixed, so its token/head split is precomputed.
+template <int HD>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
+  constexpr int BM = 64;
+  constexpr int BNW = kBwdBN;
+  using TC = TileCfg<bf16, HD, BM>;
+  constexpr int TILE = TC::kRowBytes;
+  constexpr int NKC = HD / 16;
+  constexpr int NDB = HD / 32;
+  constexpr int kPerRow = HD / 8;
+  constexpr int kPasses = TC::kRowPasses;
+  constexpr int STAGE = 2 * TILE + 2 * BM * 4;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const KVItem it = a.items[blockIdx.x];
+  const int g = it.g, G = a.G, P = a.ctx_len, wl = a.window_left;
+  const bool ctx = it.region == kRegionCtx;
+  const long qld = (long)a.Hq * HD;
+  const long kld = (long)a.Hkv * HD;
+  const int own0 = ctx ? 0 : a.cu[it.seq_lo];
+  const int nkeys = ctx ? P - it.key_start : a.cu[it.seq_lo + 1] - own0 - it.key_start;
+  const int kbase = ctx ? 0 : P;
+  const int nk_tile = min(BNW, nkeys);
+
+  const int kw0 = 32 * wave;
+  const int key = kw0 + col;
+  const bool key_valid = key < nkeys;
+  const float sf = a.scale * kLog2e;
+  const bf16 *kp = reinterpret_cast<const bf16 *>(ctx ? a.k_ctx : a.k_own) +
+                   (long)(own0 + it.key_start + (key_valid ? key : 0)) * kld + (long)g * HD;
+  const bf16 *vp = reinterpret_cast<const bf16 *>(ctx ? a.v_ctx : a.v_own) +
+                   (long)(own0 + it.key_start + (key_valid ? key : 0)) * kld + (long)g * HD;
+  bf16x8 kf[NKC], vf[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    kf[kc] = as_bf16x8(key_valid ? *reinterpret_cast<const uint4 *>(kp + kc * 16 + half * 8) : z);
+    vf[kc] = as_bf16x8(key_valid ? *reinterpret_cast<const uint4 *>(vp + kc * 16 + half * 8) : z);
+  }
+  const bool wave_active = kw0 < nkeys;
+  // Flattened query rows f (token f / G) that see this lane's key: the causal mask
+  // (key position <= P + f / G) and the window (key position >= P + f / G - wl) as
+  // bounds on f, so the per-element test needs no division.  An invalid key sees none.
+  const int kpos = kbase + it.key_start + key;
+  const int f_vis_lo = key_valid ? max(0, (kpos - P) * G) : 0x7fffffff;
+  const int f_vis_hi = (wl >= 0) ? max(0, (kpos + wl - P + 1) * G) : 0x7fffffff;
+
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dk[db] = zero16();
+    dv[db] = zero16();
+  }
+
+  // Query rows that can see this key tile, per sequence, in flattened units.
+  auto seq_range = [&](int sq, int &fa, int &fb) {
+    int len = a.cu[sq + 1] - a.cu[sq];
+    int r_lo, r_hi;
+    if (ctx) {
+      r_lo = 0;
+      r_hi = len;
+      if (wl >= 0) r_hi = min(len, it.key_start + nk_tile - 1 + wl - P + 1);
+    } else {
+      r_lo = it.key_start;
+      r_hi = len;
+      if (wl >= 0) r_hi = min(len, it.key_start + nk_tile - 1 + wl + 1);
+    }
+    fa = r_lo * G;
+    fb = r_hi > r_lo ? r_hi * G : fa;
+  };
+  // Steps sit on multiples of BM flattened rows, walked from the last one backward.
+  int cs = it.seq_hi - 1, cf = 0, cfa = 0, cfb = 0;
+  bool done = false;
+  auto seek = [&]() {
+    while (cs >= it.seq_lo) {
+      int fa, fb;
+      seq_range(cs, fa, fb);
+      if (fb > fa) {
+        cfa = fa;
+        cfb = fb;
+        cf = ((fb - 1) / BM) * BM;
+        return;
+      }
+      --cs;
+    }
+    done = true;
+  };
+  seek();
+
+  // This thread's fixed rows of a step (for the Q / dO staging).
+  int trow[kPasses], jrow[kPasses];
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int r = (p * 256 + tid) / kPerRow;
+    trow[p] = r / G;
+    jrow[p] = r - trow[p] * G;
+  }
+  const int chb = (tid % kPerRow) * 16;          // byte offset of this thread's chunk
+  const int qld_b = (int)(qld * 2);
+  const int head0_b = g * G * HD * 2;
+  uint4 qr[kPasses], dr[kPasses];
+  float lse_r = INFINITY, d_r = 0.f;
+  auto issue = [&]() {
+    const int s0 = a.cu[cs];
+    const int len = a.cu[cs + 1] - s0;
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(reinterpret_cast<const bf16 *>(a.q) + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
+    const __amdgpu_buffer_rsrc_t rd =
+        make_rsrc(reinterpret_cast<const bf16 *>(a.dout) + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
+    const int ft = cf / G, fj = cf - ft * G;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      int t = ft + trow[p], j = fj + jrow[p];
+      if (j >= G) {
+        j -= G;
+        ++t;
+      }
+      const int off = t * qld_b + head0_b + j * (HD * 2) + chb;
+      qr[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+      dr[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0));
+    }
+    if (tid < BM) {
+      const int f = cf + tid;
+      if (f >= cfa && f < cfb) {
+        const int t = f / G, j = f - t * G;
+        const long idx = (long)(g * G + j) * a.lse_ld + s0 + t;
+        lse_r = a.lse[idx] * kLog2e;
+        d_r = a.D[idx];
+      } else {
+        lse_r = INFINITY;
+        d_r = 0.f;
+      }
+    }
+  };
+  auto stage_store = [&](char *st) {
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int r = (p * 256 + tid) / kPerRow;
+      const int lo = (r * TC::kRowStride) * 2 + chb;
+      *reinterpret_cast<uint4 *>(st + lo) = qr[p];
+      *reinterpret_cast<uint4 *>(st + TILE + lo) = dr[p];
+    }
+    if (tid < BM) {
+      reinterpret_cast<float *>(st + 2 * TILE)[tid] = lse_r;
+      reinterpret_cast<float *>(st + 2 * TILE)[BM + tid] = d_r;
+    }
+  };
+
+  // Step bounds of the staged (next) step.
+  int nf0 = 0, nflo = 0, nfend = 0;
+  auto advance = [&]() {   // record the staged step's bounds, then move the cursor on
+    nf0 = cf;
+    nflo = max(cf, cfa);
+    nfend = min(cf + BM, cfb);
+    cf -= BM;
+    if (cf + BM <= cfa) {
+      --cs;
+      seek();
+    }
+  };
+  int stage = 0;
+  bool have = !done;
+  int f0 = 0, flo = 0, fend = 0;
+  if (have) {
+    issue();
+    stage_store(smem);
+    advance();
+    f0 = nf0, flo = nflo, fend = nfend;
+    if (!done) issue();
+  }
+
+  while (have) {
+    __syncthreads();
+    const bool more = !done;
+    int g0 = 0, glo = 0, gend = 0;
+    if (more) {
+      stage_store(smem + (stage ^ 1) * STAGE);
+      advance();
+      g0 = nf0, glo = nflo, gend = nfend;
+      if (!done) issue();
+    }
+    const char *qs = smem + stage * STAGE;
+    const char *dos = qs + TILE;
+    const float *lse_s = reinterpret_cast<const float *>(qs + 2 * TILE);
+    const float *d_s = lse_s + BM;
+
+    if (wave_active) {
+      const int kpa = kbase + it.key_start + kw0;
+      const int kpb = kbase + it.key_start + min(kw0 + 32, nkeys) - 1;
+#pragma unroll
+      for (int rb = 0; rb < BM / 32; ++rb) {
+        const int b0 = f0 + rb * 32;
+        if (b0 + 32 <= flo || b0 >= fend) continue;   // block outside the step's rows
+        f32x16 st = zero16(), dpt = zero16();
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+          st = mfma(row_frag<bf16, HD, BM>(qs, rb * 32 + col, kc, half), kf[kc], st);
+          dpt = mfma(row_frag<bf16, HD, BM>(dos, rb * 32 + col, kc, half), vf[kc], dpt);
+        }
+        const int ta = max(b0, flo) / G;
+        const int tb = (min(b0 + 32, fend) - 1) / G;
+        const bool full = (b0 >= flo) && (b0 + 32 <= fend) && (kw0 + 32 <= nkeys) &&
+                          (kpb <= P + ta) && (wl < 0 || kpa >= P + tb - wl);
+        float pv[16], dsv[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 l4 = *reinterpret_cast<const float4 *>(lse_s + rb * 32 + 8 * i + 4 * half);
+          const float4 d4 = *reinterpret_cast<const float4 *>(d_s + rb * 32 + 8 * i + 4 * half);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * i + e;
+            float p = fast_exp2(fmaf(st[v], sf, -lv[e]));
+            if (!full) {
+              const int f = b0 + c_row(v, half);
+              if (f < max(flo, f_vis_lo) || f >= min(fend, f_vis_hi)) p = 0.f;
+            }
+            pv[v] = p;
+            dsv[v] = p * (dpt[v] - dd[e]);
+          }
+        }
+        const bf16x8 p0 = pack8(pv), p1 = pack8(pv + 8);
+        const bf16x8 s0 = pack8(dsv), s1 = pack8(dsv + 8);
+        // dV += Pᵀ dO and dK += dSᵀ Q over the block's 32 rows.
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          dv[db] = mfma(p0, tr_frag<TC::kRowStride>(dos, rb * 32, db * 32, lane), dv[db]);
+          dv[db] = mfma(p1, tr_frag<TC::kRowStride>(dos, rb * 32 + 16, db * 32, lane), dv[db]);
+          dk[db] = mfma(s0, tr_frag<TC::kRowStride>(qs, rb * 32, db * 32, lane), dk[db]);
+          dk[db] = mfma(s1, tr_frag<TC::kRowStride>(qs, rb * 32 + 16, db * 32, lane), dk[db]);
+        }
+      }
+    }
+    have = more;
+    f0 = g0, flo = glo, fend = gend;
+    stage ^= 1;
+  }
+
+  // Epilogue: lane holds dims db*32 + col of keys kw0 + c_row(v, half).
+  if (!wave_active) return;
+  const bool to_acc = ctx || a.own_to_acc;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int k = kw0 + c_row(v, half);
+      if (k >= nkeys) continue;
+      const long off = (long)(own0 + it.key_start + k) * kld + (long)g * HD + db * 32 + col;
+      const float gk = dk[db][v] * a.scale;
+      const float gv = dv[db][v];
+      if (to_acc) {
+        atomicAdd(a.acc_dk + off, gk);
+        atomicAdd(a.acc_dv + off, gv);
+      } else {
+        reinterpret_cast<bf16 *>(a.dk_own)[off] = (bf16)gk;
+        reinterpret_cast<bf16 *>(a.dv_own)[off] = (bf16)gv;
+      }
+    }
+}
+
 // ---------------------------------------------------------------- launchers --
 
 template <typename T, int HD>
@@ -577,8 +992,14 @@ static hipError_t dq_t(const BwdQArgs &a, int n, hipStream_t s) {
 hipError_t launch_bwd_dq(int dtype, int hd, const BwdQArgs &a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (dtype == 0) {
-    if (hd == 64) return dq_t<bf16, 64>(a, n, s);
-    if (hd == 128) return dq_t<bf16, 128>(a, n, s);
+    if (hd == 64) {
+      hipLaunchKernelGGL((bwd_dq_bf16_kernel<64>), dim3(n), dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+    if (hd == 128) {
+      hipLaunchKernelGGL((bwd_dq_bf16_kernel<128>), dim3(n), dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
   } else {
     if (hd == 64) return dq_t<float, 64>(a, n, s);
     if (hd == 128) return dq_t<float, 128>(a, n, s);
@@ -595,8 +1016,14 @@ static hipError_t dkdv_t(const BwdKVArgs &a, int n, hipStream_t s) {
 hipError_t launch_bwd_dkdv(int dtype, int hd, const BwdKVArgs &a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (dtype == 0) {
-    if (hd == 64) return dkdv_t<bf16, 64>(a, n, s);
-    if (hd == 128) return dkdv_t<bf16, 128>(a, n, s);
+    if (hd == 64) {
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<64>), dim3(n), dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+    if (hd == 128) {
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<128>), dim3(n), dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
   } else {
     if (hd == 64) return dkdv_t<float, 64>(a, n, s);
     if (hd == 128) return dkdv_t<float, 128>(a, n, s);

@@ -79,6 +79,48 @@ template <typename T, int HD, int BN> struct RowRegs {
   }
 };
 
+// A buffer resource over `bytes` bytes from `base`: buffer loads at offsets past the
+// end return zero, which fills rows beyond the end of a region without a test.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// One bf16 tile of ROWS rows x HD columns (one head of a token-major tensor) staged
+// through registers into the padded row layout.  Each thread owns fixed 16-byte
+// chunks, so the per-tile cost is one buffer load and one LDS store per chunk; the
+// tile's base and valid length go into the (scalar) buffer resource.
+template <int HD, int ROWS> struct BufRows {
+  using C = TileCfg<bf16, HD, ROWS>;
+  static constexpr int kPerRow = HD / 8;
+  static constexpr int kPasses = C::kRowPasses;
+  static_assert(C::kChunks % 256 == 0, "tile must be a whole number of 256-thread passes");
+  uint4 r[kPasses];
+
+  // Byte offset in the tensor of this thread's chunk in pass p (row stride ld_bytes).
+  __device__ __forceinline__ static int goff(int p, int tid, int ld_bytes) {
+    const int id = p * 256 + tid;
+    return (id / kPerRow) * ld_bytes + (id % kPerRow) * 16;
+  }
+  __device__ __forceinline__ static int loff(int p, int tid) {
+    const int id = p * 256 + tid;
+    return ((id / kPerRow) * C::kRowStride + (id % kPerRow) * 8) * 2;
+  }
+  // base: row 0 of the tile (head offset applied); nrows: valid rows from base.
+  __device__ __forceinline__ void load(const bf16 *base, int ld_bytes, int nrows, int tid) {
+    const int n = nrows < ROWS ? (nrows > 0 ? nrows : 0) : ROWS;
+    // The last valid row ends at its head's 16-byte chunks; rows >= n read as zero.
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, n > 0 ? (uint32_t)((n - 1) * ld_bytes + HD * 2) : 0u);
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p)
+      r[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, goff(p, tid, ld_bytes), 0, 0));
+  }
+  __device__ __forceinline__ void store(char *lds, int tid) const {
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) *reinterpret_cast<uint4 *>(lds + loff(p, tid)) = r[p];
+  }
+};
+
 // Registers holding one bf16 tile in flight for the T4 layout.
 template <int HD, int BN> struct T4Regs {
   using C = TileCfg<bf16, HD, BN>;
