@@ -261,8 +261,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdQArgs a) {
 template <int HD>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
   constexpr int BN = kFwdBN;
-  using TC = TileCfg<bf16, HD, BN>;
-  constexpr int TILE = TC::kRowBytes;
+  constexpr int TILE = BN * HD * 2;
   constexpr int NKC = HD / 16;
   constexpr int NDB = HD / 32;
   __shared__ __attribute__((aligned(16))) char smem[2][2 * TILE];
@@ -315,24 +314,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
   const bf16 *ko_base = reinterpret_cast<const bf16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
   const bf16 *vo_base = reinterpret_cast<const bf16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
   const int kld_b = (int)(kld * 2);
-  BufRows<HD, BN> kregs, vregs;
-  auto issue = [&](int i) {
+  DmaRows<HD, BN> dma;
+  dma.init(wave, lane, kld_b);
+  auto issue = [&](int i) {   // tile i -> stage i % 2
+    char *st = smem[i & 1];
     if (i < n_ctx) {
       int s = ctx_t0 + i * BN;
-      kregs.load(kc_base + (long)s * kld, kld_b, P - s, tid);
-      vregs.load(vc_base + (long)s * kld, kld_b, P - s, tid);
+      dma.load(st, kc_base + (long)s * kld, kld_b, P - s, wave);
+      dma.load(st + TILE, vc_base + (long)s * kld, kld_b, P - s, wave);
     } else {
       int s = own_t0 + (i - n_ctx) * BN;
-      kregs.load(ko_base + (long)s * kld, kld_b, seqlen - s, tid);
-      vregs.load(vo_base + (long)s * kld, kld_b, seqlen - s, tid);
+      dma.load(st, ko_base + (long)s * kld, kld_b, seqlen - s, wave);
+      dma.load(st + TILE, vo_base + (long)s * kld, kld_b, seqlen - s, wave);
     }
   };
-  if (n_tiles > 0) {
-    issue(0);
-    kregs.store(smem[0], tid);
-    vregs.store(smem[0] + TILE, tid);
-    if (n_tiles > 1) issue(1);
-  }
+  if (n_tiles > 0) issue(0);
 
   for (int i = 0; i < n_tiles; ++i) {
     int nrows, kpos0;
@@ -345,12 +341,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
       nrows = seqlen - s;
       kpos0 = P + s;
     }
+    dma_wait();
     __syncthreads();
-    if (i + 1 < n_tiles) {
-      kregs.store(smem[(i + 1) & 1], tid);
-      vregs.store(smem[(i + 1) & 1] + TILE, tid);
-      if (i + 2 < n_tiles) issue(i + 2);
-    }
+    if (i + 1 < n_tiles) issue(i + 1);
     const char *ks = smem[i & 1];
     const char *vs = smem[i & 1] + TILE;
     const bool need_mask = (nrows < BN) || (kpos0 + BN - 1 > qmin) ||
@@ -361,8 +354,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
       f32x16 st = zero16(), dpt = zero16();
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
-        st = mfma(row_frag<bf16, HD, BN>(ks, hb * 32 + col, kc, half), qf[kc], st);
-        dpt = mfma(row_frag<bf16, HD, BN>(vs, hb * 32 + col, kc, half), df[kc], dpt);
+        st = mfma(sw_frag<HD>(ks, hb * 32 + col, kc, half), qf[kc], st);
+        dpt = mfma(sw_frag<HD>(vs, hb * 32 + col, kc, half), df[kc], dpt);
       }
       float ds[16];
 #pragma unroll
@@ -380,8 +373,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
       // dQᵀ += Kᵀ dSᵀ.
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        acc[db] = mfma(tr_frag<TC::kRowStride>(ks, hb * 32, db * 32, lane), d0, acc[db]);
-        acc[db] = mfma(tr_frag<TC::kRowStride>(ks, hb * 32 + 16, db * 32, lane), d1, acc[db]);
+        acc[db] = mfma(sw_tr_frag<HD>(ks, hb * 32, db * 32, lane), d0, acc[db]);
+        acc[db] = mfma(sw_tr_frag<HD>(ks, hb * 32 + 16, db * 32, lane), d1, acc[db]);
       }
     }
   }
@@ -671,20 +664,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
 // bf16 dK/dV kernel.  A workgroup owns 128 keys of one region and kv head (32 per
 // wave: K, V fragments and the dK, dV accumulators in registers) and streams the
 // query rows that see them in 64-row steps (two 32-row blocks), from the last step
-// backward.  Q, dO, LSE and D of the next step are loaded with buffer loads while
-// the current one is computed, and double-buffered in LDS (one barrier per step).
-// The rows of a step are flattened (token, head-of-group) pairs; a thread's rows
-// within the step are fixed, so its token/head split is precomputed.
+// backward.  Q, dO, LSE and D of the next step stream into LDS by DMA while the
+// current step is computed (double-buffered, one barrier per step).  The rows of a
+// step are flattened (token, head-of-group) pairs; the rows a lane fetches are fixed
+// within a step, so their token/head split is precomputed.
 template <int HD>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
   constexpr int BM = 64;
   constexpr int BNW = kBwdBN;
-  using TC = TileCfg<bf16, HD, BM>;
-  constexpr int TILE = TC::kRowBytes;
+  constexpr int TILE = BM * HD * 2;
   constexpr int NKC = HD / 16;
   constexpr int NDB = HD / 32;
-  constexpr int kPerRow = HD / 8;
-  constexpr int kPasses = TC::kRowPasses;
+  constexpr int CPR = HD / 8;                     // 16-byte chunks per row
+  constexpr int KPW = TILE / 1024 / 4;            // DMA instructions per wave per tile
   constexpr int STAGE = 2 * TILE + 2 * BM * 4;
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
@@ -746,7 +738,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
     fa = r_lo * G;
     fb = r_hi > r_lo ? r_hi * G : fa;
   };
-  // Steps sit on multiples of BM flattened rows, walked from the last one backward.
+  // Steps sit on multiples of BM flattened rows, walked from the last one backward, so
+  // every key tile of a sequence streams the same rows at the same time (L2 reuse).
   int cs = it.seq_hi - 1, cf = 0, cfa = 0, cfb = 0;
   bool done = false;
   auto seek = [&]() {
@@ -765,68 +758,58 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
   };
   seek();
 
-  // This thread's fixed rows of a step (for the Q / dO staging).
-  int trow[kPasses], jrow[kPasses];
+  // The rows and chunks this lane fetches into a step's swizzled Q / dO tiles.
+  int trow[KPW], jrow[KPW], cofs[KPW];
 #pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int r = (p * 256 + tid) / kPerRow;
-    trow[p] = r / G;
-    jrow[p] = r - trow[p] * G;
+  for (int k = 0; k < KPW; ++k) {
+    const int slot = (k * 4 + wave) * 64 + lane;
+    const int r = slot / CPR;
+    trow[k] = r / G;
+    jrow[k] = r - trow[k] * G;
+    cofs[k] = ((slot % CPR) ^ Swz<HD>::swz(r)) << 4;
   }
-  const int chb = (tid % kPerRow) * 16;          // byte offset of this thread's chunk
+  const int tl = lane / G, jl = lane - tl * G;   // this lane's row of the LSE / D fetch
   const int qld_b = (int)(qld * 2);
   const int head0_b = g * G * HD * 2;
-  uint4 qr[kPasses], dr[kPasses];
-  float lse_r = INFINITY, d_r = 0.f;
-  auto issue = [&]() {
+  // Wave 0 fetches LSE rows, wave 1 D rows.
+  const __amdgpu_buffer_rsrc_t r_ld = make_rsrc_u(wave == 0 ? (const void *)a.lse : (const void *)a.D,
+                                                  (uint32_t)((long)a.Hq * a.lse_ld * 4));
+
+  // Fetch the step at the cursor into stage `st`.
+  auto issue = [&](char *st) {
     const int s0 = a.cu[cs];
     const int len = a.cu[cs + 1] - s0;
     const __amdgpu_buffer_rsrc_t rq =
-        make_rsrc(reinterpret_cast<const bf16 *>(a.q) + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
+        make_rsrc_u(reinterpret_cast<const bf16 *>(a.q) + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
     const __amdgpu_buffer_rsrc_t rd =
-        make_rsrc(reinterpret_cast<const bf16 *>(a.dout) + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
+        make_rsrc_u(reinterpret_cast<const bf16 *>(a.dout) + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
     const int ft = cf / G, fj = cf - ft * G;
+    const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_u32(st) + wave * 1024);
 #pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      int t = ft + trow[p], j = fj + jrow[p];
+    for (int k = 0; k < KPW; ++k) {
+      int t = ft + trow[k], j = fj + jrow[k];
       if (j >= G) {
         j -= G;
         ++t;
       }
-      const int off = t * qld_b + head0_b + j * (HD * 2) + chb;
-      qr[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-      dr[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0));
+      const int off = t * qld_b + head0_b + j * (HD * 2) + cofs[k];
+      dma16(rq, l0 + k * 4096, off);
+      dma16(rd, l0 + TILE + k * 4096, off);
     }
-    if (tid < BM) {
-      const int f = cf + tid;
-      if (f >= cfa && f < cfb) {
-        const int t = f / G, j = f - t * G;
-        const long idx = (long)(g * G + j) * a.lse_ld + s0 + t;
-        lse_r = a.lse[idx] * kLog2e;
-        d_r = a.D[idx];
-      } else {
-        lse_r = INFINITY;
-        d_r = 0.f;
+    if (wave < 2) {   // LSE (wave 0) and D (wave 1) of the step's 64 rows
+      int t = ft + tl, j = fj + jl;
+      if (j >= G) {
+        j -= G;
+        ++t;
       }
-    }
-  };
-  auto stage_store = [&](char *st) {
-#pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      const int r = (p * 256 + tid) / kPerRow;
-      const int lo = (r * TC::kRowStride) * 2 + chb;
-      *reinterpret_cast<uint4 *>(st + lo) = qr[p];
-      *reinterpret_cast<uint4 *>(st + TILE + lo) = dr[p];
-    }
-    if (tid < BM) {
-      reinterpret_cast<float *>(st + 2 * TILE)[tid] = lse_r;
-      reinterpret_cast<float *>(st + 2 * TILE)[BM + tid] = d_r;
+      const int off = ((g * G + j) * a.lse_ld + s0 + t) * 4;
+      const uint32_t la = __builtin_amdgcn_readfirstlane(lds_u32(st + 2 * TILE) + wave * BM * 4);
+      dma4(r_ld, la, off);
     }
   };
 
-  // Step bounds of the staged (next) step.
   int nf0 = 0, nflo = 0, nfend = 0;
-  auto advance = [&]() {   // record the staged step's bounds, then move the cursor on
+  auto advance = [&]() {   // record the fetched step's bounds, then move the cursor on
     nf0 = cf;
     nflo = max(cf, cfa);
     nfend = min(cf + BM, cfb);
@@ -840,22 +823,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
   bool have = !done;
   int f0 = 0, flo = 0, fend = 0;
   if (have) {
-    issue();
-    stage_store(smem);
+    issue(smem);
     advance();
     f0 = nf0, flo = nflo, fend = nfend;
-    if (!done) issue();
   }
 
   while (have) {
+    dma_wait();
     __syncthreads();
     const bool more = !done;
     int g0 = 0, glo = 0, gend = 0;
     if (more) {
-      stage_store(smem + (stage ^ 1) * STAGE);
+      issue(smem + (stage ^ 1) * STAGE);
       advance();
       g0 = nf0, glo = nflo, gend = nfend;
-      if (!done) issue();
     }
     const char *qs = smem + stage * STAGE;
     const char *dos = qs + TILE;
@@ -872,13 +853,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
         f32x16 st = zero16(), dpt = zero16();
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
-          st = mfma(row_frag<bf16, HD, BM>(qs, rb * 32 + col, kc, half), kf[kc], st);
-          dpt = mfma(row_frag<bf16, HD, BM>(dos, rb * 32 + col, kc, half), vf[kc], dpt);
+          st = mfma(sw_frag<HD>(qs, rb * 32 + col, kc, half), kf[kc], st);
+          dpt = mfma(sw_frag<HD>(dos, rb * 32 + col, kc, half), vf[kc], dpt);
         }
         const int ta = max(b0, flo) / G;
         const int tb = (min(b0 + 32, fend) - 1) / G;
         const bool full = (b0 >= flo) && (b0 + 32 <= fend) && (kw0 + 32 <= nkeys) &&
                           (kpb <= P + ta) && (wl < 0 || kpa >= P + tb - wl);
+        const int vlo = max(flo, f_vis_lo), vhi = min(fend, f_vis_hi);
         float pv[16], dsv[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -889,10 +871,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int v = 4 * i + e;
-            float p = fast_exp2(fmaf(st[v], sf, -lv[e]));
+            float p = fast_exp2(fmaf(st[v], sf, -lv[e] * kLog2e));
             if (!full) {
               const int f = b0 + c_row(v, half);
-              if (f < max(flo, f_vis_lo) || f >= min(fend, f_vis_hi)) p = 0.f;
+              if (f < vlo || f >= vhi) p = 0.f;
             }
             pv[v] = p;
             dsv[v] = p * (dpt[v] - dd[e]);
@@ -903,10 +885,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
         // dV += Pᵀ dO and dK += dSᵀ Q over the block's 32 rows.
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          dv[db] = mfma(p0, tr_frag<TC::kRowStride>(dos, rb * 32, db * 32, lane), dv[db]);
-          dv[db] = mfma(p1, tr_frag<TC::kRowStride>(dos, rb * 32 + 16, db * 32, lane), dv[db]);
-          dk[db] = mfma(s0, tr_frag<TC::kRowStride>(qs, rb * 32, db * 32, lane), dk[db]);
-          dk[db] = mfma(s1, tr_frag<TC::kRowStride>(qs, rb * 32 + 16, db * 32, lane), dk[db]);
+          dv[db] = mfma(p0, sw_tr_frag<HD>(dos, rb * 32, db * 32, lane), dv[db]);
+          dv[db] = mfma(p1, sw_tr_frag<HD>(dos, rb * 32 + 16, db * 32, lane), dv[db]);
+          dk[db] = mfma(s0, sw_tr_frag<HD>(qs, rb * 32, db * 32, lane), dk[db]);
+          dk[db] = mfma(s1, sw_tr_frag<HD>(qs, rb * 32 + 16, db * 32, lane), dk[db]);
         }
       }
     }

@@ -251,8 +251,7 @@ __global__ __launch_bounds__(256, (FwdOcc<T, HD>::kWaves)) void fwd_kernel(FwdAr
 template <int HD>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int BN = kFwdBN;
-  using TC = TileCfg<bf16, HD, BN>;
-  constexpr int TILE = TC::kRowBytes;
+  constexpr int TILE = BN * HD * 2;     // dense swizzled tile
   constexpr int NKC = HD / 16;     // MFMA steps over the head dim
   constexpr int NDB = HD / 32;     // 32-wide blocks of the output head dim
   constexpr int NKB = BN / 32;     // 32-key blocks per tile
@@ -304,24 +303,21 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const bf16 *vo_base = reinterpret_cast<const bf16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
 
   const int kld_b = (int)(kld * 2);
-  BufRows<HD, BN> kregs, vregs;
-  auto issue = [&](int i) {
+  DmaRows<HD, BN> dma;
+  dma.init(wave, lane, kld_b);
+  auto issue = [&](int i) {   // tile i -> stage i % 2
+    char *st = smem[i & 1];
     if (i < n_ctx) {
       int s = ctx_t0 + i * BN;
-      kregs.load(kc_base + (long)s * kld, kld_b, P - s, tid);
-      vregs.load(vc_base + (long)s * kld, kld_b, P - s, tid);
+      dma.load(st, kc_base + (long)s * kld, kld_b, P - s, wave);
+      dma.load(st + TILE, vc_base + (long)s * kld, kld_b, P - s, wave);
     } else {
       int s = own_t0 + (i - n_ctx) * BN;
-      kregs.load(ko_base + (long)s * kld, kld_b, seqlen - s, tid);
-      vregs.load(vo_base + (long)s * kld, kld_b, seqlen - s, tid);
+      dma.load(st, ko_base + (long)s * kld, kld_b, seqlen - s, wave);
+      dma.load(st + TILE, vo_base + (long)s * kld, kld_b, seqlen - s, wave);
     }
   };
-  if (n_tiles > 0) {
-    issue(0);
-    kregs.store(smem[0], tid);
-    vregs.store(smem[0] + TILE, tid);
-    if (n_tiles > 1) issue(1);
-  }
+  if (n_tiles > 0) issue(0);
 
   for (int i = 0; i < n_tiles; ++i) {
     int nrows, kpos0;
@@ -334,13 +330,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       nrows = seqlen - s;
       kpos0 = P + s;
     }
-    // Stage i % 2 holds tile i; stage (i + 1) % 2 was last read for tile i - 1.
+    // Tile i has landed in stage i % 2 and every wave is done with tile i - 1, whose
+    // stage receives tile i + 1 while tile i is computed.
+    dma_wait();
     __syncthreads();
-    if (i + 1 < n_tiles) {
-      kregs.store(smem[(i + 1) & 1], tid);
-      vregs.store(smem[(i + 1) & 1] + TILE, tid);
-      if (i + 2 < n_tiles) issue(i + 2);
-    }
+    if (i + 1 < n_tiles) issue(i + 1);
     const char *ks = smem[i & 1];
     const char *vs = smem[i & 1] + TILE;
 
@@ -352,7 +346,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        s[kb] = mfma(row_frag<bf16, HD, BN>(ks, kb * 32 + col, kc, half), qf[kc], s[kb]);
+        s[kb] = mfma(sw_frag<HD>(ks, kb * 32 + col, kc, half), qf[kc], s[kb]);
 
     const bool need_mask = (nrows < BN) || (kpos0 + BN - 1 > qmin) ||
                            (wl >= 0 && kpos0 < qmax - wl);
@@ -404,7 +398,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     for (int u = 0; u < 2 * NKB; ++u)
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        acc[db] = mfma(tr_frag<TC::kRowStride>(vs, 16 * u, db * 32, lane), pf[u], acc[db]);
+        acc[db] = mfma(sw_tr_frag<HD>(vs, 16 * u, db * 32, lane), pf[u], acc[db]);
   }
 
   const float l = l_run + wave_xor32(l_run);

@@ -218,4 +218,126 @@ __device__ __forceinline__ bf16x8 tr_frag(const char *lds, int row0, int col0, i
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// ------------------------------------------------------------ LDS DMA tiles --
+//
+// gfx950 buffer loads with the `lds` bit write each lane's 16 bytes straight to LDS
+// at M0 + 16 * lane: one wave instruction fills 1 KB, with any source address per
+// lane, and a lane past the end of the buffer resource writes zeros.  Tiles staged
+// this way need no staging registers and no LDS store instructions.  The load is
+// issued from inline assembly so that the compiler does not wait for it before every
+// LDS read; the kernels wait (`dma_wait`) right before the barrier that publishes a
+// stage.  M0 is saved and restored around the load.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, int voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(r)
+      : "memory");
+}
+// 4-byte form: lane i's word goes to M0 + 4 * i (256 bytes per wave instruction).
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, int voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(r)
+      : "memory");
+}
+__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// A buffer resource built from values the compiler cannot prove wave-uniform (the
+// callers' are uniform by construction): the operands of the DMA instructions must
+// live in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_u(const void *base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return make_rsrc(reinterpret_cast<const void *>(((uint64_t)hi << 32) | lo),
+                   __builtin_amdgcn_readfirstlane(bytes));
+}
+
+// LDS byte address of a pointer into __shared__ memory (the low 32 bits of its flat
+// address inside the LDS aperture).
+__device__ __forceinline__ uint32_t lds_u32(const void *p) { return (uint32_t)(uintptr_t)p; }
+
+// Swizzled dense tile [row][HD] bf16: the 16-byte chunk c of row r sits in slot
+// c ^ swz(r).  swz's low bits spread 8 consecutive rows over 8 different slots (the
+// 32 query/key rows of a fragment read hit distinct banks) and map the 4 rows of a
+// transpose read's 16-lane group to 4 different slot pairs.
+template <int HD> struct Swz {
+  static constexpr int kChunks = HD / 8;   // 16-byte chunks per row
+  __device__ __forceinline__ static int swz(int r) {
+    int x = ((r & 3) << 1) | ((r >> 2) & 1);
+    if constexpr (kChunks >= 16) x |= ((r >> 3) & 1) << 3;
+    return x;
+  }
+  __device__ __forceinline__ static int off(int r, int chunk) {   // byte offset of a chunk
+    return r * (HD * 2) + ((chunk ^ swz(r)) << 4);
+  }
+};
+
+// A-/B-operand fragment (8 bf16 of one row) of a swizzled tile: row `row`, k-chunk kc.
+template <int HD>
+__device__ __forceinline__ bf16x8 sw_frag(const char *lds, int row, int kc, int half) {
+  return as_bf16x8(*reinterpret_cast<const uint4 *>(lds + Swz<HD>::off(row, kc * 2 + half)));
+}
+
+// Transposed operand from a swizzled tile (see tr_frag): column col0 + lane % 32 over
+// the 16-row slice from row0, rows in the kappa order of a C tile.
+template <int HD>
+__device__ __forceinline__ bf16x8 sw_tr_frag(const char *lds, int row0, int col0, int lane) {
+  const int half = lane >> 5, grp = (lane >> 4) & 1, j = lane & 15;
+  const int col = col0 + 16 * grp + 4 * (j & 3);
+  const int r1 = row0 + 4 * half + (j >> 2);
+  const int inb = (col & 7) * 2;
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) char lchar;
+  auto p1 = reinterpret_cast<__attribute__((address_space(3))) s16x4 *>(
+      (lchar *)(lds) + Swz<HD>::off(r1, col >> 3) + inb);
+  auto p2 = reinterpret_cast<__attribute__((address_space(3))) s16x4 *>(
+      (lchar *)(lds) + Swz<HD>::off(r1 + 8, col >> 3) + inb);
+  s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p1);
+  s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p2);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// DMA of a ROWS x HD bf16 tile of consecutive rows (row stride ld_bytes, head offset
+// already in `base`) into a swizzled tile.  Block b (1 KB) of the tile is written by
+// wave b % 4; lane i of that instruction fills slot i of the block.  The per-lane
+// source offsets depend only on the thread and the row stride.
+template <int HD, int ROWS> struct DmaRows {
+  static constexpr int kBlocks = ROWS * HD * 2 / 1024;
+  static_assert(kBlocks % 4 == 0, "tile must be a multiple of 4 KB");
+  static constexpr int kPerWave = kBlocks / 4;
+  int voff[kPerWave];
+  __device__ __forceinline__ void init(int wave, int lane, int ld_bytes) {
+#pragma unroll
+    for (int k = 0; k < kPerWave; ++k) {
+      const int slot = (k * 4 + wave) * 64 + lane;
+      const int r = slot / Swz<HD>::kChunks, cs = slot % Swz<HD>::kChunks;
+      voff[k] = r * ld_bytes + ((cs ^ Swz<HD>::swz(r)) << 4);
+    }
+  }
+  // nrows: valid rows from base (rows past them are zero-filled).
+  __device__ __forceinline__ void load(char *lds_tile, const bf16 *base, int ld_bytes, int nrows,
+                                       int wave) const {
+    const int n = nrows < ROWS ? (nrows > 0 ? nrows : 0) : ROWS;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc_u(base, n > 0 ? (uint32_t)((n - 1) * ld_bytes + HD * 2) : 0u);
+    const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_u32(lds_tile) + wave * 1024);
+#pragma unroll
+    for (int k = 0; k < kPerWave; ++k) dma16(rs, l0 + k * 4096, voff[k]);
+  }
+};
+
 }  // namespace dkv
+
