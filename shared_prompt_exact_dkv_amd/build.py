@@ -5,8 +5,9 @@ host-only translation unit gets the same flags (hipcc's host pass ignores the
 feature with a warning).  MFMA results are kept in architectural VGPRs
 (-amdgpu-mfma-vgpr-form): the softmax and the scaling work on the score tiles with
 VALU instructions, which cannot read accumulation registers, so accumulators placed
-there would be copied out and back on every tile.  Objects go to _build/ at the repository root, the shared
-library next to this file.
+there would be copied out and back on every tile (the kernels are sized so that a
+wave's state fits the architectural registers).  Objects go to _build/ at the
+repository root, the shared library next to this file.
 """
 from __future__ import annotations
 
@@ -22,16 +23,17 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["dkv_api.cpp", "dkv_fwd.hip", "dkv_bwd.hip"]
+SOURCES = ["dkv_api.cpp", "dkv_fwd.hip", "dkv_bwd.hip", "dkv_d512.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I", os.path.join(ROOT, "include")]
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+EXTRA = {"dkv_fwd.hip": VGPR_FORM, "dkv_bwd.hip": VGPR_FORM, "dkv_d512.hip": VGPR_FORM}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)

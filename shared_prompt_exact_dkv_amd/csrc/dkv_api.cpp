@@ -50,7 +50,9 @@ struct Shape {
   float scale;
   long T;                   // cu[N]
   std::vector<int> cu;
-  int bm_tok;               // query tokens per forward / dQ workgroup
+  int bm_tok;               // query tokens per forward workgroup
+  int bm_tok_dq;            // query tokens per dQ workgroup
+  int kv_tile;              // keys per dK/dV workgroup
 };
 
 dkv_status check_params(const dkv_params *p, bool is_ctx, Shape *s) {
@@ -96,7 +98,20 @@ dkv_status check_params(const dkv_params *p, bool is_ctx, Shape *s) {
   if (s->T > 0 && !p->cu_seqlens_dev)
     return fail(DKV_ERR_INVALID_ARG, "cu_seqlens_dev is NULL");
   s->bm_tok = kRowsPerWG / G;
-  if (s->d == 512) return fail(DKV_ERR_UNSUPPORTED, "head_dim 512 is not available in this build");
+  s->bm_tok_dq = s->bm_tok;
+  s->kv_tile = kBwdBN;
+  if (s->d == 512) {
+    // Head dim 512 splits the head dim across the waves of a workgroup: 64 query
+    // rows per forward workgroup, 32 per dQ workgroup, 32 keys per dK/dV workgroup;
+    // bf16 only.
+    if (s->dtype != DKV_BF16)
+      return fail(DKV_ERR_UNSUPPORTED, "head_dim 512 is implemented for bf16 only");
+    if (G > kRowsPerWG512)
+      return fail(DKV_ERR_UNSUPPORTED, "Hq/Hkv = %d exceeds %d at head_dim 512", G, kRowsPerWG512);
+    s->bm_tok = kFwdRows512 / G;
+    s->bm_tok_dq = kRowsPerWG512 / G;
+    s->kv_tile = kBwdBN512;
+  }
   return DKV_OK;
 }
 
@@ -144,26 +159,26 @@ std::vector<Item> interleave_xcds(std::vector<std::vector<Item>> &lists) {
   return out;
 }
 
-long q_item_work(const Shape &s, int tile, int seqlen, int BN) {
-  long t0 = (long)tile * s.bm_tok;
-  long t1 = std::min<long>(seqlen, t0 + s.bm_tok);
+long q_item_work(const Shape &s, int bm_tok, int tile, int seqlen, int BN) {
+  long t0 = (long)tile * bm_tok;
+  long t1 = std::min<long>(seqlen, t0 + bm_tok);
   long qmin = s.P + t0, qmax = s.P + t1 - 1;
   long lo = (s.wl >= 0) ? std::max<long>(0, qmin - s.wl) : 0;
   long keys = qmax + 1 - lo;
   return (keys + BN - 1) / BN;
 }
 
-std::vector<QItem> build_q_items(const Shape &s, int BN) {
+std::vector<QItem> build_q_items(const Shape &s, int bm_tok, int BN) {
   struct Rec { long work; int tile; };
   struct Group { long work; int seq; std::vector<Rec> recs; };
   std::vector<Group> groups;
   for (int i = 0; i < s.N; ++i) {
     int len = s.cu[i + 1] - s.cu[i];
-    int nt = (len + s.bm_tok - 1) / s.bm_tok;
+    int nt = (len + bm_tok - 1) / bm_tok;
     if (nt == 0) continue;
     Group gr{0, i, {}};
     for (int m = 0; m < nt; ++m) {
-      long w = q_item_work(s, m, len, BN);
+      long w = q_item_work(s, bm_tok, m, len, BN);
       gr.recs.push_back({w, m});
       gr.work += w;
     }
@@ -298,13 +313,18 @@ struct FwdPlan {
   size_t n_items = 0;
 };
 
-FwdPlan plan_fwd(const Shape &s) {
-  FwdPlan pl;
+size_t count_q_items(const Shape &s, int bm_tok) {
   size_t n = 0;
   for (int i = 0; i < s.N; ++i) {
     int len = s.cu[i + 1] - s.cu[i];
-    n += (size_t)((len + s.bm_tok - 1) / s.bm_tok) * s.Hkv;
+    n += (size_t)((len + bm_tok - 1) / bm_tok) * s.Hkv;
   }
+  return n;
+}
+
+FwdPlan plan_fwd(const Shape &s) {
+  FwdPlan pl;
+  size_t n = count_q_items(s, s.bm_tok);
   pl.n_items = n;
   pl.items_off = 0;
   pl.bytes = align_up(n * sizeof(QItem));
@@ -328,7 +348,7 @@ dkv_status run_fwd(const Shape &s, const void *q, const void *kc, const void *vc
   dkv_status st = check_ws(ws, ws_bytes, pl.bytes);
   if (st != DKV_OK) return st;
   if (pl.n_items == 0) return DKV_OK;
-  std::vector<QItem> items = build_q_items(s, kFwdBN);
+  std::vector<QItem> items = build_q_items(s, s.bm_tok, kFwdBN);
   char *wsb = static_cast<char *>(ws);
   st = upload(items.data(), items.size() * sizeof(QItem), wsb + pl.items_off, stream);
   if (st != DKV_OK) return st;
@@ -394,8 +414,8 @@ std::vector<KVItem> build_kv_items(const Shape &s, bool with_ctx) {
     const int hi = std::min(s.N, lo + cs);
     Group gr{0, {}};
     if (with_ctx && s.P > 0) {
-      for (int k0 = 0; k0 < s.P; k0 += kBwdBN) {
-        int nk = std::min(kBwdBN, s.P - k0);
+      for (int k0 = 0; k0 < s.P; k0 += s.kv_tile) {
+        int nk = std::min(s.kv_tile, s.P - k0);
         long w = 0;
         for (int i = lo; i < hi; ++i) w += kv_rows_visible(s, true, k0, nk, s.cu[i + 1] - s.cu[i]);
         if (w > 0) gr.recs.push_back({w, kRegionCtx, k0, lo, hi});
@@ -403,8 +423,8 @@ std::vector<KVItem> build_kv_items(const Shape &s, bool with_ctx) {
     }
     for (int i = lo; i < hi; ++i) {
       int len = s.cu[i + 1] - s.cu[i];
-      for (int k0 = 0; k0 < len; k0 += kBwdBN) {
-        int nk = std::min(kBwdBN, len - k0);
+      for (int k0 = 0; k0 < len; k0 += s.kv_tile) {
+        int nk = std::min(s.kv_tile, len - k0);
         gr.recs.push_back({kv_rows_visible(s, false, k0, nk, len), kRegionOwn, k0, i, i + 1});
       }
     }
@@ -436,16 +456,15 @@ struct BwdPlan {
 
 BwdPlan plan_bwd(const Shape &s, bool with_ctx) {
   BwdPlan pl;
-  FwdPlan fq = plan_fwd(s);
-  pl.n_q = fq.n_items;
+  pl.n_q = count_q_items(s, s.bm_tok_dq);
   size_t nkv = 0;
   for (int i = 0; i < s.N; ++i) {
     int len = s.cu[i + 1] - s.cu[i];
-    nkv += (size_t)((len + kBwdBN - 1) / kBwdBN);
+    nkv += (size_t)((len + s.kv_tile - 1) / s.kv_tile);
   }
   if (with_ctx && s.P > 0 && s.N > 0) {
     int cs = ctx_chunk(s);
-    nkv += (size_t)((s.P + kBwdBN - 1) / kBwdBN) * ((s.N + cs - 1) / cs);
+    nkv += (size_t)((s.P + s.kv_tile - 1) / s.kv_tile) * ((s.N + cs - 1) / cs);
   }
   pl.n_kv = nkv * s.Hkv;   // upper bound (empty windowed items are dropped)
   pl.d_off = 0;
@@ -487,7 +506,7 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
     float *D = reinterpret_cast<float *>(wsb + pl.d_off);
     e = timed(kKPre, stream, [&] { return launch_bwd_pre(s.dtype, s.d, io.o, io.dout, D, s.T, s.Hq, stream); });
     if (e != hipSuccess) return hip_fail(e, "bwd preprocess launch");
-    std::vector<QItem> qi = build_q_items(s, kFwdBN);
+    std::vector<QItem> qi = build_q_items(s, s.bm_tok_dq, kFwdBN);
     std::vector<KVItem> kv = build_kv_items(s, io.with_ctx);
     if ((st = upload(qi.data(), qi.size() * sizeof(QItem), wsb + pl.q_off, stream)) != DKV_OK) return st;
     if ((st = upload(kv.data(), kv.size() * sizeof(KVItem), wsb + pl.kv_off, stream)) != DKV_OK) return st;
@@ -495,7 +514,7 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
     qa.q = io.q; qa.k_ctx = io.kc; qa.v_ctx = io.vc; qa.k_own = io.ko; qa.v_own = io.vo;
     qa.dout = io.dout; qa.lse = io.lse; qa.D = D; qa.dq = io.dq;
     qa.items = reinterpret_cast<const QItem *>(wsb + pl.q_off);
-    qa.Hq = s.Hq; qa.Hkv = s.Hkv; qa.G = s.G; qa.bm_tok = s.bm_tok; qa.ctx_len = s.P;
+    qa.Hq = s.Hq; qa.Hkv = s.Hkv; qa.G = s.G; qa.bm_tok = s.bm_tok_dq; qa.ctx_len = s.P;
     qa.window_left = s.wl; qa.lse_ld = (int)s.T; qa.scale = s.scale;
     e = timed(kKDq, stream, [&] { return launch_bwd_dq(s.dtype, s.d, qa, (int)qi.size(), stream); });
     if (e != hipSuccess) return hip_fail(e, "dq kernel launch");

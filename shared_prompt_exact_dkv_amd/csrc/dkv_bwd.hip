@@ -939,6 +939,7 @@ hipError_t launch_bwd_pre(int dtype, int hd, const void *o, const void *dout, fl
   if (dtype == 0) {
     if (hd == 64) return pre_t<bf16, 64>(o, dout, D, T, Hq, s);
     if (hd == 128) return pre_t<bf16, 128>(o, dout, D, T, Hq, s);
+    if (hd == 512) return pre_t<bf16, 512>(o, dout, D, T, Hq, s);
   } else {
     if (hd == 64) return pre_t<float, 64>(o, dout, D, T, Hq, s);
     if (hd == 128) return pre_t<float, 128>(o, dout, D, T, Hq, s);
@@ -982,6 +983,7 @@ hipError_t launch_bwd_dq(int dtype, int hd, const BwdQArgs &a, int n, hipStream_
       hipLaunchKernelGGL((bwd_dq_bf16_kernel<128>), dim3(n), dim3(256), 0, s, a);
       return hipGetLastError();
     }
+    if (hd == 512) return launch_bwd_dq_d512(a, n, s);
   } else {
     if (hd == 64) return dq_t<float, 64>(a, n, s);
     if (hd == 128) return dq_t<float, 128>(a, n, s);
@@ -1006,6 +1008,7 @@ hipError_t launch_bwd_dkdv(int dtype, int hd, const BwdKVArgs &a, int n, hipStre
       hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<128>), dim3(n), dim3(256), 0, s, a);
       return hipGetLastError();
     }
+    if (hd == 512) return launch_bwd_dkdv_d512(a, n, s);
   } else {
     if (hd == 64) return dkdv_t<float, 64>(a, n, s);
     if (hd == 128) return dkdv_t<float, 128>(a, n, s);

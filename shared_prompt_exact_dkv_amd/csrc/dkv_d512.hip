@@ -1,0 +1,599 @@
+// dkv_d512.hip -- head dimension 512 ("DualKV", arXiv 2605.15422, §3 "Head dimensions
+// and sliding-window support": the d = 512 global layers of hybrid models, here also
+// with the sliding window).
+//
+// A wave's fragments and fp32 accumulators for 32 rows over the whole 512-wide head
+// dim would need 384-768 registers, so the kernels split the head dim across the
+// waves of a workgroup and keep every wave within the architectural VGPRs:
+//
+//   forward  64 query rows per workgroup; the two waves of a pair share 32 rows and
+//            each holds Q and O for one half of the head dim.  Each computes the
+//            partial scores Sᵀ over its half, the pair adds the two partials through
+//            LDS (both in the same order, so both see identical scores), and each
+//            accumulates its half of O.
+//   dQ       32 query rows per workgroup.  Waves 0 / 1 form partial Sᵀ = K Qᵀ over
+//            the two halves of the head dim (holding Q), waves 2 / 3 partial
+//            dPᵀ = V dOᵀ (holding dO).  After one exchange every wave has both tiles,
+//            forms dSᵀ and accumulates dQ for one quarter of the head dim.
+//   dK/dV    32 keys per workgroup, the same arrangement: waves 0 / 1 hold K halves
+//            and form partial S, waves 2 / 3 hold V halves and form partial dP; each
+//            wave accumulates dK and dV for one quarter of the head dim.
+// Tiles are staged by LDS DMA into swizzled dense rows (one 1 KB row per DMA block),
+// double-buffered; partial tiles are exchanged through a small LDS area.
+#include "dkv_device.h"
+#include "dkv_launch.h"
+#include "dkv_tiles.h"
+
+namespace dkv {
+
+namespace {
+
+constexpr int HD = 512;
+
+// One 32 x 32 fp32 C tile per wave in the exchange area: lane l keeps element v at
+// word v * 64 + l, and the other waves read the same slots (same C layout).
+__device__ __forceinline__ void xch_put(float *area, const f32x16 &x, int lane) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) area[v * 64 + lane] = x[v];
+}
+__device__ __forceinline__ f32x16 xch_get(const float *area, int lane) {
+  f32x16 x;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) x[v] = area[v * 64 + lane];
+  return x;
+}
+// a + b element-wise (the fixed summation order of the partial tiles).
+__device__ __forceinline__ f32x16 add16(const f32x16 &a, const f32x16 &b) {
+  f32x16 r;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) r[v] = a[v] + b[v];
+  return r;
+}
+// Partial tile of wave w: its own registers, else the exchange area.
+__device__ __forceinline__ f32x16 part_of(int w, int me, const f32x16 &mine, const float *xch,
+                                          int lane) {
+  return w == me ? mine : xch_get(xch + w * 1024, lane);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------- forward --
+
+__global__ __launch_bounds__(256, 1) void fwd_d512_kernel(FwdArgs a) {
+  constexpr int BN = 32;
+  constexpr int TILE = BN * HD * 2;      // 32 KB
+  constexpr int NKH = HD / 2 / 16;       // MFMA k-steps per half head dim
+  constexpr int NDH = HD / 2 / 32;       // 32-wide output blocks per half
+  constexpr float kSlack = 8.f;
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE + 4 * 4096];
+  float *xch = reinterpret_cast<float *>(smem + 4 * TILE);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int rb = wave >> 1, dh = wave & 1;
+  const QItem it = a.items[blockIdx.x];
+  const int g = it.g, seq0 = it.seq_start, seqlen = it.seq_len;
+  const int t0 = it.tile * a.bm_tok;
+  const int nt = min(a.bm_tok, seqlen - t0);
+  const int qr = rb * 32 + col;
+  int tok = qr / a.G;
+  const int hj = qr - tok * a.G;
+  const bool row_valid = tok < nt;
+  if (!row_valid) tok = nt - 1;
+  const int h = g * a.G + hj;
+  const int P = a.ctx_len, wl = a.window_left;
+  const int qpos = P + t0 + tok;
+  const int qmin = P + t0, qmax = P + t0 + nt - 1;
+  const long qld = (long)a.Hq * HD;
+  const long kld = (long)a.Hkv * HD;
+  const int d0 = dh * (HD / 2);
+
+  const bf16 *qptr = reinterpret_cast<const bf16 *>(a.q) + (long)(seq0 + t0 + tok) * qld + (long)h * HD + d0;
+  bf16x8 qf[NKH];
+#pragma unroll
+  for (int kc = 0; kc < NKH; ++kc)
+    qf[kc] = as_bf16x8(*reinterpret_cast<const uint4 *>(qptr + kc * 16 + half * 8));
+
+  const float sf = a.scale * kLog2e;
+  f32x16 acc[NDH];
+#pragma unroll
+  for (int db = 0; db < NDH; ++db) acc[db] = zero16();
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int ctx_lo = (wl >= 0) ? max(0, qmin - wl) : 0;
+  const int ctx_t0 = (ctx_lo / BN) * BN;
+  const int n_ctx = (P > ctx_lo) ? (P - ctx_t0 + BN - 1) / BN : 0;
+  const int own_lo = (wl >= 0) ? max(0, t0 - wl) : 0;
+  const int own_t0 = (own_lo / BN) * BN;
+  const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
+  const int n_tiles = n_ctx + n_own;
+
+  const bf16 *kc_base = reinterpret_cast<const bf16 *>(a.k_ctx) + (long)g * HD;
+  const bf16 *vc_base = reinterpret_cast<const bf16 *>(a.v_ctx) + (long)g * HD;
+  const bf16 *ko_base = reinterpret_cast<const bf16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
+  const bf16 *vo_base = reinterpret_cast<const bf16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
+  const int kld_b = (int)(kld * 2);
+  DmaRows<HD, BN> dma;
+  dma.init(wave, lane, kld_b);
+  auto issue = [&](int i) {   // tile i -> stage i % 2 (K, then V)
+    char *st = smem + (i & 1) * 2 * TILE;
+    if (i < n_ctx) {
+      int s = ctx_t0 + i * BN;
+      dma.load(st, kc_base + (long)s * kld, kld_b, P - s, wave);
+      dma.load(st + TILE, vc_base + (long)s * kld, kld_b, P - s, wave);
+    } else {
+      int s = own_t0 + (i - n_ctx) * BN;
+      dma.load(st, ko_base + (long)s * kld, kld_b, seqlen - s, wave);
+      dma.load(st + TILE, vo_base + (long)s * kld, kld_b, seqlen - s, wave);
+    }
+  };
+  if (n_tiles > 0) issue(0);
+
+  for (int i = 0; i < n_tiles; ++i) {
+    int nrows, kpos0;
+    if (i < n_ctx) {
+      int s = ctx_t0 + i * BN;
+      nrows = P - s;
+      kpos0 = s;
+    } else {
+      int s = own_t0 + (i - n_ctx) * BN;
+      nrows = seqlen - s;
+      kpos0 = P + s;
+    }
+    dma_wait();
+    __syncthreads();
+    if (i + 1 < n_tiles) issue(i + 1);
+    const char *ks = smem + (i & 1) * 2 * TILE;
+    const char *vs = ks + TILE;
+
+    // Partial Sᵀ = K Qᵀ over this wave's half of the head dim; the pair adds halves
+    // 0 + 1 in that order.
+    f32x16 part = zero16();
+#pragma unroll
+    for (int kc = 0; kc < NKH; ++kc)
+      part = mfma(sw_frag<HD>(ks, col, dh * NKH + kc, half), qf[kc], part);
+    xch_put(xch + wave * 1024, part, lane);
+    __syncthreads();
+    const f32x16 other = xch_get(xch + (wave ^ 1) * 1024, lane);
+    f32x16 s = dh == 0 ? add16(part, other) : add16(other, part);
+
+    const bool need_mask = (nrows < BN) || (kpos0 + BN - 1 > qmin) ||
+                           (wl >= 0 && kpos0 < qmax - wl);
+    if (need_mask) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        int kk = c_row(v, half);
+        int kp = kpos0 + kk;
+        bool vis = (kk < nrows) && (kp <= qpos) && (wl < 0 || kp >= qpos - wl);
+        if (!vis) s[v] = -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
+    mx = fmaxf(mx, wave_xor32(mx)) * sf;
+    const bool grow = mx > m_run + kSlack;
+    if (__any(grow)) {
+      const float alpha = grow ? fast_exp2(m_run - mx) : 1.f;
+      if (grow) m_run = mx;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDH; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float t[16];
+    float rs = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      t[v] = fast_exp2(fmaf(s[v], sf, -m_use));
+      rs += t[v];
+    }
+    l_run += rs;
+    const bf16x8 p0 = pack8(t), p1 = pack8(t + 8);
+    // Oᵀ += Vᵀ Pᵀ over this wave's half of the head dim.
+#pragma unroll
+    for (int db = 0; db < NDH; ++db) {
+      acc[db] = mfma(sw_tr_frag<HD>(vs, 0, d0 + db * 32, lane), p0, acc[db]);
+      acc[db] = mfma(sw_tr_frag<HD>(vs, 16, d0 + db * 32, lane), p1, acc[db]);
+    }
+  }
+
+  const float l = l_run + wave_xor32(l_run);
+  const float inv = 1.f / l;
+  if (row_valid) {
+    bf16 *optr = reinterpret_cast<bf16 *>(a.o) + (long)(seq0 + t0 + tok) * qld + (long)h * HD + d0;
+#pragma unroll
+    for (int db = 0; db < NDH; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int dim = db * 32 + 8 * i + 4 * half;
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * i + e] * inv);
+        *reinterpret_cast<bf16x4 *>(optr + dim) = w;
+      }
+    if (half == 0 && dh == 0)
+      a.lse[(long)h * a.lse_ld + seq0 + t0 + tok] = (m_run + fast_log2(l)) * kLn2;
+  }
+}
+
+hipError_t launch_fwd_d512(const FwdArgs &a, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fwd_d512_kernel, dim3(n), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------ dQ --
+
+__global__ __launch_bounds__(256, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
+  constexpr int BN = 32;
+  constexpr int TILE = BN * HD * 2;      // 32 KB
+  constexpr int NKH = HD / 2 / 16;
+  constexpr int NDQ = HD / 4 / 32;       // 32-wide output blocks per quarter
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE + 4 * 4096];
+  float *xch = reinterpret_cast<float *>(smem + 4 * TILE);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int role = wave >> 1, dh = wave & 1;   // role 0: partial Sᵀ from Q; 1: partial dPᵀ from dO
+  const QItem it = a.items[blockIdx.x];
+  const int g = it.g, seq0 = it.seq_start, seqlen = it.seq_len;
+  const int t0 = it.tile * a.bm_tok;
+  const int nt = min(a.bm_tok, seqlen - t0);
+  int tok = col / a.G;
+  const int hj = col - tok * a.G;
+  const bool row_valid = tok < nt;
+  if (!row_valid) tok = nt - 1;
+  const int h = g * a.G + hj;
+  const int P = a.ctx_len, wl = a.window_left;
+  const int qpos = P + t0 + tok;
+  const int qmin = P + t0, qmax = P + t0 + nt - 1;
+  const long qld = (long)a.Hq * HD;
+  const long kld = (long)a.Hkv * HD;
+  const long qrow = (long)(seq0 + t0 + tok);
+
+  const bf16 *xptr = reinterpret_cast<const bf16 *>(role == 0 ? a.q : a.dout) + qrow * qld +
+                     (long)h * HD + dh * (HD / 2);
+  bf16x8 xf[NKH];
+#pragma unroll
+  for (int kc = 0; kc < NKH; ++kc)
+    xf[kc] = as_bf16x8(*reinterpret_cast<const uint4 *>(xptr + kc * 16 + half * 8));
+  const float sf = a.scale * kLog2e;
+  const float lse2 = a.lse[(long)h * a.lse_ld + qrow] * kLog2e;
+  const float Dq = a.D[(long)h * a.lse_ld + qrow];
+  const int dq0 = wave * (HD / 4);
+
+  f32x16 acc[NDQ];
+#pragma unroll
+  for (int db = 0; db < NDQ; ++db) acc[db] = zero16();
+
+  const int ctx_lo = (wl >= 0) ? max(0, qmin - wl) : 0;
+  const int ctx_t0 = (ctx_lo / BN) * BN;
+  const int n_ctx = (P > ctx_lo) ? (P - ctx_t0 + BN - 1) / BN : 0;
+  const int own_lo = (wl >= 0) ? max(0, t0 - wl) : 0;
+  const int own_t0 = (own_lo / BN) * BN;
+  const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
+  const int n_tiles = n_ctx + n_own;
+
+  const bf16 *kc_base = reinterpret_cast<const bf16 *>(a.k_ctx) + (long)g * HD;
+  const bf16 *vc_base = reinterpret_cast<const bf16 *>(a.v_ctx) + (long)g * HD;
+  const bf16 *ko_base = reinterpret_cast<const bf16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
+  const bf16 *vo_base = reinterpret_cast<const bf16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
+  const int kld_b = (int)(kld * 2);
+  DmaRows<HD, BN> dma;
+  dma.init(wave, lane, kld_b);
+  auto issue = [&](int i) {
+    char *st = smem + (i & 1) * 2 * TILE;
+    if (i < n_ctx) {
+      int s = ctx_t0 + i * BN;
+      dma.load(st, kc_base + (long)s * kld, kld_b, P - s, wave);
+      dma.load(st + TILE, vc_base + (long)s * kld, kld_b, P - s, wave);
+    } else {
+      int s = own_t0 + (i - n_ctx) * BN;
+      dma.load(st, ko_base + (long)s * kld, kld_b, seqlen - s, wave);
+      dma.load(st + TILE, vo_base + (long)s * kld, kld_b, seqlen - s, wave);
+    }
+  };
+  if (n_tiles > 0) issue(0);
+
+  for (int i = 0; i < n_tiles; ++i) {
+    int nrows, kpos0;
+    if (i < n_ctx) {
+      int s = ctx_t0 + i * BN;
+      nrows = P - s;
+      kpos0 = s;
+    } else {
+      int s = own_t0 + (i - n_ctx) * BN;
+      nrows = seqlen - s;
+      kpos0 = P + s;
+    }
+    dma_wait();
+    __syncthreads();
+    if (i + 1 < n_tiles) issue(i + 1);
+    const char *ks = smem + (i & 1) * 2 * TILE;
+    const char *vs = ks + TILE;
+
+    const char *op = role == 0 ? ks : vs;
+    f32x16 part = zero16();
+#pragma unroll
+    for (int kc = 0; kc < NKH; ++kc)
+      part = mfma(sw_frag<HD>(op, col, dh * NKH + kc, half), xf[kc], part);
+    xch_put(xch + wave * 1024, part, lane);
+    __syncthreads();
+    const f32x16 st = add16(part_of(0, wave, part, xch, lane), part_of(1, wave, part, xch, lane));
+    const f32x16 dpt = add16(part_of(2, wave, part, xch, lane), part_of(3, wave, part, xch, lane));
+
+    const bool need_mask = (nrows < BN) || (kpos0 + BN - 1 > qmin) ||
+                           (wl >= 0 && kpos0 < qmax - wl);
+    float ds[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float p = fast_exp2(fmaf(st[v], sf, -lse2));
+      if (need_mask) {
+        int kk = c_row(v, half);
+        int kp = kpos0 + kk;
+        bool vis = (kk < nrows) && (kp <= qpos) && (wl < 0 || kp >= qpos - wl);
+        if (!vis) p = 0.f;
+      }
+      ds[v] = p * (dpt[v] - Dq);
+    }
+    const bf16x8 d0 = pack8(ds), d1 = pack8(ds + 8);
+    // dQᵀ += Kᵀ dSᵀ over this wave's quarter of the head dim.
+#pragma unroll
+    for (int db = 0; db < NDQ; ++db) {
+      acc[db] = mfma(sw_tr_frag<HD>(ks, 0, dq0 + db * 32, lane), d0, acc[db]);
+      acc[db] = mfma(sw_tr_frag<HD>(ks, 16, dq0 + db * 32, lane), d1, acc[db]);
+    }
+  }
+
+  if (row_valid) {
+    bf16 *optr = reinterpret_cast<bf16 *>(a.dq) + qrow * qld + (long)h * HD + dq0;
+#pragma unroll
+    for (int db = 0; db < NDQ; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int dim = db * 32 + 8 * i + 4 * half;
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * i + e] * a.scale);
+        *reinterpret_cast<bf16x4 *>(optr + dim) = w;
+      }
+  }
+}
+
+hipError_t launch_bwd_dq_d512(const BwdQArgs &a, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_dq_d512_kernel, dim3(n), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------- dK/dV --
+
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
+  constexpr int BM = 32;                 // query rows per step
+  constexpr int TILE = BM * HD * 2;      // 32 KB: one row per 1 KB DMA block
+  constexpr int NKH = HD / 2 / 16;
+  constexpr int NDQ = HD / 4 / 32;
+  constexpr int RPW = BM / 4;            // rows each wave fetches per step
+  constexpr int STAGE = 2 * TILE + 2 * 64 * 4;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE + 4 * 4096];
+  float *xch = reinterpret_cast<float *>(smem + 2 * STAGE);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int role = wave >> 1, dh = wave & 1;   // role 0: partial S with K; 1: partial dP with V
+  const KVItem it = a.items[blockIdx.x];
+  const int g = it.g, G = a.G, P = a.ctx_len, wl = a.window_left;
+  const bool ctx = it.region == kRegionCtx;
+  const long qld = (long)a.Hq * HD;
+  const long kld = (long)a.Hkv * HD;
+  const int own0 = ctx ? 0 : a.cu[it.seq_lo];
+  const int nkeys = ctx ? P - it.key_start : a.cu[it.seq_lo + 1] - own0 - it.key_start;
+  const int kbase = ctx ? 0 : P;
+  const int nk_tile = min(kBwdBN512, nkeys);
+
+  const int key = col;
+  const bool key_valid = key < nkeys;
+  const float sf = a.scale * kLog2e;
+  const bf16 *xp = reinterpret_cast<const bf16 *>(
+                       role == 0 ? (ctx ? a.k_ctx : a.k_own) : (ctx ? a.v_ctx : a.v_own)) +
+                   (long)(own0 + it.key_start + (key_valid ? key : 0)) * kld + (long)g * HD +
+                   dh * (HD / 2);
+  bf16x8 xf[NKH];
+#pragma unroll
+  for (int kc = 0; kc < NKH; ++kc) {
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    xf[kc] = as_bf16x8(key_valid ? *reinterpret_cast<const uint4 *>(xp + kc * 16 + half * 8) : z);
+  }
+  const int kpos = kbase + it.key_start + key;
+  const int f_vis_lo = key_valid ? max(0, (kpos - P) * G) : 0x7fffffff;
+  const int f_vis_hi = (wl >= 0) ? max(0, (kpos + wl - P + 1) * G) : 0x7fffffff;
+  const int dq0 = wave * (HD / 4);
+
+  f32x16 dk[NDQ], dv[NDQ];
+#pragma unroll
+  for (int db = 0; db < NDQ; ++db) {
+    dk[db] = zero16();
+    dv[db] = zero16();
+  }
+
+  auto seq_range = [&](int sq, int &fa, int &fb) {
+    int len = a.cu[sq + 1] - a.cu[sq];
+    int r_lo, r_hi;
+    if (ctx) {
+      r_lo = 0;
+      r_hi = len;
+      if (wl >= 0) r_hi = min(len, it.key_start + nk_tile - 1 + wl - P + 1);
+    } else {
+      r_lo = it.key_start;
+      r_hi = len;
+      if (wl >= 0) r_hi = min(len, it.key_start + nk_tile - 1 + wl + 1);
+    }
+    fa = r_lo * G;
+    fb = r_hi > r_lo ? r_hi * G : fa;
+  };
+  // Steps of BM flattened rows, walked from the last one backward.
+  int cs = it.seq_hi - 1, cf = 0, cfa = 0, cfb = 0;
+  bool done = false;
+  auto seek = [&]() {
+    while (cs >= it.seq_lo) {
+      int fa, fb;
+      seq_range(cs, fa, fb);
+      if (fb > fa) {
+        cfa = fa;
+        cfb = fb;
+        cf = ((fb - 1) / BM) * BM;
+        return;
+      }
+      --cs;
+    }
+    done = true;
+  };
+  seek();
+
+  const int qld_b = (int)(qld * 2);
+  const int head0_b = g * G * HD * 2;
+  const __amdgpu_buffer_rsrc_t r_ld = make_rsrc_u(wave == 0 ? (const void *)a.lse : (const void *)a.D,
+                                                  (uint32_t)((long)a.Hq * a.lse_ld * 4));
+  // Fetch the step at the cursor into stage `st`: row r of the step (a flattened
+  // (token, head) row) fills 1 KB block r, written by wave r % 4.
+  auto issue = [&](char *st) {
+    const int s0 = a.cu[cs];
+    const int len = a.cu[cs + 1] - s0;
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc_u(reinterpret_cast<const bf16 *>(a.q) + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
+    const __amdgpu_buffer_rsrc_t rd =
+        make_rsrc_u(reinterpret_cast<const bf16 *>(a.dout) + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
+    const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_u32(st) + wave * 1024);
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+      const int r = k * 4 + wave;
+      const int f = cf + r;
+      const int t = f / G, j = f - t * G;
+      const int off = t * qld_b + head0_b + j * (HD * 2) + ((lane ^ Swz<HD>::swz(r)) << 4);
+      dma16(rq, l0 + k * 4096, off);
+      dma16(rd, l0 + TILE + k * 4096, off);
+    }
+    if (wave < 2) {   // LSE (wave 0) and D (wave 1) of the step's rows; lanes >= BM read nothing
+      const int f = cf + lane;
+      const int t = f / G, j = f - t * G;
+      const int off = lane < BM ? ((g * G + j) * a.lse_ld + s0 + t) * 4 : 0x7fffffff;
+      const uint32_t la = __builtin_amdgcn_readfirstlane(lds_u32(st + 2 * TILE) + wave * 256);
+      dma4(r_ld, la, off);
+    }
+  };
+
+  int nf0 = 0, nflo = 0, nfend = 0;
+  auto advance = [&]() {
+    nf0 = cf;
+    nflo = max(cf, cfa);
+    nfend = min(cf + BM, cfb);
+    cf -= BM;
+    if (cf + BM <= cfa) {
+      --cs;
+      seek();
+    }
+  };
+  int stage = 0;
+  bool have = !done;
+  int f0 = 0, flo = 0, fend = 0;
+  if (have) {
+    issue(smem);
+    advance();
+    f0 = nf0, flo = nflo, fend = nfend;
+  }
+
+  const int kpa = kbase + it.key_start;
+  const int kpb = kbase + it.key_start + min(32, nkeys) - 1;
+  while (have) {
+    dma_wait();
+    __syncthreads();
+    const bool more = !done;
+    int g0 = 0, glo = 0, gend = 0;
+    if (more) {
+      issue(smem + (stage ^ 1) * STAGE);
+      advance();
+      g0 = nf0, glo = nflo, gend = nfend;
+    }
+    const char *qs = smem + stage * STAGE;
+    const char *dos = qs + TILE;
+    const float *lse_s = reinterpret_cast<const float *>(qs + 2 * TILE);
+    const float *d_s = lse_s + 64;
+
+    const char *op = role == 0 ? qs : dos;
+    f32x16 part = zero16();
+#pragma unroll
+    for (int kc = 0; kc < NKH; ++kc)
+      part = mfma(sw_frag<HD>(op, col, dh * NKH + kc, half), xf[kc], part);
+    xch_put(xch + wave * 1024, part, lane);
+    __syncthreads();
+    const f32x16 st = add16(part_of(0, wave, part, xch, lane), part_of(1, wave, part, xch, lane));
+    const f32x16 dpt = add16(part_of(2, wave, part, xch, lane), part_of(3, wave, part, xch, lane));
+
+    const int ta = flo / G, tb = (fend - 1) / G;
+    const bool full = (f0 >= flo) && (f0 + BM <= fend) && (32 <= nkeys) &&
+                      (kpb <= P + ta) && (wl < 0 || kpa >= P + tb - wl);
+    const int vlo = max(flo, f_vis_lo), vhi = min(fend, f_vis_hi);
+    float pv[16], dsv[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 l4 = *reinterpret_cast<const float4 *>(lse_s + 8 * i + 4 * half);
+      const float4 d4 = *reinterpret_cast<const float4 *>(d_s + 8 * i + 4 * half);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = 4 * i + e;
+        float p = fast_exp2(fmaf(st[v], sf, -lv[e] * kLog2e));
+        if (!full) {
+          const int f = f0 + c_row(v, half);
+          if (f < vlo || f >= vhi) p = 0.f;
+        }
+        pv[v] = p;
+        dsv[v] = p * (dpt[v] - dd[e]);
+      }
+    }
+    const bf16x8 p0 = pack8(pv), p1 = pack8(pv + 8);
+    const bf16x8 s0 = pack8(dsv), s1 = pack8(dsv + 8);
+    // dV += Pᵀ dO and dK += dSᵀ Q over this wave's quarter of the head dim.
+#pragma unroll
+    for (int db = 0; db < NDQ; ++db) {
+      dv[db] = mfma(p0, sw_tr_frag<HD>(dos, 0, dq0 + db * 32, lane), dv[db]);
+      dv[db] = mfma(p1, sw_tr_frag<HD>(dos, 16, dq0 + db * 32, lane), dv[db]);
+      dk[db] = mfma(s0, sw_tr_frag<HD>(qs, 0, dq0 + db * 32, lane), dk[db]);
+      dk[db] = mfma(s1, sw_tr_frag<HD>(qs, 16, dq0 + db * 32, lane), dk[db]);
+    }
+    have = more;
+    f0 = g0, flo = glo, fend = gend;
+    stage ^= 1;
+  }
+
+  const bool to_acc = ctx || a.own_to_acc;
+#pragma unroll
+  for (int db = 0; db < NDQ; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int k = c_row(v, half);
+      if (k >= nkeys) continue;
+      const long off = (long)(own0 + it.key_start + k) * kld + (long)g * HD + dq0 + db * 32 + col;
+      const float gk = dk[db][v] * a.scale;
+      const float gv = dv[db][v];
+      if (to_acc) {
+        atomicAdd(a.acc_dk + off, gk);
+        atomicAdd(a.acc_dv + off, gv);
+      } else {
+        reinterpret_cast<bf16 *>(a.dk_own)[off] = (bf16)gk;
+        reinterpret_cast<bf16 *>(a.dv_own)[off] = (bf16)gv;
+      }
+    }
+}
+
+hipError_t launch_bwd_dkdv_d512(const BwdKVArgs &a, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_dkdv_d512_kernel, dim3(n), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace dkv

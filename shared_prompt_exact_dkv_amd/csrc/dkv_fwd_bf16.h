@@ -1,0 +1,200 @@
+// dkv_fwd_bf16.h -- the bf16 forward kernel template ("DualKV", arXiv 2605.15422,
+// §3.1): one online softmax over the shared-prompt KV region then the sequence's own
+// region.  Instantiated for head dims 64 / 128 in dkv_fwd.hip and 512 in
+// dkv_d512.hip (built with different register-placement options).
+#pragma once
+
+#include "dkv_device.h"
+#include "dkv_launch.h"
+#include "dkv_tiles.h"
+
+namespace dkv {
+
+// ------------------------------------------------------------- bf16 kernel --
+//
+// The bf16 path for head dims 64 and 128 (HD = 512 has its own kernels): 64-key
+// tiles at two waves per SIMD (WPE = 2, <= 256 registers).
+//   - K and V tiles both in the padded row layout, double-buffered in LDS with one
+//     barrier per tile; the next-but-one tile's global loads are in flight in
+//     registers while the current tile is computed.
+//   - Vᵀ (the A operand of Oᵀ += Vᵀ Pᵀ) comes straight from the row-layout tile
+//     through the gfx950 transpose read, in the key order of the Sᵀ accumulator.
+//   - The softmax scale is folded into the exponent (one FMA per score), and the
+//     output is rescaled only when a row's running maximum grows by more than
+//     kSlack (log2 units): between rescales the probabilities are exp2(t - m) with
+//     m at most kSlack below the true running maximum, i.e. bounded by 2^kSlack,
+//     and O / l and LSE = m + log2(l) are unchanged in exact arithmetic.
+template <int HD, int BN, int WPE>
+__global__ __launch_bounds__(256, WPE) void fwd_bf16_kernel(FwdArgs a) {
+  constexpr int TILE = BN * HD * 2;     // dense swizzled tile
+  constexpr int NKC = HD / 16;     // MFMA steps over the head dim
+  constexpr int NDB = HD / 32;     // 32-wide blocks of the output head dim
+  constexpr int NKB = BN / 32;     // 32-key blocks per tile
+  constexpr float kSlack = 8.f;
+  __shared__ __attribute__((aligned(16))) char smem[2][2 * TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const QItem it = a.items[blockIdx.x];
+  const int g = it.g, seq0 = it.seq_start, seqlen = it.seq_len;
+  const int t0 = it.tile * a.bm_tok;
+  const int nt = min(a.bm_tok, seqlen - t0);
+
+  const int qr = wave * 32 + col;
+  int tok = qr / a.G;
+  const int hj = qr - tok * a.G;
+  const bool row_valid = tok < nt;
+  if (!row_valid) tok = nt - 1;   // computes a duplicate of a valid row, never stored
+  const int h = g * a.G + hj;
+  const int P = a.ctx_len, wl = a.window_left;
+  const int qpos = P + t0 + tok;
+  const int qmin = P + t0, qmax = P + t0 + nt - 1;
+
+  const long qld = (long)a.Hq * HD;
+  const long kld = (long)a.Hkv * HD;
+  const bf16 *qptr = reinterpret_cast<const bf16 *>(a.q) + (long)(seq0 + t0 + tok) * qld + (long)h * HD;
+  bf16x8 qf[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc)
+    qf[kc] = as_bf16x8(*reinterpret_cast<const uint4 *>(qptr + kc * 16 + half * 8));
+
+  const float sf = a.scale * kLog2e;
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = zero16();
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int ctx_lo = (wl >= 0) ? max(0, qmin - wl) : 0;
+  const int ctx_t0 = (ctx_lo / BN) * BN;
+  const int n_ctx = (P > ctx_lo) ? (P - ctx_t0 + BN - 1) / BN : 0;
+  const int own_lo = (wl >= 0) ? max(0, t0 - wl) : 0;
+  const int own_t0 = (own_lo / BN) * BN;
+  const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
+  const int n_tiles = n_ctx + n_own;
+
+  const bf16 *kc_base = reinterpret_cast<const bf16 *>(a.k_ctx) + (long)g * HD;
+  const bf16 *vc_base = reinterpret_cast<const bf16 *>(a.v_ctx) + (long)g * HD;
+  const bf16 *ko_base = reinterpret_cast<const bf16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
+  const bf16 *vo_base = reinterpret_cast<const bf16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
+
+  const int kld_b = (int)(kld * 2);
+  DmaRows<HD, BN> dma;
+  dma.init(wave, lane, kld_b);
+  auto issue = [&](int i) {   // tile i -> stage i % 2
+    char *st = smem[i & 1];
+    if (i < n_ctx) {
+      int s = ctx_t0 + i * BN;
+      dma.load(st, kc_base + (long)s * kld, kld_b, P - s, wave);
+      dma.load(st + TILE, vc_base + (long)s * kld, kld_b, P - s, wave);
+    } else {
+      int s = own_t0 + (i - n_ctx) * BN;
+      dma.load(st, ko_base + (long)s * kld, kld_b, seqlen - s, wave);
+      dma.load(st + TILE, vo_base + (long)s * kld, kld_b, seqlen - s, wave);
+    }
+  };
+  if (n_tiles > 0) issue(0);
+
+  for (int i = 0; i < n_tiles; ++i) {
+    int nrows, kpos0;
+    if (i < n_ctx) {
+      int s = ctx_t0 + i * BN;
+      nrows = P - s;
+      kpos0 = s;
+    } else {
+      int s = own_t0 + (i - n_ctx) * BN;
+      nrows = seqlen - s;
+      kpos0 = P + s;
+    }
+    // Tile i has landed in stage i % 2 and every wave is done with tile i - 1, whose
+    // stage receives tile i + 1 while tile i is computed.
+    dma_wait();
+    __syncthreads();
+    if (i + 1 < n_tiles) issue(i + 1);
+    const char *ks = smem[i & 1];
+    const char *vs = smem[i & 1] + TILE;
+
+    // Sᵀ = K Qᵀ for this wave's 32 query rows (raw scores).
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        s[kb] = mfma(sw_frag<HD>(ks, kb * 32 + col, kc, half), qf[kc], s[kb]);
+    }
+
+    const bool need_mask = (nrows < BN) || (kpos0 + BN - 1 > qmin) ||
+                           (wl >= 0 && kpos0 < qmax - wl);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          int kk = kb * 32 + c_row(v, half);
+          int kp = kpos0 + kk;
+          bool vis = (kk < nrows) && (kp <= qpos) && (wl < 0 || kp >= qpos - wl);
+          if (!vis) s[kb][v] = -INFINITY;
+        }
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+    mx = fmaxf(mx, wave_xor32(mx)) * sf;
+    const bool grow = mx > m_run + kSlack;
+    if (__any(grow)) {
+      const float alpha = grow ? fast_exp2(m_run - mx) : 1.f;
+      if (grow) m_run = mx;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float rs = 0.f;
+    bf16x8 pf[2 * NKB];
+#pragma unroll
+    for (int u = 0; u < 2 * NKB; ++u) {
+      float t[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        t[e] = fast_exp2(fmaf(s[u >> 1][8 * (u & 1) + e], sf, -m_use));
+        rs += t[e];
+      }
+      pf[u] = pack8(t);
+    }
+    l_run += rs;
+
+    // Oᵀ += Vᵀ Pᵀ.
+#pragma unroll
+    for (int u = 0; u < 2 * NKB; ++u)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        acc[db] = mfma(sw_tr_frag<HD>(vs, 16 * u, db * 32, lane), pf[u], acc[db]);
+      }
+  }
+
+  const float l = l_run + wave_xor32(l_run);
+  const float inv = 1.f / l;
+  if (row_valid) {
+    bf16 *optr = reinterpret_cast<bf16 *>(a.o) + (long)(seq0 + t0 + tok) * qld + (long)h * HD;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int dim = db * 32 + 8 * i + 4 * half;
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * i + e] * inv);
+        *reinterpret_cast<bf16x4 *>(optr + dim) = w;
+      }
+    if (half == 0)
+      a.lse[(long)h * a.lse_ld + seq0 + t0 + tok] = (m_run + fast_log2(l)) * kLn2;
+  }
+}
+
+}  // namespace dkv

@@ -14,6 +14,12 @@ static constexpr int kRowsPerWG = 128;
 // Key rows per dK/dV workgroup (4 waves x 32 keys) and query rows per step.
 static constexpr int kBwdBN = 128;
 static constexpr int kBwdBM = 32;
+// Head dim 512 (the head dim is split across the waves of a workgroup): query rows
+// per forward workgroup (two pairs of waves), query rows per dQ workgroup and keys
+// per dK/dV workgroup (four waves each).
+static constexpr int kFwdRows512 = 64;
+static constexpr int kRowsPerWG512 = 32;
+static constexpr int kBwdBN512 = 32;
 
 // Work item of the query-parallel kernels (forward, dQ).
 struct QItem {
@@ -36,6 +42,7 @@ struct FwdArgs {
 };
 
 hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs &a, int n_items, hipStream_t s);
+hipError_t launch_fwd_d512(const FwdArgs &a, int n_items, hipStream_t s);
 
 // ---- backward ----
 
@@ -55,6 +62,7 @@ struct BwdQArgs {
   float scale;
 };
 hipError_t launch_bwd_dq(int dtype, int head_dim, const BwdQArgs &a, int n_items, hipStream_t s);
+hipError_t launch_bwd_dq_d512(const BwdQArgs &a, int n_items, hipStream_t s);
 
 // Work item of the key-parallel dK/dV kernel: one key tile of one region of one kv
 // head, against the query rows of sequences [seq_lo, seq_hi).
@@ -80,5 +88,6 @@ struct BwdKVArgs {
 };
 hipError_t launch_bwd_dkdv(int dtype, int head_dim, const BwdKVArgs &a, int n_items,
                            hipStream_t s);
+hipError_t launch_bwd_dkdv_d512(const BwdKVArgs &a, int n_items, hipStream_t s);
 
 }  // namespace dkv

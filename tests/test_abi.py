@@ -39,6 +39,8 @@ FAKE = 0x10000   # 16-byte aligned, never dereferenced: validation fails first
     (dict(ctx_len=-1), L.DKV_ERR_INVALID_ARG, "ctx_len"),
     (dict(cu_dev=0), L.DKV_ERR_INVALID_ARG, "cu_seqlens_dev"),
     (dict(softmax_scale=float("nan")), L.DKV_ERR_INVALID_ARG, "scale"),
+    (dict(head_dim=512, dtype=L.DKV_FP32), L.DKV_ERR_UNSUPPORTED, "bf16 only"),
+    (dict(head_dim=512, num_heads_q=64, num_heads_kv=1), L.DKV_ERR_UNSUPPORTED, "head_dim 512"),
 ])
 def test_fwd_rejects_invalid_params(kw, status, frag):
     p, keep = _params(**kw)
@@ -77,6 +79,17 @@ def test_workspace_checks():
     bad, keep2 = _params(head_dim=3)
     assert lib.dkv_workspace_size(bad, L.DKV_CALL_FWD) == ctypes.c_size_t(-1).value
     assert lib.dkv_workspace_size(p, 99) == ctypes.c_size_t(-1).value
+
+
+def test_head_dim_512_workspace():
+    # d = 512 uses its own tile sizes (64 forward rows, 32 dQ rows, 32 keys per
+    # workgroup), so its work lists are longer than at d = 128 for the same shape.
+    p128, k1 = _params(cu_host=[0, 300, 700], num_heads_q=16, num_heads_kv=4)
+    p512, k2 = _params(cu_host=[0, 300, 700], num_heads_q=16, num_heads_kv=4, head_dim=512)
+    lib = L.lib()
+    for call in (L.DKV_CALL_FWD, L.DKV_CALL_BWD):
+        a, b = lib.dkv_workspace_size(p128, call), lib.dkv_workspace_size(p512, call)
+        assert 0 < a < b < (1 << 24)
 
 
 def test_empty_batch_is_a_no_op():

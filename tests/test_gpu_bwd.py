@@ -32,6 +32,12 @@ CASES = [
     (97, [120, 33], 4, 2, 128, 0, "bf16", False),
     (300, [140, 260, 1], 8, 2, 128, 200, "bf16", False),
     (5, [3, 2, 1], 1, 1, 64, -1, "bf16", False),
+    # head dim 512 (the hybrid-layer workload's GQA 4:1 included)
+    (70, [45, 100], 8, 2, 512, -1, "bf16", False),
+    (40, [70, 9], 16, 4, 512, -1, "bf16", True),
+    (129, [33, 64, 1], 4, 1, 512, 40, "bf16", False),
+    (100, [150, 20], 16, 4, 512, 63, "bf16", False),
+    (0, [80], 4, 4, 512, -1, "bf16", False),
 ]
 
 
