@@ -61,7 +61,11 @@ def _load():
                                                  _dp, _dp, _dp]
         lib.oracle_bwd_keys.argtypes = common + [_dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int,
                                                  _ip, _dp, _dp]
-        for f in (lib.oracle_fwd_rows, lib.oracle_bwd_rows, lib.oracle_bwd_keys):
+        lib.oracle_bwd_scatter.argtypes = common + [_dp, _dp, ctypes.c_int, _ip, _dp, _dp,
+                                                    _dp, _dp, _dp]
+        lib.oracle_fwd_sel.argtypes = common + [_dp, _dp, ctypes.c_int, _ip, _dp, _dp, _dp]
+        for f in (lib.oracle_fwd_rows, lib.oracle_bwd_rows, lib.oracle_bwd_keys,
+                  lib.oracle_bwd_scatter, lib.oracle_fwd_sel):
             f.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -238,3 +242,51 @@ def ncopy_reference(x: dict, *, do_copies=None, scale=None, window_left=-1, kvh=
     if keep_copies:
         res["copies"] = copies
     return res
+
+
+def rows_fwd(k, v, rows, q_rows, *, scale=None, window_left=-1, kvh=None):
+    """Eq. (2) at selected positions ``rows`` of one sequence whose keys / values are
+    ``k`` / ``v`` [S, Hkv, d]; ``q_rows`` [n, Hq, d] are those rows' queries.
+    -> (o [n, Hq, d], lse [n, Hq])."""
+    k, v, qs = _f64(k), _f64(v), _f64(q_rows)
+    S, Hkv, d = k.shape
+    Hq = qs.shape[1]
+    scale = default_scale(d) if scale is None else float(scale)
+    kv = _kvh(Hq, Hkv, kvh)
+    sel = _i32(rows)
+    o = np.zeros((len(sel), Hq, d))
+    lse = np.zeros((len(sel), Hq))
+    if len(sel):
+        rc = _load().oracle_fwd_sel(S, Hq, Hkv, d, _ptr(kv, _ip), int(window_left), scale,
+                                    _ptr(k, _dp), _ptr(v, _dp), len(sel), _ptr(sel, _ip),
+                                    _ptr(qs, _dp), _ptr(o, _dp), _ptr(lse, _dp))
+        if rc != 0:
+            raise ValueError("oracle_fwd_sel failed (%d)" % rc)
+    return o, lse
+
+
+def rows_bwd_scatter(k, v, rows, q_rows, dout_rows, dk, dv, *, scale=None, window_left=-1,
+                     kvh=None):
+    """Gradients of eq. (2) for one sequence whose upstream gradient is zero except at
+    positions ``rows`` (queries ``q_rows``, gradients ``dout_rows``, [n, Hq, d]).
+    Adds the key / value gradients into ``dk`` / ``dv`` (float64 [S, Hkv, d], modified
+    in place) and returns dq [n, Hq, d] for those rows (every other row's dq is 0)."""
+    k, v = _f64(k), _f64(v)
+    qs, ds = _f64(q_rows), _f64(dout_rows)
+    S, Hkv, d = k.shape
+    Hq = qs.shape[1]
+    assert dk.dtype == np.float64 and dk.flags.c_contiguous and dk.shape == k.shape
+    assert dv.dtype == np.float64 and dv.flags.c_contiguous and dv.shape == k.shape
+    scale = default_scale(d) if scale is None else float(scale)
+    kv = _kvh(Hq, Hkv, kvh)
+    sel = _i32(rows)
+    dq = np.zeros((len(sel), Hq, d))
+    if len(sel):
+        rc = _load().oracle_bwd_scatter(S, Hq, Hkv, d, _ptr(kv, _ip), int(window_left), scale,
+                                        _ptr(k, _dp), _ptr(v, _dp), len(sel), _ptr(sel, _ip),
+                                        _ptr(qs, _dp), _ptr(ds, _dp), _ptr(dq, _dp),
+                                        _ptr(dk, _dp), _ptr(dv, _dp))
+        if rc != 0:
+            raise ValueError("oracle_bwd_scatter failed (%d)" % rc)
+    return dq
+

@@ -259,3 +259,137 @@ int oracle_bwd_keys(int S, int Hq, int Hkv, int d, const int *kvh, int window_le
         }
     return 0;
 }
+
+/*
+ * Backward contributions of a few query rows, for an upstream gradient that is zero
+ * on every other row.  For each selected row tsel[n] (its query q_sel[n] and
+ * upstream gradient dout_sel[n], [nsel, Hq, d]) and q-head h, over the visible keys
+ * j of that row in a sequence with keys k / values v ([S, Hkv, d]):
+ *   p_j = softmax_j(scale <q, k_j>),  dP_j = <dO, v_j>,  delta = sum_j p_j dP_j,
+ *   dS_j = p_j (dP_j - delta)
+ *   dq[n, h]        = scale * sum_j dS_j k_j        (written)
+ *   dk[j, kvh[h]]  += scale * dS_j q                (added)
+ *   dv[j, kvh[h]]  += p_j dO                         (added)
+ * The same chain rule as oracle_bwd_rows / oracle_bwd_keys, restricted to the rows
+ * whose upstream gradient is non-zero (rows with dO = 0 add nothing).  Rows are taken
+ * one at a time; the keys of a row are split over threads, so no two threads add to
+ * the same key.
+ */
+int oracle_bwd_scatter(int S, int Hq, int Hkv, int d, const int *kvh, int window_left,
+                       double scale, const double *k, const double *v, int nsel,
+                       const int *tsel, const double *q_sel, const double *dout_sel,
+                       double *dq, double *dk, double *dv)
+{
+    int rc = check_args(S, Hq, Hkv, d, kvh);
+    if (rc)
+        return rc;
+    for (int n = 0; n < nsel; ++n)
+        if (tsel[n] < 0 || tsel[n] >= S)
+            return -3;
+    double *s = (double *)malloc(sizeof(double) * 2 * (size_t)(S > 0 ? S : 1));
+    if (!s)
+        return -4;
+    double *dp = s + S;
+    for (int n = 0; n < nsel; ++n) {
+        const int t = tsel[n];
+        int j0, j1;
+        visible_range(t, window_left, &j0, &j1);
+        const int cnt = j1 - j0 + 1;
+        for (int h = 0; h < Hq; ++h) {
+            const int g = kvh[h];
+            const double *qt = q_sel + ((size_t)n * Hq + h) * d;
+            const double *dot_ = dout_sel + ((size_t)n * Hq + h) * d;
+#pragma omp parallel for schedule(static)
+            for (int i = 0; i < cnt; ++i) {
+                s[i] = scale * dot(qt, k + ((size_t)(j0 + i) * Hkv + g) * d, d);
+                dp[i] = dot(dot_, v + ((size_t)(j0 + i) * Hkv + g) * d, d);
+            }
+            double m = -INFINITY;
+            for (int i = 0; i < cnt; ++i)
+                if (s[i] > m)
+                    m = s[i];
+            double l = 0.0;
+            for (int i = 0; i < cnt; ++i)
+                l += exp(s[i] - m);
+            double delta = 0.0;
+            for (int i = 0; i < cnt; ++i) {
+                s[i] = exp(s[i] - m) / l;          /* p_j */
+                delta += s[i] * dp[i];
+            }
+            double *dqt = dq + ((size_t)n * Hq + h) * d;
+            for (int c = 0; c < d; ++c)
+                dqt[c] = 0.0;
+            for (int i = 0; i < cnt; ++i) {
+                const double ds = s[i] * (dp[i] - delta);
+                const double *kj = k + ((size_t)(j0 + i) * Hkv + g) * d;
+                for (int c = 0; c < d; ++c)
+                    dqt[c] += scale * ds * kj[c];
+            }
+#pragma omp parallel for schedule(static)
+            for (int i = 0; i < cnt; ++i) {
+                const double ds = s[i] * (dp[i] - delta);
+                double *dkj = dk + ((size_t)(j0 + i) * Hkv + g) * d;
+                double *dvj = dv + ((size_t)(j0 + i) * Hkv + g) * d;
+                for (int c = 0; c < d; ++c) {
+                    dkj[c] += scale * ds * qt[c];
+                    dvj[c] += s[i] * dot_[c];
+                }
+            }
+        }
+    }
+    free(s);
+    return 0;
+}
+
+/*
+ * Forward rows as oracle_fwd_rows, with the queries of the selected rows given on
+ * their own (q_sel [nsel, Hq, d]) so that long sequences need not be materialized:
+ * row n sits at position tsel[n] of a sequence with keys k / values v [S, Hkv, d].
+ */
+int oracle_fwd_sel(int S, int Hq, int Hkv, int d, const int *kvh, int window_left,
+                   double scale, const double *k, const double *v, int nsel,
+                   const int *tsel, const double *q_sel, double *o, double *lse)
+{
+    int rc = check_args(S, Hq, Hkv, d, kvh);
+    if (rc)
+        return rc;
+    for (int n = 0; n < nsel; ++n)
+        if (tsel[n] < 0 || tsel[n] >= S)
+            return -3;
+    int bad = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int n = 0; n < nsel; ++n)
+        for (int h = 0; h < Hq; ++h) {
+            const int t = tsel[n];
+            double *p = (double *)malloc(sizeof(double) * (size_t)(t + 1));
+            if (!p) {
+                bad = 1;
+                continue;
+            }
+            int j0, j1;
+            visible_range(t, window_left, &j0, &j1);
+            const int cnt = j1 - j0 + 1, g = kvh[h];
+            const double *qt = q_sel + ((size_t)n * Hq + h) * d;
+            double m = -INFINITY;
+            for (int i = 0; i < cnt; ++i) {
+                p[i] = scale * dot(qt, k + ((size_t)(j0 + i) * Hkv + g) * d, d);
+                if (p[i] > m)
+                    m = p[i];
+            }
+            double l = 0.0;
+            for (int i = 0; i < cnt; ++i)
+                l += exp(p[i] - m);
+            double *ot = o + ((size_t)n * Hq + h) * d;
+            for (int c = 0; c < d; ++c)
+                ot[c] = 0.0;
+            for (int i = 0; i < cnt; ++i) {
+                const double w = exp(p[i] - m) / l;
+                const double *vj = v + ((size_t)(j0 + i) * Hkv + g) * d;
+                for (int c = 0; c < d; ++c)
+                    ot[c] += w * vj[c];
+            }
+            lse[(size_t)n * Hq + h] = m + log(l);
+            free(p);
+        }
+    return bad ? -4 : 0;
+}

@@ -1,0 +1,145 @@
+"""GPU parity at the full workload sizes, through the same calls (and therefore the same
+kernels, work lists and launch shapes) that bench.py times.
+
+The oracle cannot run a whole full-size backward, so the upstream gradient is made
+sparse: dO is zero except on a few response rows of a few sequences and a few prompt
+rows.  Every key / value gradient -- including the shared dK_P / dV_P summed over all
+N sequences and both calls (eq. (6)) -- is then a sum over those rows only, which
+the oracle computes exactly for ALL keys; dQ must match on the selected rows and be
+zero elsewhere.  O and LSE are checked on sampled rows of the prompt and of the
+sampled sequences.  The kernels do the same work whatever the values, so this
+exercises the full-size paths completely.
+
+In the N-copy packing (eq. (1)) each copy i gets its own prompt-row gradient; here
+dO_P^(i) = dO_P / N for every copy (a valid instance: they sum to the single prompt
+copy's dO_P, Appendix A.5), and the oracle adds the N copies' terms one by one.
+
+Tolerance (bf16 inputs): max|err| <= 2e-2 * max|ref| per tensor.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import shared_prompt_exact_dkv_amd as dkv
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+REL = 2e-2
+
+
+def _rows(n, extra=()):
+    """A few rows of a length-n range: ends, middle and the given extras."""
+    return sorted({r for r in (0, 1, n // 2, n - 2, n - 1, *extra) if 0 <= r < n})
+
+
+def _check(name, got, ref, bound=None):
+    g = got.detach().float().cpu().numpy().astype(np.float64) if isinstance(got, torch.Tensor) else got
+    assert g.shape == ref.shape, (name, g.shape, ref.shape)
+    assert np.isfinite(g).all(), name + ": non-finite values"
+    b = REL * float(np.abs(ref).max()) if bound is None else bound
+    err = float(np.abs(g - ref).max())
+    print("    %-18s max|err| %.3e  bound %.3e" % (name, err, b), flush=True)
+    assert err <= b, "%s: max|err| = %.3e > %.3e" % (name, err, b)
+
+
+@pytest.mark.parametrize("name", ["qwen3_8b", "dapo_varlen", "large_rollout", "d512_global",
+                                  "d512_swa"])
+def test_full_size_parity(name):
+    w = workloads.WORKLOADS[name]
+    lens = w.resp_lens()
+    N, P, Hq, Hkv, d, wl = w.N, w.P, w.Hq, w.Hkv, w.d, w.window_left
+    print("[full] %s: P=%d N=%d Hq=%d Hkv=%d d=%d wl=%d T=%d" % (name, P, N, Hq, Hkv, d, wl,
+                                                                 sum(lens)), flush=True)
+    x = workloads.make_inputs(P, lens, Hq, Hkv, d, "bf16", seed=w.seed, scaled=w.scaled,
+                              dout=False)
+    cu = [int(c) for c in x["cu"]]
+    T = cu[-1]
+
+    # Sampled sequences (first, last, longest, shortest) and their rows with dO != 0.
+    seqs = sorted({0, N - 1, int(np.argmax(lens)), int(np.argmin(lens))})
+    wl_extra = (wl - 1, wl, wl + 1) if wl >= 0 else ()
+    resp_rows = {i: _rows(lens[i], wl_extra) for i in seqs}
+    p_rows = _rows(P, tuple(P - 1 - e for e in wl_extra))
+    g = torch.Generator().manual_seed(7000 + w.seed)
+    do_p = torch.zeros((P, Hq, d))
+    do_r = torch.zeros((T, Hq, d))
+    do_p[p_rows] = torch.randn((len(p_rows), Hq, d), generator=g).to(torch.bfloat16).float()
+    for i in seqs:
+        idx = [cu[i] + r for r in resp_rows[i]]
+        do_r[idx] = torch.randn((len(idx), Hq, d), generator=g).to(torch.bfloat16).float()
+
+    # ---- GPU: Call 1 + Call 2 forward and backward, one shared fp32 accumulator ----
+    t = {k: x[k].to(torch.bfloat16).to(DEV) for k in ("q_p", "k_p", "v_p", "q_r", "k_r", "v_r")}
+    cu_d = x["cu"].to(DEV)
+    o_p, lse_p, o_r, lse_r = dkv.dualkv_forward(t["q_p"], t["k_p"], t["v_p"], t["q_r"], t["k_r"],
+                                                t["v_r"], cu_d, cu_host=cu, window_left=wl)
+    gr = dkv.dualkv_backward(t["q_p"], t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], o_p,
+                             lse_p, o_r, lse_r, do_p.to(torch.bfloat16).to(DEV),
+                             do_r.to(torch.bfloat16).to(DEV), cu_d, cu_host=cu, window_left=wl)
+    torch.cuda.synchronize()
+    print("[full] %s: GPU done" % name, flush=True)
+
+    # ---- oracle ----
+    f64 = lambda a: np.ascontiguousarray(a.numpy(), dtype=np.float64)
+    k_p, v_p = f64(x["k_p"]), f64(x["v_p"])
+    # forward: prompt rows (a copy's prompt prefix) and the sampled sequences' rows
+    o_ref, lse_ref = oracle.rows_fwd(k_p, v_p, p_rows, x["q_p"][p_rows], window_left=wl)
+    _check("o_p[rows]", o_p[p_rows], o_ref)
+    _check("lse_p[rows]", lse_p[:, p_rows].t(), lse_ref, bound=2e-3)
+    dk_p_ref = np.zeros((P, Hkv, d))
+    dv_p_ref = np.zeros((P, Hkv, d))
+    # prompt rows of every copy: dO_P^(i) = dO_P / N
+    dq_p_ref = np.zeros((len(p_rows), Hq, d))
+    for _ in range(N):
+        dq_p_ref += oracle.rows_bwd_scatter(k_p, v_p, p_rows, x["q_p"][p_rows],
+                                            f64(do_p[p_rows]) / N, dk_p_ref, dv_p_ref,
+                                            window_left=wl)
+    dk_r_ref = {}
+    for i in seqs:
+        a, b = cu[i], cu[i + 1]
+        k_i = np.concatenate([k_p, f64(x["k_r"][a:b])])
+        v_i = np.concatenate([v_p, f64(x["v_r"][a:b])])
+        rows = resp_rows[i]
+        idx = [a + r for r in rows]
+        o_ref, lse_ref = oracle.rows_fwd(k_i, v_i, [P + r for r in rows], x["q_r"][idx],
+                                         window_left=wl)
+        _check("o_r[seq %d]" % i, o_r[idx], o_ref)
+        _check("lse_r[seq %d]" % i, lse_r[:, idx].t(), lse_ref, bound=2e-3)
+        dk_i = np.zeros_like(k_i)
+        dv_i = np.zeros_like(v_i)
+        dq_i = oracle.rows_bwd_scatter(k_i, v_i, [P + r for r in rows], x["q_r"][idx],
+                                       f64(do_r[idx]), dk_i, dv_i, window_left=wl)
+        dk_p_ref += dk_i[:P]
+        dv_p_ref += dv_i[:P]
+        dk_r_ref[i] = (dk_i[P:], dv_i[P:])
+        _check("dq_r[seq %d rows]" % i, gr["dq_r"][idx], dq_i)
+    print("[full] %s: oracle done" % name, flush=True)
+
+    # shared prompt gradient: all P keys, summed over the N copies and both calls
+    _check("dk_p", gr["dk_p"], dk_p_ref)
+    _check("dv_p", gr["dv_p"], dv_p_ref)
+    _check("dq_p[rows]", gr["dq_p"][p_rows], dq_p_ref)
+    # response keys of the sampled sequences; every other sequence saw dO = 0
+    bound_k = REL * max(np.abs(r[0]).max() for r in dk_r_ref.values())
+    bound_v = REL * max(np.abs(r[1]).max() for r in dk_r_ref.values())
+    for i, (dk_i, dv_i) in dk_r_ref.items():
+        a, b = cu[i], cu[i + 1]
+        _check("dk_r[seq %d]" % i, gr["dk_r"][a:b], dk_i, bound=bound_k)
+        _check("dv_r[seq %d]" % i, gr["dv_r"][a:b], dv_i, bound=bound_v)
+    keep = torch.ones(T, dtype=torch.bool, device=DEV)
+    for i in seqs:
+        keep[cu[i]:cu[i + 1]] = False
+    if bool(keep.any()):
+        assert float(gr["dk_r"][keep].float().abs().max()) == 0.0
+        assert float(gr["dv_r"][keep].float().abs().max()) == 0.0
+    # dQ is zero on every row whose dO is zero
+    zr = torch.ones(T, dtype=torch.bool, device=DEV)
+    for i in seqs:
+        zr[[cu[i] + r for r in resp_rows[i]]] = False
+    assert float(gr["dq_r"][zr].float().abs().max()) == 0.0
+    zp = torch.ones(P, dtype=torch.bool, device=DEV)
+    zp[p_rows] = False
+    assert float(gr["dq_p"][zp].float().abs().max()) == 0.0

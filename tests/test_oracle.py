@@ -286,3 +286,51 @@ def test_oracle_rejects_bad_arguments():
         oracle.seq_fwd(q, k, k, kvh=[0, 1])      # kv-head index out of range
     with pytest.raises(ValueError):
         oracle.seq_fwd(q, k, k, rows=[3])        # row out of range
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,d,wl,scale", CASES)
+def test_selected_rows_match_torch_sdpa_fp64(S, Hq, Hkv, d, wl, scale):
+    # The selected-row forms used at full workload sizes (queries of the selected
+    # rows only; upstream gradient zero on every other row) against torch fp64 SDPA
+    # and autograd with dO zero outside the selected rows.
+    q = _rand((S, Hq, d), 11)
+    k = _rand((S, Hkv, d), 12)
+    v = _rand((S, Hkv, d), 13)
+    rows = sorted({0, S // 2, S - 1})
+    do = torch.zeros((S, Hq, d))
+    do[rows] = _rand((len(rows), Hq, d), 14)
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    kvh = [h // (Hq // Hkv) for h in range(Hq)]
+    o, lse = oracle.rows_fwd(k, v, rows, q[rows], scale=scale, window_left=wl)
+    qt, kt, vt = (x.clone().requires_grad_(True) for x in (q, k, v))
+    o_ref, lse_ref = _sdpa_ref(qt, kt, vt, sc, wl, kvh)
+    np.testing.assert_allclose(o, o_ref.detach().numpy()[rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref.detach().numpy()[rows], rtol=0, atol=1e-12)
+    (o_ref * do).sum().backward()
+    dk = np.zeros((S, Hkv, d))
+    dv = np.zeros((S, Hkv, d))
+    dq = oracle.rows_bwd_scatter(k, v, rows, q[rows], do[rows], dk, dv, scale=scale,
+                                 window_left=wl)
+    np.testing.assert_allclose(dq, qt.grad.numpy()[rows], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, vt.grad.numpy(), rtol=0, atol=1e-11)
+    # the rows with a zero upstream gradient have a zero query gradient
+    others = [t for t in range(S) if t not in rows]
+    assert np.abs(qt.grad.numpy()[others]).max(initial=0.0) == 0.0
+
+
+def test_scatter_accumulates_across_calls():
+    # Two calls with disjoint rows add into the same dk / dv: the sum equals one call
+    # with both row sets (what the full-size tests do over the copies of eq. (1)).
+    S, Hq, Hkv, d = 30, 4, 2, 8
+    q, k, v = _rand((S, Hq, d), 21), _rand((S, Hkv, d), 22), _rand((S, Hkv, d), 23)
+    do = _rand((S, Hq, d), 24)
+    a, b = [3, 17], [9, 29]
+    dk1, dv1 = np.zeros((S, Hkv, d)), np.zeros((S, Hkv, d))
+    oracle.rows_bwd_scatter(k, v, a, q[a], do[a], dk1, dv1)
+    oracle.rows_bwd_scatter(k, v, b, q[b], do[b], dk1, dv1)
+    dk2, dv2 = np.zeros((S, Hkv, d)), np.zeros((S, Hkv, d))
+    ab = a + b
+    oracle.rows_bwd_scatter(k, v, ab, q[ab], do[ab], dk2, dv2)
+    np.testing.assert_allclose(dk1, dk2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv1, dv2, rtol=0, atol=1e-12)
