@@ -23,7 +23,13 @@ MUTATIONS = {
                          "double ds = p * (dot(dot_, vj, d) + delta"),
     "window_off_by_one": ("lo = t - window_left;", "lo = t - window_left + 1;"),
     "dv_wrong_operand": ("dvj[c] += p * dot_[c];", "dvj[c] += p * qt[c];"),
-    "dk_missing_scale": ("dkj[c] += scale * ds * qt[c];", "dkj[c] += ds * qt[c];"),
+    "dk_missing_scale": ("dkj[c] += scale * ds * qt[c];\n                        dvj[c] += p * dot_[c];",
+                         "dkj[c] += ds * qt[c];\n                        dvj[c] += p * dot_[c];"),
+    # the selected-row forms used at full workload sizes
+    "scatter_drop_delta": ("const double ds = s[i] * (dp[i] - delta);\n                double *dkj",
+                           "const double ds = s[i] * dp[i];\n                double *dkj"),
+    "scatter_dv_wrong_weight": ("dvj[c] += s[i] * dot_[c];", "dvj[c] += dot_[c];"),
+    "fwd_sel_missing_norm": ("const double w = exp(p[i] - m) / l;", "const double w = exp(p[i] - m);"),
     "lse_missing_max": ("return m + log(l);", "return log(l);"),
     "gqa_wrong_head": ("int g = kvh[h];\n    double m", "int g = kvh[h] * 0;\n    double m"),
 }
@@ -55,6 +61,14 @@ def _pins_pass():
     ok = np.allclose(o, o_ref.detach().numpy(), atol=1e-10, rtol=0)
     ok &= np.allclose(lse, lse_ref.detach().numpy(), atol=1e-10, rtol=0)
     for a, b in ((g["dq"], qt.grad), (g["dk"], kt.grad), (g["dv"], vt.grad)):
+        ok &= np.allclose(a, b.numpy(), atol=1e-9, rtol=0)
+    # selected-row forms: every row selected, so they must reproduce the same values
+    rows = list(range(S))
+    o2, lse2 = oracle.rows_fwd(k, v, rows, q, window_left=wl)
+    ok &= np.allclose(o2, o_ref.detach().numpy(), atol=1e-10, rtol=0)
+    dk2, dv2 = np.zeros((S, Hkv, d)), np.zeros((S, Hkv, d))
+    dq2 = oracle.rows_bwd_scatter(k, v, rows, q, do, dk2, dv2, window_left=wl)
+    for a, b in ((dq2, qt.grad), (dk2, kt.grad), (dv2, vt.grad)):
         ok &= np.allclose(a, b.numpy(), atol=1e-9, rtol=0)
     return bool(ok)
 
