@@ -662,23 +662,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
 }
 
 // bf16 dK/dV kernel.  A workgroup owns 128 keys of one region and kv head (32 per
-// wave: K, V fragments and the dK, dV accumulators in registers) and streams the
-// query rows that see them in 64-row steps (two 32-row blocks), from the last step
-// backward.  Q, dO, LSE and D of the next step stream into LDS by DMA while the
-// current step is computed (double-buffered, one barrier per step).  The rows of a
-// step are flattened (token, head-of-group) pairs; the rows a lane fetches are fixed
-// within a step, so their token/head split is precomputed.
-template <int HD>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
-  constexpr int BM = 64;
+// wave: V fragments and the dK, dV accumulators in registers; the workgroup's K tile
+// stays in LDS) and streams the query rows that see them in BM-row steps (BM / 32
+// blocks of 32), from the last step backward.  Q, dO, LSE and D of the next step
+// stream into LDS by DMA while the current step is computed (double-buffered, one
+// barrier per step).  The rows of a step are flattened (token, head-of-group) pairs;
+// the rows a lane fetches are fixed within a step, so their token/head split is
+// precomputed.  With K read from LDS and 32-row steps a wave fits 256 registers and
+// the LDS of two workgroups fits a CU: two waves per SIMD.
+template <int HD, int BM, int WPE>
+__global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
   constexpr int BNW = kBwdBN;
   constexpr int TILE = BM * HD * 2;
   constexpr int NKC = HD / 16;
   constexpr int NDB = HD / 32;
   constexpr int CPR = HD / 8;                     // 16-byte chunks per row
   constexpr int KPW = TILE / 1024 / 4;            // DMA instructions per wave per tile
-  constexpr int STAGE = 2 * TILE + 2 * BM * 4;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  constexpr int STAGE = 2 * TILE + 2 * 64 * 4;
+  constexpr int KTILE = BNW * HD * 2;            // the workgroup's K tile
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE + KTILE];
+  char *ktile = smem + 2 * STAGE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -700,12 +703,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
                    (long)(own0 + it.key_start + (key_valid ? key : 0)) * kld + (long)g * HD;
   const bf16 *vp = reinterpret_cast<const bf16 *>(ctx ? a.v_ctx : a.v_own) +
                    (long)(own0 + it.key_start + (key_valid ? key : 0)) * kld + (long)g * HD;
-  bf16x8 kf[NKC], vf[NKC];
+  (void)kp;
+  bf16x8 vf[NKC];
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc) {
     const uint4 z = make_uint4(0, 0, 0, 0);
-    kf[kc] = as_bf16x8(key_valid ? *reinterpret_cast<const uint4 *>(kp + kc * 16 + half * 8) : z);
     vf[kc] = as_bf16x8(key_valid ? *reinterpret_cast<const uint4 *>(vp + kc * 16 + half * 8) : z);
+  }
+  {   // the workgroup's K tile (rows past the region's end are zero-filled)
+    DmaRows<HD, BNW> kd;
+    kd.init(wave, lane, (int)(kld * 2));
+    kd.load(ktile,
+            reinterpret_cast<const bf16 *>(ctx ? a.k_ctx : a.k_own) +
+                (long)(own0 + it.key_start) * kld + (long)g * HD,
+            (int)(kld * 2), nkeys, wave);
   }
   const bool wave_active = kw0 < nkeys;
   // Flattened query rows f (token f / G) that see this lane's key: the causal mask
@@ -796,14 +807,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
       dma16(rq, l0 + k * 4096, off);
       dma16(rd, l0 + TILE + k * 4096, off);
     }
-    if (wave < 2) {   // LSE (wave 0) and D (wave 1) of the step's 64 rows
+    if (wave < 2) {   // LSE (wave 0) and D (wave 1) of the step's rows; lanes >= BM read nothing
       int t = ft + tl, j = fj + jl;
       if (j >= G) {
         j -= G;
         ++t;
       }
-      const int off = ((g * G + j) * a.lse_ld + s0 + t) * 4;
-      const uint32_t la = __builtin_amdgcn_readfirstlane(lds_u32(st + 2 * TILE) + wave * BM * 4);
+      const int off = lane < BM ? ((g * G + j) * a.lse_ld + s0 + t) * 4 : 0x7fffffff;
+      const uint32_t la = __builtin_amdgcn_readfirstlane(lds_u32(st + 2 * TILE) + wave * 256);
       dma4(r_ld, la, off);
     }
   };
@@ -841,7 +852,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
     const char *qs = smem + stage * STAGE;
     const char *dos = qs + TILE;
     const float *lse_s = reinterpret_cast<const float *>(qs + 2 * TILE);
-    const float *d_s = lse_s + BM;
+    const float *d_s = lse_s + 64;
 
     if (wave_active) {
       const int kpa = kbase + it.key_start + kw0;
@@ -853,7 +864,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
         f32x16 st = zero16(), dpt = zero16();
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
-          st = mfma(sw_frag<HD>(qs, rb * 32 + col, kc, half), kf[kc], st);
+          st = mfma(sw_frag<HD>(qs, rb * 32 + col, kc, half), sw_frag<HD>(ktile, kw0 + col, kc, half), st);
           dpt = mfma(sw_frag<HD>(dos, rb * 32 + col, kc, half), vf[kc], dpt);
         }
         const int ta = max(b0, flo) / G;
@@ -1001,11 +1012,11 @@ hipError_t launch_bwd_dkdv(int dtype, int hd, const BwdKVArgs &a, int n, hipStre
   if (n <= 0) return hipSuccess;
   if (dtype == 0) {
     if (hd == 64) {
-      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<64>), dim3(n), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<64, 32, 2>), dim3(n), dim3(256), 0, s, a);
       return hipGetLastError();
     }
     if (hd == 128) {
-      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<128>), dim3(n), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<128, 32, 2>), dim3(n), dim3(256), 0, s, a);
       return hipGetLastError();
     }
     if (hd == 512) return launch_bwd_dkdv_d512(a, n, s);

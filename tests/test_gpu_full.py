@@ -64,12 +64,13 @@ def test_full_size_parity(name):
     resp_rows = {i: _rows(lens[i], wl_extra) for i in seqs}
     p_rows = _rows(P, tuple(P - 1 - e for e in wl_extra))
     g = torch.Generator().manual_seed(7000 + w.seed)
-    do_p = torch.zeros((P, Hq, d))
-    do_r = torch.zeros((T, Hq, d))
-    do_p[p_rows] = torch.randn((len(p_rows), Hq, d), generator=g).to(torch.bfloat16).float()
+    f32 = torch.float32
+    do_p = torch.zeros((P, Hq, d), dtype=f32)
+    do_r = torch.zeros((T, Hq, d), dtype=f32)
+    do_p[p_rows] = torch.randn((len(p_rows), Hq, d), generator=g, dtype=f32).to(torch.bfloat16).float()
     for i in seqs:
         idx = [cu[i] + r for r in resp_rows[i]]
-        do_r[idx] = torch.randn((len(idx), Hq, d), generator=g).to(torch.bfloat16).float()
+        do_r[idx] = torch.randn((len(idx), Hq, d), generator=g, dtype=f32).to(torch.bfloat16).float()
 
     # ---- GPU: Call 1 + Call 2 forward and backward, one shared fp32 accumulator ----
     t = {k: x[k].to(torch.bfloat16).to(DEV) for k in ("q_p", "k_p", "v_p", "q_r", "k_r", "v_r")}
