@@ -450,7 +450,7 @@ std::vector<KVItem> build_kv_items(const Shape &s, bool with_ctx) {
 }
 
 struct BwdPlan {
-  size_t d_off = 0, q_off = 0, kv_off = 0, bytes = 0;
+  size_t d_off = 0, l2_off = 0, q_off = 0, kv_off = 0, bytes = 0;
   size_t n_q = 0, n_kv = 0;
 };
 
@@ -468,7 +468,8 @@ BwdPlan plan_bwd(const Shape &s, bool with_ctx) {
   }
   pl.n_kv = nkv * s.Hkv;   // upper bound (empty windowed items are dropped)
   pl.d_off = 0;
-  pl.q_off = align_up((size_t)s.Hq * s.T * sizeof(float));
+  pl.l2_off = align_up((size_t)s.Hq * s.T * sizeof(float));
+  pl.q_off = pl.l2_off + align_up((size_t)s.Hq * s.T * sizeof(float));
   pl.kv_off = pl.q_off + align_up(pl.n_q * sizeof(QItem));
   pl.bytes = pl.kv_off + align_up(pl.n_kv * sizeof(KVItem));
   if (s.T == 0) pl.bytes = 0;
@@ -504,7 +505,10 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
   }
   if (s.T > 0) {
     float *D = reinterpret_cast<float *>(wsb + pl.d_off);
-    e = timed(kKPre, stream, [&] { return launch_bwd_pre(s.dtype, s.d, io.o, io.dout, D, s.T, s.Hq, stream); });
+    float *lse2 = reinterpret_cast<float *>(wsb + pl.l2_off);
+    e = timed(kKPre, stream, [&] {
+      return launch_bwd_pre(s.dtype, s.d, io.o, io.dout, io.lse, D, lse2, s.T, s.Hq, stream);
+    });
     if (e != hipSuccess) return hip_fail(e, "bwd preprocess launch");
     std::vector<QItem> qi = build_q_items(s, s.bm_tok_dq, kFwdBN);
     std::vector<KVItem> kv = build_kv_items(s, io.with_ctx);
@@ -520,7 +524,7 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
     if (e != hipSuccess) return hip_fail(e, "dq kernel launch");
     BwdKVArgs ka{};
     ka.q = io.q; ka.dout = io.dout; ka.k_ctx = io.kc; ka.v_ctx = io.vc; ka.k_own = io.ko;
-    ka.v_own = io.vo; ka.lse = io.lse; ka.D = D; ka.cu = io.cu_dev;
+    ka.v_own = io.vo; ka.lse = io.lse; ka.D = D; ka.lse2 = lse2; ka.cu = io.cu_dev;
     ka.dk_own = io.dk_own; ka.dv_own = io.dv_own; ka.acc_dk = io.acc_dk; ka.acc_dv = io.acc_dv;
     ka.items = reinterpret_cast<const KVItem *>(wsb + pl.kv_off);
     ka.Hq = s.Hq; ka.Hkv = s.Hkv; ka.G = s.G; ka.ctx_len = s.P; ka.window_left = s.wl;

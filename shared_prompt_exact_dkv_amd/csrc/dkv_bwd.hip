@@ -18,6 +18,8 @@
 //   cast      the accumulator is rounded to the tensor dtype once (§3.2 Stage 2).
 // Transposed operands (contractions over query rows or key rows) are read from the
 // same row-layout LDS tiles with the gfx950 transpose read.
+#include <type_traits>
+
 #include "dkv_device.h"
 #include "dkv_launch.h"
 #include "dkv_tiles.h"
@@ -27,8 +29,8 @@ namespace dkv {
 // ------------------------------------------------------------------ bwd_pre --
 
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const T *o, const T *dout, float *D,
-                                                      long T_tok, int Hq) {
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const T *o, const T *dout, const float *lse,
+                                                      float *D, float *lse2, long T_tok, int Hq) {
   constexpr int E = 16 / sizeof(T);          // elements per 16-byte chunk
   constexpr int TPR = HD / E;                // threads per (token, head) row
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
@@ -49,6 +51,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T *o, const T *dout,
     long t = row / Hq;
     int h = row - t * Hq;
     D[(long)h * T_tok + t] = acc;
+    lse2[(long)h * T_tok + t] = lse[(long)h * T_tok + t] * kLog2e;
   }
 }
 
@@ -783,7 +786,7 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
   const int qld_b = (int)(qld * 2);
   const int head0_b = g * G * HD * 2;
   // Wave 0 fetches LSE rows, wave 1 D rows.
-  const __amdgpu_buffer_rsrc_t r_ld = make_rsrc_u(wave == 0 ? (const void *)a.lse : (const void *)a.D,
+  const __amdgpu_buffer_rsrc_t r_ld = make_rsrc_u(wave == 0 ? (const void *)a.lse2 : (const void *)a.D,
                                                   (uint32_t)((long)a.Hq * a.lse_ld * 4));
 
   // Fetch the step at the cursor into stage `st`.
@@ -830,7 +833,6 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
       seek();
     }
   };
-  int stage = 0;
   bool have = !done;
   int f0 = 0, flo = 0, fend = 0;
   if (have) {
@@ -839,17 +841,20 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
     f0 = nf0, flo = nflo, fend = nfend;
   }
 
-  while (have) {
+  // One step computed from stage STG (a compile-time stage, so every LDS read of the
+  // step takes an immediate offset) while the next step streams into the other.
+  auto step = [&](auto stg_c) {
+    constexpr int STG = decltype(stg_c)::value;
     dma_wait();
     __syncthreads();
     const bool more = !done;
     int g0 = 0, glo = 0, gend = 0;
     if (more) {
-      issue(smem + (stage ^ 1) * STAGE);
+      issue(smem + (STG ^ 1) * STAGE);
       advance();
       g0 = nf0, glo = nflo, gend = nfend;
     }
-    const char *qs = smem + stage * STAGE;
+    const char *qs = smem + STG * STAGE;
     const char *dos = qs + TILE;
     const float *lse_s = reinterpret_cast<const float *>(qs + 2 * TILE);
     const float *d_s = lse_s + 64;
@@ -882,7 +887,7 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int v = 4 * i + e;
-            float p = fast_exp2(fmaf(st[v], sf, -lv[e] * kLog2e));
+            float p = fast_exp2(fmaf(st[v], sf, -lv[e]));
             if (!full) {
               const int f = b0 + c_row(v, half);
               if (f < vlo || f >= vhi) p = 0.f;
@@ -905,7 +910,11 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
     }
     have = more;
     f0 = g0, flo = glo, fend = gend;
-    stage ^= 1;
+  };
+  while (have) {
+    step(std::integral_constant<int, 0>{});
+    if (!have) break;
+    step(std::integral_constant<int, 1>{});
   }
 
   // Epilogue: lane holds dims db*32 + col of keys kw0 + c_row(v, half).
@@ -933,27 +942,27 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
 // ---------------------------------------------------------------- launchers --
 
 template <typename T, int HD>
-static hipError_t pre_t(const void *o, const void *dout, float *D, long T_tok, int Hq,
-                        hipStream_t s) {
+static hipError_t pre_t(const void *o, const void *dout, const float *lse, float *D, float *lse2,
+                        long T_tok, int Hq, hipStream_t s) {
   constexpr int TPR = HD / (16 / sizeof(T));
   long threads = T_tok * Hq * TPR;
   long blocks = (threads + 255) / 256;
   hipLaunchKernelGGL((bwd_pre_kernel<T, HD>), dim3(blocks), dim3(256), 0, s,
-                     reinterpret_cast<const T *>(o), reinterpret_cast<const T *>(dout), D, T_tok,
-                     Hq);
+                     reinterpret_cast<const T *>(o), reinterpret_cast<const T *>(dout), lse, D,
+                     lse2, T_tok, Hq);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_pre(int dtype, int hd, const void *o, const void *dout, float *D, long T,
-                          int Hq, hipStream_t s) {
+hipError_t launch_bwd_pre(int dtype, int hd, const void *o, const void *dout, const float *lse,
+                          float *D, float *lse2, long T, int Hq, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (dtype == 0) {
-    if (hd == 64) return pre_t<bf16, 64>(o, dout, D, T, Hq, s);
-    if (hd == 128) return pre_t<bf16, 128>(o, dout, D, T, Hq, s);
-    if (hd == 512) return pre_t<bf16, 512>(o, dout, D, T, Hq, s);
+    if (hd == 64) return pre_t<bf16, 64>(o, dout, lse, D, lse2, T, Hq, s);
+    if (hd == 128) return pre_t<bf16, 128>(o, dout, lse, D, lse2, T, Hq, s);
+    if (hd == 512) return pre_t<bf16, 512>(o, dout, lse, D, lse2, T, Hq, s);
   } else {
-    if (hd == 64) return pre_t<float, 64>(o, dout, D, T, Hq, s);
-    if (hd == 128) return pre_t<float, 128>(o, dout, D, T, Hq, s);
+    if (hd == 64) return pre_t<float, 64>(o, dout, lse, D, lse2, T, Hq, s);
+    if (hd == 128) return pre_t<float, 128>(o, dout, lse, D, lse2, T, Hq, s);
   }
   return hipErrorInvalidValue;
 }

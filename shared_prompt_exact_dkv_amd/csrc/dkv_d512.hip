@@ -455,7 +455,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
 
   const int qld_b = (int)(qld * 2);
   const int head0_b = g * G * HD * 2;
-  const __amdgpu_buffer_rsrc_t r_ld = make_rsrc_u(wave == 0 ? (const void *)a.lse : (const void *)a.D,
+  const __amdgpu_buffer_rsrc_t r_ld = make_rsrc_u(wave == 0 ? (const void *)a.lse2 : (const void *)a.D,
                                                   (uint32_t)((long)a.Hq * a.lse_ld * 4));
   // Fetch the step at the cursor into stage `st`: row r of the step (a flattened
   // (token, head) row) fills 1 KB block r, written by wave r % 4.
@@ -546,7 +546,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int v = 4 * i + e;
-        float p = fast_exp2(fmaf(st[v], sf, -lv[e] * kLog2e));
+        float p = fast_exp2(fmaf(st[v], sf, -lv[e]));
         if (!full) {
           const int f = f0 + c_row(v, half);
           if (f < vlo || f >= vhi) p = 0.f;

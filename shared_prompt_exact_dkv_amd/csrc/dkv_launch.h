@@ -46,9 +46,11 @@ hipError_t launch_fwd_d512(const FwdArgs &a, int n_items, hipStream_t s);
 
 // ---- backward ----
 
-// D[h][t] = sum_c dO[t][h][c] * O[t][h][c] (fp32), rows = T tokens x Hq heads.
-hipError_t launch_bwd_pre(int dtype, int head_dim, const void *o, const void *dout, float *D,
-                          long T, int Hq, hipStream_t s);
+// D[h][t] = sum_c dO[t][h][c] * O[t][h][c] (fp32), rows = T tokens x Hq heads; also
+// lse2[h][t] = LSE[h][t] * log2(e), the row's log-sum-exp in the exponent base the
+// bf16 kernels use.
+hipError_t launch_bwd_pre(int dtype, int head_dim, const void *o, const void *dout,
+                          const float *lse, float *D, float *lse2, long T, int Hq, hipStream_t s);
 hipError_t launch_fill_zero(float *p, long n, hipStream_t s);
 // dst[i] = round(src[i]) in dtype (a copy for fp32).
 hipError_t launch_cast(int dtype, const float *src, void *dst, long n, hipStream_t s);
@@ -78,6 +80,7 @@ struct KVItem {
 struct BwdKVArgs {
   const void *q, *dout, *k_ctx, *v_ctx, *k_own, *v_own;
   const float *lse, *D;
+  const float *lse2;           // LSE * log2(e) (from the preprocess kernel)
   const int32_t *cu;           // device prefix sums of the query sequences
   void *dk_own, *dv_own;       // direct outputs of own-region keys
   float *acc_dk, *acc_dv;      // fp32 accumulators: ctx-region keys, and own keys if own_to_acc
