@@ -268,15 +268,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_u(const void *base, 
 __device__ __forceinline__ uint32_t lds_u32(const void *p) { return (uint32_t)(uintptr_t)p; }
 
 // Swizzled dense tile [row][HD] bf16: the 16-byte chunk c of row r sits in slot
-// c ^ swz(r).  swz's low bits spread 8 consecutive rows over 8 different slots (the
-// 32 query/key rows of a fragment read hit distinct banks) and map the 4 rows of a
-// transpose read's 16-lane group to 4 different slot pairs.
+// c ^ swz(r).  With rows of 16 or more chunks, swz(r) (bits r3 r2 r1 r0 of r) is
+//   ((r0 ^ r3) << 3) | (r1 << 2) | (r0 << 1) | r2,
+// a bijection on 16 consecutive rows (a 16-byte fragment read of 16 rows touches 16
+// different slots), distinct in its low 3 bits over 8 rows, and distinct in bits 1-2
+// and in bits 2-3 over each aligned group of 4 rows (the 4 rows of a transpose read
+// land in 4 different 32- and 64-byte slot groups), so both access patterns spread
+// over all banks whether the LDS serves 128 or 256 bytes per clock.  With 8-chunk
+// rows the 3-bit form (r1 r0 r2) keeps the same properties for 8-row groups.
 template <int HD> struct Swz {
   static constexpr int kChunks = HD / 8;   // 16-byte chunks per row
   __device__ __forceinline__ static int swz(int r) {
-    int x = ((r & 3) << 1) | ((r >> 2) & 1);
-    if constexpr (kChunks >= 16) x |= ((r >> 3) & 1) << 3;
-    return x;
+    const int r0 = r & 1, r1 = (r >> 1) & 1, r2 = (r >> 2) & 1, r3 = (r >> 3) & 1;
+    if constexpr (kChunks >= 16) return ((r0 ^ r3) << 3) | (r1 << 2) | (r0 << 1) | r2;
+    return (r1 << 2) | (r0 << 1) | r2;
   }
   __device__ __forceinline__ static int off(int r, int chunk) {   // byte offset of a chunk
     return r * (HD * 2) + ((chunk ^ swz(r)) << 4);
