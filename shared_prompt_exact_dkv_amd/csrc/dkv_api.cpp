@@ -504,10 +504,11 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
     if (e != hipSuccess) return hip_fail(e, "zero acc");
   }
   if (s.T > 0) {
-    float *D = reinterpret_cast<float *>(wsb + pl.d_off);
-    float *lse2 = reinterpret_cast<float *>(wsb + pl.l2_off);
+    float *Dneg = reinterpret_cast<float *>(wsb + pl.d_off);
+    float *lsn = reinterpret_cast<float *>(wsb + pl.l2_off);
     e = timed(kKPre, stream, [&] {
-      return launch_bwd_pre(s.dtype, s.d, io.o, io.dout, io.lse, D, lse2, s.T, s.Hq, stream);
+      return launch_bwd_pre(s.dtype, s.d, io.o, io.dout, io.lse, Dneg, lsn, s.T, s.Hq, s.scale,
+                            stream);
     });
     if (e != hipSuccess) return hip_fail(e, "bwd preprocess launch");
     std::vector<QItem> qi = build_q_items(s, s.bm_tok_dq, kFwdBN);
@@ -516,7 +517,7 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
     if ((st = upload(kv.data(), kv.size() * sizeof(KVItem), wsb + pl.kv_off, stream)) != DKV_OK) return st;
     BwdQArgs qa{};
     qa.q = io.q; qa.k_ctx = io.kc; qa.v_ctx = io.vc; qa.k_own = io.ko; qa.v_own = io.vo;
-    qa.dout = io.dout; qa.lse = io.lse; qa.D = D; qa.dq = io.dq;
+    qa.dout = io.dout; qa.lse = io.lse; qa.Dneg = Dneg; qa.dq = io.dq;
     qa.items = reinterpret_cast<const QItem *>(wsb + pl.q_off);
     qa.Hq = s.Hq; qa.Hkv = s.Hkv; qa.G = s.G; qa.bm_tok = s.bm_tok_dq; qa.ctx_len = s.P;
     qa.window_left = s.wl; qa.lse_ld = (int)s.T; qa.scale = s.scale;
@@ -524,7 +525,7 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
     if (e != hipSuccess) return hip_fail(e, "dq kernel launch");
     BwdKVArgs ka{};
     ka.q = io.q; ka.dout = io.dout; ka.k_ctx = io.kc; ka.v_ctx = io.vc; ka.k_own = io.ko;
-    ka.v_own = io.vo; ka.lse = io.lse; ka.D = D; ka.lse2 = lse2; ka.cu = io.cu_dev;
+    ka.v_own = io.vo; ka.lse = io.lse; ka.Dneg = Dneg; ka.lsn = lsn; ka.cu = io.cu_dev;
     ka.dk_own = io.dk_own; ka.dv_own = io.dv_own; ka.acc_dk = io.acc_dk; ka.acc_dv = io.acc_dv;
     ka.items = reinterpret_cast<const KVItem *>(wsb + pl.kv_off);
     ka.Hq = s.Hq; ka.Hkv = s.Hkv; ka.G = s.G; ka.ctx_len = s.P; ka.window_left = s.wl;

@@ -5,7 +5,8 @@
 //   dP = <dO_t, v_j>,   dS = p * (dP - D_t),    D_t = <dO_t, O_t>
 //   dQ_t += scale * dS * k_j,   dK_j += scale * dS * q_t,   dV_j += p * dO_t
 // Kernels:
-//   bwd_pre   D = rowsum(dO * O) in fp32 (the auxiliary preprocessing launch)
+//   bwd_pre   D = rowsum(dO * O) in fp32 (the auxiliary preprocessing launch), stored
+//             negated, and the LSE in units of the raw dot product, -LSE / scale
 //   bwd_dq    query-parallel: a workgroup keeps 128 query rows in registers and
 //             walks the shared-prompt key tiles, then its own sequence's tiles,
 //             exactly like the forward; dQ is written once, no atomics.
@@ -30,7 +31,8 @@ namespace dkv {
 
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T *o, const T *dout, const float *lse,
-                                                      float *D, float *lse2, long T_tok, int Hq) {
+                                                      float *Dneg, float *lsn, long T_tok, int Hq,
+                                                      float inv_scale) {
   constexpr int E = 16 / sizeof(T);          // elements per 16-byte chunk
   constexpr int TPR = HD / E;                // threads per (token, head) row
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
@@ -50,8 +52,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T *o, const T *dout,
   if (row < T_tok * Hq && ch == 0) {
     long t = row / Hq;
     int h = row - t * Hq;
-    D[(long)h * T_tok + t] = acc;
-    lse2[(long)h * T_tok + t] = lse[(long)h * T_tok + t] * kLog2e;
+    Dneg[(long)h * T_tok + t] = -acc;
+    lsn[(long)h * T_tok + t] = -lse[(long)h * T_tok + t] * inv_scale;
   }
 }
 
@@ -127,7 +129,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdQArgs a) {
   using SM = Softmax<T>;
   const float sf = SM::factor(a.scale);
   const float lse2 = SM::lse_in(a.lse[(long)h * a.lse_ld + qrow]);
-  const float Dq = a.D[(long)h * a.lse_ld + qrow];
+  const float Dq = -a.Dneg[(long)h * a.lse_ld + qrow];
 
   f32x16 acc[NDB];
   f32x16 comp[sizeof(T) == 4 ? NDB : 1];   // Kahan terms (fp32 path only)
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
   }
   const float sf = a.scale * kLog2e;
   const float lse2 = a.lse[(long)h * a.lse_ld + qrow] * kLog2e;
-  const float Dq = a.D[(long)h * a.lse_ld + qrow];
+  const float Dq = -a.Dneg[(long)h * a.lse_ld + qrow];
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -361,17 +363,28 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
         dpt = mfma(sw_frag<HD>(vs, hb * 32 + col, kc, half), df[kc], dpt);
       }
       float ds[16];
+      // The visibility test is compiled only into the variant for tiles that need it.
+      auto grads = [&](auto masked_c) {
+        constexpr bool MASKED = decltype(masked_c)::value;
+        // Visible keys of this lane's row, as offsets r = 8 * (v / 4) + v % 4 from the
+        // lane's first key hb * 32 + 4 * half: [lo, hi).
+        const int k0 = hb * 32 + 4 * half;
+        const int lo = (wl >= 0 ? qpos - wl - kpos0 : -BN) - k0;
+        const int hi = min(nrows, qpos - kpos0 + 1) - k0;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float p = fast_exp2(fmaf(st[v], sf, -lse2));
-        if (need_mask) {
-          int kk = hb * 32 + c_row(v, half);
-          int kp = kpos0 + kk;
-          bool vis = (kk < nrows) && (kp <= qpos) && (wl < 0 || kp >= qpos - wl);
-          if (!vis) p = 0.f;
+        for (int v = 0; v < 16; ++v) {
+          float p = fast_exp2(fmaf(st[v], sf, -lse2));
+          if (MASKED) {
+            const int r = 8 * (v >> 2) + (v & 3);
+            if (r < lo || r >= hi) p = 0.f;
+          }
+          ds[v] = p * (dpt[v] - Dq);
         }
-        ds[v] = p * (dpt[v] - Dq);
-      }
+      };
+      if (need_mask)
+        grads(std::true_type{});
+      else
+        grads(std::false_type{});
       const bf16x8 d0 = pack8(ds), d1 = pack8(ds + 8);
       // dQᵀ += Kᵀ dSᵀ.
 #pragma unroll
@@ -541,7 +554,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
         int t = f / G, j = f - t * G;
         long idx = (long)(g * G + j) * a.lse_ld + s0 + t;
         lse_r = SM::lse_in(a.lse[idx]);
-        d_r = a.D[idx];
+        d_r = -a.Dneg[idx];
       } else {
         lse_r = INFINITY;
         d_r = 0.f;
@@ -722,6 +735,21 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
             (int)(kld * 2), nkeys, wave);
   }
   const bool wave_active = kw0 < nkeys;
+  // A block of 32 flattened rows [b0, b0 + 32) inside the step's rows needs no mask when
+  // every key of the wave sees every row: b0 >= the first row the wave's last key sees,
+  // and b0 + 32 <= the end of the rows its first key sees (window).
+  const int wkpa = kbase + it.key_start + kw0;
+  const int full_lo = __builtin_amdgcn_readfirstlane(
+      kw0 + 32 <= nkeys ? max(0, (wkpa + 31 - P) * G) : 0x7fffffff);
+  const int full_hi = __builtin_amdgcn_readfirstlane(
+      wl >= 0 ? max(0, (wkpa + wl - P + 1) * G) : 0x7fffffff);
+  // Per-lane byte offsets of the fragment chunks of row `col` in a swizzled tile; the
+  // wave's K rows kw0 + col share them (kw0 is a multiple of 32, the swizzle reads the
+  // row's low four bits).
+  int fo[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) fo[kc] = Swz<HD>::off(col, kc * 2 + half);
+  const uint32_t kt_wave = __builtin_amdgcn_readfirstlane(lds_u32(ktile) + kw0 * HD * 2);
   // Flattened query rows f (token f / G) that see this lane's key: the causal mask
   // (key position <= P + f / G) and the window (key position >= P + f / G - wl) as
   // bounds on f, so the per-element test needs no division.  An invalid key sees none.
@@ -786,7 +814,7 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
   const int qld_b = (int)(qld * 2);
   const int head0_b = g * G * HD * 2;
   // Wave 0 fetches LSE rows, wave 1 D rows.
-  const __amdgpu_buffer_rsrc_t r_ld = make_rsrc_u(wave == 0 ? (const void *)a.lse2 : (const void *)a.D,
+  const __amdgpu_buffer_rsrc_t r_ld = make_rsrc_u(wave == 0 ? (const void *)a.lsn : (const void *)a.Dneg,
                                                   (uint32_t)((long)a.Hq * a.lse_ld * 4));
 
   // Fetch the step at the cursor into stage `st`.
@@ -856,49 +884,67 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
     }
     const char *qs = smem + STG * STAGE;
     const char *dos = qs + TILE;
-    const float *lse_s = reinterpret_cast<const float *>(qs + 2 * TILE);
-    const float *d_s = lse_s + 64;
+    const float *lsn_s = reinterpret_cast<const float *>(qs + 2 * TILE);
+    const float *dn_s = lsn_s + 64;
 
     if (wave_active) {
-      const int kpa = kbase + it.key_start + kw0;
-      const int kpb = kbase + it.key_start + min(kw0 + 32, nkeys) - 1;
+      // Recomputed each step (opaque to the compiler) so the K addresses below stay one
+      // add each instead of eight live registers.
+      uint32_t kt = kt_wave;
+      asm volatile("" : "+s"(kt));
 #pragma unroll
       for (int rb = 0; rb < BM / 32; ++rb) {
         const int b0 = f0 + rb * 32;
         if (b0 + 32 <= flo || b0 >= fend) continue;   // block outside the step's rows
-        f32x16 st = zero16(), dpt = zero16();
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-          st = mfma(sw_frag<HD>(qs, rb * 32 + col, kc, half), sw_frag<HD>(ktile, kw0 + col, kc, half), st);
-          dpt = mfma(sw_frag<HD>(dos, rb * 32 + col, kc, half), vf[kc], dpt);
-        }
-        const int ta = max(b0, flo) / G;
-        const int tb = (min(b0 + 32, fend) - 1) / G;
-        const bool full = (b0 >= flo) && (b0 + 32 <= fend) && (kw0 + 32 <= nkeys) &&
-                          (kpb <= P + ta) && (wl < 0 || kpa >= P + tb - wl);
-        const int vlo = max(flo, f_vis_lo), vhi = min(fend, f_vis_hi);
-        float pv[16], dsv[16];
+        // The accumulators start at -LSE / scale and -D of their rows, so they end as
+        // <q, k> - LSE / scale and dP - D.
+        f32x16 st, dpt;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float4 l4 = *reinterpret_cast<const float4 *>(lse_s + rb * 32 + 8 * i + 4 * half);
-          const float4 d4 = *reinterpret_cast<const float4 *>(d_s + rb * 32 + 8 * i + 4 * half);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+          const float4 l4 = *reinterpret_cast<const float4 *>(lsn_s + rb * 32 + 8 * i + 4 * half);
+          const float4 d4 = *reinterpret_cast<const float4 *>(dn_s + rb * 32 + 8 * i + 4 * half);
+          st[4 * i] = l4.x, st[4 * i + 1] = l4.y, st[4 * i + 2] = l4.z, st[4 * i + 3] = l4.w;
+          dpt[4 * i] = d4.x, dpt[4 * i + 1] = d4.y, dpt[4 * i + 2] = d4.z, dpt[4 * i + 3] = d4.w;
+        }
+        // MFMA stretches run at raised wave priority: with two waves per SIMD, the one
+        // ready to issue matrix work goes first and the other's softmax fills the gaps.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int v = 4 * i + e;
-            float p = fast_exp2(fmaf(st[v], sf, -lv[e]));
-            if (!full) {
-              const int f = b0 + c_row(v, half);
-              if (f < vlo || f >= vhi) p = 0.f;
+        for (int kc = 0; kc < NKC; ++kc) {
+          const char *qrow = qs + rb * 32 * HD * 2 + fo[kc];
+          st = mfma(as_bf16x8(*reinterpret_cast<const uint4 *>(qrow)), lds_frag_at(kt + fo[kc]), st);
+          dpt = mfma(as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + TILE)), vf[kc], dpt);
+        }
+        __builtin_amdgcn_s_setprio(0);
+        const bool full = b0 >= max(flo, full_lo) && b0 + 32 <= min(fend, full_hi);
+        float pv[16], dsv[16];
+        // P and dS of the block; the visibility test is compiled only into the masked
+        // variant, which runs on the few blocks that straddle a mask edge or a range end.
+        auto probs = [&](auto masked_c) {
+          constexpr bool MASKED = decltype(masked_c)::value;
+          // Rows b0 + c_row(v, half) in [vlo, vhi) are visible: as offsets from this
+          // lane's first row, [lo, hi).
+          const int lo = max(flo, f_vis_lo) - b0 - 4 * half;
+          const int hi = min(fend, f_vis_hi) - b0 - 4 * half;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            float p = fast_exp2(st[v] * sf);
+            if (MASKED) {
+              const int r = 8 * (v >> 2) + (v & 3);
+              if (r < lo || r >= hi) p = 0.f;
             }
             pv[v] = p;
-            dsv[v] = p * (dpt[v] - dd[e]);
+            dsv[v] = p * dpt[v];
           }
-        }
+        };
+        if (full)
+          probs(std::false_type{});
+        else
+          probs(std::true_type{});
         const bf16x8 p0 = pack8(pv), p1 = pack8(pv + 8);
         const bf16x8 s0 = pack8(dsv), s1 = pack8(dsv + 8);
         // dV += Pᵀ dO and dK += dSᵀ Q over the block's 32 rows.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           dv[db] = mfma(p0, sw_tr_frag<HD>(dos, rb * 32, db * 32, lane), dv[db]);
@@ -906,6 +952,7 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
           dk[db] = mfma(s0, sw_tr_frag<HD>(qs, rb * 32, db * 32, lane), dk[db]);
           dk[db] = mfma(s1, sw_tr_frag<HD>(qs, rb * 32 + 16, db * 32, lane), dk[db]);
         }
+        __builtin_amdgcn_s_setprio(0);
       }
     }
     have = more;
@@ -942,27 +989,27 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
 // ---------------------------------------------------------------- launchers --
 
 template <typename T, int HD>
-static hipError_t pre_t(const void *o, const void *dout, const float *lse, float *D, float *lse2,
-                        long T_tok, int Hq, hipStream_t s) {
+static hipError_t pre_t(const void *o, const void *dout, const float *lse, float *Dneg, float *lsn,
+                        long T_tok, int Hq, float scale, hipStream_t s) {
   constexpr int TPR = HD / (16 / sizeof(T));
   long threads = T_tok * Hq * TPR;
   long blocks = (threads + 255) / 256;
   hipLaunchKernelGGL((bwd_pre_kernel<T, HD>), dim3(blocks), dim3(256), 0, s,
-                     reinterpret_cast<const T *>(o), reinterpret_cast<const T *>(dout), lse, D,
-                     lse2, T_tok, Hq);
+                     reinterpret_cast<const T *>(o), reinterpret_cast<const T *>(dout), lse, Dneg,
+                     lsn, T_tok, Hq, 1.0f / scale);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_pre(int dtype, int hd, const void *o, const void *dout, const float *lse,
-                          float *D, float *lse2, long T, int Hq, hipStream_t s) {
+                          float *Dneg, float *lsn, long T, int Hq, float scale, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (dtype == 0) {
-    if (hd == 64) return pre_t<bf16, 64>(o, dout, lse, D, lse2, T, Hq, s);
-    if (hd == 128) return pre_t<bf16, 128>(o, dout, lse, D, lse2, T, Hq, s);
-    if (hd == 512) return pre_t<bf16, 512>(o, dout, lse, D, lse2, T, Hq, s);
+    if (hd == 64) return pre_t<bf16, 64>(o, dout, lse, Dneg, lsn, T, Hq, scale, s);
+    if (hd == 128) return pre_t<bf16, 128>(o, dout, lse, Dneg, lsn, T, Hq, scale, s);
+    if (hd == 512) return pre_t<bf16, 512>(o, dout, lse, Dneg, lsn, T, Hq, scale, s);
   } else {
-    if (hd == 64) return pre_t<float, 64>(o, dout, lse, D, lse2, T, Hq, s);
-    if (hd == 128) return pre_t<float, 128>(o, dout, lse, D, lse2, T, Hq, s);
+    if (hd == 64) return pre_t<float, 64>(o, dout, lse, Dneg, lsn, T, Hq, scale, s);
+    if (hd == 128) return pre_t<float, 128>(o, dout, lse, Dneg, lsn, T, Hq, scale, s);
   }
   return hipErrorInvalidValue;
 }

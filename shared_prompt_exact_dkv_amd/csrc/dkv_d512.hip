@@ -20,6 +20,8 @@
 //            wave accumulates dK and dV for one quarter of the head dim.
 // Tiles are staged by LDS DMA into swizzled dense rows (one 1 KB row per DMA block),
 // double-buffered; partial tiles are exchanged through a small LDS area.
+#include <type_traits>
+
 #include "dkv_device.h"
 #include "dkv_launch.h"
 #include "dkv_tiles.h"
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(256, 1) void fwd_d512_kernel(FwdArgs a) {
     float mx = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
-    mx = fmaxf(mx, wave_xor32(mx)) * sf;
+    mx = pair_max(mx) * sf;
     const bool grow = mx > m_run + kSlack;
     if (__any(grow)) {
       const float alpha = grow ? fast_exp2(m_run - mx) : 1.f;
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(256, 1) void fwd_d512_kernel(FwdArgs a) {
     }
   }
 
-  const float l = l_run + wave_xor32(l_run);
+  const float l = pair_sum(l_run);
   const float inv = 1.f / l;
   if (row_valid) {
     bf16 *optr = reinterpret_cast<bf16 *>(a.o) + (long)(seq0 + t0 + tok) * qld + (long)h * HD + d0;
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
     xf[kc] = as_bf16x8(*reinterpret_cast<const uint4 *>(xptr + kc * 16 + half * 8));
   const float sf = a.scale * kLog2e;
   const float lse2 = a.lse[(long)h * a.lse_ld + qrow] * kLog2e;
-  const float Dq = a.D[(long)h * a.lse_ld + qrow];
+  const float Dq = -a.Dneg[(long)h * a.lse_ld + qrow];
   const int dq0 = wave * (HD / 4);
 
   f32x16 acc[NDQ];
@@ -455,7 +457,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
 
   const int qld_b = (int)(qld * 2);
   const int head0_b = g * G * HD * 2;
-  const __amdgpu_buffer_rsrc_t r_ld = make_rsrc_u(wave == 0 ? (const void *)a.lse2 : (const void *)a.D,
+  const __amdgpu_buffer_rsrc_t r_ld = make_rsrc_u(wave == 0 ? (const void *)a.lsn : (const void *)a.Dneg,
                                                   (uint32_t)((long)a.Hq * a.lse_ld * 4));
   // Fetch the step at the cursor into stage `st`: row r of the step (a flattened
   // (token, head) row) fills 1 KB block r, written by wave r % 4.
@@ -519,11 +521,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
     }
     const char *qs = smem + stage * STAGE;
     const char *dos = qs + TILE;
-    const float *lse_s = reinterpret_cast<const float *>(qs + 2 * TILE);
-    const float *d_s = lse_s + 64;
+    const float *lsn_s = reinterpret_cast<const float *>(qs + 2 * TILE);
+    const float *dn_s = lsn_s + 64;
 
     const char *op = role == 0 ? qs : dos;
+    // The first half's partial starts at -LSE / scale (scores) or -D (dP) of its rows, so
+    // the sums end as <q, k> - LSE / scale and dP - D.
     f32x16 part = zero16();
+    if (dh == 0) {
+      const float *init = role == 0 ? lsn_s : dn_s;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 x4 = *reinterpret_cast<const float4 *>(init + 8 * i + 4 * half);
+        part[4 * i] = x4.x, part[4 * i + 1] = x4.y, part[4 * i + 2] = x4.z, part[4 * i + 3] = x4.w;
+      }
+    }
 #pragma unroll
     for (int kc = 0; kc < NKH; ++kc)
       part = mfma(sw_frag<HD>(op, col, dh * NKH + kc, half), xf[kc], part);
@@ -535,26 +547,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
     const int ta = flo / G, tb = (fend - 1) / G;
     const bool full = (f0 >= flo) && (f0 + BM <= fend) && (32 <= nkeys) &&
                       (kpb <= P + ta) && (wl < 0 || kpa >= P + tb - wl);
-    const int vlo = max(flo, f_vis_lo), vhi = min(fend, f_vis_hi);
     float pv[16], dsv[16];
+    // The visibility test is compiled only into the variant for blocks that straddle a
+    // mask edge or a range end.
+    auto probs = [&](auto masked_c) {
+      constexpr bool MASKED = decltype(masked_c)::value;
+      const int lo = max(flo, f_vis_lo) - f0 - 4 * half;   // visible row offsets [lo, hi)
+      const int hi = min(fend, f_vis_hi) - f0 - 4 * half;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 l4 = *reinterpret_cast<const float4 *>(lse_s + 8 * i + 4 * half);
-      const float4 d4 = *reinterpret_cast<const float4 *>(d_s + 8 * i + 4 * half);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int v = 4 * i + e;
-        float p = fast_exp2(fmaf(st[v], sf, -lv[e]));
-        if (!full) {
-          const int f = f0 + c_row(v, half);
-          if (f < vlo || f >= vhi) p = 0.f;
+      for (int v = 0; v < 16; ++v) {
+        float p = fast_exp2(st[v] * sf);
+        if (MASKED) {
+          const int r = 8 * (v >> 2) + (v & 3);
+          if (r < lo || r >= hi) p = 0.f;
         }
         pv[v] = p;
-        dsv[v] = p * (dpt[v] - dd[e]);
+        dsv[v] = p * dpt[v];
       }
-    }
+    };
+    if (full)
+      probs(std::false_type{});
+    else
+      probs(std::true_type{});
     const bf16x8 p0 = pack8(pv), p1 = pack8(pv + 8);
     const bf16x8 s0 = pack8(dsv), s1 = pack8(dsv + 8);
     // dV += Pᵀ dO and dK += dSᵀ Q over this wave's quarter of the head dim.

@@ -86,6 +86,18 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// max / sum of x over the lane pair (l, l ^ 32) that shares a C-tile column, through
+// v_permlane32_swap (a VALU exchange of the two wave halves, no LDS round trip): of
+// the two results, lanes 0-31 hold (own, partner) and lanes 32-63 (partner, own).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256, WPE) void fwd_bf16_kernel(FwdArgs a) {
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-    mx = fmaxf(mx, wave_xor32(mx)) * sf;
+    mx = pair_max(mx) * sf;
     const bool grow = mx > m_run + kSlack;
     if (__any(grow)) {
       const float alpha = grow ? fast_exp2(m_run - mx) : 1.f;
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256, WPE) void fwd_bf16_kernel(FwdArgs a) {
       }
   }
 
-  const float l = l_run + wave_xor32(l_run);
+  const float l = pair_sum(l_run);
   const float inv = 1.f / l;
   if (row_valid) {
     bf16 *optr = reinterpret_cast<bf16 *>(a.o) + (long)(seq0 + t0 + tok) * qld + (long)h * HD;

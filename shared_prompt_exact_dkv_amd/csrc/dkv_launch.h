@@ -46,18 +46,21 @@ hipError_t launch_fwd_d512(const FwdArgs &a, int n_items, hipStream_t s);
 
 // ---- backward ----
 
-// D[h][t] = sum_c dO[t][h][c] * O[t][h][c] (fp32), rows = T tokens x Hq heads; also
-// lse2[h][t] = LSE[h][t] * log2(e), the row's log-sum-exp in the exponent base the
-// bf16 kernels use.
+// Dneg[h][t] = -sum_c dO[t][h][c] * O[t][h][c] (fp32), rows = T tokens x Hq heads; also
+// lsn[h][t] = -LSE[h][t] / scale, the row's log-sum-exp in units of the raw dot product
+// <q, k>, negated.  The key-parallel bf16 kernels start their score and dP accumulators
+// from these two, so p = exp2(scale * log2(e) * acc) and dS = p * acc' need no per-element
+// subtraction.
 hipError_t launch_bwd_pre(int dtype, int head_dim, const void *o, const void *dout,
-                          const float *lse, float *D, float *lse2, long T, int Hq, hipStream_t s);
+                          const float *lse, float *Dneg, float *lsn, long T, int Hq, float scale,
+                          hipStream_t s);
 hipError_t launch_fill_zero(float *p, long n, hipStream_t s);
 // dst[i] = round(src[i]) in dtype (a copy for fp32).
 hipError_t launch_cast(int dtype, const float *src, void *dst, long n, hipStream_t s);
 
 struct BwdQArgs {
   const void *q, *k_ctx, *v_ctx, *k_own, *v_own, *dout;
-  const float *lse, *D;
+  const float *lse, *Dneg;     // Dneg = -rowsum(dO * O) (from the preprocess kernel)
   void *dq;
   const QItem *items;
   int Hq, Hkv, G, bm_tok, ctx_len, window_left, lse_ld;
@@ -79,8 +82,8 @@ struct KVItem {
 
 struct BwdKVArgs {
   const void *q, *dout, *k_ctx, *v_ctx, *k_own, *v_own;
-  const float *lse, *D;
-  const float *lse2;           // LSE * log2(e) (from the preprocess kernel)
+  const float *lse, *Dneg;     // Dneg = -rowsum(dO * O) (from the preprocess kernel)
+  const float *lsn;            // -LSE / scale (from the preprocess kernel)
   const int32_t *cu;           // device prefix sums of the query sequences
   void *dk_own, *dv_own;       // direct outputs of own-region keys
   float *acc_dk, *acc_dv;      // fp32 accumulators: ctx-region keys, and own keys if own_to_acc

@@ -267,6 +267,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_u(const void *base, 
 // address inside the LDS aperture).
 __device__ __forceinline__ uint32_t lds_u32(const void *p) { return (uint32_t)(uintptr_t)p; }
 
+// 16 bytes read at a 32-bit LDS byte address.
+__device__ __forceinline__ bf16x8 lds_frag_at(uint32_t addr) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) const u32x4 lu32x4;
+  return __builtin_bit_cast(bf16x8, *(lu32x4 *)(size_t)addr);
+}
+
 // Swizzled dense tile [row][HD] bf16: the 16-byte chunk c of row r sits in slot
 // c ^ swz(r).  With rows of 16 or more chunks, swz(r) (bits r3 r2 r1 r0 of r) is
 //   ((r0 ^ r3) << 3) | (r1 << 2) | (r0 << 1) | r2,
