@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--workload", default="qwen3_8b")
     ap.add_argument("--no-ncopy", action="store_true", help="skip the N-copy comparator")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split", action="store_true",
+                    help="sum the shared-prompt gradient through per-chunk slices and a "
+                         "fixed-order reduction (DKV_ACC_SPLIT) instead of fp32 atomics")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (torch), the reference "
@@ -131,10 +134,12 @@ def main():
     dv_p = torch.empty_like(x["v_p"])
     acc = torch.empty((2, P, Hkv, d), dtype=torch.float32, device=dev)
     wsz = max(dkv.dkv_workspace_size(c, x["q_r"], x["k_r"], cu, cu_host=cu_host, ctx_len=P,
-                                     window_left=wl) for c in (1, 3))
+                                     window_left=wl) for c in (1, 3, 4 if args.split else 3))
     wsz = max(wsz, max(dkv.dkv_workspace_size(c, x["q_p"], x["k_p"], cu_p, cu_host=cu_p_host,
                                               window_left=wl) for c in (0, 2)))
     ws = torch.empty(max(wsz, 256), dtype=torch.uint8, device=dev)
+
+    bwd_flags = dkv.DKV_ACC_FINALIZE | (dkv.DKV_ACC_SPLIT if args.split else 0)
 
     def dk_step():
         dkv.dkv_ctx_fwd(x["q_p"], x["k_p"], x["v_p"], cu_p, cu_host=cu_p_host, window_left=wl,
@@ -145,7 +150,7 @@ def main():
                         cu_host=cu_p_host, window_left=wl, dq=dq_p, acc_dk=acc[0],
                         acc_dv=acc[1], acc_flags=dkv.DKV_ACC_ZERO, workspace=ws)
         dkv.dkv_bwd(x["q_r"], x["k_p"], x["v_p"], x["k_r"], x["v_r"], o_r, lse_r, x["do_r"], cu,
-                    acc_dk_p=acc[0], acc_dv_p=acc[1], acc_flags=dkv.DKV_ACC_FINALIZE,
+                    acc_dk_p=acc[0], acc_dv_p=acc[1], acc_flags=bwd_flags,
                     cu_host=cu_host, window_left=wl, dq_r=dq_r, dk_r=dk_r, dv_r=dv_r,
                     dk_p=dk_p, dv_p=dv_p, workspace=ws)
 
@@ -287,6 +292,7 @@ def main():
         "config": {"workload": w.name, "P": P, "N": N,
                    "R": w.R if w.R is not None else "U%s" % (list(w.R_range),),
                    "Hq": Hq, "Hkv": Hkv, "d": d, "window_left": wl,
+                   "prompt_grad_sum": "split" if args.split else "atomic",
                    "parallelism": "single-gpu"},
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
         "speedup_vs_ncopy": round(speedup, 3) if speedup else None,

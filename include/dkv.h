@@ -64,15 +64,25 @@ typedef enum {
     DKV_CALL_CTX_FWD = 0,
     DKV_CALL_FWD = 1,
     DKV_CALL_CTX_BWD = 2,
-    DKV_CALL_BWD = 3
+    DKV_CALL_BWD = 3,
+    DKV_CALL_BWD_SPLIT = 4     /* dkv_bwd with DKV_ACC_SPLIT (adds the slices) */
 } dkv_call;
 
 /* Flags of the shared-prompt gradient accumulator (dkv_ctx_bwd / dkv_bwd). */
 enum {
     DKV_ACC_ZERO = 1,      /* clear acc_dk_p / acc_dv_p before adding this call's terms */
     DKV_ACC_FINALIZE = 2,  /* after adding, cast the accumulator into dk_p / dv_p once */
-    DKV_ACC_SPLIT = 4      /* dkv_bwd only: per-chunk slices + fixed-order reduction
-                              instead of fp32 atomics (bitwise reproducible) */
+    /* dkv_bwd only.  §3.2 Stage 1 resolves the N-way write to the shared dK_c / dV_c
+       with fp32 atomic adds into a scratch buffer (the default here too).  This flag
+       resolves it without atomics, still summing in fp32 and casting once:
+       the responses are taken in S chunks of ceil(N / S) sequences
+       (S = min(N, 8)); a chunk's partial dK_P / dV_P, summed in registers, is stored
+       into its own fp32 slice of the workspace (size it with DKV_CALL_BWD_SPLIT), and
+       one kernel then adds the slices to the accumulator in slice order.  No atomics
+       touch the accumulator, so for given inputs and call order dk_p / dv_p are
+       bitwise reproducible (the Call-1 term of dkv_ctx_bwd has one writer per
+       element).  Workspace: 2 * S * P * Hkv * d * 4 bytes more. */
+    DKV_ACC_SPLIT = 4
 };
 
 typedef struct {

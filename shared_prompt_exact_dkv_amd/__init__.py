@@ -117,7 +117,9 @@ def dkv_bwd(q_resp, k_p, v_p, k_r, v_r, o_r, lse_r, dout_r, cu_seqlens, *, acc_d
             dv_r=None, dk_p=None, dv_p=None, workspace=None):
     """Backward of Call 2 (eq. (4), §3.2).  Adds the responses' prompt-key gradients
     into acc_dk_p/acc_dv_p (fp32 [P,Hkv,d]); with DKV_ACC_FINALIZE also casts the
-    accumulator into dk_p/dv_p.  -> (dq_r, dk_r, dv_r, dk_p, dv_p)."""
+    accumulator into dk_p/dv_p; with DKV_ACC_SPLIT the terms reach the accumulator
+    through per-chunk slices and a fixed-order sum instead of atomic adds.
+    -> (dq_r, dk_r, dv_r, dk_p, dv_p)."""
     p, keep = _params(q_resp, k_r, cu_seqlens, cu_host, k_p.shape[0], window_left,
                       softmax_scale)
     dq_r = torch.empty_like(q_resp) if dq_r is None else dq_r
@@ -126,7 +128,8 @@ def dkv_bwd(q_resp, k_p, v_p, k_r, v_r, o_r, lse_r, dout_r, cu_seqlens, *, acc_d
     if acc_flags & L.DKV_ACC_FINALIZE:
         dk_p = torch.empty_like(k_p) if dk_p is None else dk_p
         dv_p = torch.empty_like(v_p) if dv_p is None else dv_p
-    ws, nws = _ws(p, L.DKV_CALL_BWD, q_resp.device, workspace)
+    call = L.DKV_CALL_BWD_SPLIT if acc_flags & L.DKV_ACC_SPLIT else L.DKV_CALL_BWD
+    ws, nws = _ws(p, call, q_resp.device, workspace)
     L.check(L.lib().dkv_bwd(p, _p(q_resp), _p(k_p), _p(v_p), _p(k_r), _p(v_r), _p(o_r),
                             _p(lse_r), _p(dout_r), _p(dq_r), _p(dk_r), _p(dv_r), _p(acc_dk_p),
                             _p(acc_dv_p), int(acc_flags), _p(dk_p), _p(dv_p), _p(ws), nws,
@@ -159,10 +162,11 @@ def dualkv_forward(q_p, k_p, v_p, q_r, k_r, v_r, cu_seqlens, *, cu_host=None, wi
 
 def dualkv_backward(q_p, k_p, v_p, q_r, k_r, v_r, o_p, lse_p, o_r, lse_r, do_p, do_r,
                     cu_seqlens, *, cu_host=None, window_left=-1, softmax_scale=0.0,
-                    acc=None):
+                    acc=None, split=False):
     """The two calls of the backward sharing one fp32 accumulator for dK_P/dV_P
     (eq. (6)): Call 1 clears it and adds the prompt self-attention term, Call 2 adds
-    the N responses' terms and casts once.  -> dict of dq_p, dk_p, dv_p, dq_r, dk_r,
+    the N responses' terms and casts once (split=True: through per-chunk slices and a
+    fixed-order sum, bitwise reproducible).  -> dict of dq_p, dk_p, dv_p, dq_r, dk_r,
     dv_r."""
     P = q_p.shape[0]
     if acc is None:
@@ -173,7 +177,8 @@ def dualkv_backward(q_p, k_p, v_p, q_r, k_r, v_r, o_p, lse_p, o_r, lse_r, do_p, 
                              acc_dk=acc[0], acc_dv=acc[1], acc_flags=DKV_ACC_ZERO)
     dq_r, dk_r, dv_r, dk_p, dv_p = dkv_bwd(q_r, k_p, v_p, k_r, v_r, o_r, lse_r, do_r,
                                            cu_seqlens, acc_dk_p=acc[0], acc_dv_p=acc[1],
-                                           acc_flags=DKV_ACC_FINALIZE, cu_host=cu_host,
+                                           acc_flags=DKV_ACC_FINALIZE | (DKV_ACC_SPLIT if split else 0),
+                                           cu_host=cu_host,
                                            window_left=window_left,
                                            softmax_scale=softmax_scale)
     return {"dq_p": dq_p, "dk_p": dk_p, "dv_p": dv_p, "dq_r": dq_r, "dk_r": dk_r, "dv_r": dv_r}

@@ -264,9 +264,9 @@ dkv_status upload(const void *src, size_t bytes, void *dst, hipStream_t stream) 
 
 // -------------------------------------------------------------- kernel timing --
 
-enum KernelClass { kKFwd = 0, kKPre, kKDq, kKDkdv, kKZero, kKCast, kKClasses };
+enum KernelClass { kKFwd = 0, kKPre, kKDq, kKDkdv, kKZero, kKCast, kKReduce, kKClasses };
 const char *const kKernelNames[kKClasses] = {"attn_fwd", "bwd_pre", "bwd_dq", "bwd_dkdv",
-                                             "acc_zero", "acc_cast"};
+                                             "acc_zero", "acc_cast", "split_reduce"};
 
 struct Timing {
   std::mutex mu;
@@ -388,6 +388,23 @@ int ctx_chunk(const Shape &s) {
   return 1;
 }
 
+// Split mode: the prompt-key terms of the N responses go to S slices, one per chunk
+// of ceil(N / S) sequences summed in registers; S = min(N, 8) unless DKV_SPLIT_SLICES
+// sets it.  Returns the chunk size; the slice count is ceil(N / chunk).
+int split_chunk(const Shape &s) {
+  static int env = [] {
+    const char *e = getenv("DKV_SPLIT_SLICES");
+    return e ? atoi(e) : 0;
+  }();
+  const int n = std::max(1, s.N);
+  const int slices = std::min(n, env > 0 ? env : 8);
+  return (n + slices - 1) / slices;
+}
+int split_slices(const Shape &s) {
+  const int cs = split_chunk(s);
+  return (std::max(1, s.N) + cs - 1) / cs;
+}
+
 long kv_rows_visible(const Shape &s, bool ctx, int key_start, int nk, int len) {
   long lo, hi;
   if (ctx) {
@@ -402,13 +419,13 @@ long kv_rows_visible(const Shape &s, bool ctx, int key_start, int nk, int len) {
   return std::max<long>(0, hi - lo);
 }
 
-std::vector<KVItem> build_kv_items(const Shape &s, bool with_ctx) {
+std::vector<KVItem> build_kv_items(const Shape &s, bool with_ctx, bool split) {
   // One group per (chunk of sequences): the prompt key tiles that add this chunk's
   // terms to the shared accumulator, and the chunk's own response key tiles.  All of
   // them stream the chunk's query rows.
   struct Rec { long work; int region, key_start, lo, hi; };
   struct Group { long work; std::vector<Rec> recs; };
-  const int cs = (with_ctx && s.P > 0) ? ctx_chunk(s) : 1;
+  const int cs = (with_ctx && s.P > 0) ? (split ? split_chunk(s) : ctx_chunk(s)) : 1;
   std::vector<Group> groups;
   for (int lo = 0; lo < s.N; lo += cs) {
     const int hi = std::min(s.N, lo + cs);
@@ -418,7 +435,9 @@ std::vector<KVItem> build_kv_items(const Shape &s, bool with_ctx) {
         int nk = std::min(s.kv_tile, s.P - k0);
         long w = 0;
         for (int i = lo; i < hi; ++i) w += kv_rows_visible(s, true, k0, nk, s.cu[i + 1] - s.cu[i]);
-        if (w > 0) gr.recs.push_back({w, kRegionCtx, k0, lo, hi});
+        // Split mode keeps tiles no row of the chunk sees: they store the zeros of
+        // their slice, so every slice element is written.
+        if (w > 0 || split) gr.recs.push_back({w, kRegionCtx, k0, lo, hi});
       }
     }
     for (int i = lo; i < hi; ++i) {
@@ -450,11 +469,12 @@ std::vector<KVItem> build_kv_items(const Shape &s, bool with_ctx) {
 }
 
 struct BwdPlan {
-  size_t d_off = 0, l2_off = 0, q_off = 0, kv_off = 0, bytes = 0;
+  size_t d_off = 0, l2_off = 0, q_off = 0, kv_off = 0, split_off = 0, bytes = 0;
   size_t n_q = 0, n_kv = 0;
+  int slices = 0;
 };
 
-BwdPlan plan_bwd(const Shape &s, bool with_ctx) {
+BwdPlan plan_bwd(const Shape &s, bool with_ctx, bool split) {
   BwdPlan pl;
   pl.n_q = count_q_items(s, s.bm_tok_dq);
   size_t nkv = 0;
@@ -463,7 +483,7 @@ BwdPlan plan_bwd(const Shape &s, bool with_ctx) {
     nkv += (size_t)((len + s.kv_tile - 1) / s.kv_tile);
   }
   if (with_ctx && s.P > 0 && s.N > 0) {
-    int cs = ctx_chunk(s);
+    int cs = split ? split_chunk(s) : ctx_chunk(s);
     nkv += (size_t)((s.P + s.kv_tile - 1) / s.kv_tile) * ((s.N + cs - 1) / cs);
   }
   pl.n_kv = nkv * s.Hkv;   // upper bound (empty windowed items are dropped)
@@ -471,7 +491,12 @@ BwdPlan plan_bwd(const Shape &s, bool with_ctx) {
   pl.l2_off = align_up((size_t)s.Hq * s.T * sizeof(float));
   pl.q_off = pl.l2_off + align_up((size_t)s.Hq * s.T * sizeof(float));
   pl.kv_off = pl.q_off + align_up(pl.n_q * sizeof(QItem));
-  pl.bytes = pl.kv_off + align_up(pl.n_kv * sizeof(KVItem));
+  pl.split_off = pl.kv_off + align_up(pl.n_kv * sizeof(KVItem));
+  pl.bytes = pl.split_off;
+  if (split && with_ctx && s.P > 0) {   // dK and dV slices
+    pl.slices = split_slices(s);
+    pl.bytes += 2 * align_up((size_t)pl.slices * s.P * s.Hkv * s.d * sizeof(float));
+  }
   if (s.T == 0) pl.bytes = 0;
   return pl;
 }
@@ -490,7 +515,8 @@ struct BwdIO {
 
 dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
                    hipStream_t stream) {
-  BwdPlan pl = plan_bwd(s, io.with_ctx);
+  const bool split = (io.flags & DKV_ACC_SPLIT) && io.with_ctx && s.P > 0;
+  BwdPlan pl = plan_bwd(s, io.with_ctx, split);
   dkv_status st = check_ws(ws, ws_bytes, pl.bytes);
   if (st != DKV_OK) return st;
   char *wsb = static_cast<char *>(ws);
@@ -512,7 +538,7 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
     });
     if (e != hipSuccess) return hip_fail(e, "bwd preprocess launch");
     std::vector<QItem> qi = build_q_items(s, s.bm_tok_dq, kFwdBN);
-    std::vector<KVItem> kv = build_kv_items(s, io.with_ctx);
+    std::vector<KVItem> kv = build_kv_items(s, io.with_ctx, split);
     if ((st = upload(qi.data(), qi.size() * sizeof(QItem), wsb + pl.q_off, stream)) != DKV_OK) return st;
     if ((st = upload(kv.data(), kv.size() * sizeof(KVItem), wsb + pl.kv_off, stream)) != DKV_OK) return st;
     BwdQArgs qa{};
@@ -531,8 +557,27 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
     ka.Hq = s.Hq; ka.Hkv = s.Hkv; ka.G = s.G; ka.ctx_len = s.P; ka.window_left = s.wl;
     ka.lse_ld = (int)s.T; ka.own_to_acc = io.own_to_acc ? 1 : 0;
     ka.scale = s.scale;
+    float *slices = reinterpret_cast<float *>(wsb + pl.split_off);
+    const long slice_elems = (long)s.P * s.Hkv * s.d;
+    const size_t slice_bytes = align_up((size_t)pl.slices * slice_elems * sizeof(float));
+    if (split) {
+      ka.split_dk = slices;
+      ka.split_dv = reinterpret_cast<float *>(wsb + pl.split_off + slice_bytes);
+      ka.split_stride = slice_elems;
+      ka.split_chunk = split_chunk(s);
+    }
     e = timed(kKDkdv, stream, [&] { return launch_bwd_dkdv(s.dtype, s.d, ka, (int)kv.size(), stream); });
     if (e != hipSuccess) return hip_fail(e, "dkdv kernel launch");
+    if (split) {
+      e = timed(kKReduce, stream, [&] {
+        hipError_t r = launch_split_reduce(io.acc_dk, ka.split_dk, pl.slices, slice_elems,
+                                           acc_elems, stream);
+        return r != hipSuccess ? r
+                               : launch_split_reduce(io.acc_dv, ka.split_dv, pl.slices,
+                                                     slice_elems, acc_elems, stream);
+      });
+      if (e != hipSuccess) return hip_fail(e, "split reduce launch");
+    }
   }
   if ((io.flags & DKV_ACC_FINALIZE) && io.acc_dk) {
     e = timed(kKCast, stream, [&] {
@@ -597,13 +642,14 @@ int dkv_timing_read(const char **names, double *ms, int *launches, int max_entri
 size_t dkv_workspace_size(const dkv_params *p, int which_call) {
   Shape s;
   bool is_ctx = which_call == DKV_CALL_CTX_FWD || which_call == DKV_CALL_CTX_BWD;
-  if (which_call < DKV_CALL_CTX_FWD || which_call > DKV_CALL_BWD) {
+  if (which_call < DKV_CALL_CTX_FWD || which_call > DKV_CALL_BWD_SPLIT) {
     fail(DKV_ERR_INVALID_ARG, "unknown call %d", which_call);
     return (size_t)-1;
   }
   if (check_params(p, is_ctx, &s) != DKV_OK) return (size_t)-1;
   if (which_call == DKV_CALL_CTX_FWD || which_call == DKV_CALL_FWD) return plan_fwd(s).bytes;
-  return plan_bwd(s, which_call == DKV_CALL_BWD).bytes;
+  const bool with_ctx = which_call == DKV_CALL_BWD || which_call == DKV_CALL_BWD_SPLIT;
+  return plan_bwd(s, with_ctx, which_call == DKV_CALL_BWD_SPLIT).bytes;
 }
 
 dkv_status dkv_ctx_fwd(const dkv_params *p, const void *q, const void *k, const void *v,
@@ -679,9 +725,7 @@ dkv_status dkv_bwd(const dkv_params *p, const void *q_resp, const void *k_p, con
   Shape s;
   dkv_status st = check_params(p, false, &s);
   if (st != DKV_OK) return st;
-  if (acc_flags & DKV_ACC_SPLIT)
-    return fail(DKV_ERR_UNSUPPORTED, "DKV_ACC_SPLIT is not available in this build");
-  if (acc_flags & ~(DKV_ACC_ZERO | DKV_ACC_FINALIZE))
+  if (acc_flags & ~(DKV_ACC_ZERO | DKV_ACC_FINALIZE | DKV_ACC_SPLIT))
     return fail(DKV_ERR_INVALID_ARG, "unknown accumulator flags 0x%x", acc_flags);
   bool need = s.T > 0;
   bool needp = s.P > 0;

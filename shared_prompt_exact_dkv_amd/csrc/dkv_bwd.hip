@@ -66,6 +66,30 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *p, long n) {
   }
 }
 
+// Fixed-order sum of the split mode's slices into the accumulator: each element is
+// added slice by slice, so the result does not depend on scheduling.
+__global__ __launch_bounds__(256) void split_reduce_kernel(float *acc, const float *slices,
+                                                           int n_slices, long stride, long n) {
+  const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i + 3 < n) {
+    float4 v = *reinterpret_cast<const float4 *>(acc + i);
+    for (int c = 0; c < n_slices; ++c) {
+      const float4 x = *reinterpret_cast<const float4 *>(slices + c * stride + i);
+      v.x += x.x;
+      v.y += x.y;
+      v.z += x.z;
+      v.w += x.w;
+    }
+    *reinterpret_cast<float4 *>(acc + i) = v;
+  } else {
+    for (long j = i; j < n; ++j) {
+      float v = acc[j];
+      for (int c = 0; c < n_slices; ++c) v += slices[c * stride + j];
+      acc[j] = v;
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void cast_kernel(const float *src, T *dst, long n) {
   long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
@@ -667,7 +691,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
       const long off = (long)(own0 + it.key_start + k) * kld + (long)g * HD + db * 32 + col;
       const float gk = dk[db][v] * a.scale;
       const float gv = dv[db][v];
-      if (to_acc) {
+      if (ctx && a.split_dk) {   // split mode: the chunk's own slice, one writer
+        const long so = (long)(it.seq_lo / a.split_chunk) * a.split_stride + off;
+        a.split_dk[so] = gk;
+        a.split_dv[so] = gv;
+      } else if (to_acc) {
         atomicAdd(a.acc_dk + off, gk);
         atomicAdd(a.acc_dv + off, gv);
       } else {
@@ -976,7 +1004,11 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
       const long off = (long)(own0 + it.key_start + k) * kld + (long)g * HD + db * 32 + col;
       const float gk = dk[db][v] * a.scale;
       const float gv = dv[db][v];
-      if (to_acc) {
+      if (ctx && a.split_dk) {   // split mode: the chunk's own slice, one writer
+        const long so = (long)(it.seq_lo / a.split_chunk) * a.split_stride + off;
+        a.split_dk[so] = gk;
+        a.split_dv[so] = gv;
+      } else if (to_acc) {
         atomicAdd(a.acc_dk + off, gk);
         atomicAdd(a.acc_dv + off, gv);
       } else {
@@ -1018,6 +1050,15 @@ hipError_t launch_fill_zero(float *p, long n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   long blocks = (n + 1023) / 1024;
   hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_reduce(float *acc, const float *slices, int n_slices, long stride,
+                               long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  long blocks = (n + 1023) / 1024;
+  hipLaunchKernelGGL(split_reduce_kernel, dim3(blocks), dim3(256), 0, s, acc, slices, n_slices,
+                     stride, n);
   return hipGetLastError();
 }
 

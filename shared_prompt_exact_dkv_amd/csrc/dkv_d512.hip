@@ -594,7 +594,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
       const long off = (long)(own0 + it.key_start + k) * kld + (long)g * HD + dq0 + db * 32 + col;
       const float gk = dk[db][v] * a.scale;
       const float gv = dv[db][v];
-      if (to_acc) {
+      if (ctx && a.split_dk) {   // split mode: the chunk's own slice, one writer
+        const long so = (long)(it.seq_lo / a.split_chunk) * a.split_stride + off;
+        a.split_dk[so] = gk;
+        a.split_dv[so] = gv;
+      } else if (to_acc) {
         atomicAdd(a.acc_dk + off, gk);
         atomicAdd(a.acc_dv + off, gv);
       } else {

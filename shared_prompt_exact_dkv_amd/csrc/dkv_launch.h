@@ -55,6 +55,10 @@ hipError_t launch_bwd_pre(int dtype, int head_dim, const void *o, const void *do
                           const float *lse, float *Dneg, float *lsn, long T, int Hq, float scale,
                           hipStream_t s);
 hipError_t launch_fill_zero(float *p, long n, hipStream_t s);
+// acc[i] += slices[0][i] + slices[1][i] + ... + slices[n_slices - 1][i], added in
+// slice order (the fixed-order reduction of the split mode), slices `stride` apart.
+hipError_t launch_split_reduce(float *acc, const float *slices, int n_slices, long stride,
+                               long n, hipStream_t s);
 // dst[i] = round(src[i]) in dtype (a copy for fp32).
 hipError_t launch_cast(int dtype, const float *src, void *dst, long n, hipStream_t s);
 
@@ -87,6 +91,11 @@ struct BwdKVArgs {
   const int32_t *cu;           // device prefix sums of the query sequences
   void *dk_own, *dv_own;       // direct outputs of own-region keys
   float *acc_dk, *acc_dv;      // fp32 accumulators: ctx-region keys, and own keys if own_to_acc
+  // Split mode (non-null split_dk): ctx-region items store their partial sums into
+  // slice seq_lo / split_chunk of [slices][P][Hkv][d] instead of adding atomically.
+  float *split_dk, *split_dv;
+  long split_stride;           // elements per slice (P * Hkv * d)
+  int split_chunk;             // sequences per ctx item
   const KVItem *items;
   int Hq, Hkv, G, ctx_len, window_left, lse_ld;
   int own_to_acc;

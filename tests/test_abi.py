@@ -97,3 +97,36 @@ def test_empty_batch_is_a_no_op():
     lib = L.lib()
     assert lib.dkv_workspace_size(p, L.DKV_CALL_FWD) == 0
     assert lib.dkv_fwd(p, None, None, None, None, None, None, None, None, 0, None) == L.DKV_OK
+
+
+def test_split_workspace_adds_the_slices():
+    # N = 2 responses: one sequence per chunk in both modes, so the split workspace is
+    # the plain one plus the dK and dV slices, 2 * S * P * Hkv * d fp32 with S = N.
+    p, keep = _params()   # N = 2, P = 16, Hkv = 2, d = 128
+    lib = L.lib()
+    plain = lib.dkv_workspace_size(p, L.DKV_CALL_BWD)
+    split = lib.dkv_workspace_size(p, L.DKV_CALL_BWD_SPLIT)
+    assert split - plain == 2 * (2 * 16 * 2 * 128 * 4)
+    # many responses: at most 8 slices
+    cu = [0] + [5 * (i + 1) for i in range(20)]
+    p20, k20 = _params(num_seqs=20, cu_host=cu)
+    extra = lib.dkv_workspace_size(p20, L.DKV_CALL_BWD_SPLIT) - lib.dkv_workspace_size(
+        p20, L.DKV_CALL_BWD)
+    assert 0 < extra <= 2 * (8 * 16 * 2 * 128 * 4)
+
+
+def test_split_flag_validation():
+    p, keep = _params()
+    lib = L.lib()
+    plain = lib.dkv_workspace_size(p, L.DKV_CALL_BWD)
+    F = FAKE
+    # Call 1 has a single writer per element already: no split mode there
+    pc, keepc = _params(ctx_len=0)
+    st = lib.dkv_ctx_bwd(pc, F, F, F, F, F, F, F, F, F, F, F, L.DKV_ACC_SPLIT, F, 1 << 20, None)
+    assert st == L.DKV_ERR_INVALID_ARG
+    # a workspace sized for the atomic mode is too small for the slices
+    st = lib.dkv_bwd(p, F, F, F, F, F, F, F, F, F, F, F, F, F, L.DKV_ACC_SPLIT, F, F, F, plain,
+                     None)
+    assert st == L.DKV_ERR_WORKSPACE
+    st = lib.dkv_bwd(p, F, F, F, F, F, F, F, F, F, F, F, F, F, 8, F, F, F, plain, None)
+    assert st == L.DKV_ERR_INVALID_ARG and "flags" in L.last_error()

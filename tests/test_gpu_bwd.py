@@ -41,7 +41,7 @@ CASES = [
 ]
 
 
-def _run(P, lens, Hq, Hkv, d, wl, dtype, scaled, seed):
+def _run(P, lens, Hq, Hkv, d, wl, dtype, scaled, seed, split=False):
     x = workloads.make_inputs(P, lens, Hq, Hkv, d, dtype, seed=seed, scaled=scaled)
     N = len(lens)
     do_copies = workloads.split_prompt_grad(x["do_p"], N, seed=seed)
@@ -52,7 +52,7 @@ def _run(P, lens, Hq, Hkv, d, wl, dtype, scaled, seed):
                                                 cu_host=t["cu_host"], window_left=wl)
     g = dkv.dualkv_backward(t["q_p"], t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], o_p,
                             lse_p, o_r, lse_r, t["do_p"], t["do_r"], t["cu"],
-                            cu_host=t["cu_host"], window_left=wl)
+                            cu_host=t["cu_host"], window_left=wl, split=split)
     torch.cuda.synchronize()
     return x, t, ref, g, (o_p, lse_p, o_r, lse_r)
 
@@ -136,3 +136,41 @@ def test_repeated_backward_consistent():
         torch.cuda.synchronize()
         for k in GRADS:
             check(k, g2[k], ref[k], "fp32")
+
+
+# Split mode (DKV_ACC_SPLIT): chunks of ceil(N / 8) responses store their prompt-key
+# sums into slices, added in slice order.  N > 8 gives chunks of several sequences;
+# the windowed cases have prompt tiles that no row of a chunk sees (zero slices).
+SPLIT_CASES = [
+    # P, lens, Hq, Hkv, d, window_left, dtype
+    (130, [77, 64, 129], 8, 2, 128, -1, "bf16"),
+    (96, [40, 0, 33, 70, 1, 20, 55, 64, 12, 90, 8, 31], 8, 2, 128, -1, "bf16"),
+    (300, [140, 260, 1, 90, 17, 3, 200, 45, 9, 60], 8, 2, 64, 100, "bf16"),
+    (70, [65, 3, 40], 8, 2, 128, -1, "fp32"),
+    (100, [150, 20], 16, 4, 512, 63, "bf16"),
+]
+
+
+@pytest.mark.parametrize("P,lens,Hq,Hkv,d,wl,dtype", SPLIT_CASES)
+def test_split_mode_matches_oracle_and_repeats_bitwise(P, lens, Hq, Hkv, d, wl, dtype):
+    x, t, ref, g, (o_p, lse_p, o_r, lse_r) = _run(P, lens, Hq, Hkv, d, wl, dtype, False,
+                                                  seed=11 + P, split=True)
+    for k in GRADS:
+        check(k, g[k], ref[k], dtype)
+    # a second run gives the same bits for every gradient
+    g2 = dkv.dualkv_backward(t["q_p"], t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], o_p,
+                             lse_p, o_r, lse_r, t["do_p"], t["do_r"], t["cu"],
+                             cu_host=t["cu_host"], window_left=wl, split=True)
+    torch.cuda.synchronize()
+    for k in GRADS:
+        assert torch.equal(g[k], g2[k]), k
+    # the atomic mode sums the same fp32 terms in another order
+    ga = dkv.dualkv_backward(t["q_p"], t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], o_p,
+                             lse_p, o_r, lse_r, t["do_p"], t["do_r"], t["cu"],
+                             cu_host=t["cu_host"], window_left=wl)
+    torch.cuda.synchronize()
+    for k in ("dq_p", "dq_r", "dk_r", "dv_r"):
+        assert torch.equal(g[k], ga[k]), k
+    for k in ("dk_p", "dv_p"):
+        check(k + " (atomic vs split)", ga[k], g[k].detach().float().cpu().numpy().astype(np.float64),
+              dtype)

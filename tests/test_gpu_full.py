@@ -45,14 +45,16 @@ def _check(name, got, ref, bound=None):
     assert err <= b, "%s: max|err| = %.3e > %.3e" % (name, err, b)
 
 
-@pytest.mark.parametrize("name", ["qwen3_8b", "dapo_varlen", "large_rollout", "d512_global",
-                                  "d512_swa"])
-def test_full_size_parity(name):
+@pytest.mark.parametrize("name,split", [("qwen3_8b", False), ("dapo_varlen", False),
+                                        ("large_rollout", False), ("d512_global", False),
+                                        ("d512_swa", False), ("qwen3_8b", True),
+                                        ("d512_swa", True)])
+def test_full_size_parity(name, split):
     w = workloads.WORKLOADS[name]
     lens = w.resp_lens()
     N, P, Hq, Hkv, d, wl = w.N, w.P, w.Hq, w.Hkv, w.d, w.window_left
-    print("[full] %s: P=%d N=%d Hq=%d Hkv=%d d=%d wl=%d T=%d" % (name, P, N, Hq, Hkv, d, wl,
-                                                                 sum(lens)), flush=True)
+    print("[full] %s: P=%d N=%d Hq=%d Hkv=%d d=%d wl=%d T=%d split=%d" % (
+        name, P, N, Hq, Hkv, d, wl, sum(lens), split), flush=True)
     x = workloads.make_inputs(P, lens, Hq, Hkv, d, "bf16", seed=w.seed, scaled=w.scaled,
                               dout=False)
     cu = [int(c) for c in x["cu"]]
@@ -79,7 +81,8 @@ def test_full_size_parity(name):
                                                 t["v_r"], cu_d, cu_host=cu, window_left=wl)
     gr = dkv.dualkv_backward(t["q_p"], t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], o_p,
                              lse_p, o_r, lse_r, do_p.to(torch.bfloat16).to(DEV),
-                             do_r.to(torch.bfloat16).to(DEV), cu_d, cu_host=cu, window_left=wl)
+                             do_r.to(torch.bfloat16).to(DEV), cu_d, cu_host=cu, window_left=wl,
+                             split=split)
     torch.cuda.synchronize()
     print("[full] %s: GPU done" % name, flush=True)
 
