@@ -481,8 +481,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
   const bool ctx = it.region == kRegionCtx;
   const long qld = (long)a.Hq * HD;
   const long kld = (long)a.Hkv * HD;
-  const int own0 = ctx ? 0 : a.cu[it.seq_lo];                  // row of the own sequence
-  const int nkeys = ctx ? P - it.key_start : a.cu[it.seq_lo + 1] - own0 - it.key_start;
+  const int own0 = ctx ? 0 : sload_i32(a.cu, it.seq_lo);                  // row of the own sequence
+  const int nkeys = ctx ? P - it.key_start : sload_i32(a.cu, it.seq_lo + 1) - own0 - it.key_start;
   const int kbase = ctx ? 0 : P;                               // logical position offset
   const int nk_tile = min(BNW, nkeys);
 
@@ -526,7 +526,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
 
   // Query rows that can see this key tile, per sequence, in flattened units.
   auto seq_range = [&](int s, int &fa, int &fb) {
-    int len = a.cu[s + 1] - a.cu[s];
+    int len = sload_i32(a.cu, s + 1) - sload_i32(a.cu, s);
     int r_lo, r_hi;
     if (ctx) {
       r_lo = 0;
@@ -566,7 +566,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
   QStepRegs<T, HD> qregs, dregs;
   float lse_r = INFINITY, d_r = 0.f;
   auto issue = [&]() {
-    const int s0 = a.cu[cs];
+    const int s0 = sload_i32(a.cu, cs);
     const int lo = max(cf, cfa), hi = min(cf + BM, cfb);
     const T *qb = reinterpret_cast<const T *>(a.q) + (long)s0 * qld + (long)g * G * HD;
     const T *db_ = reinterpret_cast<const T *>(a.dout) + (long)s0 * qld + (long)g * G * HD;
@@ -734,8 +734,8 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
   const bool ctx = it.region == kRegionCtx;
   const long qld = (long)a.Hq * HD;
   const long kld = (long)a.Hkv * HD;
-  const int own0 = ctx ? 0 : a.cu[it.seq_lo];
-  const int nkeys = ctx ? P - it.key_start : a.cu[it.seq_lo + 1] - own0 - it.key_start;
+  const int own0 = ctx ? 0 : sload_i32(a.cu, it.seq_lo);
+  const int nkeys = ctx ? P - it.key_start : sload_i32(a.cu, it.seq_lo + 1) - own0 - it.key_start;
   const int kbase = ctx ? 0 : P;
   const int nk_tile = min(BNW, nkeys);
 
@@ -794,7 +794,7 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
 
   // Query rows that can see this key tile, per sequence, in flattened units.
   auto seq_range = [&](int sq, int &fa, int &fb) {
-    int len = a.cu[sq + 1] - a.cu[sq];
+    int len = sload_i32(a.cu, sq + 1) - sload_i32(a.cu, sq);
     int r_lo, r_hi;
     if (ctx) {
       r_lo = 0;
@@ -828,16 +828,6 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
   };
   seek();
 
-  // The rows and chunks this lane fetches into a step's swizzled Q / dO tiles.
-  int trow[KPW], jrow[KPW], cofs[KPW];
-#pragma unroll
-  for (int k = 0; k < KPW; ++k) {
-    const int slot = (k * 4 + wave) * 64 + lane;
-    const int r = slot / CPR;
-    trow[k] = r / G;
-    jrow[k] = r - trow[k] * G;
-    cofs[k] = ((slot % CPR) ^ Swz<HD>::swz(r)) << 4;
-  }
   const int tl = lane / G, jl = lane - tl * G;   // this lane's row of the LSE / D fetch
   const int qld_b = (int)(qld * 2);
   const int head0_b = g * G * HD * 2;
@@ -847,8 +837,8 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
 
   // Fetch the step at the cursor into stage `st`.
   auto issue = [&](char *st) {
-    const int s0 = a.cu[cs];
-    const int len = a.cu[cs + 1] - s0;
+    const int s0 = sload_i32(a.cu, cs);
+    const int len = sload_i32(a.cu, cs + 1) - s0;
     const __amdgpu_buffer_rsrc_t rq =
         make_rsrc_u(reinterpret_cast<const bf16 *>(a.q) + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
     const __amdgpu_buffer_rsrc_t rd =
@@ -857,12 +847,16 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
     const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_u32(st) + wave * 1024);
 #pragma unroll
     for (int k = 0; k < KPW; ++k) {
-      int t = ft + trow[k], j = fj + jrow[k];
+      // the row and chunk this lane fetches into the step's swizzled Q / dO tiles
+      const int slot = (k * 4 + wave) * 64 + lane;
+      const int r = slot / CPR;
+      const int tr_ = r / G;
+      int t = ft + tr_, j = fj + (r - tr_ * G);
       if (j >= G) {
         j -= G;
         ++t;
       }
-      const int off = t * qld_b + head0_b + j * (HD * 2) + cofs[k];
+      const int off = t * qld_b + head0_b + j * (HD * 2) + (((slot % CPR) ^ Swz<HD>::swz(r)) << 4);
       dma16(rq, l0 + k * 4096, off);
       dma16(rd, l0 + TILE + k * 4096, off);
     }

@@ -391,8 +391,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
   const bool ctx = it.region == kRegionCtx;
   const long qld = (long)a.Hq * HD;
   const long kld = (long)a.Hkv * HD;
-  const int own0 = ctx ? 0 : a.cu[it.seq_lo];
-  const int nkeys = ctx ? P - it.key_start : a.cu[it.seq_lo + 1] - own0 - it.key_start;
+  const int own0 = ctx ? 0 : sload_i32(a.cu, it.seq_lo);
+  const int nkeys = ctx ? P - it.key_start : sload_i32(a.cu, it.seq_lo + 1) - own0 - it.key_start;
   const int kbase = ctx ? 0 : P;
   const int nk_tile = min(kBwdBN512, nkeys);
 
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
   }
 
   auto seq_range = [&](int sq, int &fa, int &fb) {
-    int len = a.cu[sq + 1] - a.cu[sq];
+    int len = sload_i32(a.cu, sq + 1) - sload_i32(a.cu, sq);
     int r_lo, r_hi;
     if (ctx) {
       r_lo = 0;
@@ -462,8 +462,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
   // Fetch the step at the cursor into stage `st`: row r of the step (a flattened
   // (token, head) row) fills 1 KB block r, written by wave r % 4.
   auto issue = [&](char *st) {
-    const int s0 = a.cu[cs];
-    const int len = a.cu[cs + 1] - s0;
+    const int s0 = sload_i32(a.cu, cs);
+    const int len = sload_i32(a.cu, cs + 1) - s0;
     const __amdgpu_buffer_rsrc_t rq =
         make_rsrc_u(reinterpret_cast<const bf16 *>(a.q) + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
     const __amdgpu_buffer_rsrc_t rd =

@@ -250,7 +250,17 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr
       : "s"(lds_addr), "v"(voff), "s"(r)
       : "memory");
 }
-__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima), issued through the
+// builtin so that the compiler's own wait insertion knows every earlier vector-memory
+// load has completed.  Through inline assembly it would not: it would keep loads from
+// before the DMA loop (the Q fragments, say) pending and wait for them inside the loop
+// with counts that, since the DMA loads of the next tile also count, stall on that
+// tile's arrival.
+__device__ __forceinline__ void dma_wait() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  asm volatile("" ::: "memory");
+}
 
 // A buffer resource built from values the compiler cannot prove wave-uniform (the
 // callers' are uniform by construction): the operands of the DMA instructions must
@@ -266,6 +276,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_u(const void *base, 
 // LDS byte address of a pointer into __shared__ memory (the low 32 bits of its flat
 // address inside the LDS aperture).
 __device__ __forceinline__ uint32_t lds_u32(const void *p) { return (uint32_t)(uintptr_t)p; }
+
+// cu[i] for a wave-uniform index, through the scalar unit (waited for on the LDS /
+// scalar counter).  A vector load here would count on the vector-memory counter, and
+// the wait for it would also wait for the DMA loads of the next stage in flight.
+__device__ __forceinline__ int32_t sload_i32(const int32_t *base, int i) {
+  const uint64_t p = (uint64_t)(uintptr_t)(base + i);
+  const uint64_t pu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(pu));
+  return v;
+}
 
 // 16 bytes read at a 32-bit LDS byte address.
 __device__ __forceinline__ bf16x8 lds_frag_at(uint32_t addr) {
