@@ -937,6 +937,14 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
           st = mfma(as_bf16x8(*reinterpret_cast<const uint4 *>(qrow)), lds_frag_at(kt + fo[kc]), st);
           dpt = mfma(as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + TILE)), vf[kc], dpt);
         }
+        // three fragment reads (Q, K, dO) ahead of each pair of products
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int kc = 0; kc < NKC - 2; ++kc) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         __builtin_amdgcn_s_setprio(0);
         const bool full = b0 >= max(flo, full_lo) && b0 + 32 <= min(fend, full_hi);
         float pv[16], dsv[16];

@@ -123,6 +123,14 @@ __global__ __launch_bounds__(256, WPE) void fwd_bf16_kernel(FwdArgs a) {
       for (int kb = 0; kb < NKB; ++kb)
         s[kb] = mfma(sw_frag<HD>(ks, kb * 32 + col, kc, half), qf[kc], s[kb]);
     }
+    // K fragment reads four products ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int j = 0; j < NKC * NKB - 4; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
     const bool need_mask = (nrows < BN) || (kpos0 + BN - 1 > qmin) ||
                            (wl >= 0 && kpos0 < qmax - wl);
