@@ -325,6 +325,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
   const float sf = a.scale * kLog2e;
   const float lse2 = a.lse[(long)h * a.lse_ld + qrow] * kLog2e;
   const float Dq = -a.Dneg[(long)h * a.lse_ld + qrow];
+  // dP accumulators start from -D (this lane's row): the products end as dP - D.
+  f32x16 negd;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) negd[v] = -Dq;
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -380,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
 
 #pragma unroll
     for (int hb = 0; hb < BN / 32; ++hb) {
-      f32x16 st = zero16(), dpt = zero16();
+      f32x16 st = zero16(), dpt = negd;
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
         st = mfma(sw_frag<HD>(ks, hb * 32 + col, kc, half), qf[kc], st);
@@ -402,7 +406,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
             const int r = 8 * (v >> 2) + (v & 3);
             if (r < lo || r >= hi) p = 0.f;
           }
-          ds[v] = p * (dpt[v] - Dq);
+          ds[v] = p * dpt[v];
         }
       };
       if (need_mask)
