@@ -52,7 +52,10 @@ extern "C" {
 typedef enum {
     DKV_OK = 0,
     DKV_ERR_INVALID_ARG = 1,   /* inconsistent shapes, bad cu_seqlens, null pointers */
-    DKV_ERR_UNSUPPORTED = 2,   /* valid but not implemented (e.g. head_dim) */
+    /* valid but not implemented: head_dim 512 in fp32, Hq / Hkv above 128 (32 at
+       head_dim 512), or (bf16) a sequence whose query rows, plus 64, exceed 2^31 bytes
+       or Hq * tokens above 2^29 -- the kernels' 32-bit row offsets */
+    DKV_ERR_UNSUPPORTED = 2,
     DKV_ERR_WORKSPACE = 3,     /* ws too small or misaligned */
     DKV_ERR_HIP = 4            /* a HIP runtime call failed */
 } dkv_status;

@@ -97,6 +97,22 @@ dkv_status check_params(const dkv_params *p, bool is_ctx, Shape *s) {
   s->T = s->cu[s->N];
   if (s->T > 0 && !p->cu_seqlens_dev)
     return fail(DKV_ERR_INVALID_ARG, "cu_seqlens_dev is NULL");
+  if (s->dtype == DKV_BF16) {
+    // The bf16 backward addresses a sequence's query rows, and the LSE / D rows, with
+    // 32-bit byte offsets from the sequence's start (buffer loads): the query rows of
+    // one sequence (plus one 64-row step of slack) and Hq * T LSE entries must stay
+    // below 2^31 bytes.
+    long max_len = 0;
+    for (int i = 0; i < s->N; ++i) max_len = std::max<long>(max_len, s->cu[i + 1] - s->cu[i]);
+    const long row_bytes = (long)s->Hq * s->d * 2;
+    if ((max_len + 64) * row_bytes > 0x7fffffffL)
+      return fail(DKV_ERR_UNSUPPORTED,
+                  "a sequence of %ld query rows x %ld bytes exceeds the 2^31-byte range of "
+                  "the bf16 kernels' offsets", max_len, row_bytes);
+    if ((long)s->Hq * s->T * 4 > 0x7fffffffL)
+      return fail(DKV_ERR_UNSUPPORTED, "Hq * tokens = %ld LSE entries exceed 2^29",
+                  (long)s->Hq * s->T);
+  }
   s->bm_tok = kRowsPerWG / G;
   s->bm_tok_dq = s->bm_tok;
   s->kv_tile = kBwdBN;

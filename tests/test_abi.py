@@ -130,3 +130,23 @@ def test_split_flag_validation():
     assert st == L.DKV_ERR_WORKSPACE
     st = lib.dkv_bwd(p, F, F, F, F, F, F, F, F, F, F, F, F, F, 8, F, F, F, plain, None)
     assert st == L.DKV_ERR_INVALID_ARG and "flags" in L.last_error()
+
+
+def test_offset_range_limits():
+    # The bf16 kernels address a sequence's rows with 32-bit byte offsets: a sequence
+    # whose query rows pass 2^31 bytes is refused up front, and the largest that fits
+    # is accepted.
+    lib = L.lib()
+    row = 32 * 128 * 2                        # Hq = 32, d = 128, bf16
+    longest = (1 << 31) // row - 64 - 1
+    ok, k1 = _params(num_seqs=1, ctx_len=16, num_heads_q=32, num_heads_kv=8,
+                     cu_host=[0, longest])
+    assert lib.dkv_workspace_size(ok, L.DKV_CALL_FWD) != ctypes.c_size_t(-1).value
+    bad, k2 = _params(num_seqs=1, ctx_len=16, num_heads_q=32, num_heads_kv=8,
+                      cu_host=[0, longest + 2])
+    st = lib.dkv_fwd(bad, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None)
+    assert st == L.DKV_ERR_UNSUPPORTED and "2^31" in L.last_error()
+    # fp32 kernels use 64-bit row offsets: no such limit
+    f32, k3 = _params(num_seqs=1, ctx_len=16, num_heads_q=32, num_heads_kv=8,
+                      cu_host=[0, longest + 2], dtype=L.DKV_FP32)
+    assert lib.dkv_workspace_size(f32, L.DKV_CALL_FWD) != ctypes.c_size_t(-1).value
