@@ -97,6 +97,14 @@ dkv_status check_params(const dkv_params *p, bool is_ctx, Shape *s) {
   s->T = s->cu[s->N];
   if (s->T > 0 && !p->cu_seqlens_dev)
     return fail(DKV_ERR_INVALID_ARG, "cu_seqlens_dev is NULL");
+  {
+    // A window at least as long as the longest logical position sees every earlier
+    // key: it is the global causal mask, and is run as one (the kernels form key + wl
+    // and (key + wl) * G in 32-bit arithmetic).
+    long max_len = 0;
+    for (int i = 0; i < s->N; ++i) max_len = std::max<long>(max_len, s->cu[i + 1] - s->cu[i]);
+    if (s->wl >= 0 && (long)s->wl >= (long)s->P + max_len) s->wl = -1;
+  }
   if (s->dtype == DKV_BF16) {
     // The bf16 backward addresses a sequence's query rows, and the LSE / D rows, with
     // 32-bit byte offsets from the sequence's start (buffer loads): the query rows of

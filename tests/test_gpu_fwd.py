@@ -30,6 +30,12 @@ CASES = [
     (129, [33, 64, 1], 4, 1, 512, 40, "bf16", False),
     (100, [150, 20], 16, 4, 512, 63, "bf16", False),
     (0, [80], 4, 4, 512, -1, "bf16", False),
+    # the largest grouped-query ratios (128 at head dims 64 / 128, 32 at 512), and a
+    # window far past every position (run as the global mask)
+    (37, [40, 3], 128, 1, 64, -1, "bf16", False),
+    (20, [33], 128, 1, 128, 15, "bf16", False),
+    (24, [40, 9], 32, 1, 512, -1, "bf16", False),
+    (50, [40, 90], 8, 2, 128, 2147483647, "bf16", False),
 ]
 
 
