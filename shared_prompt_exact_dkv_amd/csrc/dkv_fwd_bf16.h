@@ -14,9 +14,9 @@ namespace dkv {
 //
 // The bf16 path for head dims 64 and 128 (HD = 512 has its own kernels): 64-key
 // tiles at two waves per SIMD (WPE = 2, <= 256 registers).
-//   - K and V tiles both in the padded row layout, double-buffered in LDS with one
-//     barrier per tile; the next-but-one tile's global loads are in flight in
-//     registers while the current tile is computed.
+//   - K and V tiles are dense swizzled tiles filled by LDS DMA, double-buffered with
+//     one barrier per tile: the next tile streams in while the current one is
+//     computed.
 //   - Vᵀ (the A operand of Oᵀ += Vᵀ Pᵀ) comes straight from the row-layout tile
 //     through the gfx950 transpose read, in the key order of the Sᵀ accumulator.
 //   - The softmax scale is folded into the exponent (one FMA per score), and the
