@@ -4,21 +4,23 @@
 //   p  = exp(scale * <q_t, k_j> - lse_t)        (recomputed from the forward's LSE)
 //   dP = <dO_t, v_j>,   dS = p * (dP - D_t),    D_t = <dO_t, O_t>
 //   dQ_t += scale * dS * k_j,   dK_j += scale * dS * q_t,   dV_j += p * dO_t
-// Kernels:
+// Kernels (each bf16 kernel has an fp32 counterpart for the 1e-5 parity workload;
+// head dim 512 is in dkv_d512.hip):
 //   bwd_pre   D = rowsum(dO * O) in fp32 (the auxiliary preprocessing launch), stored
 //             negated, and the LSE in units of the raw dot product, -LSE / scale
 //   bwd_dq    query-parallel: a workgroup keeps 128 query rows in registers and
 //             walks the shared-prompt key tiles, then its own sequence's tiles,
 //             exactly like the forward; dQ is written once, no atomics.
-//   bwd_dkdv  key-parallel: a workgroup keeps 128 keys (K, V and the dK, dV
-//             accumulators) in registers and walks the query rows that see them.
+//   bwd_dkdv  key-parallel: a workgroup owns 128 keys (V and the dK, dV accumulators
+//             in registers, K in LDS) and walks the query rows that see them.
 //             Response keys are written directly; shared-prompt keys are visited
 //             once per chunk of sequences and their partial dK_P, dV_P summed into
 //             the caller's fp32 accumulator with atomic adds (§3.2 "fp32 atomic
-//             accumulation", eq. (6)).
+//             accumulation", eq. (6)), or stored into the chunk's slice (split mode)
+//             for split_reduce to add in slice order.
 //   cast      the accumulator is rounded to the tensor dtype once (§3.2 Stage 2).
-// Transposed operands (contractions over query rows or key rows) are read from the
-// same row-layout LDS tiles with the gfx950 transpose read.
+// In the bf16 kernels, transposed operands (contractions over query rows or key rows)
+// are read from the same row-layout LDS tiles with the gfx950 transpose read.
 #include <type_traits>
 
 #include "dkv_device.h"
@@ -106,8 +108,11 @@ __global__ __launch_bounds__(256) void cast_kernel(const float *src, T *dst, lon
 
 // ------------------------------------------------------------------- bwd_dq --
 
-template <typename T, int HD>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdQArgs a) {
+// fp32 dQ kernel: the query-parallel structure of the bf16 one with fp32 MFMA, base-e
+// softmax and compensated (Kahan) accumulation, one key per product.
+template <int HD>
+__global__ __launch_bounds__(256, 1) void bwd_dq_f32_kernel(BwdQArgs a) {
+  using T = float;
   constexpr int BN = kFwdBN;
   using TC = TileCfg<T, HD, BN>;
   using M = Mfma<T>;
@@ -142,25 +147,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdQArgs a) {
   typename M::frag qf[NKC], df[NKC];
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc) {
-    if constexpr (sizeof(T) == 2) {
-      qf[kc] = as_bf16x8(*reinterpret_cast<const uint4 *>(qptr + kc * 16 + half * 8));
-      df[kc] = as_bf16x8(*reinterpret_cast<const uint4 *>(dptr + kc * 16 + half * 8));
-    } else {
-      qf[kc] = qptr[kc * 2 + half];
-      df[kc] = dptr[kc * 2 + half];
-    }
+    qf[kc] = qptr[kc * 2 + half];
+    df[kc] = dptr[kc * 2 + half];
   }
   using SM = Softmax<T>;
   const float sf = SM::factor(a.scale);
   const float lse2 = SM::lse_in(a.lse[(long)h * a.lse_ld + qrow]);
   const float Dq = -a.Dneg[(long)h * a.lse_ld + qrow];
 
-  f32x16 acc[NDB];
-  f32x16 comp[sizeof(T) == 4 ? NDB : 1];   // Kahan terms (fp32 path only)
+  f32x16 acc[NDB], comp[NDB];   // sums and their Kahan compensation terms
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = zero16();
-#pragma unroll
-  for (int db = 0; db < (sizeof(T) == 4 ? NDB : 1); ++db) comp[db] = zero16();
+  for (int db = 0; db < NDB; ++db) {
+    acc[db] = zero16();
+    comp[db] = zero16();
+  }
 
   const int ctx_lo = (wl >= 0) ? max(0, qmin - wl) : 0;
   const int ctx_t0 = (ctx_lo / BN) * BN;
@@ -233,33 +233,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdQArgs a) {
         s[kb][v] = p * (dp[kb][v] - Dq);   // dS^T
       }
 
-    // dQ^T += K^T dS^T.
-    if constexpr (sizeof(T) == 2) {
-      bf16x8 sf[2 * NKB];
+    // dQ^T += K^T dS^T, one key per product.
 #pragma unroll
-      for (int u = 0; u < 2 * NKB; ++u) {
-        float t[8];
+    for (int db = 0; db < NDB; ++db) {
+      f32x16 part = zero16();
 #pragma unroll
-        for (int e = 0; e < 8; ++e) t[e] = s[u >> 1][8 * (u & 1) + e];
-        sf[u] = pack8(t);
-      }
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int u = 0; u < 2 * NKB; ++u)
-          acc[db] = mfma(tr_frag<TC::kRowStride>(ks, 16 * u, db * 32, lane), sf[u], acc[db]);
-    } else {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        f32x16 part = zero16();
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            part = mfma(row_elem<HD, BN>(ks, kb * 32 + c_row(v, half), db * 32 + col),
-                        s[kb][v], part);
-        kahan_add(acc[db], comp[db], part);
-      }
+        for (int v = 0; v < 16; ++v)
+          part = mfma(row_elem<HD, BN>(ks, kb * 32 + c_row(v, half), db * 32 + col),
+                      s[kb][v], part);
+      kahan_add(acc[db], comp[db], part);
     }
   }
 
@@ -270,16 +254,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdQArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int dim = db * 32 + 8 * i + 4 * half;
-        if constexpr (sizeof(T) == 2) {
-          bf16x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * i + e] * a.scale);
-          *reinterpret_cast<bf16x4 *>(optr + dim) = w;
-        } else {
-          float4 w = make_float4(acc[db][4 * i] * a.scale, acc[db][4 * i + 1] * a.scale,
-                                 acc[db][4 * i + 2] * a.scale, acc[db][4 * i + 3] * a.scale);
-          *reinterpret_cast<float4 *>(optr + dim) = w;
-        }
+        float4 w = make_float4(acc[db][4 * i] * a.scale, acc[db][4 * i + 1] * a.scale,
+                               acc[db][4 * i + 2] * a.scale, acc[db][4 * i + 3] * a.scale);
+        *reinterpret_cast<float4 *>(optr + dim) = w;
       }
   }
 }
@@ -440,14 +417,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
 
 // ----------------------------------------------------------------- bwd_dkdv --
 
-// Query-step rows: 32 flattened (token, head) rows of one kv head's G q-heads.
-template <typename T, int HD> struct QStepRegs : RowRegs<T, HD, kBwdBM> {
+// Query-step rows: 32 flattened (token, head) rows of one kv head's G q-heads (fp32).
+template <int HD> struct QStepRegs : RowRegs<float, HD, kBwdBM> {
+  using T = float;
   using C = TileCfg<T, HD, kBwdBM>;
   // base: row 0 of the sequence, first q-head of the group; rows f0 .. f0+31 of the
   // flattened (token, head) index, loaded where flo <= row < fend (else zero).
   __device__ __forceinline__ void load_flat(const T *base, long qld, int G, int f0, int flo,
                                             int fend, int tid) {
-    constexpr int per_row = (sizeof(T) == 2) ? HD / 8 : HD / 4;
+    constexpr int per_row = HD / 4;   // 16-byte chunks per row
 #pragma unroll
     for (int p = 0; p < C::kRowPasses; ++p) {
       int id = p * 256 + tid;
@@ -456,16 +434,19 @@ template <typename T, int HD> struct QStepRegs : RowRegs<T, HD, kBwdBM> {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (id < C::kChunks && f >= flo && f < fend) {
         int t = f / G, j = f - t * G;
-        v = *reinterpret_cast<const uint4 *>(base + (long)t * qld + (long)j * HD +
-                                             ch * (16 / sizeof(T)));
+        v = *reinterpret_cast<const uint4 *>(base + (long)t * qld + (long)j * HD + ch * 4);
       }
       this->r[p] = v;
     }
   }
 };
 
-template <typename T, int HD>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
+// fp32 dK/dV kernel: 128 keys per workgroup with K, V and the sums in registers, query
+// rows staged through registers into LDS; fp32 MFMA, base-e softmax and compensated
+// (Kahan) accumulation, one query row per product.
+template <int HD>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdKVArgs a) {
+  using T = float;
   constexpr int BM = kBwdBM;          // query rows per step
   constexpr int BNW = kBwdBN;         // keys per workgroup (4 waves x 32)
   using TC = TileCfg<T, HD, BM>;
@@ -503,27 +484,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
   typename M::frag kf[NKC], vf[NKC];
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc) {
-    if constexpr (sizeof(T) == 2) {
-      uint4 z = make_uint4(0, 0, 0, 0);
-      kf[kc] = as_bf16x8(key_valid ? *reinterpret_cast<const uint4 *>(kp + kc * 16 + half * 8) : z);
-      vf[kc] = as_bf16x8(key_valid ? *reinterpret_cast<const uint4 *>(vp + kc * 16 + half * 8) : z);
-    } else {
-      kf[kc] = key_valid ? kp[kc * 2 + half] : 0.f;
-      vf[kc] = key_valid ? vp[kc * 2 + half] : 0.f;
-    }
+    kf[kc] = key_valid ? kp[kc * 2 + half] : 0.f;
+    vf[kc] = key_valid ? vp[kc * 2 + half] : 0.f;
   }
   const bool wave_active = kw0 < nkeys;
 
   f32x16 dk[NDB], dv[NDB];
-  constexpr int NC = sizeof(T) == 4 ? NDB : 1;   // Kahan terms (fp32 path only)
-  f32x16 ck[NC], cv[NC];
+  f32x16 ck[NDB], cv[NDB];   // Kahan compensation terms
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     dk[db] = zero16();
     dv[db] = zero16();
-  }
-#pragma unroll
-  for (int db = 0; db < NC; ++db) {
     ck[db] = zero16();
     cv[db] = zero16();
   }
@@ -567,7 +538,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
   };
   seek();
 
-  QStepRegs<T, HD> qregs, dregs;
+  QStepRegs<HD> qregs, dregs;
   float lse_r = INFINITY, d_r = 0.f;
   auto issue = [&]() {
     const int s0 = sload_i32(a.cu, cs);
@@ -646,39 +617,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdKVArgs a) {
         }
       }
       // dV += P^T dO and dK += dS^T Q (contractions over the step's query rows).
-      if constexpr (sizeof(T) == 2) {
-        bf16x8 pf[2], sf[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          float t1[8], t2[8];
+      for (int db = 0; db < NDB; ++db) {
+        f32x16 pv = zero16(), pk = zero16();
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            t1[e] = s[8 * u + e];
-            t2[e] = dp[8 * u + e];
-          }
-          pf[u] = pack8(t1);
-          sf[u] = pack8(t2);
+        for (int v = 0; v < 16; ++v) {
+          const int r = c_row(v, half);
+          pv = mfma(s[v], row_elem<HD, BM>(dos, r, db * 32 + col), pv);
+          pk = mfma(dp[v], row_elem<HD, BM>(qs, r, db * 32 + col), pk);
         }
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            dv[db] = mfma(pf[u], tr_frag<TC::kRowStride>(dos, 16 * u, db * 32, lane), dv[db]);
-            dk[db] = mfma(sf[u], tr_frag<TC::kRowStride>(qs, 16 * u, db * 32, lane), dk[db]);
-          }
-      } else {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          f32x16 pv = zero16(), pk = zero16();
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int r = c_row(v, half);
-            pv = mfma(s[v], row_elem<HD, BM>(dos, r, db * 32 + col), pv);
-            pk = mfma(dp[v], row_elem<HD, BM>(qs, r, db * 32 + col), pk);
-          }
-          kahan_add(dv[db], cv[db], pv);
-          kahan_add(dk[db], ck[db], pk);
-        }
+        kahan_add(dv[db], cv[db], pv);
+        kahan_add(dk[db], ck[db], pk);
       }
     }
   }
@@ -1080,9 +1029,9 @@ hipError_t launch_cast(int dtype, const float *src, void *dst, long n, hipStream
   return hipGetLastError();
 }
 
-template <typename T, int HD>
-static hipError_t dq_t(const BwdQArgs &a, int n, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_dq_kernel<T, HD>), dim3(n), dim3(256), 0, s, a);
+template <int HD>
+static hipError_t dq_f32(const BwdQArgs &a, int n, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_dq_f32_kernel<HD>), dim3(n), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1099,15 +1048,15 @@ hipError_t launch_bwd_dq(int dtype, int hd, const BwdQArgs &a, int n, hipStream_
     }
     if (hd == 512) return launch_bwd_dq_d512(a, n, s);
   } else {
-    if (hd == 64) return dq_t<float, 64>(a, n, s);
-    if (hd == 128) return dq_t<float, 128>(a, n, s);
+    if (hd == 64) return dq_f32<64>(a, n, s);
+    if (hd == 128) return dq_f32<128>(a, n, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <typename T, int HD>
-static hipError_t dkdv_t(const BwdKVArgs &a, int n, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, HD>), dim3(n), dim3(256), 0, s, a);
+template <int HD>
+static hipError_t dkdv_f32(const BwdKVArgs &a, int n, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_dkdv_f32_kernel<HD>), dim3(n), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1124,8 +1073,8 @@ hipError_t launch_bwd_dkdv(int dtype, int hd, const BwdKVArgs &a, int n, hipStre
     }
     if (hd == 512) return launch_bwd_dkdv_d512(a, n, s);
   } else {
-    if (hd == 64) return dkdv_t<float, 64>(a, n, s);
-    if (hd == 128) return dkdv_t<float, 128>(a, n, s);
+    if (hd == 64) return dkdv_f32<64>(a, n, s);
+    if (hd == 128) return dkdv_f32<128>(a, n, s);
   }
   return hipErrorInvalidValue;
 }

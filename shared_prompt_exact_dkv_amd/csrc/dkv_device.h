@@ -12,8 +12,8 @@
 // the softmax, and feed the C tile straight back as the B operand of the next
 // product.  A C tile used as a k-operand pairs lane-half `half`, element e with row
 //   kappa(half, e) = 8*(e/4) + 4*half + (e%4)     (within a 16-row slice)
-// and the other operand is read in that same order from an LDS layout that keeps
-// four consecutive rows of each column together ("T4": [row/4][col][row%4]).
+// and the other operand is read in that same order (the transpose read of the bf16
+// tiles, sw_tr_frag in dkv_tiles.h; single elements in the fp32 kernels).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -76,14 +76,6 @@ __device__ __forceinline__ bf16x8 pack8(const float *x) {
   return r;
 }
 
-// Low/high 16-bit halves of two words interleaved: (lo(a), lo(b)) and (hi(a), hi(b)).
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
-
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 // max / sum of x over the lane pair (l, l ^ 32) that shares a C-tile column, through
@@ -114,17 +106,12 @@ __device__ __forceinline__ void kahan_add(f32x16 &sum, f32x16 &comp, const f32x1
   }
 }
 
-// Exponent domain of the softmax.  bf16 runs in base 2 with the hardware exp2
-// (logits pre-multiplied by scale*log2(e)); the fp32 path, whose results are
-// checked at 1e-5, runs in base e with the accurate expf/logf so that neither the
-// logits nor the stored natural-log LSE pass through a rounded log2(e) factor.
-template <typename T> struct Softmax {
-  // factor applied to raw scores; LSE (natural log) -> kernel domain
-  __device__ static float factor(float scale) { return scale * kLog2e; }
-  __device__ static float lse_in(float lse) { return lse * kLog2e; }
-  __device__ static float ex(float x) { return fast_exp2(x); }
-  __device__ static float lse_out(float m, float l) { return (m + fast_log2(l)) * kLn2; }
-};
+// Exponent domain of the fp32 kernels' softmax.  The bf16 kernels run in base 2 with
+// the hardware exp2 (logits pre-multiplied by scale*log2(e)); the fp32 path, whose
+// results are checked at 1e-5, runs in base e with the accurate expf/logf so that
+// neither the logits nor the stored natural-log LSE pass through a rounded log2(e)
+// factor.
+template <typename T> struct Softmax;
 template <> struct Softmax<float> {
   __device__ static float factor(float scale) { return scale; }
   __device__ static float lse_in(float lse) { return lse; }

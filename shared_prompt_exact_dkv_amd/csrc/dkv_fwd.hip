@@ -1,9 +1,11 @@
-// dkv_fwd.hip -- forward kernel: online softmax over a shared-prompt KV region and a
-// per-sequence KV region in one pass ("DualKV", arXiv 2605.15422, §3.1).
+// dkv_fwd.hip -- forward kernels: online softmax over a shared-prompt KV region and a
+// per-sequence KV region in one pass ("DualKV", arXiv 2605.15422, §3.1).  bf16 at head
+// dims 64 / 128 runs fwd_bf16_kernel (dkv_fwd_bf16.h), head dim 512 the kernels of
+// dkv_d512.hip; this file holds the fp32 kernel and the dispatch.
 //
-// One workgroup (4 waves) owns 128 query rows = bm_tok tokens x G q-heads of one kv
-// head (grouped-query attention, §3.1 last paragraph), so every K/V tile staged in
-// LDS feeds all G heads.  It walks
+// fp32 kernel: one workgroup (4 waves) owns 128 query rows = bm_tok tokens x G q-heads
+// of one kv head (grouped-query attention, §3.1 last paragraph), so every K/V tile
+// staged in LDS feeds all G heads.  It walks
 //   1. the context tiles of K_P/V_P (keys at logical positions 0..P-1), then
 //   2. its own sequence's tiles (logical positions P + r'),
 // carrying the running max m, sum l and output o across the switch, so the result
@@ -13,11 +15,12 @@
 // one region it is plain varlen causal attention: Call 1 (eq. (3)) and the N-copy
 // packing (eq. (2)).
 //
-// Per 64-key tile each wave computes S^T = K Q^T (keys x its 32 query rows) on MFMA
-// with Q held in registers, updates the softmax with one lane owning one query row
-// (two lane-halves each hold half the keys; only the max crosses halves per tile),
-// then O^T += V^T P^T with P^T taken straight from the S^T accumulator layout and
-// V^T read from the T4 LDS layout.
+// Per 64-key tile each wave computes S^T = K Q^T (keys x its 32 query rows) with fp32
+// MFMA (v_mfma_f32_32x32x2_f32) and Q held in registers, updates the softmax with one
+// lane owning one query row (two lane-halves each hold half the keys; only the max
+// crosses halves per tile), then O^T += V^T P^T with P^T taken straight from the S^T
+// accumulator, one key per product.  Base-e softmax with accurate expf / logf: the fp32
+// path is checked at 1e-5 absolute.
 #include "dkv_device.h"
 #include "dkv_launch.h"
 #include "dkv_tiles.h"
@@ -25,24 +28,16 @@
 
 namespace dkv {
 
-template <typename T, int HD> struct FwdVRegs;
-template <int HD> struct FwdVRegs<bf16, HD> : T4Regs<HD, kFwdBN> {};
-template <int HD> struct FwdVRegs<float, HD> : RowRegs<float, HD, kFwdBN> {};
-
-// Waves per SIMD the register budget is sized for.
-template <typename T, int HD> struct FwdOcc { static constexpr int kWaves = HD <= 64 ? 2 : 1; };
-template <int HD> struct FwdOcc<float, HD> { static constexpr int kWaves = 1; };
-
-template <typename T, int HD>
-__global__ __launch_bounds__(256, (FwdOcc<T, HD>::kWaves)) void fwd_kernel(FwdArgs a) {
+template <int HD>
+__global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
+  using T = float;
   constexpr int BN = kFwdBN;
   using TC = TileCfg<T, HD, BN>;
   using M = Mfma<T>;
   constexpr int NKC = HD / M::K;   // MFMA steps over the head dim
   constexpr int NDB = HD / 32;     // 32-wide blocks of the output head dim
   constexpr int NKB = BN / 32;     // 32-key blocks per tile
-  constexpr int kVBytes = (sizeof(T) == 2) ? TC::kT4Bytes : TC::kRowBytes;
-  __shared__ __attribute__((aligned(16))) char smem[TC::kRowBytes + kVBytes];
+  __shared__ __attribute__((aligned(16))) char smem[2 * TC::kRowBytes];
   char *ks = smem;
   char *vs = smem + TC::kRowBytes;
 
@@ -69,12 +64,7 @@ __global__ __launch_bounds__(256, (FwdOcc<T, HD>::kWaves)) void fwd_kernel(FwdAr
   const T *qptr = reinterpret_cast<const T *>(a.q) + (long)(seq0 + t0 + tok) * qld + (long)h * HD;
   typename M::frag qf[NKC];
 #pragma unroll
-  for (int kc = 0; kc < NKC; ++kc) {
-    if constexpr (sizeof(T) == 2)
-      qf[kc] = as_bf16x8(*reinterpret_cast<const uint4 *>(qptr + kc * 16 + half * 8));
-    else
-      qf[kc] = qptr[kc * 2 + half];
-  }
+  for (int kc = 0; kc < NKC; ++kc) qf[kc] = qptr[kc * 2 + half];
 
   using SM = Softmax<T>;
   const float sf = SM::factor(a.scale);
@@ -97,8 +87,7 @@ __global__ __launch_bounds__(256, (FwdOcc<T, HD>::kWaves)) void fwd_kernel(FwdAr
   const T *ko_base = reinterpret_cast<const T *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
   const T *vo_base = reinterpret_cast<const T *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
 
-  RowRegs<T, HD, BN> kregs;
-  FwdVRegs<T, HD> vregs;
+  RowRegs<T, HD, BN> kregs, vregs;
   auto issue = [&](int i) {
     if (i < n_ctx) {
       int s = ctx_t0 + i * BN;
@@ -184,31 +173,15 @@ __global__ __launch_bounds__(256, (FwdOcc<T, HD>::kWaves)) void fwd_kernel(FwdAr
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
 
-    // O^T += V^T P^T.
-    if constexpr (sizeof(T) == 2) {
-      bf16x8 pf[2 * NKB];
+    // O^T += V^T P^T, one key per product.
 #pragma unroll
-      for (int u = 0; u < 2 * NKB; ++u) {
-        float t[8];
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) t[e] = s[u >> 1][8 * (u & 1) + e];
-        pf[u] = pack8(t);
-      }
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int u = 0; u < 2 * NKB; ++u)
-          acc[db] = mfma(t4_frag<HD>(vs, u, db * 32 + col, half), pf[u], acc[db]);
-    } else {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            acc[db] = mfma(row_elem<HD, BN>(vs, kb * 32 + c_row(v, half), db * 32 + col),
-                           s[kb][v], acc[db]);
-    }
+        for (int v = 0; v < 16; ++v)
+          acc[db] = mfma(row_elem<HD, BN>(vs, kb * 32 + c_row(v, half), db * 32 + col),
+                         s[kb][v], acc[db]);
   }
 
   const float l = l_run + wave_xor32(l_run);
@@ -220,25 +193,18 @@ __global__ __launch_bounds__(256, (FwdOcc<T, HD>::kWaves)) void fwd_kernel(FwdAr
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int dim = db * 32 + 8 * i + 4 * half;
-        if constexpr (sizeof(T) == 2) {
-          bf16x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * i + e] * inv);
-          *reinterpret_cast<bf16x4 *>(optr + dim) = w;
-        } else {
-          float4 w = make_float4(acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv,
-                                 acc[db][4 * i + 2] * inv, acc[db][4 * i + 3] * inv);
-          *reinterpret_cast<float4 *>(optr + dim) = w;
-        }
+        float4 w = make_float4(acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv,
+                               acc[db][4 * i + 2] * inv, acc[db][4 * i + 3] * inv);
+        *reinterpret_cast<float4 *>(optr + dim) = w;
       }
     if (half == 0)
       a.lse[(long)h * a.lse_ld + seq0 + t0 + tok] = SM::lse_out(m_run, l);
   }
 }
 
-template <typename T, int HD>
-static hipError_t launch_fwd_t(const FwdArgs &a, int n, hipStream_t s) {
-  hipLaunchKernelGGL((fwd_kernel<T, HD>), dim3(n), dim3(256), 0, s, a);
+template <int HD>
+static hipError_t launch_fwd_f32(const FwdArgs &a, int n, hipStream_t s) {
+  hipLaunchKernelGGL((fwd_f32_kernel<HD>), dim3(n), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -255,8 +221,8 @@ hipError_t launch_fwd(int dtype, int hd, const FwdArgs &a, int n, hipStream_t s)
     }
     if (hd == 512) return launch_fwd_d512(a, n, s);
   } else {
-    if (hd == 64) return launch_fwd_t<float, 64>(a, n, s);
-    if (hd == 128) return launch_fwd_t<float, 128>(a, n, s);
+    if (hd == 64) return launch_fwd_f32<64>(a, n, s);
+    if (hd == 128) return launch_fwd_f32<128>(a, n, s);
   }
   return hipErrorInvalidValue;
 }
