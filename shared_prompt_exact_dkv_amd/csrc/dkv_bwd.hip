@@ -935,6 +935,14 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
           dk[db] = mfma(s0, sw_tr_frag<HD>(qs, rb * 32, db * 32, lane), dk[db]);
           dk[db] = mfma(s1, sw_tr_frag<HD>(qs, rb * 32 + 16, db * 32, lane), dk[db]);
         }
+        // transposed dO / Q reads three products ahead
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int j = 0; j < 4 * NDB - 3; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
         __builtin_amdgcn_s_setprio(0);
       }
     }
