@@ -125,7 +125,7 @@ dkv_status check_params(const dkv_params *p, bool is_ctx, Shape *s) {
   s->bm_tok_dq = s->bm_tok;
   s->kv_tile = kBwdBN;
   if (s->d == 512) {
-    // Head dim 512 splits the head dim across the waves of a workgroup: 64 query
+    // Head dim 512 splits the head dim across the waves of a workgroup: 128 query
     // rows per forward workgroup, 32 per dQ workgroup, 32 keys per dK/dV workgroup;
     // bf16 only.
     if (s->dtype != DKV_BF16)

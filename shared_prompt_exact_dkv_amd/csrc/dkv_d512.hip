@@ -6,8 +6,8 @@
 // dim would need 384-768 registers, so the kernels split the head dim across the
 // waves of a workgroup and keep every wave within the architectural VGPRs:
 //
-//   forward  64 query rows per workgroup; the two waves of a pair share 32 rows and
-//            each holds Q and O for one half of the head dim.  Each computes the
+//   forward  128 query rows per workgroup of 8 waves (two per SIMD); the two waves of
+//            a pair share 32 rows and each holds Q and O for one half of the head dim.  Each computes the
 //            partial scores Sᵀ over its half, the pair adds the two partials through
 //            LDS (both in the same order, so both see identical scores), and each
 //            accumulates its half of O.
@@ -61,16 +61,17 @@ __device__ __forceinline__ f32x16 part_of(int w, int me, const f32x16 &mine, con
 
 // ------------------------------------------------------------------- forward --
 
-__global__ __launch_bounds__(256, 1) void fwd_d512_kernel(FwdArgs a) {
+__global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
   constexpr int BN = 32;
   constexpr int TILE = BN * HD * 2;      // 32 KB
   constexpr int NKH = HD / 2 / 16;       // MFMA k-steps per half head dim
   constexpr int NDH = HD / 2 / 32;       // 32-wide output blocks per half
   constexpr float kSlack = 8.f;
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE + 4 * 4096];
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE + 8 * 4096];
   float *xch = reinterpret_cast<float *>(smem + 4 * TILE);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int rb = wave >> 1, dh = wave & 1;
   const QItem it = a.items[blockIdx.x];
@@ -115,18 +116,20 @@ __global__ __launch_bounds__(256, 1) void fwd_d512_kernel(FwdArgs a) {
   const bf16 *ko_base = reinterpret_cast<const bf16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
   const bf16 *vo_base = reinterpret_cast<const bf16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
   const int kld_b = (int)(kld * 2);
+  // Waves 0-3 fetch the K tile, waves 4-7 the V tile.
+  const int dw = wave & 3, isv = wave >> 2;
+  const bf16 *c_base = isv ? vc_base : kc_base;
+  const bf16 *o_base = isv ? vo_base : ko_base;
   DmaRows<HD, BN> dma;
-  dma.init(wave, lane, kld_b);
+  dma.init(dw, lane, kld_b);
   auto issue = [&](int i) {   // tile i -> stage i % 2 (K, then V)
-    char *st = smem + (i & 1) * 2 * TILE;
+    char *st = smem + (i & 1) * 2 * TILE + isv * TILE;
     if (i < n_ctx) {
       int s = ctx_t0 + i * BN;
-      dma.load(st, kc_base + (long)s * kld, kld_b, P - s, wave);
-      dma.load(st + TILE, vc_base + (long)s * kld, kld_b, P - s, wave);
+      dma.load(st, c_base + (long)s * kld, kld_b, P - s, dw);
     } else {
       int s = own_t0 + (i - n_ctx) * BN;
-      dma.load(st, ko_base + (long)s * kld, kld_b, seqlen - s, wave);
-      dma.load(st + TILE, vo_base + (long)s * kld, kld_b, seqlen - s, wave);
+      dma.load(st, o_base + (long)s * kld, kld_b, seqlen - s, dw);
     }
   };
   if (n_tiles > 0) issue(0);
@@ -147,13 +150,17 @@ __global__ __launch_bounds__(256, 1) void fwd_d512_kernel(FwdArgs a) {
     if (i + 1 < n_tiles) issue(i + 1);
     const char *ks = smem + (i & 1) * 2 * TILE;
     const char *vs = ks + TILE;
+    // Opaque per tile: the swizzled fragment addresses are recomputed in the loop
+    // rather than held in registers across it.
+    int colx = col, lanex = lane, halfx = half;
+    asm volatile("" : "+v"(colx), "+v"(lanex), "+v"(halfx));
 
     // Partial Sᵀ = K Qᵀ over this wave's half of the head dim; the pair adds halves
     // 0 + 1 in that order.
     f32x16 part = zero16();
 #pragma unroll
     for (int kc = 0; kc < NKH; ++kc)
-      part = mfma(sw_frag<HD>(ks, col, dh * NKH + kc, half), qf[kc], part);
+      part = mfma(sw_frag<HD>(ks, colx, dh * NKH + kc, halfx), qf[kc], part);
     xch_put(xch + wave * 1024, part, lane);
     __syncthreads();
     const f32x16 other = xch_get(xch + (wave ^ 1) * 1024, lane);
@@ -197,8 +204,8 @@ __global__ __launch_bounds__(256, 1) void fwd_d512_kernel(FwdArgs a) {
     // Oᵀ += Vᵀ Pᵀ over this wave's half of the head dim.
 #pragma unroll
     for (int db = 0; db < NDH; ++db) {
-      acc[db] = mfma(sw_tr_frag<HD>(vs, 0, d0 + db * 32, lane), p0, acc[db]);
-      acc[db] = mfma(sw_tr_frag<HD>(vs, 16, d0 + db * 32, lane), p1, acc[db]);
+      acc[db] = mfma(sw_tr_frag<HD>(vs, 0, d0 + db * 32, lanex), p0, acc[db]);
+      acc[db] = mfma(sw_tr_frag<HD>(vs, 16, d0 + db * 32, lanex), p1, acc[db]);
     }
   }
 
@@ -223,7 +230,7 @@ __global__ __launch_bounds__(256, 1) void fwd_d512_kernel(FwdArgs a) {
 
 hipError_t launch_fwd_d512(const FwdArgs &a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fwd_d512_kernel, dim3(n), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(fwd_d512_kernel, dim3(n), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

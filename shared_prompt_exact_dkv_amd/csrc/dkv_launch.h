@@ -15,9 +15,9 @@ static constexpr int kRowsPerWG = 128;
 static constexpr int kBwdBN = 128;
 static constexpr int kBwdBM = 32;
 // Head dim 512 (the head dim is split across the waves of a workgroup): query rows
-// per forward workgroup (two pairs of waves), query rows per dQ workgroup and keys
+// per forward workgroup (four pairs of waves), query rows per dQ workgroup and keys
 // per dK/dV workgroup (four waves each).
-static constexpr int kFwdRows512 = 64;
+static constexpr int kFwdRows512 = 128;
 static constexpr int kRowsPerWG512 = 32;
 static constexpr int kBwdBN512 = 32;
 

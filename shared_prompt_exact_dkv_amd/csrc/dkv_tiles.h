@@ -221,13 +221,24 @@ template <int HD, int ROWS> struct DmaRows {
   static constexpr int kBlocks = ROWS * HD * 2 / 1024;
   static_assert(kBlocks % 4 == 0, "tile must be a multiple of 4 KB");
   static constexpr int kPerWave = kBlocks / 4;
-  int voff[kPerWave];
+  // A 1 KB block is one row at HD = 512: the row is wave-uniform, so only the lane's
+  // chunk offset is kept and the swizzle and row offset are applied per load.
+  static constexpr bool kRowPerBlock = Swz<HD>::kChunks == 64;
+  static constexpr int kRegs = kRowPerBlock ? 1 : kPerWave;
+  int voff[kRegs];
+  int ld = 0, w = 0;
   __device__ __forceinline__ void init(int wave, int lane, int ld_bytes) {
+    if constexpr (kRowPerBlock) {
+      voff[0] = lane << 4;
+      ld = ld_bytes;
+      w = wave;
+    } else {
 #pragma unroll
-    for (int k = 0; k < kPerWave; ++k) {
-      const int slot = (k * 4 + wave) * 64 + lane;
-      const int r = slot / Swz<HD>::kChunks, cs = slot % Swz<HD>::kChunks;
-      voff[k] = r * ld_bytes + ((cs ^ Swz<HD>::swz(r)) << 4);
+      for (int k = 0; k < kPerWave; ++k) {
+        const int slot = (k * 4 + wave) * 64 + lane;
+        const int r = slot / Swz<HD>::kChunks, cs = slot % Swz<HD>::kChunks;
+        voff[k] = r * ld_bytes + ((cs ^ Swz<HD>::swz(r)) << 4);
+      }
     }
   }
   // nrows: valid rows from base (rows past them are zero-filled).
@@ -237,8 +248,20 @@ template <int HD, int ROWS> struct DmaRows {
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc_u(base, n > 0 ? (uint32_t)((n - 1) * ld_bytes + HD * 2) : 0u);
     const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_u32(lds_tile) + wave * 1024);
+    if constexpr (kRowPerBlock) {
+      const int wv = __builtin_amdgcn_readfirstlane(w);
+      const int lds_ = __builtin_amdgcn_readfirstlane(ld);
 #pragma unroll
-    for (int k = 0; k < kPerWave; ++k) dma16(rs, l0 + k * 4096, voff[k]);
+      for (int k = 0; k < kPerWave; ++k) {
+        const int r = k * 4 + wv;
+        // The row offset stays in the vector offset: the buffer range check (which
+        // zero-fills rows past nrows) covers the vector and instruction offsets only.
+        dma16(rs, l0 + k * 4096, (voff[0] ^ (Swz<HD>::swz(r) << 4)) + r * lds_);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kPerWave; ++k) dma16(rs, l0 + k * 4096, voff[k]);
+    }
   }
 };
 
