@@ -126,12 +126,12 @@ dkv_status check_params(const dkv_params *p, bool is_ctx, Shape *s) {
   s->kv_tile = kBwdBN;
   if (s->d == 512) {
     // Head dim 512 splits the head dim across the waves of a workgroup: 128 query
-    // rows per forward workgroup, 32 per dQ workgroup, 32 keys per dK/dV workgroup;
+    // rows per forward workgroup, 64 per dQ workgroup, 64 keys per dK/dV workgroup;
     // bf16 only.
     if (s->dtype != DKV_BF16)
       return fail(DKV_ERR_UNSUPPORTED, "head_dim 512 is implemented for bf16 only");
-    if (G > kRowsPerWG512)
-      return fail(DKV_ERR_UNSUPPORTED, "Hq/Hkv = %d exceeds %d at head_dim 512", G, kRowsPerWG512);
+    if (G > kMaxG512)
+      return fail(DKV_ERR_UNSUPPORTED, "Hq/Hkv = %d exceeds %d at head_dim 512", G, kMaxG512);
     s->bm_tok = kFwdRows512 / G;
     s->bm_tok_dq = kRowsPerWG512 / G;
     s->kv_tile = kBwdBN512;

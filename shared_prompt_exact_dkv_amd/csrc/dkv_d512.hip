@@ -11,15 +11,19 @@
 //            partial scores Sᵀ over its half, the pair adds the two partials through
 //            LDS (both in the same order, so both see identical scores), and each
 //            accumulates its half of O.
-//   dQ       32 query rows per workgroup.  Waves 0 / 1 form partial Sᵀ = K Qᵀ over
-//            the two halves of the head dim (holding Q), waves 2 / 3 partial
-//            dPᵀ = V dOᵀ (holding dO).  After one exchange every wave has both tiles,
-//            forms dSᵀ and accumulates dQ for one quarter of the head dim.
-//   dK/dV    32 keys per workgroup, the same arrangement: waves 0 / 1 hold K halves
-//            and form partial S, waves 2 / 3 hold V halves and form partial dP; each
-//            wave accumulates dK and dV for one quarter of the head dim.
-// Tiles are staged by LDS DMA into swizzled dense rows (one 1 KB row per DMA block),
-// double-buffered; partial tiles are exchanged through a small LDS area.
+//   dQ       64 query rows per workgroup of 8 waves, two groups of four with 32 rows
+//            each.  In a group, waves 0 / 1 form partial Sᵀ = K Qᵀ over the two
+//            halves of the head dim (holding Q), waves 2 / 3 partial dPᵀ = V dOᵀ
+//            (holding dO).  After one exchange every wave has both tiles, forms dSᵀ
+//            and accumulates dQ for one quarter of the head dim.
+//   dK/dV    64 keys per workgroup of 8 waves, two groups of four with 32 keys each,
+//            the same arrangement: in a group, waves 0 / 1 hold K halves and form
+//            partial S, waves 2 / 3 hold V halves and form partial dP; each wave
+//            accumulates dK and dV for one quarter of the head dim.
+// Every kernel runs two waves per SIMD, and the two groups (pairs) of a workgroup
+// share each staged tile.  Tiles are staged by LDS DMA into swizzled dense rows (one
+// 1 KB row per DMA block), double-buffered; partial tiles are exchanged through a
+// 32 KB LDS area, so the workgroup takes the whole 160 KB of LDS.
 #include <type_traits>
 
 #include "dkv_device.h"
@@ -32,17 +36,35 @@ namespace {
 
 constexpr int HD = 512;
 
-// One 32 x 32 fp32 C tile per wave in the exchange area: lane l keeps element v at
-// word v * 64 + l, and the other waves read the same slots (same C layout).
+// One 32 x 32 fp32 C tile per wave in the exchange area, as four 1 KB quads: lane l
+// keeps elements 4q .. 4q+3 at words 256 q + 4 l .. +3 (16-byte accesses, every bank
+// once per quarter wave), and the other waves read the same slots (same C layout).
 __device__ __forceinline__ void xch_put(float *area, const f32x16 &x, int lane) {
 #pragma unroll
-  for (int v = 0; v < 16; ++v) area[v * 64 + lane] = x[v];
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<float4 *>(area + q * 256 + lane * 4) =
+        make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+}
+__device__ __forceinline__ float4 xch_quad(const float *area, int q, int lane) {
+  return *reinterpret_cast<const float4 *>(area + q * 256 + lane * 4);
 }
 __device__ __forceinline__ f32x16 xch_get(const float *area, int lane) {
   f32x16 x;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) x[v] = area[v * 64 + lane];
+  for (int q = 0; q < 4; ++q) {
+    const float4 t = xch_quad(area, q, lane);
+    x[4 * q] = t.x, x[4 * q + 1] = t.y, x[4 * q + 2] = t.z, x[4 * q + 3] = t.w;
+  }
   return x;
+}
+// Two floats as a bf16 pair (x in the low half), and four such words as 8 bf16.
+__device__ __forceinline__ uint32_t pack2(float x, float y) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
+}
+__device__ __forceinline__ bf16x8 words8(const uint32_t *w) {
+  return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
 }
 // a + b element-wise (the fixed summation order of the partial tiles).
 __device__ __forceinline__ f32x16 add16(const f32x16 &a, const f32x16 &b) {
@@ -236,23 +258,28 @@ hipError_t launch_fwd_d512(const FwdArgs &a, int n, hipStream_t s) {
 
 // ------------------------------------------------------------------------ dQ --
 
-__global__ __launch_bounds__(256, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
   constexpr int BN = 32;
   constexpr int TILE = BN * HD * 2;      // 32 KB
   constexpr int NKH = HD / 2 / 16;
   constexpr int NDQ = HD / 4 / 32;       // 32-wide output blocks per quarter
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE + 4 * 4096];
-  float *xch = reinterpret_cast<float *>(smem + 4 * TILE);
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE + 8 * 4096];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
-  const int role = wave >> 1, dh = wave & 1;   // role 0: partial Sᵀ from Q; 1: partial dPᵀ from dO
+  // Two groups of four waves, 32 rows each; in a group, role 0 forms partial Sᵀ from
+  // Q and role 1 partial dPᵀ from dO, over head-dim half dh.
+  const int grp = wave >> 2, wq = wave & 3;
+  const int role = wq >> 1, dh = wq & 1;
+  float *xch = reinterpret_cast<float *>(smem + 4 * TILE) + grp * 4 * 1024;
   const QItem it = a.items[blockIdx.x];
   const int g = it.g, seq0 = it.seq_start, seqlen = it.seq_len;
   const int t0 = it.tile * a.bm_tok;
   const int nt = min(a.bm_tok, seqlen - t0);
-  int tok = col / a.G;
-  const int hj = col - tok * a.G;
+  const int qr = grp * 32 + col;
+  int tok = qr / a.G;
+  const int hj = qr - tok * a.G;
   const bool row_valid = tok < nt;
   if (!row_valid) tok = nt - 1;
   const int h = g * a.G + hj;
@@ -272,7 +299,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
   const float sf = a.scale * kLog2e;
   const float lse2 = a.lse[(long)h * a.lse_ld + qrow] * kLog2e;
   const float Dq = -a.Dneg[(long)h * a.lse_ld + qrow];
-  const int dq0 = wave * (HD / 4);
+  const int dq0 = wq * (HD / 4);
 
   f32x16 acc[NDQ];
 #pragma unroll
@@ -291,18 +318,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
   const bf16 *ko_base = reinterpret_cast<const bf16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
   const bf16 *vo_base = reinterpret_cast<const bf16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
   const int kld_b = (int)(kld * 2);
+  // Waves 0-3 fetch the K tile, waves 4-7 the V tile.
+  const bf16 *c_base = grp ? vc_base : kc_base;
+  const bf16 *o_base = grp ? vo_base : ko_base;
   DmaRows<HD, BN> dma;
-  dma.init(wave, lane, kld_b);
+  dma.init(wq, lane, kld_b);
   auto issue = [&](int i) {
-    char *st = smem + (i & 1) * 2 * TILE;
+    char *st = smem + (i & 1) * 2 * TILE + grp * TILE;
     if (i < n_ctx) {
       int s = ctx_t0 + i * BN;
-      dma.load(st, kc_base + (long)s * kld, kld_b, P - s, wave);
-      dma.load(st + TILE, vc_base + (long)s * kld, kld_b, P - s, wave);
+      dma.load(st, c_base + (long)s * kld, kld_b, P - s, wq);
     } else {
       int s = own_t0 + (i - n_ctx) * BN;
-      dma.load(st, ko_base + (long)s * kld, kld_b, seqlen - s, wave);
-      dma.load(st + TILE, vo_base + (long)s * kld, kld_b, seqlen - s, wave);
+      dma.load(st, o_base + (long)s * kld, kld_b, seqlen - s, wq);
     }
   };
   if (n_tiles > 0) issue(0);
@@ -324,15 +352,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
     const char *ks = smem + (i & 1) * 2 * TILE;
     const char *vs = ks + TILE;
 
+    // Opaque per tile: the swizzled fragment addresses are recomputed in the loop
+    // rather than held in registers across it.
+    int colx = col, lanex = lane, halfx = half;
+    asm volatile("" : "+v"(colx), "+v"(lanex), "+v"(halfx));
     const char *op = role == 0 ? ks : vs;
     f32x16 part = zero16();
 #pragma unroll
     for (int kc = 0; kc < NKH; ++kc)
-      part = mfma(sw_frag<HD>(op, col, dh * NKH + kc, half), xf[kc], part);
-    xch_put(xch + wave * 1024, part, lane);
+      part = mfma(sw_frag<HD>(op, colx, dh * NKH + kc, halfx), xf[kc], part);
+    xch_put(xch + wq * 1024, part, lane);
     __syncthreads();
-    const f32x16 st = add16(part_of(0, wave, part, xch, lane), part_of(1, wave, part, xch, lane));
-    const f32x16 dpt = add16(part_of(2, wave, part, xch, lane), part_of(3, wave, part, xch, lane));
+    const f32x16 st = add16(part_of(0, wq, part, xch, lane), part_of(1, wq, part, xch, lane));
+    const f32x16 dpt = add16(part_of(2, wq, part, xch, lane), part_of(3, wq, part, xch, lane));
 
     const bool need_mask = (nrows < BN) || (kpos0 + BN - 1 > qmin) ||
                            (wl >= 0 && kpos0 < qmax - wl);
@@ -352,8 +384,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
     // dQᵀ += Kᵀ dSᵀ over this wave's quarter of the head dim.
 #pragma unroll
     for (int db = 0; db < NDQ; ++db) {
-      acc[db] = mfma(sw_tr_frag<HD>(ks, 0, dq0 + db * 32, lane), d0, acc[db]);
-      acc[db] = mfma(sw_tr_frag<HD>(ks, 16, dq0 + db * 32, lane), d1, acc[db]);
+      acc[db] = mfma(sw_tr_frag<HD>(ks, 0, dq0 + db * 32, lanex), d0, acc[db]);
+      acc[db] = mfma(sw_tr_frag<HD>(ks, 16, dq0 + db * 32, lanex), d1, acc[db]);
     }
   }
 
@@ -374,25 +406,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
 
 hipError_t launch_bwd_dq_d512(const BwdQArgs &a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_dq_d512_kernel, dim3(n), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bwd_dq_d512_kernel, dim3(n), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
 // --------------------------------------------------------------------- dK/dV --
 
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
   constexpr int BM = 32;                 // query rows per step
   constexpr int TILE = BM * HD * 2;      // 32 KB: one row per 1 KB DMA block
   constexpr int NKH = HD / 2 / 16;
   constexpr int NDQ = HD / 4 / 32;
   constexpr int RPW = BM / 4;            // rows each wave fetches per step
-  constexpr int STAGE = 2 * TILE + 2 * 64 * 4;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE + 4 * 4096];
-  float *xch = reinterpret_cast<float *>(smem + 2 * STAGE);
+  constexpr int STAGE = 2 * TILE;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE + 8 * 4096];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
-  const int role = wave >> 1, dh = wave & 1;   // role 0: partial S with K; 1: partial dP with V
+  // Two groups of four waves, 32 keys each; in a group, role 0 forms partial S with K
+  // and role 1 partial dP with V, over head-dim half dh.
+  const int grp = wave >> 2, wq = wave & 3;
+  const int role = wq >> 1, dh = wq & 1;
+  float *xch = reinterpret_cast<float *>(smem + 2 * STAGE) + grp * 4 * 1024;
   const KVItem it = a.items[blockIdx.x];
   const int g = it.g, G = a.G, P = a.ctx_len, wl = a.window_left;
   const bool ctx = it.region == kRegionCtx;
@@ -402,24 +438,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
   const int nkeys = ctx ? P - it.key_start : sload_i32(a.cu, it.seq_lo + 1) - own0 - it.key_start;
   const int kbase = ctx ? 0 : P;
   const int nk_tile = min(kBwdBN512, nkeys);
+  const int gk0 = grp * 32;              // the group's first key in the tile
+  const int nkeys_g = nkeys - gk0;       // keys of the tile this group holds (may be <= 0)
 
-  const int key = col;
+  const int key = gk0 + col;
   const bool key_valid = key < nkeys;
   const float sf = a.scale * kLog2e;
+  // K (role 0) or V (role 1) rows of the group's keys, this wave's head-dim half;
+  // keys past the tile's end read as zeros (buffer range check).
   const bf16 *xp = reinterpret_cast<const bf16 *>(
                        role == 0 ? (ctx ? a.k_ctx : a.k_own) : (ctx ? a.v_ctx : a.v_own)) +
-                   (long)(own0 + it.key_start + (key_valid ? key : 0)) * kld + (long)g * HD +
-                   dh * (HD / 2);
+                   (long)(own0 + it.key_start + gk0) * kld + (long)g * HD + dh * (HD / 2);
+  const __amdgpu_buffer_rsrc_t rk =
+      make_rsrc_u(xp, nkeys_g > 0 ? (uint32_t)nkeys_g * (uint32_t)(kld * 2) : 0u);
   bf16x8 xf[NKH];
 #pragma unroll
-  for (int kc = 0; kc < NKH; ++kc) {
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    xf[kc] = as_bf16x8(key_valid ? *reinterpret_cast<const uint4 *>(xp + kc * 16 + half * 8) : z);
-  }
+  for (int kc = 0; kc < NKH; ++kc)
+    xf[kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rk, col * (int)(kld * 2) + (kc * 16 + half * 8) * 2, 0, 0));
   const int kpos = kbase + it.key_start + key;
   const int f_vis_lo = key_valid ? max(0, (kpos - P) * G) : 0x7fffffff;
   const int f_vis_hi = (wl >= 0) ? max(0, (kpos + wl - P + 1) * G) : 0x7fffffff;
-  const int dq0 = wave * (HD / 4);
+  const int dq0 = wq * (HD / 4);
 
   f32x16 dk[NDQ], dv[NDQ];
 #pragma unroll
@@ -464,34 +504,37 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
 
   const int qld_b = (int)(qld * 2);
   const int head0_b = g * G * HD * 2;
-  const __amdgpu_buffer_rsrc_t r_ld = make_rsrc_u(wave == 0 ? (const void *)a.lsn : (const void *)a.Dneg,
+  // Waves 0-3 fetch the step's Q rows, waves 4-7 its dO rows: row r of the step (a
+  // flattened (token, head) row) fills 1 KB block r, written by wave r % 4.
+  const bf16 *xsrc = reinterpret_cast<const bf16 *>(grp ? a.dout : a.q);
+  // The first head-dim half of each role starts its partial at -LSE / scale (scores)
+  // or -D (dP) of the step's rows: lane l fetches row l % 32's value into a register
+  // one step ahead, and the wave spreads it over the C layout with ds_bpermute.
+  const __amdgpu_buffer_rsrc_t r_ld = make_rsrc_u(role == 0 ? (const void *)a.lsn : (const void *)a.Dneg,
                                                   (uint32_t)((long)a.Hq * a.lse_ld * 4));
-  // Fetch the step at the cursor into stage `st`: row r of the step (a flattened
-  // (token, head) row) fills 1 KB block r, written by wave r % 4.
   auto issue = [&](char *st) {
     const int s0 = sload_i32(a.cu, cs);
     const int len = sload_i32(a.cu, cs + 1) - s0;
-    const __amdgpu_buffer_rsrc_t rq =
-        make_rsrc_u(reinterpret_cast<const bf16 *>(a.q) + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
-    const __amdgpu_buffer_rsrc_t rd =
-        make_rsrc_u(reinterpret_cast<const bf16 *>(a.dout) + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
-    const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_u32(st) + wave * 1024);
+    const __amdgpu_buffer_rsrc_t rx =
+        make_rsrc_u(xsrc + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
+    const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_u32(st + grp * TILE) + wq * 1024);
 #pragma unroll
     for (int k = 0; k < RPW; ++k) {
-      const int r = k * 4 + wave;
+      const int r = k * 4 + wq;
       const int f = cf + r;
       const int t = f / G, j = f - t * G;
       const int off = t * qld_b + head0_b + j * (HD * 2) + ((lane ^ Swz<HD>::swz(r)) << 4);
-      dma16(rq, l0 + k * 4096, off);
-      dma16(rd, l0 + TILE + k * 4096, off);
+      dma16(rx, l0 + k * 4096, off);
     }
-    if (wave < 2) {   // LSE (wave 0) and D (wave 1) of the step's rows; lanes >= BM read nothing
-      const int f = cf + lane;
-      const int t = f / G, j = f - t * G;
-      const int off = lane < BM ? ((g * G + j) * a.lse_ld + s0 + t) * 4 : 0x7fffffff;
-      const uint32_t la = __builtin_amdgcn_readfirstlane(lds_u32(st + 2 * TILE) + wave * 256);
-      dma4(r_ld, la, off);
-    }
+  };
+  // Row init values of the step at the cursor (rows past the sequence read 0 and are
+  // masked later).
+  auto fetch_init = [&]() -> float {
+    const int s0 = sload_i32(a.cu, cs);
+    const int f = cf + col;
+    const int t = f / G, j = f - t * G;
+    const int off = ((g * G + j) * a.lse_ld + s0 + t) * 4;
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_ld, off, 0, 0));
   };
 
   int nf0 = 0, nflo = 0, nfend = 0;
@@ -508,84 +551,118 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
   int stage = 0;
   bool have = !done;
   int f0 = 0, flo = 0, fend = 0;
+  float xinit = 0.f;
   if (have) {
     issue(smem);
+    if (dh == 0) xinit = fetch_init();
     advance();
     f0 = nf0, flo = nflo, fend = nfend;
   }
 
-  const int kpa = kbase + it.key_start;
-  const int kpb = kbase + it.key_start + min(32, nkeys) - 1;
+  const int kpa = kbase + it.key_start + gk0;
+  const int kpb = kpa + 31;
   while (have) {
+    // The partial's start values (waits for this step's fetches, which the barrier
+    // below needs anyway).
+    f32x16 part = zero16();
+    if (dh == 0) {
+      const int xi = __builtin_bit_cast(int, xinit);
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        part[v] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(c_row(v, half) << 2, xi));
+    }
     dma_wait();
     __syncthreads();
     const bool more = !done;
     int g0 = 0, glo = 0, gend = 0;
     if (more) {
       issue(smem + (stage ^ 1) * STAGE);
+      if (dh == 0) xinit = fetch_init();
       advance();
       g0 = nf0, glo = nflo, gend = nfend;
     }
     const char *qs = smem + stage * STAGE;
     const char *dos = qs + TILE;
-    const float *lsn_s = reinterpret_cast<const float *>(qs + 2 * TILE);
-    const float *dn_s = lsn_s + 64;
+    // Opaque per step: the swizzled fragment addresses are recomputed in the loop
+    // rather than held in registers across it.
+    int colx = col, lanex = lane, halfx = half;
+    asm volatile("" : "+v"(colx), "+v"(lanex), "+v"(halfx));
 
     const char *op = role == 0 ? qs : dos;
-    // The first half's partial starts at -LSE / scale (scores) or -D (dP) of its rows, so
-    // the sums end as <q, k> - LSE / scale and dP - D.
-    f32x16 part = zero16();
-    if (dh == 0) {
-      const float *init = role == 0 ? lsn_s : dn_s;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 x4 = *reinterpret_cast<const float4 *>(init + 8 * i + 4 * half);
-        part[4 * i] = x4.x, part[4 * i + 1] = x4.y, part[4 * i + 2] = x4.z, part[4 * i + 3] = x4.w;
-      }
-    }
 #pragma unroll
     for (int kc = 0; kc < NKH; ++kc)
-      part = mfma(sw_frag<HD>(op, col, dh * NKH + kc, half), xf[kc], part);
-    xch_put(xch + wave * 1024, part, lane);
+      part = mfma(sw_frag<HD>(op, colx, dh * NKH + kc, halfx), xf[kc], part);
+    // one fragment read two products ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int kc = 0; kc < NKH - 2; ++kc) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    xch_put(xch + wq * 1024, part, lane);
     __syncthreads();
-    const f32x16 st = add16(part_of(0, wave, part, xch, lane), part_of(1, wave, part, xch, lane));
-    const f32x16 dpt = add16(part_of(2, wave, part, xch, lane), part_of(3, wave, part, xch, lane));
 
     const int ta = flo / G, tb = (fend - 1) / G;
-    const bool full = (f0 >= flo) && (f0 + BM <= fend) && (32 <= nkeys) &&
+    const bool full = (f0 >= flo) && (f0 + BM <= fend) && (32 <= nkeys_g) &&
                       (kpb <= P + ta) && (wl < 0 || kpa >= P + tb - wl);
-    float pv[16], dsv[16];
-    // The visibility test is compiled only into the variant for blocks that straddle a
-    // mask edge or a range end.
+    uint32_t pw[8], sw[8];   // P and dS as bf16 pairs (elements 2i, 2i + 1)
+    // S = partial 0 + partial 1 and dP - D = partial 2 + partial 3, then P and dS, four
+    // elements at a time: the fence keeps each quad's exchange reads next to their
+    // use, so few registers hold them.  The visibility test is compiled only into the
+    // variant for blocks that straddle a mask edge or a range end.
+    // (The wave's own partial is read back too, so it holds no registers here.)
+    auto quad_of = [&](int w, int q) -> float4 { return xch_quad(xch + w * 1024, q, lane); };
     auto probs = [&](auto masked_c) {
       constexpr bool MASKED = decltype(masked_c)::value;
       const int lo = max(flo, f_vis_lo) - f0 - 4 * half;   // visible row offsets [lo, hi)
       const int hi = min(fend, f_vis_hi) - f0 - 4 * half;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float p = fast_exp2(st[v] * sf);
-        if (MASKED) {
-          const int r = 8 * (v >> 2) + (v & 3);
-          if (r < lo || r >= hi) p = 0.f;
+      for (int q = 0; q < 4; ++q) {
+        const float4 a0 = quad_of(0, q), a1 = quad_of(1, q);
+        const float4 b0 = quad_of(2, q), b1 = quad_of(3, q);
+        const float st[4] = {a0.x + a1.x, a0.y + a1.y, a0.z + a1.z, a0.w + a1.w};
+        const float dpt[4] = {b0.x + b1.x, b0.y + b1.y, b0.z + b1.z, b0.w + b1.w};
+        float pq[4], dq[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float p = fast_exp2(st[e] * sf);
+          if (MASKED) {
+            const int r = 8 * q + e;
+            if (r < lo || r >= hi) p = 0.f;
+          }
+          pq[e] = p;
+          dq[e] = p * dpt[e];
         }
-        pv[v] = p;
-        dsv[v] = p * dpt[v];
+        pw[2 * q] = pack2(pq[0], pq[1]);
+        pw[2 * q + 1] = pack2(pq[2], pq[3]);
+        sw[2 * q] = pack2(dq[0], dq[1]);
+        sw[2 * q + 1] = pack2(dq[2], dq[3]);
+        asm volatile("" ::: "memory");
       }
     };
     if (full)
       probs(std::false_type{});
     else
       probs(std::true_type{});
-    const bf16x8 p0 = pack8(pv), p1 = pack8(pv + 8);
-    const bf16x8 s0 = pack8(dsv), s1 = pack8(dsv + 8);
+    const bf16x8 p0 = words8(pw), p1 = words8(pw + 4);
+    const bf16x8 s0 = words8(sw), s1 = words8(sw + 4);
     // dV += Pᵀ dO and dK += dSᵀ Q over this wave's quarter of the head dim.
 #pragma unroll
     for (int db = 0; db < NDQ; ++db) {
-      dv[db] = mfma(p0, sw_tr_frag<HD>(dos, 0, dq0 + db * 32, lane), dv[db]);
-      dv[db] = mfma(p1, sw_tr_frag<HD>(dos, 16, dq0 + db * 32, lane), dv[db]);
-      dk[db] = mfma(s0, sw_tr_frag<HD>(qs, 0, dq0 + db * 32, lane), dk[db]);
-      dk[db] = mfma(s1, sw_tr_frag<HD>(qs, 16, dq0 + db * 32, lane), dk[db]);
+      dv[db] = mfma(p0, sw_tr_frag<HD>(dos, 0, dq0 + db * 32, lanex), dv[db]);
+      dv[db] = mfma(p1, sw_tr_frag<HD>(dos, 16, dq0 + db * 32, lanex), dv[db]);
+      dk[db] = mfma(s0, sw_tr_frag<HD>(qs, 0, dq0 + db * 32, lanex), dk[db]);
+      dk[db] = mfma(s1, sw_tr_frag<HD>(qs, 16, dq0 + db * 32, lanex), dk[db]);
     }
+    // one transposed fragment (two reads) two products ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int m = 0; m < 4 * NDQ - 2; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     have = more;
     f0 = g0, flo = glo, fend = gend;
     stage ^= 1;
@@ -596,7 +673,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
   for (int db = 0; db < NDQ; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int k = c_row(v, half);
+      const int k = gk0 + c_row(v, half);
       if (k >= nkeys) continue;
       const long off = (long)(own0 + it.key_start + k) * kld + (long)g * HD + dq0 + db * 32 + col;
       const float gk = dk[db][v] * a.scale;
@@ -617,7 +694,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
 
 hipError_t launch_bwd_dkdv_d512(const BwdKVArgs &a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_dkdv_d512_kernel, dim3(n), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bwd_dkdv_d512_kernel, dim3(n), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -16,10 +16,12 @@ static constexpr int kBwdBN = 128;
 static constexpr int kBwdBM = 32;
 // Head dim 512 (the head dim is split across the waves of a workgroup): query rows
 // per forward workgroup (four pairs of waves), query rows per dQ workgroup and keys
-// per dK/dV workgroup (four waves each).
+// per dK/dV workgroup (two groups of four waves each), and the largest Hq / Hkv they
+// take.
 static constexpr int kFwdRows512 = 128;
-static constexpr int kRowsPerWG512 = 32;
-static constexpr int kBwdBN512 = 32;
+static constexpr int kRowsPerWG512 = 64;
+static constexpr int kBwdBN512 = 64;
+static constexpr int kMaxG512 = 32;
 
 // Work item of the query-parallel kernels (forward, dQ).
 struct QItem {
