@@ -154,6 +154,8 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
       dma.load(st, o_base + (long)s * kld, kld_b, seqlen - s, dw);
     }
   };
+  Sw512 sw;
+  sw.init(lane);
   if (n_tiles > 0) issue(0);
 
   for (int i = 0; i < n_tiles; ++i) {
@@ -172,17 +174,22 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
     if (i + 1 < n_tiles) issue(i + 1);
     const char *ks = smem + (i & 1) * 2 * TILE;
     const char *vs = ks + TILE;
-    // Opaque per tile: the swizzled fragment addresses are recomputed in the loop
-    // rather than held in registers across it.
-    int colx = col, lanex = lane, halfx = half;
-    asm volatile("" : "+v"(colx), "+v"(lanex), "+v"(halfx));
+    sw.opaque();
 
     // Partial Sᵀ = K Qᵀ over this wave's half of the head dim; the pair adds halves
     // 0 + 1 in that order.
     f32x16 part = zero16();
 #pragma unroll
     for (int kc = 0; kc < NKH; ++kc)
-      part = mfma(sw_frag<HD>(ks, colx, dh * NKH + kc, halfx), qf[kc], part);
+      part = mfma(sw.frag(lds_u32(ks) + dh * 512, kc), qf[kc], part);
+    // one fragment read two products ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int kc = 0; kc < NKH - 2; ++kc) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     xch_put(xch + wave * 1024, part, lane);
     __syncthreads();
     const f32x16 other = xch_get(xch + (wave ^ 1) * 1024, lane);
@@ -226,9 +233,17 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
     // Oᵀ += Vᵀ Pᵀ over this wave's half of the head dim.
 #pragma unroll
     for (int db = 0; db < NDH; ++db) {
-      acc[db] = mfma(sw_tr_frag<HD>(vs, 0, d0 + db * 32, lanex), p0, acc[db]);
-      acc[db] = mfma(sw_tr_frag<HD>(vs, 16, d0 + db * 32, lanex), p1, acc[db]);
+      acc[db] = mfma(sw.trfrag(lds_u32(vs) + d0 * 2, 0, db), p0, acc[db]);
+      acc[db] = mfma(sw.trfrag(lds_u32(vs) + d0 * 2, 16, db), p1, acc[db]);
     }
+    // one transposed fragment (two reads) two products ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int m = 0; m < 2 * NDH - 2; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   }
 
   const float l = pair_sum(l_run);
@@ -333,6 +348,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
       dma.load(st, o_base + (long)s * kld, kld_b, seqlen - s, wq);
     }
   };
+  Sw512 sw;
+  sw.init(lane);
   if (n_tiles > 0) issue(0);
 
   for (int i = 0; i < n_tiles; ++i) {
@@ -352,15 +369,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
     const char *ks = smem + (i & 1) * 2 * TILE;
     const char *vs = ks + TILE;
 
-    // Opaque per tile: the swizzled fragment addresses are recomputed in the loop
-    // rather than held in registers across it.
-    int colx = col, lanex = lane, halfx = half;
-    asm volatile("" : "+v"(colx), "+v"(lanex), "+v"(halfx));
+    sw.opaque();
     const char *op = role == 0 ? ks : vs;
     f32x16 part = zero16();
 #pragma unroll
     for (int kc = 0; kc < NKH; ++kc)
-      part = mfma(sw_frag<HD>(op, colx, dh * NKH + kc, halfx), xf[kc], part);
+      part = mfma(sw.frag(lds_u32(op) + dh * 512, kc), xf[kc], part);
+    // one fragment read two products ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int kc = 0; kc < NKH - 2; ++kc) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     xch_put(xch + wq * 1024, part, lane);
     __syncthreads();
     const f32x16 st = add16(part_of(0, wq, part, xch, lane), part_of(1, wq, part, xch, lane));
@@ -384,9 +406,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
     // dQᵀ += Kᵀ dSᵀ over this wave's quarter of the head dim.
 #pragma unroll
     for (int db = 0; db < NDQ; ++db) {
-      acc[db] = mfma(sw_tr_frag<HD>(ks, 0, dq0 + db * 32, lanex), d0, acc[db]);
-      acc[db] = mfma(sw_tr_frag<HD>(ks, 16, dq0 + db * 32, lanex), d1, acc[db]);
+      acc[db] = mfma(sw.trfrag(lds_u32(ks) + dq0 * 2, 0, db), d0, acc[db]);
+      acc[db] = mfma(sw.trfrag(lds_u32(ks) + dq0 * 2, 16, db), d1, acc[db]);
     }
+    // one transposed fragment (two reads) two products ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int m = 0; m < 2 * NDQ - 2; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   }
 
   if (row_valid) {
@@ -548,6 +578,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
       seek();
     }
   };
+  Sw512 sw;
+  sw.init(lane);
   int stage = 0;
   bool have = !done;
   int f0 = 0, flo = 0, fend = 0;
@@ -583,15 +615,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
     }
     const char *qs = smem + stage * STAGE;
     const char *dos = qs + TILE;
-    // Opaque per step: the swizzled fragment addresses are recomputed in the loop
-    // rather than held in registers across it.
-    int colx = col, lanex = lane, halfx = half;
-    asm volatile("" : "+v"(colx), "+v"(lanex), "+v"(halfx));
+    sw.opaque();
 
     const char *op = role == 0 ? qs : dos;
 #pragma unroll
     for (int kc = 0; kc < NKH; ++kc)
-      part = mfma(sw_frag<HD>(op, colx, dh * NKH + kc, halfx), xf[kc], part);
+      part = mfma(sw.frag(lds_u32(op) + dh * 512, kc), xf[kc], part);
     // one fragment read two products ahead
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
@@ -606,7 +635,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
     const int ta = flo / G, tb = (fend - 1) / G;
     const bool full = (f0 >= flo) && (f0 + BM <= fend) && (32 <= nkeys_g) &&
                       (kpb <= P + ta) && (wl < 0 || kpa >= P + tb - wl);
-    uint32_t pw[8], sw[8];   // P and dS as bf16 pairs (elements 2i, 2i + 1)
+    uint32_t pw[8], dsw[8];   // P and dS as bf16 pairs (elements 2i, 2i + 1)
     // S = partial 0 + partial 1 and dP - D = partial 2 + partial 3, then P and dS, four
     // elements at a time: the fence keeps each quad's exchange reads next to their
     // use, so few registers hold them.  The visibility test is compiled only into the
@@ -636,8 +665,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
         }
         pw[2 * q] = pack2(pq[0], pq[1]);
         pw[2 * q + 1] = pack2(pq[2], pq[3]);
-        sw[2 * q] = pack2(dq[0], dq[1]);
-        sw[2 * q + 1] = pack2(dq[2], dq[3]);
+        dsw[2 * q] = pack2(dq[0], dq[1]);
+        dsw[2 * q + 1] = pack2(dq[2], dq[3]);
         asm volatile("" ::: "memory");
       }
     };
@@ -646,14 +675,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
     else
       probs(std::true_type{});
     const bf16x8 p0 = words8(pw), p1 = words8(pw + 4);
-    const bf16x8 s0 = words8(sw), s1 = words8(sw + 4);
+    const bf16x8 s0 = words8(dsw), s1 = words8(dsw + 4);
     // dV += Pᵀ dO and dK += dSᵀ Q over this wave's quarter of the head dim.
 #pragma unroll
     for (int db = 0; db < NDQ; ++db) {
-      dv[db] = mfma(p0, sw_tr_frag<HD>(dos, 0, dq0 + db * 32, lanex), dv[db]);
-      dv[db] = mfma(p1, sw_tr_frag<HD>(dos, 16, dq0 + db * 32, lanex), dv[db]);
-      dk[db] = mfma(s0, sw_tr_frag<HD>(qs, 0, dq0 + db * 32, lanex), dk[db]);
-      dk[db] = mfma(s1, sw_tr_frag<HD>(qs, 16, dq0 + db * 32, lanex), dk[db]);
+      dv[db] = mfma(p0, sw.trfrag(lds_u32(dos) + dq0 * 2, 0, db), dv[db]);
+      dv[db] = mfma(p1, sw.trfrag(lds_u32(dos) + dq0 * 2, 16, db), dv[db]);
+      dk[db] = mfma(s0, sw.trfrag(lds_u32(qs) + dq0 * 2, 0, db), dk[db]);
+      dk[db] = mfma(s1, sw.trfrag(lds_u32(qs) + dq0 * 2, 16, db), dk[db]);
     }
     // one transposed fragment (two reads) two products ahead
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);

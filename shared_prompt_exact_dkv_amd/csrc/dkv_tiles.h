@@ -213,6 +213,51 @@ __device__ __forceinline__ bf16x8 sw_tr_frag(const char *lds, int row0, int col0
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// Factored fragment addresses for swizzled tiles of 1 KB rows (HD = 512).  In a
+// lane's reads of one tile the swizzle XOR touches only chunk bits 0-3, so every
+// read is one of 8 lane patterns (the XOR of a lane term with a small constant)
+// plus an immediate offset: a tile's 16 reads of each kind cost 8 address
+// operations instead of a full swizzle evaluation per read.  Tile addresses passed
+// in carry the wave's column base (2 bytes per element; a multiple of 128 elements).
+struct Sw512 {
+  uint32_t srow;    // row-operand reads: row col, at col * 1024 + ((half ^ swz(col)) << 4)
+  uint32_t tr[2];   // transposed reads: row 4 half + j / 4 (+ 8), 8 (j & 1) bytes in,
+                    // chunk term (c_l ^ swz(row)) << 4, c_l = 2 ((lane / 16) & 1) + (j & 3) / 2
+  __device__ __forceinline__ void init(int lane) {
+    const int col = lane & 31, half = lane >> 5, j = lane & 15;
+    const int c_l = 2 * ((lane >> 4) & 1) + ((j & 3) >> 1);
+    const int r = 4 * half + (j >> 2);
+    srow = col * 1024 + ((half ^ Swz<512>::swz(col)) << 4);
+    tr[0] = r * 1024 + 8 * (j & 1) + ((c_l ^ Swz<512>::swz(r)) << 4);
+    tr[1] = r * 1024 + 8 * (j & 1) + ((c_l ^ Swz<512>::swz(r + 8)) << 4);
+  }
+  // Keeps the lane terms opaque to the compiler, so the 16 patterns are formed per
+  // tile instead of living in registers across a loop.
+  __device__ __forceinline__ void opaque() { asm volatile("" : "+v"(srow), "+v"(tr[0]), "+v"(tr[1])); }
+  // Same as sw_frag<512>(tile, col, kc, half) for kc = 0 .. 15 past the column base.
+  __device__ __forceinline__ bf16x8 frag(uint32_t tile, int kc) const {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) const char lchar;
+    lchar *base = (lchar *)(size_t)(tile + (srow ^ ((kc & 7) << 5)));
+    return __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) u32x4 *)(base + (kc >> 3) * 256));
+  }
+  // Same as sw_tr_frag<512>(tile, row0, 32 db past the column base, lane), row0 a
+  // multiple of 16, db = 0 .. 7.
+  __device__ __forceinline__ bf16x8 trfrag(uint32_t tile, int row0, int db) const {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 ls16x4;
+    typedef __attribute__((address_space(3))) char lchar;
+    const int o = row0 * 1024 + (db >> 2) * 256;   // immediate offsets
+    lchar *b0 = (lchar *)(size_t)(tile + (tr[0] ^ ((db & 3) << 6)));
+    lchar *b1 = (lchar *)(size_t)(tile + (tr[1] ^ ((db & 3) << 6)));
+    s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4 *)(b0 + o));
+    s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4 *)(b1 + o + 8192));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, r);
+  }
+};
+
 // DMA of a ROWS x HD bf16 tile of consecutive rows (row stride ld_bytes, head offset
 // already in `base`) into a swizzled tile.  Block b (1 KB) of the tile is written by
 // wave b % 4; lane i of that instruction fills slot i of the block.  The per-lane
