@@ -192,8 +192,17 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     xch_put(xch + wave * 1024, part, lane);
     __syncthreads();
-    const f32x16 other = xch_get(xch + (wave ^ 1) * 1024, lane);
-    f32x16 s = dh == 0 ? add16(part, other) : add16(other, part);
+    // Full scores: own partial + the partner's, read a quad at a time (the sum is the
+    // same bits in both waves of the pair).
+    f32x16 s;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 o = xch_quad(xch + (wave ^ 1) * 1024, q, lane);
+      s[4 * q] = part[4 * q] + o.x;
+      s[4 * q + 1] = part[4 * q + 1] + o.y;
+      s[4 * q + 2] = part[4 * q + 2] + o.z;
+      s[4 * q + 3] = part[4 * q + 3] + o.w;
+    }
 
     const bool need_mask = (nrows < BN) || (kpos0 + BN - 1 > qmin) ||
                            (wl >= 0 && kpos0 < qmax - wl);
@@ -221,15 +230,18 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
         for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float t[16];
+    uint32_t pw[8];   // P as bf16 pairs
     float rs = 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      t[v] = fast_exp2(fmaf(s[v], sf, -m_use));
-      rs += t[v];
+    for (int v = 0; v < 16; v += 2) {
+      const float t0 = fast_exp2(fmaf(s[v], sf, -m_use));
+      const float t1 = fast_exp2(fmaf(s[v + 1], sf, -m_use));
+      rs += t0;
+      rs += t1;
+      pw[v / 2] = pack2(t0, t1);
     }
     l_run += rs;
-    const bf16x8 p0 = pack8(t), p1 = pack8(t + 8);
+    const bf16x8 p0 = words8(pw), p1 = words8(pw + 4);
     // Oᵀ += Vᵀ Pᵀ over this wave's half of the head dim.
 #pragma unroll
     for (int db = 0; db < NDH; ++db) {
