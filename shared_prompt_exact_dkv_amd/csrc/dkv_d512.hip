@@ -560,13 +560,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
     const __amdgpu_buffer_rsrc_t rx =
         make_rsrc_u(xsrc + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
     const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_u32(st + grp * TILE) + wq * 1024);
+    // (token, head) of the wave's first row, then stepped 4 rows at a time without a
+    // division.
+    const int f = cf + wq;
+    int t = (int)((unsigned)f / (unsigned)G);
+    int j = f - t * G;
+    int roff = t * qld_b + head0_b + j * (HD * 2);
 #pragma unroll
     for (int k = 0; k < RPW; ++k) {
       const int r = k * 4 + wq;
-      const int f = cf + r;
-      const int t = f / G, j = f - t * G;
-      const int off = t * qld_b + head0_b + j * (HD * 2) + ((lane ^ Swz<HD>::swz(r)) << 4);
-      dma16(rx, l0 + k * 4096, off);
+      dma16(rx, l0 + k * 4096, roff + ((lane ^ Swz<HD>::swz(r)) << 4));
+      j += 4;
+      roff += 4 * HD * 2;
+      while (j >= G) {
+        j -= G;
+        roff += qld_b - G * HD * 2;
+      }
     }
   };
   // Row init values of the step at the cursor (rows past the sequence read 0 and are
@@ -574,7 +583,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
   auto fetch_init = [&]() -> float {
     const int s0 = sload_i32(a.cu, cs);
     const int f = cf + col;
-    const int t = f / G, j = f - t * G;
+    const int t = (int)((unsigned)f / (unsigned)G), j = f - t * G;
     const int off = ((g * G + j) * a.lse_ld + s0 + t) * 4;
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_ld, off, 0, 0));
   };
@@ -644,9 +653,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
     xch_put(xch + wq * 1024, part, lane);
     __syncthreads();
 
-    const int ta = flo / G, tb = (fend - 1) / G;
+    // Every row of the block sees every key of the group: the last key is causal for
+    // the first row's token (kpb - P <= flo / G) and the first key is inside the last
+    // row's window (kpa >= P + (fend - 1) / G - wl), in flattened units.
     const bool full = (f0 >= flo) && (f0 + BM <= fend) && (32 <= nkeys_g) &&
-                      (kpb <= P + ta) && (wl < 0 || kpa >= P + tb - wl);
+                      ((kpb - P) * G <= flo) && (wl < 0 || fend <= (kpa - P + wl + 1) * G);
     uint32_t pw[8], dsw[8];   // P and dS as bf16 pairs (elements 2i, 2i + 1)
     // S = partial 0 + partial 1 and dP - D = partial 2 + partial 3, then P and dS, four
     // elements at a time: the fence keeps each quad's exchange reads next to their
