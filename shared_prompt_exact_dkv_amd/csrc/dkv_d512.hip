@@ -48,15 +48,6 @@ __device__ __forceinline__ void xch_put(float *area, const f32x16 &x, int lane) 
 __device__ __forceinline__ float4 xch_quad(const float *area, int q, int lane) {
   return *reinterpret_cast<const float4 *>(area + q * 256 + lane * 4);
 }
-__device__ __forceinline__ f32x16 xch_get(const float *area, int lane) {
-  f32x16 x;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float4 t = xch_quad(area, q, lane);
-    x[4 * q] = t.x, x[4 * q + 1] = t.y, x[4 * q + 2] = t.z, x[4 * q + 3] = t.w;
-  }
-  return x;
-}
 // Two floats as a bf16 pair (x in the low half), and four such words as 8 bf16.
 __device__ __forceinline__ uint32_t pack2(float x, float y) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -66,19 +57,6 @@ __device__ __forceinline__ uint32_t pack2(float x, float y) {
 __device__ __forceinline__ bf16x8 words8(const uint32_t *w) {
   return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
 }
-// a + b element-wise (the fixed summation order of the partial tiles).
-__device__ __forceinline__ f32x16 add16(const f32x16 &a, const f32x16 &b) {
-  f32x16 r;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) r[v] = a[v] + b[v];
-  return r;
-}
-// Partial tile of wave w: its own registers, else the exchange area.
-__device__ __forceinline__ f32x16 part_of(int w, int me, const f32x16 &mine, const float *xch,
-                                          int lane) {
-  return w == me ? mine : xch_get(xch + w * 1024, lane);
-}
-
 }  // namespace
 
 // ------------------------------------------------------------------- forward --
@@ -397,24 +375,35 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     xch_put(xch + wq * 1024, part, lane);
     __syncthreads();
-    const f32x16 st = add16(part_of(0, wq, part, xch, lane), part_of(1, wq, part, xch, lane));
-    const f32x16 dpt = add16(part_of(2, wq, part, xch, lane), part_of(3, wq, part, xch, lane));
-
     const bool need_mask = (nrows < BN) || (kpos0 + BN - 1 > qmin) ||
                            (wl >= 0 && kpos0 < qmax - wl);
-    float ds[16];
+    // S = partial 0 + partial 1 and dP = partial 2 + partial 3 (every wave reads all
+    // four back, its own included, and adds them in that order), then dS, a quad at a
+    // time: the fence keeps each quad's reads next to their use.
+    uint32_t dw[8];   // dS as bf16 pairs
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float p = fast_exp2(fmaf(st[v], sf, -lse2));
-      if (need_mask) {
-        int kk = c_row(v, half);
-        int kp = kpos0 + kk;
-        bool vis = (kk < nrows) && (kp <= qpos) && (wl < 0 || kp >= qpos - wl);
-        if (!vis) p = 0.f;
+    for (int q = 0; q < 4; ++q) {
+      const float4 a0 = xch_quad(xch, q, lane), a1 = xch_quad(xch + 1024, q, lane);
+      const float4 b0 = xch_quad(xch + 2048, q, lane), b1 = xch_quad(xch + 3072, q, lane);
+      const float st[4] = {a0.x + a1.x, a0.y + a1.y, a0.z + a1.z, a0.w + a1.w};
+      const float dpt[4] = {b0.x + b1.x, b0.y + b1.y, b0.z + b1.z, b0.w + b1.w};
+      float dsq[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float p = fast_exp2(fmaf(st[e], sf, -lse2));
+        if (need_mask) {
+          const int kk = 8 * q + 4 * half + e;   // c_row(4 q + e, half)
+          const int kp = kpos0 + kk;
+          const bool vis = (kk < nrows) && (kp <= qpos) && (wl < 0 || kp >= qpos - wl);
+          if (!vis) p = 0.f;
+        }
+        dsq[e] = p * (dpt[e] - Dq);
       }
-      ds[v] = p * (dpt[v] - Dq);
+      dw[2 * q] = pack2(dsq[0], dsq[1]);
+      dw[2 * q + 1] = pack2(dsq[2], dsq[3]);
+      asm volatile("" ::: "memory");
     }
-    const bf16x8 d0 = pack8(ds), d1 = pack8(ds + 8);
+    const bf16x8 d0 = words8(dw), d1 = words8(dw + 4);
     // dQᵀ += Kᵀ dSᵀ over this wave's quarter of the head dim.
 #pragma unroll
     for (int db = 0; db < NDQ; ++db) {

@@ -38,6 +38,11 @@ CASES = [
     (129, [33, 64, 1], 4, 1, 512, 40, "bf16", False),
     (100, [150, 20], 16, 4, 512, 63, "bf16", False),
     (0, [80], 4, 4, 512, -1, "bf16", False),
+    # head dim 512 with 3 and 2 query heads per kv head (rows of a step or tile split
+    # tokens unevenly), over several 128-row / 64-key tiles and ragged tails
+    (37, [61, 130], 6, 2, 512, 50, "bf16", False),
+    (90, [77], 8, 4, 512, -1, "bf16", True),
+    (200, [300, 45], 8, 2, 512, -1, "bf16", False),
     # the largest grouped-query ratios (128 at head dims 64 / 128, 32 at 512), and a
     # window far past every position (run as the global mask)
     (37, [40, 3], 128, 1, 64, -1, "bf16", False),
