@@ -7,7 +7,8 @@
 // waves of a workgroup and keep every wave within the architectural VGPRs:
 //
 //   forward  128 query rows per workgroup of 8 waves (two per SIMD); the two waves of
-//            a pair share 32 rows and each holds Q and O for one half of the head dim.  Each computes the
+//            a pair share 32 rows and each holds Q and O for one half of the head dim.
+//            Waves 0-3 run half a tile ahead of waves 4-7 (which share their SIMDs).  Each computes the
 //            partial scores Sᵀ over its half, the pair adds the two partials through
 //            LDS (both in the same order, so both see identical scores), and each
 //            accumulates its half of O.
@@ -122,7 +123,8 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
   const bf16 *o_base = isv ? vo_base : ko_base;
   DmaRows<HD, BN> dma;
   dma.init(dw, lane, kld_b);
-  auto issue = [&](int i) {   // tile i -> stage i % 2 (K, then V)
+  // Tile i goes to stage i % 2: waves 0-3 fetch its K rows, waves 4-7 its V rows.
+  auto issue = [&](int i) {
     char *st = smem + (i & 1) * 2 * TILE + isv * TILE;
     if (i < n_ctx) {
       int s = ctx_t0 + i * BN;
@@ -134,28 +136,11 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
   };
   Sw512 sw;
   sw.init(lane);
-  if (n_tiles > 0) issue(0);
 
-  for (int i = 0; i < n_tiles; ++i) {
-    int nrows, kpos0;
-    if (i < n_ctx) {
-      int s = ctx_t0 + i * BN;
-      nrows = P - s;
-      kpos0 = s;
-    } else {
-      int s = own_t0 + (i - n_ctx) * BN;
-      nrows = seqlen - s;
-      kpos0 = P + s;
-    }
-    dma_wait();
-    __syncthreads();
-    if (i + 1 < n_tiles) issue(i + 1);
+  // Partial Sᵀ = K Qᵀ of tile i over this wave's half of the head dim, into the
+  // wave's exchange slot.
+  auto scores = [&](int i) {
     const char *ks = smem + (i & 1) * 2 * TILE;
-    const char *vs = ks + TILE;
-    sw.opaque();
-
-    // Partial Sᵀ = K Qᵀ over this wave's half of the head dim; the pair adds halves
-    // 0 + 1 in that order.
     f32x16 part = zero16();
 #pragma unroll
     for (int kc = 0; kc < NKH; ++kc)
@@ -169,17 +154,31 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     xch_put(xch + wave * 1024, part, lane);
-    __syncthreads();
-    // Full scores: own partial + the partner's, read a quad at a time (the sum is the
+  };
+  // Softmax of tile i from the pair's two partials, then Oᵀ += Vᵀ Pᵀ.
+  auto accumulate = [&](int i) {
+    int nrows, kpos0;
+    if (i < n_ctx) {
+      int s = ctx_t0 + i * BN;
+      nrows = P - s;
+      kpos0 = s;
+    } else {
+      int s = own_t0 + (i - n_ctx) * BN;
+      nrows = seqlen - s;
+      kpos0 = P + s;
+    }
+    const char *vs = smem + (i & 1) * 2 * TILE + TILE;
+    // Full scores: the pair's partials 0 + 1, both read back a quad at a time (the
     // same bits in both waves of the pair).
     f32x16 s;
+    const float *pa = xch + (wave & ~1) * 1024;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float4 o = xch_quad(xch + (wave ^ 1) * 1024, q, lane);
-      s[4 * q] = part[4 * q] + o.x;
-      s[4 * q + 1] = part[4 * q + 1] + o.y;
-      s[4 * q + 2] = part[4 * q + 2] + o.z;
-      s[4 * q + 3] = part[4 * q + 3] + o.w;
+      const float4 x0 = xch_quad(pa, q, lane), x1 = xch_quad(pa + 1024, q, lane);
+      s[4 * q] = x0.x + x1.x;
+      s[4 * q + 1] = x0.y + x1.y;
+      s[4 * q + 2] = x0.z + x1.z;
+      s[4 * q + 3] = x0.w + x1.w;
     }
 
     const bool need_mask = (nrows < BN) || (kpos0 + BN - 1 > qmin) ||
@@ -234,7 +233,32 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  };
+
+  // Ping-pong: waves 0-3 run half a tile ahead of waves 4-7 (one of each per SIMD), so
+  // one group's softmax overlaps the other's products.  Both run the same loop, but
+  // waves 4-7 pass one barrier first: in phase 2i waves 0-3 form the scores of tile i
+  // while waves 4-7 accumulate tile i - 1, in phase 2i + 1 the reverse.  K of tile i + 1
+  // is fetched by waves 0-3 in phase 2i (its stage was last read in phase 2i - 1) and
+  // lands before phase 2i + 2; V of tile i + 1 by waves 4-7 in phase 2i + 1 (last read
+  // in phase 2i) and lands before phase 2i + 3.  Every wave passes 2 n + 2 barriers.
+  const bool lead = wave < 4;
+  if (n_tiles > 0) {
+    issue(0);
+    dma_wait();
   }
+  __syncthreads();
+  if (!lead) __syncthreads();
+  for (int i = 0; i < n_tiles; ++i) {
+    sw.opaque();
+    if (i + 1 < n_tiles) issue(i + 1);
+    scores(i);
+    __syncthreads();
+    accumulate(i);
+    dma_wait();
+    __syncthreads();
+  }
+  if (lead) __syncthreads();
 
   const float l = pair_sum(l_run);
   const float inv = 1.f / l;
