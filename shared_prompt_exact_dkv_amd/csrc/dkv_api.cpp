@@ -471,11 +471,18 @@ std::vector<KVItem> build_kv_items(const Shape &s, bool with_ctx, bool split) {
         gr.recs.push_back({kv_rows_visible(s, false, k0, nk, len), kRegionOwn, k0, i, i + 1});
       }
     }
-    if (gr.recs.empty()) continue;
-    for (const Rec &r : gr.recs) gr.work += r.work;
-    std::stable_sort(gr.recs.begin(), gr.recs.end(),
-                     [](const Rec &a, const Rec &b) { return a.work > b.work; });
-    groups.push_back(std::move(gr));
+    // The chunk's prompt-key tiles and its own-key tiles form separate groups: the
+    // prompt-key tiles all walk the same rows (every row of the chunk), so a group of
+    // them shares its row blocks in L2.
+    Group ctxg{0, {}}, owng{0, {}};
+    for (const Rec &r : gr.recs) (r.region == kRegionCtx ? ctxg : owng).recs.push_back(r);
+    for (Group *x : {&ctxg, &owng}) {
+      if (x->recs.empty()) continue;
+      for (const Rec &r : x->recs) x->work += r.work;
+      std::stable_sort(x->recs.begin(), x->recs.end(),
+                       [](const Rec &a, const Rec &b) { return a.work > b.work; });
+      groups.push_back(std::move(*x));
+    }
   }
   std::stable_sort(groups.begin(), groups.end(),
                    [](const Group &a, const Group &b) { return a.work > b.work; });
