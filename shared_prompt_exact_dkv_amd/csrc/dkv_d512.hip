@@ -184,12 +184,14 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
     const bool need_mask = (nrows < BN) || (kpos0 + BN - 1 > qmin) ||
                            (wl >= 0 && kpos0 < qmax - wl);
     if (need_mask) {
+      // Visible keys of this lane's row as a range of tile offsets [lo, hi): inside the
+      // tile, causal, and inside the window; compared per element without branches.
+      const int lo = (wl >= 0 ? qpos - wl - kpos0 : -BN) - 4 * half;
+      const int hi = min(nrows, qpos - kpos0 + 1) - 4 * half;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        int kk = c_row(v, half);
-        int kp = kpos0 + kk;
-        bool vis = (kk < nrows) && (kp <= qpos) && (wl < 0 || kp >= qpos - wl);
-        if (!vis) s[v] = -INFINITY;
+        const int r = 8 * (v >> 2) + (v & 3);   // c_row(v, half) - 4 half
+        s[v] = (r >= lo) & (r < hi) ? s[v] : -INFINITY;
       }
     }
     float mx = -INFINITY;
@@ -405,28 +407,37 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
     // four back, its own included, and adds them in that order), then dS, a quad at a
     // time: the fence keeps each quad's reads next to their use.
     uint32_t dw[8];   // dS as bf16 pairs
+    // The visibility test (keys of this lane's row as tile offsets [lo, hi), compared
+    // without branches) is compiled only into the variant for tiles that need it.
+    auto grads = [&](auto masked_c) {
+      constexpr bool MASKED = decltype(masked_c)::value;
+      const int lo = (wl >= 0 ? qpos - wl - kpos0 : -BN) - 4 * half;
+      const int hi = min(nrows, qpos - kpos0 + 1) - 4 * half;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 a0 = xch_quad(xch, q, lane), a1 = xch_quad(xch + 1024, q, lane);
-      const float4 b0 = xch_quad(xch + 2048, q, lane), b1 = xch_quad(xch + 3072, q, lane);
-      const float st[4] = {a0.x + a1.x, a0.y + a1.y, a0.z + a1.z, a0.w + a1.w};
-      const float dpt[4] = {b0.x + b1.x, b0.y + b1.y, b0.z + b1.z, b0.w + b1.w};
-      float dsq[4];
+      for (int q = 0; q < 4; ++q) {
+        const float4 a0 = xch_quad(xch, q, lane), a1 = xch_quad(xch + 1024, q, lane);
+        const float4 b0 = xch_quad(xch + 2048, q, lane), b1 = xch_quad(xch + 3072, q, lane);
+        const float st[4] = {a0.x + a1.x, a0.y + a1.y, a0.z + a1.z, a0.w + a1.w};
+        const float dpt[4] = {b0.x + b1.x, b0.y + b1.y, b0.z + b1.z, b0.w + b1.w};
+        float dsq[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float p = fast_exp2(fmaf(st[e], sf, -lse2));
-        if (need_mask) {
-          const int kk = 8 * q + 4 * half + e;   // c_row(4 q + e, half)
-          const int kp = kpos0 + kk;
-          const bool vis = (kk < nrows) && (kp <= qpos) && (wl < 0 || kp >= qpos - wl);
-          if (!vis) p = 0.f;
+        for (int e = 0; e < 4; ++e) {
+          float p = fast_exp2(fmaf(st[e], sf, -lse2));
+          if (MASKED) {
+            const int r = 8 * q + e;   // c_row(4 q + e, half) - 4 half
+            p = (r >= lo) & (r < hi) ? p : 0.f;
+          }
+          dsq[e] = p * (dpt[e] - Dq);
         }
-        dsq[e] = p * (dpt[e] - Dq);
+        dw[2 * q] = pack2(dsq[0], dsq[1]);
+        dw[2 * q + 1] = pack2(dsq[2], dsq[3]);
+        asm volatile("" ::: "memory");
       }
-      dw[2 * q] = pack2(dsq[0], dsq[1]);
-      dw[2 * q + 1] = pack2(dsq[2], dsq[3]);
-      asm volatile("" ::: "memory");
-    }
+    };
+    if (need_mask)
+      grads(std::true_type{});
+    else
+      grads(std::false_type{});
     const bf16x8 d0 = words8(dw), d1 = words8(dw + 4);
     // dQᵀ += Kᵀ dSᵀ over this wave's quarter of the head dim.
 #pragma unroll
