@@ -746,8 +746,9 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
   }
 
   // Query rows that can see this key tile, per sequence, in flattened units.
-  auto seq_range = [&](int sq, int &fa, int &fb) {
-    int len = sload_i32(a.cu, sq + 1) - sload_i32(a.cu, sq);
+  auto seq_range = [&](int sq, int &fa, int &fb, int &s0, int &len) {
+    s0 = sload_i32(a.cu, sq);
+    len = sload_i32(a.cu, sq + 1) - s0;
     int r_lo, r_hi;
     if (ctx) {
       r_lo = 0;
@@ -763,15 +764,19 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
   };
   // Steps sit on multiples of BM flattened rows, walked from the last one backward, so
   // every key tile of a sequence streams the same rows at the same time (L2 reuse).
-  int cs = it.seq_hi - 1, cf = 0, cfa = 0, cfb = 0;
+  // The cursor's sequence start and length are kept from the seek, so a step's
+  // fetch issues no scalar load.
+  int cs = it.seq_hi - 1, cf = 0, cfa = 0, cfb = 0, cs0 = 0, clen = 0;
   bool done = false;
   auto seek = [&]() {
     while (cs >= it.seq_lo) {
-      int fa, fb;
-      seq_range(cs, fa, fb);
+      int fa, fb, s0, len;
+      seq_range(cs, fa, fb, s0, len);
       if (fb > fa) {
         cfa = fa;
         cfb = fb;
+        cs0 = s0;
+        clen = len;
         cf = ((fb - 1) / BM) * BM;
         return;
       }
@@ -790,8 +795,8 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
 
   // Fetch the step at the cursor into stage `st`.
   auto issue = [&](char *st) {
-    const int s0 = sload_i32(a.cu, cs);
-    const int len = sload_i32(a.cu, cs + 1) - s0;
+    const int s0 = cs0;
+    const int len = clen;
     const __amdgpu_buffer_rsrc_t rq =
         make_rsrc_u(reinterpret_cast<const bf16 *>(a.q) + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
     const __amdgpu_buffer_rsrc_t rd =

@@ -534,8 +534,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
     dv[db] = zero16();
   }
 
-  auto seq_range = [&](int sq, int &fa, int &fb) {
-    int len = sload_i32(a.cu, sq + 1) - sload_i32(a.cu, sq);
+  auto seq_range = [&](int sq, int &fa, int &fb, int &s0, int &len) {
+    s0 = sload_i32(a.cu, sq);
+    len = sload_i32(a.cu, sq + 1) - s0;
     int r_lo, r_hi;
     if (ctx) {
       r_lo = 0;
@@ -550,15 +551,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
     fb = r_hi > r_lo ? r_hi * G : fa;
   };
   // Steps of BM flattened rows, walked from the last one backward.
-  int cs = it.seq_hi - 1, cf = 0, cfa = 0, cfb = 0;
+  // The cursor's sequence start and length are kept from the seek, so a step's
+  // fetch issues no scalar load.
+  int cs = it.seq_hi - 1, cf = 0, cfa = 0, cfb = 0, cs0 = 0, clen = 0;
   bool done = false;
   auto seek = [&]() {
     while (cs >= it.seq_lo) {
-      int fa, fb;
-      seq_range(cs, fa, fb);
+      int fa, fb, s0, len;
+      seq_range(cs, fa, fb, s0, len);
       if (fb > fa) {
         cfa = fa;
         cfb = fb;
+        cs0 = s0;
+        clen = len;
         cf = ((fb - 1) / BM) * BM;
         return;
       }
@@ -579,8 +584,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
   const __amdgpu_buffer_rsrc_t r_ld = make_rsrc_u(role == 0 ? (const void *)a.lsn : (const void *)a.Dneg,
                                                   (uint32_t)((long)a.Hq * a.lse_ld * 4));
   auto issue = [&](char *st) {
-    const int s0 = sload_i32(a.cu, cs);
-    const int len = sload_i32(a.cu, cs + 1) - s0;
+    const int s0 = cs0;
+    const int len = clen;
     const __amdgpu_buffer_rsrc_t rx =
         make_rsrc_u(xsrc + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
     const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_u32(st + grp * TILE) + wq * 1024);
@@ -605,7 +610,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
   // Row init values of the step at the cursor (rows past the sequence read 0 and are
   // masked later).
   auto fetch_init = [&]() -> float {
-    const int s0 = sload_i32(a.cu, cs);
+    const int s0 = cs0;
     const int f = cf + col;
     const int t = (int)((unsigned)f / (unsigned)G), j = f - t * G;
     const int off = ((g * G + j) * a.lse_ld + s0 + t) * 4;
