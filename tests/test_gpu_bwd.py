@@ -43,6 +43,7 @@ CASES = [
     (37, [61, 130], 6, 2, 512, 50, "bf16", False),
     (90, [77], 8, 4, 512, -1, "bf16", True),
     (200, [300, 45], 8, 2, 512, -1, "bf16", False),
+    (0, [3, 1], 2, 1, 512, -1, "bf16", False),   # one key tile: the shortest pipelines
     # the largest grouped-query ratios (128 at head dims 64 / 128, 32 at 512), and a
     # window far past every position (run as the global mask)
     (37, [40, 3], 128, 1, 64, -1, "bf16", False),
