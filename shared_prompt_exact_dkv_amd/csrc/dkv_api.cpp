@@ -563,11 +563,14 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
   if (s.T > 0) {
     float *Dneg = reinterpret_cast<float *>(wsb + pl.d_off);
     float *lsn = reinterpret_cast<float *>(wsb + pl.l2_off);
-    e = timed(kKPre, stream, [&] {
-      return launch_bwd_pre(s.dtype, s.d, io.o, io.dout, io.lse, Dneg, lsn, s.T, s.Hq, s.scale,
-                            stream);
-    });
-    if (e != hipSuccess) return hip_fail(e, "bwd preprocess launch");
+    const bool fused_pre = dq_fuses_pre(s.dtype, s.d);
+    if (!fused_pre) {
+      e = timed(kKPre, stream, [&] {
+        return launch_bwd_pre(s.dtype, s.d, io.o, io.dout, io.lse, Dneg, lsn, s.T, s.Hq, s.scale,
+                              stream);
+      });
+      if (e != hipSuccess) return hip_fail(e, "bwd preprocess launch");
+    }
     std::vector<QItem> qi = build_q_items(s, s.bm_tok_dq, kFwdBN);
     std::vector<KVItem> kv = build_kv_items(s, io.with_ctx, split);
     if ((st = upload(qi.data(), qi.size() * sizeof(QItem), wsb + pl.q_off, stream)) != DKV_OK) return st;
@@ -575,6 +578,11 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
     BwdQArgs qa{};
     qa.q = io.q; qa.k_ctx = io.kc; qa.v_ctx = io.vc; qa.k_own = io.ko; qa.v_own = io.vo;
     qa.dout = io.dout; qa.lse = io.lse; qa.Dneg = Dneg; qa.dq = io.dq;
+    if (fused_pre) {
+      qa.o = io.o;
+      qa.Dneg_out = Dneg;
+      qa.lsn_out = lsn;
+    }
     qa.items = reinterpret_cast<const QItem *>(wsb + pl.q_off);
     qa.Hq = s.Hq; qa.Hkv = s.Hkv; qa.G = s.G; qa.bm_tok = s.bm_tok_dq; qa.ctx_len = s.P;
     qa.window_left = s.wl; qa.lse_ld = (int)s.T; qa.scale = s.scale;

@@ -300,8 +300,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
     df[kc] = as_bf16x8(*reinterpret_cast<const uint4 *>(dptr + kc * 16 + half * 8));
   }
   const float sf = a.scale * kLog2e;
-  const float lse2 = a.lse[(long)h * a.lse_ld + qrow] * kLog2e;
-  const float Dq = -a.Dneg[(long)h * a.lse_ld + qrow];
+  const float lse = a.lse[(long)h * a.lse_ld + qrow];
+  const float lse2 = lse * kLog2e;
+  // D = rowsum(dO ∘ O) of this lane's row (the preprocess step of the backward, done
+  // here): the two lanes of a row each hold half of it, in the dO fragments' layout.
+  const bf16 *optr = reinterpret_cast<const bf16 *>(a.o) + qrow * qld + (long)h * HD;
+  float Dq = 0.f;
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    const bf16x8 o8 = as_bf16x8(*reinterpret_cast<const uint4 *>(optr + kc * 16 + half * 8));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) Dq += (float)o8[e] * (float)df[kc][e];
+  }
+  Dq = pair_sum(Dq);
+  // The dK/dV kernel, which runs next, reads -D and -LSE / scale of every row.
+  if (row_valid && half == 0) {
+    a.Dneg_out[(long)h * a.lse_ld + qrow] = -Dq;
+    a.lsn_out[(long)h * a.lse_ld + qrow] = -lse * (1.0f / a.scale);
+  }
   // dP accumulators start from -D (this lane's row): the products end as dP - D.
   f32x16 negd;
 #pragma unroll
