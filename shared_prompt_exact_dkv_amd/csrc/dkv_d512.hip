@@ -328,8 +328,31 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
   for (int kc = 0; kc < NKH; ++kc)
     xf[kc] = as_bf16x8(*reinterpret_cast<const uint4 *>(xptr + kc * 16 + half * 8));
   const float sf = a.scale * kLog2e;
-  const float lse2 = a.lse[(long)h * a.lse_ld + qrow] * kLog2e;
-  const float Dq = -a.Dneg[(long)h * a.lse_ld + qrow];
+  const float lse = a.lse[(long)h * a.lse_ld + qrow];
+  const float lse2 = lse * kLog2e;
+  // D = rowsum(dO ∘ O) of this lane's row (the preprocess step of the backward, done
+  // here): waves 2 / 3 of the group hold dO over the two halves of the head dim; each
+  // sums its half against O (the two lanes of a row a quarter each), puts it in the
+  // exchange area, and every wave adds the halves 0 + 1 after a barrier.
+  if (role == 1) {
+    const bf16 *optr = reinterpret_cast<const bf16 *>(a.o) + qrow * qld + (long)h * HD + dh * (HD / 2);
+    float dh_sum = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < NKH; ++kc) {
+      const bf16x8 o8 = as_bf16x8(*reinterpret_cast<const uint4 *>(optr + kc * 16 + half * 8));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dh_sum += (float)o8[e] * (float)xf[kc][e];
+    }
+    dh_sum = pair_sum(dh_sum);
+    if (half == 0) xch[dh * 32 + col] = dh_sum;
+  }
+  __syncthreads();
+  const float Dq = xch[col] + xch[32 + col];
+  // The dK/dV kernel, which runs next, reads -D and -LSE / scale of every row.
+  if (wq == 0 && half == 0 && row_valid) {
+    a.Dneg_out[(long)h * a.lse_ld + qrow] = -Dq;
+    a.lsn_out[(long)h * a.lse_ld + qrow] = -lse * (1.0f / a.scale);
+  }
   const int dq0 = wq * (HD / 4);
 
   f32x16 acc[NDQ];

@@ -67,8 +67,8 @@ hipError_t launch_cast(int dtype, const float *src, void *dst, long n, hipStream
 struct BwdQArgs {
   const void *q, *k_ctx, *v_ctx, *k_own, *v_own, *dout;
   const float *lse, *Dneg;     // Dneg = -rowsum(dO * O) (from the preprocess kernel)
-  // bf16 at head dims 64 / 128 (no preprocess launch): the dQ kernel forms D from O and
-  // dO itself and writes -D and -LSE / scale of its rows here, for the dK/dV kernel.
+  // bf16 (no preprocess launch): the dQ kernel forms D from O and dO itself and writes
+  // -D and -LSE / scale of its rows here, for the dK/dV kernel.
   const void *o;
   float *Dneg_out, *lsn_out;
   void *dq;
@@ -78,7 +78,7 @@ struct BwdQArgs {
 };
 hipError_t launch_bwd_dq(int dtype, int head_dim, const BwdQArgs &a, int n_items, hipStream_t s);
 // Whether launch_bwd_dq forms the preprocess terms itself (so no launch_bwd_pre).
-inline bool dq_fuses_pre(int dtype, int head_dim) { return dtype == 0 && head_dim <= 128; }
+inline bool dq_fuses_pre(int dtype, int head_dim) { (void)head_dim; return dtype == 0; }
 hipError_t launch_bwd_dq_d512(const BwdQArgs &a, int n_items, hipStream_t s);
 
 // Work item of the key-parallel dK/dV kernel: one key tile of one region of one kv
