@@ -710,47 +710,50 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
     // row's window (kpa >= P + (fend - 1) / G - wl), in flattened units.
     const bool full = (f0 >= flo) && (f0 + BM <= fend) && (32 <= nkeys_g) &&
                       ((kpb - P) * G <= flo) && (wl < 0 || fend <= (kpa - P + wl + 1) * G);
-    uint32_t pw[8], dsw[8];   // P and dS as bf16 pairs (elements 2i, 2i + 1)
-    // S = partial 0 + partial 1 and dP - D = partial 2 + partial 3, then P and dS, four
-    // elements at a time: the fence keeps each quad's exchange reads next to their
-    // use, so few registers hold them.  The visibility test is compiled only into the
-    // variant for blocks that straddle a mask edge or a range end.
-    // (The wave's own partial is read back too, so it holds no registers here.)
-    auto quad_of = [&](int w, int q) -> float4 { return xch_quad(xch + w * 1024, q, lane); };
+    // S = partial 0 + partial 1 and dP - D = partial 2 + partial 3 are formed by the four
+    // waves of the group a quad each (C-tile elements 4 wq .. 4 wq + 3): this wave reads
+    // quad wq of the four partials, turns it into P and dS, and writes them as bf16 into
+    // quad wq of its own slot (which no other wave reads); after a barrier every wave
+    // reads the four quads of P and dS back as its MFMA operands.  The visibility test
+    // is compiled only into the variant for blocks that straddle a mask edge or a range
+    // end.
     auto probs = [&](auto masked_c) {
       constexpr bool MASKED = decltype(masked_c)::value;
       const int lo = max(flo, f_vis_lo) - f0 - 4 * half;   // visible row offsets [lo, hi)
       const int hi = min(fend, f_vis_hi) - f0 - 4 * half;
+      const int q = wq;
+      const float4 a0 = xch_quad(xch, q, lane), a1 = xch_quad(xch + 1024, q, lane);
+      const float4 b0 = xch_quad(xch + 2048, q, lane), b1 = xch_quad(xch + 3072, q, lane);
+      const float st[4] = {a0.x + a1.x, a0.y + a1.y, a0.z + a1.z, a0.w + a1.w};
+      const float dpt[4] = {b0.x + b1.x, b0.y + b1.y, b0.z + b1.z, b0.w + b1.w};
+      float pq[4], dq[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 a0 = quad_of(0, q), a1 = quad_of(1, q);
-        const float4 b0 = quad_of(2, q), b1 = quad_of(3, q);
-        const float st[4] = {a0.x + a1.x, a0.y + a1.y, a0.z + a1.z, a0.w + a1.w};
-        const float dpt[4] = {b0.x + b1.x, b0.y + b1.y, b0.z + b1.z, b0.w + b1.w};
-        float pq[4], dq[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float p = fast_exp2(st[e] * sf);
-          if (MASKED) {
-            const int r = 8 * q + e;
-            if (r < lo || r >= hi) p = 0.f;
-          }
-          pq[e] = p;
-          dq[e] = p * dpt[e];
+      for (int e = 0; e < 4; ++e) {
+        float p = fast_exp2(st[e] * sf);
+        if (MASKED) {
+          const int r = 8 * q + e;
+          p = (r >= lo) & (r < hi) ? p : 0.f;
         }
-        pw[2 * q] = pack2(pq[0], pq[1]);
-        pw[2 * q + 1] = pack2(pq[2], pq[3]);
-        dsw[2 * q] = pack2(dq[0], dq[1]);
-        dsw[2 * q + 1] = pack2(dq[2], dq[3]);
-        asm volatile("" ::: "memory");
+        pq[e] = p;
+        dq[e] = p * dpt[e];
       }
+      *reinterpret_cast<uint4 *>(xch + wq * 1024 + q * 256 + lane * 4) =
+          make_uint4(pack2(pq[0], pq[1]), pack2(pq[2], pq[3]), pack2(dq[0], dq[1]),
+                     pack2(dq[2], dq[3]));
     };
     if (full)
       probs(std::false_type{});
     else
       probs(std::true_type{});
-    const bf16x8 p0 = words8(pw), p1 = words8(pw + 4);
-    const bf16x8 s0 = words8(dsw), s1 = words8(dsw + 4);
+    __syncthreads();
+    uint4 pd[4];   // quad w of slot w: P of elements 4w .. 4w+3 (x, y), dS (z, w)
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      pd[w] = *reinterpret_cast<const uint4 *>(xch + w * 1024 + w * 256 + lane * 4);
+    const bf16x8 p0 = __builtin_bit_cast(bf16x8, make_uint4(pd[0].x, pd[0].y, pd[1].x, pd[1].y));
+    const bf16x8 p1 = __builtin_bit_cast(bf16x8, make_uint4(pd[2].x, pd[2].y, pd[3].x, pd[3].y));
+    const bf16x8 s0 = __builtin_bit_cast(bf16x8, make_uint4(pd[0].z, pd[0].w, pd[1].z, pd[1].w));
+    const bf16x8 s1 = __builtin_bit_cast(bf16x8, make_uint4(pd[2].z, pd[2].w, pd[3].z, pd[3].w));
     // dV += Pᵀ dO and dK += dSᵀ Q over this wave's quarter of the head dim.
 #pragma unroll
     for (int db = 0; db < NDQ; ++db) {
