@@ -426,42 +426,46 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
     __syncthreads();
     const bool need_mask = (nrows < BN) || (kpos0 + BN - 1 > qmin) ||
                            (wl >= 0 && kpos0 < qmax - wl);
-    // S = partial 0 + partial 1 and dP = partial 2 + partial 3 (every wave reads all
-    // four back, its own included, and adds them in that order), then dS, a quad at a
-    // time: the fence keeps each quad's reads next to their use.
-    uint32_t dw[8];   // dS as bf16 pairs
-    // The visibility test (keys of this lane's row as tile offsets [lo, hi), compared
-    // without branches) is compiled only into the variant for tiles that need it.
+    // S = partial 0 + partial 1 and dP = partial 2 + partial 3 are formed by the four
+    // waves of the group a quad each (C-tile elements 4 wq .. 4 wq + 3): this wave reads
+    // quad wq of the four partials, turns it into dS, and writes it as bf16 into quad wq
+    // of its own slot (which no other wave reads); after a barrier every wave reads the
+    // four quads of dS back as its MFMA operand.  The visibility test (keys of this
+    // lane's row as tile offsets [lo, hi), compared without branches) is compiled only
+    // into the variant for tiles that need it.
     auto grads = [&](auto masked_c) {
       constexpr bool MASKED = decltype(masked_c)::value;
       const int lo = (wl >= 0 ? qpos - wl - kpos0 : -BN) - 4 * half;
       const int hi = min(nrows, qpos - kpos0 + 1) - 4 * half;
+      const int q = wq;
+      const float4 a0 = xch_quad(xch, q, lane), a1 = xch_quad(xch + 1024, q, lane);
+      const float4 b0 = xch_quad(xch + 2048, q, lane), b1 = xch_quad(xch + 3072, q, lane);
+      const float st[4] = {a0.x + a1.x, a0.y + a1.y, a0.z + a1.z, a0.w + a1.w};
+      const float dpt[4] = {b0.x + b1.x, b0.y + b1.y, b0.z + b1.z, b0.w + b1.w};
+      float dsq[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 a0 = xch_quad(xch, q, lane), a1 = xch_quad(xch + 1024, q, lane);
-        const float4 b0 = xch_quad(xch + 2048, q, lane), b1 = xch_quad(xch + 3072, q, lane);
-        const float st[4] = {a0.x + a1.x, a0.y + a1.y, a0.z + a1.z, a0.w + a1.w};
-        const float dpt[4] = {b0.x + b1.x, b0.y + b1.y, b0.z + b1.z, b0.w + b1.w};
-        float dsq[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float p = fast_exp2(fmaf(st[e], sf, -lse2));
-          if (MASKED) {
-            const int r = 8 * q + e;   // c_row(4 q + e, half) - 4 half
-            p = (r >= lo) & (r < hi) ? p : 0.f;
-          }
-          dsq[e] = p * (dpt[e] - Dq);
+      for (int e = 0; e < 4; ++e) {
+        float p = fast_exp2(fmaf(st[e], sf, -lse2));
+        if (MASKED) {
+          const int r = 8 * q + e;   // c_row(4 q + e, half) - 4 half
+          p = (r >= lo) & (r < hi) ? p : 0.f;
         }
-        dw[2 * q] = pack2(dsq[0], dsq[1]);
-        dw[2 * q + 1] = pack2(dsq[2], dsq[3]);
-        asm volatile("" ::: "memory");
+        dsq[e] = p * (dpt[e] - Dq);
       }
+      *reinterpret_cast<uint2 *>(xch + wq * 1024 + q * 256 + lane * 4) =
+          make_uint2(pack2(dsq[0], dsq[1]), pack2(dsq[2], dsq[3]));
     };
     if (need_mask)
       grads(std::true_type{});
     else
       grads(std::false_type{});
-    const bf16x8 d0 = words8(dw), d1 = words8(dw + 4);
+    __syncthreads();
+    uint2 dd[4];   // quad w of slot w: dS of elements 4w .. 4w+3
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      dd[w] = *reinterpret_cast<const uint2 *>(xch + w * 1024 + w * 256 + lane * 4);
+    const bf16x8 d0 = __builtin_bit_cast(bf16x8, make_uint4(dd[0].x, dd[0].y, dd[1].x, dd[1].y));
+    const bf16x8 d1 = __builtin_bit_cast(bf16x8, make_uint4(dd[2].x, dd[2].y, dd[3].x, dd[3].y));
     // dQᵀ += Kᵀ dSᵀ over this wave's quarter of the head dim.
 #pragma unroll
     for (int db = 0; db < NDQ; ++db) {
