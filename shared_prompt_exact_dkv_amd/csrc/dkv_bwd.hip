@@ -803,6 +803,9 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
   seek();
 
   const int tl = lane / G, jl = lane - tl * G;   // this lane's row of the LSE / D fetch
+  // ceil(2^24 / G): r * g_recip >> 24 is r / G exactly for r < 64 and G <= 128 (the
+  // rounding error r * (g_recip * G - 2^24) stays below 2^24 / G).
+  const uint32_t g_recip = __builtin_amdgcn_readfirstlane(((1u << 24) + (uint32_t)G - 1) / (uint32_t)G);
   const int qld_b = (int)(qld * 2);
   const int head0_b = g * G * HD * 2;
   // Wave 0 fetches LSE rows, wave 1 D rows.
@@ -824,7 +827,7 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
       // the row and chunk this lane fetches into the step's swizzled Q / dO tiles
       const int slot = (k * 4 + wave) * 64 + lane;
       const int r = slot / CPR;
-      const int tr_ = r / G;
+      const int tr_ = (int)(((uint32_t)r * g_recip) >> 24);   // r / G (r < 64, G <= 128)
       int t = ft + tr_, j = fj + (r - tr_ * G);
       if (j >= G) {
         j -= G;
