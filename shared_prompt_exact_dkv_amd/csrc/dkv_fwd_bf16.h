@@ -135,14 +135,16 @@ __global__ __launch_bounds__(256, WPE) void fwd_bf16_kernel(FwdArgs a) {
     const bool need_mask = (nrows < BN) || (kpos0 + BN - 1 > qmin) ||
                            (wl >= 0 && kpos0 < qmax - wl);
     if (need_mask) {
+      // Visible keys of this lane's row as tile offsets [lo, hi): inside the tile,
+      // causal, and inside the window; compared per element without branches.
+      const int lo = (wl >= 0 ? qpos - wl - kpos0 : -BN) - 4 * half;
+      const int hi = min(nrows, qpos - kpos0 + 1) - 4 * half;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          int kk = kb * 32 + c_row(v, half);
-          int kp = kpos0 + kk;
-          bool vis = (kk < nrows) && (kp <= qpos) && (wl < 0 || kp >= qpos - wl);
-          if (!vis) s[kb][v] = -INFINITY;
+          const int r = kb * 32 + 8 * (v >> 2) + (v & 3);   // kb * 32 + c_row(v, half) - 4 half
+          s[kb][v] = (r >= lo) & (r < hi) ? s[kb][v] : -INFINITY;
         }
     }
 
