@@ -563,7 +563,7 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
   if (s.T > 0) {
     float *Dneg = reinterpret_cast<float *>(wsb + pl.d_off);
     float *lsn = reinterpret_cast<float *>(wsb + pl.l2_off);
-    const bool fused_pre = dq_fuses_pre(s.dtype, s.d);
+    const bool fused_pre = s.dtype == DKV_BF16;   // the bf16 dQ kernels form -D, -LSE/scale
     if (!fused_pre) {
       e = timed(kKPre, stream, [&] {
         return launch_bwd_pre(s.dtype, s.d, io.o, io.dout, io.lse, Dneg, lsn, s.T, s.Hq, s.scale,

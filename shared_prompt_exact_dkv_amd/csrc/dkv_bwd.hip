@@ -1022,11 +1022,7 @@ static hipError_t pre_t(const void *o, const void *dout, const float *lse, float
 hipError_t launch_bwd_pre(int dtype, int hd, const void *o, const void *dout, const float *lse,
                           float *Dneg, float *lsn, long T, int Hq, float scale, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (dtype == 0) {
-    if (hd == 64) return pre_t<bf16, 64>(o, dout, lse, Dneg, lsn, T, Hq, scale, s);
-    if (hd == 128) return pre_t<bf16, 128>(o, dout, lse, Dneg, lsn, T, Hq, scale, s);
-    if (hd == 512) return pre_t<bf16, 512>(o, dout, lse, Dneg, lsn, T, Hq, scale, s);
-  } else {
+  if (dtype == 1) {   // fp32 only: the bf16 dQ kernels form these terms themselves
     if (hd == 64) return pre_t<float, 64>(o, dout, lse, Dneg, lsn, T, Hq, scale, s);
     if (hd == 128) return pre_t<float, 128>(o, dout, lse, Dneg, lsn, T, Hq, scale, s);
   }

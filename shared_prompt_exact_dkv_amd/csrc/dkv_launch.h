@@ -52,7 +52,8 @@ hipError_t launch_fwd_d512(const FwdArgs &a, int n_items, hipStream_t s);
 // lsn[h][t] = -LSE[h][t] / scale, the row's log-sum-exp in units of the raw dot product
 // <q, k>, negated.  The key-parallel bf16 kernels start their score and dP accumulators
 // from these two, so p = exp2(scale * log2(e) * acc) and dS = p * acc' need no per-element
-// subtraction.
+// subtraction.  This launch serves the fp32 path (dtype 1); in bf16 the dQ kernel writes
+// both for its rows (BwdQArgs::Dneg_out / lsn_out).
 hipError_t launch_bwd_pre(int dtype, int head_dim, const void *o, const void *dout,
                           const float *lse, float *Dneg, float *lsn, long T, int Hq, float scale,
                           hipStream_t s);
@@ -77,8 +78,6 @@ struct BwdQArgs {
   float scale;
 };
 hipError_t launch_bwd_dq(int dtype, int head_dim, const BwdQArgs &a, int n_items, hipStream_t s);
-// Whether launch_bwd_dq forms the preprocess terms itself (so no launch_bwd_pre).
-inline bool dq_fuses_pre(int dtype, int head_dim) { (void)head_dim; return dtype == 0; }
 hipError_t launch_bwd_dq_d512(const BwdQArgs &a, int n_items, hipStream_t s);
 
 // Work item of the key-parallel dK/dV kernel: one key tile of one region of one kv
