@@ -24,6 +24,9 @@ CASES = [
     (97, [120, 33], 4, 2, 128, 0, "bf16", False),
     (150, [100, 60], 8, 1, 128, 127, "fp32", False),
     (5, [3, 2, 1], 1, 1, 64, -1, "bf16", False),
+    # query heads per kv head that do not divide the 32-row steps / 128-row tiles
+    (61, [70, 131, 5], 6, 2, 128, -1, "bf16", False),
+    (45, [90, 17], 10, 2, 64, 30, "bf16", False),
     # head dim 512 (the hybrid-layer workload's GQA 4:1 included)
     (70, [45, 100], 8, 2, 512, -1, "bf16", False),
     (40, [70, 9], 16, 4, 512, -1, "bf16", True),
