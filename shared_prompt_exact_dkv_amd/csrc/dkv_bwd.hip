@@ -7,7 +7,8 @@
 // Kernels (each bf16 kernel has an fp32 counterpart for the 1e-5 parity workload;
 // head dim 512 is in dkv_d512.hip):
 //   bwd_pre   D = rowsum(dO * O) in fp32 (the auxiliary preprocessing launch), stored
-//             negated, and the LSE in units of the raw dot product, -LSE / scale
+//             negated, and the LSE in units of the raw dot product, -LSE / scale;
+//             the fp32 path only: the bf16 dQ kernel forms both for its rows
 //   bwd_dq    query-parallel: a workgroup keeps 128 query rows in registers and
 //             walks the shared-prompt key tiles, then its own sequence's tiles,
 //             exactly like the forward; dQ is written once, no atomics.

@@ -67,7 +67,7 @@ hipError_t launch_cast(int dtype, const float *src, void *dst, long n, hipStream
 
 struct BwdQArgs {
   const void *q, *k_ctx, *v_ctx, *k_own, *v_own, *dout;
-  const float *lse, *Dneg;     // Dneg = -rowsum(dO * O) (from the preprocess kernel)
+  const float *lse, *Dneg;     // Dneg = -rowsum(dO * O) (fp32: from the preprocess kernel)
   // bf16 (no preprocess launch): the dQ kernel forms D from O and dO itself and writes
   // -D and -LSE / scale of its rows here, for the dK/dV kernel.
   const void *o;
@@ -93,8 +93,8 @@ struct KVItem {
 
 struct BwdKVArgs {
   const void *q, *dout, *k_ctx, *v_ctx, *k_own, *v_own;
-  const float *lse, *Dneg;     // Dneg = -rowsum(dO * O) (from the preprocess kernel)
-  const float *lsn;            // -LSE / scale (from the preprocess kernel)
+  const float *lse, *Dneg;     // Dneg = -rowsum(dO * O) (written by the dQ kernel, or by
+  const float *lsn;            // the preprocess kernel in fp32); lsn = -LSE / scale
   const int32_t *cu;           // device prefix sums of the query sequences
   void *dk_own, *dv_own;       // direct outputs of own-region keys
   float *acc_dk, *acc_dv;      // fp32 accumulators: ctx-region keys, and own keys if own_to_acc
