@@ -8,18 +8,20 @@
 //
 //   forward  128 query rows per workgroup of 8 waves (two per SIMD); the two waves of
 //            a pair share 32 rows and each holds Q and O for one half of the head dim.
-//            Waves 0-3 run half a tile ahead of waves 4-7 (which share their SIMDs).  Each computes the
-//            partial scores Sᵀ over its half, the pair adds the two partials through
-//            LDS (both in the same order, so both see identical scores), and each
-//            accumulates its half of O.
+//            Each computes the partial scores Sᵀ over its half, the pair adds the two
+//            partials through LDS (both in the same order, so both see identical
+//            scores), and each accumulates its half of O.  Waves 0-3 run half a tile
+//            ahead of waves 4-7, which share their SIMDs.
 //   dQ       64 query rows per workgroup of 8 waves, two groups of four with 32 rows
 //            each.  In a group, waves 0 / 1 form partial Sᵀ = K Qᵀ over the two
 //            halves of the head dim (holding Q), waves 2 / 3 partial dPᵀ = V dOᵀ
-//            (holding dO).  After one exchange every wave has both tiles, forms dSᵀ
-//            and accumulates dQ for one quarter of the head dim.
+//            (holding dO).  After one exchange each wave forms dSᵀ for a quarter of the
+//            tile, and after a second every wave reads the whole dSᵀ and accumulates dQ
+//            for one quarter of the head dim.
 //   dK/dV    64 keys per workgroup of 8 waves, two groups of four with 32 keys each,
 //            the same arrangement: in a group, waves 0 / 1 hold K halves and form
-//            partial S, waves 2 / 3 hold V halves and form partial dP; each wave
+//            partial S, waves 2 / 3 hold V halves and form partial dP; P and dS are
+//            formed a quarter of the tile per wave and shared, and each wave
 //            accumulates dK and dV for one quarter of the head dim.
 // Every kernel runs two waves per SIMD, and the two groups (pairs) of a workgroup
 // share each staged tile.  Tiles are staged by LDS DMA into swizzled dense rows (one
