@@ -82,6 +82,37 @@ def test_dualkv_backward_matches_oracle(P, lens, Hq, Hkv, d, wl, dtype, scaled):
         check(k, g[k], ref[k], dtype)
 
 
+def _random_cases(n, seed):
+    """Seeded random shapes over the supported space: prompt length (0 allowed),
+    response lengths (0 and 1 allowed), grouped-query ratio, head dim, window."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        d = int(rng.choice([64, 128, 512]))
+        hkv = int(rng.choice([1, 2, 4]))
+        g = int(rng.choice([1, 2, 3, 4, 6, 8] if d < 512 else [1, 2, 3, 4]))
+        P = int(rng.choice([0, int(rng.integers(1, 200))]))
+        N = int(rng.integers(1, 5))
+        lens = [int(x) for x in rng.integers(0, 160, size=N)]
+        if sum(lens) == 0:
+            lens[0] = int(rng.integers(1, 160))
+        wl = int(rng.choice([-1, -1, int(rng.integers(0, 150))]))
+        cases.append((P, lens, hkv * g, hkv, d, wl))
+    return cases
+
+
+@pytest.mark.parametrize("P,lens,Hq,Hkv,d,wl", _random_cases(12, 2026))
+def test_random_shapes_match_oracle(P, lens, Hq, Hkv, d, wl):
+    x, t, ref, g, fwd = _run(P, lens, Hq, Hkv, d, wl, "bf16", False, seed=7 + P)
+    o_p, lse_p, o_r, lse_r = fwd
+    check("o_r", o_r, ref["o_r"], "bf16")
+    for k in GRADS:
+        if g[k] is None:
+            assert ref[k].size == 0, k
+            continue
+        check(k, g[k], ref[k], "bf16")
+
+
 def test_accumulator_order_is_free():
     # Call 2 first (clearing) then Call 1 (finalizing) gives the same dK_P / dV_P.
     P, lens, Hq, Hkv, d, dtype = 96, [50, 70, 20], 8, 2, 128, "bf16"
