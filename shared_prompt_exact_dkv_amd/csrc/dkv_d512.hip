@@ -454,7 +454,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
         }
         dsq[e] = p * (dpt[e] - Dq);
       }
-      *reinterpret_cast<uint2 *>(xch + wq * 1024 + q * 256 + lane * 4) =
+      // 8 bytes per lane, packed (consecutive lanes on consecutive banks)
+      *reinterpret_cast<uint2 *>(xch + wq * 1024 + q * 256 + lane * 2) =
           make_uint2(pack2(dsq[0], dsq[1]), pack2(dsq[2], dsq[3]));
     };
     if (need_mask)
@@ -465,7 +466,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
     uint2 dd[4];   // quad w of slot w: dS of elements 4w .. 4w+3
 #pragma unroll
     for (int w = 0; w < 4; ++w)
-      dd[w] = *reinterpret_cast<const uint2 *>(xch + w * 1024 + w * 256 + lane * 4);
+      dd[w] = *reinterpret_cast<const uint2 *>(xch + w * 1024 + w * 256 + lane * 2);
     const bf16x8 d0 = __builtin_bit_cast(bf16x8, make_uint4(dd[0].x, dd[0].y, dd[1].x, dd[1].y));
     const bf16x8 d1 = __builtin_bit_cast(bf16x8, make_uint4(dd[2].x, dd[2].y, dd[3].x, dd[3].y));
     // dQᵀ += Kᵀ dSᵀ over this wave's quarter of the head dim.
