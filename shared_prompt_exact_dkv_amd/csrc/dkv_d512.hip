@@ -605,6 +605,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
 
   const int qld_b = (int)(qld * 2);
   const int head0_b = g * G * HD * 2;
+  const int r4 = 4 % G;                                  // head step of 4 flattened rows
+  const int step4 = (4 / G) * qld_b + r4 * (HD * 2);     // their byte step before a wrap
   // Waves 0-3 fetch the step's Q rows, waves 4-7 its dO rows: row r of the step (a
   // flattened (token, head) row) fills 1 KB block r, written by wave r % 4.
   const bf16 *xsrc = reinterpret_cast<const bf16 *>(grp ? a.dout : a.q);
@@ -629,9 +631,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
     for (int k = 0; k < RPW; ++k) {
       const int r = k * 4 + wq;
       dma16(rx, l0 + k * 4096, roff + ((lane ^ Swz<HD>::swz(r)) << 4));
-      j += 4;
-      roff += 4 * HD * 2;
-      while (j >= G) {
+      // 4 rows on: q4 tokens and r4 heads, plus one token when the head index wraps
+      j += r4;
+      roff += step4;
+      if (j >= G) {
         j -= G;
         roff += qld_b - G * HD * 2;
       }
