@@ -54,9 +54,10 @@ def log(args, *a):
         print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_algo_work(w, lens, pairs):
-    """Algorithmic work per kernel class for one step: (amount, unit, bound)."""
-    d, Hq, Hkv, P = w.d, w.Hq, w.Hkv, w.P
+def kernel_algo_work(w, P, lens, pairs):
+    """Algorithmic work per kernel class for one step: (amount, unit, bound).  P is the
+    number of prompt rows (all groups' prompts)."""
+    d, Hq, Hkv = w.d, w.Hq, w.Hkv
     T = P + sum(lens)                   # query rows over both calls
     eb = 2 if w.dtype == "bf16" else 4
     return {
@@ -107,17 +108,28 @@ def main():
         sys.exit(1)
     dev = "cuda:0"
     w = workloads.WORKLOADS[args.workload]
-    lens = w.resp_lens()
-    N, P, Hq, Hkv, d, wl = w.N, w.P, w.Hq, w.Hkv, w.d, w.window_left
+    Hq, Hkv, d, wl = w.Hq, w.Hkv, w.d, w.window_left
     tdt = workloads.torch_dtype(w.dtype)
     log(args, "workload", w)
 
-    x = workloads.make_inputs(P, lens, Hq, Hkv, d, w.dtype, seed=w.seed, scaled=w.scaled,
-                              device=dev)
+    # Prompt groups [(P_j, response lengths)]: one group unless the workload packs
+    # several prompts into the micro-batch (then every call gets the group arrays).
+    shapes = w.group_shapes()
+    gkw = {}
+    if w.groups > 1:
+        _, x = workloads.make_group_inputs(shapes, Hq, Hkv, d, w.dtype, seed=w.seed,
+                                           scaled=w.scaled, device=dev)
+        cu_p_host = [int(c) for c in x.pop("ctx_cu")]
+        gkw = dict(ctx_cu_host=cu_p_host, group_seq_cu_host=[int(c) for c in x.pop("seq_cu")])
+    else:
+        x = workloads.make_inputs(shapes[0][0], shapes[0][1], Hq, Hkv, d, w.dtype, seed=w.seed,
+                                  scaled=w.scaled, device=dev)
+        cu_p_host = [0, shapes[0][0]]
+    lens = [r for _, ls in shapes for r in ls]
+    N, P = len(lens), cu_p_host[-1]
     x = {k: (v.to(tdt).contiguous() if k != "cu" else v) for k, v in x.items()}
     cu_host = [int(c) for c in x["cu"]]
     cu = x["cu"].to(dev)
-    cu_p_host = [0, P]
     cu_p = torch.tensor(cu_p_host, dtype=torch.int32, device=dev)
     T = cu_host[-1]
 
@@ -134,7 +146,7 @@ def main():
     dv_p = torch.empty_like(x["v_p"])
     acc = torch.empty((2, P, Hkv, d), dtype=torch.float32, device=dev)
     wsz = max(dkv.dkv_workspace_size(c, x["q_r"], x["k_r"], cu, cu_host=cu_host, ctx_len=P,
-                                     window_left=wl) for c in (1, 3, 4 if args.split else 3))
+                                     window_left=wl, **gkw) for c in (1, 3, 4 if args.split else 3))
     wsz = max(wsz, max(dkv.dkv_workspace_size(c, x["q_p"], x["k_p"], cu_p, cu_host=cu_p_host,
                                               window_left=wl) for c in (0, 2)))
     ws = torch.empty(max(wsz, 256), dtype=torch.uint8, device=dev)
@@ -145,14 +157,14 @@ def main():
         dkv.dkv_ctx_fwd(x["q_p"], x["k_p"], x["v_p"], cu_p, cu_host=cu_p_host, window_left=wl,
                         out=o_p, lse=lse_p, workspace=ws)
         dkv.dkv_fwd(x["q_r"], x["k_p"], x["v_p"], x["k_r"], x["v_r"], cu, cu_host=cu_host,
-                    window_left=wl, out=o_r, lse=lse_r, workspace=ws)
+                    window_left=wl, out=o_r, lse=lse_r, workspace=ws, **gkw)
         dkv.dkv_ctx_bwd(x["q_p"], x["k_p"], x["v_p"], o_p, lse_p, x["do_p"], cu_p,
                         cu_host=cu_p_host, window_left=wl, dq=dq_p, acc_dk=acc[0],
                         acc_dv=acc[1], acc_flags=dkv.DKV_ACC_ZERO, workspace=ws)
         dkv.dkv_bwd(x["q_r"], x["k_p"], x["v_p"], x["k_r"], x["v_r"], o_r, lse_r, x["do_r"], cu,
                     acc_dk_p=acc[0], acc_dv_p=acc[1], acc_flags=bwd_flags,
                     cu_host=cu_host, window_left=wl, dq_r=dq_r, dk_r=dk_r, dv_r=dv_r,
-                    dk_p=dk_p, dv_p=dv_p, workspace=ws)
+                    dk_p=dk_p, dv_p=dv_p, workspace=ws, **gkw)
 
     def timed(step, k):
         torch.cuda.synchronize()
@@ -173,7 +185,8 @@ def main():
     _lib.lib().dkv_timing_reset()
     log(args, "dualkv ms/step %.3f" % ms, ktimes)
 
-    pairs = accounting.pairs_dualkv(P, lens, wl)
+    pairs = sum(accounting.pairs_dualkv(Pj, ls, wl) for Pj, ls in shapes)
+    pairs_nc = sum(accounting.pairs_ncopy(Pj, ls, wl) for Pj, ls in shapes)
     flops = accounting.useful_flops(pairs, Hq, d)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
@@ -183,7 +196,7 @@ def main():
     bwd_ms = sum(v[0] for k, v in ktimes.items() if k != "attn_fwd") / args.steps
 
     # Roofline of the dominant kernel class.
-    algo = kernel_algo_work(w, lens, pairs)
+    algo = kernel_algo_work(w, P, lens, pairs)
     dom = max(ktimes, key=lambda k: ktimes[k][0]) if ktimes else None
     roof = None
     if dom is not None:
@@ -207,13 +220,17 @@ def main():
     # N-copy comparator: the same library's causal kernel over N sequences [P, R_i].
     ncopy_ms = None
     if not args.no_ncopy:
-        qn = torch.cat([t for i in range(N) for t in (x["q_p"], x["q_r"][cu_host[i]:cu_host[i + 1]])])
-        kn = torch.cat([t for i in range(N) for t in (x["k_p"], x["k_r"][cu_host[i]:cu_host[i + 1]])])
-        vn = torch.cat([t for i in range(N) for t in (x["v_p"], x["v_r"][cu_host[i]:cu_host[i + 1]])])
-        don = torch.cat([t for i in range(N) for t in (x["do_p"], x["do_r"][cu_host[i]:cu_host[i + 1]])])
+        # copy i: its group's prompt rows, then its own response rows
+        grp = [j for j, (_, ls) in enumerate(shapes) for _ in ls]
+        copy = lambda n, i: (x[n + "_p"][cu_p_host[grp[i]]:cu_p_host[grp[i] + 1]],
+                             x[n + "_r"][cu_host[i]:cu_host[i + 1]])
+        qn = torch.cat([t for i in range(N) for t in copy("q", i)])
+        kn = torch.cat([t for i in range(N) for t in copy("k", i)])
+        vn = torch.cat([t for i in range(N) for t in copy("v", i)])
+        don = torch.cat([t for i in range(N) for t in copy("do", i)])
         cun_host = [0]
-        for r in lens:
-            cun_host.append(cun_host[-1] + P + r)
+        for i, r in enumerate(lens):
+            cun_host.append(cun_host[-1] + shapes[grp[i]][0] + r)
         cun = torch.tensor(cun_host, dtype=torch.int32, device=dev)
         on = torch.empty_like(qn)
         lsen = torch.empty((Hq, cun_host[-1]), dtype=torch.float32, device=dev)
@@ -243,10 +260,11 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        S0 = P + lens[0]
+        P0 = shapes[0][0]
+        S0 = P0 + lens[0]
         G = Hq // Hkv
         ng = min(2, Hkv)
-        xs = workloads.make_inputs(P, [lens[0]], ng * G, ng, d, w.dtype, seed=w.seed + 100,
+        xs = workloads.make_inputs(P0, [lens[0]], ng * G, ng, d, w.dtype, seed=w.seed + 100,
                                    scaled=w.scaled)
         q0, k0, v0 = oracle.copy_of(xs, 0)
         do0 = torch.cat([xs["do_p"], xs["do_r"]]).double().numpy()
@@ -254,8 +272,7 @@ def main():
         oracle.seq_fwd(q0, k0, v0, window_left=wl)
         oracle.seq_bwd(q0, k0, v0, do0, window_left=wl)
         cpu_s = time.perf_counter() - t0
-        full_pairs = accounting.pairs_ncopy(P, lens, wl)
-        full_s = cpu_s * full_pairs / accounting.causal_pairs(S0, wl) * Hkv / ng
+        full_s = cpu_s * pairs_nc / accounting.causal_pairs(S0, wl) * Hkv / ng
         cpu = {"value": round(flops / full_s / 1e12, 6), "unit": "TFLOP/s",
                "cores": oracle.num_threads(), "kind": "oracle",
                "sample": "N-copy fwd+bwd (eq. 2, fp64) of sequence 1 (%d tokens) for %d of %d "
@@ -289,14 +306,16 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "P": P, "N": N,
+        "config": {"workload": w.name,
+                   "P": P if w.groups == 1 else [Pj for Pj, _ in shapes], "N": N,
+                   "groups": w.groups,
                    "R": w.R if w.R is not None else "U%s" % (list(w.R_range),),
                    "Hq": Hq, "Hkv": Hkv, "d": d, "window_left": wl,
                    "prompt_grad_sum": "split" if args.split else "atomic",
                    "parallelism": "single-gpu"},
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
         "speedup_vs_ncopy": round(speedup, 3) if speedup else None,
-        "ideal_speedup": round(accounting.ideal_speedup(P, lens, wl), 3),
+        "ideal_speedup": round(pairs_nc / pairs, 3),
         "ncopy_ms_per_step": round(ncopy_ms, 4) if ncopy_ms else None,
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),

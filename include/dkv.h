@@ -110,6 +110,24 @@ typedef struct {
        must hold the same values, is read by the kernels. */
     const int32_t *cu_seqlens_host;
     const int32_t *cu_seqlens_dev;
+    /* Prompt groups (dkv_fwd / dkv_bwd only; must be 0 for dkv_ctx_*).  A micro-batch
+       may hold the responses of several prompts, each group with its own shared
+       context K/V and its own sequences (§2.2 "Data pipeline": groups are processed
+       independently, each with its own context KV and cu_seqlens).
+         0: one group -- every sequence shares the ctx_len prompt rows.
+         G >= 1: group j's prompt is rows ctx_cu_host[j] .. ctx_cu_host[j+1]-1 of
+           k_p / v_p (and of acc_dk_p / acc_dv_p, dk_p / dv_p), and it is shared by
+           sequences group_seq_cu_host[j] .. group_seq_cu_host[j+1]-1 of cu_seqlens.
+           Both arrays are host int32 [G + 1], start at 0 and do not decrease;
+           ctx_cu_host[G] == ctx_len and group_seq_cu_host[G] == num_seqs.  Empty
+           prompts and groups without sequences are allowed.  A response row r of a
+           sequence of group j sits at logical position (ctx_cu_host[j+1] -
+           ctx_cu_host[j]) + r and sees only its own group's prompt.  The Call-1 term
+           of every group is the plain varlen dkv_ctx_* call with cu_seqlens =
+           ctx_cu_host. */
+    int32_t num_groups;
+    const int32_t *ctx_cu_host;
+    const int32_t *group_seq_cu_host;
 } dkv_params;
 
 /* Bytes of device workspace the given call needs for these parameters (0 means

@@ -244,6 +244,28 @@ def ncopy_reference(x: dict, *, do_copies=None, scale=None, window_left=-1, kvh=
     return res
 
 
+def grouped_reference(xs, *, do_copies=None, scale=None, window_left=-1, kvh=None,
+                      backward=True) -> dict:
+    """Expected outputs for a micro-batch of several prompt groups, packed group after
+    group (prompt rows of group 1, 2, ...; response rows of group 1, 2, ...).
+
+    Each group is its own instance of the method -- its own prompt, shared by its own
+    responses only ("Data pipeline" of §2.2: groups are processed independently, each
+    with its own context KV and cu_seqlens) -- so each is ncopy_reference() of that
+    group's inputs ``xs[j]`` (``do_copies[j]`` its per-copy prompt gradients), and the
+    results are concatenated in the packed order.  A group without responses still
+    has its prompt rows: they are the one sequence [P, 0] (eq. (3) alone).
+    """
+    parts = []
+    for j, x in enumerate(xs):
+        if len(x["cu"]) == 1:
+            x = dict(x, cu=np.zeros(2, dtype=np.int32))
+        parts.append(ncopy_reference(x, do_copies=None if do_copies is None else do_copies[j],
+                                     scale=scale, window_left=window_left, kvh=kvh,
+                                     backward=backward))
+    return {key: np.concatenate([r[key] for r in parts], 0) for key in parts[0]}
+
+
 def rows_fwd(k, v, rows, q_rows, *, scale=None, window_left=-1, kvh=None):
     """Eq. (2) at selected positions ``rows`` of one sequence whose keys / values are
     ``k`` / ``v`` [S, Hkv, d]; ``q_rows`` [n, Hq, d] are those rows' queries.

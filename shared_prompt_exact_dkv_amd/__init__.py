@@ -33,14 +33,23 @@ def _host_cu(cu_seqlens, cu_host):
     return [int(c) for c in cu_seqlens.cpu().tolist()]
 
 
-def _params(q, k, cu_seqlens, cu_host, ctx_len, window_left, softmax_scale):
+def _params(q, k, cu_seqlens, cu_host, ctx_len, window_left, softmax_scale, groups=None):
     if q.dtype not in _DT:
         raise TypeError("unsupported dtype %s" % q.dtype)
     cu = _host_cu(cu_seqlens, cu_host)
+    ctx_cu, seq_cu = groups if groups is not None else (None, None)
     return L.make_params(num_seqs=len(cu) - 1, ctx_len=ctx_len, num_heads_q=q.shape[1],
                          num_heads_kv=k.shape[1], head_dim=q.shape[2],
                          window_left=window_left, softmax_scale=softmax_scale,
-                         dtype=_DT[q.dtype], cu_host=cu, cu_dev=_p(cu_seqlens))
+                         dtype=_DT[q.dtype], cu_host=cu, cu_dev=_p(cu_seqlens),
+                         ctx_cu_host=ctx_cu, group_seq_cu_host=seq_cu)
+
+
+def _groups(ctx_cu_host, group_seq_cu_host):
+    """Prompt groups of a micro-batch: (ctx_cu_host, group_seq_cu_host) or None."""
+    if ctx_cu_host is None and group_seq_cu_host is None:
+        return None
+    return [int(c) for c in ctx_cu_host], [int(c) for c in group_seq_cu_host]
 
 
 def _stream(device):
@@ -59,8 +68,10 @@ def _ws(params, call, device, workspace):
 
 
 def dkv_workspace_size(call: int, q, k, cu_seqlens, *, cu_host=None, ctx_len=0,
-                       window_left=-1, softmax_scale=0.0) -> int:
-    p, keep = _params(q, k, cu_seqlens, cu_host, ctx_len, window_left, softmax_scale)
+                       window_left=-1, softmax_scale=0.0, ctx_cu_host=None,
+                       group_seq_cu_host=None) -> int:
+    p, keep = _params(q, k, cu_seqlens, cu_host, ctx_len, window_left, softmax_scale,
+                      _groups(ctx_cu_host, group_seq_cu_host))
     return int(L.lib().dkv_workspace_size(p, call))
 
 
@@ -79,11 +90,14 @@ def dkv_ctx_fwd(q, k, v, cu_seqlens, *, cu_host=None, window_left=-1, softmax_sc
 
 
 def dkv_fwd(q_resp, k_p, v_p, k_r, v_r, cu_seqlens, *, cu_host=None, window_left=-1,
-            softmax_scale=0.0, out=None, lse=None, workspace=None):
+            softmax_scale=0.0, out=None, lse=None, workspace=None, ctx_cu_host=None,
+            group_seq_cu_host=None):
     """Shared-prompt attention of the responses (Call 2, eq. (4)); P = k_p.shape[0].
+    With prompt groups, group j's prompt is rows ctx_cu_host[j]..ctx_cu_host[j+1] of
+    k_p/v_p, shared by sequences group_seq_cu_host[j]..group_seq_cu_host[j+1].
     -> (o_r [T_R,Hq,d], lse_r [Hq,T_R] fp32)."""
     p, keep = _params(q_resp, k_r, cu_seqlens, cu_host, k_p.shape[0], window_left,
-                      softmax_scale)
+                      softmax_scale, _groups(ctx_cu_host, group_seq_cu_host))
     T, Hq, _ = q_resp.shape
     o = torch.empty_like(q_resp) if out is None else out
     lse = torch.empty((Hq, T), dtype=torch.float32, device=q_resp.device) if lse is None else lse
@@ -114,14 +128,15 @@ def dkv_ctx_bwd(q, k, v, o, lse, dout, cu_seqlens, *, cu_host=None, window_left=
 
 def dkv_bwd(q_resp, k_p, v_p, k_r, v_r, o_r, lse_r, dout_r, cu_seqlens, *, acc_dk_p, acc_dv_p,
             acc_flags=0, cu_host=None, window_left=-1, softmax_scale=0.0, dq_r=None, dk_r=None,
-            dv_r=None, dk_p=None, dv_p=None, workspace=None):
+            dv_r=None, dk_p=None, dv_p=None, workspace=None, ctx_cu_host=None,
+            group_seq_cu_host=None):
     """Backward of Call 2 (eq. (4), §3.2).  Adds the responses' prompt-key gradients
     into acc_dk_p/acc_dv_p (fp32 [P,Hkv,d]); with DKV_ACC_FINALIZE also casts the
     accumulator into dk_p/dv_p; with DKV_ACC_SPLIT the terms reach the accumulator
     through per-chunk slices and a fixed-order sum instead of atomic adds.
-    -> (dq_r, dk_r, dv_r, dk_p, dv_p)."""
+    Prompt groups as in dkv_fwd.  -> (dq_r, dk_r, dv_r, dk_p, dv_p)."""
     p, keep = _params(q_resp, k_r, cu_seqlens, cu_host, k_p.shape[0], window_left,
-                      softmax_scale)
+                      softmax_scale, _groups(ctx_cu_host, group_seq_cu_host))
     dq_r = torch.empty_like(q_resp) if dq_r is None else dq_r
     dk_r = torch.empty_like(k_r) if dk_r is None else dk_r
     dv_r = torch.empty_like(v_r) if dv_r is None else dv_r
@@ -147,32 +162,37 @@ def dkv_cast_acc(acc_dk, acc_dv, dk, dv):
     return dk, dv
 
 
+def _prompt_cu(P, ctx_cu_host, device):
+    cu_p_host = [0, P] if ctx_cu_host is None else [int(c) for c in ctx_cu_host]
+    return torch.tensor(cu_p_host, dtype=torch.int32, device=device), cu_p_host
+
+
 def dualkv_forward(q_p, k_p, v_p, q_r, k_r, v_r, cu_seqlens, *, cu_host=None, window_left=-1,
-                   softmax_scale=0.0):
-    """The two calls of the forward: Call 1 over the prompt, Call 2 over the responses.
-    -> (o_p, lse_p, o_r, lse_r)."""
-    P = q_p.shape[0]
-    cu_p = torch.tensor([0, P], dtype=torch.int32, device=q_p.device)
-    o_p, lse_p = dkv_ctx_fwd(q_p, k_p, v_p, cu_p, cu_host=[0, P], window_left=window_left,
+                   softmax_scale=0.0, ctx_cu_host=None, group_seq_cu_host=None):
+    """The two calls of the forward: Call 1 over the prompt(s), Call 2 over the
+    responses.  With prompt groups (see dkv_fwd), Call 1 is varlen causal attention
+    over the prompts.  -> (o_p, lse_p, o_r, lse_r)."""
+    cu_p, cu_p_host = _prompt_cu(q_p.shape[0], ctx_cu_host, q_p.device)
+    o_p, lse_p = dkv_ctx_fwd(q_p, k_p, v_p, cu_p, cu_host=cu_p_host, window_left=window_left,
                              softmax_scale=softmax_scale)
     o_r, lse_r = dkv_fwd(q_r, k_p, v_p, k_r, v_r, cu_seqlens, cu_host=cu_host,
-                         window_left=window_left, softmax_scale=softmax_scale)
+                         window_left=window_left, softmax_scale=softmax_scale,
+                         ctx_cu_host=ctx_cu_host, group_seq_cu_host=group_seq_cu_host)
     return o_p, lse_p, o_r, lse_r
 
 
 def dualkv_backward(q_p, k_p, v_p, q_r, k_r, v_r, o_p, lse_p, o_r, lse_r, do_p, do_r,
                     cu_seqlens, *, cu_host=None, window_left=-1, softmax_scale=0.0,
-                    acc=None, split=False):
+                    acc=None, split=False, ctx_cu_host=None, group_seq_cu_host=None):
     """The two calls of the backward sharing one fp32 accumulator for dK_P/dV_P
     (eq. (6)): Call 1 clears it and adds the prompt self-attention term, Call 2 adds
     the N responses' terms and casts once (split=True: through per-chunk slices and a
     fixed-order sum, bitwise reproducible).  -> dict of dq_p, dk_p, dv_p, dq_r, dk_r,
     dv_r."""
-    P = q_p.shape[0]
     if acc is None:
         acc = torch.empty((2,) + tuple(k_p.shape), dtype=torch.float32, device=k_p.device)
-    cu_p = torch.tensor([0, P], dtype=torch.int32, device=q_p.device)
-    dq_p, _, _ = dkv_ctx_bwd(q_p, k_p, v_p, o_p, lse_p, do_p, cu_p, cu_host=[0, P],
+    cu_p, cu_p_host = _prompt_cu(q_p.shape[0], ctx_cu_host, q_p.device)
+    dq_p, _, _ = dkv_ctx_bwd(q_p, k_p, v_p, o_p, lse_p, do_p, cu_p, cu_host=cu_p_host,
                              window_left=window_left, softmax_scale=softmax_scale,
                              acc_dk=acc[0], acc_dv=acc[1], acc_flags=DKV_ACC_ZERO)
     dq_r, dk_r, dv_r, dk_p, dv_p = dkv_bwd(q_r, k_p, v_p, k_r, v_r, o_r, lse_r, do_r,
@@ -180,5 +200,7 @@ def dualkv_backward(q_p, k_p, v_p, q_r, k_r, v_r, o_p, lse_p, o_r, lse_r, do_p, 
                                            acc_flags=DKV_ACC_FINALIZE | (DKV_ACC_SPLIT if split else 0),
                                            cu_host=cu_host,
                                            window_left=window_left,
-                                           softmax_scale=softmax_scale)
+                                           softmax_scale=softmax_scale,
+                                           ctx_cu_host=ctx_cu_host,
+                                           group_seq_cu_host=group_seq_cu_host)
     return {"dq_p": dq_p, "dk_p": dk_p, "dv_p": dv_p, "dq_r": dq_r, "dk_r": dk_r, "dv_r": dv_r}

@@ -32,6 +32,9 @@ class DkvParams(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32)),
         ("cu_seqlens_dev", ctypes.c_void_p),
+        ("num_groups", ctypes.c_int32),
+        ("ctx_cu_host", ctypes.POINTER(ctypes.c_int32)),
+        ("group_seq_cu_host", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -105,14 +108,26 @@ def timing_read() -> dict:
     return {names[i].decode(): (ms[i], cnt[i]) for i in range(k)}
 
 
+def _i32(vals):
+    if vals is None:
+        return None, None
+    arr = (ctypes.c_int32 * len(vals))(*[int(c) for c in vals])
+    return arr, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+
+
 def make_params(*, num_seqs, ctx_len, num_heads_q, num_heads_kv, head_dim, window_left=-1,
-                softmax_scale=0.0, dtype=DKV_BF16, cu_host=None, cu_dev=0):
+                softmax_scale=0.0, dtype=DKV_BF16, cu_host=None, cu_dev=0, ctx_cu_host=None,
+                group_seq_cu_host=None):
     """Build a DkvParams.  Returns (params, keepalive); keep the second alive while the
-    params are in use (it owns the host copy of cu_seqlens)."""
-    n = num_seqs + 1
-    arr = (ctypes.c_int32 * n)(*[int(c) for c in cu_host]) if cu_host is not None else None
+    params are in use (it owns the host arrays: cu_seqlens and the prompt groups)."""
+    arr, ptr = _i32(cu_host)
+    carr, cptr = _i32(ctx_cu_host)
+    garr, gptr = _i32(group_seq_cu_host)
+    ng = 0
+    if ctx_cu_host is not None or group_seq_cu_host is not None:
+        if ctx_cu_host is None or group_seq_cu_host is None:
+            raise ValueError("ctx_cu_host and group_seq_cu_host go together")
+        ng = len(ctx_cu_host) - 1
     p = DkvParams(num_seqs, ctx_len, num_heads_q, num_heads_kv, head_dim, window_left,
-                  float(softmax_scale), dtype,
-                  ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)) if arr is not None else None,
-                  cu_dev)
-    return p, arr
+                  float(softmax_scale), dtype, ptr, cu_dev, ng, cptr, gptr)
+    return p, (arr, carr, garr)

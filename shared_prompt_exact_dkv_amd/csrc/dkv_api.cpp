@@ -50,6 +50,11 @@ struct Shape {
   float scale;
   long T;                   // cu[N]
   std::vector<int> cu;
+  // Prompt groups: group j's prompt is rows [gctx[j], gctx[j + 1]) of the prompt
+  // tensors (and of the shared accumulator) and serves sequences [gseq[j], gseq[j + 1]).
+  // A call without groups has one, of all P rows and all N sequences.
+  std::vector<int> gctx, gseq;
+  std::vector<int> sctx0, sP;  // per sequence: first row and length of its prompt
   int bm_tok;               // query tokens per forward workgroup
   int bm_tok_dq;            // query tokens per dQ workgroup
   int kv_tile;              // keys per dK/dV workgroup
@@ -98,12 +103,51 @@ dkv_status check_params(const dkv_params *p, bool is_ctx, Shape *s) {
   if (s->T > 0 && !p->cu_seqlens_dev)
     return fail(DKV_ERR_INVALID_ARG, "cu_seqlens_dev is NULL");
   {
+    const int ng = p->num_groups;
+    if (ng < 0) return fail(DKV_ERR_INVALID_ARG, "num_groups < 0 (%d)", ng);
+    if (is_ctx && ng != 0)
+      return fail(DKV_ERR_INVALID_ARG, "num_groups must be 0 for dkv_ctx_* calls (got %d)", ng);
+    if (ng == 0) {
+      s->gctx = {0, s->P};
+      s->gseq = {0, s->N};
+    } else {
+      if (!p->ctx_cu_host || !p->group_seq_cu_host)
+        return fail(DKV_ERR_INVALID_ARG, "num_groups = %d needs ctx_cu_host and group_seq_cu_host", ng);
+      s->gctx.assign(p->ctx_cu_host, p->ctx_cu_host + ng + 1);
+      s->gseq.assign(p->group_seq_cu_host, p->group_seq_cu_host + ng + 1);
+      if (s->gctx[0] != 0 || s->gseq[0] != 0)
+        return fail(DKV_ERR_INVALID_ARG, "ctx_cu_host[0] and group_seq_cu_host[0] must be 0");
+      for (int j = 0; j < ng; ++j) {
+        if (s->gctx[j + 1] < s->gctx[j])
+          return fail(DKV_ERR_INVALID_ARG, "ctx_cu_host decreases at %d (%d -> %d)", j,
+                      s->gctx[j], s->gctx[j + 1]);
+        if (s->gseq[j + 1] < s->gseq[j])
+          return fail(DKV_ERR_INVALID_ARG, "group_seq_cu_host decreases at %d (%d -> %d)", j,
+                      s->gseq[j], s->gseq[j + 1]);
+      }
+      if (s->gctx[ng] != s->P)
+        return fail(DKV_ERR_INVALID_ARG, "ctx_cu_host[num_groups] = %d, ctx_len = %d",
+                    s->gctx[ng], s->P);
+      if (s->gseq[ng] != s->N)
+        return fail(DKV_ERR_INVALID_ARG, "group_seq_cu_host[num_groups] = %d, num_seqs = %d",
+                    s->gseq[ng], s->N);
+    }
+    s->sctx0.assign(s->N, 0);
+    s->sP.assign(s->N, 0);
+    for (size_t j = 0; j + 1 < s->gseq.size(); ++j)
+      for (int i = s->gseq[j]; i < s->gseq[j + 1]; ++i) {
+        s->sctx0[i] = s->gctx[j];
+        s->sP[i] = s->gctx[j + 1] - s->gctx[j];
+      }
+  }
+  {
     // A window at least as long as the longest logical position sees every earlier
     // key: it is the global causal mask, and is run as one (the kernels form key + wl
     // and (key + wl) * G in 32-bit arithmetic).
-    long max_len = 0;
-    for (int i = 0; i < s->N; ++i) max_len = std::max<long>(max_len, s->cu[i + 1] - s->cu[i]);
-    if (s->wl >= 0 && (long)s->wl >= (long)s->P + max_len) s->wl = -1;
+    long max_pos = 0;
+    for (int i = 0; i < s->N; ++i)
+      max_pos = std::max<long>(max_pos, (long)s->sP[i] + s->cu[i + 1] - s->cu[i]);
+    if (s->wl >= 0 && (long)s->wl >= max_pos) s->wl = -1;
   }
   if (s->dtype == DKV_BF16) {
     // The bf16 backward addresses a sequence's query rows, and the LSE / D rows, with
@@ -183,10 +227,10 @@ std::vector<Item> interleave_xcds(std::vector<std::vector<Item>> &lists) {
   return out;
 }
 
-long q_item_work(const Shape &s, int bm_tok, int tile, int seqlen, int BN) {
+long q_item_work(const Shape &s, int bm_tok, int tile, int seqlen, int P, int BN) {
   long t0 = (long)tile * bm_tok;
   long t1 = std::min<long>(seqlen, t0 + bm_tok);
-  long qmin = s.P + t0, qmax = s.P + t1 - 1;
+  long qmin = P + t0, qmax = P + t1 - 1;
   long lo = (s.wl >= 0) ? std::max<long>(0, qmin - s.wl) : 0;
   long keys = qmax + 1 - lo;
   return (keys + BN - 1) / BN;
@@ -202,7 +246,7 @@ std::vector<QItem> build_q_items(const Shape &s, int bm_tok, int BN) {
     if (nt == 0) continue;
     Group gr{0, i, {}};
     for (int m = 0; m < nt; ++m) {
-      long w = q_item_work(s, bm_tok, m, len, BN);
+      long w = q_item_work(s, bm_tok, m, len, s.sP[i], BN);
       gr.recs.push_back({w, m});
       gr.work += w;
     }
@@ -221,7 +265,8 @@ std::vector<QItem> build_q_items(const Shape &s, int bm_tok, int BN) {
     const int start = s.cu[gr.seq], len = s.cu[gr.seq + 1] - start;
     for (int g = 0; g < s.Hkv; ++g)
       for (size_t r = 0; r < gr.recs.size(); ++r)
-        lists[hx.xcd(g, (int)(by_tile ? r : gi))].push_back({g, gr.recs[r].tile, start, len});
+        lists[hx.xcd(g, (int)(by_tile ? r : gi))].push_back(
+            {g, gr.recs[r].tile, start, len, s.sctx0[gr.seq], s.sP[gr.seq], {0, 0}});
   }
   return interleave_xcds(lists);
 }
@@ -389,7 +434,6 @@ dkv_status run_fwd(const Shape &s, const void *q, const void *kc, const void *vc
   a.Hkv = s.Hkv;
   a.G = s.G;
   a.bm_tok = s.bm_tok;
-  a.ctx_len = s.P;
   a.window_left = s.wl;
   a.lse_ld = (int)s.T;
   a.scale = s.scale;
@@ -429,12 +473,12 @@ int split_slices(const Shape &s) {
   return (std::max(1, s.N) + cs - 1) / cs;
 }
 
-long kv_rows_visible(const Shape &s, bool ctx, int key_start, int nk, int len) {
+long kv_rows_visible(const Shape &s, bool ctx, int key_start, int nk, int len, int P) {
   long lo, hi;
   if (ctx) {
     lo = 0;
     hi = len;
-    if (s.wl >= 0) hi = std::min<long>(len, (long)key_start + nk - 1 + s.wl - s.P + 1);
+    if (s.wl >= 0) hi = std::min<long>(len, (long)key_start + nk - 1 + s.wl - P + 1);
   } else {
     lo = key_start;
     hi = len;
@@ -443,45 +487,74 @@ long kv_rows_visible(const Shape &s, bool ctx, int key_start, int nk, int len) {
   return std::max<long>(0, hi - lo);
 }
 
+// The chunks of sequences [lo, hi) of prompt group pg whose prompt-key tiles are
+// separate work items.  Split mode takes the global chunks of split_chunk() sequences
+// (chunk c fills slice c), clipped to the group; a chunk holding no sequence of the
+// group becomes the empty range [c * chunk, c * chunk), whose items store zeros, so that
+// every slice element of the group's prompt rows is written once.  Otherwise chunks of
+// ctx_chunk() sequences from the group's first one.
+std::vector<std::pair<int, int>> ctx_chunks(const Shape &s, int pg, bool split) {
+  std::vector<std::pair<int, int>> out;
+  const int q0 = s.gseq[pg], q1 = s.gseq[pg + 1];
+  if (split) {
+    const int cs = split_chunk(s), n = split_slices(s);
+    for (int c = 0; c < n; ++c) {
+      int lo = std::max(q0, c * cs), hi = std::min(q1, (c + 1) * cs);
+      if (hi <= lo) lo = hi = c * cs;
+      out.push_back({lo, hi});
+    }
+  } else {
+    const int cs = ctx_chunk(s);
+    for (int lo = q0; lo < q1; lo += cs) out.push_back({lo, std::min(q1, lo + cs)});
+  }
+  return out;
+}
+
 std::vector<KVItem> build_kv_items(const Shape &s, bool with_ctx, bool split) {
-  // One group per (chunk of sequences): the prompt key tiles that add this chunk's
-  // terms to the shared accumulator, and the chunk's own response key tiles.  All of
-  // them stream the chunk's query rows.
-  struct Rec { long work; int region, key_start, lo, hi; };
+  // Per prompt group and chunk of its sequences: the prompt key tiles that add the
+  // chunk's terms to the shared accumulator, and the chunk's own response key tiles.
+  // All of them stream the chunk's query rows.
+  struct Rec { long work; int region, key_start, lo, hi, c0, Pg; };
   struct Group { long work; std::vector<Rec> recs; };
-  const int cs = (with_ctx && s.P > 0) ? (split ? split_chunk(s) : ctx_chunk(s)) : 1;
   std::vector<Group> groups;
-  for (int lo = 0; lo < s.N; lo += cs) {
-    const int hi = std::min(s.N, lo + cs);
-    Group gr{0, {}};
-    if (with_ctx && s.P > 0) {
-      for (int k0 = 0; k0 < s.P; k0 += s.kv_tile) {
-        int nk = std::min(s.kv_tile, s.P - k0);
-        long w = 0;
-        for (int i = lo; i < hi; ++i) w += kv_rows_visible(s, true, k0, nk, s.cu[i + 1] - s.cu[i]);
-        // Split mode keeps tiles no row of the chunk sees: they store the zeros of
-        // their slice, so every slice element is written.
-        if (w > 0 || split) gr.recs.push_back({w, kRegionCtx, k0, lo, hi});
+  auto add = [&](Group &x) {
+    if (x.recs.empty()) return;
+    for (const Rec &r : x.recs) x.work += r.work;
+    std::stable_sort(x.recs.begin(), x.recs.end(),
+                     [](const Rec &a, const Rec &b) { return a.work > b.work; });
+    groups.push_back(std::move(x));
+  };
+  for (int pg = 0; pg + 1 < (int)s.gseq.size(); ++pg) {
+    const int c0 = s.gctx[pg], Pg = s.gctx[pg + 1] - c0;
+    const bool ctx_here = with_ctx && Pg > 0;
+    std::vector<std::pair<int, int>> chunks = ctx_chunks(s, pg, split && ctx_here);
+    for (const auto &ch : chunks) {
+      const int lo = ch.first, hi = ch.second;
+      // The chunk's prompt-key tiles and its own-key tiles form separate groups: the
+      // prompt-key tiles all walk the same rows (every row of the chunk), so a group of
+      // them shares its row blocks in L2.
+      Group ctxg{0, {}}, owng{0, {}};
+      if (ctx_here) {
+        for (int k0 = 0; k0 < Pg; k0 += s.kv_tile) {
+          int nk = std::min(s.kv_tile, Pg - k0);
+          long w = 0;
+          for (int i = lo; i < hi; ++i)
+            w += kv_rows_visible(s, true, k0, nk, s.cu[i + 1] - s.cu[i], Pg);
+          // Split mode keeps tiles no row of the chunk sees: they store the zeros of
+          // their slice, so every slice element is written.
+          if (w > 0 || split) ctxg.recs.push_back({w, kRegionCtx, k0, lo, hi, c0, Pg});
+        }
       }
-    }
-    for (int i = lo; i < hi; ++i) {
-      int len = s.cu[i + 1] - s.cu[i];
-      for (int k0 = 0; k0 < len; k0 += s.kv_tile) {
-        int nk = std::min(s.kv_tile, len - k0);
-        gr.recs.push_back({kv_rows_visible(s, false, k0, nk, len), kRegionOwn, k0, i, i + 1});
+      for (int i = lo; i < hi; ++i) {
+        int len = s.cu[i + 1] - s.cu[i];
+        for (int k0 = 0; k0 < len; k0 += s.kv_tile) {
+          int nk = std::min(s.kv_tile, len - k0);
+          owng.recs.push_back(
+              {kv_rows_visible(s, false, k0, nk, len, Pg), kRegionOwn, k0, i, i + 1, c0, Pg});
+        }
       }
-    }
-    // The chunk's prompt-key tiles and its own-key tiles form separate groups: the
-    // prompt-key tiles all walk the same rows (every row of the chunk), so a group of
-    // them shares its row blocks in L2.
-    Group ctxg{0, {}}, owng{0, {}};
-    for (const Rec &r : gr.recs) (r.region == kRegionCtx ? ctxg : owng).recs.push_back(r);
-    for (Group *x : {&ctxg, &owng}) {
-      if (x->recs.empty()) continue;
-      for (const Rec &r : x->recs) x->work += r.work;
-      std::stable_sort(x->recs.begin(), x->recs.end(),
-                       [](const Rec &a, const Rec &b) { return a.work > b.work; });
-      groups.push_back(std::move(*x));
+      add(ctxg);
+      add(owng);
     }
   }
   std::stable_sort(groups.begin(), groups.end(),
@@ -494,7 +567,7 @@ std::vector<KVItem> build_kv_items(const Shape &s, bool with_ctx, bool split) {
       for (size_t r = 0; r < groups[gi].recs.size(); ++r) {
         const Rec &x = groups[gi].recs[r];
         lists[hx.xcd(g, (int)(by_tile ? r : gi))].push_back(
-            {g, x.region, x.key_start, x.lo, x.hi, {0, 0, 0}});
+            {g, x.region, x.key_start, x.lo, x.hi, x.c0, x.Pg, 0});
       }
   return interleave_xcds(lists);
 }
@@ -513,10 +586,12 @@ BwdPlan plan_bwd(const Shape &s, bool with_ctx, bool split) {
     int len = s.cu[i + 1] - s.cu[i];
     nkv += (size_t)((len + s.kv_tile - 1) / s.kv_tile);
   }
-  if (with_ctx && s.P > 0 && s.N > 0) {
-    int cs = split ? split_chunk(s) : ctx_chunk(s);
-    nkv += (size_t)((s.P + s.kv_tile - 1) / s.kv_tile) * ((s.N + cs - 1) / cs);
-  }
+  if (with_ctx)
+    for (int pg = 0; pg + 1 < (int)s.gseq.size(); ++pg) {
+      const int Pg = s.gctx[pg + 1] - s.gctx[pg];
+      if (Pg > 0)
+        nkv += (size_t)((Pg + s.kv_tile - 1) / s.kv_tile) * ctx_chunks(s, pg, split).size();
+    }
   pl.n_kv = nkv * s.Hkv;   // upper bound (empty windowed items are dropped)
   pl.d_off = 0;
   pl.l2_off = align_up((size_t)s.Hq * s.T * sizeof(float));
@@ -584,7 +659,7 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
       qa.lsn_out = lsn;
     }
     qa.items = reinterpret_cast<const QItem *>(wsb + pl.q_off);
-    qa.Hq = s.Hq; qa.Hkv = s.Hkv; qa.G = s.G; qa.bm_tok = s.bm_tok_dq; qa.ctx_len = s.P;
+    qa.Hq = s.Hq; qa.Hkv = s.Hkv; qa.G = s.G; qa.bm_tok = s.bm_tok_dq;
     qa.window_left = s.wl; qa.lse_ld = (int)s.T; qa.scale = s.scale;
     e = timed(kKDq, stream, [&] { return launch_bwd_dq(s.dtype, s.d, qa, (int)qi.size(), stream); });
     if (e != hipSuccess) return hip_fail(e, "dq kernel launch");
@@ -593,7 +668,7 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
     ka.v_own = io.vo; ka.lse = io.lse; ka.Dneg = Dneg; ka.lsn = lsn; ka.cu = io.cu_dev;
     ka.dk_own = io.dk_own; ka.dv_own = io.dv_own; ka.acc_dk = io.acc_dk; ka.acc_dv = io.acc_dv;
     ka.items = reinterpret_cast<const KVItem *>(wsb + pl.kv_off);
-    ka.Hq = s.Hq; ka.Hkv = s.Hkv; ka.G = s.G; ka.ctx_len = s.P; ka.window_left = s.wl;
+    ka.Hq = s.Hq; ka.Hkv = s.Hkv; ka.G = s.G; ka.window_left = s.wl;
     ka.lse_ld = (int)s.T; ka.own_to_acc = io.own_to_acc ? 1 : 0;
     ka.scale = s.scale;
     float *slices = reinterpret_cast<float *>(wsb + pl.split_off);

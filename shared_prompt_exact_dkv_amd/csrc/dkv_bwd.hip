@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_f32_kernel(BwdQArgs a) {
   const bool row_valid = tok < nt;
   if (!row_valid) tok = nt - 1;
   const int h = g * a.G + hj;
-  const int P = a.ctx_len, wl = a.window_left;
+  const int P = it.ctx_len, wl = a.window_left;
   const int qpos = P + t0 + tok;
   const int qmin = P + t0, qmax = P + t0 + nt - 1;
   const long qld = (long)a.Hq * HD;
@@ -171,8 +171,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_f32_kernel(BwdQArgs a) {
   const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
   const int n_tiles = n_ctx + n_own;
 
-  const T *kc_base = reinterpret_cast<const T *>(a.k_ctx) + (long)g * HD;
-  const T *vc_base = reinterpret_cast<const T *>(a.v_ctx) + (long)g * HD;
+  const T *kc_base = reinterpret_cast<const T *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
+  const T *vc_base = reinterpret_cast<const T *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
   const T *ko_base = reinterpret_cast<const T *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
   const T *vo_base = reinterpret_cast<const T *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
 
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
   const bool row_valid = tok < nt;
   if (!row_valid) tok = nt - 1;
   const int h = g * a.G + hj;
-  const int P = a.ctx_len, wl = a.window_left;
+  const int P = it.ctx_len, wl = a.window_left;
   const int qpos = P + t0 + tok;
   const int qmin = P + t0, qmax = P + t0 + nt - 1;
   const long qld = (long)a.Hq * HD;
@@ -336,8 +336,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
   const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
   const int n_tiles = n_ctx + n_own;
 
-  const bf16 *kc_base = reinterpret_cast<const bf16 *>(a.k_ctx) + (long)g * HD;
-  const bf16 *vc_base = reinterpret_cast<const bf16 *>(a.v_ctx) + (long)g * HD;
+  const bf16 *kc_base = reinterpret_cast<const bf16 *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
+  const bf16 *vc_base = reinterpret_cast<const bf16 *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
   const bf16 *ko_base = reinterpret_cast<const bf16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
   const bf16 *vo_base = reinterpret_cast<const bf16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
   const int kld_b = (int)(kld * 2);
@@ -479,11 +479,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdKVArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const KVItem it = a.items[blockIdx.x];
-  const int g = it.g, G = a.G, P = a.ctx_len, wl = a.window_left;
+  const int g = it.g, G = a.G, P = it.ctx_len, wl = a.window_left;
   const bool ctx = it.region == kRegionCtx;
   const long qld = (long)a.Hq * HD;
   const long kld = (long)a.Hkv * HD;
-  const int own0 = ctx ? 0 : sload_i32(a.cu, it.seq_lo);                  // row of the own sequence
+  const int own0 = ctx ? it.ctx_start : sload_i32(a.cu, it.seq_lo);                  // row of the own sequence
   const int nkeys = ctx ? P - it.key_start : sload_i32(a.cu, it.seq_lo + 1) - own0 - it.key_start;
   const int kbase = ctx ? 0 : P;                               // logical position offset
   const int nk_tile = min(BNW, nkeys);
@@ -700,11 +700,11 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const KVItem it = a.items[blockIdx.x];
-  const int g = it.g, G = a.G, P = a.ctx_len, wl = a.window_left;
+  const int g = it.g, G = a.G, P = it.ctx_len, wl = a.window_left;
   const bool ctx = it.region == kRegionCtx;
   const long qld = (long)a.Hq * HD;
   const long kld = (long)a.Hkv * HD;
-  const int own0 = ctx ? 0 : sload_i32(a.cu, it.seq_lo);
+  const int own0 = ctx ? it.ctx_start : sload_i32(a.cu, it.seq_lo);
   const int nkeys = ctx ? P - it.key_start : sload_i32(a.cu, it.seq_lo + 1) - own0 - it.key_start;
   const int kbase = ctx ? 0 : P;
   const int nk_tile = min(BNW, nkeys);

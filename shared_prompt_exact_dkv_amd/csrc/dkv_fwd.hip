@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
   const bool row_valid = tok < nt;
   if (!row_valid) tok = nt - 1;   // computes a duplicate of a valid row, never stored
   const int h = g * a.G + hj;
-  const int P = a.ctx_len, wl = a.window_left;
+  const int P = it.ctx_len, wl = a.window_left;
   const int qpos = P + t0 + tok;
   const int qmin = P + t0, qmax = P + t0 + nt - 1;
 
@@ -82,8 +82,8 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
   const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
   const int n_tiles = n_ctx + n_own;
 
-  const T *kc_base = reinterpret_cast<const T *>(a.k_ctx) + (long)g * HD;
-  const T *vc_base = reinterpret_cast<const T *>(a.v_ctx) + (long)g * HD;
+  const T *kc_base = reinterpret_cast<const T *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
+  const T *vc_base = reinterpret_cast<const T *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
   const T *ko_base = reinterpret_cast<const T *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
   const T *vo_base = reinterpret_cast<const T *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
 

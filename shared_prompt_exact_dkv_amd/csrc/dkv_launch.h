@@ -29,6 +29,11 @@ struct QItem {
   int32_t tile;       // query tile index within the sequence
   int32_t seq_start;  // first row of the sequence in the query / own-key tensors
   int32_t seq_len;    // rows of the sequence
+  // The sequence's shared prompt: its first row in the prompt key / value tensors and
+  // its length P (the logical offset of the sequence's own rows; 0 = no shared region).
+  int32_t ctx_start;
+  int32_t ctx_len;
+  int32_t pad[2];
 };
 
 struct FwdArgs {
@@ -37,7 +42,6 @@ struct FwdArgs {
   float *lse;
   const QItem *items;
   int Hq, Hkv, G, bm_tok;
-  int ctx_len;        // P: logical offset of the own region (0 = no shared region)
   int window_left;    // -1 global
   int lse_ld;         // tokens per LSE row
   float scale;        // softmax scale
@@ -74,21 +78,25 @@ struct BwdQArgs {
   float *Dneg_out, *lsn_out;
   void *dq;
   const QItem *items;
-  int Hq, Hkv, G, bm_tok, ctx_len, window_left, lse_ld;
+  int Hq, Hkv, G, bm_tok, window_left, lse_ld;
   float scale;
 };
 hipError_t launch_bwd_dq(int dtype, int head_dim, const BwdQArgs &a, int n_items, hipStream_t s);
 hipError_t launch_bwd_dq_d512(const BwdQArgs &a, int n_items, hipStream_t s);
 
 // Work item of the key-parallel dK/dV kernel: one key tile of one region of one kv
-// head, against the query rows of sequences [seq_lo, seq_hi).
+// head, against the query rows of sequences [seq_lo, seq_hi) (all of one prompt group).
 enum { kRegionCtx = 0, kRegionOwn = 1 };
 struct KVItem {
   int32_t g;
   int32_t region;     // kRegionCtx: keys of the shared prompt; kRegionOwn: of seq_lo
   int32_t key_start;  // first key of the tile within its region
   int32_t seq_lo, seq_hi;
-  int32_t pad[3];
+  // The shared prompt of sequences [seq_lo, seq_hi): its first row in the prompt key /
+  // value tensors (and the accumulator) and its length P.
+  int32_t ctx_start;
+  int32_t ctx_len;
+  int32_t pad;
 };
 
 struct BwdKVArgs {
@@ -99,12 +107,13 @@ struct BwdKVArgs {
   void *dk_own, *dv_own;       // direct outputs of own-region keys
   float *acc_dk, *acc_dv;      // fp32 accumulators: ctx-region keys, and own keys if own_to_acc
   // Split mode (non-null split_dk): ctx-region items store their partial sums into
-  // slice seq_lo / split_chunk of [slices][P][Hkv][d] instead of adding atomically.
+  // slice seq_lo / split_chunk of [slices][prompt rows][Hkv][d] instead of adding
+  // atomically.
   float *split_dk, *split_dv;
-  long split_stride;           // elements per slice (P * Hkv * d)
+  long split_stride;           // elements per slice (prompt rows * Hkv * d)
   int split_chunk;             // sequences per ctx item
   const KVItem *items;
-  int Hq, Hkv, G, ctx_len, window_left, lse_ld;
+  int Hq, Hkv, G, window_left, lse_ld;
   int own_to_acc;
   float scale;
 };

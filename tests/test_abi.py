@@ -152,3 +152,38 @@ def test_offset_range_limits():
     f32, k3 = _params(num_seqs=1, ctx_len=16, num_heads_q=32, num_heads_kv=8,
                       cu_host=[0, longest + 2], dtype=L.DKV_FP32)
     assert lib.dkv_workspace_size(f32, L.DKV_CALL_FWD) != ctypes.c_size_t(-1).value
+
+
+@pytest.mark.parametrize("groups,frag", [
+    (([0, 10, 17], [0, 1, 2]), "ctx_cu_host[num_groups]"),     # prompts sum to 17, P = 16
+    (([0, 10, 16], [0, 1, 3]), "group_seq_cu_host[num_groups]"),
+    (([0, 10, 8, 16], [0, 1, 1, 2]), "ctx_cu_host decreases"),
+    (([0, 8, 16], [0, 2, 1, 2][:3]), "group_seq_cu_host decreases"),
+    (([1, 8, 16], [0, 1, 2]), "must be 0"),
+])
+def test_prompt_groups_are_validated(groups, frag):
+    p, keep = _params(ctx_cu_host=groups[0], group_seq_cu_host=groups[1])
+    st = L.lib().dkv_fwd(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None)
+    assert st == L.DKV_ERR_INVALID_ARG
+    assert frag in L.last_error()
+
+
+def test_prompt_groups_only_for_the_response_call():
+    p, keep = _params(ctx_len=0, ctx_cu_host=[0, 0], group_seq_cu_host=[0, 2])
+    st = L.lib().dkv_ctx_fwd(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None)
+    assert st == L.DKV_ERR_INVALID_ARG and "num_groups" in L.last_error()
+
+
+def test_prompt_groups_workspace_matches_one_group():
+    # Groups that span every sequence with one prompt plan the same work as no groups;
+    # splitting the prompt in two adds at most the second group's prompt-key tiles.
+    lib = L.lib()
+    p0, k0 = _params(num_seqs=3, cu_host=[0, 100, 300, 301], ctx_len=300)
+    p1, k1 = _params(num_seqs=3, cu_host=[0, 100, 300, 301], ctx_len=300,
+                     ctx_cu_host=[0, 300], group_seq_cu_host=[0, 3])
+    p2, k2 = _params(num_seqs=3, cu_host=[0, 100, 300, 301], ctx_len=300,
+                     ctx_cu_host=[0, 200, 300], group_seq_cu_host=[0, 2, 3])
+    for call in (L.DKV_CALL_FWD, L.DKV_CALL_BWD, L.DKV_CALL_BWD_SPLIT):
+        a, b, c = (lib.dkv_workspace_size(p, call) for p in (p0, p1, p2))
+        assert a == b, call
+        assert c != (1 << 64) - 1 and c > 0, call

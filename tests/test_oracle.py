@@ -334,3 +334,64 @@ def test_scatter_accumulates_across_calls():
     oracle.rows_bwd_scatter(k, v, ab, q[ab], do[ab], dk2, dv2)
     np.testing.assert_allclose(dk1, dk2, rtol=0, atol=1e-12)
     np.testing.assert_allclose(dv1, dv2, rtol=0, atol=1e-12)
+
+
+def _two_call_grouped(packed, wl, scale):
+    """Several prompt groups in one packed micro-batch, as one autograd graph: each
+    prompt's Call 1 (eq. 3) over its own rows, and each response's Call 2 (eq. 4)
+    over its own group's prompt rows then its own rows.  Prompt K/V rows are slices
+    of one leaf tensor, so autograd sums every call's gradient into the right rows."""
+    t = {n: torch.as_tensor(np.asarray(packed[n]), dtype=torch.float64).clone().requires_grad_(True)
+         for n in ("q_p", "k_p", "v_p", "q_r", "k_r", "v_r")}
+    cu = [int(c) for c in packed["cu"]]
+    ccu = [int(c) for c in packed["ctx_cu"]]
+    scu = [int(c) for c in packed["seq_cu"]]
+    Hq, Hkv = t["q_p"].shape[1], t["k_p"].shape[1]
+    kvh = [h // (Hq // Hkv) for h in range(Hq)]
+    o_p, lse_p, o_r, lse_r = [], [], [], []
+    for j in range(len(ccu) - 1):
+        c0, c1 = ccu[j], ccu[j + 1]
+        P = c1 - c0
+        ppos = torch.arange(P)
+        o, l = _attend(t["q_p"][c0:c1], t["k_p"][c0:c1], t["v_p"][c0:c1], ppos, ppos, scale,
+                       wl, kvh)
+        o_p.append(o)
+        lse_p.append(l)
+        for i in range(scu[j], scu[j + 1]):
+            a, b = cu[i], cu[i + 1]
+            kk = torch.cat([t["k_p"][c0:c1], t["k_r"][a:b]], 0)
+            vv = torch.cat([t["v_p"][c0:c1], t["v_r"][a:b]], 0)
+            o, l = _attend(t["q_r"][a:b], kk, vv, P + torch.arange(b - a),
+                           torch.arange(P + b - a), scale, wl, kvh)
+            o_r.append(o)
+            lse_r.append(l)
+    o_p, lse_p, o_r, lse_r = (torch.cat(z, 0) for z in (o_p, lse_p, o_r, lse_r))
+    loss = (o_p * torch.as_tensor(np.asarray(packed["do_p"]))).sum() + \
+        (o_r * torch.as_tensor(np.asarray(packed["do_r"]))).sum()
+    loss.backward()
+    out = {"o_p": o_p, "lse_p": lse_p, "o_r": o_r, "lse_r": lse_r}
+    out = {k: v.detach().numpy() for k, v in out.items()}
+    for n in ("q_p", "k_p", "v_p", "q_r", "k_r", "v_r"):
+        out["d" + n] = t[n].grad.numpy()
+    return out
+
+
+@pytest.mark.parametrize("wl", [-1, 3])
+def test_grouped_reference_matches_packed_two_call_autograd(wl):
+    # Three prompt groups, one of them without a prompt and one without responses:
+    # every response must see only its own group's prompt, and each prompt's K/V
+    # gradient must collect only its own group's terms.
+    groups = [(5, [3, 4]), (0, [6]), (7, [2, 0, 5]), (4, [])]
+    Hq, Hkv, d = 4, 2, 4
+    xs, packed = workloads.make_group_inputs(groups, Hq, Hkv, d, "fp32", seed=31)
+    ref = oracle.grouped_reference(xs, window_left=wl)
+    two = _two_call_grouped(packed, wl, 1.0 / math.sqrt(d))
+    for key in ("o_p", "lse_p", "o_r", "lse_r", "dq_p", "dk_p", "dv_p", "dq_r", "dk_r", "dv_r"):
+        np.testing.assert_allclose(ref[key], two[key], rtol=0, atol=1e-11, err_msg=key)
+    # Sharing one prompt across all groups would change the answer.
+    assert np.abs(ref["o_r"][:7] - oracle.ncopy_reference(
+        dict(xs[0], q_r=packed["q_r"][:7], k_r=packed["k_r"][:7], v_r=packed["v_r"][:7],
+             do_r=packed["do_r"][:7], cu=packed["cu"][:3]), window_left=wl, backward=False)["o_r"]).max() == 0
+    assert np.abs(ref["o_r"][7:13] - oracle.ncopy_reference(
+        dict(xs[0], q_r=packed["q_r"][7:13], k_r=packed["k_r"][7:13], v_r=packed["v_r"][7:13],
+             do_r=packed["do_r"][7:13], cu=workloads.cu_seqlens([6])), window_left=wl, backward=False)["o_r"]).max() > 1e-3

@@ -38,6 +38,8 @@ class Workload:
     window_left: int = -1       # -1 = global causal
     seed: int = 0
     scaled: bool = True         # values ~ N(0,1)/sqrt(d) (else N(0,1))
+    groups: int = 1             # prompt groups in the micro-batch, N responses each
+    P_range: Optional[tuple] = None   # (lo, hi) inclusive: per-group prompt lengths drawn
 
     def resp_lens(self) -> list:
         if self.R is not None:
@@ -45,6 +47,23 @@ class Workload:
         g = torch.Generator().manual_seed(10_000 + self.seed)
         lo, hi = self.R_range
         return torch.randint(lo, hi + 1, (self.N,), generator=g).tolist()
+
+    def group_shapes(self) -> list:
+        """[(P_j, response lengths of group j)] of the micro-batch's prompt groups."""
+        if self.groups == 1 and self.P_range is None:
+            return [(self.P, self.resp_lens())]
+        g = torch.Generator().manual_seed(30_000 + self.seed)
+        out = []
+        for _ in range(self.groups):
+            P = self.P if self.P_range is None else \
+                int(torch.randint(self.P_range[0], self.P_range[1] + 1, (1,), generator=g))
+            if self.R is not None:
+                lens = [self.R] * self.N
+            else:
+                lens = torch.randint(self.R_range[0], self.R_range[1] + 1, (self.N,),
+                                     generator=g).tolist()
+            out.append((P, lens))
+        return out
 
 
 # The five workloads (the d=512 "layer pair" is two layers: global and windowed).
@@ -63,6 +82,12 @@ WORKLOADS = {
                             Hkv=4, d=512, dtype="bf16", seed=5),
     "d512_swa": Workload("d512_swa", P=57344, N=8, R=8192, R_range=None, Hq=16, Hkv=4,
                          d=512, dtype="bf16", window_left=1023, seed=6),
+    # A GRPO micro-batch holding several prompts (§2.2 "Data pipeline"): 4 prompt
+    # groups of 8 responses, prompts U{2048..8192} and responses U{512..2048} tokens
+    # (the LongReason setting of §4.2 caps prompts at 8192 and responses at 2048).
+    "multi_group": Workload("multi_group", P=0, N=8, R=None, R_range=(512, 2048), Hq=32,
+                            Hkv=8, d=128, dtype="bf16", seed=7, groups=4,
+                            P_range=(2048, 8192)),
 }
 
 
@@ -115,6 +140,28 @@ def make_inputs(P: int, lens, Hq: int, Hkv: int, d: int, dtype: str = "fp32",
         out["do_p"] = _draw(g, (P, Hq, d), dtype, 1.0, keep)
         out["do_r"] = _draw(g, (T, Hq, d), dtype, 1.0, keep)
     return out
+
+
+def make_group_inputs(groups, Hq: int, Hkv: int, d: int, dtype: str = "fp32", seed: int = 0,
+                      scaled: bool = False, dout: bool = True, device: str = "cpu") -> tuple:
+    """A micro-batch of several prompt groups: ``groups`` is a list of (P_j, lens_j).
+
+    Group j's tensors are drawn by make_inputs with seed ``seed + j``.  Returns
+    (per-group input dicts, packed dict): the packed dict concatenates the groups'
+    prompt rows (q_p, k_p, v_p, do_p) and response rows (q_r, k_r, v_r, do_r) in group
+    order, with cu (int32 [N+1] over all responses), ctx_cu (prefix sums of the P_j)
+    and seq_cu (prefix sums of the groups' response counts).
+    """
+    xs = [make_inputs(P, lens, Hq, Hkv, d, dtype, seed=seed + j, scaled=scaled, dout=dout,
+                      device=device)
+          for j, (P, lens) in enumerate(groups)]
+    names = ["q_p", "k_p", "v_p", "q_r", "k_r", "v_r"] + (["do_p", "do_r"] if dout else [])
+    packed = {n: torch.cat([x[n] for x in xs], 0) for n in names}
+    all_lens = [int(r) for _, lens in groups for r in lens]
+    packed["cu"] = cu_seqlens(all_lens)
+    packed["ctx_cu"] = cu_seqlens([P for P, _ in groups])
+    packed["seq_cu"] = cu_seqlens([len(lens) for _, lens in groups])
+    return xs, packed
 
 
 def split_prompt_grad(do_p: torch.Tensor, N: int, seed: int) -> torch.Tensor:
