@@ -43,6 +43,12 @@ def parse():
                     help="sum the shared-prompt gradient through per-chunk slices and a "
                          "fixed-order reduction (DKV_ACC_SPLIT) instead of fp32 atomics")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--layout", action="store_true",
+                    help="time the layout conversions (dkv_layout: N-copy <-> single-prompt "
+                         "packing and first-token rows) on the workload's token layout "
+                         "instead of the attention step")
+    ap.add_argument("--hidden", type=int, default=4096,
+                    help="elements per token row for --layout (Qwen3-8B hidden size)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (torch), the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -91,6 +97,100 @@ def traffic_for(kernel, workload):
     return rec.get("bytes_per_launch")
 
 
+def layout_main(args):
+    """One step = the five layout conversions of one micro-batch: UNPACK and PACK of a
+    hidden-state tensor, UNPACK_BWD of its gradient, and the first-token GATHER and
+    SCATTER, each on rows of --hidden bf16 elements.  Algorithmic bytes per op: every
+    distinct input row read once plus every output row written once."""
+    import torch
+    import workloads
+    from shared_prompt_exact_dkv_amd import _lib
+    import shared_prompt_exact_dkv_amd as dkv
+
+    dev = "cuda:0"
+    w = workloads.WORKLOADS[args.workload]
+    shapes = w.group_shapes()
+    cu, ccu, scu = [0], [0], [0]
+    for Pj, ls in shapes:
+        ccu.append(ccu[-1] + Pj)
+        scu.append(scu[-1] + len(ls))
+        for r in ls:
+            cu.append(cu[-1] + r)
+    P, T, N = ccu[-1], cu[-1], len(cu) - 1
+    gkw = dict(ctx_cu_host=ccu, group_seq_cu_host=scu) if w.groups > 1 else {}
+    nrows = lambda op: dkv.layout_rows(op, cu, P, ccu if gkw else None, scu if gkw else None)
+    H, eb = args.hidden, 2
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    ops = [dkv.DKV_UNPACK, dkv.DKV_PACK, dkv.DKV_UNPACK_BWD, dkv.DKV_FIRST_TOKEN_GATHER,
+           dkv.DKV_FIRST_TOKEN_SCATTER]
+    names = {dkv.DKV_UNPACK: "unpack", dkv.DKV_PACK: "pack", dkv.DKV_UNPACK_BWD: "unpack_bwd",
+             dkv.DKV_FIRST_TOKEN_GATHER: "first_token_gather",
+             dkv.DKV_FIRST_TOKEN_SCATTER: "first_token_scatter"}
+    ncopy = nrows(dkv.DKV_UNPACK)[1]
+    # distinct input rows read + output rows written, per op
+    rows_moved = {dkv.DKV_UNPACK: (P + T) + ncopy, dkv.DKV_PACK: 2 * (P + T),
+                  dkv.DKV_UNPACK_BWD: ncopy + (P + T), dkv.DKV_FIRST_TOKEN_GATHER: 2 * T,
+                  dkv.DKV_FIRST_TOKEN_SCATTER: T + (P + T)}
+    bufs = {}
+    for op in ops:
+        ri, ro = nrows(op)
+        bufs[op] = (torch.randn((ri, H), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16),
+                    torch.empty((ro, H), dtype=torch.bfloat16, device=dev))
+    wsz = max(_lib.lib().dkv_layout_workspace_size(
+        _lib.make_params(num_seqs=N, ctx_len=P, num_heads_q=1, num_heads_kv=1, head_dim=64,
+                         cu_host=cu, **({"ctx_cu_host": ccu, "group_seq_cu_host": scu} if gkw else {}))[0], op)
+        for op in ops)
+    ws = torch.empty(max(wsz, 256), dtype=torch.uint8, device=dev)
+
+    def step():
+        for op in ops:
+            dkv.dkv_layout(op, bufs[op][0], cu, P, out=bufs[op][1], workspace=ws, **gkw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    _lib.lib().dkv_timing_reset()
+    _lib.lib().dkv_timing_enable(1)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    _lib.lib().dkv_timing_enable(0)
+    # per-op durations: one timed launch per op per step, in op order
+    per_op = {}
+    for op in ops:
+        _lib.lib().dkv_timing_reset()
+        _lib.lib().dkv_timing_enable(1)
+        for _ in range(args.steps):
+            dkv.dkv_layout(op, bufs[op][0], cu, P, out=bufs[op][1], workspace=ws, **gkw)
+        _lib.lib().dkv_timing_enable(0)
+        tot, n = _lib.timing_read()["layout"]
+        per_op[op] = tot / n
+    _lib.lib().dkv_timing_reset()
+    total_bytes = sum(rows_moved[op] * H * eb for op in ops)
+    gbs = total_bytes / (ms * 1e-3) / 1e9
+    dom = max(ops, key=lambda op: per_op[op])
+    dom_gbs = rows_moved[dom] * H * eb / (per_op[dom] * 1e-3) / 1e9
+    out = {
+        "metric": "DualKV layout conversions GB/s (% HBM peak)",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "P": P, "N": N, "T_R": T, "groups": len(shapes),
+                   "row_elems": H, "ops": [names[op] for op in ops]},
+        "pct_hbm_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "kernels": {names[op]: {"ms": round(per_op[op], 4),
+                                "GB/s": round(rows_moved[op] * H * eb / (per_op[op] * 1e-3) / 1e9, 1)}
+                    for op in ops},
+        "roofline": {"kernel": "layout:" + names[dom], "bound": "hbm", "achieved": round(dom_gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dom_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None, "avg_launch_ms": round(per_op[dom], 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -106,6 +206,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.layout:
+        return layout_main(args)
     dev = "cuda:0"
     w = workloads.WORKLOADS[args.workload]
     Hq, Hkv, d, wl = w.Hq, w.Hkv, w.d, w.window_left

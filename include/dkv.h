@@ -191,6 +191,51 @@ dkv_status dkv_cast_acc(const dkv_params *p, int32_t rows, const float *acc_dk,
                         const float *acc_dv, void *dk, void *dv, hipStream_t stream);
 
 /*
+ * Layout conversions of per-token rows between the two packings of a micro-batch
+ * (any per-token tensor: hidden states, Q/K/V, their gradients), so that every
+ * per-token operation of the model can run on the single-prompt packing (§2.2,
+ * App. A.3: all per-token operations process P + sum_i R_i tokens):
+ *   N-copy packing (§2.1, eq. (1)): for each sequence i in order, its prompt's rows
+ *     then its own R_i rows -- sum_i (P_g(i) + R_i) rows.
+ *   single-prompt packing (eq. (5)): every prompt once (group order, as ctx_cu_host
+ *     lays them out; one prompt of ctx_len rows without groups), then every response
+ *     (cu_seqlens order) -- ctx_len + T_R rows.
+ * Rows are row_elems elements of p->dtype (a multiple of 16 bytes); in/out are
+ * 16-byte aligned device buffers that must not overlap.  The head fields of p are
+ * not used.  Ops:
+ *   DKV_PACK        N-copy -> single-prompt.  A prompt row comes from its group's first
+ *                   copy (every copy holds the same prompt rows, App. A.2); a prompt
+ *                   whose group has no response is not in the N-copy packing and is
+ *                   written as zeros.
+ *   DKV_UNPACK      single-prompt -> N-copy: every copy receives its group's prompt.
+ *   DKV_UNPACK_BWD  the adjoint of DKV_UNPACK, for gradients: a prompt row receives
+ *                   the sum over its group's copies (App. A.5: the shared prompt
+ *                   collects every branch's gradient), accumulated in fp32 in sequence
+ *                   order and rounded once; response rows are copied.
+ *   DKV_FIRST_TOKEN_GATHER  out [T_R, row]: the hidden state that predicts each
+ *                   response token -- for token r > 0 of response i its row r - 1, for
+ *                   r = 0 the last row of its group's prompt (§2.3: the last prompt
+ *                   token predicts the first token of every response of its group);
+ *                   zeros for a first token whose prompt is empty.
+ *   DKV_FIRST_TOKEN_SCATTER  the adjoint of the gather, in [T_R, row] -> out
+ *                   [ctx_len + T_R, row]: the last row of each prompt receives the sum
+ *                   (fp32, sequence order, one rounding) of its responses' first-token
+ *                   gradients, a response row r the gradient of token r + 1, and every
+ *                   other row zero.
+ * Workspace (work lists) from dkv_layout_workspace_size(p, op).  Rows above 2^31 or
+ * rows of 2^31 / 16 vectors or more return DKV_ERR_UNSUPPORTED.
+ */
+typedef enum {
+    DKV_PACK = 0,
+    DKV_UNPACK = 1,
+    DKV_UNPACK_BWD = 2,
+    DKV_FIRST_TOKEN_GATHER = 3,
+    DKV_FIRST_TOKEN_SCATTER = 4
+} dkv_layout_op;
+size_t dkv_layout_workspace_size(const dkv_params *p, int op);
+dkv_status dkv_layout(const dkv_params *p, int op, int64_t row_elems, const void *in, void *out,
+                      void *ws, size_t ws_bytes, hipStream_t stream);
+/*
  * Per-kernel timing, a profiling aid.  While enabled, every kernel the library
  * launches is bracketed by two HIP events recorded on its own stream.
  * dkv_timing_read() waits for those events and reports, per kernel class, the

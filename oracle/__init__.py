@@ -312,3 +312,114 @@ def rows_bwd_scatter(k, v, rows, q_rows, dout_rows, dk, dv, *, scale=None, windo
             raise ValueError("oracle_bwd_scatter failed (%d)" % rc)
     return dq
 
+
+
+# ---------------------------------------------------------------------------
+# Layout conversions between the two packings (§2.1 eq. (1), §2.2 eq. (5), §2.3,
+# App. A.2 / A.3 / A.5).  ``groups`` is [(P_j, [R_i of group j])]; tensors are
+# [rows, ...] with any trailing shape.  The N-copy packing holds, sequence after
+# sequence, the sequence's prompt then its response; the single-prompt packing holds
+# every prompt once, in group order, then every response.
+
+
+def _split_packed(x, groups):
+    x = np.asarray(x)
+    prompts, resps, at = [], [], 0
+    for P, _ in groups:
+        prompts.append(x[at:at + P])
+        at += P
+    for _, lens in groups:
+        rs = []
+        for R in lens:
+            rs.append(x[at:at + R])
+            at += R
+        resps.append(rs)
+    assert at == x.shape[0]
+    return prompts, resps
+
+
+def _split_ncopy(x, groups):
+    x = np.asarray(x)
+    copies, at = [], 0
+    for P, lens in groups:
+        cs = []
+        for R in lens:
+            cs.append((x[at:at + P], x[at + P:at + P + R]))
+            at += P + R
+        copies.append(cs)
+    assert at == x.shape[0]
+    return copies
+
+
+def layout_pack(x_ncopy, groups):
+    """N-copy -> single-prompt packing: each prompt from its group's first copy (every
+    copy holds the same prompt rows, App. A.2); zeros for a prompt without copies."""
+    copies = _split_ncopy(x_ncopy, groups)
+    x = np.asarray(x_ncopy)
+    prompts = [cs[0][0] if cs else np.zeros((P,) + x.shape[1:], x.dtype)
+               for (P, _), cs in zip(groups, copies)]
+    resps = [r for cs in copies for _, r in cs]
+    return np.concatenate(prompts + resps, 0)
+
+
+def layout_unpack(x_packed, groups):
+    """Single-prompt -> N-copy packing: every sequence gets its group's prompt rows
+    followed by its own rows (eq. (1))."""
+    prompts, resps = _split_packed(x_packed, groups)
+    x = np.asarray(x_packed)
+    parts = [z for p, rs in zip(prompts, resps) for r in rs for z in (p, r)]
+    return np.concatenate(parts, 0) if parts else np.zeros((0,) + x.shape[1:], x.dtype)
+
+
+def layout_unpack_bwd(g_ncopy, groups):
+    """Gradient of layout_unpack: a prompt row collects the sum of its group's copies'
+    gradients (App. A.5), in float64; response rows are passed through."""
+    copies = _split_ncopy(g_ncopy, groups)
+    g = _f64(g_ncopy)
+    prompts = []
+    for (P, _), cs in zip(groups, copies):
+        acc = np.zeros((P,) + g.shape[1:])
+        for p, _ in cs:
+            acc += _f64(p)
+        prompts.append(acc)
+    resps = [_f64(r) for cs in copies for _, r in cs]
+    return np.concatenate(prompts + resps, 0)
+
+
+def first_token_gather(h_packed, groups):
+    """The hidden state that predicts each response token: for token r > 0 of a
+    response its row r - 1, for r = 0 the last row of its group's prompt (§2.3);
+    zeros when the prompt is empty.  [T_R, ...]."""
+    prompts, resps = _split_packed(h_packed, groups)
+    h = np.asarray(h_packed)
+    out = []
+    for p, rs in zip(prompts, resps):
+        for r in rs:
+            if r.shape[0] == 0:
+                continue
+            first = p[-1:] if p.shape[0] else np.zeros((1,) + h.shape[1:], h.dtype)
+            out += [first, r[:-1]]
+    return np.concatenate(out, 0) if out else np.zeros((0,) + h.shape[1:], h.dtype)
+
+
+def first_token_scatter(g_pred, groups):
+    """Gradient of first_token_gather, in float64: the last prompt row of a group gets
+    the sum of its responses' first-token gradients, response row r the gradient of
+    token r + 1, every other row zero.  [sum P_j + T_R, ...]."""
+    g = _f64(g_pred)
+    tail = g.shape[1:]
+    prompts, resps, at = [], [], 0
+    for P, lens in groups:
+        pg = np.zeros((P,) + tail)
+        for R in lens:
+            seg = g[at:at + R]
+            at += R
+            if R == 0:
+                resps.append(seg)
+                continue
+            if P > 0:
+                pg[P - 1] += seg[0]
+            resps.append(np.concatenate([seg[1:], np.zeros((1,) + tail)], 0))
+        prompts.append(pg)
+    assert at == g.shape[0]
+    return np.concatenate(prompts + resps, 0)

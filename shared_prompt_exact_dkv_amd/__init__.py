@@ -16,9 +16,13 @@ import torch
 
 from . import _lib as L
 from ._lib import DKV_ACC_FINALIZE, DKV_ACC_SPLIT, DKV_ACC_ZERO, DkvError  # noqa: F401
+from ._lib import (DKV_FIRST_TOKEN_GATHER, DKV_FIRST_TOKEN_SCATTER, DKV_PACK,  # noqa: F401
+                   DKV_UNPACK, DKV_UNPACK_BWD)
 
 __all__ = ["dkv_workspace_size", "dkv_ctx_fwd", "dkv_fwd", "dkv_ctx_bwd", "dkv_bwd",
-           "dkv_cast_acc", "dualkv_forward", "dualkv_backward", "DkvError", "DKV_ACC_ZERO", "DKV_ACC_FINALIZE", "DKV_ACC_SPLIT"]
+           "dkv_cast_acc", "dkv_layout", "layout_rows", "dualkv_forward", "dualkv_backward",
+           "DkvError", "DKV_ACC_ZERO", "DKV_ACC_FINALIZE", "DKV_ACC_SPLIT", "DKV_PACK",
+           "DKV_UNPACK", "DKV_UNPACK_BWD", "DKV_FIRST_TOKEN_GATHER", "DKV_FIRST_TOKEN_SCATTER"]
 
 _DT = {torch.bfloat16: L.DKV_BF16, torch.float32: L.DKV_FP32}
 
@@ -160,6 +164,52 @@ def dkv_cast_acc(acc_dk, acc_dv, dk, dv):
     L.check(L.lib().dkv_cast_acc(p, rows, _p(acc_dk), _p(acc_dv), _p(dk), _p(dv),
                                  _stream(dk.device)))
     return dk, dv
+
+
+def layout_rows(op: int, cu_host, ctx_len: int, ctx_cu_host=None, group_seq_cu_host=None):
+    """(input rows, output rows) of a layout op for these sequences and groups."""
+    cu = [int(c) for c in cu_host]
+    N, T = len(cu) - 1, cu[-1]
+    if ctx_cu_host is None:
+        plen = [ctx_len] * N
+    else:
+        plen = [0] * N
+        for j in range(len(ctx_cu_host) - 1):
+            for i in range(group_seq_cu_host[j], group_seq_cu_host[j + 1]):
+                plen[i] = ctx_cu_host[j + 1] - ctx_cu_host[j]
+    ncopy = sum(plen) + T
+    packed = ctx_len + T
+    return {L.DKV_PACK: (ncopy, packed), L.DKV_UNPACK: (packed, ncopy),
+            L.DKV_UNPACK_BWD: (ncopy, packed), L.DKV_FIRST_TOKEN_GATHER: (packed, T),
+            L.DKV_FIRST_TOKEN_SCATTER: (T, packed)}[op]
+
+
+def dkv_layout(op: int, x, cu_host, ctx_len: int, *, ctx_cu_host=None, group_seq_cu_host=None,
+               out=None, workspace=None):
+    """Move per-token rows between the N-copy and the single-prompt packing, or form /
+    scatter the first-token predictor rows (see dkv_layout_op in include/dkv.h).
+    x [rows_in, ...] (bf16 or fp32, contiguous); returns out [rows_out, ...]."""
+    if x.dtype not in _DT:
+        raise TypeError("unsupported dtype %s" % x.dtype)
+    rows_in, rows_out = layout_rows(op, cu_host, ctx_len, ctx_cu_host, group_seq_cu_host)
+    if x.shape[0] != rows_in:
+        raise ValueError("layout op %d expects %d input rows, got %d" % (op, rows_in, x.shape[0]))
+    row_elems = x[0].numel() if x.shape[0] else int(torch.tensor(x.shape[1:]).prod())
+    cu = [int(c) for c in cu_host]
+    p, keep = L.make_params(num_seqs=len(cu) - 1, ctx_len=ctx_len, num_heads_q=1,
+                            num_heads_kv=1, head_dim=64, dtype=_DT[x.dtype], cu_host=cu,
+                            ctx_cu_host=ctx_cu_host, group_seq_cu_host=group_seq_cu_host)
+    out = torch.empty((rows_out,) + tuple(x.shape[1:]), dtype=x.dtype, device=x.device) \
+        if out is None else out
+    n = L.lib().dkv_layout_workspace_size(p, op)
+    if n == (1 << 64) - 1:
+        L.check(L.DKV_ERR_INVALID_ARG)
+    ws, nws = (None, 0) if n == 0 else (
+        (workspace, workspace.numel()) if workspace is not None and workspace.numel() >= n
+        else (torch.empty(n, dtype=torch.uint8, device=x.device), n))
+    L.check(L.lib().dkv_layout(p, op, row_elems, _p(x), _p(out), _p(ws), nws,
+                               _stream(x.device)))
+    return out
 
 
 def _prompt_cu(P, ctx_cu_host, device):

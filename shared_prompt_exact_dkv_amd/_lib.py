@@ -18,6 +18,8 @@ DKV_OK, DKV_ERR_INVALID_ARG, DKV_ERR_UNSUPPORTED, DKV_ERR_WORKSPACE, DKV_ERR_HIP
 DKV_BF16, DKV_FP32 = 0, 1
 DKV_CALL_CTX_FWD, DKV_CALL_FWD, DKV_CALL_CTX_BWD, DKV_CALL_BWD, DKV_CALL_BWD_SPLIT = range(5)
 DKV_ACC_ZERO, DKV_ACC_FINALIZE, DKV_ACC_SPLIT = 1, 2, 4
+(DKV_PACK, DKV_UNPACK, DKV_UNPACK_BWD, DKV_FIRST_TOKEN_GATHER,
+ DKV_FIRST_TOKEN_SCATTER) = range(5)
 
 
 class DkvParams(ctypes.Structure):
@@ -58,6 +60,8 @@ _SIGS = {
     "dkv_bwd": (ctypes.c_int, [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                _vp, ctypes.c_int, _vp, _vp, _vp, _sz, _vp]),
     "dkv_cast_acc": (ctypes.c_int, [_pp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]),
+    "dkv_layout_workspace_size": (_sz, [_pp, ctypes.c_int]),
+    "dkv_layout": (ctypes.c_int, [_pp, ctypes.c_int, ctypes.c_int64, _vp, _vp, _vp, _sz, _vp]),
     "dkv_timing_enable": (None, [ctypes.c_int]),
     "dkv_timing_reset": (None, []),
     "dkv_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_char_p),

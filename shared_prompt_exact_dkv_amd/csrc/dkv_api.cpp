@@ -60,39 +60,13 @@ struct Shape {
   int kv_tile;              // keys per dK/dV workgroup
 };
 
-dkv_status check_params(const dkv_params *p, bool is_ctx, Shape *s) {
-  if (!p) return fail(DKV_ERR_INVALID_ARG, "params is NULL");
-  if (p->num_seqs < 0) return fail(DKV_ERR_INVALID_ARG, "num_seqs < 0 (%d)", p->num_seqs);
-  if (p->ctx_len < 0) return fail(DKV_ERR_INVALID_ARG, "ctx_len < 0 (%d)", p->ctx_len);
-  if (is_ctx && p->ctx_len != 0)
-    return fail(DKV_ERR_INVALID_ARG, "ctx_len must be 0 for dkv_ctx_* calls (got %d)", p->ctx_len);
-  if (p->num_heads_q <= 0 || p->num_heads_kv <= 0)
-    return fail(DKV_ERR_INVALID_ARG, "head counts must be positive (Hq=%d, Hkv=%d)",
-                p->num_heads_q, p->num_heads_kv);
-  if (p->num_heads_q % p->num_heads_kv != 0)
-    return fail(DKV_ERR_INVALID_ARG, "Hq (%d) is not a multiple of Hkv (%d)", p->num_heads_q,
-                p->num_heads_kv);
-  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 512)
-    return fail(DKV_ERR_INVALID_ARG, "head_dim must be 64, 128 or 512 (got %d)", p->head_dim);
-  if (p->window_left < -1)
-    return fail(DKV_ERR_INVALID_ARG, "window_left must be -1 or >= 0 (got %d)", p->window_left);
-  if (p->dtype != DKV_BF16 && p->dtype != DKV_FP32)
-    return fail(DKV_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
-  if (!(std::isfinite(p->softmax_scale)))
-    return fail(DKV_ERR_INVALID_ARG, "softmax_scale is not finite");
+// Sequences and prompt groups: cu_seqlens, and the group arrays (dkv_fwd / dkv_bwd
+// and the layout conversions).  Fills N, P, T, cu and the per-group / per-sequence
+// prompt rows.
+dkv_status check_seqs(const dkv_params *p, bool is_ctx, Shape *s) {
   if (!p->cu_seqlens_host) return fail(DKV_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
-  const int G = p->num_heads_q / p->num_heads_kv;
-  if (G > kRowsPerWG)
-    return fail(DKV_ERR_UNSUPPORTED, "Hq/Hkv = %d exceeds %d", G, kRowsPerWG);
   s->N = p->num_seqs;
   s->P = p->ctx_len;
-  s->Hq = p->num_heads_q;
-  s->Hkv = p->num_heads_kv;
-  s->G = G;
-  s->d = p->head_dim;
-  s->wl = p->window_left;
-  s->dtype = p->dtype;
-  s->scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
   s->cu.assign(p->cu_seqlens_host, p->cu_seqlens_host + p->num_seqs + 1);
   if (s->cu[0] != 0) return fail(DKV_ERR_INVALID_ARG, "cu_seqlens[0] must be 0 (got %d)", s->cu[0]);
   for (int i = 0; i < s->N; ++i)
@@ -100,8 +74,6 @@ dkv_status check_params(const dkv_params *p, bool is_ctx, Shape *s) {
       return fail(DKV_ERR_INVALID_ARG, "cu_seqlens decreases at %d (%d -> %d)", i, s->cu[i],
                   s->cu[i + 1]);
   s->T = s->cu[s->N];
-  if (s->T > 0 && !p->cu_seqlens_dev)
-    return fail(DKV_ERR_INVALID_ARG, "cu_seqlens_dev is NULL");
   {
     const int ng = p->num_groups;
     if (ng < 0) return fail(DKV_ERR_INVALID_ARG, "num_groups < 0 (%d)", ng);
@@ -140,6 +112,42 @@ dkv_status check_params(const dkv_params *p, bool is_ctx, Shape *s) {
         s->sP[i] = s->gctx[j + 1] - s->gctx[j];
       }
   }
+  return DKV_OK;
+}
+
+dkv_status check_params(const dkv_params *p, bool is_ctx, Shape *s) {
+  if (!p) return fail(DKV_ERR_INVALID_ARG, "params is NULL");
+  if (p->num_seqs < 0) return fail(DKV_ERR_INVALID_ARG, "num_seqs < 0 (%d)", p->num_seqs);
+  if (p->ctx_len < 0) return fail(DKV_ERR_INVALID_ARG, "ctx_len < 0 (%d)", p->ctx_len);
+  if (is_ctx && p->ctx_len != 0)
+    return fail(DKV_ERR_INVALID_ARG, "ctx_len must be 0 for dkv_ctx_* calls (got %d)", p->ctx_len);
+  if (p->num_heads_q <= 0 || p->num_heads_kv <= 0)
+    return fail(DKV_ERR_INVALID_ARG, "head counts must be positive (Hq=%d, Hkv=%d)",
+                p->num_heads_q, p->num_heads_kv);
+  if (p->num_heads_q % p->num_heads_kv != 0)
+    return fail(DKV_ERR_INVALID_ARG, "Hq (%d) is not a multiple of Hkv (%d)", p->num_heads_q,
+                p->num_heads_kv);
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 512)
+    return fail(DKV_ERR_INVALID_ARG, "head_dim must be 64, 128 or 512 (got %d)", p->head_dim);
+  if (p->window_left < -1)
+    return fail(DKV_ERR_INVALID_ARG, "window_left must be -1 or >= 0 (got %d)", p->window_left);
+  if (p->dtype != DKV_BF16 && p->dtype != DKV_FP32)
+    return fail(DKV_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
+  if (!(std::isfinite(p->softmax_scale)))
+    return fail(DKV_ERR_INVALID_ARG, "softmax_scale is not finite");
+  const int G = p->num_heads_q / p->num_heads_kv;
+  if (G > kRowsPerWG)
+    return fail(DKV_ERR_UNSUPPORTED, "Hq/Hkv = %d exceeds %d", G, kRowsPerWG);
+  s->Hq = p->num_heads_q;
+  s->Hkv = p->num_heads_kv;
+  s->G = G;
+  s->d = p->head_dim;
+  s->wl = p->window_left;
+  s->dtype = p->dtype;
+  s->scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
+  if (dkv_status st = check_seqs(p, is_ctx, s)) return st;
+  if (s->T > 0 && !p->cu_seqlens_dev)
+    return fail(DKV_ERR_INVALID_ARG, "cu_seqlens_dev is NULL");
   {
     // A window at least as long as the longest logical position sees every earlier
     // key: it is the global causal mask, and is run as one (the kernels form key + wl
@@ -333,9 +341,9 @@ dkv_status upload(const void *src, size_t bytes, void *dst, hipStream_t stream) 
 
 // -------------------------------------------------------------- kernel timing --
 
-enum KernelClass { kKFwd = 0, kKPre, kKDq, kKDkdv, kKZero, kKCast, kKReduce, kKClasses };
-const char *const kKernelNames[kKClasses] = {"attn_fwd", "bwd_pre", "bwd_dq", "bwd_dkdv",
-                                             "acc_zero", "acc_cast", "split_reduce"};
+enum KernelClass { kKFwd = 0, kKPre, kKDq, kKDkdv, kKZero, kKCast, kKReduce, kKLayout, kKClasses };
+const char *const kKernelNames[kKClasses] = {"attn_fwd", "bwd_pre",  "bwd_dq",       "bwd_dkdv",
+                                             "acc_zero", "acc_cast", "split_reduce", "layout"};
 
 struct Timing {
   std::mutex mu;
@@ -703,6 +711,131 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
   return DKV_OK;
 }
 
+// ------------------------------------------------------- layout conversions --
+//
+// Row maps between the N-copy packing (copy i = its prompt's rows then its own rows,
+// copies in sequence order) and the single-prompt packing (every prompt once, in group
+// order, then every response).  Each segment of consecutive rows becomes work items of
+// at most kRowsPerItem rows.
+
+struct LayoutPlan {
+  std::vector<RowItem> items;
+  std::vector<int32_t> src;
+  long in_rows = 0, out_rows = 0;
+  size_t items_off = 0, src_off = 0, bytes = 0;
+};
+
+// Output rows [dst, dst + n): the sum over the given input row starts (each advanced
+// with the row), a copy for one start, zeros for none.  An item of several sources
+// takes fewer rows, so that it reads about as much as a copy item.
+void add_segment(LayoutPlan &pl, long dst, long n, const std::vector<long> &starts) {
+  const long rows = std::max<long>(1, kRowsPerItem / std::max<long>(1, (long)starts.size()));
+  for (long k = 0; k < n; k += rows) {
+    RowItem it;
+    it.dst_row = (int32_t)(dst + k);
+    it.nrows = (int32_t)std::min<long>(rows, n - k);
+    it.src_off = (int32_t)pl.src.size();
+    it.nsrc = (int32_t)starts.size();
+    for (long st : starts) pl.src.push_back((int32_t)(st + k));
+    pl.items.push_back(it);
+  }
+}
+
+LayoutPlan plan_layout(const Shape &s, int op) {
+  LayoutPlan pl;
+  std::vector<long> nc0(s.N + 1, 0);   // first row of each copy in the N-copy packing
+  for (int i = 0; i < s.N; ++i) nc0[i + 1] = nc0[i] + s.sP[i] + (s.cu[i + 1] - s.cu[i]);
+  const long packed = (long)s.P + s.T;
+  const int ngroups = (int)s.gseq.size() - 1;
+  auto len = [&](int i) { return (long)(s.cu[i + 1] - s.cu[i]); };
+  switch (op) {
+    case DKV_PACK:   // N-copy -> single-prompt: prompts from each group's first copy
+      pl.in_rows = nc0[s.N];
+      pl.out_rows = packed;
+      for (int j = 0; j < ngroups; ++j) {
+        std::vector<long> st;
+        if (s.gseq[j + 1] > s.gseq[j]) st.push_back(nc0[s.gseq[j]]);
+        add_segment(pl, s.gctx[j], s.gctx[j + 1] - s.gctx[j], st);
+      }
+      for (int i = 0; i < s.N; ++i) add_segment(pl, s.P + s.cu[i], len(i), {nc0[i] + s.sP[i]});
+      break;
+    case DKV_UNPACK:   // single-prompt -> N-copy: each copy takes its group's prompt
+      pl.in_rows = packed;
+      pl.out_rows = nc0[s.N];
+      for (int i = 0; i < s.N; ++i) {
+        add_segment(pl, nc0[i], s.sP[i], {(long)s.sctx0[i]});
+        add_segment(pl, nc0[i] + s.sP[i], len(i), {(long)s.P + s.cu[i]});
+      }
+      break;
+    case DKV_UNPACK_BWD:   // adjoint of UNPACK: a prompt row sums its group's copies
+      pl.in_rows = nc0[s.N];
+      pl.out_rows = packed;
+      for (int j = 0; j < ngroups; ++j) {
+        std::vector<long> st;
+        for (int i = s.gseq[j]; i < s.gseq[j + 1]; ++i) st.push_back(nc0[i]);
+        add_segment(pl, s.gctx[j], s.gctx[j + 1] - s.gctx[j], st);
+      }
+      for (int i = 0; i < s.N; ++i) add_segment(pl, s.P + s.cu[i], len(i), {nc0[i] + s.sP[i]});
+      break;
+    case DKV_FIRST_TOKEN_GATHER:   // predictor row of every response token
+      pl.in_rows = packed;
+      pl.out_rows = s.T;
+      for (int i = 0; i < s.N; ++i) {
+        if (len(i) == 0) continue;
+        std::vector<long> st;
+        if (s.sP[i] > 0) st.push_back(s.sctx0[i] + s.sP[i] - 1);   // the last prompt row
+        add_segment(pl, s.cu[i], 1, st);
+        add_segment(pl, s.cu[i] + 1, len(i) - 1, {(long)s.P + s.cu[i]});
+      }
+      break;
+    case DKV_FIRST_TOKEN_SCATTER:   // adjoint of the gather
+      pl.in_rows = s.T;
+      pl.out_rows = packed;
+      for (int j = 0; j < ngroups; ++j) {
+        const long Pg = s.gctx[j + 1] - s.gctx[j];
+        if (Pg == 0) continue;
+        add_segment(pl, s.gctx[j], Pg - 1, {});
+        std::vector<long> st;
+        for (int i = s.gseq[j]; i < s.gseq[j + 1]; ++i)
+          if (len(i) > 0) st.push_back(s.cu[i]);
+        add_segment(pl, s.gctx[j + 1] - 1, 1, st);
+      }
+      for (int i = 0; i < s.N; ++i) {
+        if (len(i) == 0) continue;
+        add_segment(pl, s.P + s.cu[i], len(i) - 1, {(long)s.cu[i] + 1});
+        add_segment(pl, s.P + s.cu[i] + len(i) - 1, 1, {});
+      }
+      break;
+  }
+  pl.items_off = 0;
+  pl.src_off = align_up(pl.items.size() * sizeof(RowItem));
+  pl.bytes = pl.items.empty() ? 0 : pl.src_off + align_up(pl.src.size() * sizeof(int32_t));
+  return pl;
+}
+
+dkv_status check_layout(const dkv_params *p, int op, long row_elems, Shape *s) {
+  if (!p) return fail(DKV_ERR_INVALID_ARG, "params is NULL");
+  if (op < DKV_PACK || op > DKV_FIRST_TOKEN_SCATTER)
+    return fail(DKV_ERR_INVALID_ARG, "unknown layout op %d", op);
+  if (p->num_seqs < 0) return fail(DKV_ERR_INVALID_ARG, "num_seqs < 0 (%d)", p->num_seqs);
+  if (p->ctx_len < 0) return fail(DKV_ERR_INVALID_ARG, "ctx_len < 0 (%d)", p->ctx_len);
+  if (p->dtype != DKV_BF16 && p->dtype != DKV_FP32)
+    return fail(DKV_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
+  s->dtype = p->dtype;
+  if (dkv_status st = check_seqs(p, false, s)) return st;
+  const long vec = 16 / (long)elem_size(p->dtype);
+  if (row_elems <= 0 || row_elems % vec != 0)
+    return fail(DKV_ERR_INVALID_ARG, "row_elems (%ld) must be a positive multiple of %ld", row_elems,
+                vec);
+  long rows = 0;
+  for (int i = 0; i < s->N; ++i) rows += (long)s->sP[i] + s->cu[i + 1] - s->cu[i];
+  rows = std::max<long>(rows, (long)s->P + s->T);
+  if (rows >= (1L << 31) || row_elems / vec >= (1L << 31) / kRowsPerItem)
+    return fail(DKV_ERR_UNSUPPORTED, "layout of %ld rows x %ld elements exceeds the 32-bit row "
+                "indices of the kernels", rows, row_elems);
+  return DKV_OK;
+}
+
 }  // namespace
 
 // ====================================================================== C ABI ==
@@ -885,6 +1018,40 @@ dkv_status dkv_cast_acc(const dkv_params *p, int32_t rows, const float *acc_dk,
     return r != hipSuccess ? r : launch_cast(p->dtype, acc_dv, dv, n, stream);
   });
   if (e != hipSuccess) return hip_fail(e, "cast");
+  return DKV_OK;
+}
+
+size_t dkv_layout_workspace_size(const dkv_params *p, int op) {
+  Shape s;
+  if (check_layout(p, op, 16 / (p && p->dtype == DKV_FP32 ? 4 : 2), &s) != DKV_OK)
+    return (size_t)-1;
+  return plan_layout(s, op).bytes;
+}
+
+dkv_status dkv_layout(const dkv_params *p, int op, int64_t row_elems, const void *in, void *out,
+                      void *ws, size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  dkv_status st = check_layout(p, op, (long)row_elems, &s);
+  if (st != DKV_OK) return st;
+  LayoutPlan pl = plan_layout(s, op);
+  if ((st = check_ptr(in, "in", pl.in_rows > 0)) || (st = check_ptr(out, "out", pl.out_rows > 0)))
+    return st;
+  if ((st = check_ws(ws, ws_bytes, pl.bytes)) != DKV_OK) return st;
+  if (pl.items.empty()) return DKV_OK;
+  char *wsb = static_cast<char *>(ws);
+  if ((st = upload(pl.items.data(), pl.items.size() * sizeof(RowItem), wsb + pl.items_off,
+                   stream)) != DKV_OK)
+    return st;
+  if (!pl.src.empty() &&
+      (st = upload(pl.src.data(), pl.src.size() * sizeof(int32_t), wsb + pl.src_off, stream)) != DKV_OK)
+    return st;
+  const int row_vecs = (int)(row_elems * (long)elem_size(s.dtype) / 16);
+  hipError_t e = timed(kKLayout, stream, [&] {
+    return launch_row_sum(s.dtype, in, out, reinterpret_cast<const RowItem *>(wsb + pl.items_off),
+                          (int)pl.items.size(), reinterpret_cast<const int32_t *>(wsb + pl.src_off),
+                          row_vecs, stream);
+  });
+  if (e != hipSuccess) return hip_fail(e, "layout kernel launch");
   return DKV_OK;
 }
 

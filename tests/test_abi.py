@@ -187,3 +187,19 @@ def test_prompt_groups_workspace_matches_one_group():
         a, b, c = (lib.dkv_workspace_size(p, call) for p in (p0, p1, p2))
         assert a == b, call
         assert c != (1 << 64) - 1 and c > 0, call
+
+
+def test_layout_validation():
+    lib = L.lib()
+    p, keep = _params()
+    st = lib.dkv_layout(p, 7, 64, FAKE, FAKE, FAKE, 1 << 20, None)
+    assert st == L.DKV_ERR_INVALID_ARG and "op" in L.last_error()
+    st = lib.dkv_layout(p, L.DKV_PACK, 12, FAKE, FAKE, FAKE, 1 << 20, None)   # not 16-byte rows
+    assert st == L.DKV_ERR_INVALID_ARG and "row_elems" in L.last_error()
+    st = lib.dkv_layout(p, L.DKV_UNPACK, 64, FAKE, FAKE, FAKE, 0, None)
+    assert st == L.DKV_ERR_WORKSPACE
+    st = lib.dkv_layout(p, L.DKV_UNPACK, 64, None, FAKE, FAKE, 1 << 20, None)
+    assert st == L.DKV_ERR_INVALID_ARG and "in" in L.last_error()
+    # work lists: unpack of N = 2 copies of a 16-row prompt plus 9 response rows
+    n = lib.dkv_layout_workspace_size(p, L.DKV_UNPACK)
+    assert 0 < n < 4096
