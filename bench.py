@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--split", action="store_true",
                     help="sum the shared-prompt gradient through per-chunk slices and a "
                          "fixed-order reduction (DKV_ACC_SPLIT) instead of fp32 atomics")
+    ap.add_argument("--dtype", choices=["bf16", "fp16"], default=None,
+                    help="run a 16-bit workload in this element type instead of its own "
+                         "(fp16: the precision of the paper's kernel benchmark)")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--layout", action="store_true",
                     help="time the layout conversions (dkv_layout: N-copy <-> single-prompt "
@@ -65,7 +68,7 @@ def kernel_algo_work(w, P, lens, pairs):
     number of prompt rows (all groups' prompts)."""
     d, Hq, Hkv = w.d, w.Hq, w.Hkv
     T = P + sum(lens)                   # query rows over both calls
-    eb = 2 if w.dtype == "bf16" else 4
+    eb = 4 if w.dtype == "fp32" else 2
     return {
         # forward: Q K^T and P V on every visible pair
         "attn_fwd": (4 * d * Hq * pairs, "flop", "mfma"),
@@ -210,6 +213,12 @@ def main():
         return layout_main(args)
     dev = "cuda:0"
     w = workloads.WORKLOADS[args.workload]
+    if args.dtype is not None:
+        if w.dtype == "fp32":
+            print("--dtype applies to the 16-bit workloads only", file=sys.stderr)
+            sys.exit(2)
+        import dataclasses
+        w = dataclasses.replace(w, dtype=args.dtype)
     Hq, Hkv, d, wl = w.Hq, w.Hkv, w.d, w.window_left
     tdt = workloads.torch_dtype(w.dtype)
     log(args, "workload", w)
@@ -291,7 +300,7 @@ def main():
     pairs_nc = sum(accounting.pairs_ncopy(Pj, ls, wl) for Pj, ls in shapes)
     flops = accounting.useful_flops(pairs, Hq, d)
     tflops = flops / (ms * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    peak = PEAK_FP32_TFLOPS if w.dtype == "fp32" else PEAK_BF16_TFLOPS   # fp16 = bf16 peak
 
     # Fwd/bwd split of the step (per call classes), from the live kernel times.
     fwd_ms = ktimes.get("attn_fwd", (0.0, 0))[0] / args.steps

@@ -24,7 +24,7 @@
  *       queries / outputs / output grads  [tokens, Hq,  d]
  *       keys / values / their grads       [tokens, Hkv, d]
  *       LSE                               [Hq, tokens] fp32, natural log
- *     in the dtype named by dkv_params.dtype (bf16 or fp32).  Device pointers must
+ *     in the dtype named by dkv_params.dtype (bf16, fp16 or fp32).  Device pointers must
  *     be 16-byte aligned.
  *   - The library never allocates or frees device memory.  Scratch space comes from
  *     `ws` (device memory, `ws_bytes` long, 256-byte aligned), sized by
@@ -53,14 +53,17 @@ typedef enum {
     DKV_OK = 0,
     DKV_ERR_INVALID_ARG = 1,   /* inconsistent shapes, bad cu_seqlens, null pointers */
     /* valid but not implemented: head_dim 512 in fp32, Hq / Hkv above 128 (32 at
-       head_dim 512), or (bf16) a sequence whose query rows, plus 64, exceed 2^31 bytes
+       head_dim 512), or (bf16 / fp16) a sequence whose query rows, plus 64, exceed 2^31 bytes
        or Hq * tokens above 2^29 -- the kernels' 32-bit row offsets */
     DKV_ERR_UNSUPPORTED = 2,
     DKV_ERR_WORKSPACE = 3,     /* ws too small or misaligned */
     DKV_ERR_HIP = 4            /* a HIP runtime call failed */
 } dkv_status;
 
-typedef enum { DKV_BF16 = 0, DKV_FP32 = 1 } dkv_dtype;
+/* Tensor element types.  bf16 and fp16 run the same 16-bit MFMA kernels (fp32
+   accumulation, softmax and LSE in fp32); fp16 is the precision of the paper's kernel
+   benchmark (§4.1, Table 1). */
+typedef enum { DKV_BF16 = 0, DKV_FP32 = 1, DKV_FP16 = 2 } dkv_dtype;
 
 /* Which call a workspace is sized for. */
 typedef enum {

@@ -24,7 +24,7 @@ __all__ = ["dkv_workspace_size", "dkv_ctx_fwd", "dkv_fwd", "dkv_ctx_bwd", "dkv_b
            "DkvError", "DKV_ACC_ZERO", "DKV_ACC_FINALIZE", "DKV_ACC_SPLIT", "DKV_PACK",
            "DKV_UNPACK", "DKV_UNPACK_BWD", "DKV_FIRST_TOKEN_GATHER", "DKV_FIRST_TOKEN_SCATTER"]
 
-_DT = {torch.bfloat16: L.DKV_BF16, torch.float32: L.DKV_FP32}
+_DT = {torch.bfloat16: L.DKV_BF16, torch.float32: L.DKV_FP32, torch.float16: L.DKV_FP16}
 
 
 def _p(t):

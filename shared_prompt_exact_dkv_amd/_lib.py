@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG, "libdkv.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "dkv.h")
 
 DKV_OK, DKV_ERR_INVALID_ARG, DKV_ERR_UNSUPPORTED, DKV_ERR_WORKSPACE, DKV_ERR_HIP = range(5)
-DKV_BF16, DKV_FP32 = 0, 1
+DKV_BF16, DKV_FP32, DKV_FP16 = 0, 1, 2
 DKV_CALL_CTX_FWD, DKV_CALL_FWD, DKV_CALL_CTX_BWD, DKV_CALL_BWD, DKV_CALL_BWD_SPLIT = range(5)
 DKV_ACC_ZERO, DKV_ACC_FINALIZE, DKV_ACC_SPLIT = 1, 2, 4
 (DKV_PACK, DKV_UNPACK, DKV_UNPACK_BWD, DKV_FIRST_TOKEN_GATHER,

@@ -41,7 +41,11 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-size_t elem_size(int dtype) { return dtype == DKV_BF16 ? 2 : 4; }
+size_t elem_size(int dtype) { return dtype == DKV_FP32 ? 4 : 2; }
+
+// bf16 and fp16 run the same 16-bit MFMA kernels.
+bool is16(int dtype) { return dtype == DKV_BF16 || dtype == DKV_FP16; }
+bool known_dtype(int dtype) { return is16(dtype) || dtype == DKV_FP32; }
 
 // ---------------------------------------------------------------- validation --
 
@@ -131,7 +135,7 @@ dkv_status check_params(const dkv_params *p, bool is_ctx, Shape *s) {
     return fail(DKV_ERR_INVALID_ARG, "head_dim must be 64, 128 or 512 (got %d)", p->head_dim);
   if (p->window_left < -1)
     return fail(DKV_ERR_INVALID_ARG, "window_left must be -1 or >= 0 (got %d)", p->window_left);
-  if (p->dtype != DKV_BF16 && p->dtype != DKV_FP32)
+  if (!known_dtype(p->dtype))
     return fail(DKV_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
   if (!(std::isfinite(p->softmax_scale)))
     return fail(DKV_ERR_INVALID_ARG, "softmax_scale is not finite");
@@ -157,8 +161,8 @@ dkv_status check_params(const dkv_params *p, bool is_ctx, Shape *s) {
       max_pos = std::max<long>(max_pos, (long)s->sP[i] + s->cu[i + 1] - s->cu[i]);
     if (s->wl >= 0 && (long)s->wl >= max_pos) s->wl = -1;
   }
-  if (s->dtype == DKV_BF16) {
-    // The bf16 backward addresses a sequence's query rows, and the LSE / D rows, with
+  if (is16(s->dtype)) {
+    // The 16-bit backward addresses a sequence's query rows, and the LSE / D rows, with
     // 32-bit byte offsets from the sequence's start (buffer loads): the query rows of
     // one sequence (plus one 64-row step of slack) and Hq * T LSE entries must stay
     // below 2^31 bytes.
@@ -180,8 +184,8 @@ dkv_status check_params(const dkv_params *p, bool is_ctx, Shape *s) {
     // Head dim 512 splits the head dim across the waves of a workgroup: 128 query
     // rows per forward workgroup, 64 per dQ workgroup, 64 keys per dK/dV workgroup;
     // bf16 only.
-    if (s->dtype != DKV_BF16)
-      return fail(DKV_ERR_UNSUPPORTED, "head_dim 512 is implemented for bf16 only");
+    if (!is16(s->dtype))
+      return fail(DKV_ERR_UNSUPPORTED, "head_dim 512 is implemented for bf16 / fp16 only");
     if (G > kMaxG512)
       return fail(DKV_ERR_UNSUPPORTED, "Hq/Hkv = %d exceeds %d at head_dim 512", G, kMaxG512);
     s->bm_tok = kFwdRows512 / G;
@@ -646,7 +650,7 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
   if (s.T > 0) {
     float *Dneg = reinterpret_cast<float *>(wsb + pl.d_off);
     float *lsn = reinterpret_cast<float *>(wsb + pl.l2_off);
-    const bool fused_pre = s.dtype == DKV_BF16;   // the bf16 dQ kernels form -D, -LSE/scale
+    const bool fused_pre = is16(s.dtype);   // the 16-bit dQ kernels form -D, -LSE/scale
     if (!fused_pre) {
       e = timed(kKPre, stream, [&] {
         return launch_bwd_pre(s.dtype, s.d, io.o, io.dout, io.lse, Dneg, lsn, s.T, s.Hq, s.scale,
@@ -819,7 +823,7 @@ dkv_status check_layout(const dkv_params *p, int op, long row_elems, Shape *s) {
     return fail(DKV_ERR_INVALID_ARG, "unknown layout op %d", op);
   if (p->num_seqs < 0) return fail(DKV_ERR_INVALID_ARG, "num_seqs < 0 (%d)", p->num_seqs);
   if (p->ctx_len < 0) return fail(DKV_ERR_INVALID_ARG, "ctx_len < 0 (%d)", p->ctx_len);
-  if (p->dtype != DKV_BF16 && p->dtype != DKV_FP32)
+  if (!known_dtype(p->dtype))
     return fail(DKV_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
   s->dtype = p->dtype;
   if (dkv_status st = check_seqs(p, false, s)) return st;
@@ -1002,7 +1006,7 @@ dkv_status dkv_cast_acc(const dkv_params *p, int32_t rows, const float *acc_dk,
                         const float *acc_dv, void *dk, void *dv, hipStream_t stream) {
   if (!p) return fail(DKV_ERR_INVALID_ARG, "params is NULL");
   if (rows < 0) return fail(DKV_ERR_INVALID_ARG, "rows < 0");
-  if (p->dtype != DKV_BF16 && p->dtype != DKV_FP32)
+  if (!known_dtype(p->dtype))
     return fail(DKV_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
   if (p->num_heads_kv <= 0 || p->head_dim <= 0)
     return fail(DKV_ERR_INVALID_ARG, "bad head shape");
@@ -1023,7 +1027,7 @@ dkv_status dkv_cast_acc(const dkv_params *p, int32_t rows, const float *acc_dk,
 
 size_t dkv_layout_workspace_size(const dkv_params *p, int op) {
   Shape s;
-  if (check_layout(p, op, 16 / (p && p->dtype == DKV_FP32 ? 4 : 2), &s) != DKV_OK)
+  if (check_layout(p, op, 16 / (p ? (long)elem_size(p->dtype) : 2), &s) != DKV_OK)
     return (size_t)-1;
   return plan_layout(s, op).bytes;
 }

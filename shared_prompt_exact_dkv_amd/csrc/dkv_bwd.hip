@@ -4,11 +4,11 @@
 //   p  = exp(scale * <q_t, k_j> - lse_t)        (recomputed from the forward's LSE)
 //   dP = <dO_t, v_j>,   dS = p * (dP - D_t),    D_t = <dO_t, O_t>
 //   dQ_t += scale * dS * k_j,   dK_j += scale * dS * q_t,   dV_j += p * dO_t
-// Kernels (each bf16 kernel has an fp32 counterpart for the 1e-5 parity workload;
+// Kernels (each h16 kernel has an fp32 counterpart for the 1e-5 parity workload;
 // head dim 512 is in dkv_d512.hip):
 //   bwd_pre   D = rowsum(dO * O) in fp32 (the auxiliary preprocessing launch), stored
 //             negated, and the LSE in units of the raw dot product, -LSE / scale;
-//             the fp32 path only: the bf16 dQ kernel forms both for its rows
+//             the fp32 path only: the h16 dQ kernel forms both for its rows
 //   bwd_dq    query-parallel: a workgroup keeps 128 query rows in registers and
 //             walks the shared-prompt key tiles, then its own sequence's tiles,
 //             exactly like the forward; dQ is written once, no atomics.
@@ -20,7 +20,7 @@
 //             accumulation", eq. (6)), or stored into the chunk's slice (split mode)
 //             for split_reduce to add in slice order.
 //   cast      the accumulator is rounded to the tensor dtype once (§3.2 Stage 2).
-// In the bf16 kernels, transposed operands (contractions over query rows or key rows)
+// In the h16 kernels, transposed operands (contractions over query rows or key rows)
 // are read from the same row-layout LDS tiles with the gfx950 transpose read.
 #include <type_traits>
 
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void cast_kernel(const float *src, T *dst, lon
 
 // ------------------------------------------------------------------- bwd_dq --
 
-// fp32 dQ kernel: the query-parallel structure of the bf16 one with fp32 MFMA, base-e
+// fp32 dQ kernel: the query-parallel structure of the h16 one with fp32 MFMA, base-e
 // softmax and compensated (Kahan) accumulation, one key per product.
 template <int HD>
 __global__ __launch_bounds__(256, 1) void bwd_dq_f32_kernel(BwdQArgs a) {
@@ -262,11 +262,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_f32_kernel(BwdQArgs a) {
   }
 }
 
-// bf16 dQ kernel with two waves per SIMD: K and V tiles double-buffered in LDS
+// h16 dQ kernel with two waves per SIMD: K and V tiles double-buffered in LDS
 // through buffer loads (one barrier per 64-key tile), each tile taken as two 32-key
 // halves so that Sᵀ, dPᵀ and dSᵀ of one half are live at a time.
-template <int HD>
-__global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
+template <typename E, int HD>
+__global__ __launch_bounds__(256, 2) void bwd_dq_h16_kernel(BwdQArgs a) {
   constexpr int BN = kFwdBN;
   constexpr int TILE = BN * HD * 2;
   constexpr int NKC = HD / 16;
@@ -292,26 +292,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
   const long kld = (long)a.Hkv * HD;
   const long qrow = (long)(seq0 + t0 + tok);
 
-  const bf16 *qptr = reinterpret_cast<const bf16 *>(a.q) + qrow * qld + (long)h * HD;
-  const bf16 *dptr = reinterpret_cast<const bf16 *>(a.dout) + qrow * qld + (long)h * HD;
-  bf16x8 qf[NKC], df[NKC];
+  const h16 *qptr = reinterpret_cast<const h16 *>(a.q) + qrow * qld + (long)h * HD;
+  const h16 *dptr = reinterpret_cast<const h16 *>(a.dout) + qrow * qld + (long)h * HD;
+  h16x8 qf[NKC], df[NKC];
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc) {
-    qf[kc] = as_bf16x8(*reinterpret_cast<const uint4 *>(qptr + kc * 16 + half * 8));
-    df[kc] = as_bf16x8(*reinterpret_cast<const uint4 *>(dptr + kc * 16 + half * 8));
+    qf[kc] = as_h16x8(*reinterpret_cast<const uint4 *>(qptr + kc * 16 + half * 8));
+    df[kc] = as_h16x8(*reinterpret_cast<const uint4 *>(dptr + kc * 16 + half * 8));
   }
   const float sf = a.scale * kLog2e;
   const float lse = a.lse[(long)h * a.lse_ld + qrow];
   const float lse2 = lse * kLog2e;
   // D = rowsum(dO ∘ O) of this lane's row (the preprocess step of the backward, done
   // here): the two lanes of a row each hold half of it, in the dO fragments' layout.
-  const bf16 *optr = reinterpret_cast<const bf16 *>(a.o) + qrow * qld + (long)h * HD;
+  const h16 *optr = reinterpret_cast<const h16 *>(a.o) + qrow * qld + (long)h * HD;
   float Dq = 0.f;
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc) {
-    const bf16x8 o8 = as_bf16x8(*reinterpret_cast<const uint4 *>(optr + kc * 16 + half * 8));
+    const h16x8 o8 = as_h16x8(*reinterpret_cast<const uint4 *>(optr + kc * 16 + half * 8));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) Dq += (float)o8[e] * (float)df[kc][e];
+    for (int e = 0; e < 8; ++e) Dq += val<E>(o8[e]) * val<E>(df[kc][e]);
   }
   Dq = pair_sum(Dq);
   // The dK/dV kernel, which runs next, reads -D and -LSE / scale of every row.
@@ -336,10 +336,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
   const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
   const int n_tiles = n_ctx + n_own;
 
-  const bf16 *kc_base = reinterpret_cast<const bf16 *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
-  const bf16 *vc_base = reinterpret_cast<const bf16 *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
-  const bf16 *ko_base = reinterpret_cast<const bf16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
-  const bf16 *vo_base = reinterpret_cast<const bf16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
+  const h16 *kc_base = reinterpret_cast<const h16 *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
+  const h16 *vc_base = reinterpret_cast<const h16 *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
+  const h16 *ko_base = reinterpret_cast<const h16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
+  const h16 *vo_base = reinterpret_cast<const h16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
   const int kld_b = (int)(kld * 2);
   DmaRows<HD, BN> dma;
   dma.init(wave, lane, kld_b);
@@ -381,8 +381,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
       f32x16 st = zero16(), dpt = negd;
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
-        st = mfma(sw_frag<HD>(ks, hb * 32 + col, kc, half), qf[kc], st);
-        dpt = mfma(sw_frag<HD>(vs, hb * 32 + col, kc, half), df[kc], dpt);
+        st = mma16<E>(sw_frag<HD>(ks, hb * 32 + col, kc, half), qf[kc], st);
+        dpt = mma16<E>(sw_frag<HD>(vs, hb * 32 + col, kc, half), df[kc], dpt);
       }
       float ds[16];
       // The visibility test is compiled only into the variant for tiles that need it.
@@ -407,27 +407,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdQArgs a) {
         grads(std::true_type{});
       else
         grads(std::false_type{});
-      const bf16x8 d0 = pack8(ds), d1 = pack8(ds + 8);
+      const h16x8 d0 = pack8<E>(ds), d1 = pack8<E>(ds + 8);
       // dQᵀ += Kᵀ dSᵀ.
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        acc[db] = mfma(sw_tr_frag<HD>(ks, hb * 32, db * 32, lane), d0, acc[db]);
-        acc[db] = mfma(sw_tr_frag<HD>(ks, hb * 32 + 16, db * 32, lane), d1, acc[db]);
+        acc[db] = mma16<E>(sw_tr_frag<HD>(ks, hb * 32, db * 32, lane), d0, acc[db]);
+        acc[db] = mma16<E>(sw_tr_frag<HD>(ks, hb * 32 + 16, db * 32, lane), d1, acc[db]);
       }
     }
   }
 
   if (row_valid) {
-    bf16 *optr = reinterpret_cast<bf16 *>(a.dq) + qrow * qld + (long)h * HD;
+    h16 *optr = reinterpret_cast<h16 *>(a.dq) + qrow * qld + (long)h * HD;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int dim = db * 32 + 8 * i + 4 * half;
-        bf16x4 w;
+        h16x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * i + e] * a.scale);
-        *reinterpret_cast<bf16x4 *>(optr + dim) = w;
+        for (int e = 0; e < 4; ++e) w[e] = rnd<E>(acc[db][4 * i + e] * a.scale);
+        *reinterpret_cast<h16x4 *>(optr + dim) = w;
       }
   }
 }
@@ -675,7 +675,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdKVArgs a) {
     }
 }
 
-// bf16 dK/dV kernel.  A workgroup owns 128 keys of one region and kv head (32 per
+// h16 dK/dV kernel.  A workgroup owns 128 keys of one region and kv head (32 per
 // wave: V fragments and the dK, dV accumulators in registers; the workgroup's K tile
 // stays in LDS) and streams the query rows that see them in BM-row steps (BM / 32
 // blocks of 32), from the last step backward.  Q, dO, LSE and D of the next step
@@ -684,8 +684,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdKVArgs a) {
 // the rows a lane fetches are fixed within a step, so their token/head split is
 // precomputed.  With K read from LDS and 32-row steps a wave fits 256 registers and
 // the LDS of two workgroups fits a CU: two waves per SIMD.
-template <int HD, int BM, int WPE>
-__global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
+template <typename E, int HD, int BM, int WPE>
+__global__ __launch_bounds__(256, WPE) void bwd_dkdv_h16_kernel(BwdKVArgs a) {
   constexpr int BNW = kBwdBN;
   constexpr int TILE = BM * HD * 2;
   constexpr int NKC = HD / 16;
@@ -713,22 +713,22 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
   const int key = kw0 + col;
   const bool key_valid = key < nkeys;
   const float sf = a.scale * kLog2e;
-  const bf16 *kp = reinterpret_cast<const bf16 *>(ctx ? a.k_ctx : a.k_own) +
+  const h16 *kp = reinterpret_cast<const h16 *>(ctx ? a.k_ctx : a.k_own) +
                    (long)(own0 + it.key_start + (key_valid ? key : 0)) * kld + (long)g * HD;
-  const bf16 *vp = reinterpret_cast<const bf16 *>(ctx ? a.v_ctx : a.v_own) +
+  const h16 *vp = reinterpret_cast<const h16 *>(ctx ? a.v_ctx : a.v_own) +
                    (long)(own0 + it.key_start + (key_valid ? key : 0)) * kld + (long)g * HD;
   (void)kp;
-  bf16x8 vf[NKC];
+  h16x8 vf[NKC];
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc) {
     const uint4 z = make_uint4(0, 0, 0, 0);
-    vf[kc] = as_bf16x8(key_valid ? *reinterpret_cast<const uint4 *>(vp + kc * 16 + half * 8) : z);
+    vf[kc] = as_h16x8(key_valid ? *reinterpret_cast<const uint4 *>(vp + kc * 16 + half * 8) : z);
   }
   {   // the workgroup's K tile (rows past the region's end are zero-filled)
     DmaRows<HD, BNW> kd;
     kd.init(wave, lane, (int)(kld * 2));
     kd.load(ktile,
-            reinterpret_cast<const bf16 *>(ctx ? a.k_ctx : a.k_own) +
+            reinterpret_cast<const h16 *>(ctx ? a.k_ctx : a.k_own) +
                 (long)(own0 + it.key_start) * kld + (long)g * HD,
             (int)(kld * 2), nkeys, wave);
   }
@@ -818,9 +818,9 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
     const int s0 = cs0;
     const int len = clen;
     const __amdgpu_buffer_rsrc_t rq =
-        make_rsrc_u(reinterpret_cast<const bf16 *>(a.q) + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
+        make_rsrc_u(reinterpret_cast<const h16 *>(a.q) + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
     const __amdgpu_buffer_rsrc_t rd =
-        make_rsrc_u(reinterpret_cast<const bf16 *>(a.dout) + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
+        make_rsrc_u(reinterpret_cast<const h16 *>(a.dout) + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
     const int ft = cf / G, fj = cf - ft * G;
     const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_u32(st) + wave * 1024);
 #pragma unroll
@@ -912,8 +912,8 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
           const char *qrow = qs + rb * 32 * HD * 2 + fo[kc];
-          st = mfma(as_bf16x8(*reinterpret_cast<const uint4 *>(qrow)), lds_frag_at(kt + fo[kc]), st);
-          dpt = mfma(as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + TILE)), vf[kc], dpt);
+          st = mma16<E>(as_h16x8(*reinterpret_cast<const uint4 *>(qrow)), lds_frag_at(kt + fo[kc]), st);
+          dpt = mma16<E>(as_h16x8(*reinterpret_cast<const uint4 *>(qrow + TILE)), vf[kc], dpt);
         }
         // three fragment reads (Q, K, dO) ahead of each pair of products
         __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
@@ -949,16 +949,16 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
           probs(std::false_type{});
         else
           probs(std::true_type{});
-        const bf16x8 p0 = pack8(pv), p1 = pack8(pv + 8);
-        const bf16x8 s0 = pack8(dsv), s1 = pack8(dsv + 8);
+        const h16x8 p0 = pack8<E>(pv), p1 = pack8<E>(pv + 8);
+        const h16x8 s0 = pack8<E>(dsv), s1 = pack8<E>(dsv + 8);
         // dV += Pᵀ dO and dK += dSᵀ Q over the block's 32 rows.
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          dv[db] = mfma(p0, sw_tr_frag<HD>(dos, rb * 32, db * 32, lane), dv[db]);
-          dv[db] = mfma(p1, sw_tr_frag<HD>(dos, rb * 32 + 16, db * 32, lane), dv[db]);
-          dk[db] = mfma(s0, sw_tr_frag<HD>(qs, rb * 32, db * 32, lane), dk[db]);
-          dk[db] = mfma(s1, sw_tr_frag<HD>(qs, rb * 32 + 16, db * 32, lane), dk[db]);
+          dv[db] = mma16<E>(p0, sw_tr_frag<HD>(dos, rb * 32, db * 32, lane), dv[db]);
+          dv[db] = mma16<E>(p1, sw_tr_frag<HD>(dos, rb * 32 + 16, db * 32, lane), dv[db]);
+          dk[db] = mma16<E>(s0, sw_tr_frag<HD>(qs, rb * 32, db * 32, lane), dk[db]);
+          dk[db] = mma16<E>(s1, sw_tr_frag<HD>(qs, rb * 32 + 16, db * 32, lane), dk[db]);
         }
         // transposed dO / Q reads three products ahead
         __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
@@ -1000,8 +1000,8 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_bf16_kernel(BwdKVArgs a) {
         atomicAdd(a.acc_dk + off, gk);
         atomicAdd(a.acc_dv + off, gv);
       } else {
-        reinterpret_cast<bf16 *>(a.dk_own)[off] = (bf16)gk;
-        reinterpret_cast<bf16 *>(a.dv_own)[off] = (bf16)gv;
+        reinterpret_cast<h16 *>(a.dk_own)[off] = rnd<E>(gk);
+        reinterpret_cast<h16 *>(a.dv_own)[off] = rnd<E>(gv);
       }
     }
 }
@@ -1023,7 +1023,7 @@ static hipError_t pre_t(const void *o, const void *dout, const float *lse, float
 hipError_t launch_bwd_pre(int dtype, int hd, const void *o, const void *dout, const float *lse,
                           float *Dneg, float *lsn, long T, int Hq, float scale, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (dtype == 1) {   // fp32 only: the bf16 dQ kernels form these terms themselves
+  if (dtype == 1) {   // fp32 only: the h16 dQ kernels form these terms themselves
     if (hd == 64) return pre_t<float, 64>(o, dout, lse, Dneg, lsn, T, Hq, scale, s);
     if (hd == 128) return pre_t<float, 128>(o, dout, lse, Dneg, lsn, T, Hq, scale, s);
   }
@@ -1049,9 +1049,12 @@ hipError_t launch_split_reduce(float *acc, const float *slices, int n_slices, lo
 hipError_t launch_cast(int dtype, const float *src, void *dst, long n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   long blocks = (n + 1023) / 1024;
-  if (dtype == 0)
-    hipLaunchKernelGGL(cast_kernel<bf16>, dim3(blocks), dim3(256), 0, s, src,
-                       reinterpret_cast<bf16 *>(dst), n);
+  if (dtype == 2)
+    hipLaunchKernelGGL(cast_kernel<f16>, dim3(blocks), dim3(256), 0, s, src,
+                       reinterpret_cast<f16 *>(dst), n);
+  else if (dtype == 0)
+    hipLaunchKernelGGL(cast_kernel<h16>, dim3(blocks), dim3(256), 0, s, src,
+                       reinterpret_cast<h16 *>(dst), n);
   else
     hipLaunchKernelGGL(cast_kernel<float>, dim3(blocks), dim3(256), 0, s, src,
                        reinterpret_cast<float *>(dst), n);
@@ -1066,16 +1069,22 @@ static hipError_t dq_f32(const BwdQArgs &a, int n, hipStream_t s) {
 
 hipError_t launch_bwd_dq(int dtype, int hd, const BwdQArgs &a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  if (dtype == 0) {
+  if (dtype == 0 || dtype == 2) {   // bf16, fp16
+    if (hd == 512) return launch_bwd_dq_d512(dtype, a, n, s);
     if (hd == 64) {
-      hipLaunchKernelGGL((bwd_dq_bf16_kernel<64>), dim3(n), dim3(256), 0, s, a);
+      if (dtype == 2)
+        hipLaunchKernelGGL((bwd_dq_h16_kernel<f16, 64>), dim3(n), dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((bwd_dq_h16_kernel<h16, 64>), dim3(n), dim3(256), 0, s, a);
       return hipGetLastError();
     }
     if (hd == 128) {
-      hipLaunchKernelGGL((bwd_dq_bf16_kernel<128>), dim3(n), dim3(256), 0, s, a);
+      if (dtype == 2)
+        hipLaunchKernelGGL((bwd_dq_h16_kernel<f16, 128>), dim3(n), dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((bwd_dq_h16_kernel<h16, 128>), dim3(n), dim3(256), 0, s, a);
       return hipGetLastError();
     }
-    if (hd == 512) return launch_bwd_dq_d512(a, n, s);
   } else {
     if (hd == 64) return dq_f32<64>(a, n, s);
     if (hd == 128) return dq_f32<128>(a, n, s);
@@ -1091,16 +1100,22 @@ static hipError_t dkdv_f32(const BwdKVArgs &a, int n, hipStream_t s) {
 
 hipError_t launch_bwd_dkdv(int dtype, int hd, const BwdKVArgs &a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  if (dtype == 0) {
+  if (dtype == 0 || dtype == 2) {   // bf16, fp16
+    if (hd == 512) return launch_bwd_dkdv_d512(dtype, a, n, s);
     if (hd == 64) {
-      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<64, 32, 2>), dim3(n), dim3(256), 0, s, a);
+      if (dtype == 2)
+        hipLaunchKernelGGL((bwd_dkdv_h16_kernel<f16, 64, 32, 2>), dim3(n), dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((bwd_dkdv_h16_kernel<h16, 64, 32, 2>), dim3(n), dim3(256), 0, s, a);
       return hipGetLastError();
     }
     if (hd == 128) {
-      hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<128, 32, 2>), dim3(n), dim3(256), 0, s, a);
+      if (dtype == 2)
+        hipLaunchKernelGGL((bwd_dkdv_h16_kernel<f16, 128, 32, 2>), dim3(n), dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((bwd_dkdv_h16_kernel<h16, 128, 32, 2>), dim3(n), dim3(256), 0, s, a);
       return hipGetLastError();
     }
-    if (hd == 512) return launch_bwd_dkdv_d512(a, n, s);
   } else {
     if (hd == 64) return dkdv_f32<64>(a, n, s);
     if (hd == 128) return dkdv_f32<128>(a, n, s);

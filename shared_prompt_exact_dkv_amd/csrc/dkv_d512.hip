@@ -51,19 +51,21 @@ __device__ __forceinline__ void xch_put(float *area, const f32x16 &x, int lane) 
 __device__ __forceinline__ float4 xch_quad(const float *area, int q, int lane) {
   return *reinterpret_cast<const float4 *>(area + q * 256 + lane * 4);
 }
-// Two floats as a bf16 pair (x in the low half), and four such words as 8 bf16.
-__device__ __forceinline__ uint32_t pack2(float x, float y) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Two floats as an E pair (x in the low half, nearest even), and four such words as an
+// 8-element fragment.
+template <typename E> __device__ __forceinline__ uint32_t pack2(float x, float y) {
+  typedef E e16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, e16x2));
 }
-__device__ __forceinline__ bf16x8 words8(const uint32_t *w) {
-  return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+__device__ __forceinline__ h16x8 words8(const uint32_t *w) {
+  return __builtin_bit_cast(h16x8, make_uint4(w[0], w[1], w[2], w[3]));
 }
 }  // namespace
 
 // ------------------------------------------------------------------- forward --
 
+template <typename E>
 __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
   constexpr int BN = 32;
   constexpr int TILE = BN * HD * 2;      // 32 KB
@@ -94,11 +96,11 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
   const long kld = (long)a.Hkv * HD;
   const int d0 = dh * (HD / 2);
 
-  const bf16 *qptr = reinterpret_cast<const bf16 *>(a.q) + (long)(seq0 + t0 + tok) * qld + (long)h * HD + d0;
-  bf16x8 qf[NKH];
+  const h16 *qptr = reinterpret_cast<const h16 *>(a.q) + (long)(seq0 + t0 + tok) * qld + (long)h * HD + d0;
+  h16x8 qf[NKH];
 #pragma unroll
   for (int kc = 0; kc < NKH; ++kc)
-    qf[kc] = as_bf16x8(*reinterpret_cast<const uint4 *>(qptr + kc * 16 + half * 8));
+    qf[kc] = as_h16x8(*reinterpret_cast<const uint4 *>(qptr + kc * 16 + half * 8));
 
   const float sf = a.scale * kLog2e;
   f32x16 acc[NDH];
@@ -114,15 +116,15 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
   const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
   const int n_tiles = n_ctx + n_own;
 
-  const bf16 *kc_base = reinterpret_cast<const bf16 *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
-  const bf16 *vc_base = reinterpret_cast<const bf16 *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
-  const bf16 *ko_base = reinterpret_cast<const bf16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
-  const bf16 *vo_base = reinterpret_cast<const bf16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
+  const h16 *kc_base = reinterpret_cast<const h16 *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
+  const h16 *vc_base = reinterpret_cast<const h16 *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
+  const h16 *ko_base = reinterpret_cast<const h16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
+  const h16 *vo_base = reinterpret_cast<const h16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
   const int kld_b = (int)(kld * 2);
   // Waves 0-3 fetch the K tile, waves 4-7 the V tile.
   const int dw = wave & 3, isv = wave >> 2;
-  const bf16 *c_base = isv ? vc_base : kc_base;
-  const bf16 *o_base = isv ? vo_base : ko_base;
+  const h16 *c_base = isv ? vc_base : kc_base;
+  const h16 *o_base = isv ? vo_base : ko_base;
   DmaRows<HD, BN> dma;
   dma.init(dw, lane, kld_b);
   // Tile i goes to stage i % 2: waves 0-3 fetch its K rows, waves 4-7 its V rows.
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
     f32x16 part = zero16();
 #pragma unroll
     for (int kc = 0; kc < NKH; ++kc)
-      part = mfma(sw.frag(lds_u32(ks) + dh * 512, kc), qf[kc], part);
+      part = mma16<E>(sw.frag(lds_u32(ks) + dh * 512, kc), qf[kc], part);
     // one fragment read two products ahead
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
         for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    uint32_t pw[8];   // P as bf16 pairs
+    uint32_t pw[8];   // P as h16 pairs
     float rs = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; v += 2) {
@@ -219,15 +221,15 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
       const float t1 = fast_exp2(fmaf(s[v + 1], sf, -m_use));
       rs += t0;
       rs += t1;
-      pw[v / 2] = pack2(t0, t1);
+      pw[v / 2] = pack2<E>(t0, t1);
     }
     l_run += rs;
-    const bf16x8 p0 = words8(pw), p1 = words8(pw + 4);
+    const h16x8 p0 = words8(pw), p1 = words8(pw + 4);
     // Oᵀ += Vᵀ Pᵀ over this wave's half of the head dim.
 #pragma unroll
     for (int db = 0; db < NDH; ++db) {
-      acc[db] = mfma(sw.trfrag(lds_u32(vs) + d0 * 2, 0, db), p0, acc[db]);
-      acc[db] = mfma(sw.trfrag(lds_u32(vs) + d0 * 2, 16, db), p1, acc[db]);
+      acc[db] = mma16<E>(sw.trfrag(lds_u32(vs) + d0 * 2, 0, db), p0, acc[db]);
+      acc[db] = mma16<E>(sw.trfrag(lds_u32(vs) + d0 * 2, 16, db), p1, acc[db]);
     }
     // one transposed fragment (two reads) two products ahead
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -267,30 +269,34 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
   const float l = pair_sum(l_run);
   const float inv = 1.f / l;
   if (row_valid) {
-    bf16 *optr = reinterpret_cast<bf16 *>(a.o) + (long)(seq0 + t0 + tok) * qld + (long)h * HD + d0;
+    h16 *optr = reinterpret_cast<h16 *>(a.o) + (long)(seq0 + t0 + tok) * qld + (long)h * HD + d0;
 #pragma unroll
     for (int db = 0; db < NDH; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int dim = db * 32 + 8 * i + 4 * half;
-        bf16x4 w;
+        h16x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * i + e] * inv);
-        *reinterpret_cast<bf16x4 *>(optr + dim) = w;
+        for (int e = 0; e < 4; ++e) w[e] = rnd<E>(acc[db][4 * i + e] * inv);
+        *reinterpret_cast<h16x4 *>(optr + dim) = w;
       }
     if (half == 0 && dh == 0)
       a.lse[(long)h * a.lse_ld + seq0 + t0 + tok] = (m_run + fast_log2(l)) * kLn2;
   }
 }
 
-hipError_t launch_fwd_d512(const FwdArgs &a, int n, hipStream_t s) {
+hipError_t launch_fwd_d512(int dtype, const FwdArgs &a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fwd_d512_kernel, dim3(n), dim3(512), 0, s, a);
+  if (dtype == 2)
+    hipLaunchKernelGGL(fwd_d512_kernel<f16>, dim3(n), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(fwd_d512_kernel<h16>, dim3(n), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------ dQ --
 
+template <typename E>
 __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
   constexpr int BN = 32;
   constexpr int TILE = BN * HD * 2;      // 32 KB
@@ -323,12 +329,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
   const long kld = (long)a.Hkv * HD;
   const long qrow = (long)(seq0 + t0 + tok);
 
-  const bf16 *xptr = reinterpret_cast<const bf16 *>(role == 0 ? a.q : a.dout) + qrow * qld +
+  const h16 *xptr = reinterpret_cast<const h16 *>(role == 0 ? a.q : a.dout) + qrow * qld +
                      (long)h * HD + dh * (HD / 2);
-  bf16x8 xf[NKH];
+  h16x8 xf[NKH];
 #pragma unroll
   for (int kc = 0; kc < NKH; ++kc)
-    xf[kc] = as_bf16x8(*reinterpret_cast<const uint4 *>(xptr + kc * 16 + half * 8));
+    xf[kc] = as_h16x8(*reinterpret_cast<const uint4 *>(xptr + kc * 16 + half * 8));
   const float sf = a.scale * kLog2e;
   const float lse = a.lse[(long)h * a.lse_ld + qrow];
   const float lse2 = lse * kLog2e;
@@ -337,13 +343,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
   // sums its half against O (the two lanes of a row a quarter each), puts it in the
   // exchange area, and every wave adds the halves 0 + 1 after a barrier.
   if (role == 1) {
-    const bf16 *optr = reinterpret_cast<const bf16 *>(a.o) + qrow * qld + (long)h * HD + dh * (HD / 2);
+    const h16 *optr = reinterpret_cast<const h16 *>(a.o) + qrow * qld + (long)h * HD + dh * (HD / 2);
     float dh_sum = 0.f;
 #pragma unroll
     for (int kc = 0; kc < NKH; ++kc) {
-      const bf16x8 o8 = as_bf16x8(*reinterpret_cast<const uint4 *>(optr + kc * 16 + half * 8));
+      const h16x8 o8 = as_h16x8(*reinterpret_cast<const uint4 *>(optr + kc * 16 + half * 8));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dh_sum += (float)o8[e] * (float)xf[kc][e];
+      for (int e = 0; e < 8; ++e) dh_sum += val<E>(o8[e]) * val<E>(xf[kc][e]);
     }
     dh_sum = pair_sum(dh_sum);
     if (half == 0) xch[dh * 32 + col] = dh_sum;
@@ -369,14 +375,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
   const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
   const int n_tiles = n_ctx + n_own;
 
-  const bf16 *kc_base = reinterpret_cast<const bf16 *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
-  const bf16 *vc_base = reinterpret_cast<const bf16 *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
-  const bf16 *ko_base = reinterpret_cast<const bf16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
-  const bf16 *vo_base = reinterpret_cast<const bf16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
+  const h16 *kc_base = reinterpret_cast<const h16 *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
+  const h16 *vc_base = reinterpret_cast<const h16 *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
+  const h16 *ko_base = reinterpret_cast<const h16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
+  const h16 *vo_base = reinterpret_cast<const h16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
   const int kld_b = (int)(kld * 2);
   // Waves 0-3 fetch the K tile, waves 4-7 the V tile.
-  const bf16 *c_base = grp ? vc_base : kc_base;
-  const bf16 *o_base = grp ? vo_base : ko_base;
+  const h16 *c_base = grp ? vc_base : kc_base;
+  const h16 *o_base = grp ? vo_base : ko_base;
   DmaRows<HD, BN> dma;
   dma.init(wq, lane, kld_b);
   auto issue = [&](int i) {
@@ -415,7 +421,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
     f32x16 part = zero16();
 #pragma unroll
     for (int kc = 0; kc < NKH; ++kc)
-      part = mfma(sw.frag(lds_u32(op) + dh * 512, kc), xf[kc], part);
+      part = mma16<E>(sw.frag(lds_u32(op) + dh * 512, kc), xf[kc], part);
     // one fragment read two products ahead
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
@@ -430,7 +436,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
                            (wl >= 0 && kpos0 < qmax - wl);
     // S = partial 0 + partial 1 and dP = partial 2 + partial 3 are formed by the four
     // waves of the group a quad each (C-tile elements 4 wq .. 4 wq + 3): this wave reads
-    // quad wq of the four partials, turns it into dS, and writes it as bf16 into quad wq
+    // quad wq of the four partials, turns it into dS, and writes it as h16 into quad wq
     // of its own slot (which no other wave reads); after a barrier every wave reads the
     // four quads of dS back as its MFMA operand.  The visibility test (keys of this
     // lane's row as tile offsets [lo, hi), compared without branches) is compiled only
@@ -456,7 +462,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
       }
       // 8 bytes per lane, packed (consecutive lanes on consecutive banks)
       *reinterpret_cast<uint2 *>(xch + wq * 1024 + q * 256 + lane * 2) =
-          make_uint2(pack2(dsq[0], dsq[1]), pack2(dsq[2], dsq[3]));
+          make_uint2(pack2<E>(dsq[0], dsq[1]), pack2<E>(dsq[2], dsq[3]));
     };
     if (need_mask)
       grads(std::true_type{});
@@ -467,13 +473,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
 #pragma unroll
     for (int w = 0; w < 4; ++w)
       dd[w] = *reinterpret_cast<const uint2 *>(xch + w * 1024 + w * 256 + lane * 2);
-    const bf16x8 d0 = __builtin_bit_cast(bf16x8, make_uint4(dd[0].x, dd[0].y, dd[1].x, dd[1].y));
-    const bf16x8 d1 = __builtin_bit_cast(bf16x8, make_uint4(dd[2].x, dd[2].y, dd[3].x, dd[3].y));
+    const h16x8 d0 = __builtin_bit_cast(h16x8, make_uint4(dd[0].x, dd[0].y, dd[1].x, dd[1].y));
+    const h16x8 d1 = __builtin_bit_cast(h16x8, make_uint4(dd[2].x, dd[2].y, dd[3].x, dd[3].y));
     // dQᵀ += Kᵀ dSᵀ over this wave's quarter of the head dim.
 #pragma unroll
     for (int db = 0; db < NDQ; ++db) {
-      acc[db] = mfma(sw.trfrag(lds_u32(ks) + dq0 * 2, 0, db), d0, acc[db]);
-      acc[db] = mfma(sw.trfrag(lds_u32(ks) + dq0 * 2, 16, db), d1, acc[db]);
+      acc[db] = mma16<E>(sw.trfrag(lds_u32(ks) + dq0 * 2, 0, db), d0, acc[db]);
+      acc[db] = mma16<E>(sw.trfrag(lds_u32(ks) + dq0 * 2, 16, db), d1, acc[db]);
     }
     // one transposed fragment (two reads) two products ahead
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -486,28 +492,32 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
   }
 
   if (row_valid) {
-    bf16 *optr = reinterpret_cast<bf16 *>(a.dq) + qrow * qld + (long)h * HD + dq0;
+    h16 *optr = reinterpret_cast<h16 *>(a.dq) + qrow * qld + (long)h * HD + dq0;
 #pragma unroll
     for (int db = 0; db < NDQ; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int dim = db * 32 + 8 * i + 4 * half;
-        bf16x4 w;
+        h16x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * i + e] * a.scale);
-        *reinterpret_cast<bf16x4 *>(optr + dim) = w;
+        for (int e = 0; e < 4; ++e) w[e] = rnd<E>(acc[db][4 * i + e] * a.scale);
+        *reinterpret_cast<h16x4 *>(optr + dim) = w;
       }
   }
 }
 
-hipError_t launch_bwd_dq_d512(const BwdQArgs &a, int n, hipStream_t s) {
+hipError_t launch_bwd_dq_d512(int dtype, const BwdQArgs &a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_dq_d512_kernel, dim3(n), dim3(512), 0, s, a);
+  if (dtype == 2)
+    hipLaunchKernelGGL(bwd_dq_d512_kernel<f16>, dim3(n), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(bwd_dq_d512_kernel<h16>, dim3(n), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
 // --------------------------------------------------------------------- dK/dV --
 
+template <typename E>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
   constexpr int BM = 32;                 // query rows per step
   constexpr int TILE = BM * HD * 2;      // 32 KB: one row per 1 KB DMA block
@@ -542,15 +552,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
   const float sf = a.scale * kLog2e;
   // K (role 0) or V (role 1) rows of the group's keys, this wave's head-dim half;
   // keys past the tile's end read as zeros (buffer range check).
-  const bf16 *xp = reinterpret_cast<const bf16 *>(
+  const h16 *xp = reinterpret_cast<const h16 *>(
                        role == 0 ? (ctx ? a.k_ctx : a.k_own) : (ctx ? a.v_ctx : a.v_own)) +
                    (long)(own0 + it.key_start + gk0) * kld + (long)g * HD + dh * (HD / 2);
   const __amdgpu_buffer_rsrc_t rk =
       make_rsrc_u(xp, nkeys_g > 0 ? (uint32_t)nkeys_g * (uint32_t)(kld * 2) : 0u);
-  bf16x8 xf[NKH];
+  h16x8 xf[NKH];
 #pragma unroll
   for (int kc = 0; kc < NKH; ++kc)
-    xf[kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+    xf[kc] = __builtin_bit_cast(h16x8, __builtin_amdgcn_raw_buffer_load_b128(
                                             rk, col * (int)(kld * 2) + (kc * 16 + half * 8) * 2, 0, 0));
   const int kpos = kbase + it.key_start + key;
   const int f_vis_lo = key_valid ? max(0, (kpos - P) * G) : 0x7fffffff;
@@ -609,7 +619,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
   const int step4 = (4 / G) * qld_b + r4 * (HD * 2);     // their byte step before a wrap
   // Waves 0-3 fetch the step's Q rows, waves 4-7 its dO rows: row r of the step (a
   // flattened (token, head) row) fills 1 KB block r, written by wave r % 4.
-  const bf16 *xsrc = reinterpret_cast<const bf16 *>(grp ? a.dout : a.q);
+  const h16 *xsrc = reinterpret_cast<const h16 *>(grp ? a.dout : a.q);
   // The first head-dim half of each role starts its partial at -LSE / scale (scores)
   // or -D (dP) of the step's rows: lane l fetches row l % 32's value into a register
   // one step ahead, and the wave spreads it over the C layout with ds_bpermute.
@@ -703,7 +713,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
     const char *op = role == 0 ? qs : dos;
 #pragma unroll
     for (int kc = 0; kc < NKH; ++kc)
-      part = mfma(sw.frag(lds_u32(op) + dh * 512, kc), xf[kc], part);
+      part = mma16<E>(sw.frag(lds_u32(op) + dh * 512, kc), xf[kc], part);
     // one fragment read two products ahead
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
@@ -722,7 +732,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
                       ((kpb - P) * G <= flo) && (wl < 0 || fend <= (kpa - P + wl + 1) * G);
     // S = partial 0 + partial 1 and dP - D = partial 2 + partial 3 are formed by the four
     // waves of the group a quad each (C-tile elements 4 wq .. 4 wq + 3): this wave reads
-    // quad wq of the four partials, turns it into P and dS, and writes them as bf16 into
+    // quad wq of the four partials, turns it into P and dS, and writes them as h16 into
     // quad wq of its own slot (which no other wave reads); after a barrier every wave
     // reads the four quads of P and dS back as its MFMA operands.  The visibility test
     // is compiled only into the variant for blocks that straddle a mask edge or a range
@@ -748,8 +758,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
         dq[e] = p * dpt[e];
       }
       *reinterpret_cast<uint4 *>(xch + wq * 1024 + q * 256 + lane * 4) =
-          make_uint4(pack2(pq[0], pq[1]), pack2(pq[2], pq[3]), pack2(dq[0], dq[1]),
-                     pack2(dq[2], dq[3]));
+          make_uint4(pack2<E>(pq[0], pq[1]), pack2<E>(pq[2], pq[3]), pack2<E>(dq[0], dq[1]),
+                     pack2<E>(dq[2], dq[3]));
     };
     if (full)
       probs(std::false_type{});
@@ -760,17 +770,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
 #pragma unroll
     for (int w = 0; w < 4; ++w)
       pd[w] = *reinterpret_cast<const uint4 *>(xch + w * 1024 + w * 256 + lane * 4);
-    const bf16x8 p0 = __builtin_bit_cast(bf16x8, make_uint4(pd[0].x, pd[0].y, pd[1].x, pd[1].y));
-    const bf16x8 p1 = __builtin_bit_cast(bf16x8, make_uint4(pd[2].x, pd[2].y, pd[3].x, pd[3].y));
-    const bf16x8 s0 = __builtin_bit_cast(bf16x8, make_uint4(pd[0].z, pd[0].w, pd[1].z, pd[1].w));
-    const bf16x8 s1 = __builtin_bit_cast(bf16x8, make_uint4(pd[2].z, pd[2].w, pd[3].z, pd[3].w));
+    const h16x8 p0 = __builtin_bit_cast(h16x8, make_uint4(pd[0].x, pd[0].y, pd[1].x, pd[1].y));
+    const h16x8 p1 = __builtin_bit_cast(h16x8, make_uint4(pd[2].x, pd[2].y, pd[3].x, pd[3].y));
+    const h16x8 s0 = __builtin_bit_cast(h16x8, make_uint4(pd[0].z, pd[0].w, pd[1].z, pd[1].w));
+    const h16x8 s1 = __builtin_bit_cast(h16x8, make_uint4(pd[2].z, pd[2].w, pd[3].z, pd[3].w));
     // dV += Pᵀ dO and dK += dSᵀ Q over this wave's quarter of the head dim.
 #pragma unroll
     for (int db = 0; db < NDQ; ++db) {
-      dv[db] = mfma(p0, sw.trfrag(lds_u32(dos) + dq0 * 2, 0, db), dv[db]);
-      dv[db] = mfma(p1, sw.trfrag(lds_u32(dos) + dq0 * 2, 16, db), dv[db]);
-      dk[db] = mfma(s0, sw.trfrag(lds_u32(qs) + dq0 * 2, 0, db), dk[db]);
-      dk[db] = mfma(s1, sw.trfrag(lds_u32(qs) + dq0 * 2, 16, db), dk[db]);
+      dv[db] = mma16<E>(p0, sw.trfrag(lds_u32(dos) + dq0 * 2, 0, db), dv[db]);
+      dv[db] = mma16<E>(p1, sw.trfrag(lds_u32(dos) + dq0 * 2, 16, db), dv[db]);
+      dk[db] = mma16<E>(s0, sw.trfrag(lds_u32(qs) + dq0 * 2, 0, db), dk[db]);
+      dk[db] = mma16<E>(s1, sw.trfrag(lds_u32(qs) + dq0 * 2, 16, db), dk[db]);
     }
     // one transposed fragment (two reads) two products ahead
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -803,15 +813,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
         atomicAdd(a.acc_dk + off, gk);
         atomicAdd(a.acc_dv + off, gv);
       } else {
-        reinterpret_cast<bf16 *>(a.dk_own)[off] = (bf16)gk;
-        reinterpret_cast<bf16 *>(a.dv_own)[off] = (bf16)gv;
+        reinterpret_cast<h16 *>(a.dk_own)[off] = rnd<E>(gk);
+        reinterpret_cast<h16 *>(a.dv_own)[off] = rnd<E>(gv);
       }
     }
 }
 
-hipError_t launch_bwd_dkdv_d512(const BwdKVArgs &a, int n, hipStream_t s) {
+hipError_t launch_bwd_dkdv_d512(int dtype, const BwdKVArgs &a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_dkdv_d512_kernel, dim3(n), dim3(512), 0, s, a);
+  if (dtype == 2)
+    hipLaunchKernelGGL(bwd_dkdv_d512_kernel<f16>, dim3(n), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(bwd_dkdv_d512_kernel<h16>, dim3(n), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -2,9 +2,10 @@
 //
 // Matrix products use the CDNA4 32x32 MFMA forms:
 //   bf16: v_mfma_f32_32x32x16_bf16  A[32x16] * B[16x32] -> C[32x32] fp32
+//   fp16: v_mfma_f32_32x32x16_f16   (same shapes and lane layout)
 //   fp32: v_mfma_f32_32x32x2_f32    A[32x2]  * B[2x32]  -> C[32x32] fp32
 // Lane layout (wave64, lane l, col = l % 32, half = l / 32):
-//   A operand: row = col, k = half * KL + [0, KL)      (KL = 8 bf16 / 1 fp32)
+//   A operand: row = col, k = half * KL + [0, KL)      (KL = 8 16-bit / 1 fp32)
 //   B operand: column = col, same k split
 //   C: column = col; element v (0..15) is row 8*(v/4) + 4*half + (v%4)
 // So a C tile read back per lane is "one column, 16 rows"; the kernels compute
@@ -12,7 +13,7 @@
 // the softmax, and feed the C tile straight back as the B operand of the next
 // product.  A C tile used as a k-operand pairs lane-half `half`, element e with row
 //   kappa(half, e) = 8*(e/4) + 4*half + (e%4)     (within a 16-row slice)
-// and the other operand is read in that same order (the transpose read of the bf16
+// and the other operand is read in that same order (the transpose read of the h16
 // tiles, sw_tr_frag in dkv_tiles.h; single elements in the fp32 kernels).
 #pragma once
 
@@ -21,25 +22,37 @@
 
 namespace dkv {
 
-typedef __bf16 bf16;
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+// 16-bit tensors (bf16 or fp16) are moved as h16 payloads: global rows, LDS tiles and
+// MFMA fragments never look at the bits.  A 16-bit kernel's element type E (h16 itself
+// for bf16, f16 for fp16) interprets them: mma16<E> runs that type's MFMA, rnd<E> /
+// pack8<E> round fp32 values into payloads (nearest even) and val<E> reads a payload
+// element as fp32.
+typedef __bf16 h16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 h16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 h16x4;
+typedef _Float16 f16;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 static constexpr float kLog2e = 1.4426950408889634f;
 static constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+template <typename E> __device__ __forceinline__ f32x16 mma16(h16x8 a, h16x8 b, f32x16 c);
+template <> __device__ __forceinline__ f32x16 mma16<h16>(h16x8 a, h16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x16 mma16<f16>(h16x8 a, h16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x16 mfma(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
 template <typename T> struct Mfma;
-template <> struct Mfma<bf16> {
-  using frag = bf16x8;
+template <> struct Mfma<h16> {
+  using frag = h16x8;
   static constexpr int K = 16;   // contraction depth of one MFMA
   static constexpr int KL = 8;   // k values per lane
 };
@@ -59,21 +72,44 @@ __device__ __forceinline__ f32x16 zero16() {
 // Row index (within a 32-row C tile) of element v held by lane-half `half`.
 __device__ __forceinline__ int c_row(int v, int half) { return 8 * (v >> 2) + 4 * half + (v & 3); }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ h16x8 as_h16x8(uint4 u) { return __builtin_bit_cast(h16x8, u); }
 
+// Element conversions of the simple kernels (cast, preprocess, layout), whose tensors
+// are typed by their element type: float, h16 (bf16) or f16.
 __device__ __forceinline__ float to_f32(float x) { return x; }
-__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(h16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(f16 x) { return (float)x; }
 
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
-template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ h16 from_f32<h16>(float x) { return (h16)x; }
+template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }
 
-// Pack eight fp32 values into a bf16 fragment (round to nearest even).
-__device__ __forceinline__ bf16x8 pack8(const float *x) {
-  bf16x8 r;
+// Payload conversions of the MFMA kernels (see h16 above).
+template <typename E> __device__ __forceinline__ float val(h16 x);
+template <> __device__ __forceinline__ float val<h16>(h16 x) { return (float)x; }
+template <> __device__ __forceinline__ float val<f16>(h16 x) {
+  return (float)__builtin_bit_cast(f16, x);
+}
+template <typename E> __device__ __forceinline__ h16 rnd(float x);
+template <> __device__ __forceinline__ h16 rnd<h16>(float x) { return (h16)x; }
+template <> __device__ __forceinline__ h16 rnd<f16>(float x) {
+  return __builtin_bit_cast(h16, (f16)x);
+}
+
+// Pack eight fp32 values into an E fragment (round to nearest even).
+template <typename E> __device__ __forceinline__ h16x8 pack8(const float *x) {
+  if constexpr (sizeof(E) == 2 && !__is_same(E, h16)) {
+    f16x8 r;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (bf16)x[i];
-  return r;
+    for (int i = 0; i < 8; ++i) r[i] = (f16)x[i];
+    return __builtin_bit_cast(h16x8, r);
+  } else {
+    h16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (h16)x[i];
+    return r;
+  }
 }
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
@@ -106,7 +142,7 @@ __device__ __forceinline__ void kahan_add(f32x16 &sum, f32x16 &comp, const f32x1
   }
 }
 
-// Exponent domain of the fp32 kernels' softmax.  The bf16 kernels run in base 2 with
+// Exponent domain of the fp32 kernels' softmax.  The 16-bit kernels run in base 2 with
 // the hardware exp2 (logits pre-multiplied by scale*log2(e)); the fp32 path, whose
 // results are checked at 1e-5, runs in base e with the accurate expf/logf so that
 // neither the logits nor the stored natural-log LSE pass through a rounded log2(e)

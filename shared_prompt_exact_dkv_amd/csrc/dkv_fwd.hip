@@ -1,5 +1,5 @@
 // dkv_fwd.hip -- forward kernels: online softmax over a shared-prompt KV region and a
-// per-sequence KV region in one pass ("DualKV", arXiv 2605.15422, §3.1).  bf16 at head
+// per-sequence KV region in one pass ("DualKV", arXiv 2605.15422, §3.1).  h16 at head
 // dims 64 / 128 runs fwd_bf16_kernel (dkv_fwd_bf16.h), head dim 512 the kernels of
 // dkv_d512.hip; this file holds the fp32 kernel and the dispatch.
 //
@@ -210,16 +210,22 @@ static hipError_t launch_fwd_f32(const FwdArgs &a, int n, hipStream_t s) {
 
 hipError_t launch_fwd(int dtype, int hd, const FwdArgs &a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  if (dtype == 0) {
+  if (dtype == 0 || dtype == 2) {   // bf16, fp16
+    if (hd == 512) return launch_fwd_d512(dtype, a, n, s);
     if (hd == 64) {
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, kFwdBN, 2>), dim3(n), dim3(256), 0, s, a);
+      if (dtype == 2)
+        hipLaunchKernelGGL((fwd_h16_kernel<f16, 64, kFwdBN, 2>), dim3(n), dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((fwd_h16_kernel<h16, 64, kFwdBN, 2>), dim3(n), dim3(256), 0, s, a);
       return hipGetLastError();
     }
     if (hd == 128) {
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, kFwdBN, 2>), dim3(n), dim3(256), 0, s, a);
+      if (dtype == 2)
+        hipLaunchKernelGGL((fwd_h16_kernel<f16, 128, kFwdBN, 2>), dim3(n), dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((fwd_h16_kernel<h16, 128, kFwdBN, 2>), dim3(n), dim3(256), 0, s, a);
       return hipGetLastError();
     }
-    if (hd == 512) return launch_fwd_d512(a, n, s);
   } else {
     if (hd == 64) return launch_fwd_f32<64>(a, n, s);
     if (hd == 128) return launch_fwd_f32<128>(a, n, s);

@@ -1,4 +1,4 @@
-// dkv_fwd_bf16.h -- the bf16 forward kernel template ("DualKV", arXiv 2605.15422,
+// dkv_fwd_bf16.h -- the h16 forward kernel template ("DualKV", arXiv 2605.15422,
 // §3.1): one online softmax over the shared-prompt KV region then the sequence's own
 // region.  Instantiated for head dims 64 / 128 in dkv_fwd.hip and 512 in
 // dkv_d512.hip (built with different register-placement options).
@@ -10,9 +10,9 @@
 
 namespace dkv {
 
-// ------------------------------------------------------------- bf16 kernel --
+// ------------------------------------------------------------- h16 kernel --
 //
-// The bf16 path for head dims 64 and 128 (HD = 512 has its own kernels): 64-key
+// The h16 path for head dims 64 and 128 (HD = 512 has its own kernels): 64-key
 // tiles at two waves per SIMD (WPE = 2, <= 256 registers).
 //   - K and V tiles are dense swizzled tiles filled by LDS DMA, double-buffered with
 //     one barrier per tile: the next tile streams in while the current one is
@@ -24,8 +24,8 @@ namespace dkv {
 //     kSlack (log2 units): between rescales the probabilities are exp2(t - m) with
 //     m at most kSlack below the true running maximum, i.e. bounded by 2^kSlack,
 //     and O / l and LSE = m + log2(l) are unchanged in exact arithmetic.
-template <int HD, int BN, int WPE>
-__global__ __launch_bounds__(256, WPE) void fwd_bf16_kernel(FwdArgs a) {
+template <typename E, int HD, int BN, int WPE>
+__global__ __launch_bounds__(256, WPE) void fwd_h16_kernel(FwdArgs a) {
   constexpr int TILE = BN * HD * 2;     // dense swizzled tile
   constexpr int NKC = HD / 16;     // MFMA steps over the head dim
   constexpr int NDB = HD / 32;     // 32-wide blocks of the output head dim
@@ -52,11 +52,11 @@ __global__ __launch_bounds__(256, WPE) void fwd_bf16_kernel(FwdArgs a) {
 
   const long qld = (long)a.Hq * HD;
   const long kld = (long)a.Hkv * HD;
-  const bf16 *qptr = reinterpret_cast<const bf16 *>(a.q) + (long)(seq0 + t0 + tok) * qld + (long)h * HD;
-  bf16x8 qf[NKC];
+  const h16 *qptr = reinterpret_cast<const h16 *>(a.q) + (long)(seq0 + t0 + tok) * qld + (long)h * HD;
+  h16x8 qf[NKC];
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc)
-    qf[kc] = as_bf16x8(*reinterpret_cast<const uint4 *>(qptr + kc * 16 + half * 8));
+    qf[kc] = as_h16x8(*reinterpret_cast<const uint4 *>(qptr + kc * 16 + half * 8));
 
   const float sf = a.scale * kLog2e;
   f32x16 acc[NDB];
@@ -72,10 +72,10 @@ __global__ __launch_bounds__(256, WPE) void fwd_bf16_kernel(FwdArgs a) {
   const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
   const int n_tiles = n_ctx + n_own;
 
-  const bf16 *kc_base = reinterpret_cast<const bf16 *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
-  const bf16 *vc_base = reinterpret_cast<const bf16 *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
-  const bf16 *ko_base = reinterpret_cast<const bf16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
-  const bf16 *vo_base = reinterpret_cast<const bf16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
+  const h16 *kc_base = reinterpret_cast<const h16 *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
+  const h16 *vc_base = reinterpret_cast<const h16 *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
+  const h16 *ko_base = reinterpret_cast<const h16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
+  const h16 *vo_base = reinterpret_cast<const h16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
 
   const int kld_b = (int)(kld * 2);
   DmaRows<HD, BN> dma;
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256, WPE) void fwd_bf16_kernel(FwdArgs a) {
     for (int kc = 0; kc < NKC; ++kc) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        s[kb] = mfma(sw_frag<HD>(ks, kb * 32 + col, kc, half), qf[kc], s[kb]);
+        s[kb] = mma16<E>(sw_frag<HD>(ks, kb * 32 + col, kc, half), qf[kc], s[kb]);
     }
     // K fragment reads four products ahead
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256, WPE) void fwd_bf16_kernel(FwdArgs a) {
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float rs = 0.f;
-    bf16x8 pf[2 * NKB];
+    h16x8 pf[2 * NKB];
 #pragma unroll
     for (int u = 0; u < 2 * NKB; ++u) {
       float t[8];
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256, WPE) void fwd_bf16_kernel(FwdArgs a) {
         t[e] = fast_exp2(fmaf(s[u >> 1][8 * (u & 1) + e], sf, -m_use));
         rs += t[e];
       }
-      pf[u] = pack8(t);
+      pf[u] = pack8<E>(t);
     }
     l_run += rs;
 
@@ -184,23 +184,23 @@ __global__ __launch_bounds__(256, WPE) void fwd_bf16_kernel(FwdArgs a) {
     for (int u = 0; u < 2 * NKB; ++u)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        acc[db] = mfma(sw_tr_frag<HD>(vs, 16 * u, db * 32, lane), pf[u], acc[db]);
+        acc[db] = mma16<E>(sw_tr_frag<HD>(vs, 16 * u, db * 32, lane), pf[u], acc[db]);
       }
   }
 
   const float l = pair_sum(l_run);
   const float inv = 1.f / l;
   if (row_valid) {
-    bf16 *optr = reinterpret_cast<bf16 *>(a.o) + (long)(seq0 + t0 + tok) * qld + (long)h * HD;
+    h16 *optr = reinterpret_cast<h16 *>(a.o) + (long)(seq0 + t0 + tok) * qld + (long)h * HD;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int dim = db * 32 + 8 * i + 4 * half;
-        bf16x4 w;
+        h16x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * i + e] * inv);
-        *reinterpret_cast<bf16x4 *>(optr + dim) = w;
+        for (int e = 0; e < 4; ++e) w[e] = rnd<E>(acc[db][4 * i + e] * inv);
+        *reinterpret_cast<h16x4 *>(optr + dim) = w;
       }
     if (half == 0)
       a.lse[(long)h * a.lse_ld + seq0 + t0 + tok] = (m_run + fast_log2(l)) * kLn2;

@@ -48,7 +48,7 @@ struct FwdArgs {
 };
 
 hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs &a, int n_items, hipStream_t s);
-hipError_t launch_fwd_d512(const FwdArgs &a, int n_items, hipStream_t s);
+hipError_t launch_fwd_d512(int dtype, const FwdArgs &a, int n_items, hipStream_t s);
 
 // ---- backward ----
 
@@ -82,7 +82,7 @@ struct BwdQArgs {
   float scale;
 };
 hipError_t launch_bwd_dq(int dtype, int head_dim, const BwdQArgs &a, int n_items, hipStream_t s);
-hipError_t launch_bwd_dq_d512(const BwdQArgs &a, int n_items, hipStream_t s);
+hipError_t launch_bwd_dq_d512(int dtype, const BwdQArgs &a, int n_items, hipStream_t s);
 
 // Work item of the key-parallel dK/dV kernel: one key tile of one region of one kv
 // head, against the query rows of sequences [seq_lo, seq_hi) (all of one prompt group).
@@ -119,7 +119,7 @@ struct BwdKVArgs {
 };
 hipError_t launch_bwd_dkdv(int dtype, int head_dim, const BwdKVArgs &a, int n_items,
                            hipStream_t s);
-hipError_t launch_bwd_dkdv_d512(const BwdKVArgs &a, int n_items, hipStream_t s);
+hipError_t launch_bwd_dkdv_d512(int dtype, const BwdKVArgs &a, int n_items, hipStream_t s);
 
 // ---- layout conversions (N-copy <-> single-prompt packing, first-token rows) ----
 

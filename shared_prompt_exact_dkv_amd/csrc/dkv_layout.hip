@@ -78,9 +78,13 @@ __global__ __launch_bounds__(256) void row_sum_kernel(const T *__restrict__ in, 
 hipError_t launch_row_sum(int dtype, const void *in, void *out, const RowItem *items, int n_items,
                           const int32_t *src_tab, int row_vecs, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
-  if (dtype == 0)
-    hipLaunchKernelGGL(row_sum_kernel<bf16>, dim3(n_items), dim3(256), 0, s,
-                       reinterpret_cast<const bf16 *>(in), reinterpret_cast<bf16 *>(out), items,
+  if (dtype == 2)
+    hipLaunchKernelGGL(row_sum_kernel<f16>, dim3(n_items), dim3(256), 0, s,
+                       reinterpret_cast<const f16 *>(in), reinterpret_cast<f16 *>(out), items,
+                       src_tab, row_vecs);
+  else if (dtype == 0)
+    hipLaunchKernelGGL(row_sum_kernel<h16>, dim3(n_items), dim3(256), 0, s,
+                       reinterpret_cast<const h16 *>(in), reinterpret_cast<h16 *>(out), items,
                        src_tab, row_vecs);
   else
     hipLaunchKernelGGL(row_sum_kernel<float>, dim3(n_items), dim3(256), 0, s,

@@ -2,7 +2,7 @@
 //
 // A tile is consecutive rows of one head of a token-major [rows, H, HD] tensor.  Two
 // mechanisms:
-//   - bf16 kernels: LDS DMA (buffer loads that write LDS directly) into dense tiles
+//   - h16 kernels: LDS DMA (buffer loads that write LDS directly) into dense tiles
 //     whose 16-byte chunks are swizzled per row (below); rows past a region's end
 //     read as zeros through the buffer resource's size.
 //   - fp32 kernels: 256 threads load the tile with 16-byte reads into registers (the
@@ -153,13 +153,13 @@ __device__ __forceinline__ int32_t sload_i32(const int32_t *base, int i) {
 }
 
 // 16 bytes read at a 32-bit LDS byte address.
-__device__ __forceinline__ bf16x8 lds_frag_at(uint32_t addr) {
+__device__ __forceinline__ h16x8 lds_frag_at(uint32_t addr) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) const u32x4 lu32x4;
-  return __builtin_bit_cast(bf16x8, *(lu32x4 *)(size_t)addr);
+  return __builtin_bit_cast(h16x8, *(lu32x4 *)(size_t)addr);
 }
 
-// Swizzled dense tile [row][HD] bf16: the 16-byte chunk c of row r sits in slot
+// Swizzled dense tile [row][HD] h16: the 16-byte chunk c of row r sits in slot
 // c ^ swz(r).  With rows of 16 or more chunks, swz(r) (bits r3 r2 r1 r0 of r) is
 //   ((r0 ^ r3) << 3) | (r1 << 2) | (r0 << 1) | r2,
 // a bijection on 16 consecutive rows (a 16-byte fragment read of 16 rows touches 16
@@ -180,10 +180,10 @@ template <int HD> struct Swz {
   }
 };
 
-// A-/B-operand fragment (8 bf16 of one row) of a swizzled tile: row `row`, k-chunk kc.
+// A-/B-operand fragment (8 h16 of one row) of a swizzled tile: row `row`, k-chunk kc.
 template <int HD>
-__device__ __forceinline__ bf16x8 sw_frag(const char *lds, int row, int kc, int half) {
-  return as_bf16x8(*reinterpret_cast<const uint4 *>(lds + Swz<HD>::off(row, kc * 2 + half)));
+__device__ __forceinline__ h16x8 sw_frag(const char *lds, int row, int kc, int half) {
+  return as_h16x8(*reinterpret_cast<const uint4 *>(lds + Swz<HD>::off(row, kc * 2 + half)));
 }
 
 // Transposed operand from a swizzled tile with the gfx950 transpose read
@@ -195,7 +195,7 @@ __device__ __forceinline__ bf16x8 sw_frag(const char *lds, int row, int kc, int 
 // at row0, in the kappa row order of a C tile (rows 4*half + 0..3, then
 // 8 + 4*half + 0..3).
 template <int HD>
-__device__ __forceinline__ bf16x8 sw_tr_frag(const char *lds, int row0, int col0, int lane) {
+__device__ __forceinline__ h16x8 sw_tr_frag(const char *lds, int row0, int col0, int lane) {
   const int half = lane >> 5, grp = (lane >> 4) & 1, j = lane & 15;
   const int col = col0 + 16 * grp + 4 * (j & 3);
   const int r1 = row0 + 4 * half + (j >> 2);
@@ -210,7 +210,7 @@ __device__ __forceinline__ bf16x8 sw_tr_frag(const char *lds, int row0, int col0
   s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p2);
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return __builtin_bit_cast(bf16x8, r);
+  return __builtin_bit_cast(h16x8, r);
 }
 
 // Factored fragment addresses for swizzled tiles of 1 KB rows (HD = 512).  In a
@@ -235,15 +235,15 @@ struct Sw512 {
   // tile instead of living in registers across a loop.
   __device__ __forceinline__ void opaque() { asm volatile("" : "+v"(srow), "+v"(tr[0]), "+v"(tr[1])); }
   // Same as sw_frag<512>(tile, col, kc, half) for kc = 0 .. 15 past the column base.
-  __device__ __forceinline__ bf16x8 frag(uint32_t tile, int kc) const {
+  __device__ __forceinline__ h16x8 frag(uint32_t tile, int kc) const {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) const char lchar;
     lchar *base = (lchar *)(size_t)(tile + (srow ^ ((kc & 7) << 5)));
-    return __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) u32x4 *)(base + (kc >> 3) * 256));
+    return __builtin_bit_cast(h16x8, *(const __attribute__((address_space(3))) u32x4 *)(base + (kc >> 3) * 256));
   }
   // Same as sw_tr_frag<512>(tile, row0, 32 db past the column base, lane), row0 a
   // multiple of 16, db = 0 .. 7.
-  __device__ __forceinline__ bf16x8 trfrag(uint32_t tile, int row0, int db) const {
+  __device__ __forceinline__ h16x8 trfrag(uint32_t tile, int row0, int db) const {
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) s16x4 ls16x4;
     typedef __attribute__((address_space(3))) char lchar;
@@ -254,11 +254,11 @@ struct Sw512 {
     s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4 *)(b1 + o + 8192));
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    return __builtin_bit_cast(bf16x8, r);
+    return __builtin_bit_cast(h16x8, r);
   }
 };
 
-// DMA of a ROWS x HD bf16 tile of consecutive rows (row stride ld_bytes, head offset
+// DMA of a ROWS x HD h16 tile of consecutive rows (row stride ld_bytes, head offset
 // already in `base`) into a swizzled tile.  Block b (1 KB) of the tile is written by
 // wave b % 4; lane i of that instruction fills slot i of the block.  The per-lane
 // source offsets depend only on the thread and the row stride.
@@ -287,7 +287,7 @@ template <int HD, int ROWS> struct DmaRows {
     }
   }
   // nrows: valid rows from base (rows past them are zero-filled).
-  __device__ __forceinline__ void load(char *lds_tile, const bf16 *base, int ld_bytes, int nrows,
+  __device__ __forceinline__ void load(char *lds_tile, const h16 *base, int ld_bytes, int nrows,
                                        int wave) const {
     const int n = nrows < ROWS ? (nrows > 0 ? nrows : 0) : ROWS;
     const __amdgpu_buffer_rsrc_t rs =

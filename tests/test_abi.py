@@ -39,7 +39,8 @@ FAKE = 0x10000   # 16-byte aligned, never dereferenced: validation fails first
     (dict(ctx_len=-1), L.DKV_ERR_INVALID_ARG, "ctx_len"),
     (dict(cu_dev=0), L.DKV_ERR_INVALID_ARG, "cu_seqlens_dev"),
     (dict(softmax_scale=float("nan")), L.DKV_ERR_INVALID_ARG, "scale"),
-    (dict(head_dim=512, dtype=L.DKV_FP32), L.DKV_ERR_UNSUPPORTED, "bf16 only"),
+    (dict(head_dim=512, dtype=L.DKV_FP32), L.DKV_ERR_UNSUPPORTED, "fp16 only"),
+    (dict(dtype=3), L.DKV_ERR_INVALID_ARG, "dtype"),
     (dict(head_dim=512, num_heads_q=64, num_heads_kv=1), L.DKV_ERR_UNSUPPORTED, "head_dim 512"),
 ])
 def test_fwd_rejects_invalid_params(kw, status, frag):

@@ -34,7 +34,7 @@ class Workload:
     Hq: int
     Hkv: int
     d: int
-    dtype: str                  # "fp32" or "bf16"
+    dtype: str                  # "fp32", "bf16" or "fp16"
     window_left: int = -1       # -1 = global causal
     seed: int = 0
     scaled: bool = True         # values ~ N(0,1)/sqrt(d) (else N(0,1))
@@ -92,7 +92,7 @@ WORKLOADS = {
 
 
 def torch_dtype(name: str) -> torch.dtype:
-    return {"fp32": torch.float32, "bf16": torch.bfloat16}[name]
+    return {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[name]
 
 
 def cu_seqlens(lens) -> torch.Tensor:
@@ -106,8 +106,8 @@ def _draw(g: torch.Generator, shape, dtype: str, scale: float, keep: bool = Fals
     """Values exactly representable in ``dtype``: fp32 tensors, or (``keep``) tensors
     already in ``dtype``."""
     x = torch.randn(shape, generator=g, dtype=torch.float32, device=g.device) * scale
-    if dtype == "bf16":
-        x = x.to(torch.bfloat16)
+    if dtype in ("bf16", "fp16"):
+        x = x.to(torch_dtype(dtype))
         if not keep:
             x = x.to(torch.float32)
     return x
