@@ -82,6 +82,16 @@ WORKLOADS = {
                             Hkv=4, d=512, dtype="bf16", seed=5),
     "d512_swa": Workload("d512_swa", P=57344, N=8, R=8192, R_range=None, Hq=16, Hkv=4,
                          d=512, dtype="bf16", window_left=1023, seed=6),
+    # The shapes of the paper's kernel benchmark (§4.1, Table 1): Qwen3-8B attention
+    # dimensions, R = 2048 per response, fp16, global causal.
+    "table1_p4k": Workload("table1_p4k", P=4096, N=28, R=2048, R_range=None, Hq=32, Hkv=8,
+                           d=128, dtype="fp16", seed=11),
+    "table1_p16k": Workload("table1_p16k", P=16384, N=28, R=2048, R_range=None, Hq=32,
+                            Hkv=8, d=128, dtype="fp16", seed=12),
+    "table1_p32k": Workload("table1_p32k", P=32768, N=16, R=2048, R_range=None, Hq=32,
+                            Hkv=8, d=128, dtype="fp16", seed=13),
+    "table1_p64k": Workload("table1_p64k", P=65536, N=16, R=2048, R_range=None, Hq=32,
+                            Hkv=8, d=128, dtype="fp16", seed=14),
     # A GRPO micro-batch holding several prompts (§2.2 "Data pipeline"): 4 prompt
     # groups of 8 responses, prompts U{2048..8192} and responses U{512..2048} tokens
     # (the LongReason setting of §4.2 caps prompts at 8192 and responses at 2048).
