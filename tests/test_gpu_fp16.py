@@ -1,7 +1,7 @@
 """GPU parity in fp16, the precision of the paper's kernel benchmark (§4.1, Table 1):
 the same 16-bit MFMA kernels as bf16, with the fp16 MFMA and fp16 rounding of P, dS
 and the outputs.  Forward and backward of both calls against the oracle on the same
-fp16-rounded inputs, max|err| <= 5e-3 * max|ref| per tensor (LSE 1e-3 absolute)."""
+fp16-rounded inputs, max|err| <= 5e-3 * max|ref| + 2^-24 per tensor (LSE 1e-3 absolute)."""
 import numpy as np
 import pytest
 import torch

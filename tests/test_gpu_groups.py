@@ -199,3 +199,35 @@ def test_full_size_groups_sparse_gradient():
     check("dv_p", gr["dv_p"], dv_p_ref, "bf16")
     check("dk_r", gr["dk_r"], dk_r_ref, "bf16")
     check("dv_r", gr["dv_r"], dv_r_ref, "bf16")
+
+
+def _random_group_cases(n, seed):
+    """Seeded random micro-batches of prompt groups: group count, prompt lengths (0
+    allowed), response counts (0 allowed) and lengths (0 and 1 allowed), GQA ratio,
+    head dim, window and 16-bit type."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        d = int(rng.choice([64, 128, 512]))
+        hkv = int(rng.choice([1, 2, 4]))
+        g = int(rng.choice([1, 2, 3, 4, 6] if d < 512 else [1, 2, 4]))
+        groups = []
+        for _ in range(int(rng.integers(1, 5))):
+            P = int(rng.choice([0, int(rng.integers(1, 160))]))
+            lens = [int(x) for x in rng.integers(0, 120, size=int(rng.integers(0, 4)))]
+            groups.append((P, lens))
+        if sum(sum(ls) for _, ls in groups) == 0:
+            groups.append((int(rng.integers(1, 100)), [int(rng.integers(1, 100))]))
+        wl = int(rng.choice([-1, -1, int(rng.integers(0, 120))]))
+        cases.append((groups, hkv * g, hkv, d, wl, str(rng.choice(["bf16", "fp16"]))))
+    return cases
+
+
+@pytest.mark.parametrize("groups,Hq,Hkv,d,wl,dtype", _random_group_cases(10, 77))
+def test_random_prompt_groups(groups, Hq, Hkv, d, wl, dtype):
+    t, ref, (o_p, lse_p, o_r, lse_r), g, _ = _run(groups, Hq, Hkv, d, wl, dtype,
+                                                  seed=300 + d + Hq)
+    check("o_p", o_p, ref["o_p"], dtype)
+    check("o_r", o_r, ref["o_r"], dtype)
+    for k in GRADS:
+        check(k, g[k], ref[k], dtype)
