@@ -36,6 +36,9 @@
  *     thread).  Validation happens before any device work is enqueued, so an
  *     invalid call enqueues nothing.
  *   - Concurrent calls on different streams must not share a workspace.
+ *   - Calls on a stream that is capturing a HIP graph return DKV_ERR_UNSUPPORTED
+ *     (work lists are staged through reused pinned host buffers, which a graph would
+ *     read again at every replay).
  */
 #ifndef DKV_H
 #define DKV_H

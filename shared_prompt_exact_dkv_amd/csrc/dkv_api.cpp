@@ -306,6 +306,19 @@ StagingRing &ring() {
   return r;
 }
 
+// Work lists go through reusable pinned host slots, which a captured graph would read
+// again at every replay, after later calls have overwritten them: calls on a
+// capturing stream are refused before anything is enqueued.
+dkv_status check_not_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &cs);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(DKV_ERR_UNSUPPORTED, "calls on a capturing stream are not supported (work lists "
+                "are staged through reused host buffers)");
+  return DKV_OK;
+}
+
 dkv_status upload(const void *src, size_t bytes, void *dst, hipStream_t stream) {
   if (bytes == 0) return DKV_OK;
   int dev = 0;
@@ -428,6 +441,7 @@ dkv_status run_fwd(const Shape &s, const void *q, const void *kc, const void *vc
   FwdPlan pl = plan_fwd(s);
   dkv_status st = check_ws(ws, ws_bytes, pl.bytes);
   if (st != DKV_OK) return st;
+  if (pl.n_items > 0 && (st = check_not_capturing(stream)) != DKV_OK) return st;
   if (pl.n_items == 0) return DKV_OK;
   std::vector<QItem> items = build_q_items(s, s.bm_tok, kFwdBN);
   char *wsb = static_cast<char *>(ws);
@@ -637,6 +651,7 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
   BwdPlan pl = plan_bwd(s, io.with_ctx, split);
   dkv_status st = check_ws(ws, ws_bytes, pl.bytes);
   if (st != DKV_OK) return st;
+  if ((st = check_not_capturing(stream)) != DKV_OK) return st;
   char *wsb = static_cast<char *>(ws);
   const long acc_elems = io.acc_rows * s.Hkv * s.d;
   hipError_t e;
@@ -1042,6 +1057,7 @@ dkv_status dkv_layout(const dkv_params *p, int op, int64_t row_elems, const void
     return st;
   if ((st = check_ws(ws, ws_bytes, pl.bytes)) != DKV_OK) return st;
   if (pl.items.empty()) return DKV_OK;
+  if ((st = check_not_capturing(stream)) != DKV_OK) return st;
   char *wsb = static_cast<char *>(ws);
   if ((st = upload(pl.items.data(), pl.items.size() * sizeof(RowItem), wsb + pl.items_off,
                    stream)) != DKV_OK)
