@@ -1,0 +1,172 @@
+// Host-only check of the work lists that libdkv's scheduler builds (no GPU needed):
+// the library's source is included so that its internal list builders can be called.
+//
+// For seeded random shapes (prompt groups with empty prompts and empty groups, ragged
+// and empty responses, windows, GQA ratios, head dims, split mode) it checks:
+//   * forward / dQ items: every (kv head, sequence, query tile) exactly once, with the
+//     sequence's rows and its own group's prompt rows;
+//   * dK/dV items: every (kv head, sequence, own key tile) exactly once; every
+//     (kv head, prompt key tile, sequence of the prompt's group whose rows see the
+//     tile) exactly once in atomic mode; in split mode every (kv head, prompt key tile,
+//     slice) exactly once, its sequence range inside both the slice's chunk and the
+//     tile's group;
+//   * layout items: every output row written exactly once, all rows in bounds.
+// Exit status 0 and "ok <n>" on success; the first violation is printed otherwise.
+#include "../shared_prompt_exact_dkv_amd/csrc/dkv_api.cpp"
+
+#include <map>
+#include <random>
+#include <tuple>
+
+#define REQUIRE(c, ...)                          \
+  do {                                           \
+    if (!(c)) {                                  \
+      printf("FAIL %s: ", #c);                   \
+      printf(__VA_ARGS__);                       \
+      printf("\n");                              \
+      exit(1);                                   \
+    }                                            \
+  } while (0)
+
+int main(int argc, char **argv) {
+  const int trials = argc > 1 ? atoi(argv[1]) : 400;
+  std::mt19937 rng(2026);
+  long checked = 0;
+  for (int trial = 0; trial < trials; ++trial) {
+    const int ng = 1 + rng() % 4;
+    std::vector<int> ctx{0}, seq{0}, cu{0};
+    for (int j = 0; j < ng; ++j) {
+      const int P = (rng() % 4 == 0) ? 0 : rng() % 400;
+      const int n = rng() % 5;
+      ctx.push_back(ctx.back() + P);
+      seq.push_back(seq.back() + n);
+      for (int i = 0; i < n; ++i) cu.push_back(cu.back() + ((rng() % 5 == 0) ? rng() % 2 : rng() % 300));
+    }
+    const int hds[3] = {64, 128, 512};
+    const int Gs[5] = {1, 2, 3, 4, 8};
+    dkv_params p{};
+    p.num_seqs = seq.back();
+    p.ctx_len = ctx.back();
+    p.num_heads_kv = 1 + rng() % 4;
+    p.num_heads_q = p.num_heads_kv * Gs[rng() % 5];
+    p.head_dim = hds[rng() % 3];
+    p.window_left = (rng() % 3 == 0) ? (int)(rng() % 200) : -1;
+    p.dtype = DKV_BF16;
+    p.cu_seqlens_host = cu.data();
+    p.cu_seqlens_dev = cu.data();   // never dereferenced here
+    p.num_groups = (ng > 1 || rng() % 2) ? ng : 0;
+    p.ctx_cu_host = ctx.data();
+    p.group_seq_cu_host = seq.data();
+    Shape s;
+    REQUIRE(check_params(&p, false, &s) == DKV_OK, "%s", dkv_last_error());
+    const int N = s.N;
+    auto len = [&](int i) { return s.cu[i + 1] - s.cu[i]; };
+    auto group_of = [&](int i) {
+      int j = 0;
+      while (s.gseq[j + 1] <= i) ++j;
+      return j;
+    };
+
+    // ---- query-parallel items (forward, dQ)
+    for (int bm : {s.bm_tok, s.bm_tok_dq}) {
+      std::map<std::tuple<int, int, int>, int> seen;
+      for (const QItem &it : build_q_items(s, bm, kFwdBN)) {
+        int i = 0;
+        while (i < N && !(s.cu[i] == it.seq_start && len(i) == it.seq_len && len(i) > 0)) ++i;
+        REQUIRE(i < N, "item with seq_start %d len %d", it.seq_start, it.seq_len);
+        // several sequences may share a start (empty ones); take the non-empty one
+        REQUIRE(it.g >= 0 && it.g < s.Hkv, "g %d", it.g);
+        REQUIRE(it.tile >= 0 && (long)it.tile * bm < it.seq_len, "tile %d", it.tile);
+        const int j = group_of(i);
+        REQUIRE(it.ctx_start == s.gctx[j] && it.ctx_len == s.gctx[j + 1] - s.gctx[j],
+                "prompt of seq %d", i);
+        REQUIRE(++seen[std::make_tuple(it.g, i, it.tile)] == 1, "q item repeated");
+      }
+      long want = 0;
+      for (int i = 0; i < N; ++i) want += (long)((len(i) + bm - 1) / bm) * s.Hkv;
+      REQUIRE((long)seen.size() == want, "q items %zu of %ld", seen.size(), want);
+    }
+
+    // ---- key-parallel items (dK/dV), atomic and split modes
+    for (int split = 0; split < 2; ++split) {
+      std::map<std::tuple<int, int, int>, int> own, ctxc, slice;
+      const int cs = split ? split_chunk(s) : 1;
+      for (const KVItem &it : build_kv_items(s, true, split)) {
+        REQUIRE(it.g >= 0 && it.g < s.Hkv, "g");
+        REQUIRE(it.seq_lo >= 0 && it.seq_lo <= it.seq_hi && it.seq_hi <= N, "range");
+        if (it.region == kRegionOwn) {
+          REQUIRE(it.seq_hi == it.seq_lo + 1, "own item spans sequences");
+          const int i = it.seq_lo, j = group_of(i);
+          REQUIRE(it.key_start >= 0 && it.key_start < len(i), "own key tile");
+          REQUIRE(it.ctx_start == s.gctx[j] && it.ctx_len == s.gctx[j + 1] - s.gctx[j], "own prompt");
+          REQUIRE(++own[std::make_tuple(it.g, i, it.key_start)] == 1, "own item repeated");
+        } else {
+          REQUIRE(it.region == kRegionCtx, "region");
+          // the group whose (non-empty) prompt the item names: prompts of positive
+          // length have distinct first rows
+          int j = 0;
+          while (j < (int)s.gseq.size() - 1 &&
+                 !(s.gctx[j] == it.ctx_start && s.gctx[j + 1] - s.gctx[j] == it.ctx_len))
+            ++j;
+          REQUIRE(j < (int)s.gseq.size() - 1, "ctx item group");
+          const int Pg = s.gctx[j + 1] - s.gctx[j];
+          REQUIRE(it.ctx_len == Pg && Pg > 0, "ctx prompt length");
+          REQUIRE(it.key_start >= 0 && it.key_start < Pg && it.key_start % s.kv_tile == 0, "ctx key tile");
+          if (it.seq_hi > it.seq_lo)
+            REQUIRE(it.seq_lo >= s.gseq[j] && it.seq_hi <= s.gseq[j + 1], "ctx range outside group");
+          if (split) {
+            const int c = it.seq_lo / cs;
+            REQUIRE(it.seq_hi <= (c + 1) * cs, "split range outside chunk");
+            REQUIRE(++slice[std::make_tuple(it.g, s.gctx[j] + it.key_start, c)] == 1, "slice item repeated");
+          } else {
+            for (int i = it.seq_lo; i < it.seq_hi; ++i)
+              REQUIRE(++ctxc[std::make_tuple(it.g, s.gctx[j] + it.key_start, i)] == 1, "ctx pair repeated");
+          }
+        }
+      }
+      long want_own = 0;
+      for (int i = 0; i < N; ++i) want_own += (long)((len(i) + s.kv_tile - 1) / s.kv_tile) * s.Hkv;
+      REQUIRE((long)own.size() == want_own, "own items %zu of %ld", own.size(), want_own);
+      for (int j = 0; j + 1 < (int)s.gseq.size(); ++j) {
+        const int Pg = s.gctx[j + 1] - s.gctx[j];
+        for (int g = 0; g < s.Hkv; ++g)
+          for (int k0 = 0; k0 < Pg; k0 += s.kv_tile) {
+            const int nk = std::min(s.kv_tile, Pg - k0);
+            if (split) {
+              for (int c = 0; c < split_slices(s); ++c)
+                REQUIRE(slice.count(std::make_tuple(g, s.gctx[j] + k0, c)) == 1, "slice %d of tile missing", c);
+            } else {
+              for (int i = s.gseq[j]; i < s.gseq[j + 1]; ++i) {
+                const bool sees = kv_rows_visible(s, true, k0, nk, len(i), Pg) > 0;
+                REQUIRE(ctxc.count(std::make_tuple(g, s.gctx[j] + k0, i)) == (sees ? 1u : 0u),
+                        "ctx pair (g %d, key %d, seq %d) coverage", g, s.gctx[j] + k0, i);
+              }
+            }
+          }
+      }
+    }
+
+    // ---- layout items
+    Shape sl;
+    REQUIRE(check_layout(&p, DKV_PACK, 64, &sl) == DKV_OK, "%s", dkv_last_error());
+    for (int op = DKV_PACK; op <= DKV_FIRST_TOKEN_SCATTER; ++op) {
+      LayoutPlan pl = plan_layout(sl, op);
+      std::vector<int> cover(pl.out_rows, 0);
+      for (const RowItem &it : pl.items) {
+        REQUIRE(it.dst_row >= 0 && it.nrows >= 1 && it.nrows <= kRowsPerItem &&
+                    it.dst_row + it.nrows <= pl.out_rows, "layout dst, op %d", op);
+        REQUIRE(it.src_off >= 0 && it.src_off + it.nsrc <= (int)pl.src.size(), "layout table");
+        for (int k = 0; k < it.nsrc; ++k) {
+          const int st = pl.src[it.src_off + k];
+          REQUIRE(st >= 0 && st + it.nrows <= pl.in_rows, "layout src, op %d", op);
+        }
+        for (int r = 0; r < it.nrows; ++r) cover[it.dst_row + r]++;
+      }
+      for (long r = 0; r < pl.out_rows; ++r)
+        REQUIRE(cover[r] == 1, "layout op %d row %ld written %d times", op, r, cover[r]);
+    }
+    ++checked;
+  }
+  printf("ok %ld\n", checked);
+  return 0;
+}
