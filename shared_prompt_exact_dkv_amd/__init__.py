@@ -12,6 +12,8 @@ eq. (4); the shared prompt K/V gradient is the sum of eq. (6).
 """
 from __future__ import annotations
 
+import math
+
 import torch
 
 from . import _lib as L
@@ -194,7 +196,13 @@ def dkv_layout(op: int, x, cu_host, ctx_len: int, *, ctx_cu_host=None, group_seq
     rows_in, rows_out = layout_rows(op, cu_host, ctx_len, ctx_cu_host, group_seq_cu_host)
     if x.shape[0] != rows_in:
         raise ValueError("layout op %d expects %d input rows, got %d" % (op, rows_in, x.shape[0]))
-    row_elems = x[0].numel() if x.shape[0] else int(torch.tensor(x.shape[1:]).prod())
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    row_elems = math.prod(x.shape[1:])
+    if out is not None and (tuple(out.shape) != (rows_out,) + tuple(x.shape[1:])
+                            or out.dtype != x.dtype or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous %s tensor of shape %s"
+                         % (x.dtype, (rows_out,) + tuple(x.shape[1:])))
     cu = [int(c) for c in cu_host]
     p, keep = L.make_params(num_seqs=len(cu) - 1, ctx_len=ctx_len, num_heads_q=1,
                             num_heads_kv=1, head_dim=64, dtype=_DT[x.dtype], cu_host=cu,
