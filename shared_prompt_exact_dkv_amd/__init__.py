@@ -58,6 +58,24 @@ def _groups(ctx_cu_host, group_seq_cu_host):
     return [int(c) for c in ctx_cu_host], [int(c) for c in group_seq_cu_host]
 
 
+def _need(t, shape, dtype, name):
+    """The C ABI takes plain pointers: check here that a tensor has the shape, dtype and
+    layout the call reads or writes through it."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError("%s: expected a contiguous %s tensor of shape %s, got %s %s%s"
+                         % (name, dtype, tuple(shape), t.dtype, tuple(t.shape),
+                            "" if t.is_contiguous() else " (not contiguous)"))
+
+
+def _need_qkv(q, k, v, T, name):
+    Hq, d = q.shape[1], q.shape[2]
+    _need(q, (T, Hq, d), q.dtype, "q" + name)
+    _need(k, (T, k.shape[1], d), q.dtype, "k" + name)
+    _need(v, (T, k.shape[1], d), q.dtype, "v" + name)
+
+
 def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -87,8 +105,11 @@ def dkv_ctx_fwd(q, k, v, cu_seqlens, *, cu_host=None, window_left=-1, softmax_sc
     q [T,Hq,d], k/v [T,Hkv,d] -> (o [T,Hq,d], lse [Hq,T] fp32)."""
     p, keep = _params(q, k, cu_seqlens, cu_host, 0, window_left, softmax_scale)
     T, Hq, _ = q.shape
+    _need_qkv(q, k, v, p.cu_seqlens_host[p.num_seqs], "")
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, q.shape, q.dtype, "out")
+    _need(lse, (Hq, T), torch.float32, "lse")
     ws, nws = _ws(p, L.DKV_CALL_CTX_FWD, q.device, workspace)
     L.check(L.lib().dkv_ctx_fwd(p, _p(q), _p(k), _p(v), _p(o), _p(lse), _p(ws), nws,
                                 _stream(q.device)))
@@ -105,8 +126,13 @@ def dkv_fwd(q_resp, k_p, v_p, k_r, v_r, cu_seqlens, *, cu_host=None, window_left
     p, keep = _params(q_resp, k_r, cu_seqlens, cu_host, k_p.shape[0], window_left,
                       softmax_scale, _groups(ctx_cu_host, group_seq_cu_host))
     T, Hq, _ = q_resp.shape
+    _need_qkv(q_resp, k_r, v_r, p.cu_seqlens_host[p.num_seqs], "_r")
+    _need(k_p, (k_p.shape[0],) + tuple(k_r.shape[1:]), q_resp.dtype, "k_p")
+    _need(v_p, k_p.shape, q_resp.dtype, "v_p")
     o = torch.empty_like(q_resp) if out is None else out
     lse = torch.empty((Hq, T), dtype=torch.float32, device=q_resp.device) if lse is None else lse
+    _need(o, q_resp.shape, q_resp.dtype, "out")
+    _need(lse, (Hq, T), torch.float32, "lse")
     ws, nws = _ws(p, L.DKV_CALL_FWD, q_resp.device, workspace)
     L.check(L.lib().dkv_fwd(p, _p(q_resp), _p(k_p), _p(v_p), _p(k_r), _p(v_r), _p(o), _p(lse),
                             _p(ws), nws, _stream(q_resp.device)))
@@ -121,10 +147,19 @@ def dkv_ctx_bwd(q, k, v, o, lse, dout, cu_seqlens, *, cu_host=None, window_left=
     (cleared first with DKV_ACC_ZERO, cast into dk/dv with DKV_ACC_FINALIZE).
     -> (dq, dk, dv)."""
     p, keep = _params(q, k, cu_seqlens, cu_host, 0, window_left, softmax_scale)
+    _need_qkv(q, k, v, p.cu_seqlens_host[p.num_seqs], "")
+    _need(o, q.shape, q.dtype, "o")
+    _need(dout, q.shape, q.dtype, "dout")
+    _need(lse, (q.shape[1], q.shape[0]), torch.float32, "lse")
     dq = torch.empty_like(q) if dq is None else dq
     if acc_dk is None or (acc_flags & L.DKV_ACC_FINALIZE):
         dk = torch.empty_like(k) if dk is None else dk
         dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, q.shape, q.dtype, "dq")
+    _need(dk, k.shape, k.dtype, "dk")
+    _need(dv, k.shape, k.dtype, "dv")
+    _need(acc_dk, k.shape, torch.float32, "acc_dk")
+    _need(acc_dv, k.shape, torch.float32, "acc_dv")
     ws, nws = _ws(p, L.DKV_CALL_CTX_BWD, q.device, workspace)
     L.check(L.lib().dkv_ctx_bwd(p, _p(q), _p(k), _p(v), _p(o), _p(lse), _p(dout), _p(dq),
                                 _p(dk), _p(dv), _p(acc_dk), _p(acc_dv), int(acc_flags), _p(ws),
@@ -143,12 +178,25 @@ def dkv_bwd(q_resp, k_p, v_p, k_r, v_r, o_r, lse_r, dout_r, cu_seqlens, *, acc_d
     Prompt groups as in dkv_fwd.  -> (dq_r, dk_r, dv_r, dk_p, dv_p)."""
     p, keep = _params(q_resp, k_r, cu_seqlens, cu_host, k_p.shape[0], window_left,
                       softmax_scale, _groups(ctx_cu_host, group_seq_cu_host))
+    _need_qkv(q_resp, k_r, v_r, p.cu_seqlens_host[p.num_seqs], "_r")
+    _need(k_p, (k_p.shape[0],) + tuple(k_r.shape[1:]), q_resp.dtype, "k_p")
+    _need(v_p, k_p.shape, q_resp.dtype, "v_p")
+    _need(o_r, q_resp.shape, q_resp.dtype, "o_r")
+    _need(dout_r, q_resp.shape, q_resp.dtype, "dout_r")
+    _need(lse_r, (q_resp.shape[1], q_resp.shape[0]), torch.float32, "lse_r")
+    _need(acc_dk_p, k_p.shape, torch.float32, "acc_dk_p")
+    _need(acc_dv_p, k_p.shape, torch.float32, "acc_dv_p")
     dq_r = torch.empty_like(q_resp) if dq_r is None else dq_r
     dk_r = torch.empty_like(k_r) if dk_r is None else dk_r
     dv_r = torch.empty_like(v_r) if dv_r is None else dv_r
     if acc_flags & L.DKV_ACC_FINALIZE:
         dk_p = torch.empty_like(k_p) if dk_p is None else dk_p
         dv_p = torch.empty_like(v_p) if dv_p is None else dv_p
+    _need(dq_r, q_resp.shape, q_resp.dtype, "dq_r")
+    _need(dk_r, k_r.shape, k_r.dtype, "dk_r")
+    _need(dv_r, k_r.shape, k_r.dtype, "dv_r")
+    _need(dk_p, k_p.shape, k_p.dtype, "dk_p")
+    _need(dv_p, k_p.shape, k_p.dtype, "dv_p")
     call = L.DKV_CALL_BWD_SPLIT if acc_flags & L.DKV_ACC_SPLIT else L.DKV_CALL_BWD
     ws, nws = _ws(p, call, q_resp.device, workspace)
     L.check(L.lib().dkv_bwd(p, _p(q_resp), _p(k_p), _p(v_p), _p(k_r), _p(v_r), _p(o_r),

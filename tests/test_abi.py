@@ -204,3 +204,30 @@ def test_layout_validation():
     # work lists: unpack of N = 2 copies of a 16-row prompt plus 9 response rows
     n = lib.dkv_layout_workspace_size(p, L.DKV_UNPACK)
     assert 0 < n < 4096
+
+
+def test_binding_checks_tensor_shapes():
+    # The C ABI takes plain pointers, so the binding checks shapes, dtypes and layout
+    # before any call: a short query tensor, a wrong output shape or a transposed view
+    # would otherwise be read or written out of bounds.
+    import torch
+    import shared_prompt_exact_dkv_amd as dkv
+    P, T, Hq, Hkv, d = 8, 12, 4, 2, 64
+    bf = torch.bfloat16
+    q = torch.zeros(T, Hq, d, dtype=bf)
+    k = torch.zeros(T, Hkv, d, dtype=bf)
+    kp = torch.zeros(P, Hkv, d, dtype=bf)
+    cu = torch.tensor([0, 5, T], dtype=torch.int32)
+    with pytest.raises(ValueError, match="q_r"):
+        dkv.dkv_fwd(q[:10], kp, kp, k[:10], k[:10], cu)            # cu says 12 rows
+    with pytest.raises(ValueError, match="out"):
+        dkv.dkv_fwd(q, kp, kp, k, k, cu, out=torch.zeros(T - 1, Hq, d, dtype=bf))
+    with pytest.raises(ValueError, match="lse"):
+        dkv.dkv_fwd(q, kp, kp, k, k, cu, lse=torch.zeros(T, Hq))   # transposed layout
+    with pytest.raises(ValueError, match="v_p"):
+        dkv.dkv_fwd(q, kp, kp[:4], k, k, cu)
+    with pytest.raises(ValueError, match="acc_dk_p"):
+        dkv.dkv_bwd(q, kp, kp, k, k, q, torch.zeros(Hq, T), q, cu,
+                    acc_dk_p=torch.zeros(P, Hkv, d, dtype=bf), acc_dv_p=None)
+    with pytest.raises(ValueError, match="not contiguous"):
+        dkv.dkv_ctx_fwd(q.transpose(0, 1).contiguous().transpose(0, 1), k, k, cu)
