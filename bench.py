@@ -100,6 +100,19 @@ def traffic_for(kernel, workload):
     return rec.get("bytes_per_launch")
 
 
+def copy_calibration(args):
+    """A plain copy of known size: 1 GiB read, 1 GiB written.  Under rocprofv3 --pmc its
+    FETCH_SIZE / WRITE_SIZE readings give the counters' scale factor."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(args, "copy calibration: %d bytes read, %d bytes written" % (4 << 28, 4 << 28))
+    del src, dst
+
+
 def layout_main(args):
     """One step = the five layout conversions of one micro-batch: UNPACK and PACK of a
     hidden-state tensor, UNPACK_BWD of its gradient, and the first-token GATHER and
@@ -171,6 +184,8 @@ def layout_main(args):
         tot, n = _lib.timing_read()["layout"]
         per_op[op] = tot / n
     _lib.lib().dkv_timing_reset()
+    if args.copy_calibration:
+        copy_calibration(args)
     total_bytes = sum(rows_moved[op] * H * eb for op in ops)
     gbs = total_bytes / (ms * 1e-3) / 1e9
     dom = max(ops, key=lambda op: per_op[op])
@@ -393,15 +408,7 @@ def main():
         log(args, "cpu oracle sample %.2f s" % cpu_s)
 
     if args.copy_calibration:
-        # A plain copy of known size: 1 GiB read, 1 GiB written.  Under rocprofv3 --pmc
-        # its FETCH_SIZE / WRITE_SIZE readings give the counters' scale factor.
-        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(args, "copy calibration: %d bytes read, %d bytes written" % (4 << 28, 4 << 28))
-        del src, dst
+        copy_calibration(args)
 
     speedup = (ncopy_ms / ms) if ncopy_ms else None
     out = {
