@@ -739,25 +739,32 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
 
 struct LayoutPlan {
   std::vector<RowItem> items;
-  std::vector<int32_t> src;
+  std::vector<int32_t> src;   // per item: its source row starts, then its destination starts
   long in_rows = 0, out_rows = 0;
   size_t items_off = 0, src_off = 0, bytes = 0;
 };
 
-// Output rows [dst, dst + n): the sum over the given input row starts (each advanced
-// with the row), a copy for one start, zeros for none.  An item of several sources
-// takes fewer rows, so that it reads about as much as a copy item.
-void add_segment(LayoutPlan &pl, long dst, long n, const std::vector<long> &starts) {
-  const long rows = std::max<long>(1, kRowsPerItem / std::max<long>(1, (long)starts.size()));
+// n rows written to each output range starting at dsts: the sum over the given input
+// row starts (each advanced with the row), a copy for one start, zeros for none.  An
+// item of several sources or destinations takes fewer rows, so that it moves about as
+// much as a plain copy item.
+void add_segment(LayoutPlan &pl, const std::vector<long> &dsts, long n,
+                 const std::vector<long> &starts) {
+  const long fan = std::max<long>(1, std::max<long>((long)starts.size(), (long)dsts.size()));
+  const long rows = std::max<long>(1, kRowsPerItem / fan);
   for (long k = 0; k < n; k += rows) {
     RowItem it;
-    it.dst_row = (int32_t)(dst + k);
+    it.tab_off = (int32_t)pl.src.size();
     it.nrows = (int32_t)std::min<long>(rows, n - k);
-    it.src_off = (int32_t)pl.src.size();
     it.nsrc = (int32_t)starts.size();
+    it.ndst = (int32_t)dsts.size();
     for (long st : starts) pl.src.push_back((int32_t)(st + k));
+    for (long d : dsts) pl.src.push_back((int32_t)(d + k));
     pl.items.push_back(it);
   }
+}
+void add_segment(LayoutPlan &pl, long dst, long n, const std::vector<long> &starts) {
+  add_segment(pl, std::vector<long>{dst}, n, starts);
 }
 
 LayoutPlan plan_layout(const Shape &s, int op) {
@@ -781,10 +788,12 @@ LayoutPlan plan_layout(const Shape &s, int op) {
     case DKV_UNPACK:   // single-prompt -> N-copy: each copy takes its group's prompt
       pl.in_rows = packed;
       pl.out_rows = nc0[s.N];
-      for (int i = 0; i < s.N; ++i) {
-        add_segment(pl, nc0[i], s.sP[i], {(long)s.sctx0[i]});
-        add_segment(pl, nc0[i] + s.sP[i], len(i), {(long)s.P + s.cu[i]});
+      for (int j = 0; j < ngroups; ++j) {   // a prompt chunk is read once per group
+        std::vector<long> dsts;
+        for (int i = s.gseq[j]; i < s.gseq[j + 1]; ++i) dsts.push_back(nc0[i]);
+        if (!dsts.empty()) add_segment(pl, dsts, s.gctx[j + 1] - s.gctx[j], {(long)s.gctx[j]});
       }
+      for (int i = 0; i < s.N; ++i) add_segment(pl, nc0[i] + s.sP[i], len(i), {(long)s.P + s.cu[i]});
       break;
     case DKV_UNPACK_BWD:   // adjoint of UNPACK: a prompt row sums its group's copies
       pl.in_rows = nc0[s.N];

@@ -123,15 +123,16 @@ hipError_t launch_bwd_dkdv_d512(int dtype, const BwdKVArgs &a, int n_items, hipS
 
 // ---- layout conversions (N-copy <-> single-prompt packing, first-token rows) ----
 
-// Output rows [dst_row, dst_row + nrows): row dst_row + r is the sum over s < nsrc of
-// input row src_tab[src_off + s] + r (fp32 accumulation, rounded once); nsrc == 1 is
-// a copy, nsrc == 0 writes zeros.
+// nrows rows written to each of ndst destination ranges: with t = tab + tab_off, row r
+// of the range starting at output row t[nsrc + k] (k < ndst) is the sum over s < nsrc
+// of input row t[s] + r (fp32 accumulation, rounded once); nsrc == 1 is a copy (read
+// once, written ndst times), nsrc == 0 writes zeros.
 struct RowItem {
-  int32_t dst_row, nrows, src_off, nsrc;
+  int32_t tab_off, nrows, nsrc, ndst;
 };
 static constexpr int kRowsPerItem = 16;
 // row_vecs = 16-byte vectors per row.
 hipError_t launch_row_sum(int dtype, const void *in, void *out, const RowItem *items, int n_items,
-                          const int32_t *src_tab, int row_vecs, hipStream_t s);
+                          const int32_t *tab, int row_vecs, hipStream_t s);
 
 }  // namespace dkv

@@ -153,14 +153,17 @@ int main(int argc, char **argv) {
       LayoutPlan pl = plan_layout(sl, op);
       std::vector<int> cover(pl.out_rows, 0);
       for (const RowItem &it : pl.items) {
-        REQUIRE(it.dst_row >= 0 && it.nrows >= 1 && it.nrows <= kRowsPerItem &&
-                    it.dst_row + it.nrows <= pl.out_rows, "layout dst, op %d", op);
-        REQUIRE(it.src_off >= 0 && it.src_off + it.nsrc <= (int)pl.src.size(), "layout table");
+        REQUIRE(it.nrows >= 1 && it.nrows <= kRowsPerItem && it.ndst >= 1, "layout item, op %d", op);
+        REQUIRE(it.tab_off >= 0 && it.tab_off + it.nsrc + it.ndst <= (int)pl.src.size(), "layout table");
         for (int k = 0; k < it.nsrc; ++k) {
-          const int st = pl.src[it.src_off + k];
+          const int st = pl.src[it.tab_off + k];
           REQUIRE(st >= 0 && st + it.nrows <= pl.in_rows, "layout src, op %d", op);
         }
-        for (int r = 0; r < it.nrows; ++r) cover[it.dst_row + r]++;
+        for (int k = 0; k < it.ndst; ++k) {
+          const int d = pl.src[it.tab_off + it.nsrc + k];
+          REQUIRE(d >= 0 && d + it.nrows <= pl.out_rows, "layout dst, op %d", op);
+          for (int r = 0; r < it.nrows; ++r) cover[d + r]++;
+        }
       }
       for (long r = 0; r < pl.out_rows; ++r)
         REQUIRE(cover[r] == 1, "layout op %d row %ld written %d times", op, r, cover[r]);
