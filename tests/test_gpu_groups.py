@@ -132,7 +132,7 @@ def test_full_size_groups_sparse_gradient():
     print("[groups] P=%s T=%d" % ([p for p, _ in shapes], T), flush=True)
     rows_of = lambda n: sorted({r for r in (0, 1, n // 2, n - 2, n - 1) if 0 <= r < n})
     g = torch.Generator().manual_seed(4242)
-    f32 = torch.float32   # explicit: another test module sets a float64 default
+    f32 = torch.float32
     do_p = torch.zeros((P, Hq, d), dtype=f32)
     do_r = torch.zeros((T, Hq, d), dtype=f32)
     p_rows, seqs = {}, {}

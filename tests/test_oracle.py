@@ -23,7 +23,16 @@ import torch
 import oracle
 import workloads
 
-torch.set_default_dtype(torch.float64)
+
+
+@pytest.fixture(autouse=True)
+def _float64_default():
+    """The pins build tensors in float64; the default is restored after each test so
+    that no other test module sees it."""
+    old = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(old)
 
 
 def _sdpa_ref(q, k, v, scale, window_left, kvh):

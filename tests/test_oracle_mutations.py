@@ -73,15 +73,22 @@ def _pins_pass():
     return bool(ok)
 
 
-def test_unmutated_oracle_passes_pins():
+@pytest.fixture(autouse=True)
+def _float64_default():
+    """The pins build tensors in float64; the default is restored after each test."""
+    old = torch.get_default_dtype()
     torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(old)
+
+
+def test_unmutated_oracle_passes_pins():
     oracle.use_library(None)
     assert _pins_pass()
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_pins_reject_planted_mistake(tmp_path, name):
-    torch.set_default_dtype(torch.float64)
     old, new = MUTATIONS[name]
     so = _build(tmp_path, name, old, new)
     try:
