@@ -29,9 +29,12 @@
  *   - The library never allocates or frees device memory.  Scratch space comes from
  *     `ws` (device memory, `ws_bytes` long, 256-byte aligned), sized by
  *     dkv_workspace_size() for the same parameters and call.
- *   - Calls only enqueue work on `stream` and return; they never synchronize.  The
- *     returned status reports argument validation and launch errors; a fault inside
- *     a kernel surfaces at the caller's next synchronization.
+ *   - Calls only enqueue work on `stream` and return; they never wait for the device.
+ *     Work lists are copied from pinned host buffers that are reused once their copy
+ *     has completed (polled); when all are in flight another is allocated, so the
+ *     pinned pool grows with the caller's run-ahead instead of blocking.  The returned
+ *     status reports argument validation and launch errors; a fault inside a kernel
+ *     surfaces at the caller's next synchronization.
  *   - A non-OK status leaves a message retrievable with dkv_last_error() (per host
  *     thread).  Validation happens before any device work is enqueued, so an
  *     invalid call enqueues nothing.
@@ -103,7 +106,8 @@ typedef struct {
        response row r sits at logical position P + r.  Must be 0 for dkv_ctx_*. */
     int32_t ctx_len;
     int32_t num_heads_q;       /* Hq, a multiple of Hkv (grouped-query attention) */
-    int32_t num_heads_kv;      /* Hkv; q-head h reads kv-head h / (Hq / Hkv) */
+    int32_t num_heads_kv;      /* Hkv; q-head h reads kv head h / (Hq / Hkv) unless
+                                  kv_head_of_q says otherwise */
     int32_t head_dim;          /* d: 64, 128 or 512 */
     /* -1: global causal.  w >= 0: key at logical position j is visible from the query
        at logical position t iff t - w <= j <= t (applies to the prompt region too). */
@@ -112,8 +116,11 @@ typedef struct {
     int32_t dtype;             /* dkv_dtype of every tensor except LSE/accumulators */
     /* Prefix sums of the per-sequence query lengths, int32 [num_seqs + 1] with
        cu[0] = 0, non-decreasing (zero-length sequences allowed).  The host copy is
-       read during the call (validation and tile scheduling); the device copy, which
-       must hold the same values, is read by the kernels. */
+       read during the call: it is validated, drives the tile schedule, and is staged
+       into the workspace with the work lists, which is where the kernels read the
+       sequence bounds.  cu_seqlens_dev is optional (may be NULL) and not read: a device
+       copy that disagreed with the host copy could otherwise send the kernels outside
+       the tensors the host copy describes. */
     const int32_t *cu_seqlens_host;
     const int32_t *cu_seqlens_dev;
     /* Prompt groups (dkv_fwd / dkv_bwd only; must be 0 for dkv_ctx_*).  A micro-batch
@@ -134,10 +141,21 @@ typedef struct {
     int32_t num_groups;
     const int32_t *ctx_cu_host;
     const int32_t *group_seq_cu_host;
+    /* Grouped-query attention head map (§3.1 and §4.1: several query heads share one
+       key/value head; the paper's Qwen3-8B dimensions use 4 query heads per kv head).
+       NULL: q-head h reads kv head h / (Hq / Hkv).  Otherwise a host int32 [Hq] array
+       read during the call: q-head h reads kv head kv_head_of_q[h], in [0, Hkv), and
+       every kv head must be named by exactly Hq / Hkv q-heads (DKV_ERR_INVALID_ARG
+       otherwise).  It applies to every tensor of the call: O, LSE and the gradients
+       stay indexed by q-head and kv head as given. */
+    const int32_t *kv_head_of_q;
 } dkv_params;
 
 /* Bytes of device workspace the given call needs for these parameters (0 means
-   none; a valid pointer is still fine).  Returns (size_t)-1 for invalid params. */
+   none; a valid pointer is still fine).  Returns (size_t)-1 for invalid params.  The
+   workspace holds the call's work lists and tables (staged from pinned host memory on
+   the call's stream) and, for the backward calls, the per-row terms -D and -LSE / scale
+   ([Hq, tokens] fp32 each) and, with DKV_ACC_SPLIT, the accumulator slices. */
 size_t dkv_workspace_size(const dkv_params *p, int which_call);
 
 /*

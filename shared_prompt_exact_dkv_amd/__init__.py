@@ -34,21 +34,45 @@ def _p(t):
 
 
 def _host_cu(cu_seqlens, cu_host):
-    if cu_host is not None:
+    """The host copy of cu_seqlens, which the library validates and schedules from (the
+    kernels read the bounds staged from it, never a device copy).  cu_seqlens must be an
+    int32 tensor of N + 1 prefix sums; given alone it is read back (on a GPU tensor that
+    waits for the device).  Given with cu_host it must agree in length, and, when it is
+    on the CPU, in every value (a GPU tensor's values are not read back: the call would
+    otherwise wait for the device)."""
+    if cu_seqlens is None:
+        if cu_host is None:
+            raise ValueError("cu_seqlens or cu_host is required")
         return [int(c) for c in cu_host]
-    return [int(c) for c in cu_seqlens.cpu().tolist()]
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 \
+            or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous 1-D torch.int32 tensor")
+    if cu_host is None:
+        return [int(c) for c in cu_seqlens.cpu().tolist()]
+    cu = [int(c) for c in cu_host]
+    if cu_seqlens.numel() != len(cu):
+        raise ValueError("cu_seqlens has %d entries, cu_host %d" % (cu_seqlens.numel(), len(cu)))
+    if cu_seqlens.device.type == "cpu" and cu_seqlens.tolist() != cu:
+        raise ValueError("cu_seqlens and cu_host disagree")
+    return cu
 
 
-def _params(q, k, cu_seqlens, cu_host, ctx_len, window_left, softmax_scale, groups=None):
+def _params(q, k, cu_seqlens, cu_host, ctx_len, window_left, softmax_scale, groups=None,
+            kv_head_of_q=None):
     if q.dtype not in _DT:
         raise TypeError("unsupported dtype %s" % q.dtype)
     cu = _host_cu(cu_seqlens, cu_host)
     ctx_cu, seq_cu = groups if groups is not None else (None, None)
+    if kv_head_of_q is not None:
+        kv_head_of_q = [int(h) for h in kv_head_of_q]
+        if len(kv_head_of_q) != q.shape[1]:
+            raise ValueError("kv_head_of_q has %d entries for %d q-heads"
+                             % (len(kv_head_of_q), q.shape[1]))
     return L.make_params(num_seqs=len(cu) - 1, ctx_len=ctx_len, num_heads_q=q.shape[1],
                          num_heads_kv=k.shape[1], head_dim=q.shape[2],
                          window_left=window_left, softmax_scale=softmax_scale,
-                         dtype=_DT[q.dtype], cu_host=cu, cu_dev=_p(cu_seqlens),
-                         ctx_cu_host=ctx_cu, group_seq_cu_host=seq_cu)
+                         dtype=_DT[q.dtype], cu_host=cu, ctx_cu_host=ctx_cu,
+                         group_seq_cu_host=seq_cu, kv_head_of_q=kv_head_of_q)
 
 
 def _groups(ctx_cu_host, group_seq_cu_host):
@@ -58,22 +82,35 @@ def _groups(ctx_cu_host, group_seq_cu_host):
     return [int(c) for c in ctx_cu_host], [int(c) for c in group_seq_cu_host]
 
 
-def _need(t, shape, dtype, name):
-    """The C ABI takes plain pointers: check here that a tensor has the shape, dtype and
-    layout the call reads or writes through it."""
+def _need(t, shape, dtype, name, device=None):
+    """The C ABI takes plain pointers: check here that a tensor has the shape, dtype,
+    layout and device the call reads or writes through it (device: the first tensor's,
+    which must be a GPU)."""
     if t is None:
         return
     if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
         raise ValueError("%s: expected a contiguous %s tensor of shape %s, got %s %s%s"
                          % (name, dtype, tuple(shape), t.dtype, tuple(t.shape),
                             "" if t.is_contiguous() else " (not contiguous)"))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s; every tensor of the call must be on %s"
+                         % (name, t.device, device))
+
+
+def _gpu(t, name):
+    """The device of a call: its first tensor's, which must be a GPU tensor."""
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor (the kernels read device memory)" % name)
+    return t.device
 
 
 def _need_qkv(q, k, v, T, name):
     Hq, d = q.shape[1], q.shape[2]
-    _need(q, (T, Hq, d), q.dtype, "q" + name)
-    _need(k, (T, k.shape[1], d), q.dtype, "k" + name)
-    _need(v, (T, k.shape[1], d), q.dtype, "v" + name)
+    dev = _gpu(q, "q" + name)
+    _need(q, (T, Hq, d), q.dtype, "q" + name, dev)
+    _need(k, (T, k.shape[1], d), q.dtype, "k" + name, dev)
+    _need(v, (T, k.shape[1], d), q.dtype, "v" + name, dev)
+    return dev
 
 
 def _stream(device):
@@ -86,30 +123,35 @@ def _ws(params, call, device, workspace):
         L.check(L.DKV_ERR_INVALID_ARG)
     if n == 0:
         return None, 0
-    if workspace is not None and workspace.numel() * workspace.element_size() >= n:
-        return workspace, workspace.numel() * workspace.element_size()
+    if workspace is not None:
+        if workspace.device != device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on %s" % device)
+        if workspace.numel() * workspace.element_size() >= n:
+            return workspace, workspace.numel() * workspace.element_size()
     return torch.empty(n, dtype=torch.uint8, device=device), n
 
 
 def dkv_workspace_size(call: int, q, k, cu_seqlens, *, cu_host=None, ctx_len=0,
                        window_left=-1, softmax_scale=0.0, ctx_cu_host=None,
-                       group_seq_cu_host=None) -> int:
+                       group_seq_cu_host=None, kv_head_of_q=None) -> int:
     p, keep = _params(q, k, cu_seqlens, cu_host, ctx_len, window_left, softmax_scale,
-                      _groups(ctx_cu_host, group_seq_cu_host))
+                      _groups(ctx_cu_host, group_seq_cu_host), kv_head_of_q)
     return int(L.lib().dkv_workspace_size(p, call))
 
 
 def dkv_ctx_fwd(q, k, v, cu_seqlens, *, cu_host=None, window_left=-1, softmax_scale=0.0,
-                out=None, lse=None, workspace=None):
+                out=None, lse=None, workspace=None, kv_head_of_q=None):
     """Causal self-attention of each sequence of ``cu_seqlens`` (Call 1, eq. (3)).
-    q [T,Hq,d], k/v [T,Hkv,d] -> (o [T,Hq,d], lse [Hq,T] fp32)."""
-    p, keep = _params(q, k, cu_seqlens, cu_host, 0, window_left, softmax_scale)
+    q [T,Hq,d], k/v [T,Hkv,d] -> (o [T,Hq,d], lse [Hq,T] fp32).  kv_head_of_q: optional
+    GQA map (q-head h reads kv head kv_head_of_q[h]; default h // (Hq / Hkv))."""
+    p, keep = _params(q, k, cu_seqlens, cu_host, 0, window_left, softmax_scale,
+                      kv_head_of_q=kv_head_of_q)
     T, Hq, _ = q.shape
-    _need_qkv(q, k, v, p.cu_seqlens_host[p.num_seqs], "")
+    dev = _need_qkv(q, k, v, p.cu_seqlens_host[p.num_seqs], "")
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device) if lse is None else lse
-    _need(o, q.shape, q.dtype, "out")
-    _need(lse, (Hq, T), torch.float32, "lse")
+    _need(o, q.shape, q.dtype, "out", dev)
+    _need(lse, (Hq, T), torch.float32, "lse", dev)
     ws, nws = _ws(p, L.DKV_CALL_CTX_FWD, q.device, workspace)
     L.check(L.lib().dkv_ctx_fwd(p, _p(q), _p(k), _p(v), _p(o), _p(lse), _p(ws), nws,
                                 _stream(q.device)))
@@ -118,21 +160,21 @@ def dkv_ctx_fwd(q, k, v, cu_seqlens, *, cu_host=None, window_left=-1, softmax_sc
 
 def dkv_fwd(q_resp, k_p, v_p, k_r, v_r, cu_seqlens, *, cu_host=None, window_left=-1,
             softmax_scale=0.0, out=None, lse=None, workspace=None, ctx_cu_host=None,
-            group_seq_cu_host=None):
+            group_seq_cu_host=None, kv_head_of_q=None):
     """Shared-prompt attention of the responses (Call 2, eq. (4)); P = k_p.shape[0].
     With prompt groups, group j's prompt is rows ctx_cu_host[j]..ctx_cu_host[j+1] of
     k_p/v_p, shared by sequences group_seq_cu_host[j]..group_seq_cu_host[j+1].
-    -> (o_r [T_R,Hq,d], lse_r [Hq,T_R] fp32)."""
+    kv_head_of_q as in dkv_ctx_fwd.  -> (o_r [T_R,Hq,d], lse_r [Hq,T_R] fp32)."""
     p, keep = _params(q_resp, k_r, cu_seqlens, cu_host, k_p.shape[0], window_left,
-                      softmax_scale, _groups(ctx_cu_host, group_seq_cu_host))
+                      softmax_scale, _groups(ctx_cu_host, group_seq_cu_host), kv_head_of_q)
     T, Hq, _ = q_resp.shape
-    _need_qkv(q_resp, k_r, v_r, p.cu_seqlens_host[p.num_seqs], "_r")
-    _need(k_p, (k_p.shape[0],) + tuple(k_r.shape[1:]), q_resp.dtype, "k_p")
-    _need(v_p, k_p.shape, q_resp.dtype, "v_p")
+    dev = _need_qkv(q_resp, k_r, v_r, p.cu_seqlens_host[p.num_seqs], "_r")
+    _need(k_p, (k_p.shape[0],) + tuple(k_r.shape[1:]), q_resp.dtype, "k_p", dev)
+    _need(v_p, k_p.shape, q_resp.dtype, "v_p", dev)
     o = torch.empty_like(q_resp) if out is None else out
     lse = torch.empty((Hq, T), dtype=torch.float32, device=q_resp.device) if lse is None else lse
-    _need(o, q_resp.shape, q_resp.dtype, "out")
-    _need(lse, (Hq, T), torch.float32, "lse")
+    _need(o, q_resp.shape, q_resp.dtype, "out", dev)
+    _need(lse, (Hq, T), torch.float32, "lse", dev)
     ws, nws = _ws(p, L.DKV_CALL_FWD, q_resp.device, workspace)
     L.check(L.lib().dkv_fwd(p, _p(q_resp), _p(k_p), _p(v_p), _p(k_r), _p(v_r), _p(o), _p(lse),
                             _p(ws), nws, _stream(q_resp.device)))
@@ -141,25 +183,28 @@ def dkv_fwd(q_resp, k_p, v_p, k_r, v_r, cu_seqlens, *, cu_host=None, window_left
 
 def dkv_ctx_bwd(q, k, v, o, lse, dout, cu_seqlens, *, cu_host=None, window_left=-1,
                 softmax_scale=0.0, dq=None, dk=None, dv=None, acc_dk=None, acc_dv=None,
-                acc_flags=0, workspace=None):
+                acc_flags=0, workspace=None, kv_head_of_q=None):
     """Backward of Call 1 (eq. (3)).  Without accumulators dk/dv are written directly;
     with acc_dk/acc_dv (fp32 [T,Hkv,d]) the key/value gradients are added into them
     (cleared first with DKV_ACC_ZERO, cast into dk/dv with DKV_ACC_FINALIZE).
-    -> (dq, dk, dv)."""
-    p, keep = _params(q, k, cu_seqlens, cu_host, 0, window_left, softmax_scale)
-    _need_qkv(q, k, v, p.cu_seqlens_host[p.num_seqs], "")
-    _need(o, q.shape, q.dtype, "o")
-    _need(dout, q.shape, q.dtype, "dout")
-    _need(lse, (q.shape[1], q.shape[0]), torch.float32, "lse")
+    kv_head_of_q as in dkv_ctx_fwd.  -> (dq, dk, dv)."""
+    p, keep = _params(q, k, cu_seqlens, cu_host, 0, window_left, softmax_scale,
+                      kv_head_of_q=kv_head_of_q)
+    dev = _need_qkv(q, k, v, p.cu_seqlens_host[p.num_seqs], "")
+    _need(o, q.shape, q.dtype, "o", dev)
+    _need(dout, q.shape, q.dtype, "dout", dev)
+    _need(lse, (q.shape[1], q.shape[0]), torch.float32, "lse", dev)
+    if (acc_dk is None) != (acc_dv is None):
+        raise ValueError("acc_dk and acc_dv go together")
     dq = torch.empty_like(q) if dq is None else dq
     if acc_dk is None or (acc_flags & L.DKV_ACC_FINALIZE):
         dk = torch.empty_like(k) if dk is None else dk
         dv = torch.empty_like(v) if dv is None else dv
-    _need(dq, q.shape, q.dtype, "dq")
-    _need(dk, k.shape, k.dtype, "dk")
-    _need(dv, k.shape, k.dtype, "dv")
-    _need(acc_dk, k.shape, torch.float32, "acc_dk")
-    _need(acc_dv, k.shape, torch.float32, "acc_dv")
+    _need(dq, q.shape, q.dtype, "dq", dev)
+    _need(dk, k.shape, k.dtype, "dk", dev)
+    _need(dv, k.shape, k.dtype, "dv", dev)
+    _need(acc_dk, k.shape, torch.float32, "acc_dk", dev)
+    _need(acc_dv, k.shape, torch.float32, "acc_dv", dev)
     ws, nws = _ws(p, L.DKV_CALL_CTX_BWD, q.device, workspace)
     L.check(L.lib().dkv_ctx_bwd(p, _p(q), _p(k), _p(v), _p(o), _p(lse), _p(dout), _p(dq),
                                 _p(dk), _p(dv), _p(acc_dk), _p(acc_dv), int(acc_flags), _p(ws),
@@ -170,33 +215,33 @@ def dkv_ctx_bwd(q, k, v, o, lse, dout, cu_seqlens, *, cu_host=None, window_left=
 def dkv_bwd(q_resp, k_p, v_p, k_r, v_r, o_r, lse_r, dout_r, cu_seqlens, *, acc_dk_p, acc_dv_p,
             acc_flags=0, cu_host=None, window_left=-1, softmax_scale=0.0, dq_r=None, dk_r=None,
             dv_r=None, dk_p=None, dv_p=None, workspace=None, ctx_cu_host=None,
-            group_seq_cu_host=None):
+            group_seq_cu_host=None, kv_head_of_q=None):
     """Backward of Call 2 (eq. (4), §3.2).  Adds the responses' prompt-key gradients
     into acc_dk_p/acc_dv_p (fp32 [P,Hkv,d]); with DKV_ACC_FINALIZE also casts the
     accumulator into dk_p/dv_p; with DKV_ACC_SPLIT the terms reach the accumulator
     through per-chunk slices and a fixed-order sum instead of atomic adds.
-    Prompt groups as in dkv_fwd.  -> (dq_r, dk_r, dv_r, dk_p, dv_p)."""
+    Prompt groups and kv_head_of_q as in dkv_fwd.  -> (dq_r, dk_r, dv_r, dk_p, dv_p)."""
     p, keep = _params(q_resp, k_r, cu_seqlens, cu_host, k_p.shape[0], window_left,
-                      softmax_scale, _groups(ctx_cu_host, group_seq_cu_host))
-    _need_qkv(q_resp, k_r, v_r, p.cu_seqlens_host[p.num_seqs], "_r")
-    _need(k_p, (k_p.shape[0],) + tuple(k_r.shape[1:]), q_resp.dtype, "k_p")
-    _need(v_p, k_p.shape, q_resp.dtype, "v_p")
-    _need(o_r, q_resp.shape, q_resp.dtype, "o_r")
-    _need(dout_r, q_resp.shape, q_resp.dtype, "dout_r")
-    _need(lse_r, (q_resp.shape[1], q_resp.shape[0]), torch.float32, "lse_r")
-    _need(acc_dk_p, k_p.shape, torch.float32, "acc_dk_p")
-    _need(acc_dv_p, k_p.shape, torch.float32, "acc_dv_p")
+                      softmax_scale, _groups(ctx_cu_host, group_seq_cu_host), kv_head_of_q)
+    dev = _need_qkv(q_resp, k_r, v_r, p.cu_seqlens_host[p.num_seqs], "_r")
+    _need(k_p, (k_p.shape[0],) + tuple(k_r.shape[1:]), q_resp.dtype, "k_p", dev)
+    _need(v_p, k_p.shape, q_resp.dtype, "v_p", dev)
+    _need(o_r, q_resp.shape, q_resp.dtype, "o_r", dev)
+    _need(dout_r, q_resp.shape, q_resp.dtype, "dout_r", dev)
+    _need(lse_r, (q_resp.shape[1], q_resp.shape[0]), torch.float32, "lse_r", dev)
+    _need(acc_dk_p, k_p.shape, torch.float32, "acc_dk_p", dev)
+    _need(acc_dv_p, k_p.shape, torch.float32, "acc_dv_p", dev)
     dq_r = torch.empty_like(q_resp) if dq_r is None else dq_r
     dk_r = torch.empty_like(k_r) if dk_r is None else dk_r
     dv_r = torch.empty_like(v_r) if dv_r is None else dv_r
     if acc_flags & L.DKV_ACC_FINALIZE:
         dk_p = torch.empty_like(k_p) if dk_p is None else dk_p
         dv_p = torch.empty_like(v_p) if dv_p is None else dv_p
-    _need(dq_r, q_resp.shape, q_resp.dtype, "dq_r")
-    _need(dk_r, k_r.shape, k_r.dtype, "dk_r")
-    _need(dv_r, k_r.shape, k_r.dtype, "dv_r")
-    _need(dk_p, k_p.shape, k_p.dtype, "dk_p")
-    _need(dv_p, k_p.shape, k_p.dtype, "dv_p")
+    _need(dq_r, q_resp.shape, q_resp.dtype, "dq_r", dev)
+    _need(dk_r, k_r.shape, k_r.dtype, "dk_r", dev)
+    _need(dv_r, k_r.shape, k_r.dtype, "dv_r", dev)
+    _need(dk_p, k_p.shape, k_p.dtype, "dk_p", dev)
+    _need(dv_p, k_p.shape, k_p.dtype, "dv_p", dev)
     call = L.DKV_CALL_BWD_SPLIT if acc_flags & L.DKV_ACC_SPLIT else L.DKV_CALL_BWD
     ws, nws = _ws(p, call, q_resp.device, workspace)
     L.check(L.lib().dkv_bwd(p, _p(q_resp), _p(k_p), _p(v_p), _p(k_r), _p(v_r), _p(o_r),
@@ -207,7 +252,17 @@ def dkv_bwd(q_resp, k_p, v_p, k_r, v_r, o_r, lse_r, dout_r, cu_seqlens, *, acc_d
 
 
 def dkv_cast_acc(acc_dk, acc_dv, dk, dv):
-    """Cast the fp32 accumulators into dk/dv (their dtype), once."""
+    """Cast the fp32 accumulators acc_dk/acc_dv [rows, Hkv, d] into dk/dv (same shape,
+    bf16 / fp16 / fp32), once."""
+    dev = _gpu(acc_dk, "acc_dk")
+    if acc_dk.dim() != 3:
+        raise ValueError("acc_dk must be [rows, Hkv, d]")
+    if dk is None or dv is None or dk.dtype not in _DT:
+        raise ValueError("dk and dv must be bf16, fp16 or fp32 tensors")
+    _need(acc_dk, acc_dk.shape, torch.float32, "acc_dk", dev)
+    _need(acc_dv, acc_dk.shape, torch.float32, "acc_dv", dev)
+    _need(dk, acc_dk.shape, dk.dtype, "dk", dev)
+    _need(dv, acc_dk.shape, dk.dtype, "dv", dev)
     rows, Hkv, d = acc_dk.shape
     p, keep = L.make_params(num_seqs=0, ctx_len=0, num_heads_q=Hkv, num_heads_kv=Hkv,
                             head_dim=d, dtype=_DT[dk.dtype], cu_host=[0])
@@ -246,6 +301,9 @@ def dkv_layout(op: int, x, cu_host, ctx_len: int, *, ctx_cu_host=None, group_seq
         raise ValueError("layout op %d expects %d input rows, got %d" % (op, rows_in, x.shape[0]))
     if not x.is_contiguous():
         raise ValueError("x must be contiguous")
+    dev = _gpu(x, "x")
+    if out is not None and out.device != dev:
+        raise ValueError("out is on %s; x is on %s" % (out.device, dev))
     row_elems = math.prod(x.shape[1:])
     if out is not None and (tuple(out.shape) != (rows_out,) + tuple(x.shape[1:])
                             or out.dtype != x.dtype or not out.is_contiguous()):
@@ -274,22 +332,25 @@ def _prompt_cu(P, ctx_cu_host, device):
 
 
 def dualkv_forward(q_p, k_p, v_p, q_r, k_r, v_r, cu_seqlens, *, cu_host=None, window_left=-1,
-                   softmax_scale=0.0, ctx_cu_host=None, group_seq_cu_host=None):
+                   softmax_scale=0.0, ctx_cu_host=None, group_seq_cu_host=None,
+                   kv_head_of_q=None):
     """The two calls of the forward: Call 1 over the prompt(s), Call 2 over the
     responses.  With prompt groups (see dkv_fwd), Call 1 is varlen causal attention
     over the prompts.  -> (o_p, lse_p, o_r, lse_r)."""
     cu_p, cu_p_host = _prompt_cu(q_p.shape[0], ctx_cu_host, q_p.device)
     o_p, lse_p = dkv_ctx_fwd(q_p, k_p, v_p, cu_p, cu_host=cu_p_host, window_left=window_left,
-                             softmax_scale=softmax_scale)
+                             softmax_scale=softmax_scale, kv_head_of_q=kv_head_of_q)
     o_r, lse_r = dkv_fwd(q_r, k_p, v_p, k_r, v_r, cu_seqlens, cu_host=cu_host,
                          window_left=window_left, softmax_scale=softmax_scale,
-                         ctx_cu_host=ctx_cu_host, group_seq_cu_host=group_seq_cu_host)
+                         ctx_cu_host=ctx_cu_host, group_seq_cu_host=group_seq_cu_host,
+                         kv_head_of_q=kv_head_of_q)
     return o_p, lse_p, o_r, lse_r
 
 
 def dualkv_backward(q_p, k_p, v_p, q_r, k_r, v_r, o_p, lse_p, o_r, lse_r, do_p, do_r,
                     cu_seqlens, *, cu_host=None, window_left=-1, softmax_scale=0.0,
-                    acc=None, split=False, ctx_cu_host=None, group_seq_cu_host=None):
+                    acc=None, split=False, ctx_cu_host=None, group_seq_cu_host=None,
+                    kv_head_of_q=None):
     """The two calls of the backward sharing one fp32 accumulator for dK_P/dV_P
     (eq. (6)): Call 1 clears it and adds the prompt self-attention term, Call 2 adds
     the N responses' terms and casts once (split=True: through per-chunk slices and a
@@ -300,7 +361,8 @@ def dualkv_backward(q_p, k_p, v_p, q_r, k_r, v_r, o_p, lse_p, o_r, lse_r, do_p, 
     cu_p, cu_p_host = _prompt_cu(q_p.shape[0], ctx_cu_host, q_p.device)
     dq_p, _, _ = dkv_ctx_bwd(q_p, k_p, v_p, o_p, lse_p, do_p, cu_p, cu_host=cu_p_host,
                              window_left=window_left, softmax_scale=softmax_scale,
-                             acc_dk=acc[0], acc_dv=acc[1], acc_flags=DKV_ACC_ZERO)
+                             acc_dk=acc[0], acc_dv=acc[1], acc_flags=DKV_ACC_ZERO,
+                             kv_head_of_q=kv_head_of_q)
     dq_r, dk_r, dv_r, dk_p, dv_p = dkv_bwd(q_r, k_p, v_p, k_r, v_r, o_r, lse_r, do_r,
                                            cu_seqlens, acc_dk_p=acc[0], acc_dv_p=acc[1],
                                            acc_flags=DKV_ACC_FINALIZE | (DKV_ACC_SPLIT if split else 0),
@@ -308,5 +370,6 @@ def dualkv_backward(q_p, k_p, v_p, q_r, k_r, v_r, o_p, lse_p, o_r, lse_r, do_p, 
                                            window_left=window_left,
                                            softmax_scale=softmax_scale,
                                            ctx_cu_host=ctx_cu_host,
-                                           group_seq_cu_host=group_seq_cu_host)
+                                           group_seq_cu_host=group_seq_cu_host,
+                                           kv_head_of_q=kv_head_of_q)
     return {"dq_p": dq_p, "dk_p": dk_p, "dv_p": dv_p, "dq_r": dq_r, "dk_r": dk_r, "dv_r": dv_r}

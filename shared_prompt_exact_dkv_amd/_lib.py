@@ -37,6 +37,7 @@ class DkvParams(ctypes.Structure):
         ("num_groups", ctypes.c_int32),
         ("ctx_cu_host", ctypes.POINTER(ctypes.c_int32)),
         ("group_seq_cu_host", ctypes.POINTER(ctypes.c_int32)),
+        ("kv_head_of_q", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -121,17 +122,19 @@ def _i32(vals):
 
 def make_params(*, num_seqs, ctx_len, num_heads_q, num_heads_kv, head_dim, window_left=-1,
                 softmax_scale=0.0, dtype=DKV_BF16, cu_host=None, cu_dev=0, ctx_cu_host=None,
-                group_seq_cu_host=None):
+                group_seq_cu_host=None, kv_head_of_q=None):
     """Build a DkvParams.  Returns (params, keepalive); keep the second alive while the
-    params are in use (it owns the host arrays: cu_seqlens and the prompt groups)."""
+    params are in use (it owns the host arrays: cu_seqlens, the prompt groups and the
+    head map)."""
     arr, ptr = _i32(cu_host)
     carr, cptr = _i32(ctx_cu_host)
     garr, gptr = _i32(group_seq_cu_host)
+    harr, hptr = _i32(kv_head_of_q)
     ng = 0
     if ctx_cu_host is not None or group_seq_cu_host is not None:
         if ctx_cu_host is None or group_seq_cu_host is None:
             raise ValueError("ctx_cu_host and group_seq_cu_host go together")
         ng = len(ctx_cu_host) - 1
     p = DkvParams(num_seqs, ctx_len, num_heads_q, num_heads_kv, head_dim, window_left,
-                  float(softmax_scale), dtype, ptr, cu_dev, ng, cptr, gptr)
-    return p, (arr, carr, garr)
+                  float(softmax_scale), dtype, ptr, cu_dev, ng, cptr, gptr, hptr)
+    return p, (arr, carr, garr, harr)

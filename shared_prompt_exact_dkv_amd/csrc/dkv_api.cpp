@@ -59,6 +59,10 @@ struct Shape {
   // A call without groups has one, of all P rows and all N sequences.
   std::vector<int> gctx, gseq;
   std::vector<int> sctx0, sP;  // per sequence: first row and length of its prompt
+  // Explicit GQA head map (dkv_params::kv_head_of_q): qhead[g * G + j] is the j-th
+  // q-head (in increasing order) of kv head g.  Empty for the contiguous map
+  // h = g * G + j, which the kernels compute themselves.
+  std::vector<int32_t> qhead;
   int bm_tok;               // query tokens per forward workgroup
   int bm_tok_dq;            // query tokens per dQ workgroup
   int kv_tile;              // keys per dK/dV workgroup
@@ -150,8 +154,33 @@ dkv_status check_params(const dkv_params *p, bool is_ctx, Shape *s) {
   s->dtype = p->dtype;
   s->scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
   if (dkv_status st = check_seqs(p, is_ctx, s)) return st;
-  if (s->T > 0 && !p->cu_seqlens_dev)
-    return fail(DKV_ERR_INVALID_ARG, "cu_seqlens_dev is NULL");
+  s->qhead.clear();
+  if (p->kv_head_of_q) {
+    // Every kv head must serve exactly G q-heads; the kernels take the members of a kv
+    // head in increasing q-head order.  The contiguous map is run as no map.
+    std::vector<int> cnt(s->Hkv, 0);
+    bool contiguous = true;
+    for (int h = 0; h < s->Hq; ++h) {
+      const int k = p->kv_head_of_q[h];
+      if (k < 0 || k >= s->Hkv)
+        return fail(DKV_ERR_INVALID_ARG, "kv_head_of_q[%d] = %d is outside [0, %d)", h, k, s->Hkv);
+      ++cnt[k];
+      contiguous = contiguous && k == h / G;
+    }
+    for (int k = 0; k < s->Hkv; ++k)
+      if (cnt[k] != G)
+        return fail(DKV_ERR_INVALID_ARG,
+                    "kv_head_of_q gives kv head %d %d q-heads; every kv head needs Hq / Hkv = %d",
+                    k, cnt[k], G);
+    if (!contiguous) {
+      s->qhead.assign((size_t)s->Hq, 0);
+      std::vector<int> fill(s->Hkv, 0);
+      for (int h = 0; h < s->Hq; ++h) {
+        const int k = p->kv_head_of_q[h];
+        s->qhead[(size_t)k * G + fill[k]++] = h;
+      }
+    }
+  }
   {
     // A window at least as long as the longest logical position sees every earlier
     // key: it is the global causal mask, and is run as one (the kernels form key + wl
@@ -283,11 +312,17 @@ std::vector<QItem> build_q_items(const Shape &s, int bm_tok, int BN) {
   return interleave_xcds(lists);
 }
 
-// ----------------------------------------------------- pinned staging of lists --
+// ------------------------------------------------------- staging of lists --
 //
-// Work lists are built on the host and copied into the workspace on the caller's
-// stream.  Each copy reads from a pinned host slot that is not reused before an
-// event recorded after the copy has completed.
+// Work lists and the per-call tables (sequence bounds, head map) are built on the host
+// and copied into the workspace on the caller's stream, in one copy per call.
+//   Pinned (the entry points with a caller workspace): the copy reads a pinned host
+//   slot, reused only once the event recorded after its copy has completed.  Slots are
+//   polled, never waited for: when every slot is still in flight a new one is added, so
+//   a call never blocks the host (the pool grows with the caller's run-ahead).
+//   Pageable (the entry point that allocates nothing): the copy reads the host vector
+//   itself; HIP performs a copy from unpinned host memory synchronously, so the call
+//   returns once the data has left the host buffer, which is then free to go.
 
 struct StagingRing {
   struct Slot {
@@ -298,7 +333,6 @@ struct StagingRing {
   };
   std::mutex mu;
   std::map<int, std::vector<Slot>> per_device;
-  size_t next = 0;
 };
 
 StagingRing &ring() {
@@ -319,42 +353,72 @@ dkv_status check_not_capturing(hipStream_t stream) {
   return DKV_OK;
 }
 
-dkv_status upload(const void *src, size_t bytes, void *dst, hipStream_t stream) {
+enum class Staging { kPinned, kPageable };
+
+dkv_status upload(const void *src, size_t bytes, void *dst, hipStream_t stream,
+                  Staging how = Staging::kPinned) {
   if (bytes == 0) return DKV_OK;
+  hipError_t e;
+  if (how == Staging::kPageable) {
+    e = hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work lists, pageable)");
+    return DKV_OK;
+  }
   int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   StagingRing &r = ring();
   std::lock_guard<std::mutex> lock(r.mu);
   auto &slots = r.per_device[dev];
-  if (slots.empty()) slots.resize(8);
-  StagingRing::Slot &sl = slots[r.next++ % slots.size()];
-  if (sl.pending) {
-    e = hipEventSynchronize(sl.ev);
-    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(staging)");
-    sl.pending = false;
+  StagingRing::Slot *fit = nullptr, *any = nullptr;
+  for (auto &x : slots) {
+    if (x.pending) {
+      e = hipEventQuery(x.ev);
+      if (e == hipSuccess)
+        x.pending = false;
+      else if (e != hipErrorNotReady)
+        return hip_fail(e, "hipEventQuery(staging)");
+    }
+    if (x.pending) continue;
+    if (!any) any = &x;
+    if (x.cap >= bytes && (!fit || x.cap < fit->cap)) fit = &x;
   }
-  if (!sl.ev) {
-    e = hipEventCreateWithFlags(&sl.ev, hipEventDisableTiming);
+  StagingRing::Slot *sl = fit ? fit : any;
+  if (!sl) {
+    slots.emplace_back();
+    sl = &slots.back();
+  }
+  if (!sl->ev) {
+    e = hipEventCreateWithFlags(&sl->ev, hipEventDisableTiming);
     if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
   }
-  if (sl.cap < bytes) {
-    if (sl.host) (void)hipHostFree(sl.host);
-    sl.host = nullptr;
-    sl.cap = 0;
+  if (sl->cap < bytes) {
+    if (sl->host) (void)hipHostFree(sl->host);
+    sl->host = nullptr;
+    sl->cap = 0;
     size_t cap = std::max<size_t>(bytes, 64 * 1024);
-    e = hipHostMalloc(&sl.host, cap, hipHostMallocDefault);
+    e = hipHostMalloc(&sl->host, cap, hipHostMallocDefault);
     if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(staging)");
-    sl.cap = cap;
+    sl->cap = cap;
   }
-  std::memcpy(sl.host, src, bytes);
-  e = hipMemcpyAsync(dst, sl.host, bytes, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work list)");
-  e = hipEventRecord(sl.ev, stream);
+  std::memcpy(sl->host, src, bytes);
+  e = hipMemcpyAsync(dst, sl->host, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work lists)");
+  e = hipEventRecord(sl->ev, stream);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord(staging)");
-  sl.pending = true;
+  sl->pending = true;
   return DKV_OK;
 }
+
+// The host image of a call's staged region (work lists and tables at the offsets of the
+// workspace plan), copied to the workspace in one upload.
+struct StagedImage {
+  std::vector<char> bytes;
+  explicit StagedImage(size_t n) : bytes(n, 0) {}
+  void put(size_t off, const void *src, size_t n) {
+    if (n) std::memcpy(bytes.data() + off, src, n);
+  }
+};
 
 // -------------------------------------------------------------- kernel timing --
 
@@ -402,9 +466,29 @@ template <typename F> hipError_t timed(int cls, hipStream_t stream, F &&fn) {
 
 // ------------------------------------------------------------ workspace plans --
 
+// A call's staged region: its work lists, then the tables the kernels read (the host
+// copy of cu_seqlens for the key-parallel kernels, the GQA head table when a map is
+// given), at 256-byte aligned offsets from the region's start.
+struct StagedPlan {
+  size_t q_off = 0, kv_off = 0, cu_off = 0, qhead_off = 0, bytes = 0;
+  size_t n_q = 0, n_kv = 0;
+};
+
+StagedPlan plan_staged(const Shape &s, size_t n_q, size_t n_kv, bool with_cu) {
+  StagedPlan sp;
+  sp.n_q = n_q;
+  sp.n_kv = n_kv;
+  sp.q_off = 0;
+  sp.kv_off = sp.q_off + align_up(n_q * sizeof(QItem));
+  sp.cu_off = sp.kv_off + align_up(n_kv * sizeof(KVItem));
+  sp.qhead_off = sp.cu_off + (with_cu ? align_up((size_t)(s.N + 1) * sizeof(int32_t)) : 0);
+  sp.bytes = sp.qhead_off + align_up(s.qhead.size() * sizeof(int32_t));
+  return sp;
+}
+
 struct FwdPlan {
-  size_t items_off = 0, bytes = 0;
-  size_t n_items = 0;
+  StagedPlan st;   // at offset 0 of the workspace
+  size_t bytes = 0;
 };
 
 size_t count_q_items(const Shape &s, int bm_tok) {
@@ -418,10 +502,8 @@ size_t count_q_items(const Shape &s, int bm_tok) {
 
 FwdPlan plan_fwd(const Shape &s) {
   FwdPlan pl;
-  size_t n = count_q_items(s, s.bm_tok);
-  pl.n_items = n;
-  pl.items_off = 0;
-  pl.bytes = align_up(n * sizeof(QItem));
+  pl.st = plan_staged(s, count_q_items(s, s.bm_tok), 0, false);
+  pl.bytes = pl.st.n_q ? pl.st.bytes : 0;
   return pl;
 }
 
@@ -435,17 +517,24 @@ dkv_status check_ws(void *ws, size_t ws_bytes, size_t need) {
   return DKV_OK;
 }
 
+const int32_t *qhead_dev(const Shape &s, char *staged, const StagedPlan &sp) {
+  return s.qhead.empty() ? nullptr : reinterpret_cast<const int32_t *>(staged + sp.qhead_off);
+}
+
 dkv_status run_fwd(const Shape &s, const void *q, const void *kc, const void *vc,
                    const void *ko, const void *vo, void *o, float *lse, void *ws,
-                   size_t ws_bytes, hipStream_t stream) {
+                   size_t ws_bytes, hipStream_t stream, Staging how) {
   FwdPlan pl = plan_fwd(s);
   dkv_status st = check_ws(ws, ws_bytes, pl.bytes);
   if (st != DKV_OK) return st;
-  if (pl.n_items > 0 && (st = check_not_capturing(stream)) != DKV_OK) return st;
-  if (pl.n_items == 0) return DKV_OK;
+  if (pl.st.n_q > 0 && (st = check_not_capturing(stream)) != DKV_OK) return st;
+  if (pl.st.n_q == 0) return DKV_OK;
   std::vector<QItem> items = build_q_items(s, s.bm_tok, kFwdBN);
   char *wsb = static_cast<char *>(ws);
-  st = upload(items.data(), items.size() * sizeof(QItem), wsb + pl.items_off, stream);
+  StagedImage img(pl.st.bytes);
+  img.put(pl.st.q_off, items.data(), items.size() * sizeof(QItem));
+  img.put(pl.st.qhead_off, s.qhead.data(), s.qhead.size() * sizeof(int32_t));
+  st = upload(img.bytes.data(), img.bytes.size(), wsb, stream, how);
   if (st != DKV_OK) return st;
   FwdArgs a{};
   a.q = q;
@@ -455,7 +544,8 @@ dkv_status run_fwd(const Shape &s, const void *q, const void *kc, const void *vc
   a.v_own = vo;
   a.o = o;
   a.lse = lse;
-  a.items = reinterpret_cast<const QItem *>(wsb + pl.items_off);
+  a.items = reinterpret_cast<const QItem *>(wsb + pl.st.q_off);
+  a.qhead = qhead_dev(s, wsb, pl.st);
   a.Hq = s.Hq;
   a.Hkv = s.Hkv;
   a.G = s.G;
@@ -599,14 +689,13 @@ std::vector<KVItem> build_kv_items(const Shape &s, bool with_ctx, bool split) {
 }
 
 struct BwdPlan {
-  size_t d_off = 0, l2_off = 0, q_off = 0, kv_off = 0, split_off = 0, bytes = 0;
-  size_t n_q = 0, n_kv = 0;
+  size_t d_off = 0, l2_off = 0, st_off = 0, split_off = 0, bytes = 0;
+  StagedPlan st;   // at st_off
   int slices = 0;
 };
 
 BwdPlan plan_bwd(const Shape &s, bool with_ctx, bool split) {
   BwdPlan pl;
-  pl.n_q = count_q_items(s, s.bm_tok_dq);
   size_t nkv = 0;
   for (int i = 0; i < s.N; ++i) {
     int len = s.cu[i + 1] - s.cu[i];
@@ -618,12 +707,12 @@ BwdPlan plan_bwd(const Shape &s, bool with_ctx, bool split) {
       if (Pg > 0)
         nkv += (size_t)((Pg + s.kv_tile - 1) / s.kv_tile) * ctx_chunks(s, pg, split).size();
     }
-  pl.n_kv = nkv * s.Hkv;   // upper bound (empty windowed items are dropped)
+  // nkv * Hkv is an upper bound (empty windowed items are dropped)
+  pl.st = plan_staged(s, count_q_items(s, s.bm_tok_dq), nkv * s.Hkv, true);
   pl.d_off = 0;
   pl.l2_off = align_up((size_t)s.Hq * s.T * sizeof(float));
-  pl.q_off = pl.l2_off + align_up((size_t)s.Hq * s.T * sizeof(float));
-  pl.kv_off = pl.q_off + align_up(pl.n_q * sizeof(QItem));
-  pl.split_off = pl.kv_off + align_up(pl.n_kv * sizeof(KVItem));
+  pl.st_off = pl.l2_off + align_up((size_t)s.Hq * s.T * sizeof(float));
+  pl.split_off = pl.st_off + pl.st.bytes;
   pl.bytes = pl.split_off;
   if (split && with_ctx && s.P > 0) {   // dK and dV slices
     pl.slices = split_slices(s);
@@ -634,7 +723,6 @@ BwdPlan plan_bwd(const Shape &s, bool with_ctx, bool split) {
 }
 
 struct BwdIO {
-  const int32_t *cu_dev;
   const void *q, *kc, *vc, *ko, *vo, *o, *dout;
   const float *lse;
   void *dq, *dk_own, *dv_own;
@@ -646,7 +734,7 @@ struct BwdIO {
 };
 
 dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
-                   hipStream_t stream) {
+                   hipStream_t stream, Staging how) {
   const bool split = (io.flags & DKV_ACC_SPLIT) && io.with_ctx && s.P > 0;
   BwdPlan pl = plan_bwd(s, io.with_ctx, split);
   dkv_status st = check_ws(ws, ws_bytes, pl.bytes);
@@ -675,8 +763,17 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
     }
     std::vector<QItem> qi = build_q_items(s, s.bm_tok_dq, kFwdBN);
     std::vector<KVItem> kv = build_kv_items(s, io.with_ctx, split);
-    if ((st = upload(qi.data(), qi.size() * sizeof(QItem), wsb + pl.q_off, stream)) != DKV_OK) return st;
-    if ((st = upload(kv.data(), kv.size() * sizeof(KVItem), wsb + pl.kv_off, stream)) != DKV_OK) return st;
+    if (qi.size() != pl.st.n_q || kv.size() > pl.st.n_kv)
+      return fail(DKV_ERR_INVALID_ARG, "internal: work lists exceed their plan");
+    char *stb = wsb + pl.st_off;
+    {
+      StagedImage img(pl.st.bytes);
+      img.put(pl.st.q_off, qi.data(), qi.size() * sizeof(QItem));
+      img.put(pl.st.kv_off, kv.data(), kv.size() * sizeof(KVItem));
+      img.put(pl.st.cu_off, s.cu.data(), s.cu.size() * sizeof(int32_t));
+      img.put(pl.st.qhead_off, s.qhead.data(), s.qhead.size() * sizeof(int32_t));
+      if ((st = upload(img.bytes.data(), img.bytes.size(), stb, stream, how)) != DKV_OK) return st;
+    }
     BwdQArgs qa{};
     qa.q = io.q; qa.k_ctx = io.kc; qa.v_ctx = io.vc; qa.k_own = io.ko; qa.v_own = io.vo;
     qa.dout = io.dout; qa.lse = io.lse; qa.Dneg = Dneg; qa.dq = io.dq;
@@ -685,16 +782,19 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
       qa.Dneg_out = Dneg;
       qa.lsn_out = lsn;
     }
-    qa.items = reinterpret_cast<const QItem *>(wsb + pl.q_off);
+    qa.items = reinterpret_cast<const QItem *>(stb + pl.st.q_off);
+    qa.qhead = qhead_dev(s, stb, pl.st);
     qa.Hq = s.Hq; qa.Hkv = s.Hkv; qa.G = s.G; qa.bm_tok = s.bm_tok_dq;
     qa.window_left = s.wl; qa.lse_ld = (int)s.T; qa.scale = s.scale;
     e = timed(kKDq, stream, [&] { return launch_bwd_dq(s.dtype, s.d, qa, (int)qi.size(), stream); });
     if (e != hipSuccess) return hip_fail(e, "dq kernel launch");
     BwdKVArgs ka{};
     ka.q = io.q; ka.dout = io.dout; ka.k_ctx = io.kc; ka.v_ctx = io.vc; ka.k_own = io.ko;
-    ka.v_own = io.vo; ka.lse = io.lse; ka.Dneg = Dneg; ka.lsn = lsn; ka.cu = io.cu_dev;
+    ka.v_own = io.vo; ka.lse = io.lse; ka.Dneg = Dneg; ka.lsn = lsn;
+    ka.cu = reinterpret_cast<const int32_t *>(stb + pl.st.cu_off);
+    ka.qhead = qa.qhead;
     ka.dk_own = io.dk_own; ka.dv_own = io.dv_own; ka.acc_dk = io.acc_dk; ka.acc_dv = io.acc_dv;
-    ka.items = reinterpret_cast<const KVItem *>(wsb + pl.kv_off);
+    ka.items = reinterpret_cast<const KVItem *>(stb + pl.st.kv_off);
     ka.Hq = s.Hq; ka.Hkv = s.Hkv; ka.G = s.G; ka.window_left = s.wl;
     ka.lse_ld = (int)s.T; ka.own_to_acc = io.own_to_acc ? 1 : 0;
     ka.scale = s.scale;
@@ -937,7 +1037,7 @@ dkv_status dkv_ctx_fwd(const dkv_params *p, const void *q, const void *k, const 
       (st = check_ptr(v, "v", need)) || (st = check_ptr(o, "o", need)) ||
       (st = check_ptr(lse, "lse", need)))
     return st;
-  return run_fwd(s, q, k, v, k, v, o, lse, ws, ws_bytes, stream);
+  return run_fwd(s, q, k, v, k, v, o, lse, ws, ws_bytes, stream, Staging::kPinned);
 }
 
 dkv_status dkv_fwd(const dkv_params *p, const void *q_resp, const void *k_p, const void *v_p,
@@ -952,7 +1052,7 @@ dkv_status dkv_fwd(const dkv_params *p, const void *q_resp, const void *k_p, con
       (st = check_ptr(v_r, "v_r", need)) || (st = check_ptr(o_r, "o_r", need)) ||
       (st = check_ptr(lse_r, "lse_r", need)))
     return st;
-  return run_fwd(s, q_resp, k_p, v_p, k_r, v_r, o_r, lse_r, ws, ws_bytes, stream);
+  return run_fwd(s, q_resp, k_p, v_p, k_r, v_r, o_r, lse_r, ws, ws_bytes, stream, Staging::kPinned);
 }
 
 dkv_status dkv_ctx_bwd(const dkv_params *p, const void *q, const void *k, const void *v,
@@ -984,12 +1084,11 @@ dkv_status dkv_ctx_bwd(const dkv_params *p, const void *q, const void *k, const 
     if ((st = check_ptr(dk, "dk", need)) || (st = check_ptr(dv, "dv", need))) return st;
   }
   BwdIO io{};
-  io.cu_dev = p->cu_seqlens_dev;
   io.q = q; io.kc = k; io.vc = v; io.ko = k; io.vo = v; io.o = o; io.dout = dout; io.lse = lse;
   io.dq = dq; io.dk_own = dk; io.dv_own = dv; io.acc_dk = acc_dk; io.acc_dv = acc_dv;
   io.acc_rows = s.T; io.flags = acc_flags; io.dk_fin = dk; io.dv_fin = dv;
   io.with_ctx = false; io.own_to_acc = use_acc;
-  return run_bwd(s, io, ws, ws_bytes, stream);
+  return run_bwd(s, io, ws, ws_bytes, stream, Staging::kPinned);
 }
 
 dkv_status dkv_bwd(const dkv_params *p, const void *q_resp, const void *k_p, const void *v_p,
@@ -1017,13 +1116,12 @@ dkv_status dkv_bwd(const dkv_params *p, const void *q_resp, const void *k_p, con
       ((st = check_ptr(dk_p, "dk_p", needp)) || (st = check_ptr(dv_p, "dv_p", needp))))
     return st;
   BwdIO io{};
-  io.cu_dev = p->cu_seqlens_dev;
   io.q = q_resp; io.kc = k_p; io.vc = v_p; io.ko = k_r; io.vo = v_r; io.o = o_r;
   io.dout = dout_r; io.lse = lse_r; io.dq = dq_r; io.dk_own = dk_r; io.dv_own = dv_r;
   io.acc_dk = needp ? acc_dk_p : nullptr; io.acc_dv = needp ? acc_dv_p : nullptr;
   io.acc_rows = s.P; io.flags = acc_flags; io.dk_fin = dk_p; io.dv_fin = dv_p;
   io.with_ctx = true; io.own_to_acc = false;
-  return run_bwd(s, io, ws, ws_bytes, stream);
+  return run_bwd(s, io, ws, ws_bytes, stream, Staging::kPinned);
 }
 
 dkv_status dkv_cast_acc(const dkv_params *p, int32_t rows, const float *acc_dk,
@@ -1068,12 +1166,12 @@ dkv_status dkv_layout(const dkv_params *p, int op, int64_t row_elems, const void
   if (pl.items.empty()) return DKV_OK;
   if ((st = check_not_capturing(stream)) != DKV_OK) return st;
   char *wsb = static_cast<char *>(ws);
-  if ((st = upload(pl.items.data(), pl.items.size() * sizeof(RowItem), wsb + pl.items_off,
-                   stream)) != DKV_OK)
-    return st;
-  if (!pl.src.empty() &&
-      (st = upload(pl.src.data(), pl.src.size() * sizeof(int32_t), wsb + pl.src_off, stream)) != DKV_OK)
-    return st;
+  {
+    StagedImage img(pl.bytes);
+    img.put(pl.items_off, pl.items.data(), pl.items.size() * sizeof(RowItem));
+    img.put(pl.src_off, pl.src.data(), pl.src.size() * sizeof(int32_t));
+    if ((st = upload(img.bytes.data(), img.bytes.size(), wsb, stream)) != DKV_OK) return st;
+  }
   const int row_vecs = (int)(row_elems * (long)elem_size(s.dtype) / 16);
   hipError_t e = timed(kKLayout, stream, [&] {
     return launch_row_sum(s.dtype, in, out, reinterpret_cast<const RowItem *>(wsb + pl.items_off),

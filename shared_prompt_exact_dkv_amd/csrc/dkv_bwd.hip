@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_f32_kernel(BwdQArgs a) {
   const int hj = qr - tok * a.G;
   const bool row_valid = tok < nt;
   if (!row_valid) tok = nt - 1;
-  const int h = g * a.G + hj;
+  const int h = q_head(a.qhead, g, a.G, hj);
   const int P = it.ctx_len, wl = a.window_left;
   const int qpos = P + t0 + tok;
   const int qmin = P + t0, qmax = P + t0 + nt - 1;
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_h16_kernel(BwdQArgs a) {
   const int hj = qr - tok * a.G;
   const bool row_valid = tok < nt;
   if (!row_valid) tok = nt - 1;
-  const int h = g * a.G + hj;
+  const int h = q_head(a.qhead, g, a.G, hj);
   const int P = it.ctx_len, wl = a.window_left;
   const int qpos = P + t0 + tok;
   const int qmin = P + t0, qmax = P + t0 + nt - 1;
@@ -438,10 +438,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_h16_kernel(BwdQArgs a) {
 template <int HD> struct QStepRegs : RowRegs<float, HD, kBwdBM> {
   using T = float;
   using C = TileCfg<T, HD, kBwdBM>;
-  // base: row 0 of the sequence, first q-head of the group; rows f0 .. f0+31 of the
-  // flattened (token, head) index, loaded where flo <= row < fend (else zero).
-  __device__ __forceinline__ void load_flat(const T *base, long qld, int G, int f0, int flo,
-                                            int fend, int tid) {
+  // base: row 0 of the sequence, q-head 0; rows f0 .. f0+31 of the flattened (token,
+  // member j of kv head g) index, loaded where flo <= row < fend (else zero).
+  __device__ __forceinline__ void load_flat(const T *base, long qld, int G, int g,
+                                            const int32_t *qhead, int f0, int flo, int fend,
+                                            int tid) {
     constexpr int per_row = HD / 4;   // 16-byte chunks per row
 #pragma unroll
     for (int p = 0; p < C::kRowPasses; ++p) {
@@ -451,7 +452,8 @@ template <int HD> struct QStepRegs : RowRegs<float, HD, kBwdBM> {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (id < C::kChunks && f >= flo && f < fend) {
         int t = f / G, j = f - t * G;
-        v = *reinterpret_cast<const uint4 *>(base + (long)t * qld + (long)j * HD + ch * 4);
+        v = *reinterpret_cast<const uint4 *>(base + (long)t * qld +
+                                             (long)q_head(qhead, g, G, j) * HD + ch * 4);
       }
       this->r[p] = v;
     }
@@ -560,15 +562,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdKVArgs a) {
   auto issue = [&]() {
     const int s0 = sload_i32(a.cu, cs);
     const int lo = max(cf, cfa), hi = min(cf + BM, cfb);
-    const T *qb = reinterpret_cast<const T *>(a.q) + (long)s0 * qld + (long)g * G * HD;
-    const T *db_ = reinterpret_cast<const T *>(a.dout) + (long)s0 * qld + (long)g * G * HD;
-    qregs.load_flat(qb, qld, G, cf, lo, hi, tid);
-    dregs.load_flat(db_, qld, G, cf, lo, hi, tid);
+    const T *qb = reinterpret_cast<const T *>(a.q) + (long)s0 * qld;
+    const T *db_ = reinterpret_cast<const T *>(a.dout) + (long)s0 * qld;
+    qregs.load_flat(qb, qld, G, g, a.qhead, cf, lo, hi, tid);
+    dregs.load_flat(db_, qld, G, g, a.qhead, cf, lo, hi, tid);
     if (tid < BM) {
       int f = cf + tid;
       if (f >= lo && f < hi) {
         int t = f / G, j = f - t * G;
-        long idx = (long)(g * G + j) * a.lse_ld + s0 + t;
+        long idx = (long)q_head(a.qhead, g, G, j) * a.lse_ld + s0 + t;
         lse_r = SM::lse_in(a.lse[idx]);
         d_r = -a.Dneg[idx];
       } else {
@@ -683,8 +685,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdKVArgs a) {
 // barrier per step).  The rows of a step are flattened (token, head-of-group) pairs;
 // the rows a lane fetches are fixed within a step, so their token/head split is
 // precomputed.  With K read from LDS and 32-row steps a wave fits 256 registers and
-// the LDS of two workgroups fits a CU: two waves per SIMD.
-template <typename E, int HD, int BM, int WPE>
+// the LDS of two workgroups fits a CU: two waves per SIMD.  MAP: the q-heads of the
+// kv head come from the GQA head table (a.qhead) instead of g * G + j.
+template <typename E, int HD, int BM, int WPE, bool MAP>
 __global__ __launch_bounds__(256, WPE) void bwd_dkdv_h16_kernel(BwdKVArgs a) {
   constexpr int BNW = kBwdBN;
   constexpr int TILE = BM * HD * 2;
@@ -809,6 +812,8 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_h16_kernel(BwdKVArgs a) {
   const uint32_t g_recip = __builtin_amdgcn_readfirstlane(((1u << 24) + (uint32_t)G - 1) / (uint32_t)G);
   const int qld_b = (int)(qld * 2);
   const int head0_b = g * G * HD * 2;
+  HeadMap hm;
+  if constexpr (MAP) hm.init(a.qhead, g, G, lane);
   // Wave 0 fetches LSE rows, wave 1 D rows.
   const __amdgpu_buffer_rsrc_t r_ld = make_rsrc_u(wave == 0 ? (const void *)a.lsn : (const void *)a.Dneg,
                                                   (uint32_t)((long)a.Hq * a.lse_ld * 4));
@@ -834,7 +839,8 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_h16_kernel(BwdKVArgs a) {
         j -= G;
         ++t;
       }
-      const int off = t * qld_b + head0_b + j * (HD * 2) + (((slot % CPR) ^ Swz<HD>::swz(r)) << 4);
+      const int hoff = MAP ? hm.at(j, G) * (HD * 2) : head0_b + j * (HD * 2);
+      const int off = t * qld_b + hoff + (((slot % CPR) ^ Swz<HD>::swz(r)) << 4);
       dma16(rq, l0 + k * 4096, off);
       dma16(rd, l0 + TILE + k * 4096, off);
     }
@@ -844,7 +850,8 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_h16_kernel(BwdKVArgs a) {
         j -= G;
         ++t;
       }
-      const int off = lane < BM ? ((g * G + j) * a.lse_ld + s0 + t) * 4 : 0x7fffffff;
+      const int hq = MAP ? hm.at(j, G) : g * G + j;
+      const int off = lane < BM ? (hq * a.lse_ld + s0 + t) * 4 : 0x7fffffff;
       const uint32_t la = __builtin_amdgcn_readfirstlane(lds_u32(st + 2 * TILE) + wave * 256);
       dma4(r_ld, la, off);
     }
@@ -1098,24 +1105,21 @@ static hipError_t dkdv_f32(const BwdKVArgs &a, int n, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename E, int HD>
+static hipError_t dkdv_h16(const BwdKVArgs &a, int n, hipStream_t s) {
+  if (a.qhead)
+    hipLaunchKernelGGL((bwd_dkdv_h16_kernel<E, HD, 32, 2, true>), dim3(n), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_h16_kernel<E, HD, 32, 2, false>), dim3(n), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_dkdv(int dtype, int hd, const BwdKVArgs &a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (dtype == 0 || dtype == 2) {   // bf16, fp16
     if (hd == 512) return launch_bwd_dkdv_d512(dtype, a, n, s);
-    if (hd == 64) {
-      if (dtype == 2)
-        hipLaunchKernelGGL((bwd_dkdv_h16_kernel<f16, 64, 32, 2>), dim3(n), dim3(256), 0, s, a);
-      else
-        hipLaunchKernelGGL((bwd_dkdv_h16_kernel<h16, 64, 32, 2>), dim3(n), dim3(256), 0, s, a);
-      return hipGetLastError();
-    }
-    if (hd == 128) {
-      if (dtype == 2)
-        hipLaunchKernelGGL((bwd_dkdv_h16_kernel<f16, 128, 32, 2>), dim3(n), dim3(256), 0, s, a);
-      else
-        hipLaunchKernelGGL((bwd_dkdv_h16_kernel<h16, 128, 32, 2>), dim3(n), dim3(256), 0, s, a);
-      return hipGetLastError();
-    }
+    if (hd == 64) return dtype == 2 ? dkdv_h16<f16, 64>(a, n, s) : dkdv_h16<h16, 64>(a, n, s);
+    if (hd == 128) return dtype == 2 ? dkdv_h16<f16, 128>(a, n, s) : dkdv_h16<h16, 128>(a, n, s);
   } else {
     if (hd == 64) return dkdv_f32<64>(a, n, s);
     if (hd == 128) return dkdv_f32<128>(a, n, s);

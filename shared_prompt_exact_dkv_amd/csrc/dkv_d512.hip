@@ -88,7 +88,7 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
   const int hj = qr - tok * a.G;
   const bool row_valid = tok < nt;
   if (!row_valid) tok = nt - 1;
-  const int h = g * a.G + hj;
+  const int h = q_head(a.qhead, g, a.G, hj);
   const int P = it.ctx_len, wl = a.window_left;
   const int qpos = P + t0 + tok;
   const int qmin = P + t0, qmax = P + t0 + nt - 1;
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
   const int hj = qr - tok * a.G;
   const bool row_valid = tok < nt;
   if (!row_valid) tok = nt - 1;
-  const int h = g * a.G + hj;
+  const int h = q_head(a.qhead, g, a.G, hj);
   const int P = it.ctx_len, wl = a.window_left;
   const int qpos = P + t0 + tok;
   const int qmin = P + t0, qmax = P + t0 + nt - 1;
@@ -517,7 +517,8 @@ hipError_t launch_bwd_dq_d512(int dtype, const BwdQArgs &a, int n, hipStream_t s
 
 // --------------------------------------------------------------------- dK/dV --
 
-template <typename E>
+// MAP: the q-heads of the kv head come from the GQA head table (a.qhead).
+template <typename E, bool MAP>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
   constexpr int BM = 32;                 // query rows per step
   constexpr int TILE = BM * HD * 2;      // 32 KB: one row per 1 KB DMA block
@@ -615,6 +616,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
 
   const int qld_b = (int)(qld * 2);
   const int head0_b = g * G * HD * 2;
+  HeadMap hm;
+  if constexpr (MAP) hm.init(a.qhead, g, G, lane);
   const int r4 = 4 % G;                                  // head step of 4 flattened rows
   const int step4 = (4 / G) * qld_b + r4 * (HD * 2);     // their byte step before a wrap
   // Waves 0-3 fetch the step's Q rows, waves 4-7 its dO rows: row r of the step (a
@@ -640,7 +643,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
 #pragma unroll
     for (int k = 0; k < RPW; ++k) {
       const int r = k * 4 + wq;
-      dma16(rx, l0 + k * 4096, roff + ((lane ^ Swz<HD>::swz(r)) << 4));
+      // With a head table the row's head (wave-uniform) comes from the table.
+      const int ro = MAP ? roff - head0_b - j * (HD * 2) + hm.at_uniform(j) * (HD * 2) : roff;
+      dma16(rx, l0 + k * 4096, ro + ((lane ^ Swz<HD>::swz(r)) << 4));
       // 4 rows on: q4 tokens and r4 heads, plus one token when the head index wraps
       j += r4;
       roff += step4;
@@ -656,7 +661,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
     const int s0 = cs0;
     const int f = cf + col;
     const int t = (int)((unsigned)f / (unsigned)G), j = f - t * G;
-    const int off = ((g * G + j) * a.lse_ld + s0 + t) * 4;
+    const int hq = MAP ? hm.at(j, G) : g * G + j;
+    const int off = (hq * a.lse_ld + s0 + t) * 4;
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_ld, off, 0, 0));
   };
 
@@ -819,13 +825,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
     }
 }
 
+template <typename E>
+static hipError_t dkdv_d512(const BwdKVArgs &a, int n, hipStream_t s) {
+  if (a.qhead)
+    hipLaunchKernelGGL((bwd_dkdv_d512_kernel<E, true>), dim3(n), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_d512_kernel<E, false>), dim3(n), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_dkdv_d512(int dtype, const BwdKVArgs &a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  if (dtype == 2)
-    hipLaunchKernelGGL(bwd_dkdv_d512_kernel<f16>, dim3(n), dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL(bwd_dkdv_d512_kernel<h16>, dim3(n), dim3(512), 0, s, a);
-  return hipGetLastError();
+  return dtype == 2 ? dkdv_d512<f16>(a, n, s) : dkdv_d512<h16>(a, n, s);
 }
 
 }  // namespace dkv

@@ -129,6 +129,33 @@ __device__ __forceinline__ float pair_sum(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// The GQA head table of one kv head held in registers: lane l keeps the q-head of member
+// l (t0) and of member l + 64 (t1, only when G > 64).  at(j) returns member j's q-head
+// for a per-lane j < G through ds_bpermute (a cross-lane read, no LDS allocation); every
+// lane of the wave must be active.
+struct HeadMap {
+  int t0 = 0, t1 = 0;
+  __device__ __forceinline__ void init(const int32_t *qhead, int g, int G, int lane) {
+    t0 = lane < G ? qhead[g * G + lane] : 0;
+    t1 = lane + 64 < G ? qhead[g * G + 64 + lane] : 0;
+  }
+  __device__ __forceinline__ int at(int j, int G) const {
+    const int a = __builtin_amdgcn_ds_bpermute((j & 63) << 2, t0);
+    if (G <= 64) return a;
+    const int b = __builtin_amdgcn_ds_bpermute((j & 63) << 2, t1);
+    return j >= 64 ? b : a;
+  }
+  // Member j's q-head for a wave-uniform j < min(G, 64).
+  __device__ __forceinline__ int at_uniform(int j) const {
+    return __builtin_amdgcn_readlane(t0, __builtin_amdgcn_readfirstlane(j));
+  }
+};
+
+// q-head of member j of kv head g: the table's entry, or g * G + j for the contiguous map.
+__device__ __forceinline__ int q_head(const int32_t *qhead, int g, int G, int j) {
+  return qhead ? qhead[g * G + j] : g * G + j;
+}
+
 // Compensated (Kahan) add of a partial tile sum into a running fp32 accumulator.
 // Used on the fp32 path, whose gradients are summed over thousands of terms and
 // checked at 1e-5 absolute.

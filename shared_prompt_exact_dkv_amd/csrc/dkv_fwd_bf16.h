@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256, WPE) void fwd_h16_kernel(FwdArgs a) {
   const int hj = qr - tok * a.G;
   const bool row_valid = tok < nt;
   if (!row_valid) tok = nt - 1;   // computes a duplicate of a valid row, never stored
-  const int h = g * a.G + hj;
+  const int h = q_head(a.qhead, g, a.G, hj);
   const int P = it.ctx_len, wl = a.window_left;
   const int qpos = P + t0 + tok;
   const int qmin = P + t0, qmax = P + t0 + nt - 1;

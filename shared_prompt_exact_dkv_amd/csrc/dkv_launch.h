@@ -41,6 +41,9 @@ struct FwdArgs {
   void *o;
   float *lse;
   const QItem *items;
+  // GQA head table, or null for the contiguous map: member j of kv head g is q-head
+  // qhead[g * G + j] (else g * G + j).
+  const int32_t *qhead;
   int Hq, Hkv, G, bm_tok;
   int window_left;    // -1 global
   int lse_ld;         // tokens per LSE row
@@ -78,6 +81,7 @@ struct BwdQArgs {
   float *Dneg_out, *lsn_out;
   void *dq;
   const QItem *items;
+  const int32_t *qhead;        // GQA head table (as FwdArgs::qhead)
   int Hq, Hkv, G, bm_tok, window_left, lse_ld;
   float scale;
 };
@@ -103,7 +107,8 @@ struct BwdKVArgs {
   const void *q, *dout, *k_ctx, *v_ctx, *k_own, *v_own;
   const float *lse, *Dneg;     // Dneg = -rowsum(dO * O) (written by the dQ kernel, or by
   const float *lsn;            // the preprocess kernel in fp32); lsn = -LSE / scale
-  const int32_t *cu;           // device prefix sums of the query sequences
+  const int32_t *cu;           // prefix sums of the query sequences (the workspace's copy)
+  const int32_t *qhead;        // GQA head table (as FwdArgs::qhead)
   void *dk_own, *dv_own;       // direct outputs of own-region keys
   float *acc_dk, *acc_dv;      // fp32 accumulators: ctx-region keys, and own keys if own_to_acc
   // Split mode (non-null split_dk): ctx-region items store their partial sums into

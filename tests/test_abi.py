@@ -37,7 +37,9 @@ FAKE = 0x10000   # 16-byte aligned, never dereferenced: validation fails first
     (dict(cu_host=[0, 5, 4]), L.DKV_ERR_INVALID_ARG, "decreases"),
     (dict(dtype=7), L.DKV_ERR_INVALID_ARG, "dtype"),
     (dict(ctx_len=-1), L.DKV_ERR_INVALID_ARG, "ctx_len"),
-    (dict(cu_dev=0), L.DKV_ERR_INVALID_ARG, "cu_seqlens_dev"),
+    (dict(kv_head_of_q=[0, 0, 0, 1, 1, 1, 1, 1]), L.DKV_ERR_INVALID_ARG, "kv head 0"),
+    (dict(kv_head_of_q=[0, 0, 0, 0, 1, 1, 1, 2]), L.DKV_ERR_INVALID_ARG, "outside"),
+    (dict(kv_head_of_q=[0, 0, 0, 0, 1, 1, 1, -1]), L.DKV_ERR_INVALID_ARG, "outside"),
     (dict(softmax_scale=float("nan")), L.DKV_ERR_INVALID_ARG, "scale"),
     (dict(head_dim=512, dtype=L.DKV_FP32), L.DKV_ERR_UNSUPPORTED, "fp16 only"),
     (dict(dtype=3), L.DKV_ERR_INVALID_ARG, "dtype"),
@@ -49,6 +51,36 @@ def test_fwd_rejects_invalid_params(kw, status, frag):
     st = lib.dkv_fwd(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None)
     assert st == status
     assert frag in L.last_error()
+
+
+def test_cu_seqlens_dev_is_optional():
+    # The kernels read sequence bounds staged from the host copy, so the device copy may
+    # be absent; validation and sizing do not depend on it.
+    lib = L.lib()
+    p0, k0 = _params(cu_dev=0)
+    p1, k1 = _params()
+    for call in (L.DKV_CALL_FWD, L.DKV_CALL_BWD):
+        assert lib.dkv_workspace_size(p0, call) == lib.dkv_workspace_size(p1, call)
+    st = lib.dkv_fwd(p0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None)
+    assert st == L.DKV_ERR_WORKSPACE
+
+
+def test_head_map_validation_and_workspace():
+    # A permuted GQA map (every kv head named by Hq / Hkv q-heads) is accepted and adds
+    # its head table to the staged workspace; the contiguous map given explicitly is run
+    # as no map.
+    lib = L.lib()
+    none, k0 = _params()
+    contig, k1 = _params(kv_head_of_q=[h // 4 for h in range(8)])
+    perm, k2 = _params(kv_head_of_q=[1, 0, 1, 0, 0, 1, 1, 0])
+    for call in (L.DKV_CALL_CTX_FWD, L.DKV_CALL_FWD, L.DKV_CALL_BWD):
+        p_ctx = call in (L.DKV_CALL_CTX_FWD,)
+        if p_ctx:
+            none, k0 = _params(ctx_len=0)
+            contig, k1 = _params(ctx_len=0, kv_head_of_q=[h // 4 for h in range(8)])
+            perm, k2 = _params(ctx_len=0, kv_head_of_q=[1, 0, 1, 0, 0, 1, 1, 0])
+        a, b, c = (lib.dkv_workspace_size(p, call) for p in (none, contig, perm))
+        assert a == b and c > a, (call, a, b, c)
 
 
 def test_ctx_calls_require_zero_ctx_len():
@@ -206,12 +238,33 @@ def test_layout_validation():
     assert 0 < n < 4096
 
 
-def test_binding_checks_tensor_shapes():
-    # The C ABI takes plain pointers, so the binding checks shapes, dtypes and layout
-    # before any call: a short query tensor, a wrong output shape or a transposed view
-    # would otherwise be read or written out of bounds.
+def test_binding_rejects_host_tensors():
+    # The kernels dereference every pointer on the GPU: a host tensor's pointer would be
+    # read as a device address.
     import torch
     import shared_prompt_exact_dkv_amd as dkv
+    q = torch.zeros(12, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(12, 2, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 5, 12], dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        dkv.dkv_fwd(q, k[:8], k[:8], k, k, cu)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        dkv.dkv_ctx_fwd(q, k, k, cu)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        dkv.dkv_cast_acc(torch.zeros(8, 2, 64), torch.zeros(8, 2, 64), k[:8], k[:8])
+    with pytest.raises(ValueError, match="GPU tensor"):
+        dkv.dkv_layout(dkv.DKV_PACK, torch.zeros(12, 64, dtype=torch.bfloat16), [0, 4], 8)
+
+
+def test_binding_checks_tensor_shapes(monkeypatch):
+    # The C ABI takes plain pointers, so the binding checks shapes, dtypes, layout and
+    # devices before any call: a short query tensor, a wrong output shape, a transposed
+    # view or a tensor on another device would otherwise be read or written out of
+    # bounds.  Without a GPU the checks run on CPU tensors (the call's device is taken to
+    # be the CPU), and a meta tensor stands for a tensor on another device.
+    import torch
+    import shared_prompt_exact_dkv_amd as dkv
+    monkeypatch.setattr(dkv, "_gpu", lambda t, name: t.device)
     P, T, Hq, Hkv, d = 8, 12, 4, 2, 64
     bf = torch.bfloat16
     q = torch.zeros(T, Hq, d, dtype=bf)
@@ -231,3 +284,26 @@ def test_binding_checks_tensor_shapes():
                     acc_dk_p=torch.zeros(P, Hkv, d, dtype=bf), acc_dv_p=None)
     with pytest.raises(ValueError, match="not contiguous"):
         dkv.dkv_ctx_fwd(q.transpose(0, 1).contiguous().transpose(0, 1), k, k, cu)
+    # every tensor on the call's device
+    with pytest.raises(ValueError, match="k_p is on meta"):
+        dkv.dkv_fwd(q, kp.to("meta"), kp, k, k, cu)
+    with pytest.raises(ValueError, match="dout_r is on meta"):
+        dkv.dkv_bwd(q, kp, kp, k, k, q, torch.zeros(Hq, T), q.to("meta"), cu,
+                    acc_dk_p=torch.zeros(P, Hkv, d), acc_dv_p=torch.zeros(P, Hkv, d))
+    # cu_seqlens: int32 prefix sums, consistent with cu_host
+    with pytest.raises(ValueError, match="int32"):
+        dkv.dkv_fwd(q, kp, kp, k, k, cu.long())
+    with pytest.raises(ValueError, match="entries"):
+        dkv.dkv_fwd(q, kp, kp, k, k, cu, cu_host=[0, T])
+    with pytest.raises(ValueError, match="disagree"):
+        dkv.dkv_fwd(q, kp, kp, k, k, cu, cu_host=[0, 6, T])
+    with pytest.raises(ValueError, match="kv_head_of_q"):
+        dkv.dkv_fwd(q, kp, kp, k, k, cu, kv_head_of_q=[0, 1, 0])
+    # the standalone cast: outputs of the accumulator's shape and of one dtype
+    acc = torch.zeros(P, Hkv, d)
+    with pytest.raises(ValueError, match="dk"):
+        dkv.dkv_cast_acc(acc, acc, kp[:4], kp)
+    with pytest.raises(ValueError, match="dv"):
+        dkv.dkv_cast_acc(acc, acc, kp, kp.half())
+    with pytest.raises(ValueError, match="acc_dv"):
+        dkv.dkv_cast_acc(acc, acc[:4], kp, kp)

@@ -1,0 +1,141 @@
+"""GPU parity on logits that grow along the key axis: the online softmax's rescale path.
+
+The 16-bit forward kernels keep a running row maximum m and rescale the output and the
+row sum only when a tile's maximum exceeds m by more than 8 (log2 units); the fp32
+kernel rescales on every tile.  Inputs drawn N(0,1) almost never raise a row's maximum
+that far after its first tile, so these cases add a component along one direction to
+every query and, to every key, one proportional to its logical position
+(workloads.add_key_ramp): a row's logits then climb by tens of log2 units across the
+prompt region and on through its own response, the case of attention sinks late in a
+long context.  Each case first counts, on the host, the rescale events the kernels'
+tile walk meets (prompt tiles, then the row's own tiles, as in eq. (4) and §3.1 of the
+paper: one online softmax carried across the two key regions), and requires several
+in Call 1, in Call 2's prompt region and in Call 2's own region.  Then the forward and
+the backward of both calls are compared element by element with the oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import shared_prompt_exact_dkv_amd as dkv
+from tests._gpu import check, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SLACK = 8.0   # log2 units a 16-bit kernel's row maximum may lag before it rescales
+
+
+def _tile_max_log2(q, k, qpos, kpos, scale, wl):
+    """[rows, heads, keys] scores in log2 units, -inf where masked (fp64)."""
+    s = np.einsum("thc,jhc->thj", q, k) * scale * math.log2(math.e)
+    vis = kpos[None, :] <= qpos[:, None]
+    if wl >= 0:
+        vis &= kpos[None, :] >= qpos[:, None] - wl
+    return np.where(vis[:, None, :], s, -np.inf)
+
+
+def _count(scores, tiles):
+    """Lazy-rescale events per (row, head) over the given key tiles (index arrays into
+    the last axis), in order: the first tile with a visible key sets the maximum, and
+    every later tile whose maximum exceeds it by more than SLACK is one event."""
+    m = np.full(scores.shape[:2], -np.inf)
+    events = 0
+    for idx in tiles:
+        if len(idx) == 0:
+            continue
+        mx = scores[:, :, idx].max(axis=2)
+        grow = mx > m + SLACK
+        events += int((grow & np.isfinite(m)).sum())
+        m = np.where(grow, mx, m)
+    return events
+
+
+def _tiles(lo, hi, BN, base=0):
+    """BN-key tiles covering keys [lo, hi), aligned at multiples of BN from base."""
+    out = []
+    t = base + ((lo - base) // BN) * BN if hi > lo else hi
+    while t < hi:
+        out.append(np.arange(max(t, lo), min(t + BN, hi)))
+        t += BN
+    return out
+
+
+def rescale_events(x, P, lens, Hq, Hkv, d, wl, BN):
+    """(Call 1, Call 2 prompt region, Call 2 own region) rescale events of the lazy
+    online softmax, per the kernels' tile walk.  The maximum carries over from the
+    prompt region into the own region, so an event counted in the own region is one
+    against a maximum set by prompt keys or earlier own keys."""
+    scale = 1.0 / math.sqrt(d)
+    G = Hq // Hkv
+    rep = lambda t: np.repeat(t.numpy().astype(np.float64), G, axis=1)
+    kp = rep(x["k_p"])
+    c1 = _count(_tile_max_log2(x["q_p"].numpy().astype(np.float64), kp, np.arange(P),
+                               np.arange(P), scale, wl), _tiles(0, P, BN))
+    cu = [int(c) for c in x["cu"]]
+    c2p = c2o = 0
+    for i in range(len(lens)):
+        a, b = cu[i], cu[i + 1]
+        if b == a:
+            continue
+        q = x["q_r"][a:b].numpy().astype(np.float64)
+        k = np.concatenate([kp, rep(x["k_r"][a:b])], 0)
+        qpos = P + np.arange(b - a)
+        kpos = np.arange(P + b - a)
+        sc = _tile_max_log2(q, k, qpos, kpos, scale, wl)
+        ptiles = _tiles(0, P, BN)
+        otiles = [t + P for t in _tiles(0, b - a, BN)]
+        m_events_p = _count(sc, ptiles)
+        m_events_all = _count(sc, ptiles + otiles)
+        c2p += m_events_p
+        c2o += m_events_all - m_events_p
+    return c1, c2p, c2o
+
+
+CASES = [
+    # P, lens, Hq, Hkv, d, window_left, dtype, rise (log2 units over the longest row)
+    (300, [260, 150], 8, 2, 128, -1, "bf16", 60.0),
+    (256, [300, 40], 8, 2, 64, 150, "bf16", 60.0),
+    (250, [200, 100], 6, 2, 128, 120, "fp16", 60.0),
+    (200, [180, 90], 4, 2, 64, -1, "fp16", 60.0),
+    (160, [200, 70], 8, 2, 512, -1, "bf16", 60.0),
+    (150, [220], 8, 2, 512, 100, "bf16", 80.0),
+    (200, [150, 60], 4, 2, 64, -1, "fp32", 16.0),
+    (130, [140], 4, 1, 128, 90, "fp32", 16.0),
+]
+
+
+@pytest.mark.parametrize("P,lens,Hq,Hkv,d,wl,dtype,rise", CASES)
+def test_rising_logits_match_oracle(P, lens, Hq, Hkv, d, wl, dtype, rise):
+    seed = P + 17 * len(lens) + d
+    x = workloads.make_inputs(P, lens, Hq, Hkv, d, dtype, seed=seed)
+    x = workloads.add_key_ramp(x, P, lens, d, dtype, rise, seed)
+    if dtype != "fp32":
+        # the 16-bit kernels' lazy rescale is reached in every part of the walk
+        BN = 32 if d == 512 else 64
+        c1, c2p, c2o = rescale_events(x, P, lens, Hq, Hkv, d, wl, BN)
+        rows = (P + sum(lens)) * Hq
+        print("[rescale] events: call 1 %d, call 2 prompt %d, own %d (rows %d)"
+              % (c1, c2p, c2o, rows), flush=True)
+        assert min(c1, c2p, c2o) >= 32 * Hq, (c1, c2p, c2o)
+    N = len(lens)
+    do_copies = workloads.split_prompt_grad(x["do_p"], N, seed=seed)
+    ref = oracle.ncopy_reference(x, do_copies=do_copies, window_left=wl)
+    t = to_dev(x, dtype)
+    o_p, lse_p, o_r, lse_r = dkv.dualkv_forward(t["q_p"], t["k_p"], t["v_p"], t["q_r"],
+                                                t["k_r"], t["v_r"], t["cu"],
+                                                cu_host=t["cu_host"], window_left=wl)
+    g = dkv.dualkv_backward(t["q_p"], t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], o_p,
+                            lse_p, o_r, lse_r, t["do_p"], t["do_r"], t["cu"],
+                            cu_host=t["cu_host"], window_left=wl)
+    torch.cuda.synchronize()
+    check("o_p", o_p, ref["o_p"], dtype)
+    check("o_r", o_r, ref["o_r"], dtype)
+    lb = 1e-5 if dtype == "fp32" else 2e-3
+    check("lse_p", lse_p.t(), ref["lse_p"], dtype, bound=lb)
+    check("lse_r", lse_r.t(), ref["lse_r"], dtype, bound=lb)
+    for k in ("dq_p", "dk_p", "dv_p", "dq_r", "dk_r", "dv_r"):
+        check(k, g[k], ref[k], dtype)

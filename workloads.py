@@ -123,6 +123,38 @@ def _draw(g: torch.Generator, shape, dtype: str, scale: float, keep: bool = Fals
     return x
 
 
+def _round(x: torch.Tensor, dtype: str) -> torch.Tensor:
+    return x.to(torch_dtype(dtype)).to(torch.float32) if dtype in ("bf16", "fp16") else x
+
+
+def add_key_ramp(x: dict, P: int, lens, d: int, dtype: str, rise: float, seed: int,
+                 q_shift: float = 4.0) -> dict:
+    """Logits that grow along the key axis (for inputs of make_inputs on the CPU).
+
+    A seeded unit vector u is added, times q_shift, to every query row, and every key
+    at logical position pos (prompt row j: j; row r of a response: P + r) gets
+    c * pos * u, with c chosen so that <q_shift u, c L u> / sqrt(d) * log2(e) = rise
+    for L = the longest logical position.  A query's logit against keys further along
+    its row then grows by about rise * (distance / L) log2 units on top of its N(0,1)
+    spread, as with attention sinks late in a long context.  Values are rounded to
+    ``dtype`` again, so both sides of a comparison see the same numbers.
+    """
+    g = torch.Generator().manual_seed(90_000 + seed)
+    u = torch.randn(d, generator=g, dtype=torch.float64)
+    u = (u / u.norm()).to(torch.float32)
+    L = max(1, P + max([int(r) for r in lens] + [0]) - 1)
+    c = rise * math.sqrt(d) / (q_shift * L * math.log2(math.e))
+    out = dict(x)
+    for name in ("q_p", "q_r"):
+        out[name] = _round(x[name] + q_shift * u, dtype)
+    out["k_p"] = _round(x["k_p"] + (c * torch.arange(P, dtype=torch.float32)).view(-1, 1, 1) * u,
+                        dtype)
+    pos = torch.cat([torch.arange(int(r), dtype=torch.float32) + P for r in lens]) \
+        if len(lens) else torch.zeros(0)
+    out["k_r"] = _round(x["k_r"] + (c * pos).view(-1, 1, 1) * u, dtype)
+    return out
+
+
 def make_inputs(P: int, lens, Hq: int, Hkv: int, d: int, dtype: str = "fp32",
                 seed: int = 0, scaled: bool = False, dout: bool = True,
                 device: str = "cpu") -> dict:
