@@ -155,6 +155,38 @@ def add_key_ramp(x: dict, P: int, lens, d: int, dtype: str, rise: float, seed: i
     return out
 
 
+def add_key_sinks(x: dict, P: int, lens, d: int, dtype: str, step: int, gain: float,
+                  seed: int, q_shift: float = 4.0) -> dict:
+    """Attention sinks whose logits climb along the key axis (inputs of make_inputs on
+    the CPU).
+
+    A seeded unit vector u is added, times q_shift, to every query row; the key at every
+    logical position pos = step - 1, 2 step - 1, ... (prompt row j: j; row r of a
+    response: P + r) gets a * (pos // step + 1) * u, with a chosen so that
+    <q_shift u, a u> / sqrt(d) * log2(e) = gain: each sink outscores the previous one by
+    about gain log2 units (for the query's component along u near q_shift), so a row's
+    maximum jumps at every sink it reaches while the other keys keep N(0,1) logits.
+    Values are rounded to ``dtype`` again.
+    """
+    g = torch.Generator().manual_seed(91_000 + seed)
+    u = torch.randn(d, generator=g, dtype=torch.float64)
+    u = (u / u.norm()).to(torch.float32)
+    a = gain * math.sqrt(d) / (q_shift * math.log2(math.e))
+
+    def boost(pos):
+        lvl = torch.where((pos + 1) % step == 0, (pos + 1) // step, torch.zeros_like(pos))
+        return (a * lvl.to(torch.float32)).view(-1, 1, 1) * u
+
+    out = dict(x)
+    for name in ("q_p", "q_r"):
+        out[name] = _round(x[name] + q_shift * u, dtype)
+    out["k_p"] = _round(x["k_p"] + boost(torch.arange(P)), dtype)
+    pos = torch.cat([torch.arange(int(r)) + P for r in lens]) if len(lens) \
+        else torch.zeros(0, dtype=torch.long)
+    out["k_r"] = _round(x["k_r"] + boost(pos), dtype)
+    return out
+
+
 def make_inputs(P: int, lens, Hq: int, Hkv: int, d: int, dtype: str = "fp32",
                 seed: int = 0, scaled: bool = False, dout: bool = True,
                 device: str = "cpu") -> dict:
