@@ -4,10 +4,9 @@ The 16-bit forward kernels keep a running row maximum m and rescale the output a
 row sum only when a tile's maximum exceeds m by more than 8 (log2 units); the fp32
 kernel rescales on every tile.  Inputs drawn N(0,1) almost never raise a row's maximum
 that far after its first tile, so these cases add a component along one direction to
-every query and, to keys, one that grows with their logical position -- to every key
-(workloads.add_key_ramp) or to sparse attention sinks (workloads.add_key_sinks): a
-row's logits then climb by tens of log2 units across the prompt region and on through
-its own response.  Each case first counts, on the host, the rescale events the kernels'
+every query and, to every key, a small one that grows with its logical position
+(workloads.add_key_ramp): a row's logits then climb by tens of log2 units across the
+prompt region and on through its own response.  Each case first counts, on the host, the rescale events the kernels'
 tile walk meets (prompt tiles, then the row's own tiles, as in eq. (4) and §3.1 of the
 paper: one online softmax carried across the two key regions), and requires several
 in Call 1, in Call 2's prompt region and in Call 2's own region.  Then the forward and
@@ -108,68 +107,44 @@ CASES = [
 ]
 
 
-def _inputs(kind, P, lens, Hq, Hkv, d, wl, dtype):
+def _inputs(P, lens, Hq, Hkv, d, wl, dtype):
     seed = P + 17 * len(lens) + d
     x = workloads.make_inputs(P, lens, Hq, Hkv, d, dtype, seed=seed)
-    if kind == "ramp":
-        # fp32: a gentler climb keeps the fp32 scores' own rounding well inside 1e-5
-        x = workloads.add_key_ramp(x, P, lens, d, dtype, 16.0 if dtype == "fp32" else 60.0, seed)
+    # fp32 takes a gentler climb (its kernel rescales on every tile anyway): the 1e-5
+    # absolute bound needs gradients of the size plain N(0,1) inputs give, and a steep
+    # climb's large query component scales dK to ~70, where 1e-5 is two fp32 spacings
+    if dtype == "fp32":
+        x = workloads.add_key_ramp(x, P, lens, d, dtype, 8.0, seed, key_span=8.0)
     else:
-        x = workloads.add_key_sinks(x, P, lens, d, dtype, 48, 16.0, seed)
+        x = workloads.add_key_ramp(x, P, lens, d, dtype, 60.0, seed)
     if dtype != "fp32":
         # the 16-bit kernels' lazy rescale is reached in every part of the walk
         BN = 32 if d == 512 else 64
         c1, c2p, c2o = rescale_events(x, P, lens, Hq, Hkv, d, wl, BN)
-        print("[rescale] %s: events call 1 %d, call 2 prompt %d, own %d"
-              % (kind, c1, c2p, c2o), flush=True)
+        print("[rescale] events call 1 %d, call 2 prompt %d, own %d" % (c1, c2p, c2o),
+              flush=True)
         assert min(c1, c2p, c2o) >= 32 * Hq, (c1, c2p, c2o)
     return x, seed
 
 
-def _forward(x, dtype, wl):
+@pytest.mark.parametrize("P,lens,Hq,Hkv,d,wl,dtype", CASES)
+def test_climbing_logits_match_oracle(P, lens, Hq, Hkv, d, wl, dtype):
+    x, seed = _inputs(P, lens, Hq, Hkv, d, wl, dtype)
+    N = len(lens)
+    do_copies = workloads.split_prompt_grad(x["do_p"], N, seed=seed)
+    ref = oracle.ncopy_reference(x, do_copies=do_copies, window_left=wl)
     t = to_dev(x, dtype)
-    f = dkv.dualkv_forward(t["q_p"], t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], t["cu"],
-                           cu_host=t["cu_host"], window_left=wl)
-    return t, f
-
-
-def _check_forward(f, ref, dtype):
-    o_p, lse_p, o_r, lse_r = f
+    o_p, lse_p, o_r, lse_r = dkv.dualkv_forward(t["q_p"], t["k_p"], t["v_p"], t["q_r"],
+                                                t["k_r"], t["v_r"], t["cu"],
+                                                cu_host=t["cu_host"], window_left=wl)
+    g = dkv.dualkv_backward(t["q_p"], t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], o_p,
+                            lse_p, o_r, lse_r, t["do_p"], t["do_r"], t["cu"],
+                            cu_host=t["cu_host"], window_left=wl)
+    torch.cuda.synchronize()
     check("o_p", o_p, ref["o_p"], dtype)
     check("o_r", o_r, ref["o_r"], dtype)
     lb = 1e-5 if dtype == "fp32" else 2e-3
     check("lse_p", lse_p.t(), ref["lse_p"], dtype, bound=lb)
     check("lse_r", lse_r.t(), ref["lse_r"], dtype, bound=lb)
-
-
-@pytest.mark.parametrize("P,lens,Hq,Hkv,d,wl,dtype", CASES)
-def test_rising_logits_forward_matches_oracle(P, lens, Hq, Hkv, d, wl, dtype):
-    # Every key carries a component along u that grows with its position.  Only the
-    # forward is held to the bounds here: with keys that share a large, slowly varying
-    # component, dQ = sum_j dS_j k_j cancels (sum_j dS_j = 0) and the 16-bit rounding
-    # of dS before the dS K product -- the backward's contraction in 16-bit operands --
-    # leaves errors of order 2^-9 sum_j |dS_j| |k_j|, above 2e-2 max|dQ| for these inputs.
-    x, seed = _inputs("ramp", P, lens, Hq, Hkv, d, wl, dtype)
-    ref = oracle.ncopy_reference(x, window_left=wl, backward=False)
-    t, f = _forward(x, dtype, wl)
-    torch.cuda.synchronize()
-    _check_forward(f, ref, dtype)
-
-
-@pytest.mark.parametrize("P,lens,Hq,Hkv,d,wl,dtype", CASES)
-def test_attention_sinks_match_oracle(P, lens, Hq, Hkv, d, wl, dtype):
-    # Sinks every 48 positions, each outscoring the previous one by about 16 log2 units:
-    # every sink a row reaches rescales its output, and only the latest carries weight.
-    x, seed = _inputs("sinks", P, lens, Hq, Hkv, d, wl, dtype)
-    N = len(lens)
-    do_copies = workloads.split_prompt_grad(x["do_p"], N, seed=seed)
-    ref = oracle.ncopy_reference(x, do_copies=do_copies, window_left=wl)
-    t, f = _forward(x, dtype, wl)
-    o_p, lse_p, o_r, lse_r = f
-    g = dkv.dualkv_backward(t["q_p"], t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], o_p,
-                            lse_p, o_r, lse_r, t["do_p"], t["do_r"], t["cu"],
-                            cu_host=t["cu_host"], window_left=wl)
-    torch.cuda.synchronize()
-    _check_forward(f, ref, dtype)
     for k in ("dq_p", "dk_p", "dv_p", "dq_r", "dk_r", "dv_r"):
         check(k, g[k], ref[k], dtype)

@@ -128,62 +128,33 @@ def _round(x: torch.Tensor, dtype: str) -> torch.Tensor:
 
 
 def add_key_ramp(x: dict, P: int, lens, d: int, dtype: str, rise: float, seed: int,
-                 q_shift: float = 4.0) -> dict:
-    """Logits that grow along the key axis (for inputs of make_inputs on the CPU).
+                 key_span: float = 3.0) -> dict:
+    """Logits that climb along the key axis (for inputs of make_inputs on the CPU).
 
-    A seeded unit vector u is added, times q_shift, to every query row, and every key
-    at logical position pos (prompt row j: j; row r of a response: P + r) gets
-    c * pos * u, with c chosen so that <q_shift u, c L u> / sqrt(d) * log2(e) = rise
-    for L = the longest logical position.  A query's logit against keys further along
-    its row then grows by about rise * (distance / L) log2 units on top of its N(0,1)
-    spread, as with attention sinks late in a long context.  Values are rounded to
-    ``dtype`` again, so both sides of a comparison see the same numbers.
+    A seeded unit vector u is added to every key at logical position pos (prompt row j:
+    j; row r of a response: P + r) as key_span * pos / L * u, L the longest logical
+    position, and to every query row as a * u, with a chosen so that a query's logit
+    climbs by ``rise`` log2 units from key position 0 to L: a * key_span / sqrt(d) *
+    log2(e) = rise.  The queries carry the large component and the keys only a small,
+    slowly growing one, so the softmax weight spreads over a row's latest keys (about
+    L / rise positions per halving) instead of one key, and keys share no large common
+    component: the backward stays well conditioned.  Values are rounded to ``dtype``
+    again, so both sides of a comparison see the same numbers.
     """
     g = torch.Generator().manual_seed(90_000 + seed)
     u = torch.randn(d, generator=g, dtype=torch.float64)
     u = (u / u.norm()).to(torch.float32)
     L = max(1, P + max([int(r) for r in lens] + [0]) - 1)
-    c = rise * math.sqrt(d) / (q_shift * L * math.log2(math.e))
+    a = rise * math.sqrt(d) / (key_span * math.log2(math.e))
+    c = key_span / L
     out = dict(x)
     for name in ("q_p", "q_r"):
-        out[name] = _round(x[name] + q_shift * u, dtype)
+        out[name] = _round(x[name] + a * u, dtype)
     out["k_p"] = _round(x["k_p"] + (c * torch.arange(P, dtype=torch.float32)).view(-1, 1, 1) * u,
                         dtype)
     pos = torch.cat([torch.arange(int(r), dtype=torch.float32) + P for r in lens]) \
         if len(lens) else torch.zeros(0)
     out["k_r"] = _round(x["k_r"] + (c * pos).view(-1, 1, 1) * u, dtype)
-    return out
-
-
-def add_key_sinks(x: dict, P: int, lens, d: int, dtype: str, step: int, gain: float,
-                  seed: int, q_shift: float = 4.0) -> dict:
-    """Attention sinks whose logits climb along the key axis (inputs of make_inputs on
-    the CPU).
-
-    A seeded unit vector u is added, times q_shift, to every query row; the key at every
-    logical position pos = step - 1, 2 step - 1, ... (prompt row j: j; row r of a
-    response: P + r) gets a * (pos // step + 1) * u, with a chosen so that
-    <q_shift u, a u> / sqrt(d) * log2(e) = gain: each sink outscores the previous one by
-    about gain log2 units (for the query's component along u near q_shift), so a row's
-    maximum jumps at every sink it reaches while the other keys keep N(0,1) logits.
-    Values are rounded to ``dtype`` again.
-    """
-    g = torch.Generator().manual_seed(91_000 + seed)
-    u = torch.randn(d, generator=g, dtype=torch.float64)
-    u = (u / u.norm()).to(torch.float32)
-    a = gain * math.sqrt(d) / (q_shift * math.log2(math.e))
-
-    def boost(pos):
-        lvl = torch.where((pos + 1) % step == 0, (pos + 1) // step, torch.zeros_like(pos))
-        return (a * lvl.to(torch.float32)).view(-1, 1, 1) * u
-
-    out = dict(x)
-    for name in ("q_p", "q_r"):
-        out[name] = _round(x[name] + q_shift * u, dtype)
-    out["k_p"] = _round(x["k_p"] + boost(torch.arange(P)), dtype)
-    pos = torch.cat([torch.arange(int(r)) + P for r in lens]) if len(lens) \
-        else torch.zeros(0, dtype=torch.long)
-    out["k_r"] = _round(x["k_r"] + boost(pos), dtype)
     return out
 
 
