@@ -208,6 +208,27 @@ dkv_status dkv_bwd(const dkv_params *p, const void *q_resp, const void *k_p,
                    void *dk_p, void *dv_p, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * dkv_bwd without a workspace, for callers that cannot allocate (code that must not
+ * call hipMalloc, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments, validation, results and accumulator protocol as dkv_bwd; the scratch space
+ * dkv_bwd takes from `ws` comes instead from a device array inside the library of
+ * 64 MiB per GPU (held from the first such call on a device until the process ends),
+ * and the work lists are copied from pageable host memory, a copy HIP performs
+ * synchronously: the call returns once the lists have left the host, and it allocates
+ * neither device nor pinned host memory.  A call whose dkv_workspace_size (DKV_CALL_BWD,
+ * or DKV_CALL_BWD_SPLIT with DKV_ACC_SPLIT) exceeds 64 MiB returns DKV_ERR_UNSUPPORTED
+ * and enqueues nothing (the Qwen3-8B-shaped micro-batch, 131 072 response rows x 32
+ * q-heads, needs about 36 MiB).  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (other streams, other host threads) race, so run them one
+ * after another.
+ */
+dkv_status dkv_bwd_noalloc(const dkv_params *p, const void *q_resp, const void *k_p,
+                           const void *v_p, const void *k_r, const void *v_r, const void *o_r,
+                           const float *lse_r, const void *dout_r, void *dq_r, void *dk_r,
+                           void *dv_r, float *acc_dk_p, float *acc_dv_p, int acc_flags,
+                           void *dk_p, void *dv_p, hipStream_t stream);
+
+/*
  * The single cast of §3.2 (Stage 2) on its own: acc_dk/acc_dv fp32 [rows, Hkv, d]
  * -> dk/dv [rows, Hkv, d] in p->dtype, round-to-nearest-even (a copy for fp32).
  */

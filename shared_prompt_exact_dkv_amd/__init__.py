@@ -22,6 +22,7 @@ from ._lib import (DKV_FIRST_TOKEN_GATHER, DKV_FIRST_TOKEN_SCATTER, DKV_PACK,  #
                    DKV_UNPACK, DKV_UNPACK_BWD)
 
 __all__ = ["dkv_workspace_size", "dkv_ctx_fwd", "dkv_fwd", "dkv_ctx_bwd", "dkv_bwd",
+           "dkv_bwd_noalloc",
            "dkv_cast_acc", "dkv_layout", "layout_rows", "dualkv_forward", "dualkv_backward",
            "DkvError", "DKV_ACC_ZERO", "DKV_ACC_FINALIZE", "DKV_ACC_SPLIT", "DKV_PACK",
            "DKV_UNPACK", "DKV_UNPACK_BWD", "DKV_FIRST_TOKEN_GATHER", "DKV_FIRST_TOKEN_SCATTER"]
@@ -215,7 +216,7 @@ def dkv_ctx_bwd(q, k, v, o, lse, dout, cu_seqlens, *, cu_host=None, window_left=
 def dkv_bwd(q_resp, k_p, v_p, k_r, v_r, o_r, lse_r, dout_r, cu_seqlens, *, acc_dk_p, acc_dv_p,
             acc_flags=0, cu_host=None, window_left=-1, softmax_scale=0.0, dq_r=None, dk_r=None,
             dv_r=None, dk_p=None, dv_p=None, workspace=None, ctx_cu_host=None,
-            group_seq_cu_host=None, kv_head_of_q=None):
+            group_seq_cu_host=None, kv_head_of_q=None, _noalloc=False):
     """Backward of Call 2 (eq. (4), §3.2).  Adds the responses' prompt-key gradients
     into acc_dk_p/acc_dv_p (fp32 [P,Hkv,d]); with DKV_ACC_FINALIZE also casts the
     accumulator into dk_p/dv_p; with DKV_ACC_SPLIT the terms reach the accumulator
@@ -242,6 +243,12 @@ def dkv_bwd(q_resp, k_p, v_p, k_r, v_r, o_r, lse_r, dout_r, cu_seqlens, *, acc_d
     _need(dv_r, k_r.shape, k_r.dtype, "dv_r", dev)
     _need(dk_p, k_p.shape, k_p.dtype, "dk_p", dev)
     _need(dv_p, k_p.shape, k_p.dtype, "dv_p", dev)
+    if _noalloc:
+        L.check(L.lib().dkv_bwd_noalloc(p, _p(q_resp), _p(k_p), _p(v_p), _p(k_r), _p(v_r),
+                                        _p(o_r), _p(lse_r), _p(dout_r), _p(dq_r), _p(dk_r),
+                                        _p(dv_r), _p(acc_dk_p), _p(acc_dv_p), int(acc_flags),
+                                        _p(dk_p), _p(dv_p), _stream(q_resp.device)))
+        return dq_r, dk_r, dv_r, dk_p, dv_p
     call = L.DKV_CALL_BWD_SPLIT if acc_flags & L.DKV_ACC_SPLIT else L.DKV_CALL_BWD
     ws, nws = _ws(p, call, q_resp.device, workspace)
     L.check(L.lib().dkv_bwd(p, _p(q_resp), _p(k_p), _p(v_p), _p(k_r), _p(v_r), _p(o_r),
@@ -249,6 +256,23 @@ def dkv_bwd(q_resp, k_p, v_p, k_r, v_r, o_r, lse_r, dout_r, cu_seqlens, *, acc_d
                             _p(acc_dv_p), int(acc_flags), _p(dk_p), _p(dv_p), _p(ws), nws,
                             _stream(q_resp.device)))
     return dq_r, dk_r, dv_r, dk_p, dv_p
+
+
+def dkv_bwd_noalloc(q_resp, k_p, v_p, k_r, v_r, o_r, lse_r, dout_r, cu_seqlens, *, acc_dk_p,
+                    acc_dv_p, acc_flags=0, cu_host=None, window_left=-1, softmax_scale=0.0,
+                    dq_r=None, dk_r=None, dv_r=None, dk_p=None, dv_p=None, ctx_cu_host=None,
+                    group_seq_cu_host=None, kv_head_of_q=None):
+    """dkv_bwd without a workspace (the library's own 64 MiB scratch array per GPU; see
+    dkv_bwd_noalloc in include/dkv.h).  Pass every output tensor to avoid torch
+    allocations here too.  Calls that overlap on one GPU race."""
+    return dkv_bwd(q_resp, k_p, v_p, k_r, v_r, o_r, lse_r, dout_r, cu_seqlens,
+                   acc_dk_p=acc_dk_p, acc_dv_p=acc_dv_p, acc_flags=acc_flags, cu_host=cu_host,
+                   window_left=window_left, softmax_scale=softmax_scale, dq_r=dq_r, dk_r=dk_r,
+                   dv_r=dv_r, dk_p=dk_p, dv_p=dv_p, ctx_cu_host=ctx_cu_host,
+                   group_seq_cu_host=group_seq_cu_host, kv_head_of_q=kv_head_of_q,
+                   _noalloc=True)
+
+
 
 
 def dkv_cast_acc(acc_dk, acc_dv, dk, dv):

@@ -60,6 +60,8 @@ _SIGS = {
                                    ctypes.c_int, _vp, _sz, _vp]),
     "dkv_bwd": (ctypes.c_int, [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                _vp, ctypes.c_int, _vp, _vp, _vp, _sz, _vp]),
+    "dkv_bwd_noalloc": (ctypes.c_int, [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp]),
     "dkv_cast_acc": (ctypes.c_int, [_pp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]),
     "dkv_layout_workspace_size": (_sz, [_pp, ctypes.c_int]),
     "dkv_layout": (ctypes.c_int, [_pp, ctypes.c_int, ctypes.c_int64, _vp, _vp, _vp, _sz, _vp]),

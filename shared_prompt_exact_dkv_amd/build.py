@@ -23,7 +23,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["dkv_api.cpp", "dkv_fwd.hip", "dkv_bwd.hip", "dkv_d512.hip", "dkv_layout.hip"]
+SOURCES = ["dkv_api.cpp", "dkv_fwd.hip", "dkv_bwd.hip", "dkv_d512.hip", "dkv_layout.hip",
+           "dkv_noalloc.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include")]

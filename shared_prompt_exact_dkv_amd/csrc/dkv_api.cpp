@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "../../include/dkv.h"
+#include "dkv_internal.h"
 #include "dkv_launch.h"
 
 using namespace dkv;
@@ -966,6 +967,47 @@ dkv_status check_layout(const dkv_params *p, int op, long row_elems, Shape *s) {
 
 }  // namespace
 
+// ------------------------------------------------------ internal entry points --
+
+namespace dkv {
+
+dkv_status bwd_call(const dkv_params *p, const void *q_resp, const void *k_p, const void *v_p,
+                    const void *k_r, const void *v_r, const void *o_r, const float *lse_r,
+                    const void *dout_r, void *dq_r, void *dk_r, void *dv_r, float *acc_dk_p,
+                    float *acc_dv_p, int acc_flags, void *dk_p, void *dv_p, void *ws,
+                    size_t ws_bytes, hipStream_t stream, bool pageable) {
+  Shape s;
+  dkv_status st = check_params(p, false, &s);
+  if (st != DKV_OK) return st;
+  if (acc_flags & ~(DKV_ACC_ZERO | DKV_ACC_FINALIZE | DKV_ACC_SPLIT))
+    return fail(DKV_ERR_INVALID_ARG, "unknown accumulator flags 0x%x", acc_flags);
+  bool need = s.T > 0;
+  bool needp = s.P > 0;
+  if ((st = check_ptr(q_resp, "q_resp", need)) || (st = check_ptr(k_p, "k_p", need && needp)) ||
+      (st = check_ptr(v_p, "v_p", need && needp)) || (st = check_ptr(k_r, "k_r", need)) ||
+      (st = check_ptr(v_r, "v_r", need)) || (st = check_ptr(o_r, "o_r", need)) ||
+      (st = check_ptr(lse_r, "lse_r", need)) || (st = check_ptr(dout_r, "dout_r", need)) ||
+      (st = check_ptr(dq_r, "dq_r", need)) || (st = check_ptr(dk_r, "dk_r", need)) ||
+      (st = check_ptr(dv_r, "dv_r", need)) ||
+      (st = check_ptr(acc_dk_p, "acc_dk_p", needp)) ||
+      (st = check_ptr(acc_dv_p, "acc_dv_p", needp)))
+    return st;
+  if ((acc_flags & DKV_ACC_FINALIZE) &&
+      ((st = check_ptr(dk_p, "dk_p", needp)) || (st = check_ptr(dv_p, "dv_p", needp))))
+    return st;
+  BwdIO io{};
+  io.q = q_resp; io.kc = k_p; io.vc = v_p; io.ko = k_r; io.vo = v_r; io.o = o_r;
+  io.dout = dout_r; io.lse = lse_r; io.dq = dq_r; io.dk_own = dk_r; io.dv_own = dv_r;
+  io.acc_dk = needp ? acc_dk_p : nullptr; io.acc_dv = needp ? acc_dv_p : nullptr;
+  io.acc_rows = s.P; io.flags = acc_flags; io.dk_fin = dk_p; io.dv_fin = dv_p;
+  io.with_ctx = true; io.own_to_acc = false;
+  return run_bwd(s, io, ws, ws_bytes, stream, pageable ? Staging::kPageable : Staging::kPinned);
+}
+
+dkv_status report(dkv_status st, const char *msg) { return fail(st, "%s", msg); }
+
+}  // namespace dkv
+
 // ====================================================================== C ABI ==
 
 extern "C" {
@@ -1096,32 +1138,8 @@ dkv_status dkv_bwd(const dkv_params *p, const void *q_resp, const void *k_p, con
                    const void *dout_r, void *dq_r, void *dk_r, void *dv_r, float *acc_dk_p,
                    float *acc_dv_p, int acc_flags, void *dk_p, void *dv_p, void *ws,
                    size_t ws_bytes, hipStream_t stream) {
-  Shape s;
-  dkv_status st = check_params(p, false, &s);
-  if (st != DKV_OK) return st;
-  if (acc_flags & ~(DKV_ACC_ZERO | DKV_ACC_FINALIZE | DKV_ACC_SPLIT))
-    return fail(DKV_ERR_INVALID_ARG, "unknown accumulator flags 0x%x", acc_flags);
-  bool need = s.T > 0;
-  bool needp = s.P > 0;
-  if ((st = check_ptr(q_resp, "q_resp", need)) || (st = check_ptr(k_p, "k_p", need && needp)) ||
-      (st = check_ptr(v_p, "v_p", need && needp)) || (st = check_ptr(k_r, "k_r", need)) ||
-      (st = check_ptr(v_r, "v_r", need)) || (st = check_ptr(o_r, "o_r", need)) ||
-      (st = check_ptr(lse_r, "lse_r", need)) || (st = check_ptr(dout_r, "dout_r", need)) ||
-      (st = check_ptr(dq_r, "dq_r", need)) || (st = check_ptr(dk_r, "dk_r", need)) ||
-      (st = check_ptr(dv_r, "dv_r", need)) ||
-      (st = check_ptr(acc_dk_p, "acc_dk_p", needp)) ||
-      (st = check_ptr(acc_dv_p, "acc_dv_p", needp)))
-    return st;
-  if ((acc_flags & DKV_ACC_FINALIZE) &&
-      ((st = check_ptr(dk_p, "dk_p", needp)) || (st = check_ptr(dv_p, "dv_p", needp))))
-    return st;
-  BwdIO io{};
-  io.q = q_resp; io.kc = k_p; io.vc = v_p; io.ko = k_r; io.vo = v_r; io.o = o_r;
-  io.dout = dout_r; io.lse = lse_r; io.dq = dq_r; io.dk_own = dk_r; io.dv_own = dv_r;
-  io.acc_dk = needp ? acc_dk_p : nullptr; io.acc_dv = needp ? acc_dv_p : nullptr;
-  io.acc_rows = s.P; io.flags = acc_flags; io.dk_fin = dk_p; io.dv_fin = dv_p;
-  io.with_ctx = true; io.own_to_acc = false;
-  return run_bwd(s, io, ws, ws_bytes, stream, Staging::kPinned);
+  return dkv::bwd_call(p, q_resp, k_p, v_p, k_r, v_r, o_r, lse_r, dout_r, dq_r, dk_r, dv_r,
+                       acc_dk_p, acc_dv_p, acc_flags, dk_p, dv_p, ws, ws_bytes, stream, false);
 }
 
 dkv_status dkv_cast_acc(const dkv_params *p, int32_t rows, const float *acc_dk,

@@ -83,6 +83,22 @@ def test_head_map_validation_and_workspace():
         assert a == b and c > a, (call, a, b, c)
 
 
+def test_noalloc_backward_refuses_on_the_host():
+    # The entry point without a workspace validates like dkv_bwd and refuses calls whose
+    # scratch exceeds its 64 MiB array, before any device work (and before it looks up
+    # the array's device address).
+    lib = L.lib()
+    args = [FAKE] * 13 + [0, FAKE, FAKE, None]
+    bad, k0 = _params(head_dim=3)
+    assert lib.dkv_bwd_noalloc(bad, *args) == L.DKV_ERR_INVALID_ARG
+    assert "head_dim" in L.last_error()
+    T = 200_000   # 64 q-heads: the -D and -LSE / scale rows alone need 102 MB
+    big, k1 = _params(num_seqs=2, cu_host=[0, T // 2, T], num_heads_q=64, num_heads_kv=8)
+    assert lib.dkv_workspace_size(big, L.DKV_CALL_BWD) > (64 << 20)
+    assert lib.dkv_bwd_noalloc(big, *args) == L.DKV_ERR_UNSUPPORTED
+    assert "64" in L.last_error() or str(64 << 20) in L.last_error()
+
+
 def test_ctx_calls_require_zero_ctx_len():
     p, keep = _params(ctx_len=4)
     st = L.lib().dkv_ctx_fwd(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None)
