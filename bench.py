@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (torch), the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
+    ap.add_argument("--gemm-calibration", action="store_true",
+                    help="also time a plain bf16 8192^3 matrix product (torch / hipBLASLt) "
+                         "and report its TFLOP/s beside the published peak")
     return ap.parse_args()
 
 
@@ -111,6 +114,32 @@ def copy_calibration(args):
     torch.cuda.synchronize()
     log(args, "copy calibration: %d bytes read, %d bytes written" % (4 << 28, 4 << 28))
     del src, dst
+
+
+def gemm_calibration(args):
+    """TFLOP/s of a plain bf16 8192^3 matrix product through torch (hipBLASLt): what a
+    tuned dense contraction reaches on this GPU under sustained load, beside the
+    published peak (context only; the roofline uses the published peak)."""
+    import torch
+    n = 8192
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tf = 2 * n ** 3 / (ms * 1e-3) / 1e12
+    log(args, "gemm calibration: bf16 %d^3 in %.3f ms = %.1f TFLOP/s" % (n, ms, tf))
+    del a, b
+    return round(tf, 1)
 
 
 def layout_main(args):
@@ -311,6 +340,46 @@ def main():
     _lib.lib().dkv_timing_reset()
     log(args, "dualkv ms/step %.3f" % ms, ktimes)
 
+    # Per-call breakdown, from a separate pass with events between the four calls (the
+    # timed region above has none): the time of Call 1 and Call 2 against their own
+    # visible pairs.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    call_names = ("ctx_fwd", "fwd", "ctx_bwd", "bwd")
+    call_ms = dict.fromkeys(call_names, 0.0)
+    n_call_steps = max(2, min(args.steps, 5))
+    for _ in range(n_call_steps):
+        ev[0].record()
+        dkv.dkv_ctx_fwd(x["q_p"], x["k_p"], x["v_p"], cu_p, cu_host=cu_p_host, window_left=wl,
+                        out=o_p, lse=lse_p, workspace=ws)
+        ev[1].record()
+        dkv.dkv_fwd(x["q_r"], x["k_p"], x["v_p"], x["k_r"], x["v_r"], cu, cu_host=cu_host,
+                    window_left=wl, out=o_r, lse=lse_r, workspace=ws, **gkw)
+        ev[2].record()
+        dkv.dkv_ctx_bwd(x["q_p"], x["k_p"], x["v_p"], o_p, lse_p, x["do_p"], cu_p,
+                        cu_host=cu_p_host, window_left=wl, dq=dq_p, acc_dk=acc[0],
+                        acc_dv=acc[1], acc_flags=dkv.DKV_ACC_ZERO, workspace=ws)
+        ev[3].record()
+        dkv.dkv_bwd(x["q_r"], x["k_p"], x["v_p"], x["k_r"], x["v_r"], o_r, lse_r, x["do_r"], cu,
+                    acc_dk_p=acc[0], acc_dv_p=acc[1], acc_flags=bwd_flags,
+                    cu_host=cu_host, window_left=wl, dq_r=dq_r, dk_r=dk_r, dv_r=dv_r,
+                    dk_p=dk_p, dv_p=dv_p, workspace=ws, **gkw)
+        ev[4].record()
+        torch.cuda.synchronize()
+        for i, c in enumerate(call_names):
+            call_ms[c] += ev[i].elapsed_time(ev[i + 1]) / n_call_steps
+    pairs_c1 = sum(accounting.pairs_call1(Pj, wl) for Pj, _ in shapes)
+    pairs_c2 = sum(accounting.pairs_call2(Pj, ls, wl) for Pj, ls in shapes)
+    call_pairs = {"ctx_fwd": pairs_c1, "fwd": pairs_c2, "ctx_bwd": pairs_c1, "bwd": pairs_c2}
+    calls = {}
+    for c in call_names:
+        fl = accounting.useful_flops(call_pairs[c], Hq, d, fwd=c.endswith("fwd"),
+                                     bwd=c.endswith("bwd"))
+        calls[c] = {"ms": round(call_ms[c], 4), "pairs_per_head": call_pairs[c],
+                    # picoseconds per visible (row, key) pair of one q-head
+                    "ps_per_pair": round(call_ms[c] * 1e9 / max(1, call_pairs[c] * Hq), 4),
+                    "tflops": round(fl / max(call_ms[c], 1e-9) / 1e9, 2)}
+    log(args, "calls", calls)
+
     pairs = sum(accounting.pairs_dualkv(Pj, ls, wl) for Pj, ls in shapes)
     pairs_nc = sum(accounting.pairs_ncopy(Pj, ls, wl) for Pj, ls in shapes)
     flops = accounting.useful_flops(pairs, Hq, d)
@@ -382,7 +451,9 @@ def main():
 
     # CPU oracle on a bounded sample: the N-copy fwd+bwd of sequence 1 for two kv-head
     # groups (about 10-20 s on the host), extrapolated to the whole workload by
-    # visible-pair count.
+    # visible-pair count.  value: the metric's useful work (DualKV's visible pairs) over
+    # the time the oracle takes to produce the same outputs (the full N-copy problem,
+    # extrapolated); sample_tflops: the oracle's own rate on the work it did.
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -396,19 +467,33 @@ def main():
         do0 = torch.cat([xs["do_p"], xs["do_r"]]).double().numpy()
         t0 = time.perf_counter()
         oracle.seq_fwd(q0, k0, v0, window_left=wl)
+        t1 = time.perf_counter()
         oracle.seq_bwd(q0, k0, v0, do0, window_left=wl)
-        cpu_s = time.perf_counter() - t0
-        full_s = cpu_s * pairs_nc / accounting.causal_pairs(S0, wl) * Hkv / ng
+        t2 = time.perf_counter()
+        fwd_s, bwd_s, cpu_s = t1 - t0, t2 - t1, t2 - t0
+        sample_pairs = accounting.causal_pairs(S0, wl)
+        scale_up = pairs_nc / sample_pairs * Hkv / ng
+        full_s = cpu_s * scale_up
+        sample_flops = accounting.useful_flops(sample_pairs, ng * G, d)
         cpu = {"value": round(flops / full_s / 1e12, 6), "unit": "TFLOP/s",
                "cores": oracle.num_threads(), "kind": "oracle",
+               "affinity_cpus": len(os.sched_getaffinity(0)),
+               "fwd_s": round(fwd_s, 3), "bwd_s": round(bwd_s, 3),
+               "sample_tflops": round(sample_flops / cpu_s / 1e12, 6),
+               "extrapolated_fwd_s": round(fwd_s * scale_up, 1),
+               "extrapolated_bwd_s": round(bwd_s * scale_up, 1),
                "sample": "N-copy fwd+bwd (eq. 2, fp64) of sequence 1 (%d tokens) for %d of %d "
-                         "kv-head groups (%d q-heads); %.1f s, extrapolated by visible-pair "
-                         "count to the full N-copy workload (%.0f s)"
-                         % (S0, ng, Hkv, ng * G, cpu_s, full_s)}
+                         "kv-head groups (%d q-heads): fwd %.1f s + bwd %.1f s with %d OpenMP "
+                         "threads (%d CPUs in the affinity mask); extrapolated by visible-pair "
+                         "count to the full N-copy workload (%.0f s); value = the workload's "
+                         "useful FLOPs over that time"
+                         % (S0, ng, Hkv, ng * G, fwd_s, bwd_s, oracle.num_threads(),
+                            len(os.sched_getaffinity(0)), full_s)}
         log(args, "cpu oracle sample %.2f s" % cpu_s)
 
     if args.copy_calibration:
         copy_calibration(args)
+    gemm = gemm_calibration(args) if args.gemm_calibration else None
 
     speedup = (ncopy_ms / ms) if ncopy_ms else None
     out = {
@@ -439,9 +524,12 @@ def main():
         "bwd_ms": round(bwd_ms, 4),
         "useful_tflop_per_step": round(flops / 1e12, 4),
         "kernels": kernels,
+        "calls": calls,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if gemm is not None:
+        out["gemm_calibration_tflops"] = gemm
     print(json.dumps(out), flush=True)
 
 
