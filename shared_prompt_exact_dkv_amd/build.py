@@ -23,13 +23,13 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["dkv_api.cpp", "dkv_fwd.hip", "dkv_bwd.hip", "dkv_d512.hip", "dkv_layout.hip",
+SOURCES = ["dkv_api.cpp", "dkv_fwd.hip", "dkv_bwd.hip", "dkv_wide.hip", "dkv_layout.hip",
            "dkv_noalloc.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include")]
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
-EXTRA = {"dkv_fwd.hip": VGPR_FORM, "dkv_bwd.hip": VGPR_FORM, "dkv_d512.hip": VGPR_FORM}
+EXTRA = {"dkv_fwd.hip": VGPR_FORM, "dkv_bwd.hip": VGPR_FORM, "dkv_wide.hip": VGPR_FORM}
 
 
 def _compile(src: str) -> str:

@@ -44,6 +44,12 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t elem_size(int dtype) { return dtype == DKV_FP32 ? 4 : 2; }
 
+// Head dims: 64, 96 and 128 run the kernels in which a wave holds whole rows (96 staged
+// in 128-wide rows); 192, 256 and 512 the kernels that split the head dim across waves
+// (192 staged in 256-wide rows).
+bool is_wide(int d) { return d == 192 || d == 256 || d == 512; }
+bool is_head_dim(int d) { return d == 64 || d == 96 || d == 128 || is_wide(d); }
+
 // bf16 and fp16 run the same 16-bit MFMA kernels.
 bool is16(int dtype) { return dtype == DKV_BF16 || dtype == DKV_FP16; }
 bool known_dtype(int dtype) { return is16(dtype) || dtype == DKV_FP32; }
@@ -136,8 +142,9 @@ dkv_status check_params(const dkv_params *p, bool is_ctx, Shape *s) {
   if (p->num_heads_q % p->num_heads_kv != 0)
     return fail(DKV_ERR_INVALID_ARG, "Hq (%d) is not a multiple of Hkv (%d)", p->num_heads_q,
                 p->num_heads_kv);
-  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 512)
-    return fail(DKV_ERR_INVALID_ARG, "head_dim must be 64, 128 or 512 (got %d)", p->head_dim);
+  if (!is_head_dim(p->head_dim))
+    return fail(DKV_ERR_INVALID_ARG, "head_dim must be 64, 96, 128, 192, 256 or 512 (got %d)",
+                p->head_dim);
   if (p->window_left < -1)
     return fail(DKV_ERR_INVALID_ARG, "window_left must be -1 or >= 0 (got %d)", p->window_left);
   if (!known_dtype(p->dtype))
@@ -210,17 +217,17 @@ dkv_status check_params(const dkv_params *p, bool is_ctx, Shape *s) {
   s->bm_tok = kRowsPerWG / G;
   s->bm_tok_dq = s->bm_tok;
   s->kv_tile = kBwdBN;
-  if (s->d == 512) {
-    // Head dim 512 splits the head dim across the waves of a workgroup: 128 query
-    // rows per forward workgroup, 64 per dQ workgroup, 64 keys per dK/dV workgroup;
-    // bf16 only.
+  if (is_wide(s->d)) {
+    // Head dims 192, 256 and 512 split the head dim across the waves of a workgroup:
+    // 128 query rows per forward workgroup, 64 per dQ workgroup, 64 keys per dK/dV
+    // workgroup; 16-bit element types only.
     if (!is16(s->dtype))
-      return fail(DKV_ERR_UNSUPPORTED, "head_dim 512 is implemented for bf16 / fp16 only");
-    if (G > kMaxG512)
-      return fail(DKV_ERR_UNSUPPORTED, "Hq/Hkv = %d exceeds %d at head_dim 512", G, kMaxG512);
-    s->bm_tok = kFwdRows512 / G;
-    s->bm_tok_dq = kRowsPerWG512 / G;
-    s->kv_tile = kBwdBN512;
+      return fail(DKV_ERR_UNSUPPORTED, "head_dim %d is implemented for bf16 / fp16 only", s->d);
+    if (G > kMaxGWide)
+      return fail(DKV_ERR_UNSUPPORTED, "Hq/Hkv = %d exceeds %d at head_dim %d", G, kMaxGWide, s->d);
+    s->bm_tok = kFwdRowsWide / G;
+    s->bm_tok_dq = kRowsPerWGWide / G;
+    s->kv_tile = kBwdBNWide;
   }
   return DKV_OK;
 }

@@ -5,7 +5,7 @@
 //   dP = <dO_t, v_j>,   dS = p * (dP - D_t),    D_t = <dO_t, O_t>
 //   dQ_t += scale * dS * k_j,   dK_j += scale * dS * q_t,   dV_j += p * dO_t
 // Kernels (each h16 kernel has an fp32 counterpart for the 1e-5 parity workload;
-// head dim 512 is in dkv_d512.hip):
+// head dim 512 is in dkv_wide.hip):
 //   bwd_pre   D = rowsum(dO * O) in fp32 (the auxiliary preprocessing launch), stored
 //             negated, and the LSE in units of the raw dot product, -LSE / scale;
 //             the fp32 path only: the h16 dQ kernel forms both for its rows
@@ -32,17 +32,27 @@ namespace dkv {
 
 // ------------------------------------------------------------------ bwd_pre --
 
+// Threads per (token, head) row of the preprocess: one per 16-byte chunk, the group
+// padded to a power of two (24 chunks at head dim 96 -> 32 lanes) so that a row's lanes
+// are aligned inside the wave and the shuffle reduction stays within them.
+template <typename T, int HD> struct PreCfg {
+  static constexpr int E = 16 / sizeof(T);     // elements per 16-byte chunk
+  static constexpr int TPR = HD / E;           // chunks per row
+  static constexpr int TPRP = TPR <= 8 ? 8 : TPR <= 16 ? 16 : TPR <= 32 ? 32 : 64;
+  static_assert(TPR <= 64, "a row's chunks fit one wave");
+};
+
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T *o, const T *dout, const float *lse,
                                                       float *Dneg, float *lsn, long T_tok, int Hq,
                                                       float inv_scale) {
-  constexpr int E = 16 / sizeof(T);          // elements per 16-byte chunk
-  constexpr int TPR = HD / E;                // threads per (token, head) row
+  using C = PreCfg<T, HD>;
+  constexpr int E = C::E;
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-  const long row = gid / TPR;                // token-major: row = t * Hq + h
-  const int ch = gid % TPR;
+  const long row = gid / C::TPRP;            // token-major: row = t * Hq + h
+  const int ch = gid % C::TPRP;
   float acc = 0.f;
-  if (row < T_tok * Hq) {
+  if (row < T_tok * Hq && ch < C::TPR) {
     uint4 a = *reinterpret_cast<const uint4 *>(o + row * HD + ch * E);
     uint4 b = *reinterpret_cast<const uint4 *>(dout + row * HD + ch * E);
     const T *x = reinterpret_cast<const T *>(&a);
@@ -51,7 +61,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T *o, const T *dout,
     for (int e = 0; e < E; ++e) acc += to_f32(x[e]) * to_f32(y[e]);
   }
 #pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  for (int off = C::TPRP / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (row < T_tok * Hq && ch == 0) {
     long t = row / Hq;
     int h = row - t * Hq;
@@ -265,10 +275,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_f32_kernel(BwdQArgs a) {
 // h16 dQ kernel with two waves per SIMD: K and V tiles double-buffered in LDS
 // through buffer loads (one barrier per 64-key tile), each tile taken as two 32-key
 // halves so that Sᵀ, dPᵀ and dSᵀ of one half are live at a time.
-template <typename E, int HD>
+// HDP >= HD: the width of the staged rows (as in the forward).
+template <typename E, int HD, int HDP = HD>
 __global__ __launch_bounds__(256, 2) void bwd_dq_h16_kernel(BwdQArgs a) {
   constexpr int BN = kFwdBN;
-  constexpr int TILE = BN * HD * 2;
+  constexpr int TILE = BN * HDP * 2;
   constexpr int NKC = HD / 16;
   constexpr int NDB = HD / 32;
   __shared__ __attribute__((aligned(16))) char smem[2][2 * TILE];
@@ -341,7 +352,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_h16_kernel(BwdQArgs a) {
   const h16 *ko_base = reinterpret_cast<const h16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
   const h16 *vo_base = reinterpret_cast<const h16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
   const int kld_b = (int)(kld * 2);
-  DmaRows<HD, BN> dma;
+  DmaRows<HDP, BN, HD> dma;
   dma.init(wave, lane, kld_b);
   auto issue = [&](int i) {   // tile i -> stage i % 2
     char *st = smem[i & 1];
@@ -381,8 +392,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_h16_kernel(BwdQArgs a) {
       f32x16 st = zero16(), dpt = negd;
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
-        st = mma16<E>(sw_frag<HD>(ks, hb * 32 + col, kc, half), qf[kc], st);
-        dpt = mma16<E>(sw_frag<HD>(vs, hb * 32 + col, kc, half), df[kc], dpt);
+        st = mma16<E>(sw_frag<HDP>(ks, hb * 32 + col, kc, half), qf[kc], st);
+        dpt = mma16<E>(sw_frag<HDP>(vs, hb * 32 + col, kc, half), df[kc], dpt);
       }
       float ds[16];
       // The visibility test is compiled only into the variant for tiles that need it.
@@ -411,8 +422,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_h16_kernel(BwdQArgs a) {
       // dQᵀ += Kᵀ dSᵀ.
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        acc[db] = mma16<E>(sw_tr_frag<HD>(ks, hb * 32, db * 32, lane), d0, acc[db]);
-        acc[db] = mma16<E>(sw_tr_frag<HD>(ks, hb * 32 + 16, db * 32, lane), d1, acc[db]);
+        acc[db] = mma16<E>(sw_tr_frag<HDP>(ks, hb * 32, db * 32, lane), d0, acc[db]);
+        acc[db] = mma16<E>(sw_tr_frag<HDP>(ks, hb * 32 + 16, db * 32, lane), d1, acc[db]);
       }
     }
   }
@@ -687,16 +698,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdKVArgs a) {
 // precomputed.  With K read from LDS and 32-row steps a wave fits 256 registers and
 // the LDS of two workgroups fits a CU: two waves per SIMD.  MAP: the q-heads of the
 // kv head come from the GQA head table (a.qhead) instead of g * G + j.
-template <typename E, int HD, int BM, int WPE, bool MAP>
+// HDP >= HD: the width of the staged rows (as in the forward).
+template <typename E, int HD, int BM, int WPE, bool MAP, int HDP = HD>
 __global__ __launch_bounds__(256, WPE) void bwd_dkdv_h16_kernel(BwdKVArgs a) {
   constexpr int BNW = kBwdBN;
-  constexpr int TILE = BM * HD * 2;
+  constexpr int TILE = BM * HDP * 2;
   constexpr int NKC = HD / 16;
   constexpr int NDB = HD / 32;
-  constexpr int CPR = HD / 8;                     // 16-byte chunks per row
+  constexpr int CPR = HDP / 8;                    // 16-byte chunks per staged row
   constexpr int KPW = TILE / 1024 / 4;            // DMA instructions per wave per tile
   constexpr int STAGE = 2 * TILE + 2 * 64 * 4;
-  constexpr int KTILE = BNW * HD * 2;            // the workgroup's K tile
+  constexpr int KTILE = BNW * HDP * 2;           // the workgroup's K tile
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE + KTILE];
   char *ktile = smem + 2 * STAGE;
 
@@ -728,7 +740,7 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_h16_kernel(BwdKVArgs a) {
     vf[kc] = as_h16x8(key_valid ? *reinterpret_cast<const uint4 *>(vp + kc * 16 + half * 8) : z);
   }
   {   // the workgroup's K tile (rows past the region's end are zero-filled)
-    DmaRows<HD, BNW> kd;
+    DmaRows<HDP, BNW, HD> kd;
     kd.init(wave, lane, (int)(kld * 2));
     kd.load(ktile,
             reinterpret_cast<const h16 *>(ctx ? a.k_ctx : a.k_own) +
@@ -749,8 +761,8 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_h16_kernel(BwdKVArgs a) {
   // row's low four bits).
   int fo[NKC];
 #pragma unroll
-  for (int kc = 0; kc < NKC; ++kc) fo[kc] = Swz<HD>::off(col, kc * 2 + half);
-  const uint32_t kt_wave = __builtin_amdgcn_readfirstlane(lds_u32(ktile) + kw0 * HD * 2);
+  for (int kc = 0; kc < NKC; ++kc) fo[kc] = Swz<HDP>::off(col, kc * 2 + half);
+  const uint32_t kt_wave = __builtin_amdgcn_readfirstlane(lds_u32(ktile) + kw0 * HDP * 2);
   // Flattened query rows f (token f / G) that see this lane's key: the causal mask
   // (key position <= P + f / G) and the window (key position >= P + f / G - wl) as
   // bounds on f, so the per-element test needs no division.  An invalid key sees none.
@@ -840,7 +852,9 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_h16_kernel(BwdKVArgs a) {
         ++t;
       }
       const int hoff = MAP ? hm.at(j, G) * (HD * 2) : head0_b + j * (HD * 2);
-      const int off = t * qld_b + hoff + (((slot % CPR) ^ Swz<HD>::swz(r)) << 4);
+      const int src = (slot % CPR) ^ Swz<HDP>::swz(r);   // source chunk of this slot
+      // chunks past a padded row's head dim are out of every buffer's range: zeros
+      const int off = (HD == HDP || src < HD / 8) ? t * qld_b + hoff + (src << 4) : 0x7ffffff0;
       dma16(rq, l0 + k * 4096, off);
       dma16(rd, l0 + TILE + k * 4096, off);
     }
@@ -918,7 +932,7 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_h16_kernel(BwdKVArgs a) {
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
-          const char *qrow = qs + rb * 32 * HD * 2 + fo[kc];
+          const char *qrow = qs + rb * 32 * HDP * 2 + fo[kc];
           st = mma16<E>(as_h16x8(*reinterpret_cast<const uint4 *>(qrow)), lds_frag_at(kt + fo[kc]), st);
           dpt = mma16<E>(as_h16x8(*reinterpret_cast<const uint4 *>(qrow + TILE)), vf[kc], dpt);
         }
@@ -962,10 +976,10 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_h16_kernel(BwdKVArgs a) {
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          dv[db] = mma16<E>(p0, sw_tr_frag<HD>(dos, rb * 32, db * 32, lane), dv[db]);
-          dv[db] = mma16<E>(p1, sw_tr_frag<HD>(dos, rb * 32 + 16, db * 32, lane), dv[db]);
-          dk[db] = mma16<E>(s0, sw_tr_frag<HD>(qs, rb * 32, db * 32, lane), dk[db]);
-          dk[db] = mma16<E>(s1, sw_tr_frag<HD>(qs, rb * 32 + 16, db * 32, lane), dk[db]);
+          dv[db] = mma16<E>(p0, sw_tr_frag<HDP>(dos, rb * 32, db * 32, lane), dv[db]);
+          dv[db] = mma16<E>(p1, sw_tr_frag<HDP>(dos, rb * 32 + 16, db * 32, lane), dv[db]);
+          dk[db] = mma16<E>(s0, sw_tr_frag<HDP>(qs, rb * 32, db * 32, lane), dk[db]);
+          dk[db] = mma16<E>(s1, sw_tr_frag<HDP>(qs, rb * 32 + 16, db * 32, lane), dk[db]);
         }
         // transposed dO / Q reads three products ahead
         __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
@@ -1018,8 +1032,7 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_h16_kernel(BwdKVArgs a) {
 template <typename T, int HD>
 static hipError_t pre_t(const void *o, const void *dout, const float *lse, float *Dneg, float *lsn,
                         long T_tok, int Hq, float scale, hipStream_t s) {
-  constexpr int TPR = HD / (16 / sizeof(T));
-  long threads = T_tok * Hq * TPR;
+  long threads = T_tok * Hq * PreCfg<T, HD>::TPRP;
   long blocks = (threads + 255) / 256;
   hipLaunchKernelGGL((bwd_pre_kernel<T, HD>), dim3(blocks), dim3(256), 0, s,
                      reinterpret_cast<const T *>(o), reinterpret_cast<const T *>(dout), lse, Dneg,
@@ -1032,6 +1045,7 @@ hipError_t launch_bwd_pre(int dtype, int hd, const void *o, const void *dout, co
   if (T <= 0) return hipSuccess;
   if (dtype == 1) {   // fp32 only: the h16 dQ kernels form these terms themselves
     if (hd == 64) return pre_t<float, 64>(o, dout, lse, Dneg, lsn, T, Hq, scale, s);
+    if (hd == 96) return pre_t<float, 96>(o, dout, lse, Dneg, lsn, T, Hq, scale, s);
     if (hd == 128) return pre_t<float, 128>(o, dout, lse, Dneg, lsn, T, Hq, scale, s);
   }
   return hipErrorInvalidValue;
@@ -1074,26 +1088,28 @@ static hipError_t dq_f32(const BwdQArgs &a, int n, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename E, int HD, int HDP = HD>
+static hipError_t dq_h16(const BwdQArgs &a, int n, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_dq_h16_kernel<E, HD, HDP>), dim3(n), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_dq(int dtype, int hd, const BwdQArgs &a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (dtype == 0 || dtype == 2) {   // bf16, fp16
-    if (hd == 512) return launch_bwd_dq_d512(dtype, a, n, s);
-    if (hd == 64) {
-      if (dtype == 2)
-        hipLaunchKernelGGL((bwd_dq_h16_kernel<f16, 64>), dim3(n), dim3(256), 0, s, a);
-      else
-        hipLaunchKernelGGL((bwd_dq_h16_kernel<h16, 64>), dim3(n), dim3(256), 0, s, a);
-      return hipGetLastError();
-    }
-    if (hd == 128) {
-      if (dtype == 2)
-        hipLaunchKernelGGL((bwd_dq_h16_kernel<f16, 128>), dim3(n), dim3(256), 0, s, a);
-      else
-        hipLaunchKernelGGL((bwd_dq_h16_kernel<h16, 128>), dim3(n), dim3(256), 0, s, a);
-      return hipGetLastError();
+    const bool f = dtype == 2;
+    switch (hd) {
+      case 64: return f ? dq_h16<f16, 64>(a, n, s) : dq_h16<h16, 64>(a, n, s);
+      case 96: return f ? dq_h16<f16, 96, 128>(a, n, s) : dq_h16<h16, 96, 128>(a, n, s);
+      case 128: return f ? dq_h16<f16, 128>(a, n, s) : dq_h16<h16, 128>(a, n, s);
+      case 192:
+      case 256:
+      case 512: return launch_bwd_dq_wide(dtype, hd, a, n, s);
+      default: break;
     }
   } else {
     if (hd == 64) return dq_f32<64>(a, n, s);
+    if (hd == 96) return dq_f32<96>(a, n, s);
     if (hd == 128) return dq_f32<128>(a, n, s);
   }
   return hipErrorInvalidValue;
@@ -1105,23 +1121,31 @@ static hipError_t dkdv_f32(const BwdKVArgs &a, int n, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename E, int HD>
+template <typename E, int HD, int HDP = HD>
 static hipError_t dkdv_h16(const BwdKVArgs &a, int n, hipStream_t s) {
   if (a.qhead)
-    hipLaunchKernelGGL((bwd_dkdv_h16_kernel<E, HD, 32, 2, true>), dim3(n), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv_h16_kernel<E, HD, 32, 2, true, HDP>), dim3(n), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_dkdv_h16_kernel<E, HD, 32, 2, false>), dim3(n), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv_h16_kernel<E, HD, 32, 2, false, HDP>), dim3(n), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dkdv(int dtype, int hd, const BwdKVArgs &a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (dtype == 0 || dtype == 2) {   // bf16, fp16
-    if (hd == 512) return launch_bwd_dkdv_d512(dtype, a, n, s);
-    if (hd == 64) return dtype == 2 ? dkdv_h16<f16, 64>(a, n, s) : dkdv_h16<h16, 64>(a, n, s);
-    if (hd == 128) return dtype == 2 ? dkdv_h16<f16, 128>(a, n, s) : dkdv_h16<h16, 128>(a, n, s);
+    const bool f = dtype == 2;
+    switch (hd) {
+      case 64: return f ? dkdv_h16<f16, 64>(a, n, s) : dkdv_h16<h16, 64>(a, n, s);
+      case 96: return f ? dkdv_h16<f16, 96, 128>(a, n, s) : dkdv_h16<h16, 96, 128>(a, n, s);
+      case 128: return f ? dkdv_h16<f16, 128>(a, n, s) : dkdv_h16<h16, 128>(a, n, s);
+      case 192:
+      case 256:
+      case 512: return launch_bwd_dkdv_wide(dtype, hd, a, n, s);
+      default: break;
+    }
   } else {
     if (hd == 64) return dkdv_f32<64>(a, n, s);
+    if (hd == 96) return dkdv_f32<96>(a, n, s);
     if (hd == 128) return dkdv_f32<128>(a, n, s);
   }
   return hipErrorInvalidValue;

@@ -1,7 +1,7 @@
 // dkv_fwd.hip -- forward kernels: online softmax over a shared-prompt KV region and a
 // per-sequence KV region in one pass ("DualKV", arXiv 2605.15422, §3.1).  h16 at head
 // dims 64 / 128 runs fwd_bf16_kernel (dkv_fwd_bf16.h), head dim 512 the kernels of
-// dkv_d512.hip; this file holds the fp32 kernel and the dispatch.
+// dkv_wide.hip; this file holds the fp32 kernel and the dispatch.
 //
 // fp32 kernel: one workgroup (4 waves) owns 128 query rows = bm_tok tokens x G q-heads
 // of one kv head (grouped-query attention, §3.1 last paragraph), so every K/V tile
@@ -208,26 +208,28 @@ static hipError_t launch_fwd_f32(const FwdArgs &a, int n, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename E, int HD, int HDP = HD>
+static hipError_t fwd_h16(const FwdArgs &a, int n, hipStream_t s) {
+  hipLaunchKernelGGL((fwd_h16_kernel<E, HD, kFwdBN, 2, HDP>), dim3(n), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd(int dtype, int hd, const FwdArgs &a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (dtype == 0 || dtype == 2) {   // bf16, fp16
-    if (hd == 512) return launch_fwd_d512(dtype, a, n, s);
-    if (hd == 64) {
-      if (dtype == 2)
-        hipLaunchKernelGGL((fwd_h16_kernel<f16, 64, kFwdBN, 2>), dim3(n), dim3(256), 0, s, a);
-      else
-        hipLaunchKernelGGL((fwd_h16_kernel<h16, 64, kFwdBN, 2>), dim3(n), dim3(256), 0, s, a);
-      return hipGetLastError();
-    }
-    if (hd == 128) {
-      if (dtype == 2)
-        hipLaunchKernelGGL((fwd_h16_kernel<f16, 128, kFwdBN, 2>), dim3(n), dim3(256), 0, s, a);
-      else
-        hipLaunchKernelGGL((fwd_h16_kernel<h16, 128, kFwdBN, 2>), dim3(n), dim3(256), 0, s, a);
-      return hipGetLastError();
+    const bool f = dtype == 2;
+    switch (hd) {
+      case 64: return f ? fwd_h16<f16, 64>(a, n, s) : fwd_h16<h16, 64>(a, n, s);
+      case 96: return f ? fwd_h16<f16, 96, 128>(a, n, s) : fwd_h16<h16, 96, 128>(a, n, s);
+      case 128: return f ? fwd_h16<f16, 128>(a, n, s) : fwd_h16<h16, 128>(a, n, s);
+      case 192:
+      case 256:
+      case 512: return launch_fwd_wide(dtype, hd, a, n, s);
+      default: break;
     }
   } else {
     if (hd == 64) return launch_fwd_f32<64>(a, n, s);
+    if (hd == 96) return launch_fwd_f32<96>(a, n, s);
     if (hd == 128) return launch_fwd_f32<128>(a, n, s);
   }
   return hipErrorInvalidValue;

@@ -24,9 +24,11 @@ namespace dkv {
 //     kSlack (log2 units): between rescales the probabilities are exp2(t - m) with
 //     m at most kSlack below the true running maximum, i.e. bounded by 2^kSlack,
 //     and O / l and LSE = m + log2(l) are unchanged in exact arithmetic.
-template <typename E, int HD, int BN, int WPE>
+//   - HDP >= HD is the width of the staged rows (a power of two; head dim 96 is staged
+//     in 128-wide rows whose last chunks read as zeros and are never used).
+template <typename E, int HD, int BN, int WPE, int HDP = HD>
 __global__ __launch_bounds__(256, WPE) void fwd_h16_kernel(FwdArgs a) {
-  constexpr int TILE = BN * HD * 2;     // dense swizzled tile
+  constexpr int TILE = BN * HDP * 2;    // dense swizzled tile
   constexpr int NKC = HD / 16;     // MFMA steps over the head dim
   constexpr int NDB = HD / 32;     // 32-wide blocks of the output head dim
   constexpr int NKB = BN / 32;     // 32-key blocks per tile
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(256, WPE) void fwd_h16_kernel(FwdArgs a) {
   const h16 *vo_base = reinterpret_cast<const h16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
 
   const int kld_b = (int)(kld * 2);
-  DmaRows<HD, BN> dma;
+  DmaRows<HDP, BN, HD> dma;
   dma.init(wave, lane, kld_b);
   auto issue = [&](int i) {   // tile i -> stage i % 2
     char *st = smem[i & 1];
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(256, WPE) void fwd_h16_kernel(FwdArgs a) {
     for (int kc = 0; kc < NKC; ++kc) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        s[kb] = mma16<E>(sw_frag<HD>(ks, kb * 32 + col, kc, half), qf[kc], s[kb]);
+        s[kb] = mma16<E>(sw_frag<HDP>(ks, kb * 32 + col, kc, half), qf[kc], s[kb]);
     }
     // K fragment reads four products ahead
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(256, WPE) void fwd_h16_kernel(FwdArgs a) {
     for (int u = 0; u < 2 * NKB; ++u)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        acc[db] = mma16<E>(sw_tr_frag<HD>(vs, 16 * u, db * 32, lane), pf[u], acc[db]);
+        acc[db] = mma16<E>(sw_tr_frag<HDP>(vs, 16 * u, db * 32, lane), pf[u], acc[db]);
       }
   }
 

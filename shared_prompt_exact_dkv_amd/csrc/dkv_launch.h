@@ -14,14 +14,14 @@ static constexpr int kRowsPerWG = 128;
 // Key rows per dK/dV workgroup (4 waves x 32 keys) and query rows per step.
 static constexpr int kBwdBN = 128;
 static constexpr int kBwdBM = 32;
-// Head dim 512 (the head dim is split across the waves of a workgroup): query rows
-// per forward workgroup (four pairs of waves), query rows per dQ workgroup and keys
-// per dK/dV workgroup (two groups of four waves each), and the largest Hq / Hkv they
-// take.
-static constexpr int kFwdRows512 = 128;
-static constexpr int kRowsPerWG512 = 64;
-static constexpr int kBwdBN512 = 64;
-static constexpr int kMaxG512 = 32;
+// Head dims 192, 256, 512 (the head dim is split across the waves of a workgroup):
+// query rows per forward workgroup (four pairs of waves), query rows per dQ workgroup
+// and keys per dK/dV workgroup (two groups of four waves each), and the largest
+// Hq / Hkv they take.
+static constexpr int kFwdRowsWide = 128;
+static constexpr int kRowsPerWGWide = 64;
+static constexpr int kBwdBNWide = 64;
+static constexpr int kMaxGWide = 32;
 
 // Work item of the query-parallel kernels (forward, dQ).
 struct QItem {
@@ -51,7 +51,7 @@ struct FwdArgs {
 };
 
 hipError_t launch_fwd(int dtype, int head_dim, const FwdArgs &a, int n_items, hipStream_t s);
-hipError_t launch_fwd_d512(int dtype, const FwdArgs &a, int n_items, hipStream_t s);
+hipError_t launch_fwd_wide(int dtype, int head_dim, const FwdArgs &a, int n_items, hipStream_t s);
 
 // ---- backward ----
 
@@ -86,7 +86,7 @@ struct BwdQArgs {
   float scale;
 };
 hipError_t launch_bwd_dq(int dtype, int head_dim, const BwdQArgs &a, int n_items, hipStream_t s);
-hipError_t launch_bwd_dq_d512(int dtype, const BwdQArgs &a, int n_items, hipStream_t s);
+hipError_t launch_bwd_dq_wide(int dtype, int head_dim, const BwdQArgs &a, int n_items, hipStream_t s);
 
 // Work item of the key-parallel dK/dV kernel: one key tile of one region of one kv
 // head, against the query rows of sequences [seq_lo, seq_hi) (all of one prompt group).
@@ -124,7 +124,8 @@ struct BwdKVArgs {
 };
 hipError_t launch_bwd_dkdv(int dtype, int head_dim, const BwdKVArgs &a, int n_items,
                            hipStream_t s);
-hipError_t launch_bwd_dkdv_d512(int dtype, const BwdKVArgs &a, int n_items, hipStream_t s);
+hipError_t launch_bwd_dkdv_wide(int dtype, int head_dim, const BwdKVArgs &a, int n_items,
+                                hipStream_t s);
 
 // ---- layout conversions (N-copy <-> single-prompt packing, first-token rows) ----
 

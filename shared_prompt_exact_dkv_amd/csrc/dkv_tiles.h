@@ -213,45 +213,47 @@ __device__ __forceinline__ h16x8 sw_tr_frag(const char *lds, int row0, int col0,
   return __builtin_bit_cast(h16x8, r);
 }
 
-// Factored fragment addresses for swizzled tiles of 1 KB rows (HD = 512).  In a
-// lane's reads of one tile the swizzle XOR touches only chunk bits 0-3, so every
-// read is one of 8 lane patterns (the XOR of a lane term with a small constant)
-// plus an immediate offset: a tile's 16 reads of each kind cost 8 address
-// operations instead of a full swizzle evaluation per read.  Tile addresses passed
-// in carry the wave's column base (2 bytes per element; a multiple of 128 elements).
-struct Sw512 {
-  uint32_t srow;    // row-operand reads: row col, at col * 1024 + ((half ^ swz(col)) << 4)
+// Factored fragment addresses for swizzled tiles of HDP-wide rows (HDP = 256 or 512:
+// RB = 512 or 1024 bytes per row).  In a lane's reads of one tile the swizzle XOR touches
+// only chunk bits 0-3, so every read is one of 8 lane patterns (the XOR of a lane term
+// with a small constant) plus an immediate offset: a tile's reads of each kind cost 8
+// address operations instead of a full swizzle evaluation per read.
+template <int HDP> struct SwWide {
+  static constexpr int RB = HDP * 2;
+  uint32_t srow;    // row-operand reads: row col, at col * RB + ((half ^ swz(col)) << 4)
   uint32_t tr[2];   // transposed reads: row 4 half + j / 4 (+ 8), 8 (j & 1) bytes in,
                     // chunk term (c_l ^ swz(row)) << 4, c_l = 2 ((lane / 16) & 1) + (j & 3) / 2
   __device__ __forceinline__ void init(int lane) {
     const int col = lane & 31, half = lane >> 5, j = lane & 15;
     const int c_l = 2 * ((lane >> 4) & 1) + ((j & 3) >> 1);
     const int r = 4 * half + (j >> 2);
-    srow = col * 1024 + ((half ^ Swz<512>::swz(col)) << 4);
-    tr[0] = r * 1024 + 8 * (j & 1) + ((c_l ^ Swz<512>::swz(r)) << 4);
-    tr[1] = r * 1024 + 8 * (j & 1) + ((c_l ^ Swz<512>::swz(r + 8)) << 4);
+    srow = col * RB + ((half ^ Swz<HDP>::swz(col)) << 4);
+    tr[0] = r * RB + 8 * (j & 1) + ((c_l ^ Swz<HDP>::swz(r)) << 4);
+    tr[1] = r * RB + 8 * (j & 1) + ((c_l ^ Swz<HDP>::swz(r + 8)) << 4);
   }
   // Keeps the lane terms opaque to the compiler, so the 16 patterns are formed per
   // tile instead of living in registers across a loop.
   __device__ __forceinline__ void opaque() { asm volatile("" : "+v"(srow), "+v"(tr[0]), "+v"(tr[1])); }
-  // Same as sw_frag<512>(tile, col, kc, half) for kc = 0 .. 15 past the column base.
+  // Same as sw_frag<HDP>(tile, col, kc, half) for kc >= 0 past a column base that is a
+  // multiple of 128 elements (folded into `tile`).
   __device__ __forceinline__ h16x8 frag(uint32_t tile, int kc) const {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) const char lchar;
     lchar *base = (lchar *)(size_t)(tile + (srow ^ ((kc & 7) << 5)));
     return __builtin_bit_cast(h16x8, *(const __attribute__((address_space(3))) u32x4 *)(base + (kc >> 3) * 256));
   }
-  // Same as sw_tr_frag<512>(tile, row0, 32 db past the column base, lane), row0 a
-  // multiple of 16, db = 0 .. 7.
+  // Same as sw_tr_frag<HDP>(tile, row0, 32 db, lane): row0 a multiple of 16, db the
+  // 32-wide column block counted from `tile`, which holds a column base that is a
+  // multiple of 128 elements (or none).
   __device__ __forceinline__ h16x8 trfrag(uint32_t tile, int row0, int db) const {
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) s16x4 ls16x4;
     typedef __attribute__((address_space(3))) char lchar;
-    const int o = row0 * 1024 + (db >> 2) * 256;   // immediate offsets
+    const int o = row0 * RB + (db >> 2) * 256;   // immediate offsets
     lchar *b0 = (lchar *)(size_t)(tile + (tr[0] ^ ((db & 3) << 6)));
     lchar *b1 = (lchar *)(size_t)(tile + (tr[1] ^ ((db & 3) << 6)));
     s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4 *)(b0 + o));
-    s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4 *)(b1 + o + 8192));
+    s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ls16x4 *)(b1 + o + 8 * RB));
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     return __builtin_bit_cast(h16x8, r);
@@ -259,17 +261,23 @@ struct Sw512 {
 };
 
 // DMA of a ROWS x HD h16 tile of consecutive rows (row stride ld_bytes, head offset
-// already in `base`) into a swizzled tile.  Block b (1 KB) of the tile is written by
-// wave b % 4; lane i of that instruction fills slot i of the block.  The per-lane
-// source offsets depend only on the thread and the row stride.
-template <int HD, int ROWS> struct DmaRows {
-  static constexpr int kBlocks = ROWS * HD * 2 / 1024;
+// already in `base`) into a swizzled tile of HDP-wide rows (HDP >= HD, a power of two:
+// head dims 96 and 192 are staged in 128- and 256-wide rows whose chunks past HD read as
+// zeros).  Block b (1 KB) of the tile is written by wave b % 4; lane i of that
+// instruction fills slot i of the block.  The per-lane source offsets depend only on
+// the thread and the row stride.
+template <int HDP, int ROWS, int HD = HDP> struct DmaRows {
+  static_assert(HD <= HDP && HD % 8 == 0, "real head dim within the staged row");
+  static constexpr int kBlocks = ROWS * HDP * 2 / 1024;
   static_assert(kBlocks % 4 == 0, "tile must be a multiple of 4 KB");
   static constexpr int kPerWave = kBlocks / 4;
-  // A 1 KB block is one row at HD = 512: the row is wave-uniform, so only the lane's
+  // A 1 KB block is one row at HDP = 512: the row is wave-uniform, so only the lane's
   // chunk offset is kept and the swizzle and row offset are applied per load.
-  static constexpr bool kRowPerBlock = Swz<HD>::kChunks == 64;
+  static constexpr bool kRowPerBlock = Swz<HDP>::kChunks == 64;
+  static_assert(!kRowPerBlock || HD == HDP, "1 KB rows are never padded");
   static constexpr int kRegs = kRowPerBlock ? 1 : kPerWave;
+  // A source offset no buffer range reaches: the lane's slot is zero-filled.
+  static constexpr int kZeroOff = 0x7ffffff0;
   int voff[kRegs];
   int ld = 0, w = 0;
   __device__ __forceinline__ void init(int wave, int lane, int ld_bytes) {
@@ -281,8 +289,9 @@ template <int HD, int ROWS> struct DmaRows {
 #pragma unroll
       for (int k = 0; k < kPerWave; ++k) {
         const int slot = (k * 4 + wave) * 64 + lane;
-        const int r = slot / Swz<HD>::kChunks, cs = slot % Swz<HD>::kChunks;
-        voff[k] = r * ld_bytes + ((cs ^ Swz<HD>::swz(r)) << 4);
+        const int r = slot / Swz<HDP>::kChunks, cs = slot % Swz<HDP>::kChunks;
+        const int src = cs ^ Swz<HDP>::swz(r);   // the source chunk this slot holds
+        voff[k] = src < HD / 8 ? r * ld_bytes + (src << 4) : kZeroOff;
       }
     }
   }
@@ -301,7 +310,7 @@ template <int HD, int ROWS> struct DmaRows {
         const int r = k * 4 + wv;
         // The row offset stays in the vector offset: the buffer range check (which
         // zero-fills rows past nrows) covers the vector and instruction offsets only.
-        dma16(rs, l0 + k * 4096, (voff[0] ^ (Swz<HD>::swz(r) << 4)) + r * lds_);
+        dma16(rs, l0 + k * 4096, (voff[0] ^ (Swz<HDP>::swz(r) << 4)) + r * lds_);
       }
     } else {
 #pragma unroll

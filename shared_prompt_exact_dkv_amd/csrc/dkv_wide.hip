@@ -1,10 +1,14 @@
-// dkv_d512.hip -- head dimension 512 ("DualKV", arXiv 2605.15422, §3 "Head dimensions
-// and sliding-window support": the d = 512 global layers of hybrid models, here also
-// with the sliding window).
+// dkv_wide.hip -- head dimensions 192, 256 and 512 ("DualKV", arXiv 2605.15422, §3 "Head
+// dimensions and sliding-window support": the d = 512 global layers and d = 256
+// sliding-window layers of hybrid models; 192 completes the head dims of App. E.1).
 //
-// A wave's fragments and fp32 accumulators for 32 rows over the whole 512-wide head
-// dim would need 384-768 registers, so the kernels split the head dim across the
-// waves of a workgroup and keep every wave within the architectural VGPRs:
+// A wave's fragments and fp32 accumulators for 32 rows over a wide head dim would need
+// up to 768 registers, so the kernels split the head dim across the waves of a
+// workgroup and keep every wave within the architectural VGPRs.  Tiles are staged in
+// rows of HDP elements (256 or 512, a power of two); head dim 192 is staged in 256-wide
+// rows whose last 64 elements read as zeros (its fragments past the head dim are zero
+// and its outputs there are never stored), so it runs the d = 256 kernels' products.
+// With HDP the staged width:
 //
 //   forward  128 query rows per workgroup of 8 waves (two per SIMD); the two waves of
 //            a pair share 32 rows and each holds Q and O for one half of the head dim.
@@ -25,8 +29,9 @@
 //            accumulates dK and dV for one quarter of the head dim.
 // Every kernel runs two waves per SIMD, and the two groups (pairs) of a workgroup
 // share each staged tile.  Tiles are staged by LDS DMA into swizzled dense rows (one
-// 1 KB row per DMA block), double-buffered; partial tiles are exchanged through a
-// 32 KB LDS area, so the workgroup takes the whole 160 KB of LDS.
+// 1 KB DMA block holds one 512-wide row or two 256-wide rows), double-buffered;
+// partial tiles are exchanged through a 32 KB LDS area (the whole 160 KB of LDS at
+// HDP = 512, 96 KB at 256).
 #include <type_traits>
 
 #include "dkv_device.h"
@@ -36,8 +41,6 @@
 namespace dkv {
 
 namespace {
-
-constexpr int HD = 512;
 
 // One 32 x 32 fp32 C tile per wave in the exchange area, as four 1 KB quads: lane l
 // keeps elements 4q .. 4q+3 at words 256 q + 4 l .. +3 (16-byte accesses, every bank
@@ -65,12 +68,12 @@ __device__ __forceinline__ h16x8 words8(const uint32_t *w) {
 
 // ------------------------------------------------------------------- forward --
 
-template <typename E>
-__global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
+template <typename E, int HD, int HDP>
+__global__ __launch_bounds__(512, 1) void fwd_wide_kernel(FwdArgs a) {
   constexpr int BN = 32;
-  constexpr int TILE = BN * HD * 2;      // 32 KB
-  constexpr int NKH = HD / 2 / 16;       // MFMA k-steps per half head dim
-  constexpr int NDH = HD / 2 / 32;       // 32-wide output blocks per half
+  constexpr int TILE = BN * HDP * 2;     // 32 KB at HDP = 512
+  constexpr int NKH = HDP / 2 / 16;      // MFMA k-steps per half head dim
+  constexpr int NDH = HDP / 2 / 32;      // 32-wide output blocks per half
   constexpr float kSlack = 8.f;
   __shared__ __attribute__((aligned(16))) char smem[4 * TILE + 8 * 4096];
   float *xch = reinterpret_cast<float *>(smem + 4 * TILE);
@@ -94,13 +97,15 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
   const int qmin = P + t0, qmax = P + t0 + nt - 1;
   const long qld = (long)a.Hq * HD;
   const long kld = (long)a.Hkv * HD;
-  const int d0 = dh * (HD / 2);
+  const int d0 = dh * (HDP / 2);
 
   const h16 *qptr = reinterpret_cast<const h16 *>(a.q) + (long)(seq0 + t0 + tok) * qld + (long)h * HD + d0;
   h16x8 qf[NKH];
 #pragma unroll
-  for (int kc = 0; kc < NKH; ++kc)
-    qf[kc] = as_h16x8(*reinterpret_cast<const uint4 *>(qptr + kc * 16 + half * 8));
+  for (int kc = 0; kc < NKH; ++kc)   // dims past the head dim (padded rows) are zero
+    qf[kc] = (HD == HDP || d0 + kc * 16 < HD)
+                 ? as_h16x8(*reinterpret_cast<const uint4 *>(qptr + kc * 16 + half * 8))
+                 : as_h16x8(make_uint4(0, 0, 0, 0));
 
   const float sf = a.scale * kLog2e;
   f32x16 acc[NDH];
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
   const int dw = wave & 3, isv = wave >> 2;
   const h16 *c_base = isv ? vc_base : kc_base;
   const h16 *o_base = isv ? vo_base : ko_base;
-  DmaRows<HD, BN> dma;
+  DmaRows<HDP, BN, HD> dma;
   dma.init(dw, lane, kld_b);
   // Tile i goes to stage i % 2: waves 0-3 fetch its K rows, waves 4-7 its V rows.
   auto issue = [&](int i) {
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
       dma.load(st, o_base + (long)s * kld, kld_b, seqlen - s, dw);
     }
   };
-  Sw512 sw;
+  SwWide<HDP> sw;
   sw.init(lane);
 
   // Partial Sᵀ = K Qᵀ of tile i over this wave's half of the head dim, into the
@@ -148,7 +153,7 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
     f32x16 part = zero16();
 #pragma unroll
     for (int kc = 0; kc < NKH; ++kc)
-      part = mma16<E>(sw.frag(lds_u32(ks) + dh * 512, kc), qf[kc], part);
+      part = mma16<E>(sw.frag(lds_u32(ks) + dh * HDP, kc), qf[kc], part);
     // one fragment read two products ahead
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
@@ -271,7 +276,8 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
   if (row_valid) {
     h16 *optr = reinterpret_cast<h16 *>(a.o) + (long)(seq0 + t0 + tok) * qld + (long)h * HD + d0;
 #pragma unroll
-    for (int db = 0; db < NDH; ++db)
+    for (int db = 0; db < NDH; ++db) {
+      if (HD != HDP && d0 + db * 32 >= HD) continue;   // padded dims: not stored
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int dim = db * 32 + 8 * i + 4 * half;
@@ -280,28 +286,37 @@ __global__ __launch_bounds__(512, 1) void fwd_d512_kernel(FwdArgs a) {
         for (int e = 0; e < 4; ++e) w[e] = rnd<E>(acc[db][4 * i + e] * inv);
         *reinterpret_cast<h16x4 *>(optr + dim) = w;
       }
+    }
     if (half == 0 && dh == 0)
       a.lse[(long)h * a.lse_ld + seq0 + t0 + tok] = (m_run + fast_log2(l)) * kLn2;
   }
 }
 
-hipError_t launch_fwd_d512(int dtype, const FwdArgs &a, int n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  if (dtype == 2)
-    hipLaunchKernelGGL(fwd_d512_kernel<f16>, dim3(n), dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL(fwd_d512_kernel<h16>, dim3(n), dim3(512), 0, s, a);
+template <typename E, int HD, int HDP>
+static hipError_t fwd_wide(const FwdArgs &a, int n, hipStream_t s) {
+  hipLaunchKernelGGL((fwd_wide_kernel<E, HD, HDP>), dim3(n), dim3(512), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_wide(int dtype, int hd, const FwdArgs &a, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const bool f = dtype == 2;
+  switch (hd) {
+    case 192: return f ? fwd_wide<f16, 192, 256>(a, n, s) : fwd_wide<h16, 192, 256>(a, n, s);
+    case 256: return f ? fwd_wide<f16, 256, 256>(a, n, s) : fwd_wide<h16, 256, 256>(a, n, s);
+    case 512: return f ? fwd_wide<f16, 512, 512>(a, n, s) : fwd_wide<h16, 512, 512>(a, n, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // ------------------------------------------------------------------------ dQ --
 
-template <typename E>
-__global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
+template <typename E, int HD, int HDP>
+__global__ __launch_bounds__(512, 1) void bwd_dq_wide_kernel(BwdQArgs a) {
   constexpr int BN = 32;
-  constexpr int TILE = BN * HD * 2;      // 32 KB
-  constexpr int NKH = HD / 2 / 16;
-  constexpr int NDQ = HD / 4 / 32;       // 32-wide output blocks per quarter
+  constexpr int TILE = BN * HDP * 2;     // 32 KB at HDP = 512
+  constexpr int NKH = HDP / 2 / 16;
+  constexpr int NDQ = HDP / 4 / 32;      // 32-wide output blocks per quarter
   __shared__ __attribute__((aligned(16))) char smem[4 * TILE + 8 * 4096];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -329,12 +344,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
   const long kld = (long)a.Hkv * HD;
   const long qrow = (long)(seq0 + t0 + tok);
 
+  const int xd0 = dh * (HDP / 2);   // first dim of this wave's half
   const h16 *xptr = reinterpret_cast<const h16 *>(role == 0 ? a.q : a.dout) + qrow * qld +
-                     (long)h * HD + dh * (HD / 2);
+                     (long)h * HD + xd0;
+  // dims past the head dim (padded rows) are zero
+  auto real = [&](int kc) { return HD == HDP || xd0 + kc * 16 < HD; };
   h16x8 xf[NKH];
 #pragma unroll
   for (int kc = 0; kc < NKH; ++kc)
-    xf[kc] = as_h16x8(*reinterpret_cast<const uint4 *>(xptr + kc * 16 + half * 8));
+    xf[kc] = real(kc) ? as_h16x8(*reinterpret_cast<const uint4 *>(xptr + kc * 16 + half * 8))
+                      : as_h16x8(make_uint4(0, 0, 0, 0));
   const float sf = a.scale * kLog2e;
   const float lse = a.lse[(long)h * a.lse_ld + qrow];
   const float lse2 = lse * kLog2e;
@@ -343,10 +362,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
   // sums its half against O (the two lanes of a row a quarter each), puts it in the
   // exchange area, and every wave adds the halves 0 + 1 after a barrier.
   if (role == 1) {
-    const h16 *optr = reinterpret_cast<const h16 *>(a.o) + qrow * qld + (long)h * HD + dh * (HD / 2);
+    const h16 *optr = reinterpret_cast<const h16 *>(a.o) + qrow * qld + (long)h * HD + xd0;
     float dh_sum = 0.f;
 #pragma unroll
     for (int kc = 0; kc < NKH; ++kc) {
+      if (!real(kc)) continue;
       const h16x8 o8 = as_h16x8(*reinterpret_cast<const uint4 *>(optr + kc * 16 + half * 8));
 #pragma unroll
       for (int e = 0; e < 8; ++e) dh_sum += val<E>(o8[e]) * val<E>(xf[kc][e]);
@@ -361,7 +381,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
     a.Dneg_out[(long)h * a.lse_ld + qrow] = -Dq;
     a.lsn_out[(long)h * a.lse_ld + qrow] = -lse * (1.0f / a.scale);
   }
-  const int dq0 = wq * (HD / 4);
+  const int dq0 = wq * (HDP / 4);
 
   f32x16 acc[NDQ];
 #pragma unroll
@@ -383,7 +403,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
   // Waves 0-3 fetch the K tile, waves 4-7 the V tile.
   const h16 *c_base = grp ? vc_base : kc_base;
   const h16 *o_base = grp ? vo_base : ko_base;
-  DmaRows<HD, BN> dma;
+  DmaRows<HDP, BN, HD> dma;
   dma.init(wq, lane, kld_b);
   auto issue = [&](int i) {
     char *st = smem + (i & 1) * 2 * TILE + grp * TILE;
@@ -395,7 +415,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
       dma.load(st, o_base + (long)s * kld, kld_b, seqlen - s, wq);
     }
   };
-  Sw512 sw;
+  SwWide<HDP> sw;
   sw.init(lane);
   if (n_tiles > 0) issue(0);
 
@@ -421,7 +441,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
     f32x16 part = zero16();
 #pragma unroll
     for (int kc = 0; kc < NKH; ++kc)
-      part = mma16<E>(sw.frag(lds_u32(op) + dh * 512, kc), xf[kc], part);
+      part = mma16<E>(sw.frag(lds_u32(op) + dh * HDP, kc), xf[kc], part);
     // one fragment read two products ahead
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
@@ -475,11 +495,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
       dd[w] = *reinterpret_cast<const uint2 *>(xch + w * 1024 + w * 256 + lane * 2);
     const h16x8 d0 = __builtin_bit_cast(h16x8, make_uint4(dd[0].x, dd[0].y, dd[1].x, dd[1].y));
     const h16x8 d1 = __builtin_bit_cast(h16x8, make_uint4(dd[2].x, dd[2].y, dd[3].x, dd[3].y));
-    // dQᵀ += Kᵀ dSᵀ over this wave's quarter of the head dim.
+    // dQᵀ += Kᵀ dSᵀ over this wave's quarter of the head dim (column blocks counted
+    // from the tile's start: a quarter of a 256-wide row starts inside a swizzle group).
 #pragma unroll
     for (int db = 0; db < NDQ; ++db) {
-      acc[db] = mma16<E>(sw.trfrag(lds_u32(ks) + dq0 * 2, 0, db), d0, acc[db]);
-      acc[db] = mma16<E>(sw.trfrag(lds_u32(ks) + dq0 * 2, 16, db), d1, acc[db]);
+      acc[db] = mma16<E>(sw.trfrag(lds_u32(ks), 0, dq0 / 32 + db), d0, acc[db]);
+      acc[db] = mma16<E>(sw.trfrag(lds_u32(ks), 16, dq0 / 32 + db), d1, acc[db]);
     }
     // one transposed fragment (two reads) two products ahead
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -494,7 +515,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
   if (row_valid) {
     h16 *optr = reinterpret_cast<h16 *>(a.dq) + qrow * qld + (long)h * HD + dq0;
 #pragma unroll
-    for (int db = 0; db < NDQ; ++db)
+    for (int db = 0; db < NDQ; ++db) {
+      if (HD != HDP && dq0 + db * 32 >= HD) continue;   // padded dims: not stored
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int dim = db * 32 + 8 * i + 4 * half;
@@ -503,28 +525,39 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d512_kernel(BwdQArgs a) {
         for (int e = 0; e < 4; ++e) w[e] = rnd<E>(acc[db][4 * i + e] * a.scale);
         *reinterpret_cast<h16x4 *>(optr + dim) = w;
       }
+    }
   }
 }
 
-hipError_t launch_bwd_dq_d512(int dtype, const BwdQArgs &a, int n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  if (dtype == 2)
-    hipLaunchKernelGGL(bwd_dq_d512_kernel<f16>, dim3(n), dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL(bwd_dq_d512_kernel<h16>, dim3(n), dim3(512), 0, s, a);
+template <typename E, int HD, int HDP>
+static hipError_t dq_wide(const BwdQArgs &a, int n, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_dq_wide_kernel<E, HD, HDP>), dim3(n), dim3(512), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_wide(int dtype, int hd, const BwdQArgs &a, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const bool f = dtype == 2;
+  switch (hd) {
+    case 192: return f ? dq_wide<f16, 192, 256>(a, n, s) : dq_wide<h16, 192, 256>(a, n, s);
+    case 256: return f ? dq_wide<f16, 256, 256>(a, n, s) : dq_wide<h16, 256, 256>(a, n, s);
+    case 512: return f ? dq_wide<f16, 512, 512>(a, n, s) : dq_wide<h16, 512, 512>(a, n, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // --------------------------------------------------------------------- dK/dV --
 
 // MAP: the q-heads of the kv head come from the GQA head table (a.qhead).
-template <typename E, bool MAP>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
+template <typename E, int HD, int HDP, bool MAP>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
   constexpr int BM = 32;                 // query rows per step
-  constexpr int TILE = BM * HD * 2;      // 32 KB: one row per 1 KB DMA block
-  constexpr int NKH = HD / 2 / 16;
-  constexpr int NDQ = HD / 4 / 32;
-  constexpr int RPW = BM / 4;            // rows each wave fetches per step
+  constexpr int TILE = BM * HDP * 2;     // 32 KB at HDP = 512
+  constexpr int NKH = HDP / 2 / 16;
+  constexpr int NDQ = HDP / 4 / 32;
+  constexpr int RPB = 1024 / (HDP * 2);  // staged rows per 1 KB DMA block (1 or 2)
+  constexpr int CPR = HDP / 8;           // 16-byte chunks per staged row
+  constexpr int NIW = BM / RPB / 4;      // DMA instructions of each wave per step
   constexpr int STAGE = 2 * TILE;
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE + 8 * 4096];
 
@@ -544,7 +577,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
   const int own0 = ctx ? it.ctx_start : sload_i32(a.cu, it.seq_lo);
   const int nkeys = ctx ? P - it.key_start : sload_i32(a.cu, it.seq_lo + 1) - own0 - it.key_start;
   const int kbase = ctx ? 0 : P;
-  const int nk_tile = min(kBwdBN512, nkeys);
+  const int nk_tile = min(kBwdBNWide, nkeys);
   const int gk0 = grp * 32;              // the group's first key in the tile
   const int nkeys_g = nkeys - gk0;       // keys of the tile this group holds (may be <= 0)
 
@@ -553,20 +586,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
   const float sf = a.scale * kLog2e;
   // K (role 0) or V (role 1) rows of the group's keys, this wave's head-dim half;
   // keys past the tile's end read as zeros (buffer range check).
+  const int xd0 = dh * (HDP / 2);   // first dim of this wave's half
   const h16 *xp = reinterpret_cast<const h16 *>(
                        role == 0 ? (ctx ? a.k_ctx : a.k_own) : (ctx ? a.v_ctx : a.v_own)) +
-                   (long)(own0 + it.key_start + gk0) * kld + (long)g * HD + dh * (HD / 2);
+                   (long)(own0 + it.key_start + gk0) * kld + (long)g * HD + xd0;
   const __amdgpu_buffer_rsrc_t rk =
       make_rsrc_u(xp, nkeys_g > 0 ? (uint32_t)nkeys_g * (uint32_t)(kld * 2) : 0u);
   h16x8 xf[NKH];
 #pragma unroll
-  for (int kc = 0; kc < NKH; ++kc)
-    xf[kc] = __builtin_bit_cast(h16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rk, col * (int)(kld * 2) + (kc * 16 + half * 8) * 2, 0, 0));
+  for (int kc = 0; kc < NKH; ++kc)   // dims past the head dim (padded rows) are zero
+    xf[kc] = (HD == HDP || xd0 + kc * 16 < HD)
+                 ? __builtin_bit_cast(h16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rk, col * (int)(kld * 2) + (kc * 16 + half * 8) * 2, 0, 0))
+                 : as_h16x8(make_uint4(0, 0, 0, 0));
   const int kpos = kbase + it.key_start + key;
   const int f_vis_lo = key_valid ? max(0, (kpos - P) * G) : 0x7fffffff;
   const int f_vis_hi = (wl >= 0) ? max(0, (kpos + wl - P + 1) * G) : 0x7fffffff;
-  const int dq0 = wq * (HD / 4);
+  const int dq0 = wq * (HDP / 4);
 
   f32x16 dk[NDQ], dv[NDQ];
 #pragma unroll
@@ -620,8 +656,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
   if constexpr (MAP) hm.init(a.qhead, g, G, lane);
   const int r4 = 4 % G;                                  // head step of 4 flattened rows
   const int step4 = (4 / G) * qld_b + r4 * (HD * 2);     // their byte step before a wrap
-  // Waves 0-3 fetch the step's Q rows, waves 4-7 its dO rows: row r of the step (a
-  // flattened (token, head) row) fills 1 KB block r, written by wave r % 4.
+  // Waves 0-3 fetch the step's Q rows, waves 4-7 its dO rows: 1 KB block b of the step's
+  // tile (staged rows RPB b .. RPB b + RPB - 1, flattened (token, head) rows) is
+  // written by wave b % 4.
+  // ceil(2^24 / G): r * g_recip >> 24 is r / G exactly for r < 64 and G <= 128.
+  const uint32_t g_recip = __builtin_amdgcn_readfirstlane(((1u << 24) + (uint32_t)G - 1) / (uint32_t)G);
   const h16 *xsrc = reinterpret_cast<const h16 *>(grp ? a.dout : a.q);
   // The first head-dim half of each role starts its partial at -LSE / scale (scores)
   // or -D (dP) of the step's rows: lane l fetches row l % 32's value into a register
@@ -634,24 +673,44 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
     const __amdgpu_buffer_rsrc_t rx =
         make_rsrc_u(xsrc + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
     const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_u32(st + grp * TILE) + wq * 1024);
-    // (token, head) of the wave's first row, then stepped 4 rows at a time without a
-    // division.
-    const int f = cf + wq;
-    int t = (int)((unsigned)f / (unsigned)G);
-    int j = f - t * G;
-    int roff = t * qld_b + head0_b + j * (HD * 2);
+    if constexpr (RPB == 1) {
+      // One row per block, wave-uniform: (token, head) of the wave's first row, then
+      // stepped 4 rows at a time without a division.
+      const int f = cf + wq;
+      int t = (int)((unsigned)f / (unsigned)G);
+      int j = f - t * G;
+      int roff = t * qld_b + head0_b + j * (HD * 2);
 #pragma unroll
-    for (int k = 0; k < RPW; ++k) {
-      const int r = k * 4 + wq;
-      // With a head table the row's head (wave-uniform) comes from the table.
-      const int ro = MAP ? roff - head0_b - j * (HD * 2) + hm.at_uniform(j) * (HD * 2) : roff;
-      dma16(rx, l0 + k * 4096, ro + ((lane ^ Swz<HD>::swz(r)) << 4));
-      // 4 rows on: q4 tokens and r4 heads, plus one token when the head index wraps
-      j += r4;
-      roff += step4;
-      if (j >= G) {
-        j -= G;
-        roff += qld_b - G * HD * 2;
+      for (int k = 0; k < NIW; ++k) {
+        const int r = k * 4 + wq;
+        // With a head table the row's head (wave-uniform) comes from the table.
+        const int ro = MAP ? roff - head0_b - j * (HD * 2) + hm.at_uniform(j) * (HD * 2) : roff;
+        dma16(rx, l0 + k * 4096, ro + ((lane ^ Swz<HDP>::swz(r)) << 4));
+        // 4 rows on: q4 tokens and r4 heads, plus one token when the head index wraps
+        j += r4;
+        roff += step4;
+        if (j >= G) {
+          j -= G;
+          roff += qld_b - G * HD * 2;
+        }
+      }
+    } else {
+      // RPB rows per block: lane l fills chunk slot l % CPR of row RPB b + l / CPR, with
+      // the source chunk that the swizzle puts there (zeros past the head dim).
+      const int ft = cf / G, fj = cf - ft * G;
+#pragma unroll
+      for (int k = 0; k < NIW; ++k) {
+        const int r = RPB * (k * 4 + wq) + lane / CPR;
+        const int tr_ = (int)(((uint32_t)r * g_recip) >> 24);   // r / G (r < 64)
+        int t = ft + tr_, j = fj + (r - tr_ * G);
+        if (j >= G) {
+          j -= G;
+          ++t;
+        }
+        const int hoff = MAP ? hm.at(j, G) * (HD * 2) : head0_b + j * (HD * 2);
+        const int src = (lane % CPR) ^ Swz<HDP>::swz(r);
+        const int off = (HD == HDP || src < HD / 8) ? t * qld_b + hoff + (src << 4) : 0x7ffffff0;
+        dma16(rx, l0 + k * 4096, off);
       }
     }
   };
@@ -677,7 +736,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
       seek();
     }
   };
-  Sw512 sw;
+  SwWide<HDP> sw;
   sw.init(lane);
   int stage = 0;
   bool have = !done;
@@ -719,7 +778,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
     const char *op = role == 0 ? qs : dos;
 #pragma unroll
     for (int kc = 0; kc < NKH; ++kc)
-      part = mma16<E>(sw.frag(lds_u32(op) + dh * 512, kc), xf[kc], part);
+      part = mma16<E>(sw.frag(lds_u32(op) + dh * HDP, kc), xf[kc], part);
     // one fragment read two products ahead
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
@@ -783,10 +842,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
     // dV += Pᵀ dO and dK += dSᵀ Q over this wave's quarter of the head dim.
 #pragma unroll
     for (int db = 0; db < NDQ; ++db) {
-      dv[db] = mma16<E>(p0, sw.trfrag(lds_u32(dos) + dq0 * 2, 0, db), dv[db]);
-      dv[db] = mma16<E>(p1, sw.trfrag(lds_u32(dos) + dq0 * 2, 16, db), dv[db]);
-      dk[db] = mma16<E>(s0, sw.trfrag(lds_u32(qs) + dq0 * 2, 0, db), dk[db]);
-      dk[db] = mma16<E>(s1, sw.trfrag(lds_u32(qs) + dq0 * 2, 16, db), dk[db]);
+      const int cb = dq0 / 32 + db;   // column block counted from the tile's start
+      dv[db] = mma16<E>(p0, sw.trfrag(lds_u32(dos), 0, cb), dv[db]);
+      dv[db] = mma16<E>(p1, sw.trfrag(lds_u32(dos), 16, cb), dv[db]);
+      dk[db] = mma16<E>(s0, sw.trfrag(lds_u32(qs), 0, cb), dk[db]);
+      dk[db] = mma16<E>(s1, sw.trfrag(lds_u32(qs), 16, cb), dk[db]);
     }
     // one transposed fragment (two reads) two products ahead
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -803,7 +863,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
 
   const bool to_acc = ctx || a.own_to_acc;
 #pragma unroll
-  for (int db = 0; db < NDQ; ++db)
+  for (int db = 0; db < NDQ; ++db) {
+    if (HD != HDP && dq0 + db * 32 >= HD) continue;   // padded dims: not stored
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int k = gk0 + c_row(v, half);
@@ -823,20 +884,27 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_d512_kernel(BwdKVArgs a) {
         reinterpret_cast<h16 *>(a.dv_own)[off] = rnd<E>(gv);
       }
     }
+  }
 }
 
-template <typename E>
-static hipError_t dkdv_d512(const BwdKVArgs &a, int n, hipStream_t s) {
+template <typename E, int HD, int HDP>
+static hipError_t dkdv_wide(const BwdKVArgs &a, int n, hipStream_t s) {
   if (a.qhead)
-    hipLaunchKernelGGL((bwd_dkdv_d512_kernel<E, true>), dim3(n), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv_wide_kernel<E, HD, HDP, true>), dim3(n), dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_dkdv_d512_kernel<E, false>), dim3(n), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv_wide_kernel<E, HD, HDP, false>), dim3(n), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv_d512(int dtype, const BwdKVArgs &a, int n, hipStream_t s) {
+hipError_t launch_bwd_dkdv_wide(int dtype, int hd, const BwdKVArgs &a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  return dtype == 2 ? dkdv_d512<f16>(a, n, s) : dkdv_d512<h16>(a, n, s);
+  const bool f = dtype == 2;
+  switch (hd) {
+    case 192: return f ? dkdv_wide<f16, 192, 256>(a, n, s) : dkdv_wide<h16, 192, 256>(a, n, s);
+    case 256: return f ? dkdv_wide<f16, 256, 256>(a, n, s) : dkdv_wide<h16, 256, 256>(a, n, s);
+    case 512: return f ? dkdv_wide<f16, 512, 512>(a, n, s) : dkdv_wide<h16, 512, 512>(a, n, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace dkv

@@ -31,7 +31,10 @@ FAKE = 0x10000   # 16-byte aligned, never dereferenced: validation fails first
 
 @pytest.mark.parametrize("kw,status,frag", [
     (dict(num_heads_q=6, num_heads_kv=4), L.DKV_ERR_INVALID_ARG, "multiple"),
-    (dict(head_dim=96), L.DKV_ERR_INVALID_ARG, "head_dim"),
+    (dict(head_dim=80), L.DKV_ERR_INVALID_ARG, "head_dim"),
+    (dict(head_dim=320), L.DKV_ERR_INVALID_ARG, "head_dim"),
+    (dict(head_dim=256, dtype=L.DKV_FP32), L.DKV_ERR_UNSUPPORTED, "fp16 only"),
+    (dict(head_dim=192, dtype=L.DKV_FP32), L.DKV_ERR_UNSUPPORTED, "fp16 only"),
     (dict(window_left=-2), L.DKV_ERR_INVALID_ARG, "window_left"),
     (dict(cu_host=[1, 5, 9]), L.DKV_ERR_INVALID_ARG, "cu_seqlens[0]"),
     (dict(cu_host=[0, 5, 4]), L.DKV_ERR_INVALID_ARG, "decreases"),

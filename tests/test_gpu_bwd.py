@@ -88,9 +88,9 @@ def _random_cases(n, seed):
     rng = np.random.default_rng(seed)
     cases = []
     for _ in range(n):
-        d = int(rng.choice([64, 128, 512]))
+        d = int(rng.choice([64, 96, 128, 192, 256, 512]))
         hkv = int(rng.choice([1, 2, 4]))
-        g = int(rng.choice([1, 2, 3, 4, 6, 8] if d < 512 else [1, 2, 3, 4]))
+        g = int(rng.choice([1, 2, 3, 4, 6, 8] if d <= 128 else [1, 2, 3, 4]))
         P = int(rng.choice([0, int(rng.integers(1, 200))]))
         N = int(rng.integers(1, 5))
         lens = [int(x) for x in rng.integers(0, 160, size=N)]

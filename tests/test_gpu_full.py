@@ -53,7 +53,8 @@ def _check(name, got, ref, bound=None, rel=REL["bf16"], floor=0.0):
 @pytest.mark.parametrize("name,split", [("qwen3_8b", False), ("dapo_varlen", False),
                                         ("large_rollout", False), ("d512_global", False),
                                         ("d512_swa", False), ("qwen3_8b", True),
-                                        ("d512_swa", True), ("table1_p4k", False),
+                                        ("d512_swa", True), ("d256_swa", False),
+                                        ("table1_p4k", False),
                                         ("table1_p64k", True)])
 def test_full_size_parity(name, split):
     w = workloads.WORKLOADS[name]

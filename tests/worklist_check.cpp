@@ -42,14 +42,14 @@ int main(int argc, char **argv) {
       seq.push_back(seq.back() + n);
       for (int i = 0; i < n; ++i) cu.push_back(cu.back() + ((rng() % 5 == 0) ? rng() % 2 : rng() % 300));
     }
-    const int hds[3] = {64, 128, 512};
+    const int hds[6] = {64, 96, 128, 192, 256, 512};
     const int Gs[5] = {1, 2, 3, 4, 8};
     dkv_params p{};
     p.num_seqs = seq.back();
     p.ctx_len = ctx.back();
     p.num_heads_kv = 1 + rng() % 4;
     p.num_heads_q = p.num_heads_kv * Gs[rng() % 5];
-    p.head_dim = hds[rng() % 3];
+    p.head_dim = hds[rng() % 6];
     p.window_left = (rng() % 3 == 0) ? (int)(rng() % 200) : -1;
     p.dtype = DKV_BF16;
     p.cu_seqlens_host = cu.data();

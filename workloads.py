@@ -6,7 +6,7 @@ the CPU oracle (``oracle/``) and the HIP path may use it without sharing method 
 Shapes follow the workloads in "DualKV: Shared-Prompt Flash Attention for Efficient
 RL Training with Large Rollouts and Long Contexts" (arXiv 2605.15422): Qwen3-8B
 attention dimensions (H=32 query heads, 8 KV heads, d=128, §4.1 / Table 1),
-GRPO/DAPO rollout sizes (§4.2), and the Gemma-4 head-dim-512 global and
+GRPO/DAPO rollout sizes (§4.2), and the Gemma-4 head-dim-512 global and head-dim-256
 sliding-window layers (§3 "Head dimensions and sliding-window support").  No
 dataset is read: every tensor is drawn from a seeded CPU generator.
 
@@ -82,6 +82,11 @@ WORKLOADS = {
                             Hkv=4, d=512, dtype="bf16", seed=5),
     "d512_swa": Workload("d512_swa", P=57344, N=8, R=8192, R_range=None, Hq=16, Hkv=4,
                          d=512, dtype="bf16", window_left=1023, seed=6),
+    # The sliding-window layers of the same hybrid model run at head dim 256 (§3 "Head
+    # dimensions and sliding-window support"): the d = 512 pair's shape and window at
+    # d = 256.
+    "d256_swa": Workload("d256_swa", P=57344, N=8, R=8192, R_range=None, Hq=16, Hkv=4,
+                         d=256, dtype="bf16", window_left=1023, seed=15),
     # The shapes of the paper's kernel benchmark (§4.1, Table 1): Qwen3-8B attention
     # dimensions, R = 2048 per response, fp16, global causal.
     "table1_p4k": Workload("table1_p4k", P=4096, N=28, R=2048, R_range=None, Hq=32, Hkv=8,
