@@ -58,9 +58,10 @@ extern "C" {
 typedef enum {
     DKV_OK = 0,
     DKV_ERR_INVALID_ARG = 1,   /* inconsistent shapes, bad cu_seqlens, null pointers */
-    /* valid but not implemented: head_dim 512 in fp32, Hq / Hkv above 128 (32 at
-       head_dim 512), or (bf16 / fp16) a sequence whose query rows, plus 64, exceed 2^31 bytes
-       or Hq * tokens above 2^29 -- the kernels' 32-bit row offsets */
+    /* valid but not implemented: head_dim 192, 256 or 512 in fp32, Hq / Hkv above 128
+       (32 at head_dim 192, 256, 512), or (bf16 / fp16) a sequence whose query rows, plus
+       64, exceed 2^31 bytes or Hq * tokens above 2^29 -- the kernels' 32-bit row
+       offsets */
     DKV_ERR_UNSUPPORTED = 2,
     DKV_ERR_WORKSPACE = 3,     /* ws too small or misaligned */
     DKV_ERR_HIP = 4            /* a HIP runtime call failed */
@@ -108,7 +109,10 @@ typedef struct {
     int32_t num_heads_q;       /* Hq, a multiple of Hkv (grouped-query attention) */
     int32_t num_heads_kv;      /* Hkv; q-head h reads kv head h / (Hq / Hkv) unless
                                   kv_head_of_q says otherwise */
-    int32_t head_dim;          /* d: 64, 128 or 512 */
+    /* d: 64, 96, 128, 192, 256 or 512 (the head dims of the paper's kernel checks,
+       App. E.1, and the d = 512 / d = 256 global / sliding-window layers of §3); fp32
+       tensors take 64, 96 and 128 */
+    int32_t head_dim;
     /* -1: global causal.  w >= 0: key at logical position j is visible from the query
        at logical position t iff t - w <= j <= t (applies to the prompt region too). */
     int32_t window_left;
