@@ -97,7 +97,10 @@ def traffic_for(kernel, workload):
     rec = json.load(open(path))
     h = hashlib.sha256()
     for f in rec.get("sources", []):
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        path = os.path.join(ROOT, f)
+        if not os.path.exists(path):   # a source since renamed or removed: stale
+            return None
+        h.update(open(path, "rb").read())
     if h.hexdigest() != rec.get("sources_sha256"):
         return None
     return rec.get("bytes_per_launch")
