@@ -125,6 +125,16 @@ __device__ __forceinline__ void dma_wait() {
   asm volatile("" ::: "memory");
 }
 
+// s_waitcnt vmcnt(K) (K < 64): wait until at most the K most recently issued vector
+// memory loads are outstanding (loads complete in issue order), e.g. all but the next
+// stage's DMA loads.  Through the builtin, for the same reason as dma_wait.
+template <int K> __device__ __forceinline__ void dma_wait_keep() {
+  static_assert(K >= 0 && K < 64, "vmcnt field");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (K & 15) | ((K >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+
 // A buffer resource built from values the compiler cannot prove wave-uniform (the
 // callers' are uniform by construction): the operands of the DMA instructions must
 // live in scalar registers.

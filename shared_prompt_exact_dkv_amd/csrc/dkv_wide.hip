@@ -200,7 +200,7 @@ __global__ __launch_bounds__(512, 1) void fwd_wide_kernel(FwdArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = 8 * (v >> 2) + (v & 3);   // c_row(v, half) - 4 half
-        s[v] = (r >= lo) & (r < hi) ? s[v] : -INFINITY;
+        s[v] = ((r >= lo) & (r < hi)) ? s[v] : -INFINITY;
       }
     }
     float mx = -INFINITY;
@@ -254,10 +254,11 @@ __global__ __launch_bounds__(512, 1) void fwd_wide_kernel(FwdArgs a) {
   // lands before phase 2i + 2; V of tile i + 1 by waves 4-7 in phase 2i + 1 (last read
   // in phase 2i) and lands before phase 2i + 3.  Every wave passes 2 n + 2 barriers.
   const bool lead = wave < 4;
-  if (n_tiles > 0) {
-    issue(0);
-    dma_wait();
-  }
+  // The wait is taken on every path, tile or not: it also covers the Q fragments loaded
+  // above, so no path reaches the loop with those loads still counted as in flight
+  // (the compiler would then wait for them inside the loop, behind the next tile's DMA).
+  if (n_tiles > 0) issue(0);
+  dma_wait();
   __syncthreads();
   if (!lead) __syncthreads();
   for (int i = 0; i < n_tiles; ++i) {
@@ -417,6 +418,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_wide_kernel(BwdQArgs a) {
   };
   SwWide<HDP> sw;
   sw.init(lane);
+  // Every load above has landed before the first DMA: the loop's waits count DMAs only,
+  // and no fragment load is left for the compiler to wait on inside the loop (where
+  // its wait would drain the next tile's DMA as well).
+  dma_wait();
   if (n_tiles > 0) issue(0);
 
   for (int i = 0; i < n_tiles; ++i) {
@@ -476,7 +481,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_wide_kernel(BwdQArgs a) {
         float p = fast_exp2(fmaf(st[e], sf, -lse2));
         if (MASKED) {
           const int r = 8 * q + e;   // c_row(4 q + e, half) - 4 half
-          p = (r >= lo) & (r < hi) ? p : 0.f;
+          p = ((r >= lo) & (r < hi)) ? p : 0.f;
         }
         dsq[e] = p * (dpt[e] - Dq);
       }
@@ -549,7 +554,11 @@ hipError_t launch_bwd_dq_wide(int dtype, int hd, const BwdQArgs &a, int n, hipSt
 // --------------------------------------------------------------------- dK/dV --
 
 // MAP: the q-heads of the kv head come from the GQA head table (a.qhead).
-template <typename E, int HD, int HDP, bool MAP>
+// NST: Q/dO stages in flight (3 where the LDS holds them, at HDP = 256: a step's fetch
+// then has two steps' time to land; the rows' -LSE / scale and -D then travel with the
+// stage, fetched into its LDS, so that every load of the loop is a DMA load whose
+// completion the kernel counts itself).
+template <typename E, int HD, int HDP, bool MAP, int NST>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
   constexpr int BM = 32;                 // query rows per step
   constexpr int TILE = BM * HDP * 2;     // 32 KB at HDP = 512
@@ -558,8 +567,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
   constexpr int RPB = 1024 / (HDP * 2);  // staged rows per 1 KB DMA block (1 or 2)
   constexpr int CPR = HDP / 8;           // 16-byte chunks per staged row
   constexpr int NIW = BM / RPB / 4;      // DMA instructions of each wave per step
-  constexpr int STAGE = 2 * TILE;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE + 8 * 4096];
+  static_assert(NST == 2 || NST == 3, "double or triple buffering");
+  // With NST = 3 a stage also holds 64 words of -LSE / scale and 64 of -D (rows 0..31
+  // of the step, then the zeros of the DMA lanes past them).
+  constexpr int STAGE = 2 * TILE + (NST > 2 ? 512 : 0);
+  __shared__ __attribute__((aligned(16))) char smem[NST * STAGE + 8 * 4096];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -568,7 +580,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
   // and role 1 partial dP with V, over head-dim half dh.
   const int grp = wave >> 2, wq = wave & 3;
   const int role = wq >> 1, dh = wq & 1;
-  float *xch = reinterpret_cast<float *>(smem + 2 * STAGE) + grp * 4 * 1024;
+  float *xch = reinterpret_cast<float *>(smem + NST * STAGE) + grp * 4 * 1024;
   const KVItem it = a.items[blockIdx.x];
   const int g = it.g, G = a.G, P = it.ctx_len, wl = a.window_left;
   const bool ctx = it.region == kRegionCtx;
@@ -667,6 +679,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
   // one step ahead, and the wave spreads it over the C layout with ds_bpermute.
   const __amdgpu_buffer_rsrc_t r_ld = make_rsrc_u(role == 0 ? (const void *)a.lsn : (const void *)a.Dneg,
                                                   (uint32_t)((long)a.Hq * a.lse_ld * 4));
+  // With NST = 3: the first group's first wave stages -LSE / scale, the second's -D.
+  const __amdgpu_buffer_rsrc_t r_init = make_rsrc_u(grp == 0 ? (const void *)a.lsn : (const void *)a.Dneg,
+                                                    (uint32_t)((long)a.Hq * a.lse_ld * 4));
   auto issue = [&](char *st) {
     const int s0 = cs0;
     const int len = clen;
@@ -713,6 +728,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
         dma16(rx, l0 + k * 4096, off);
       }
     }
+    if constexpr (NST > 2) {
+      // The rows' -LSE / scale (first wave of the first group) and -D (first wave of
+      // the second) into the stage: lane l < 32 fetches row l's word, the other lanes
+      // nothing (zeros).
+      if (wq == 0) {
+        const int f = cf + lane;
+        const int t = (int)((unsigned)f / (unsigned)G), j = f - t * G;
+        const int hq = MAP ? hm.at(j & 63, G) : g * G + j;   // j < G for every lane
+        const int off = lane < BM ? (hq * a.lse_ld + s0 + t) * 4 : 0x7fffffff;
+        dma4(r_init, __builtin_amdgcn_readfirstlane(lds_u32(st + 2 * TILE) + grp * 256), off);
+      }
+    }
   };
   // Row init values of the step at the cursor (rows past the sequence read 0 and are
   // masked later).
@@ -738,41 +765,82 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
   };
   SwWide<HDP> sw;
   sw.init(lane);
+  // Every load above has landed before the first DMA (see the dQ kernel).
+  dma_wait();
   int stage = 0;
   bool have = !done;
-  int f0 = 0, flo = 0, fend = 0;
+  int f0 = 0, flo = 0, fend = 0;   // the step at hand
+  bool have1 = false;              // NST = 3: the next step, already in flight
+  int h0 = 0, hlo = 0, hend = 0;
   float xinit = 0.f;
   if (have) {
     issue(smem);
-    if (dh == 0) xinit = fetch_init();
+    if constexpr (NST == 2) {
+      if (dh == 0) xinit = fetch_init();
+    }
     advance();
     f0 = nf0, flo = nflo, fend = nfend;
+    if constexpr (NST > 2) {
+      have1 = !done;
+      if (have1) {
+        issue(smem + STAGE);
+        advance();
+        h0 = nf0, hlo = nflo, hend = nfend;
+      }
+    }
   }
 
   const int kpa = kbase + it.key_start + gk0;
   const int kpb = kpa + 31;
   while (have) {
-    // The partial's start values (waits for this step's fetches, which the barrier
-    // below needs anyway).
     f32x16 part = zero16();
-    if (dh == 0) {
-      const int xi = __builtin_bit_cast(int, xinit);
+    if constexpr (NST == 2) {
+      // The partial's start values (waits for this step's fetches, which the barrier
+      // below needs anyway).
+      if (dh == 0) {
+        const int xi = __builtin_bit_cast(int, xinit);
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        part[v] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(c_row(v, half) << 2, xi));
+        for (int v = 0; v < 16; ++v)
+          part[v] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(c_row(v, half) << 2, xi));
+      }
+      dma_wait();
+    } else {
+      // This step has landed; the next step's loads, issued after it, may still be in
+      // flight (each wave's own count: its row DMAs, plus the init words of a group's
+      // first wave).
+      if (have1) {
+        if (wq == 0)
+          dma_wait_keep<NIW + 1>();
+        else
+          dma_wait_keep<NIW>();
+      } else {
+        dma_wait();
+      }
     }
-    dma_wait();
     __syncthreads();
     const bool more = !done;
     int g0 = 0, glo = 0, gend = 0;
-    if (more) {
-      issue(smem + (stage ^ 1) * STAGE);
-      if (dh == 0) xinit = fetch_init();
+    if (more) {   // every wave is done with the stage of the previous step
+      issue(smem + (NST == 2 ? (stage ^ 1) : (stage == 0 ? 2 : stage - 1)) * STAGE);
+      if constexpr (NST == 2) {
+        if (dh == 0) xinit = fetch_init();
+      }
       advance();
       g0 = nf0, glo = nflo, gend = nfend;
     }
     const char *qs = smem + stage * STAGE;
     const char *dos = qs + TILE;
+    if constexpr (NST > 2) {
+      // start values from the stage: rows 8 i + 4 half .. + 3 of the C layout
+      if (dh == 0) {
+        const float *ini = reinterpret_cast<const float *>(qs + 2 * TILE) + (role ? 64 : 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 x = *reinterpret_cast<const float4 *>(ini + 8 * i + 4 * half);
+          part[4 * i] = x.x, part[4 * i + 1] = x.y, part[4 * i + 2] = x.z, part[4 * i + 3] = x.w;
+        }
+      }
+    }
     sw.opaque();
 
     const char *op = role == 0 ? qs : dos;
@@ -817,7 +885,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
         float p = fast_exp2(st[e] * sf);
         if (MASKED) {
           const int r = 8 * q + e;
-          p = (r >= lo) & (r < hi) ? p : 0.f;
+          p = ((r >= lo) & (r < hi)) ? p : 0.f;
         }
         pq[e] = p;
         dq[e] = p * dpt[e];
@@ -856,9 +924,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    have = more;
-    f0 = g0, flo = glo, fend = gend;
-    stage ^= 1;
+    if constexpr (NST == 2) {
+      have = more;
+      f0 = g0, flo = glo, fend = gend;
+      stage ^= 1;
+    } else {
+      have = have1;
+      have1 = more;
+      f0 = h0, flo = hlo, fend = hend;
+      h0 = g0, hlo = glo, hend = gend;
+      stage = stage == 2 ? 0 : stage + 1;
+    }
   }
 
   const bool to_acc = ctx || a.own_to_acc;
@@ -889,10 +965,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
 
 template <typename E, int HD, int HDP>
 static hipError_t dkdv_wide(const BwdKVArgs &a, int n, hipStream_t s) {
+  constexpr int NST = HDP <= 256 ? 3 : 2;
   if (a.qhead)
-    hipLaunchKernelGGL((bwd_dkdv_wide_kernel<E, HD, HDP, true>), dim3(n), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv_wide_kernel<E, HD, HDP, true, NST>), dim3(n), dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_dkdv_wide_kernel<E, HD, HDP, false>), dim3(n), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv_wide_kernel<E, HD, HDP, false, NST>), dim3(n), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
