@@ -64,6 +64,19 @@ template <typename E> __device__ __forceinline__ uint32_t pack2(float x, float y
 __device__ __forceinline__ h16x8 words8(const uint32_t *w) {
   return __builtin_bit_cast(h16x8, make_uint4(w[0], w[1], w[2], w[3]));
 }
+// Issue order of a run of N products, each fed by R LDS reads: the reads run A
+// products ahead (A * R reads first, then a product and the next product's reads, and
+// the last A products at the end).
+template <int N, int R, int A> __device__ __forceinline__ void reads_ahead() {
+  static_assert(A >= 1 && A <= N, "read-ahead depth");
+  __builtin_amdgcn_sched_group_barrier(0x100, A * R, 0);
+#pragma unroll
+  for (int i = 0; i < N - A; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
+}
 }  // namespace
 
 // ------------------------------------------------------------------- forward --
@@ -154,14 +167,7 @@ __global__ __launch_bounds__(512, 1) void fwd_wide_kernel(FwdArgs a) {
 #pragma unroll
     for (int kc = 0; kc < NKH; ++kc)
       part = mma16<E>(sw.frag(lds_u32(ks) + dh * HDP, kc), qf[kc], part);
-    // one fragment read two products ahead
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int kc = 0; kc < NKH - 2; ++kc) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    reads_ahead<NKH, 1, 2>();   // one fragment read per product, two products ahead
     xch_put(xch + wave * 1024, part, lane);
   };
   // Softmax of tile i from the pair's two partials, then Oᵀ += Vᵀ Pᵀ.
@@ -236,14 +242,7 @@ __global__ __launch_bounds__(512, 1) void fwd_wide_kernel(FwdArgs a) {
       acc[db] = mma16<E>(sw.trfrag(lds_u32(vs) + d0 * 2, 0, db), p0, acc[db]);
       acc[db] = mma16<E>(sw.trfrag(lds_u32(vs) + d0 * 2, 16, db), p1, acc[db]);
     }
-    // one transposed fragment (two reads) two products ahead
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int m = 0; m < 2 * NDH - 2; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    reads_ahead<2 * NDH, 2, 2>();   // a transposed fragment (two reads) per product, two ahead
   };
 
   // Ping-pong: waves 0-3 run half a tile ahead of waves 4-7 (one of each per SIMD), so
@@ -447,14 +446,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_wide_kernel(BwdQArgs a) {
 #pragma unroll
     for (int kc = 0; kc < NKH; ++kc)
       part = mma16<E>(sw.frag(lds_u32(op) + dh * HDP, kc), xf[kc], part);
-    // one fragment read two products ahead
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int kc = 0; kc < NKH - 2; ++kc) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    reads_ahead<NKH, 1, 2>();   // one fragment read per product, two products ahead
     xch_put(xch + wq * 1024, part, lane);
     __syncthreads();
     const bool need_mask = (nrows < BN) || (kpos0 + BN - 1 > qmin) ||
@@ -507,14 +499,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_wide_kernel(BwdQArgs a) {
       acc[db] = mma16<E>(sw.trfrag(lds_u32(ks), 0, dq0 / 32 + db), d0, acc[db]);
       acc[db] = mma16<E>(sw.trfrag(lds_u32(ks), 16, dq0 / 32 + db), d1, acc[db]);
     }
-    // one transposed fragment (two reads) two products ahead
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int m = 0; m < 2 * NDQ - 2; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    reads_ahead<2 * NDQ, 2, 2>();   // a transposed fragment (two reads) per product, two ahead
   }
 
   if (row_valid) {
@@ -847,14 +832,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
 #pragma unroll
     for (int kc = 0; kc < NKH; ++kc)
       part = mma16<E>(sw.frag(lds_u32(op) + dh * HDP, kc), xf[kc], part);
-    // one fragment read two products ahead
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int kc = 0; kc < NKH - 2; ++kc) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    reads_ahead<NKH, 1, 2>();   // one fragment read per product, two products ahead
     xch_put(xch + wq * 1024, part, lane);
     __syncthreads();
 
@@ -916,14 +894,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
       dk[db] = mma16<E>(s0, sw.trfrag(lds_u32(qs), 0, cb), dk[db]);
       dk[db] = mma16<E>(s1, sw.trfrag(lds_u32(qs), 16, cb), dk[db]);
     }
-    // one transposed fragment (two reads) two products ahead
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int m = 0; m < 4 * NDQ - 2; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    reads_ahead<4 * NDQ, 2, 2>();   // a transposed fragment (two reads) per product, two ahead
     if constexpr (NST == 2) {
       have = more;
       f0 = g0, flo = glo, fend = gend;
