@@ -934,8 +934,329 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
   }
 }
 
+// dK/dV at HDP = 256 (head dims 192 and 256): 128 keys per workgroup of 8 waves, four
+// pairs of 32 keys.  In pair p, wave p (role 0) holds K of the pair's keys over the
+// whole head dim and forms S, P and dV; wave p + 4 (role 1, on the same SIMD) holds V
+// and forms dP, dS and dK.  P crosses from role 0 to role 1 through LDS in fp32, so
+// dS = P (dP - D) is formed as in the other kernels.  Each wave accumulates one
+// gradient over the whole head dim (128 registers).  Three Q / dO stages (each with the
+// rows' -LSE / scale and -D as DMA words) and a double-buffered P area let one barrier
+// per step both hand over the next stage and pass P: every wave waits for its own loads
+// of step i + 1 before the barrier of step i, and the stage of step i - 1, which all
+// waves have finished with by then, takes step i + 2.
+template <typename E, int HD, bool MAP>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdKVArgs a) {
+  constexpr int HDP = 256;
+  constexpr int BM = 32;                 // query rows per step
+  constexpr int TILE = BM * HDP * 2;     // 16 KB
+  constexpr int NKC = HD / 16;           // k-steps over the real head dim
+  constexpr int NDB = HD / 32;           // real 32-wide output blocks
+  constexpr int RPB = 2;                 // staged rows per 1 KB DMA block
+  constexpr int CPR = HDP / 8;           // 16-byte chunks per staged row
+  constexpr int NIW = BM / RPB / 4;      // DMA instructions of each wave per step
+  constexpr int NST = 3;
+  constexpr int STAGE = 2 * TILE + 512;  // Q, dO, then 64 words each of -LSE / scale and -D
+  static_assert(HD == 192 || HD == 256, "head dims staged in 256-wide rows");
+  constexpr int PA = 2;   // fragment reads ahead of the products
+  __shared__ __attribute__((aligned(16))) char smem[NST * STAGE + 2 * 4 * 4096];
+  float *pbuf = reinterpret_cast<float *>(smem + NST * STAGE);   // [2][pair] 32 x 32 P tiles
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int role = wave >> 2, pair = wave & 3;
+  const KVItem it = a.items[blockIdx.x];
+  const int g = it.g, G = a.G, P = it.ctx_len, wl = a.window_left;
+  const bool ctx = it.region == kRegionCtx;
+  const long qld = (long)a.Hq * HD;
+  const long kld = (long)a.Hkv * HD;
+  const int own0 = ctx ? it.ctx_start : sload_i32(a.cu, it.seq_lo);
+  const int nkeys = ctx ? P - it.key_start : sload_i32(a.cu, it.seq_lo + 1) - own0 - it.key_start;
+  const int kbase = ctx ? 0 : P;
+  const int nk_tile = min(kBwdBNPair, nkeys);
+  const int gk0 = pair * 32;             // the pair's first key in the tile
+  const int nkeys_g = nkeys - gk0;       // keys of the tile this pair holds (may be <= 0)
+
+  const int key = gk0 + col;
+  const bool key_valid = key < nkeys;
+  const float sf = a.scale * kLog2e;
+  // K (role 0) or V (role 1) rows of the pair's keys over the whole head dim; keys past
+  // the tile's end read as zeros (buffer range check).
+  const h16 *xp = reinterpret_cast<const h16 *>(
+                       role == 0 ? (ctx ? a.k_ctx : a.k_own) : (ctx ? a.v_ctx : a.v_own)) +
+                   (long)(own0 + it.key_start + gk0) * kld + (long)g * HD;
+  const __amdgpu_buffer_rsrc_t rk =
+      make_rsrc_u(xp, nkeys_g > 0 ? (uint32_t)nkeys_g * (uint32_t)(kld * 2) : 0u);
+  h16x8 xf[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc)
+    xf[kc] = __builtin_bit_cast(h16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rk, col * (int)(kld * 2) + (kc * 16 + half * 8) * 2, 0, 0));
+  const int kpos = kbase + it.key_start + key;
+  const int f_vis_lo = key_valid ? max(0, (kpos - P) * G) : 0x7fffffff;
+  const int f_vis_hi = (wl >= 0) ? max(0, (kpos + wl - P + 1) * G) : 0x7fffffff;
+
+  f32x16 acc[NDB];   // dV (role 0) or dK (role 1) of the pair's keys
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = zero16();
+
+  auto seq_range = [&](int sq, int &fa, int &fb, int &s0, int &len) {
+    s0 = sload_i32(a.cu, sq);
+    len = sload_i32(a.cu, sq + 1) - s0;
+    int r_lo, r_hi;
+    if (ctx) {
+      r_lo = 0;
+      r_hi = len;
+      if (wl >= 0) r_hi = min(len, it.key_start + nk_tile - 1 + wl - P + 1);
+    } else {
+      r_lo = it.key_start;
+      r_hi = len;
+      if (wl >= 0) r_hi = min(len, it.key_start + nk_tile - 1 + wl + 1);
+    }
+    fa = r_lo * G;
+    fb = r_hi > r_lo ? r_hi * G : fa;
+  };
+  // Steps of BM flattened rows, walked from the last one backward; the cursor keeps the
+  // sequence start and length of its seek.
+  int cs = it.seq_hi - 1, cf = 0, cfa = 0, cfb = 0, cs0 = 0, clen = 0;
+  bool done = false;
+  auto seek = [&]() {
+    while (cs >= it.seq_lo) {
+      int fa, fb, s0, len;
+      seq_range(cs, fa, fb, s0, len);
+      if (fb > fa) {
+        cfa = fa;
+        cfb = fb;
+        cs0 = s0;
+        clen = len;
+        cf = ((fb - 1) / BM) * BM;
+        return;
+      }
+      --cs;
+    }
+    done = true;
+  };
+  seek();
+
+  const int qld_b = (int)(qld * 2);
+  const int head0_b = g * G * HD * 2;
+  HeadMap hm;
+  if constexpr (MAP) hm.init(a.qhead, g, G, lane);
+  // ceil(2^24 / G): r * g_recip >> 24 is r / G exactly for r < 64 and G <= 128.
+  const uint32_t g_recip = __builtin_amdgcn_readfirstlane(((1u << 24) + (uint32_t)G - 1) / (uint32_t)G);
+  const h16 *xsrc = reinterpret_cast<const h16 *>(role ? a.dout : a.q);
+  // Role 0 waves fetch the step's Q rows, role 1 waves its dO rows: 1 KB block b of a
+  // tile (staged rows 2 b and 2 b + 1) is written by the wave of pair b % 4.  The first
+  // wave of each role also fetches its rows' -LSE / scale (role 0) or -D (role 1).
+  const __amdgpu_buffer_rsrc_t r_init = make_rsrc_u(role == 0 ? (const void *)a.lsn : (const void *)a.Dneg,
+                                                    (uint32_t)((long)a.Hq * a.lse_ld * 4));
+  auto issue = [&](char *st) {
+    const int s0 = cs0;
+    const int len = clen;
+    const __amdgpu_buffer_rsrc_t rx =
+        make_rsrc_u(xsrc + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
+    const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_u32(st + role * TILE) + pair * 1024);
+    const int ft = cf / G, fj = cf - ft * G;
+#pragma unroll
+    for (int k = 0; k < NIW; ++k) {
+      const int r = RPB * (k * 4 + pair) + lane / CPR;
+      const int tr_ = (int)(((uint32_t)r * g_recip) >> 24);   // r / G (r < 64)
+      int t = ft + tr_, j = fj + (r - tr_ * G);
+      if (j >= G) {
+        j -= G;
+        ++t;
+      }
+      const int hoff = MAP ? hm.at(j, G) * (HD * 2) : head0_b + j * (HD * 2);
+      const int src = (lane % CPR) ^ Swz<HDP>::swz(r);
+      const int off = (HD == HDP || src < HD / 8) ? t * qld_b + hoff + (src << 4) : 0x7ffffff0;
+      dma16(rx, l0 + k * 4096, off);
+    }
+    if (pair == 0) {   // lane l < 32 fetches row l's word, the other lanes zeros
+      const int f = cf + lane;
+      const int t = (int)((unsigned)f / (unsigned)G), j = f - t * G;
+      const int hq = MAP ? hm.at(j & 63, G) : g * G + j;   // j < G for every lane
+      const int off = lane < BM ? (hq * a.lse_ld + s0 + t) * 4 : 0x7fffffff;
+      dma4(r_init, __builtin_amdgcn_readfirstlane(lds_u32(st + 2 * TILE) + role * 256), off);
+    }
+  };
+
+  int nf0 = 0, nflo = 0, nfend = 0;
+  auto advance = [&]() {
+    nf0 = cf;
+    nflo = max(cf, cfa);
+    nfend = min(cf + BM, cfb);
+    cf -= BM;
+    if (cf + BM <= cfa) {
+      --cs;
+      seek();
+    }
+  };
+  SwWide<HDP> sw;
+  sw.init(lane);
+  // Every load above has landed before the first DMA (see the dQ kernel).
+  dma_wait();
+  int stage = 0, pb = 0;
+  bool have = !done;
+  int f0 = 0, flo = 0, fend = 0;   // the step at hand
+  bool have1 = false;              // the next step, already in flight
+  int h0 = 0, hlo = 0, hend = 0;
+  if (have) {
+    issue(smem);
+    advance();
+    f0 = nf0, flo = nflo, fend = nfend;
+    have1 = !done;
+    if (have1) {
+      issue(smem + STAGE);
+      advance();
+      h0 = nf0, hlo = nflo, hend = nfend;
+    }
+  }
+  // Step 0 has landed (step 1's loads, issued after it, may still be in flight).
+  if (have1) {
+    if (pair == 0)
+      dma_wait_keep<NIW + 1>();
+    else
+      dma_wait_keep<NIW>();
+  } else {
+    dma_wait();
+  }
+  __syncthreads();
+
+  const int kpa = kbase + it.key_start + gk0;
+  const int kpb = kpa + 31;
+  while (have) {
+    const char *qs = smem + stage * STAGE;
+    const char *dos = qs + TILE;
+    float *pt = pbuf + (pb * 4 + pair) * 1024;
+    // Scores (role 0) or dP (role 1) of the pair's keys over the whole head dim, started
+    // at -LSE / scale or -D of the rows (C layout: rows 8 i + 4 half .. + 3).
+    auto product = [&]() {
+      f32x16 part;
+      const float *ini = reinterpret_cast<const float *>(qs + 2 * TILE) + role * 64;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 x = *reinterpret_cast<const float4 *>(ini + 8 * i + 4 * half);
+        part[4 * i] = x.x, part[4 * i + 1] = x.y, part[4 * i + 2] = x.z, part[4 * i + 3] = x.w;
+      }
+      sw.opaque();
+      const char *op = role == 0 ? qs : dos;
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+        part = mma16<E>(sw.frag(lds_u32(op), kc), xf[kc], part);
+      reads_ahead<NKC, 1, PA>();   // one fragment read per product, PA products ahead
+      return part;
+    };
+    h16x8 x0, x1;   // P (role 0) or dS (role 1), rows 0..15 and 16..31 of the step
+    if (role == 0) {
+      // S, then P; the visibility test is compiled only into the variant for steps that
+      // straddle a mask edge or a range end.  Every row of the step sees every key of
+      // the pair when the step lies inside the causal and window bounds of both its
+      // first and last key.
+      const f32x16 st = product();
+      const bool full = (f0 >= flo) && (f0 + BM <= fend) && (32 <= nkeys_g) &&
+                        ((kpb - P) * G <= flo) && (wl < 0 || fend <= (kpa - P + wl + 1) * G);
+      float pv[16];
+      auto probs = [&](auto masked_c) {
+        constexpr bool MASKED = decltype(masked_c)::value;
+        const int lo = max(flo, f_vis_lo) - f0 - 4 * half;   // visible row offsets [lo, hi)
+        const int hi = min(fend, f_vis_hi) - f0 - 4 * half;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float p = fast_exp2(st[v] * sf);
+          if (MASKED) {
+            const int r = 8 * (v >> 2) + (v & 3);   // c_row(v, half) - 4 half
+            p = ((r >= lo) & (r < hi)) ? p : 0.f;
+          }
+          pv[v] = p;
+        }
+      };
+      if (full)
+        probs(std::false_type{});
+      else
+        probs(std::true_type{});
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4 *>(pt + q * 256 + lane * 4) =
+            make_float4(pv[4 * q], pv[4 * q + 1], pv[4 * q + 2], pv[4 * q + 3]);
+      x0 = pack8<E>(pv);   // packed before the barrier: only these cross it
+      x1 = pack8<E>(pv + 8);
+    }
+    // This wave's loads of the next step have landed (nothing newer is in flight); after
+    // the barrier the next stage and this step's P are visible to every wave, and every
+    // wave is done with the previous step's stage.
+    dma_wait();
+    __syncthreads();
+    const bool more = !done;
+    int g0 = 0, glo = 0, gend = 0;
+    if (more) {
+      issue(smem + (stage == 0 ? 2 : stage - 1) * STAGE);
+      advance();
+      g0 = nf0, glo = nflo, gend = nfend;
+    }
+    if (role == 1) {
+      // dP - D after the barrier (so it is not held across it), then dS = P (dP - D)
+      const f32x16 dpt = product();
+      float dsv[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 p4 = xch_quad(pt, q, lane);
+        dsv[4 * q] = p4.x * dpt[4 * q];
+        dsv[4 * q + 1] = p4.y * dpt[4 * q + 1];
+        dsv[4 * q + 2] = p4.z * dpt[4 * q + 2];
+        dsv[4 * q + 3] = p4.w * dpt[4 * q + 3];
+      }
+      x0 = pack8<E>(dsv);
+      x1 = pack8<E>(dsv + 8);
+    }
+    // dV += Pᵀ dO (role 0) or dK += dSᵀ Q (role 1) over the whole head dim.
+    const char *bs = role == 0 ? dos : qs;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      acc[db] = mma16<E>(x0, sw.trfrag(lds_u32(bs), 0, db), acc[db]);
+      acc[db] = mma16<E>(x1, sw.trfrag(lds_u32(bs), 16, db), acc[db]);
+    }
+    reads_ahead<2 * NDB, 2, PA>();   // a transposed fragment (two reads) per product, PA ahead
+    have = have1;
+    have1 = more;
+    f0 = h0, flo = hlo, fend = hend;
+    h0 = g0, hlo = glo, hend = gend;
+    stage = stage == 2 ? 0 : stage + 1;
+    pb ^= 1;
+  }
+
+  const bool to_acc = ctx || a.own_to_acc;
+  const float gs = role == 0 ? 1.f : a.scale;   // dK carries the softmax scale
+  float *acc_out = role == 0 ? a.acc_dv : a.acc_dk;
+  float *split_out = role == 0 ? a.split_dv : a.split_dk;
+  h16 *own_out = reinterpret_cast<h16 *>(role == 0 ? a.dv_own : a.dk_own);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int k = gk0 + c_row(v, half);
+      if (k >= nkeys) continue;
+      const long off = (long)(own0 + it.key_start + k) * kld + (long)g * HD + db * 32 + col;
+      const float gv = acc[db][v] * gs;
+      if (ctx && a.split_dk) {   // split mode: the chunk's own slice, one writer
+        split_out[(long)(it.seq_lo / a.split_chunk) * a.split_stride + off] = gv;
+      } else if (to_acc) {
+        atomicAdd(acc_out + off, gv);
+      } else {
+        own_out[off] = rnd<E>(gv);
+      }
+    }
+  }
+}
+
 template <typename E, int HD, int HDP>
 static hipError_t dkdv_wide(const BwdKVArgs &a, int n, hipStream_t s) {
+  if constexpr (HDP == 256) {
+    if (a.qhead)
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<E, HD, true>), dim3(n), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<E, HD, false>), dim3(n), dim3(512), 0, s, a);
+    return hipGetLastError();
+  }
   constexpr int NST = HDP <= 256 ? 3 : 2;
   if (a.qhead)
     hipLaunchKernelGGL((bwd_dkdv_wide_kernel<E, HD, HDP, true, NST>), dim3(n), dim3(512), 0, s, a);

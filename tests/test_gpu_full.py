@@ -7,7 +7,8 @@ rows.  Every key / value gradient -- including the shared dK_P / dV_P summed ove
 N sequences and both calls (eq. (6)) -- is then a sum over those rows only, which
 the oracle computes exactly for ALL keys; dQ must match on the selected rows and be
 zero elsewhere.  O and LSE are checked on sampled rows of the prompt and of the
-sampled sequences.  The kernels do the same work whatever the values, so this
+sampled sequences: the ends, the middle, the window edges and six seeded interior
+rows of each.  The kernels do the same work whatever the values, so this
 exercises the full-size paths completely.
 
 In the N-copy packing (eq. (1)) each copy i gets its own prompt-row gradient; here
@@ -101,10 +102,15 @@ def test_full_size_parity(name, split):
     # ---- oracle ----
     f64 = lambda a: np.ascontiguousarray(a.numpy(), dtype=np.float64)
     k_p, v_p = f64(x["k_p"]), f64(x["v_p"])
-    # forward: prompt rows (a copy's prompt prefix) and the sampled sequences' rows
-    o_ref, lse_ref = oracle.rows_fwd(k_p, v_p, p_rows, x["q_p"][p_rows], window_left=wl)
-    chk("o_p[rows]", o_p[p_rows], o_ref)
-    chk("lse_p[rows]", lse_p[:, p_rows].t(), lse_ref, bound=2e-3)
+    # forward: prompt rows (a copy's prompt prefix) and the sampled sequences' rows, each
+    # with a few seeded interior rows besides the ends (other query tiles, other offsets
+    # from the key-tile edges; forward only, dO stays zero there)
+    rng = np.random.default_rng(9000 + w.seed)
+    interior = lambda n: sorted(set(rng.integers(2, max(3, n - 2), size=6).tolist()))
+    fwd_p_rows = sorted(set(p_rows) | set(interior(P)))
+    o_ref, lse_ref = oracle.rows_fwd(k_p, v_p, fwd_p_rows, x["q_p"][fwd_p_rows], window_left=wl)
+    chk("o_p[rows]", o_p[fwd_p_rows], o_ref)
+    chk("lse_p[rows]", lse_p[:, fwd_p_rows].t(), lse_ref, bound=2e-3)
     dk_p_ref = np.zeros((P, Hkv, d))
     dv_p_ref = np.zeros((P, Hkv, d))
     # prompt rows of every copy: dO_P^(i) = dO_P / N
@@ -120,10 +126,12 @@ def test_full_size_parity(name, split):
         v_i = np.concatenate([v_p, f64(x["v_r"][a:b])])
         rows = resp_rows[i]
         idx = [a + r for r in rows]
-        o_ref, lse_ref = oracle.rows_fwd(k_i, v_i, [P + r for r in rows], x["q_r"][idx],
+        frows = sorted(set(rows) | set(interior(b - a)))
+        fidx = [a + r for r in frows]
+        o_ref, lse_ref = oracle.rows_fwd(k_i, v_i, [P + r for r in frows], x["q_r"][fidx],
                                          window_left=wl)
-        chk("o_r[seq %d]" % i, o_r[idx], o_ref)
-        chk("lse_r[seq %d]" % i, lse_r[:, idx].t(), lse_ref, bound=2e-3)
+        chk("o_r[seq %d]" % i, o_r[fidx], o_ref)
+        chk("lse_r[seq %d]" % i, lse_r[:, fidx].t(), lse_ref, bound=2e-3)
         dk_i = np.zeros_like(k_i)
         dv_i = np.zeros_like(v_i)
         dq_i = oracle.rows_bwd_scatter(k_i, v_i, [P + r for r in rows], x["q_r"][idx],
