@@ -219,15 +219,15 @@ dkv_status check_params(const dkv_params *p, bool is_ctx, Shape *s) {
   s->kv_tile = kBwdBN;
   if (is_wide(s->d)) {
     // Head dims 192, 256 and 512 split the head dim across the waves of a workgroup:
-    // 128 query rows per forward workgroup, 64 per dQ workgroup, 64 keys per dK/dV
-    // workgroup at 512 and 128 at 192 / 256 (pairs of waves there); 16-bit element
-    // types only.
+    // 128 query rows per forward workgroup; at 512, 64 query rows per dQ and 64 keys per
+    // dK/dV workgroup, at 192 / 256 (pairs of waves) 128 of each; 16-bit element types
+    // only.
     if (!is16(s->dtype))
       return fail(DKV_ERR_UNSUPPORTED, "head_dim %d is implemented for bf16 / fp16 only", s->d);
     if (G > kMaxGWide)
       return fail(DKV_ERR_UNSUPPORTED, "Hq/Hkv = %d exceeds %d at head_dim %d", G, kMaxGWide, s->d);
     s->bm_tok = kFwdRowsWide / G;
-    s->bm_tok_dq = kRowsPerWGWide / G;
+    s->bm_tok_dq = (s->d == 512 ? kRowsPerWGWide : kRowsPerWGPair) / G;
     s->kv_tile = s->d == 512 ? kBwdBNWide : kBwdBNPair;
   }
   return DKV_OK;

@@ -21,8 +21,10 @@ static constexpr int kBwdBM = 32;
 static constexpr int kFwdRowsWide = 128;
 static constexpr int kRowsPerWGWide = 64;
 static constexpr int kBwdBNWide = 64;
-// Keys per dK/dV workgroup at head dims 192 and 256 (four pairs of waves, 32 keys each).
+// Head dims 192 and 256 run the backward in pairs of waves: keys per dK/dV workgroup
+// and query rows per dQ workgroup (four pairs, 32 each).
 static constexpr int kBwdBNPair = 128;
+static constexpr int kRowsPerWGPair = 128;
 static constexpr int kMaxGWide = 32;
 
 // Work item of the query-parallel kernels (forward, dQ).

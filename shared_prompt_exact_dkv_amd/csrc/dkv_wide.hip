@@ -519,9 +519,223 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_wide_kernel(BwdQArgs a) {
   }
 }
 
+// dQ at HDP = 256 (head dims 192 and 256): 128 query rows per workgroup of 8 waves,
+// four pairs of 32 rows.  In pair p, wave p (role 0) holds Q of the pair's rows over the
+// whole head dim and forms Sᵀ = K Qᵀ; wave p + 4 (role 1, on the same SIMD) holds dO and
+// forms dPᵀ = V dOᵀ.  Each writes its tile to LDS, and after one barrier both read the
+// two tiles back, form dSᵀ for the whole tile and accumulate dQ over their half of the
+// head dim.  Three K / V stages and a double-buffered tile area let that one barrier
+// per key tile also hand over the next stage (each wave waits for its own loads of
+// tile i + 1 first; the stage of tile i - 1, finished by every wave at the barrier of
+// tile i, takes tile i + 2).
+template <typename E, int HD>
+__global__ __launch_bounds__(512, 1) void bwd_dq_pair_kernel(BwdQArgs a) {
+  constexpr int HDP = 256;
+  constexpr int BN = 32;
+  constexpr int TILE = BN * HDP * 2;     // 16 KB
+  constexpr int NKC = HD / 16;           // k-steps over the real head dim
+  constexpr int NDH = HDP / 2 / 32;      // 32-wide output blocks per half of the head dim
+  constexpr int NST = 3;
+  constexpr int PA = 2;                  // fragment reads ahead of the products
+  static_assert(HD == 192 || HD == 256, "head dims staged in 256-wide rows");
+  __shared__ __attribute__((aligned(16))) char smem[NST * 2 * TILE + 2 * 8 * 4096];
+  float *tbuf = reinterpret_cast<float *>(smem + NST * 2 * TILE);   // [2][wave] 32 x 32 tiles
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int role = wave >> 2, pair = wave & 3;
+  const QItem it = a.items[blockIdx.x];
+  const int g = it.g, seq0 = it.seq_start, seqlen = it.seq_len;
+  const int t0 = it.tile * a.bm_tok;
+  const int nt = min(a.bm_tok, seqlen - t0);
+  const int qr = pair * 32 + col;
+  int tok = qr / a.G;
+  const int hj = qr - tok * a.G;
+  const bool row_valid = tok < nt;
+  if (!row_valid) tok = nt - 1;
+  const int h = q_head(a.qhead, g, a.G, hj);
+  const int P = it.ctx_len, wl = a.window_left;
+  const int qpos = P + t0 + tok;
+  const int qmin = P + t0, qmax = P + t0 + nt - 1;
+  const long qld = (long)a.Hq * HD;
+  const long kld = (long)a.Hkv * HD;
+  const long qrow = (long)(seq0 + t0 + tok);
+
+  const h16 *xptr = reinterpret_cast<const h16 *>(role == 0 ? a.q : a.dout) + qrow * qld + (long)h * HD;
+  h16x8 xf[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc)
+    xf[kc] = as_h16x8(*reinterpret_cast<const uint4 *>(xptr + kc * 16 + half * 8));
+  const float sf = a.scale * kLog2e;
+  const float lse = a.lse[(long)h * a.lse_ld + qrow];
+  const float lse2 = lse * kLog2e;
+  // D = rowsum(dO ∘ O) of this lane's row (the backward's preprocess, done here): the
+  // dO-holding wave sums the row against O (the two lanes of a row half each) and
+  // passes it to its partner through LDS.
+  float *dx = tbuf + pair * 32;
+  if (role == 1) {
+    const h16 *optr = reinterpret_cast<const h16 *>(a.o) + qrow * qld + (long)h * HD;
+    float dsum = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const h16x8 o8 = as_h16x8(*reinterpret_cast<const uint4 *>(optr + kc * 16 + half * 8));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum += val<E>(o8[e]) * val<E>(xf[kc][e]);
+    }
+    dsum = pair_sum(dsum);
+    if (half == 0) dx[col] = dsum;
+  }
+  __syncthreads();
+  const float Dq = dx[col];
+  // The dK/dV kernel, which runs next, reads -D and -LSE / scale of every row.
+  if (role == 1 && half == 0 && row_valid) {
+    a.Dneg_out[(long)h * a.lse_ld + qrow] = -Dq;
+    a.lsn_out[(long)h * a.lse_ld + qrow] = -lse * (1.0f / a.scale);
+  }
+  const int dq0 = role * (HDP / 2);   // first dim of this wave's half of dQ
+
+  f32x16 acc[NDH];
+#pragma unroll
+  for (int db = 0; db < NDH; ++db) acc[db] = zero16();
+
+  const int ctx_lo = (wl >= 0) ? max(0, qmin - wl) : 0;
+  const int ctx_t0 = (ctx_lo / BN) * BN;
+  const int n_ctx = (P > ctx_lo) ? (P - ctx_t0 + BN - 1) / BN : 0;
+  const int own_lo = (wl >= 0) ? max(0, t0 - wl) : 0;
+  const int own_t0 = (own_lo / BN) * BN;
+  const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
+  const int n_tiles = n_ctx + n_own;
+
+  const h16 *kc_base = reinterpret_cast<const h16 *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
+  const h16 *vc_base = reinterpret_cast<const h16 *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
+  const h16 *ko_base = reinterpret_cast<const h16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
+  const h16 *vo_base = reinterpret_cast<const h16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
+  const int kld_b = (int)(kld * 2);
+  // Role 0 waves fetch the K tile, role 1 waves the V tile.
+  const h16 *c_base = role ? vc_base : kc_base;
+  const h16 *o_base = role ? vo_base : ko_base;
+  DmaRows<HDP, BN, HD> dma;
+  dma.init(pair, lane, kld_b);
+  auto issue = [&](int i) {   // tile i -> stage i % 3
+    char *st = smem + (i % NST) * 2 * TILE + role * TILE;
+    if (i < n_ctx) {
+      int s = ctx_t0 + i * BN;
+      dma.load(st, c_base + (long)s * kld, kld_b, P - s, pair);
+    } else {
+      int s = own_t0 + (i - n_ctx) * BN;
+      dma.load(st, o_base + (long)s * kld, kld_b, seqlen - s, pair);
+    }
+  };
+  SwWide<HDP> sw;
+  sw.init(lane);
+  // Every load above has landed before the first DMA (see the head-dim-split kernel).
+  dma_wait();
+  if (n_tiles > 0) issue(0);
+  if (n_tiles > 1) issue(1);
+  // Tile 0 has landed (tile 1's loads, issued after it, may still be in flight).
+  if (n_tiles > 1)
+    dma_wait_keep<DmaRows<HDP, BN, HD>::kPerWave>();
+  else
+    dma_wait();
+  __syncthreads();
+
+  for (int i = 0; i < n_tiles; ++i) {
+    int nrows, kpos0;
+    if (i < n_ctx) {
+      int s = ctx_t0 + i * BN;
+      nrows = P - s;
+      kpos0 = s;
+    } else {
+      int s = own_t0 + (i - n_ctx) * BN;
+      nrows = seqlen - s;
+      kpos0 = P + s;
+    }
+    const char *ks = smem + (i % NST) * 2 * TILE;
+    float *tb = tbuf + (i & 1) * 8 * 1024;
+    {   // Sᵀ (role 0) or dPᵀ (role 1) over the whole head dim, into this wave's slot
+      sw.opaque();
+      const char *op = ks + role * TILE;
+      f32x16 part = zero16();
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+        part = mma16<E>(sw.frag(lds_u32(op), kc), xf[kc], part);
+      reads_ahead<NKC, 1, PA>();   // one fragment read per product, PA products ahead
+      xch_put(tb + wave * 1024, part, lane);
+    }
+    // This wave's loads of tile i + 1 have landed (nothing newer is in flight); after the
+    // barrier the next stage and both tiles of every pair are visible, and every wave is
+    // done with tile i - 1's stage.
+    dma_wait();
+    __syncthreads();
+    if (i + 2 < n_tiles) issue(i + 2);
+    const bool need_mask = (nrows < BN) || (kpos0 + BN - 1 > qmin) ||
+                           (wl >= 0 && kpos0 < qmax - wl);
+    // dSᵀ = P (dPᵀ - D) of the whole tile (both waves of the pair form the same values);
+    // the visibility test (keys of this lane's row as tile offsets [lo, hi)) is
+    // compiled only into the variant for tiles that need it.
+    const float *st = tb + pair * 1024, *dp = tb + (pair + 4) * 1024;
+    h16x8 d0, d1;
+    auto grads = [&](auto masked_c) {
+      constexpr bool MASKED = decltype(masked_c)::value;
+      const int lo = (wl >= 0 ? qpos - wl - kpos0 : -BN) - 4 * half;
+      const int hi = min(nrows, qpos - kpos0 + 1) - 4 * half;
+      float dsv[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 s4 = xch_quad(st, q, lane), p4 = xch_quad(dp, q, lane);
+        const float sv[4] = {s4.x, s4.y, s4.z, s4.w}, pv[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float p = fast_exp2(fmaf(sv[e], sf, -lse2));
+          if (MASKED) {
+            const int r = 8 * q + e;   // c_row(4 q + e, half) - 4 half
+            p = ((r >= lo) & (r < hi)) ? p : 0.f;
+          }
+          dsv[4 * q + e] = p * (pv[e] - Dq);
+        }
+      }
+      d0 = pack8<E>(dsv);
+      d1 = pack8<E>(dsv + 8);
+    };
+    if (need_mask)
+      grads(std::true_type{});
+    else
+      grads(std::false_type{});
+    // dQᵀ += Kᵀ dSᵀ over this wave's half of the head dim (column blocks counted from
+    // the tile's start; blocks past a 192-wide head dim are skipped).
+#pragma unroll
+    for (int db = 0; db < NDH; ++db) {
+      if (HD != HDP && dq0 + db * 32 >= HD) continue;
+      acc[db] = mma16<E>(sw.trfrag(lds_u32(ks), 0, dq0 / 32 + db), d0, acc[db]);
+      acc[db] = mma16<E>(sw.trfrag(lds_u32(ks), 16, dq0 / 32 + db), d1, acc[db]);
+    }
+    reads_ahead<2 * NDH, 2, PA>();   // a transposed fragment (two reads) per product, PA ahead
+  }
+
+  if (row_valid) {
+    h16 *optr = reinterpret_cast<h16 *>(a.dq) + qrow * qld + (long)h * HD + dq0;
+#pragma unroll
+    for (int db = 0; db < NDH; ++db) {
+      if (HD != HDP && dq0 + db * 32 >= HD) continue;   // past a 192-wide head dim
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int dim = db * 32 + 8 * i + 4 * half;
+        h16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = rnd<E>(acc[db][4 * i + e] * a.scale);
+        *reinterpret_cast<h16x4 *>(optr + dim) = w;
+      }
+    }
+  }
+}
+
 template <typename E, int HD, int HDP>
 static hipError_t dq_wide(const BwdQArgs &a, int n, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_dq_wide_kernel<E, HD, HDP>), dim3(n), dim3(512), 0, s, a);
+  if constexpr (HDP == 256)
+    hipLaunchKernelGGL((bwd_dq_pair_kernel<E, HD>), dim3(n), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_dq_wide_kernel<E, HD, HDP>), dim3(n), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
