@@ -2,36 +2,39 @@
 // dimensions and sliding-window support": the d = 512 global layers and d = 256
 // sliding-window layers of hybrid models; 192 completes the head dims of App. E.1).
 //
-// A wave's fragments and fp32 accumulators for 32 rows over a wide head dim would need
-// up to 768 registers, so the kernels split the head dim across the waves of a
-// workgroup and keep every wave within the architectural VGPRs.  Tiles are staged in
-// rows of HDP elements (256 or 512, a power of two); head dim 192 is staged in 256-wide
-// rows whose last 64 elements read as zeros (its fragments past the head dim are zero
-// and its outputs there are never stored), so it runs the d = 256 kernels' products.
-// With HDP the staged width:
+// A wave's fragments and fp32 accumulators for 32 rows over a wide head dim need up to
+// 768 registers, so the kernels share each 32-row (or 32-key) block between waves and
+// keep every wave within the architectural VGPRs, two waves per SIMD.  Tiles are staged
+// in rows of HDP elements (256 or 512, a power of two); head dim 192 is staged in
+// 256-wide rows whose last 64 elements read as zeros (its fragments past the head dim
+// are zero, its products there are skipped where whole blocks are padding, and its
+// outputs there are never stored), so it runs the d = 256 kernels.  Tiles are staged by
+// LDS DMA into swizzled dense rows (one 1 KB DMA block holds one 512-wide row or two
+// 256-wide rows).
 //
-//   forward  128 query rows per workgroup of 8 waves (two per SIMD); the two waves of
+//   forward  (both widths) 128 query rows per workgroup of 8 waves; the two waves of
 //            a pair share 32 rows and each holds Q and O for one half of the head dim.
 //            Each computes the partial scores Sᵀ over its half, the pair adds the two
 //            partials through LDS (both in the same order, so both see identical
 //            scores), and each accumulates its half of O.  Waves 0-3 run half a tile
-//            ahead of waves 4-7, which share their SIMDs.
-//   dQ       64 query rows per workgroup of 8 waves, two groups of four with 32 rows
-//            each.  In a group, waves 0 / 1 form partial Sᵀ = K Qᵀ over the two
+//            ahead of waves 4-7, which share their SIMDs.  Double-buffered K / V.
+//   dQ, HDP = 512: 64 query rows per workgroup of 8 waves, two groups of four with 32
+//            rows each.  In a group, waves 0 / 1 form partial Sᵀ = K Qᵀ over the two
 //            halves of the head dim (holding Q), waves 2 / 3 partial dPᵀ = V dOᵀ
 //            (holding dO).  After one exchange each wave forms dSᵀ for a quarter of the
 //            tile, and after a second every wave reads the whole dSᵀ and accumulates dQ
 //            for one quarter of the head dim.
-//   dK/dV    64 keys per workgroup of 8 waves, two groups of four with 32 keys each,
-//            the same arrangement: in a group, waves 0 / 1 hold K halves and form
-//            partial S, waves 2 / 3 hold V halves and form partial dP; P and dS are
-//            formed a quarter of the tile per wave and shared, and each wave
-//            accumulates dK and dV for one quarter of the head dim.
-// Every kernel runs two waves per SIMD, and the two groups (pairs) of a workgroup
-// share each staged tile.  Tiles are staged by LDS DMA into swizzled dense rows (one
-// 1 KB DMA block holds one 512-wide row or two 256-wide rows), double-buffered;
-// partial tiles are exchanged through a 32 KB LDS area (the whole 160 KB of LDS at
-// HDP = 512, 96 KB at 256).
+//   dK/dV, HDP = 512: 64 keys per workgroup, the same arrangement: in a group, waves
+//            0 / 1 hold K halves and form partial S, waves 2 / 3 hold V halves and form
+//            partial dP; P and dS are formed a quarter of the tile per wave and shared,
+//            and each wave accumulates dK and dV for one quarter of the head dim.
+//            Both double-buffered, three barriers per tile; the exchange area takes
+//            the last 32 KB of the 160 KB of LDS.
+//   dQ and dK/dV, HDP = 256: pairs of waves, each wave over the whole head dim
+//            (bwd_dq_pair_kernel, bwd_dkdv_pair_kernel): 128 rows or keys per
+//            workgroup; one wave of a pair forms the scores, the other dP, and the
+//            tiles cross through LDS once.  Three stages and a double-buffered exchange
+//            area let one barrier per tile hand over both.
 #include <type_traits>
 
 #include "dkv_device.h"
@@ -753,11 +756,7 @@ hipError_t launch_bwd_dq_wide(int dtype, int hd, const BwdQArgs &a, int n, hipSt
 // --------------------------------------------------------------------- dK/dV --
 
 // MAP: the q-heads of the kv head come from the GQA head table (a.qhead).
-// NST: Q/dO stages in flight (3 where the LDS holds them, at HDP = 256: a step's fetch
-// then has two steps' time to land; the rows' -LSE / scale and -D then travel with the
-// stage, fetched into its LDS, so that every load of the loop is a DMA load whose
-// completion the kernel counts itself).
-template <typename E, int HD, int HDP, bool MAP, int NST>
+template <typename E, int HD, int HDP, bool MAP>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
   constexpr int BM = 32;                 // query rows per step
   constexpr int TILE = BM * HDP * 2;     // 32 KB at HDP = 512
@@ -766,11 +765,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
   constexpr int RPB = 1024 / (HDP * 2);  // staged rows per 1 KB DMA block (1 or 2)
   constexpr int CPR = HDP / 8;           // 16-byte chunks per staged row
   constexpr int NIW = BM / RPB / 4;      // DMA instructions of each wave per step
-  static_assert(NST == 2 || NST == 3, "double or triple buffering");
-  // With NST = 3 a stage also holds 64 words of -LSE / scale and 64 of -D (rows 0..31
-  // of the step, then the zeros of the DMA lanes past them).
-  constexpr int STAGE = 2 * TILE + (NST > 2 ? 512 : 0);
-  __shared__ __attribute__((aligned(16))) char smem[NST * STAGE + 8 * 4096];
+  constexpr int STAGE = 2 * TILE;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE + 8 * 4096];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -779,7 +775,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
   // and role 1 partial dP with V, over head-dim half dh.
   const int grp = wave >> 2, wq = wave & 3;
   const int role = wq >> 1, dh = wq & 1;
-  float *xch = reinterpret_cast<float *>(smem + NST * STAGE) + grp * 4 * 1024;
+  float *xch = reinterpret_cast<float *>(smem + 2 * STAGE) + grp * 4 * 1024;
   const KVItem it = a.items[blockIdx.x];
   const int g = it.g, G = a.G, P = it.ctx_len, wl = a.window_left;
   const bool ctx = it.region == kRegionCtx;
@@ -878,9 +874,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
   // one step ahead, and the wave spreads it over the C layout with ds_bpermute.
   const __amdgpu_buffer_rsrc_t r_ld = make_rsrc_u(role == 0 ? (const void *)a.lsn : (const void *)a.Dneg,
                                                   (uint32_t)((long)a.Hq * a.lse_ld * 4));
-  // With NST = 3: the first group's first wave stages -LSE / scale, the second's -D.
-  const __amdgpu_buffer_rsrc_t r_init = make_rsrc_u(grp == 0 ? (const void *)a.lsn : (const void *)a.Dneg,
-                                                    (uint32_t)((long)a.Hq * a.lse_ld * 4));
   auto issue = [&](char *st) {
     const int s0 = cs0;
     const int len = clen;
@@ -927,18 +920,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
         dma16(rx, l0 + k * 4096, off);
       }
     }
-    if constexpr (NST > 2) {
-      // The rows' -LSE / scale (first wave of the first group) and -D (first wave of
-      // the second) into the stage: lane l < 32 fetches row l's word, the other lanes
-      // nothing (zeros).
-      if (wq == 0) {
-        const int f = cf + lane;
-        const int t = (int)((unsigned)f / (unsigned)G), j = f - t * G;
-        const int hq = MAP ? hm.at(j & 63, G) : g * G + j;   // j < G for every lane
-        const int off = lane < BM ? (hq * a.lse_ld + s0 + t) * 4 : 0x7fffffff;
-        dma4(r_init, __builtin_amdgcn_readfirstlane(lds_u32(st + 2 * TILE) + grp * 256), off);
-      }
-    }
   };
   // Row init values of the step at the cursor (rows past the sequence read 0 and are
   // masked later).
@@ -969,77 +950,38 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
   int stage = 0;
   bool have = !done;
   int f0 = 0, flo = 0, fend = 0;   // the step at hand
-  bool have1 = false;              // NST = 3: the next step, already in flight
-  int h0 = 0, hlo = 0, hend = 0;
   float xinit = 0.f;
   if (have) {
     issue(smem);
-    if constexpr (NST == 2) {
-      if (dh == 0) xinit = fetch_init();
-    }
+    if (dh == 0) xinit = fetch_init();
     advance();
     f0 = nf0, flo = nflo, fend = nfend;
-    if constexpr (NST > 2) {
-      have1 = !done;
-      if (have1) {
-        issue(smem + STAGE);
-        advance();
-        h0 = nf0, hlo = nflo, hend = nfend;
-      }
-    }
   }
 
   const int kpa = kbase + it.key_start + gk0;
   const int kpb = kpa + 31;
   while (have) {
     f32x16 part = zero16();
-    if constexpr (NST == 2) {
-      // The partial's start values (waits for this step's fetches, which the barrier
-      // below needs anyway).
-      if (dh == 0) {
-        const int xi = __builtin_bit_cast(int, xinit);
+    // The partial's start values (waits for this step's fetches, which the barrier
+    // below needs anyway).
+    if (dh == 0) {
+      const int xi = __builtin_bit_cast(int, xinit);
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          part[v] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(c_row(v, half) << 2, xi));
-      }
-      dma_wait();
-    } else {
-      // This step has landed; the next step's loads, issued after it, may still be in
-      // flight (each wave's own count: its row DMAs, plus the init words of a group's
-      // first wave).
-      if (have1) {
-        if (wq == 0)
-          dma_wait_keep<NIW + 1>();
-        else
-          dma_wait_keep<NIW>();
-      } else {
-        dma_wait();
-      }
+      for (int v = 0; v < 16; ++v)
+        part[v] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(c_row(v, half) << 2, xi));
     }
+    dma_wait();
     __syncthreads();
     const bool more = !done;
     int g0 = 0, glo = 0, gend = 0;
     if (more) {   // every wave is done with the stage of the previous step
-      issue(smem + (NST == 2 ? (stage ^ 1) : (stage == 0 ? 2 : stage - 1)) * STAGE);
-      if constexpr (NST == 2) {
-        if (dh == 0) xinit = fetch_init();
-      }
+      issue(smem + (stage ^ 1) * STAGE);
+      if (dh == 0) xinit = fetch_init();
       advance();
       g0 = nf0, glo = nflo, gend = nfend;
     }
     const char *qs = smem + stage * STAGE;
     const char *dos = qs + TILE;
-    if constexpr (NST > 2) {
-      // start values from the stage: rows 8 i + 4 half .. + 3 of the C layout
-      if (dh == 0) {
-        const float *ini = reinterpret_cast<const float *>(qs + 2 * TILE) + (role ? 64 : 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 x = *reinterpret_cast<const float4 *>(ini + 8 * i + 4 * half);
-          part[4 * i] = x.x, part[4 * i + 1] = x.y, part[4 * i + 2] = x.z, part[4 * i + 3] = x.w;
-        }
-      }
-    }
     sw.opaque();
 
     const char *op = role == 0 ? qs : dos;
@@ -1109,17 +1051,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
       dk[db] = mma16<E>(s1, sw.trfrag(lds_u32(qs), 16, cb), dk[db]);
     }
     reads_ahead<4 * NDQ, 2, 2>();   // a transposed fragment (two reads) per product, two ahead
-    if constexpr (NST == 2) {
-      have = more;
-      f0 = g0, flo = glo, fend = gend;
-      stage ^= 1;
-    } else {
-      have = have1;
-      have1 = more;
-      f0 = h0, flo = hlo, fend = hend;
-      h0 = g0, hlo = glo, hend = gend;
-      stage = stage == 2 ? 0 : stage + 1;
-    }
+    have = more;
+    f0 = g0, flo = glo, fend = gend;
+    stage ^= 1;
   }
 
   const bool to_acc = ctx || a.own_to_acc;
@@ -1469,13 +1403,12 @@ static hipError_t dkdv_wide(const BwdKVArgs &a, int n, hipStream_t s) {
       hipLaunchKernelGGL((bwd_dkdv_pair_kernel<E, HD, true>), dim3(n), dim3(512), 0, s, a);
     else
       hipLaunchKernelGGL((bwd_dkdv_pair_kernel<E, HD, false>), dim3(n), dim3(512), 0, s, a);
-    return hipGetLastError();
+  } else {
+    if (a.qhead)
+      hipLaunchKernelGGL((bwd_dkdv_wide_kernel<E, HD, HDP, true>), dim3(n), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_wide_kernel<E, HD, HDP, false>), dim3(n), dim3(512), 0, s, a);
   }
-  constexpr int NST = HDP <= 256 ? 3 : 2;
-  if (a.qhead)
-    hipLaunchKernelGGL((bwd_dkdv_wide_kernel<E, HD, HDP, true, NST>), dim3(n), dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_wide_kernel<E, HD, HDP, false, NST>), dim3(n), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
