@@ -295,9 +295,240 @@ __global__ __launch_bounds__(512, 1) void fwd_wide_kernel(FwdArgs a) {
   }
 }
 
+// Forward at HDP = 256 (head dims 192 and 256): 128 query rows per workgroup of 8
+// waves, four pairs of 32 rows.  In pair p, wave p (role 0) holds Q of the pair's rows
+// over the whole head dim, forms Sᵀ = K Qᵀ, runs the online softmax and accumulates
+// the first half of O; wave p + 4 (role 1, on the same SIMD) accumulates the second
+// half from the P (packed 16-bit, as the product's operand) and the rows' rescale
+// factors that role 0 leaves in LDS.  Three K / V stages and a double-buffered P area
+// let one barrier per tile hand over both (each wave waits for its own loads of tile
+// i + 1 first; the stage of tile i - 1, finished by every wave at the barrier of tile
+// i, takes tile i + 2).  Role 1's products of tile i run beside role 0's scores of
+// tile i + 1.
+template <typename E, int HD>
+__global__ __launch_bounds__(512, 1) void fwd_pair_kernel(FwdArgs a) {
+  constexpr int HDP = 256;
+  constexpr int BN = 32;
+  constexpr int TILE = BN * HDP * 2;     // 16 KB
+  constexpr int NKC = HD / 16;           // k-steps over the real head dim
+  constexpr int NDH = HDP / 2 / 32;      // 32-wide output blocks per half of the head dim
+  constexpr int NST = 3;
+  constexpr int PA = 2;                  // fragment reads ahead of the products
+  constexpr int XS = 64 * 32 + 64 * 4;   // per pair and buffer: P words, then rescale factors
+  constexpr float kSlack = 8.f;
+  static_assert(HD == 192 || HD == 256, "head dims staged in 256-wide rows");
+  __shared__ __attribute__((aligned(16))) char smem[NST * 2 * TILE + 2 * 4 * XS];
+  char *xbase = smem + NST * 2 * TILE;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int role = wave >> 2, pair = wave & 3;
+  const QItem it = a.items[blockIdx.x];
+  const int g = it.g, seq0 = it.seq_start, seqlen = it.seq_len;
+  const int t0 = it.tile * a.bm_tok;
+  const int nt = min(a.bm_tok, seqlen - t0);
+  const int qr = pair * 32 + col;
+  int tok = qr / a.G;
+  const int hj = qr - tok * a.G;
+  const bool row_valid = tok < nt;
+  if (!row_valid) tok = nt - 1;
+  const int h = q_head(a.qhead, g, a.G, hj);
+  const int P = it.ctx_len, wl = a.window_left;
+  const int qpos = P + t0 + tok;
+  const int qmin = P + t0, qmax = P + t0 + nt - 1;
+  const long qld = (long)a.Hq * HD;
+  const long kld = (long)a.Hkv * HD;
+  const int d0 = role * (HDP / 2);   // first dim of this wave's half of O
+
+  h16x8 qf[NKC];
+  if (role == 0) {
+    const h16 *qptr = reinterpret_cast<const h16 *>(a.q) + (long)(seq0 + t0 + tok) * qld + (long)h * HD;
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+      qf[kc] = as_h16x8(*reinterpret_cast<const uint4 *>(qptr + kc * 16 + half * 8));
+  }
+
+  const float sf = a.scale * kLog2e;
+  f32x16 acc[NDH];
+#pragma unroll
+  for (int db = 0; db < NDH; ++db) acc[db] = zero16();
+  float m_run = -INFINITY, l_run = 0.f;   // role 0
+
+  const int ctx_lo = (wl >= 0) ? max(0, qmin - wl) : 0;
+  const int ctx_t0 = (ctx_lo / BN) * BN;
+  const int n_ctx = (P > ctx_lo) ? (P - ctx_t0 + BN - 1) / BN : 0;
+  const int own_lo = (wl >= 0) ? max(0, t0 - wl) : 0;
+  const int own_t0 = (own_lo / BN) * BN;
+  const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
+  const int n_tiles = n_ctx + n_own;
+
+  const h16 *kc_base = reinterpret_cast<const h16 *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
+  const h16 *vc_base = reinterpret_cast<const h16 *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
+  const h16 *ko_base = reinterpret_cast<const h16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
+  const h16 *vo_base = reinterpret_cast<const h16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
+  const int kld_b = (int)(kld * 2);
+  // Role 0 waves fetch the K tile, role 1 waves the V tile.
+  const h16 *c_base = role ? vc_base : kc_base;
+  const h16 *o_base = role ? vo_base : ko_base;
+  DmaRows<HDP, BN, HD> dma;
+  dma.init(pair, lane, kld_b);
+  auto issue = [&](int i) {   // tile i -> stage i % 3
+    char *st = smem + (i % NST) * 2 * TILE + role * TILE;
+    if (i < n_ctx) {
+      int s = ctx_t0 + i * BN;
+      dma.load(st, c_base + (long)s * kld, kld_b, P - s, pair);
+    } else {
+      int s = own_t0 + (i - n_ctx) * BN;
+      dma.load(st, o_base + (long)s * kld, kld_b, seqlen - s, pair);
+    }
+  };
+  SwWide<HDP> sw;
+  sw.init(lane);
+  // Every load above has landed before the first DMA (see the head-dim-split kernel).
+  dma_wait();
+  if (n_tiles > 0) issue(0);
+  if (n_tiles > 1) issue(1);
+  // Tile 0 has landed (tile 1's loads, issued after it, may still be in flight).
+  if (n_tiles > 1)
+    dma_wait_keep<DmaRows<HDP, BN, HD>::kPerWave>();
+  else
+    dma_wait();
+  __syncthreads();
+
+  for (int i = 0; i < n_tiles; ++i) {
+    const char *ks = smem + (i % NST) * 2 * TILE;
+    const char *vs = ks + TILE;
+    char *xp = xbase + ((i & 1) * 4 + pair) * XS;
+    h16x8 p0, p1;   // P of the tile (keys 0..15, 16..31 in the operand's order)
+    float alpha = 1.f;
+    if (role == 0) {
+      int nrows, kpos0;
+      if (i < n_ctx) {
+        int s = ctx_t0 + i * BN;
+        nrows = P - s;
+        kpos0 = s;
+      } else {
+        int s = own_t0 + (i - n_ctx) * BN;
+        nrows = seqlen - s;
+        kpos0 = P + s;
+      }
+      sw.opaque();
+      f32x16 st = zero16();
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+        st = mma16<E>(sw.frag(lds_u32(ks), kc), qf[kc], st);
+      reads_ahead<NKC, 1, PA>();   // one fragment read per product, PA products ahead
+      const bool need_mask = (nrows < BN) || (kpos0 + BN - 1 > qmin) ||
+                             (wl >= 0 && kpos0 < qmax - wl);
+      if (need_mask) {
+        // Visible keys of this lane's row as a range of tile offsets [lo, hi): inside
+        // the tile, causal, and inside the window; compared per element without branches.
+        const int lo = (wl >= 0 ? qpos - wl - kpos0 : -BN) - 4 * half;
+        const int hi = min(nrows, qpos - kpos0 + 1) - 4 * half;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = 8 * (v >> 2) + (v & 3);   // c_row(v, half) - 4 half
+          st[v] = ((r >= lo) & (r < hi)) ? st[v] : -INFINITY;
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, st[v]);
+      mx = pair_max(mx) * sf;
+      const bool grow = mx > m_run + kSlack;
+      if (__any(grow)) {
+        alpha = grow ? fast_exp2(m_run - mx) : 1.f;
+        if (grow) m_run = mx;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDH; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      uint32_t pw[8];   // P as 16-bit pairs
+      float rs = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const float e0 = fast_exp2(fmaf(st[v], sf, -m_use));
+        const float e1 = fast_exp2(fmaf(st[v + 1], sf, -m_use));
+        rs += e0;
+        rs += e1;
+        pw[v / 2] = pack2<E>(e0, e1);
+      }
+      l_run += rs;
+      p0 = words8(pw);
+      p1 = words8(pw + 4);
+      *reinterpret_cast<uint4 *>(xp + lane * 32) = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+      *reinterpret_cast<uint4 *>(xp + lane * 32 + 16) = make_uint4(pw[4], pw[5], pw[6], pw[7]);
+      *reinterpret_cast<float *>(xp + 64 * 32 + lane * 4) = alpha;
+    }
+    // This wave's loads of tile i + 1 have landed (nothing newer is in flight); after the
+    // barrier the next stage and every pair's P are visible, and every wave is done with
+    // tile i - 1's stage.
+    dma_wait();
+    __syncthreads();
+    if (i + 2 < n_tiles) issue(i + 2);
+    if (role == 1) {
+      const uint4 w0 = *reinterpret_cast<const uint4 *>(xp + lane * 32);
+      const uint4 w1 = *reinterpret_cast<const uint4 *>(xp + lane * 32 + 16);
+      p0 = __builtin_bit_cast(h16x8, w0);
+      p1 = __builtin_bit_cast(h16x8, w1);
+      alpha = *reinterpret_cast<const float *>(xp + 64 * 32 + lane * 4);
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < NDH; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
+      }
+    }
+    // Oᵀ += Vᵀ Pᵀ over this wave's half of the head dim (blocks past a 192-wide head dim
+    // are skipped).
+#pragma unroll
+    for (int db = 0; db < NDH; ++db) {
+      if (HD != HDP && d0 + db * 32 >= HD) continue;
+      acc[db] = mma16<E>(sw.trfrag(lds_u32(vs), 0, d0 / 32 + db), p0, acc[db]);
+      acc[db] = mma16<E>(sw.trfrag(lds_u32(vs), 16, d0 / 32 + db), p1, acc[db]);
+    }
+    reads_ahead<2 * NDH, 2, PA>();   // a transposed fragment (two reads) per product, PA ahead
+  }
+
+  // Row sums: role 0 holds them (its two lanes of a row a half each) and passes them on,
+  // through the P buffer of the parity the last tile did not use (its readers were done
+  // before the last barrier).
+  float *lx = reinterpret_cast<float *>(xbase + ((n_tiles & 1) * 4 + pair) * XS);
+  if (role == 0) {
+    const float l = pair_sum(l_run);
+    if (half == 0) lx[col] = l;
+    if (half == 0 && row_valid)
+      a.lse[(long)h * a.lse_ld + seq0 + t0 + tok] = (m_run + fast_log2(l)) * kLn2;
+  }
+  __syncthreads();
+  const float inv = 1.f / lx[col];
+  if (row_valid) {
+    h16 *optr = reinterpret_cast<h16 *>(a.o) + (long)(seq0 + t0 + tok) * qld + (long)h * HD + d0;
+#pragma unroll
+    for (int db = 0; db < NDH; ++db) {
+      if (HD != HDP && d0 + db * 32 >= HD) continue;   // past a 192-wide head dim
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int dim = db * 32 + 8 * i + 4 * half;
+        h16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = rnd<E>(acc[db][4 * i + e] * inv);
+        *reinterpret_cast<h16x4 *>(optr + dim) = w;
+      }
+    }
+  }
+}
+
 template <typename E, int HD, int HDP>
 static hipError_t fwd_wide(const FwdArgs &a, int n, hipStream_t s) {
-  hipLaunchKernelGGL((fwd_wide_kernel<E, HD, HDP>), dim3(n), dim3(512), 0, s, a);
+  if constexpr (HDP == 256)
+    hipLaunchKernelGGL((fwd_pair_kernel<E, HD>), dim3(n), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_wide_kernel<E, HD, HDP>), dim3(n), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -102,6 +102,9 @@ CASES = [
     (200, [180, 90], 4, 2, 64, -1, "fp16"),
     (160, [200, 70], 8, 2, 512, -1, "bf16"),
     (150, [220], 8, 2, 512, 100, "bf16"),
+    (170, [190, 80], 8, 2, 256, -1, "bf16"),    # role 1 of the d = 256 forward rescales
+    (280, [210], 8, 2, 256, 150, "fp16"),       # from the factors role 0 passes on
+    (150, [160, 90], 6, 2, 192, -1, "bf16"),
     (200, [150, 60], 4, 2, 64, -1, "fp32"),
     (130, [140], 4, 1, 128, 90, "fp32"),
 ]
@@ -119,7 +122,7 @@ def _inputs(P, lens, Hq, Hkv, d, wl, dtype):
         x = workloads.add_key_ramp(x, P, lens, d, dtype, 60.0, seed)
     if dtype != "fp32":
         # the 16-bit kernels' lazy rescale is reached in every part of the walk
-        BN = 32 if d == 512 else 64
+        BN = 32 if d >= 192 else 64
         c1, c2p, c2o = rescale_events(x, P, lens, Hq, Hkv, d, wl, BN)
         print("[rescale] events call 1 %d, call 2 prompt %d, own %d" % (c1, c2p, c2o),
               flush=True)
