@@ -80,6 +80,133 @@ template <int N, int R, int A> __device__ __forceinline__ void reads_ahead() {
   }
   __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
 }
+
+// The key tiles of a query work item (rows t0 .. t0 + nt - 1 of its sequence, after a
+// P-token prompt): the prompt tiles its rows can see, then its own tiles, BN keys each
+// at multiples of BN.  `v` picks the V rows (else K); the wave with index w among the
+// four that fetch a tile writes its blocks b % 4 == w (DmaRows).
+template <int HD, int HDP, int BN> struct KVTiles {
+  int ctx_t0, n_ctx, own_t0, n, P, seqlen, w, kld_b;
+  long kld;
+  const h16 *c_base, *o_base;
+  DmaRows<HDP, BN, HD> dma;
+  template <typename Args>
+  __device__ __forceinline__ void init(const Args &a, const QItem &it, int t0, int nt, bool v,
+                                       int w_, int lane) {
+    P = it.ctx_len;
+    seqlen = it.seq_len;
+    w = w_;
+    const int wl = a.window_left;
+    const int ctx_lo = (wl >= 0) ? max(0, P + t0 - wl) : 0;
+    ctx_t0 = (ctx_lo / BN) * BN;
+    n_ctx = (P > ctx_lo) ? (P - ctx_t0 + BN - 1) / BN : 0;
+    const int own_lo = (wl >= 0) ? max(0, t0 - wl) : 0;
+    own_t0 = (own_lo / BN) * BN;
+    n = n_ctx + (t0 + nt - own_t0 + BN - 1) / BN;
+    kld = (long)a.Hkv * HD;
+    kld_b = (int)(kld * 2);
+    c_base = reinterpret_cast<const h16 *>(v ? a.v_ctx : a.k_ctx) + (long)it.ctx_start * kld + (long)it.g * HD;
+    o_base = reinterpret_cast<const h16 *>(v ? a.v_own : a.k_own) + (long)it.seq_start * kld + (long)it.g * HD;
+    dma.init(w, lane, kld_b);
+  }
+  // Tile i: the rows of its region from its first key (nrows; rows past them are zero
+  // filled) and the logical position of its first key.
+  __device__ __forceinline__ void at(int i, int &nrows, int &kpos0) const {
+    if (i < n_ctx) {
+      const int s = ctx_t0 + i * BN;
+      nrows = P - s;
+      kpos0 = s;
+    } else {
+      const int s = own_t0 + (i - n_ctx) * BN;
+      nrows = seqlen - s;
+      kpos0 = P + s;
+    }
+  }
+  // This wave's share of tile i into the LDS tile at st.
+  __device__ __forceinline__ void fetch(char *st, int i) {
+    if (i < n_ctx) {
+      const int s = ctx_t0 + i * BN;
+      dma.load(st, c_base + (long)s * kld, kld_b, P - s, w);
+    } else {
+      const int s = own_t0 + (i - n_ctx) * BN;
+      dma.load(st, o_base + (long)s * kld, kld_b, seqlen - s, w);
+    }
+  }
+};
+
+// The query-row steps of a key work item: BM flattened (token, head) rows at a time,
+// walked from the item's last sequence and its last step backward, so that every key
+// tile of a sequence streams the same rows at the same time (L2 reuse).  A sequence's
+// visible rows are [fa, fb) in flattened units: for prompt keys (ctx) all of its rows,
+// for its own keys the rows from the tile's first key on, either cut at the window's
+// end.  The cursor keeps the sequence start and length of its seek, so a step's fetch
+// issues no scalar load.
+template <int BM> struct RowSteps {
+  const int32_t *cu;
+  int seq_lo, key_start, nk_tile, P, wl, G;
+  bool ctx;
+  int cs, cf, cfa, cfb, cs0, clen;
+  bool done;
+  __device__ __forceinline__ void seq_range(int sq, int &fa, int &fb, int &s0, int &len) const {
+    s0 = sload_i32(cu, sq);
+    len = sload_i32(cu, sq + 1) - s0;
+    int r_lo, r_hi;
+    if (ctx) {
+      r_lo = 0;
+      r_hi = len;
+      if (wl >= 0) r_hi = min(len, key_start + nk_tile - 1 + wl - P + 1);
+    } else {
+      r_lo = key_start;
+      r_hi = len;
+      if (wl >= 0) r_hi = min(len, key_start + nk_tile - 1 + wl + 1);
+    }
+    fa = r_lo * G;
+    fb = r_hi > r_lo ? r_hi * G : fa;
+  }
+  __device__ __forceinline__ void seek() {
+    while (cs >= seq_lo) {
+      int fa, fb, s0, len;
+      seq_range(cs, fa, fb, s0, len);
+      if (fb > fa) {
+        cfa = fa;
+        cfb = fb;
+        cs0 = s0;
+        clen = len;
+        cf = ((fb - 1) / BM) * BM;
+        return;
+      }
+      --cs;
+    }
+    done = true;
+  }
+  __device__ __forceinline__ void init(const int32_t *cu_, const KVItem &it, int nk_tile_, int P_,
+                                       int wl_, int G_, bool ctx_) {
+    cu = cu_;
+    seq_lo = it.seq_lo;
+    key_start = it.key_start;
+    nk_tile = nk_tile_;
+    P = P_;
+    wl = wl_;
+    G = G_;
+    ctx = ctx_;
+    cs = it.seq_hi - 1;
+    cf = cfa = cfb = cs0 = clen = 0;
+    done = false;
+    seek();
+  }
+  // The step at the cursor (first row f0, rows [flo, fend) inside the visible range),
+  // then the cursor moves on.
+  __device__ __forceinline__ void advance(int &f0, int &flo, int &fend) {
+    f0 = cf;
+    flo = max(cf, cfa);
+    fend = min(cf + BM, cfb);
+    cf -= BM;
+    if (cf + BM <= cfa) {
+      --cs;
+      seek();
+    }
+  }
+};
 }  // namespace
 
 // ------------------------------------------------------------------- forward --
@@ -129,36 +256,12 @@ __global__ __launch_bounds__(512, 1) void fwd_wide_kernel(FwdArgs a) {
   for (int db = 0; db < NDH; ++db) acc[db] = zero16();
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int ctx_lo = (wl >= 0) ? max(0, qmin - wl) : 0;
-  const int ctx_t0 = (ctx_lo / BN) * BN;
-  const int n_ctx = (P > ctx_lo) ? (P - ctx_t0 + BN - 1) / BN : 0;
-  const int own_lo = (wl >= 0) ? max(0, t0 - wl) : 0;
-  const int own_t0 = (own_lo / BN) * BN;
-  const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
-  const int n_tiles = n_ctx + n_own;
-
-  const h16 *kc_base = reinterpret_cast<const h16 *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
-  const h16 *vc_base = reinterpret_cast<const h16 *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
-  const h16 *ko_base = reinterpret_cast<const h16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
-  const h16 *vo_base = reinterpret_cast<const h16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
-  const int kld_b = (int)(kld * 2);
-  // Waves 0-3 fetch the K tile, waves 4-7 the V tile.
-  const int dw = wave & 3, isv = wave >> 2;
-  const h16 *c_base = isv ? vc_base : kc_base;
-  const h16 *o_base = isv ? vo_base : ko_base;
-  DmaRows<HDP, BN, HD> dma;
-  dma.init(dw, lane, kld_b);
   // Tile i goes to stage i % 2: waves 0-3 fetch its K rows, waves 4-7 its V rows.
-  auto issue = [&](int i) {
-    char *st = smem + (i & 1) * 2 * TILE + isv * TILE;
-    if (i < n_ctx) {
-      int s = ctx_t0 + i * BN;
-      dma.load(st, c_base + (long)s * kld, kld_b, P - s, dw);
-    } else {
-      int s = own_t0 + (i - n_ctx) * BN;
-      dma.load(st, o_base + (long)s * kld, kld_b, seqlen - s, dw);
-    }
-  };
+  const int dw = wave & 3, isv = wave >> 2;
+  KVTiles<HD, HDP, BN> kv;
+  kv.init(a, it, t0, nt, isv, dw, lane);
+  const int n_tiles = kv.n;
+  auto issue = [&](int i) { kv.fetch(smem + (i & 1) * 2 * TILE + isv * TILE, i); };
   SwWide<HDP> sw;
   sw.init(lane);
 
@@ -176,15 +279,7 @@ __global__ __launch_bounds__(512, 1) void fwd_wide_kernel(FwdArgs a) {
   // Softmax of tile i from the pair's two partials, then Oᵀ += Vᵀ Pᵀ.
   auto accumulate = [&](int i) {
     int nrows, kpos0;
-    if (i < n_ctx) {
-      int s = ctx_t0 + i * BN;
-      nrows = P - s;
-      kpos0 = s;
-    } else {
-      int s = own_t0 + (i - n_ctx) * BN;
-      nrows = seqlen - s;
-      kpos0 = P + s;
-    }
+    kv.at(i, nrows, kpos0);
     const char *vs = smem + (i & 1) * 2 * TILE + TILE;
     // Full scores: the pair's partials 0 + 1, both read back a quad at a time (the
     // same bits in both waves of the pair).
@@ -355,34 +450,11 @@ __global__ __launch_bounds__(512, 1) void fwd_pair_kernel(FwdArgs a) {
   for (int db = 0; db < NDH; ++db) acc[db] = zero16();
   float m_run = -INFINITY, l_run = 0.f;   // role 0
 
-  const int ctx_lo = (wl >= 0) ? max(0, qmin - wl) : 0;
-  const int ctx_t0 = (ctx_lo / BN) * BN;
-  const int n_ctx = (P > ctx_lo) ? (P - ctx_t0 + BN - 1) / BN : 0;
-  const int own_lo = (wl >= 0) ? max(0, t0 - wl) : 0;
-  const int own_t0 = (own_lo / BN) * BN;
-  const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
-  const int n_tiles = n_ctx + n_own;
-
-  const h16 *kc_base = reinterpret_cast<const h16 *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
-  const h16 *vc_base = reinterpret_cast<const h16 *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
-  const h16 *ko_base = reinterpret_cast<const h16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
-  const h16 *vo_base = reinterpret_cast<const h16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
-  const int kld_b = (int)(kld * 2);
-  // Role 0 waves fetch the K tile, role 1 waves the V tile.
-  const h16 *c_base = role ? vc_base : kc_base;
-  const h16 *o_base = role ? vo_base : ko_base;
-  DmaRows<HDP, BN, HD> dma;
-  dma.init(pair, lane, kld_b);
-  auto issue = [&](int i) {   // tile i -> stage i % 3
-    char *st = smem + (i % NST) * 2 * TILE + role * TILE;
-    if (i < n_ctx) {
-      int s = ctx_t0 + i * BN;
-      dma.load(st, c_base + (long)s * kld, kld_b, P - s, pair);
-    } else {
-      int s = own_t0 + (i - n_ctx) * BN;
-      dma.load(st, o_base + (long)s * kld, kld_b, seqlen - s, pair);
-    }
-  };
+  // Role 0 waves fetch the K tile, role 1 waves the V tile; tile i goes to stage i % 3.
+  KVTiles<HD, HDP, BN> kv;
+  kv.init(a, it, t0, nt, role, pair, lane);
+  const int n_tiles = kv.n;
+  auto issue = [&](int i) { kv.fetch(smem + (i % NST) * 2 * TILE + role * TILE, i); };
   SwWide<HDP> sw;
   sw.init(lane);
   // Every load above has landed before the first DMA (see the head-dim-split kernel).
@@ -404,15 +476,7 @@ __global__ __launch_bounds__(512, 1) void fwd_pair_kernel(FwdArgs a) {
     float alpha = 1.f;
     if (role == 0) {
       int nrows, kpos0;
-      if (i < n_ctx) {
-        int s = ctx_t0 + i * BN;
-        nrows = P - s;
-        kpos0 = s;
-      } else {
-        int s = own_t0 + (i - n_ctx) * BN;
-        nrows = seqlen - s;
-        kpos0 = P + s;
-      }
+      kv.at(i, nrows, kpos0);
       sw.opaque();
       f32x16 st = zero16();
 #pragma unroll
@@ -621,34 +685,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_wide_kernel(BwdQArgs a) {
 #pragma unroll
   for (int db = 0; db < NDQ; ++db) acc[db] = zero16();
 
-  const int ctx_lo = (wl >= 0) ? max(0, qmin - wl) : 0;
-  const int ctx_t0 = (ctx_lo / BN) * BN;
-  const int n_ctx = (P > ctx_lo) ? (P - ctx_t0 + BN - 1) / BN : 0;
-  const int own_lo = (wl >= 0) ? max(0, t0 - wl) : 0;
-  const int own_t0 = (own_lo / BN) * BN;
-  const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
-  const int n_tiles = n_ctx + n_own;
-
-  const h16 *kc_base = reinterpret_cast<const h16 *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
-  const h16 *vc_base = reinterpret_cast<const h16 *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
-  const h16 *ko_base = reinterpret_cast<const h16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
-  const h16 *vo_base = reinterpret_cast<const h16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
-  const int kld_b = (int)(kld * 2);
-  // Waves 0-3 fetch the K tile, waves 4-7 the V tile.
-  const h16 *c_base = grp ? vc_base : kc_base;
-  const h16 *o_base = grp ? vo_base : ko_base;
-  DmaRows<HDP, BN, HD> dma;
-  dma.init(wq, lane, kld_b);
-  auto issue = [&](int i) {
-    char *st = smem + (i & 1) * 2 * TILE + grp * TILE;
-    if (i < n_ctx) {
-      int s = ctx_t0 + i * BN;
-      dma.load(st, c_base + (long)s * kld, kld_b, P - s, wq);
-    } else {
-      int s = own_t0 + (i - n_ctx) * BN;
-      dma.load(st, o_base + (long)s * kld, kld_b, seqlen - s, wq);
-    }
-  };
+  // Waves 0-3 fetch the K tile, waves 4-7 the V tile; tile i goes to stage i % 2.
+  KVTiles<HD, HDP, BN> kv;
+  kv.init(a, it, t0, nt, grp, wq, lane);
+  const int n_tiles = kv.n;
+  auto issue = [&](int i) { kv.fetch(smem + (i & 1) * 2 * TILE + grp * TILE, i); };
   SwWide<HDP> sw;
   sw.init(lane);
   // Every load above has landed before the first DMA: the loop's waits count DMAs only,
@@ -659,15 +700,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_wide_kernel(BwdQArgs a) {
 
   for (int i = 0; i < n_tiles; ++i) {
     int nrows, kpos0;
-    if (i < n_ctx) {
-      int s = ctx_t0 + i * BN;
-      nrows = P - s;
-      kpos0 = s;
-    } else {
-      int s = own_t0 + (i - n_ctx) * BN;
-      nrows = seqlen - s;
-      kpos0 = P + s;
-    }
+    kv.at(i, nrows, kpos0);
     dma_wait();
     __syncthreads();
     if (i + 1 < n_tiles) issue(i + 1);
@@ -833,34 +866,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_pair_kernel(BwdQArgs a) {
 #pragma unroll
   for (int db = 0; db < NDH; ++db) acc[db] = zero16();
 
-  const int ctx_lo = (wl >= 0) ? max(0, qmin - wl) : 0;
-  const int ctx_t0 = (ctx_lo / BN) * BN;
-  const int n_ctx = (P > ctx_lo) ? (P - ctx_t0 + BN - 1) / BN : 0;
-  const int own_lo = (wl >= 0) ? max(0, t0 - wl) : 0;
-  const int own_t0 = (own_lo / BN) * BN;
-  const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
-  const int n_tiles = n_ctx + n_own;
-
-  const h16 *kc_base = reinterpret_cast<const h16 *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
-  const h16 *vc_base = reinterpret_cast<const h16 *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
-  const h16 *ko_base = reinterpret_cast<const h16 *>(a.k_own) + (long)seq0 * kld + (long)g * HD;
-  const h16 *vo_base = reinterpret_cast<const h16 *>(a.v_own) + (long)seq0 * kld + (long)g * HD;
-  const int kld_b = (int)(kld * 2);
-  // Role 0 waves fetch the K tile, role 1 waves the V tile.
-  const h16 *c_base = role ? vc_base : kc_base;
-  const h16 *o_base = role ? vo_base : ko_base;
-  DmaRows<HDP, BN, HD> dma;
-  dma.init(pair, lane, kld_b);
-  auto issue = [&](int i) {   // tile i -> stage i % 3
-    char *st = smem + (i % NST) * 2 * TILE + role * TILE;
-    if (i < n_ctx) {
-      int s = ctx_t0 + i * BN;
-      dma.load(st, c_base + (long)s * kld, kld_b, P - s, pair);
-    } else {
-      int s = own_t0 + (i - n_ctx) * BN;
-      dma.load(st, o_base + (long)s * kld, kld_b, seqlen - s, pair);
-    }
-  };
+  // Role 0 waves fetch the K tile, role 1 waves the V tile; tile i goes to stage i % 3.
+  KVTiles<HD, HDP, BN> kv;
+  kv.init(a, it, t0, nt, role, pair, lane);
+  const int n_tiles = kv.n;
+  auto issue = [&](int i) { kv.fetch(smem + (i % NST) * 2 * TILE + role * TILE, i); };
   SwWide<HDP> sw;
   sw.init(lane);
   // Every load above has landed before the first DMA (see the head-dim-split kernel).
@@ -876,15 +886,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_pair_kernel(BwdQArgs a) {
 
   for (int i = 0; i < n_tiles; ++i) {
     int nrows, kpos0;
-    if (i < n_ctx) {
-      int s = ctx_t0 + i * BN;
-      nrows = P - s;
-      kpos0 = s;
-    } else {
-      int s = own_t0 + (i - n_ctx) * BN;
-      nrows = seqlen - s;
-      kpos0 = P + s;
-    }
+    kv.at(i, nrows, kpos0);
     const char *ks = smem + (i % NST) * 2 * TILE;
     float *tb = tbuf + (i & 1) * 8 * 1024;
     {   // Sᵀ (role 0) or dPᵀ (role 1) over the whole head dim, into this wave's slot
@@ -1049,44 +1051,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
     dv[db] = zero16();
   }
 
-  auto seq_range = [&](int sq, int &fa, int &fb, int &s0, int &len) {
-    s0 = sload_i32(a.cu, sq);
-    len = sload_i32(a.cu, sq + 1) - s0;
-    int r_lo, r_hi;
-    if (ctx) {
-      r_lo = 0;
-      r_hi = len;
-      if (wl >= 0) r_hi = min(len, it.key_start + nk_tile - 1 + wl - P + 1);
-    } else {
-      r_lo = it.key_start;
-      r_hi = len;
-      if (wl >= 0) r_hi = min(len, it.key_start + nk_tile - 1 + wl + 1);
-    }
-    fa = r_lo * G;
-    fb = r_hi > r_lo ? r_hi * G : fa;
-  };
   // Steps of BM flattened rows, walked from the last one backward.
-  // The cursor's sequence start and length are kept from the seek, so a step's
-  // fetch issues no scalar load.
-  int cs = it.seq_hi - 1, cf = 0, cfa = 0, cfb = 0, cs0 = 0, clen = 0;
-  bool done = false;
-  auto seek = [&]() {
-    while (cs >= it.seq_lo) {
-      int fa, fb, s0, len;
-      seq_range(cs, fa, fb, s0, len);
-      if (fb > fa) {
-        cfa = fa;
-        cfb = fb;
-        cs0 = s0;
-        clen = len;
-        cf = ((fb - 1) / BM) * BM;
-        return;
-      }
-      --cs;
-    }
-    done = true;
-  };
-  seek();
+  RowSteps<BM> rs;
+  rs.init(a.cu, it, nk_tile, P, wl, G, ctx);
 
   const int qld_b = (int)(qld * 2);
   const int head0_b = g * G * HD * 2;
@@ -1106,15 +1073,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
   const __amdgpu_buffer_rsrc_t r_ld = make_rsrc_u(role == 0 ? (const void *)a.lsn : (const void *)a.Dneg,
                                                   (uint32_t)((long)a.Hq * a.lse_ld * 4));
   auto issue = [&](char *st) {
-    const int s0 = cs0;
-    const int len = clen;
+    const int s0 = rs.cs0;
+    const int len = rs.clen;
     const __amdgpu_buffer_rsrc_t rx =
         make_rsrc_u(xsrc + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
     const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_u32(st + grp * TILE) + wq * 1024);
     if constexpr (RPB == 1) {
       // One row per block, wave-uniform: (token, head) of the wave's first row, then
       // stepped 4 rows at a time without a division.
-      const int f = cf + wq;
+      const int f = rs.cf + wq;
       int t = (int)((unsigned)f / (unsigned)G);
       int j = f - t * G;
       int roff = t * qld_b + head0_b + j * (HD * 2);
@@ -1135,7 +1102,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
     } else {
       // RPB rows per block: lane l fills chunk slot l % CPR of row RPB b + l / CPR, with
       // the source chunk that the swizzle puts there (zeros past the head dim).
-      const int ft = cf / G, fj = cf - ft * G;
+      const int ft = rs.cf / G, fj = rs.cf - ft * G;
 #pragma unroll
       for (int k = 0; k < NIW; ++k) {
         const int r = RPB * (k * 4 + wq) + lane / CPR;
@@ -1155,38 +1122,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
   // Row init values of the step at the cursor (rows past the sequence read 0 and are
   // masked later).
   auto fetch_init = [&]() -> float {
-    const int s0 = cs0;
-    const int f = cf + col;
+    const int s0 = rs.cs0;
+    const int f = rs.cf + col;
     const int t = (int)((unsigned)f / (unsigned)G), j = f - t * G;
     const int hq = MAP ? hm.at(j, G) : g * G + j;
     const int off = (hq * a.lse_ld + s0 + t) * 4;
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_ld, off, 0, 0));
   };
 
-  int nf0 = 0, nflo = 0, nfend = 0;
-  auto advance = [&]() {
-    nf0 = cf;
-    nflo = max(cf, cfa);
-    nfend = min(cf + BM, cfb);
-    cf -= BM;
-    if (cf + BM <= cfa) {
-      --cs;
-      seek();
-    }
-  };
   SwWide<HDP> sw;
   sw.init(lane);
   // Every load above has landed before the first DMA (see the dQ kernel).
   dma_wait();
   int stage = 0;
-  bool have = !done;
+  bool have = !rs.done;
   int f0 = 0, flo = 0, fend = 0;   // the step at hand
   float xinit = 0.f;
   if (have) {
     issue(smem);
     if (dh == 0) xinit = fetch_init();
-    advance();
-    f0 = nf0, flo = nflo, fend = nfend;
+    rs.advance(f0, flo, fend);
   }
 
   const int kpa = kbase + it.key_start + gk0;
@@ -1203,13 +1158,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
     }
     dma_wait();
     __syncthreads();
-    const bool more = !done;
+    const bool more = !rs.done;
     int g0 = 0, glo = 0, gend = 0;
     if (more) {   // every wave is done with the stage of the previous step
       issue(smem + (stage ^ 1) * STAGE);
       if (dh == 0) xinit = fetch_init();
-      advance();
-      g0 = nf0, glo = nflo, gend = nfend;
+      rs.advance(g0, glo, gend);
     }
     const char *qs = smem + stage * STAGE;
     const char *dos = qs + TILE;
@@ -1379,43 +1333,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdKVArgs a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = zero16();
 
-  auto seq_range = [&](int sq, int &fa, int &fb, int &s0, int &len) {
-    s0 = sload_i32(a.cu, sq);
-    len = sload_i32(a.cu, sq + 1) - s0;
-    int r_lo, r_hi;
-    if (ctx) {
-      r_lo = 0;
-      r_hi = len;
-      if (wl >= 0) r_hi = min(len, it.key_start + nk_tile - 1 + wl - P + 1);
-    } else {
-      r_lo = it.key_start;
-      r_hi = len;
-      if (wl >= 0) r_hi = min(len, it.key_start + nk_tile - 1 + wl + 1);
-    }
-    fa = r_lo * G;
-    fb = r_hi > r_lo ? r_hi * G : fa;
-  };
-  // Steps of BM flattened rows, walked from the last one backward; the cursor keeps the
-  // sequence start and length of its seek.
-  int cs = it.seq_hi - 1, cf = 0, cfa = 0, cfb = 0, cs0 = 0, clen = 0;
-  bool done = false;
-  auto seek = [&]() {
-    while (cs >= it.seq_lo) {
-      int fa, fb, s0, len;
-      seq_range(cs, fa, fb, s0, len);
-      if (fb > fa) {
-        cfa = fa;
-        cfb = fb;
-        cs0 = s0;
-        clen = len;
-        cf = ((fb - 1) / BM) * BM;
-        return;
-      }
-      --cs;
-    }
-    done = true;
-  };
-  seek();
+  // Steps of BM flattened rows, walked from the last one backward.
+  RowSteps<BM> rs;
+  rs.init(a.cu, it, nk_tile, P, wl, G, ctx);
 
   const int qld_b = (int)(qld * 2);
   const int head0_b = g * G * HD * 2;
@@ -1430,12 +1350,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdKVArgs a) {
   const __amdgpu_buffer_rsrc_t r_init = make_rsrc_u(role == 0 ? (const void *)a.lsn : (const void *)a.Dneg,
                                                     (uint32_t)((long)a.Hq * a.lse_ld * 4));
   auto issue = [&](char *st) {
-    const int s0 = cs0;
-    const int len = clen;
+    const int s0 = rs.cs0;
+    const int len = rs.clen;
     const __amdgpu_buffer_rsrc_t rx =
         make_rsrc_u(xsrc + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
     const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_u32(st + role * TILE) + pair * 1024);
-    const int ft = cf / G, fj = cf - ft * G;
+    const int ft = rs.cf / G, fj = rs.cf - ft * G;
 #pragma unroll
     for (int k = 0; k < NIW; ++k) {
       const int r = RPB * (k * 4 + pair) + lane / CPR;
@@ -1451,7 +1371,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdKVArgs a) {
       dma16(rx, l0 + k * 4096, off);
     }
     if (pair == 0) {   // lane l < 32 fetches row l's word, the other lanes zeros
-      const int f = cf + lane;
+      const int f = rs.cf + lane;
       const int t = (int)((unsigned)f / (unsigned)G), j = f - t * G;
       const int hq = MAP ? hm.at(j & 63, G) : g * G + j;   // j < G for every lane
       const int off = lane < BM ? (hq * a.lse_ld + s0 + t) * 4 : 0x7fffffff;
@@ -1459,35 +1379,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdKVArgs a) {
     }
   };
 
-  int nf0 = 0, nflo = 0, nfend = 0;
-  auto advance = [&]() {
-    nf0 = cf;
-    nflo = max(cf, cfa);
-    nfend = min(cf + BM, cfb);
-    cf -= BM;
-    if (cf + BM <= cfa) {
-      --cs;
-      seek();
-    }
-  };
   SwWide<HDP> sw;
   sw.init(lane);
   // Every load above has landed before the first DMA (see the dQ kernel).
   dma_wait();
   int stage = 0, pb = 0;
-  bool have = !done;
+  bool have = !rs.done;
   int f0 = 0, flo = 0, fend = 0;   // the step at hand
   bool have1 = false;              // the next step, already in flight
   int h0 = 0, hlo = 0, hend = 0;
   if (have) {
     issue(smem);
-    advance();
-    f0 = nf0, flo = nflo, fend = nfend;
-    have1 = !done;
+    rs.advance(f0, flo, fend);
+    have1 = !rs.done;
     if (have1) {
       issue(smem + STAGE);
-      advance();
-      h0 = nf0, hlo = nflo, hend = nfend;
+      rs.advance(h0, hlo, hend);
     }
   }
   // Step 0 has landed (step 1's loads, issued after it, may still be in flight).
@@ -1565,12 +1472,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdKVArgs a) {
     // wave is done with the previous step's stage.
     dma_wait();
     __syncthreads();
-    const bool more = !done;
+    const bool more = !rs.done;
     int g0 = 0, glo = 0, gend = 0;
     if (more) {
       issue(smem + (stage == 0 ? 2 : stage - 1) * STAGE);
-      advance();
-      g0 = nf0, glo = nflo, gend = nfend;
+      rs.advance(g0, glo, gend);
     }
     if (role == 1) {
       // dP - D after the barrier (so it is not held across it), then dS = P (dP - D)
