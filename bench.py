@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (torch), the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture the step (both calls, forward and backward) into a "
+                         "HIP graph once and time the same number of replays")
     ap.add_argument("--gemm-calibration", action="store_true",
                     help="also time a plain bf16 8192^3 matrix product (torch / hipBLASLt) "
                          "and report its TFLOP/s beside the published peak")
@@ -343,6 +346,21 @@ def main():
     _lib.lib().dkv_timing_reset()
     log(args, "dualkv ms/step %.3f" % ms, ktimes)
 
+    # The same step replayed from a HIP graph (no host work per step: the calls' work
+    # lists and launches are captured once).
+    graph_ms = None
+    if args.graph:
+        gs = torch.cuda.Stream()
+        gs.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gs):
+            dk_step()
+        torch.cuda.synchronize()
+        graph.replay()
+        graph_ms = timed(graph.replay, args.steps)
+        log(args, "graph replay ms/step %.3f" % graph_ms)
+        del graph
+
     # Per-call breakdown, from a separate pass with events between the four calls (the
     # timed region above has none): the time of Call 1 and Call 2 against their own
     # visible pairs.
@@ -533,6 +551,9 @@ def main():
     }
     if gemm is not None:
         out["gemm_calibration_tflops"] = gemm
+    if graph_ms is not None:
+        out["graph"] = {"ms_per_step": round(graph_ms, 4),
+                        "tflops": round(flops / (graph_ms * 1e-3) / 1e12, 3)}
     print(json.dumps(out), flush=True)
 
 

@@ -39,9 +39,16 @@
  *     thread).  Validation happens before any device work is enqueued, so an
  *     invalid call enqueues nothing.
  *   - Concurrent calls on different streams must not share a workspace.
- *   - Calls on a stream that is capturing a HIP graph return DKV_ERR_UNSUPPORTED
- *     (work lists are staged through reused pinned host buffers, which a graph would
- *     read again at every replay).
+ *   - Calls may be captured into a HIP graph (hipStreamBeginCapture on `stream`, any
+ *     capture mode).  The work-list copy and the kernels become nodes of the graph, and
+ *     every replay computes the call again on the buffers and shapes it was captured
+ *     with: the buffers' contents may change between replays, the shapes (and the host
+ *     cu_seqlens) may not.  The pinned buffer that a captured call copies its lists
+ *     from is reserved for that graph until the process ends (32 bytes per work item
+ *     plus the sequence and head tables: under 1 MB for the Qwen3-8B-shaped
+ *     micro-batch).  The workspace of a captured call belongs to the graph: calls that
+ *     may run at the same time as a replay need another.  Per-kernel timing records
+ *     nothing under capture.  dkv_bwd_noalloc refuses a capturing stream.
  */
 #ifndef DKV_H
 #define DKV_H
@@ -224,7 +231,8 @@ dkv_status dkv_bwd(const dkv_params *p, const void *q_resp, const void *k_p,
  * and enqueues nothing (the Qwen3-8B-shaped micro-batch, 131 072 response rows x 32
  * q-heads, needs about 36 MiB).  Every call on one GPU shares that GPU's array: calls
  * that overlap on one GPU (other streams, other host threads) race, so run them one
- * after another.
+ * after another.  A pageable copy cannot be captured into a graph: on a capturing
+ * stream the call returns DKV_ERR_UNSUPPORTED and enqueues nothing.
  */
 dkv_status dkv_bwd_noalloc(const dkv_params *p, const void *q_resp, const void *k_p,
                            const void *v_p, const void *k_r, const void *v_r, const void *o_r,

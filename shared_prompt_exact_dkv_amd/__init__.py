@@ -350,9 +350,11 @@ def dkv_layout(op: int, x, cu_host, ctx_len: int, *, ctx_cu_host=None, group_seq
     return out
 
 
-def _prompt_cu(P, ctx_cu_host, device):
-    cu_p_host = [0, P] if ctx_cu_host is None else [int(c) for c in ctx_cu_host]
-    return torch.tensor(cu_p_host, dtype=torch.int32, device=device), cu_p_host
+def _prompt_cu(P, ctx_cu_host):
+    """Sequence bounds of Call 1 over the prompt(s), as a host list only: the library
+    schedules from the host copy, so no device tensor (and no copy to the device, which
+    a stream capturing a graph would refuse) is made."""
+    return [0, P] if ctx_cu_host is None else [int(c) for c in ctx_cu_host]
 
 
 def dualkv_forward(q_p, k_p, v_p, q_r, k_r, v_r, cu_seqlens, *, cu_host=None, window_left=-1,
@@ -361,8 +363,8 @@ def dualkv_forward(q_p, k_p, v_p, q_r, k_r, v_r, cu_seqlens, *, cu_host=None, wi
     """The two calls of the forward: Call 1 over the prompt(s), Call 2 over the
     responses.  With prompt groups (see dkv_fwd), Call 1 is varlen causal attention
     over the prompts.  -> (o_p, lse_p, o_r, lse_r)."""
-    cu_p, cu_p_host = _prompt_cu(q_p.shape[0], ctx_cu_host, q_p.device)
-    o_p, lse_p = dkv_ctx_fwd(q_p, k_p, v_p, cu_p, cu_host=cu_p_host, window_left=window_left,
+    cu_p_host = _prompt_cu(q_p.shape[0], ctx_cu_host)
+    o_p, lse_p = dkv_ctx_fwd(q_p, k_p, v_p, None, cu_host=cu_p_host, window_left=window_left,
                              softmax_scale=softmax_scale, kv_head_of_q=kv_head_of_q)
     o_r, lse_r = dkv_fwd(q_r, k_p, v_p, k_r, v_r, cu_seqlens, cu_host=cu_host,
                          window_left=window_left, softmax_scale=softmax_scale,
@@ -382,8 +384,8 @@ def dualkv_backward(q_p, k_p, v_p, q_r, k_r, v_r, o_p, lse_p, o_r, lse_r, do_p, 
     dv_r."""
     if acc is None:
         acc = torch.empty((2,) + tuple(k_p.shape), dtype=torch.float32, device=k_p.device)
-    cu_p, cu_p_host = _prompt_cu(q_p.shape[0], ctx_cu_host, q_p.device)
-    dq_p, _, _ = dkv_ctx_bwd(q_p, k_p, v_p, o_p, lse_p, do_p, cu_p, cu_host=cu_p_host,
+    cu_p_host = _prompt_cu(q_p.shape[0], ctx_cu_host)
+    dq_p, _, _ = dkv_ctx_bwd(q_p, k_p, v_p, o_p, lse_p, do_p, None, cu_host=cu_p_host,
                              window_left=window_left, softmax_scale=softmax_scale,
                              acc_dk=acc[0], acc_dv=acc[1], acc_flags=DKV_ACC_ZERO,
                              kv_head_of_q=kv_head_of_q)

@@ -326,47 +326,62 @@ std::vector<QItem> build_q_items(const Shape &s, int bm_tok, int BN) {
 // Work lists and the per-call tables (sequence bounds, head map) are built on the host
 // and copied into the workspace on the caller's stream, in one copy per call.
 //   Pinned (the entry points with a caller workspace): the copy reads a pinned host
-//   slot, reused only once the event recorded after its copy has completed.  Slots are
-//   polled, never waited for: when every slot is still in flight a new one is added, so
-//   a call never blocks the host (the pool grows with the caller's run-ahead).
+//   slot.  Outside graph capture a slot is reused only once the event recorded after
+//   its copy has completed.  Slots are polled, never waited for: when every slot is
+//   still in flight a new one is added, so a call never blocks the host (the pool grows
+//   with the caller's run-ahead).  Under HIP graph capture the copy becomes a node of
+//   the graph, which reads the slot again at every replay, so the slot is reserved for
+//   that graph and no later call writes it; it stays reserved until the process ends
+//   (a call's staged bytes: 32 per work item plus the sequence and head tables).
+//   Slots are never freed while the process runs: freeing pinned memory may wait for
+//   the device.
 //   Pageable (the entry point that allocates nothing): the copy reads the host vector
 //   itself; HIP performs a copy from unpinned host memory synchronously, so the call
-//   returns once the data has left the host buffer, which is then free to go.
+//   returns once the data has left the host buffer, which is then free to go.  Such a
+//   copy cannot be captured into a graph, so this path refuses a capturing stream.
+
+enum class Staging { kPinned, kPageable };
 
 struct StagingRing {
   struct Slot {
     void *host = nullptr;
     size_t cap = 0;
     hipEvent_t ev = nullptr;
-    bool pending = false;
+    bool pending = false;    // an eager copy from it may still be running
+    bool captured = false;   // a captured graph reads it at every replay
   };
   std::mutex mu;
   std::map<int, std::vector<Slot>> per_device;
 };
 
+// Never destroyed: slots reserved by graphs must outlive every replay.
 StagingRing &ring() {
-  static StagingRing r;
-  return r;
+  static StagingRing *r = new StagingRing;
+  return *r;
 }
 
-// Work lists go through reusable pinned host slots, which a captured graph would read
-// again at every replay, after later calls have overwritten them: calls on a
-// capturing stream are refused before anything is enqueued.
-dkv_status check_not_capturing(hipStream_t stream) {
+// Whether `stream` is capturing a graph.  A capture that an earlier error invalidated
+// is reported as an error; with pageable staging an active capture is refused too.
+// Runs before anything is enqueued.
+dkv_status capture_state(hipStream_t stream, Staging how, bool *capturing) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   hipError_t e = hipStreamIsCapturing(stream, &cs);
   if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
-  if (cs != hipStreamCaptureStatusNone)
-    return fail(DKV_ERR_UNSUPPORTED, "calls on a capturing stream are not supported (work lists "
-                "are staged through reused host buffers)");
+  if (cs == hipStreamCaptureStatusInvalidated)
+    return fail(DKV_ERR_HIP, "the stream's graph capture has been invalidated");
+  *capturing = cs == hipStreamCaptureStatusActive;
+  if (*capturing && how == Staging::kPageable)
+    return fail(DKV_ERR_UNSUPPORTED, "calls without a workspace cannot run on a capturing "
+                "stream (their work lists are copied from pageable host memory)");
   return DKV_OK;
 }
-
-enum class Staging { kPinned, kPageable };
 
 dkv_status upload(const void *src, size_t bytes, void *dst, hipStream_t stream,
                   Staging how = Staging::kPinned) {
   if (bytes == 0) return DKV_OK;
+  bool capturing = false;
+  dkv_status st = capture_state(stream, how, &capturing);
+  if (st != DKV_OK) return st;
   hipError_t e;
   if (how == Staging::kPageable) {
     e = hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, stream);
@@ -379,9 +394,11 @@ dkv_status upload(const void *src, size_t bytes, void *dst, hipStream_t stream,
   StagingRing &r = ring();
   std::lock_guard<std::mutex> lock(r.mu);
   auto &slots = r.per_device[dev];
-  StagingRing::Slot *fit = nullptr, *any = nullptr;
+  StagingRing::Slot *fit = nullptr;
   for (auto &x : slots) {
-    if (x.pending) {
+    if (x.captured) continue;
+    // Under capture the events are not polled (a slot still pending stays skipped).
+    if (x.pending && !capturing) {
       e = hipEventQuery(x.ev);
       if (e == hipSuccess)
         x.pending = false;
@@ -389,30 +406,35 @@ dkv_status upload(const void *src, size_t bytes, void *dst, hipStream_t stream,
         return hip_fail(e, "hipEventQuery(staging)");
     }
     if (x.pending) continue;
-    if (!any) any = &x;
     if (x.cap >= bytes && (!fit || x.cap < fit->cap)) fit = &x;
   }
-  StagingRing::Slot *sl = fit ? fit : any;
+  StagingRing::Slot *sl = fit;
   if (!sl) {
-    slots.emplace_back();
+    // A new slot (a smaller idle one is kept for smaller lists).  Allocating pinned
+    // memory is not a stream operation; the thread's capture mode is relaxed around it
+    // so that a capture in global mode accepts the call.
+    StagingRing::Slot fresh;
+    const size_t cap = std::max<size_t>(bytes, 64 * 1024);
+    hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+    if (capturing) (void)hipThreadExchangeStreamCaptureMode(&mode);
+    e = hipHostMalloc(&fresh.host, cap, hipHostMallocDefault);
+    if (capturing) (void)hipThreadExchangeStreamCaptureMode(&mode);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(staging)");
+    fresh.cap = cap;
+    slots.push_back(fresh);
     sl = &slots.back();
+  }
+  std::memcpy(sl->host, src, bytes);
+  e = hipMemcpyAsync(dst, sl->host, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work lists)");
+  if (capturing) {
+    sl->captured = true;
+    return DKV_OK;
   }
   if (!sl->ev) {
     e = hipEventCreateWithFlags(&sl->ev, hipEventDisableTiming);
     if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
   }
-  if (sl->cap < bytes) {
-    if (sl->host) (void)hipHostFree(sl->host);
-    sl->host = nullptr;
-    sl->cap = 0;
-    size_t cap = std::max<size_t>(bytes, 64 * 1024);
-    e = hipHostMalloc(&sl->host, cap, hipHostMallocDefault);
-    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(staging)");
-    sl->cap = cap;
-  }
-  std::memcpy(sl->host, src, bytes);
-  e = hipMemcpyAsync(dst, sl->host, bytes, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work lists)");
   e = hipEventRecord(sl->ev, stream);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord(staging)");
   sl->pending = true;
@@ -463,6 +485,10 @@ hipEvent_t get_event(Timing &t) {
 template <typename F> hipError_t timed(int cls, hipStream_t stream, F &&fn) {
   Timing &t = timing();
   if (!t.on) return fn();
+  // A capturing stream records no timing events (they would become nodes of the graph).
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+    return fn();
   std::lock_guard<std::mutex> lock(t.mu);
   hipEvent_t a = get_event(t), b = get_event(t);
   if (!a || !b) return fn();
@@ -536,7 +562,8 @@ dkv_status run_fwd(const Shape &s, const void *q, const void *kc, const void *vc
   FwdPlan pl = plan_fwd(s);
   dkv_status st = check_ws(ws, ws_bytes, pl.bytes);
   if (st != DKV_OK) return st;
-  if (pl.st.n_q > 0 && (st = check_not_capturing(stream)) != DKV_OK) return st;
+  bool capturing = false;
+  if (pl.st.n_q > 0 && (st = capture_state(stream, how, &capturing)) != DKV_OK) return st;
   if (pl.st.n_q == 0) return DKV_OK;
   std::vector<QItem> items = build_q_items(s, s.bm_tok, kFwdBN);
   char *wsb = static_cast<char *>(ws);
@@ -748,7 +775,8 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
   BwdPlan pl = plan_bwd(s, io.with_ctx, split);
   dkv_status st = check_ws(ws, ws_bytes, pl.bytes);
   if (st != DKV_OK) return st;
-  if ((st = check_not_capturing(stream)) != DKV_OK) return st;
+  bool capturing = false;
+  if ((st = capture_state(stream, how, &capturing)) != DKV_OK) return st;
   char *wsb = static_cast<char *>(ws);
   const long acc_elems = io.acc_rows * s.Hkv * s.d;
   hipError_t e;
@@ -1190,7 +1218,8 @@ dkv_status dkv_layout(const dkv_params *p, int op, int64_t row_elems, const void
     return st;
   if ((st = check_ws(ws, ws_bytes, pl.bytes)) != DKV_OK) return st;
   if (pl.items.empty()) return DKV_OK;
-  if ((st = check_not_capturing(stream)) != DKV_OK) return st;
+  bool capturing = false;
+  if ((st = capture_state(stream, Staging::kPinned, &capturing)) != DKV_OK) return st;
   char *wsb = static_cast<char *>(ws);
   {
     StagedImage img(pl.bytes);
