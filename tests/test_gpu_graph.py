@@ -26,13 +26,13 @@ CASES = [
 ]
 
 
-def _step(t, wl, split):
+def _step(t, wl, split, **kw):
     o_p, lse_p, o_r, lse_r = dkv.dualkv_forward(t["q_p"], t["k_p"], t["v_p"], t["q_r"],
                                                 t["k_r"], t["v_r"], t["cu"],
-                                                cu_host=t["cu_host"], window_left=wl)
+                                                cu_host=t["cu_host"], window_left=wl, **kw)
     g = dkv.dualkv_backward(t["q_p"], t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], o_p,
                             lse_p, o_r, lse_r, t["do_p"], t["do_r"], t["cu"],
-                            cu_host=t["cu_host"], window_left=wl, split=split)
+                            cu_host=t["cu_host"], window_left=wl, split=split, **kw)
     return dict(o_p=o_p, lse_p=lse_p, o_r=o_r, lse_r=lse_r, **g)
 
 
@@ -44,26 +44,23 @@ def _other_shape_work(d, seed):
     _step(u, -1, False)
 
 
-@pytest.mark.parametrize("P,lens,Hq,Hkv,d,wl,split", CASES)
-def test_graph_replays_match_eager_calls(P, lens, Hq, Hkv, d, wl, split):
-    print("graph case P=%d lens=%s Hq=%d Hkv=%d d=%d wl=%d split=%s" %
-          (P, lens, Hq, Hkv, d, wl, split), flush=True)
-    t = to_dev(workloads.make_inputs(P, lens, Hq, Hkv, d, "bf16", seed=500 + d, dout=True),
-               "bf16")
-    _step(t, wl, split)            # eager first: the library and its kernels are loaded
+def _capture_and_replay(t, step, new_inputs, d, split):
+    """Capture step(t) into a graph; then three times: load new inputs into t, run eager
+    calls of another shape, run step(t) eagerly, replay the graph, and compare."""
+    step(t)                        # eager first: the library and its kernels are loaded
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=s):
-        out = _step(t, wl, split)
+        out = step(t)
     torch.cuda.synchronize()
     for r in range(3):
-        x = workloads.make_inputs(P, lens, Hq, Hkv, d, "bf16", seed=600 + 10 * d + r, dout=True)
+        x = new_inputs(r)
         for k in INPUTS:
             t[k].copy_(x[k].to(torch.bfloat16).to(DEV))
         _other_shape_work(d, seed=700 + r)
-        ref = _step(t, wl, split)
+        ref = step(t)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
@@ -76,6 +73,36 @@ def test_graph_replays_match_eager_calls(P, lens, Hq, Hkv, d, wl, split):
                       v.float().cpu().numpy().astype(np.float64), "bf16")
     del graph
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("P,lens,Hq,Hkv,d,wl,split", CASES)
+def test_graph_replays_match_eager_calls(P, lens, Hq, Hkv, d, wl, split):
+    print("graph case P=%d lens=%s Hq=%d Hkv=%d d=%d wl=%d split=%s" %
+          (P, lens, Hq, Hkv, d, wl, split), flush=True)
+    t = to_dev(workloads.make_inputs(P, lens, Hq, Hkv, d, "bf16", seed=500 + d, dout=True),
+               "bf16")
+    _capture_and_replay(
+        t, lambda u: _step(u, wl, split),
+        lambda r: workloads.make_inputs(P, lens, Hq, Hkv, d, "bf16", seed=600 + 10 * d + r,
+                                        dout=True), d, split)
+
+
+def test_graph_with_prompt_groups_and_head_map():
+    # Several prompts in the micro-batch (each shared by its own responses, one of them
+    # empty, one group without responses) and a shuffled GQA head map: the group and
+    # head tables travel in the captured copy with the work lists.
+    groups = [(64, [32, 20]), (100, [50]), (0, [40, 7]), (30, [])]
+    Hq, Hkv, d, wl = 8, 2, 128, 50
+    kvh = [1, 0, 1, 0, 0, 1, 1, 0]
+    print("graph case: prompt groups %s, head map %s, window %d" % (groups, kvh, wl), flush=True)
+    pk = workloads.make_group_inputs(groups, Hq, Hkv, d, "bf16", seed=801)[1]
+    t = to_dev(pk, "bf16")
+    kw = dict(ctx_cu_host=[int(c) for c in pk["ctx_cu"]],
+              group_seq_cu_host=[int(c) for c in pk["seq_cu"]], kv_head_of_q=kvh)
+    _capture_and_replay(
+        t, lambda u: _step(u, wl, True, **kw),
+        lambda r: workloads.make_group_inputs(groups, Hq, Hkv, d, "bf16", seed=810 + r)[1],
+        d, True)
 
 
 def test_noalloc_refuses_a_capturing_stream():
