@@ -173,13 +173,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_f32_kernel(BwdQArgs a) {
     comp[db] = zero16();
   }
 
-  const int ctx_lo = (wl >= 0) ? max(0, qmin - wl) : 0;
-  const int ctx_t0 = (ctx_lo / BN) * BN;
-  const int n_ctx = (P > ctx_lo) ? (P - ctx_t0 + BN - 1) / BN : 0;
-  const int own_lo = (wl >= 0) ? max(0, t0 - wl) : 0;
-  const int own_t0 = (own_lo / BN) * BN;
-  const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
-  const int n_tiles = n_ctx + n_own;
+  KeyTiles<BN> kt;
+  kt.init(P, wl, t0, nt);
+  const int n_tiles = kt.n;
 
   const T *kc_base = reinterpret_cast<const T *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
   const T *vc_base = reinterpret_cast<const T *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
@@ -188,12 +184,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_f32_kernel(BwdQArgs a) {
 
   RowRegs<T, HD, BN> kregs, vregs;
   auto issue = [&](int i) {
-    if (i < n_ctx) {
-      int s = ctx_t0 + i * BN;
+    if (kt.in_ctx(i)) {
+      const int s = kt.ctx_start(i);
       kregs.load(kc_base + (long)s * kld, kld, P - s, tid);
       vregs.load(vc_base + (long)s * kld, kld, P - s, tid);
     } else {
-      int s = own_t0 + (i - n_ctx) * BN;
+      const int s = kt.own_start(i);
       kregs.load(ko_base + (long)s * kld, kld, seqlen - s, tid);
       vregs.load(vo_base + (long)s * kld, kld, seqlen - s, tid);
     }
@@ -202,15 +198,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_f32_kernel(BwdQArgs a) {
 
   for (int i = 0; i < n_tiles; ++i) {
     int nrows, kpos0;
-    if (i < n_ctx) {
-      int s = ctx_t0 + i * BN;
-      nrows = P - s;
-      kpos0 = s;
-    } else {
-      int s = own_t0 + (i - n_ctx) * BN;
-      nrows = seqlen - s;
-      kpos0 = P + s;
-    }
+    kt.at(i, P, seqlen, nrows, kpos0);
     __syncthreads();
     kregs.store(ks, tid);
     vregs.store(vs, tid);
@@ -339,13 +327,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_h16_kernel(BwdQArgs a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = zero16();
 
-  const int ctx_lo = (wl >= 0) ? max(0, qmin - wl) : 0;
-  const int ctx_t0 = (ctx_lo / BN) * BN;
-  const int n_ctx = (P > ctx_lo) ? (P - ctx_t0 + BN - 1) / BN : 0;
-  const int own_lo = (wl >= 0) ? max(0, t0 - wl) : 0;
-  const int own_t0 = (own_lo / BN) * BN;
-  const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
-  const int n_tiles = n_ctx + n_own;
+  KeyTiles<BN> kt;
+  kt.init(P, wl, t0, nt);
+  const int n_tiles = kt.n;
 
   const h16 *kc_base = reinterpret_cast<const h16 *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
   const h16 *vc_base = reinterpret_cast<const h16 *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
@@ -356,12 +340,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_h16_kernel(BwdQArgs a) {
   dma.init(wave, lane, kld_b);
   auto issue = [&](int i) {   // tile i -> stage i % 2
     char *st = smem[i & 1];
-    if (i < n_ctx) {
-      int s = ctx_t0 + i * BN;
+    if (kt.in_ctx(i)) {
+      const int s = kt.ctx_start(i);
       dma.load(st, kc_base + (long)s * kld, kld_b, P - s, wave);
       dma.load(st + TILE, vc_base + (long)s * kld, kld_b, P - s, wave);
     } else {
-      int s = own_t0 + (i - n_ctx) * BN;
+      const int s = kt.own_start(i);
       dma.load(st, ko_base + (long)s * kld, kld_b, seqlen - s, wave);
       dma.load(st + TILE, vo_base + (long)s * kld, kld_b, seqlen - s, wave);
     }
@@ -370,15 +354,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_h16_kernel(BwdQArgs a) {
 
   for (int i = 0; i < n_tiles; ++i) {
     int nrows, kpos0;
-    if (i < n_ctx) {
-      int s = ctx_t0 + i * BN;
-      nrows = P - s;
-      kpos0 = s;
-    } else {
-      int s = own_t0 + (i - n_ctx) * BN;
-      nrows = seqlen - s;
-      kpos0 = P + s;
-    }
+    kt.at(i, P, seqlen, nrows, kpos0);
     dma_wait();
     __syncthreads();
     if (i + 1 < n_tiles) issue(i + 1);
@@ -529,50 +505,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdKVArgs a) {
     cv[db] = zero16();
   }
 
-  // Query rows that can see this key tile, per sequence, in flattened units.
-  auto seq_range = [&](int s, int &fa, int &fb) {
-    int len = sload_i32(a.cu, s + 1) - sload_i32(a.cu, s);
-    int r_lo, r_hi;
-    if (ctx) {
-      r_lo = 0;
-      r_hi = len;
-      if (wl >= 0) r_hi = min(len, it.key_start + nk_tile - 1 + wl - P + 1);
-    } else {
-      r_lo = it.key_start;
-      r_hi = len;
-      if (wl >= 0) r_hi = min(len, it.key_start + nk_tile - 1 + wl + 1);
-    }
-    fa = r_lo * G;
-    fb = r_hi > r_lo ? r_hi * G : fa;
-  };
-
-  // Cursor over (sequence, 32-row step), walked from the last visible row of the
-  // last sequence backward.  Steps sit on multiples of 32 flattened rows, so every
-  // key tile of one sequence starts on the same block: the workgroups that share a
-  // sequence stream the same query rows at the same time and hit in L2.
-  int cs = it.seq_hi - 1, cf = 0, cfa = 0, cfb = 0;
-  bool done = false;
-  auto seek = [&]() {   // from sequence cs downward, find a non-empty range
-    while (cs >= it.seq_lo) {
-      int fa, fb;
-      seq_range(cs, fa, fb);
-      if (fb > fa) {
-        cfa = fa;
-        cfb = fb;
-        cf = ((fb - 1) / BM) * BM;
-        return;
-      }
-      --cs;
-    }
-    done = true;
-  };
-  seek();
+  // Steps of BM flattened rows (RowSteps), walked from the last visible row of the last
+  // sequence backward.
+  RowSteps<BM> rs;
+  rs.init(a.cu, it, nk_tile, P, wl, G, ctx);
 
   QStepRegs<HD> qregs, dregs;
   float lse_r = INFINITY, d_r = 0.f;
   auto issue = [&]() {
-    const int s0 = sload_i32(a.cu, cs);
-    const int lo = max(cf, cfa), hi = min(cf + BM, cfb);
+    const int cf = rs.cf, s0 = rs.cs0;
+    const int lo = max(cf, rs.cfa), hi = min(cf + BM, rs.cfb);
     const T *qb = reinterpret_cast<const T *>(a.q) + (long)s0 * qld;
     const T *db_ = reinterpret_cast<const T *>(a.dout) + (long)s0 * qld;
     qregs.load_flat(qb, qld, G, g, a.qhead, cf, lo, hi, tid);
@@ -590,10 +532,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdKVArgs a) {
       }
     }
   };
-  if (!done) issue();
+  if (!rs.done) issue();
 
-  while (!done) {
-    const int f0 = cf, flo = max(cf, cfa), fend = min(cf + BM, cfb);
+  while (!rs.done) {
+    int f0, flo, fend;
+    rs.advance(f0, flo, fend);
     __syncthreads();
     qregs.store(qs, tid);
     dregs.store(dos, tid);
@@ -602,12 +545,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdKVArgs a) {
       d_s[tid] = d_r;
     }
     __syncthreads();
-    cf -= BM;
-    if (cf + BM <= cfa) {
-      --cs;
-      seek();
-    }
-    if (!done) issue();
+    if (!rs.done) issue();
 
     if (wave_active) {
       // S = Q K^T and dP = dO V^T for 32 query rows x this wave's 32 keys.
@@ -777,46 +715,9 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_h16_kernel(BwdKVArgs a) {
     dv[db] = zero16();
   }
 
-  // Query rows that can see this key tile, per sequence, in flattened units.
-  auto seq_range = [&](int sq, int &fa, int &fb, int &s0, int &len) {
-    s0 = sload_i32(a.cu, sq);
-    len = sload_i32(a.cu, sq + 1) - s0;
-    int r_lo, r_hi;
-    if (ctx) {
-      r_lo = 0;
-      r_hi = len;
-      if (wl >= 0) r_hi = min(len, it.key_start + nk_tile - 1 + wl - P + 1);
-    } else {
-      r_lo = it.key_start;
-      r_hi = len;
-      if (wl >= 0) r_hi = min(len, it.key_start + nk_tile - 1 + wl + 1);
-    }
-    fa = r_lo * G;
-    fb = r_hi > r_lo ? r_hi * G : fa;
-  };
-  // Steps sit on multiples of BM flattened rows, walked from the last one backward, so
-  // every key tile of a sequence streams the same rows at the same time (L2 reuse).
-  // The cursor's sequence start and length are kept from the seek, so a step's
-  // fetch issues no scalar load.
-  int cs = it.seq_hi - 1, cf = 0, cfa = 0, cfb = 0, cs0 = 0, clen = 0;
-  bool done = false;
-  auto seek = [&]() {
-    while (cs >= it.seq_lo) {
-      int fa, fb, s0, len;
-      seq_range(cs, fa, fb, s0, len);
-      if (fb > fa) {
-        cfa = fa;
-        cfb = fb;
-        cs0 = s0;
-        clen = len;
-        cf = ((fb - 1) / BM) * BM;
-        return;
-      }
-      --cs;
-    }
-    done = true;
-  };
-  seek();
+  // Steps of BM flattened rows, walked from the last one backward.
+  RowSteps<BM> rs;
+  rs.init(a.cu, it, nk_tile, P, wl, G, ctx);
 
   const int tl = lane / G, jl = lane - tl * G;   // this lane's row of the LSE / D fetch
   // ceil(2^24 / G): r * g_recip >> 24 is r / G exactly for r < 64 and G <= 128 (the
@@ -832,13 +733,13 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_h16_kernel(BwdKVArgs a) {
 
   // Fetch the step at the cursor into stage `st`.
   auto issue = [&](char *st) {
-    const int s0 = cs0;
-    const int len = clen;
+    const int s0 = rs.cs0;
+    const int len = rs.clen;
     const __amdgpu_buffer_rsrc_t rq =
         make_rsrc_u(reinterpret_cast<const h16 *>(a.q) + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
     const __amdgpu_buffer_rsrc_t rd =
         make_rsrc_u(reinterpret_cast<const h16 *>(a.dout) + (long)s0 * qld, (uint32_t)len * (uint32_t)qld_b);
-    const int ft = cf / G, fj = cf - ft * G;
+    const int ft = rs.cf / G, fj = rs.cf - ft * G;
     const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_u32(st) + wave * 1024);
 #pragma unroll
     for (int k = 0; k < KPW; ++k) {
@@ -871,23 +772,11 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_h16_kernel(BwdKVArgs a) {
     }
   };
 
-  int nf0 = 0, nflo = 0, nfend = 0;
-  auto advance = [&]() {   // record the fetched step's bounds, then move the cursor on
-    nf0 = cf;
-    nflo = max(cf, cfa);
-    nfend = min(cf + BM, cfb);
-    cf -= BM;
-    if (cf + BM <= cfa) {
-      --cs;
-      seek();
-    }
-  };
-  bool have = !done;
+  bool have = !rs.done;
   int f0 = 0, flo = 0, fend = 0;
   if (have) {
     issue(smem);
-    advance();
-    f0 = nf0, flo = nflo, fend = nfend;
+    rs.advance(f0, flo, fend);
   }
 
   // One step computed from stage STG (a compile-time stage, so every LDS read of the
@@ -896,12 +785,11 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_h16_kernel(BwdKVArgs a) {
     constexpr int STG = decltype(stg_c)::value;
     dma_wait();
     __syncthreads();
-    const bool more = !done;
+    const bool more = !rs.done;
     int g0 = 0, glo = 0, gend = 0;
     if (more) {
       issue(smem + (STG ^ 1) * STAGE);
-      advance();
-      g0 = nf0, glo = nflo, gend = nfend;
+      rs.advance(g0, glo, gend);
     }
     const char *qs = smem + STG * STAGE;
     const char *dos = qs + TILE;

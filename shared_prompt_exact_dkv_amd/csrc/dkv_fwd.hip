@@ -74,13 +74,9 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
 
   // Key tile ranges of the two regions for this tile of queries.
-  const int ctx_lo = (wl >= 0) ? max(0, qmin - wl) : 0;
-  const int ctx_t0 = (ctx_lo / BN) * BN;
-  const int n_ctx = (P > ctx_lo) ? (P - ctx_t0 + BN - 1) / BN : 0;
-  const int own_lo = (wl >= 0) ? max(0, t0 - wl) : 0;
-  const int own_t0 = (own_lo / BN) * BN;
-  const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
-  const int n_tiles = n_ctx + n_own;
+  KeyTiles<BN> kt;
+  kt.init(P, wl, t0, nt);
+  const int n_tiles = kt.n;
 
   const T *kc_base = reinterpret_cast<const T *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
   const T *vc_base = reinterpret_cast<const T *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
@@ -89,12 +85,12 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
 
   RowRegs<T, HD, BN> kregs, vregs;
   auto issue = [&](int i) {
-    if (i < n_ctx) {
-      int s = ctx_t0 + i * BN;
+    if (kt.in_ctx(i)) {
+      const int s = kt.ctx_start(i);
       kregs.load(kc_base + (long)s * kld, kld, P - s, tid);
       vregs.load(vc_base + (long)s * kld, kld, P - s, tid);
     } else {
-      int s = own_t0 + (i - n_ctx) * BN;
+      const int s = kt.own_start(i);
       kregs.load(ko_base + (long)s * kld, kld, seqlen - s, tid);
       vregs.load(vo_base + (long)s * kld, kld, seqlen - s, tid);
     }
@@ -103,15 +99,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(FwdArgs a) {
 
   for (int i = 0; i < n_tiles; ++i) {
     int nrows, kpos0;
-    if (i < n_ctx) {
-      int s = ctx_t0 + i * BN;
-      nrows = P - s;
-      kpos0 = s;
-    } else {
-      int s = own_t0 + (i - n_ctx) * BN;
-      nrows = seqlen - s;
-      kpos0 = P + s;
-    }
+    kt.at(i, P, seqlen, nrows, kpos0);
     __syncthreads();
     kregs.store(ks, tid);
     vregs.store(vs, tid);

@@ -66,13 +66,9 @@ __global__ __launch_bounds__(256, WPE) void fwd_h16_kernel(FwdArgs a) {
   for (int db = 0; db < NDB; ++db) acc[db] = zero16();
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int ctx_lo = (wl >= 0) ? max(0, qmin - wl) : 0;
-  const int ctx_t0 = (ctx_lo / BN) * BN;
-  const int n_ctx = (P > ctx_lo) ? (P - ctx_t0 + BN - 1) / BN : 0;
-  const int own_lo = (wl >= 0) ? max(0, t0 - wl) : 0;
-  const int own_t0 = (own_lo / BN) * BN;
-  const int n_own = (t0 + nt - own_t0 + BN - 1) / BN;
-  const int n_tiles = n_ctx + n_own;
+  KeyTiles<BN> kt;
+  kt.init(P, wl, t0, nt);
+  const int n_tiles = kt.n;
 
   const h16 *kc_base = reinterpret_cast<const h16 *>(a.k_ctx) + (long)it.ctx_start * kld + (long)g * HD;
   const h16 *vc_base = reinterpret_cast<const h16 *>(a.v_ctx) + (long)it.ctx_start * kld + (long)g * HD;
@@ -84,12 +80,12 @@ __global__ __launch_bounds__(256, WPE) void fwd_h16_kernel(FwdArgs a) {
   dma.init(wave, lane, kld_b);
   auto issue = [&](int i) {   // tile i -> stage i % 2
     char *st = smem[i & 1];
-    if (i < n_ctx) {
-      int s = ctx_t0 + i * BN;
+    if (kt.in_ctx(i)) {
+      const int s = kt.ctx_start(i);
       dma.load(st, kc_base + (long)s * kld, kld_b, P - s, wave);
       dma.load(st + TILE, vc_base + (long)s * kld, kld_b, P - s, wave);
     } else {
-      int s = own_t0 + (i - n_ctx) * BN;
+      const int s = kt.own_start(i);
       dma.load(st, ko_base + (long)s * kld, kld_b, seqlen - s, wave);
       dma.load(st + TILE, vo_base + (long)s * kld, kld_b, seqlen - s, wave);
     }
@@ -98,15 +94,7 @@ __global__ __launch_bounds__(256, WPE) void fwd_h16_kernel(FwdArgs a) {
 
   for (int i = 0; i < n_tiles; ++i) {
     int nrows, kpos0;
-    if (i < n_ctx) {
-      int s = ctx_t0 + i * BN;
-      nrows = P - s;
-      kpos0 = s;
-    } else {
-      int s = own_t0 + (i - n_ctx) * BN;
-      nrows = seqlen - s;
-      kpos0 = P + s;
-    }
+    kt.at(i, P, seqlen, nrows, kpos0);
     // Tile i has landed in stage i % 2 and every wave is done with tile i - 1, whose
     // stage receives tile i + 1 while tile i is computed.
     dma_wait();

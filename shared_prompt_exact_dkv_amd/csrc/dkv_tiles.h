@@ -12,6 +12,7 @@
 #pragma once
 
 #include "dkv_device.h"
+#include "dkv_launch.h"
 
 namespace dkv {
 
@@ -329,5 +330,115 @@ template <int HDP, int ROWS, int HD = HDP> struct DmaRows {
   }
 };
 
-}  // namespace dkv
 
+// ------------------------------------------------------- work-item walks --
+
+// The key tiles of a query work item (rows t0 .. t0 + nt - 1 of its sequence, after a
+// P-token prompt, window wl or -1): first the prompt tiles its rows can see, then tiles
+// of its own keys, BN keys each, at multiples of BN within their region.
+template <int BN> struct KeyTiles {
+  int ctx_t0, n_ctx, own_t0, n;
+  __device__ __forceinline__ void init(int P, int wl, int t0, int nt) {
+    const int ctx_lo = (wl >= 0) ? max(0, P + t0 - wl) : 0;
+    ctx_t0 = (ctx_lo / BN) * BN;
+    n_ctx = (P > ctx_lo) ? (P - ctx_t0 + BN - 1) / BN : 0;
+    const int own_lo = (wl >= 0) ? max(0, t0 - wl) : 0;
+    own_t0 = (own_lo / BN) * BN;
+    n = n_ctx + (t0 + nt - own_t0 + BN - 1) / BN;
+  }
+  // Whether tile i lies in the prompt (else in the item's own keys), and its first key
+  // within that region.
+  __device__ __forceinline__ bool in_ctx(int i) const { return i < n_ctx; }
+  __device__ __forceinline__ int ctx_start(int i) const { return ctx_t0 + i * BN; }
+  __device__ __forceinline__ int own_start(int i) const { return own_t0 + (i - n_ctx) * BN; }
+  // Tile i: the rows of its region from its first key (nrows; rows past them are zero
+  // filled) and the logical position of its first key.
+  __device__ __forceinline__ void at(int i, int P, int seqlen, int &nrows, int &kpos0) const {
+    if (in_ctx(i)) {
+      const int s = ctx_start(i);
+      nrows = P - s;
+      kpos0 = s;
+    } else {
+      const int s = own_start(i);
+      nrows = seqlen - s;
+      kpos0 = P + s;
+    }
+  }
+};
+
+// The query-row steps of a key work item: BM flattened (token, head) rows at a time,
+// walked from the item's last sequence and its last step backward, so that every key
+// tile of a sequence streams the same rows at the same time (L2 reuse).  A sequence's
+// visible rows are [fa, fb) in flattened units: for prompt keys (ctx) all of its rows,
+// for its own keys the rows from the tile's first key on, either cut at the window's
+// end.  The cursor keeps the sequence start and length of its seek, so a step's fetch
+// issues no scalar load.
+template <int BM> struct RowSteps {
+  const int32_t *cu;
+  int seq_lo, key_start, nk_tile, P, wl, G;
+  bool ctx;
+  int cs, cf, cfa, cfb, cs0, clen;
+  bool done;
+  __device__ __forceinline__ void seq_range(int sq, int &fa, int &fb, int &s0, int &len) const {
+    s0 = sload_i32(cu, sq);
+    len = sload_i32(cu, sq + 1) - s0;
+    int r_lo, r_hi;
+    if (ctx) {
+      r_lo = 0;
+      r_hi = len;
+      if (wl >= 0) r_hi = min(len, key_start + nk_tile - 1 + wl - P + 1);
+    } else {
+      r_lo = key_start;
+      r_hi = len;
+      if (wl >= 0) r_hi = min(len, key_start + nk_tile - 1 + wl + 1);
+    }
+    fa = r_lo * G;
+    fb = r_hi > r_lo ? r_hi * G : fa;
+  }
+  // From sequence cs downward, the first one with visible rows; its last step.
+  __device__ __forceinline__ void seek() {
+    while (cs >= seq_lo) {
+      int fa, fb, s0, len;
+      seq_range(cs, fa, fb, s0, len);
+      if (fb > fa) {
+        cfa = fa;
+        cfb = fb;
+        cs0 = s0;
+        clen = len;
+        cf = ((fb - 1) / BM) * BM;
+        return;
+      }
+      --cs;
+    }
+    done = true;
+  }
+  __device__ __forceinline__ void init(const int32_t *cu_, const KVItem &it, int nk_tile_, int P_,
+                                       int wl_, int G_, bool ctx_) {
+    cu = cu_;
+    seq_lo = it.seq_lo;
+    key_start = it.key_start;
+    nk_tile = nk_tile_;
+    P = P_;
+    wl = wl_;
+    G = G_;
+    ctx = ctx_;
+    cs = it.seq_hi - 1;
+    cf = cfa = cfb = cs0 = clen = 0;
+    done = false;
+    seek();
+  }
+  // The step at the cursor (first row f0, rows [flo, fend) inside the visible range),
+  // then the cursor moves on.
+  __device__ __forceinline__ void advance(int &f0, int &flo, int &fend) {
+    f0 = cf;
+    flo = max(cf, cfa);
+    fend = min(cf + BM, cfb);
+    cf -= BM;
+    if (cf + BM <= cfa) {
+      --cs;
+      seek();
+    }
+  }
+};
+
+}  // namespace dkv

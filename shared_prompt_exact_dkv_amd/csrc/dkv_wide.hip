@@ -81,12 +81,11 @@ template <int N, int R, int A> __device__ __forceinline__ void reads_ahead() {
   __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
 }
 
-// The key tiles of a query work item (rows t0 .. t0 + nt - 1 of its sequence, after a
-// P-token prompt): the prompt tiles its rows can see, then its own tiles, BN keys each
-// at multiples of BN.  `v` picks the V rows (else K); the wave with index w among the
-// four that fetch a tile writes its blocks b % 4 == w (DmaRows).
-template <int HD, int HDP, int BN> struct KVTiles {
-  int ctx_t0, n_ctx, own_t0, n, P, seqlen, w, kld_b;
+// The key tiles of a query work item (KeyTiles) with the K or V rows they fetch: `v`
+// picks the V rows (else K); the wave with index w among the four that fetch a tile
+// writes its blocks b % 4 == w (DmaRows).
+template <int HD, int HDP, int BN> struct KVTiles : KeyTiles<BN> {
+  int P, seqlen, w, kld_b;
   long kld;
   const h16 *c_base, *o_base;
   DmaRows<HDP, BN, HD> dma;
@@ -96,114 +95,24 @@ template <int HD, int HDP, int BN> struct KVTiles {
     P = it.ctx_len;
     seqlen = it.seq_len;
     w = w_;
-    const int wl = a.window_left;
-    const int ctx_lo = (wl >= 0) ? max(0, P + t0 - wl) : 0;
-    ctx_t0 = (ctx_lo / BN) * BN;
-    n_ctx = (P > ctx_lo) ? (P - ctx_t0 + BN - 1) / BN : 0;
-    const int own_lo = (wl >= 0) ? max(0, t0 - wl) : 0;
-    own_t0 = (own_lo / BN) * BN;
-    n = n_ctx + (t0 + nt - own_t0 + BN - 1) / BN;
+    KeyTiles<BN>::init(P, a.window_left, t0, nt);
     kld = (long)a.Hkv * HD;
     kld_b = (int)(kld * 2);
     c_base = reinterpret_cast<const h16 *>(v ? a.v_ctx : a.k_ctx) + (long)it.ctx_start * kld + (long)it.g * HD;
     o_base = reinterpret_cast<const h16 *>(v ? a.v_own : a.k_own) + (long)it.seq_start * kld + (long)it.g * HD;
     dma.init(w, lane, kld_b);
   }
-  // Tile i: the rows of its region from its first key (nrows; rows past them are zero
-  // filled) and the logical position of its first key.
   __device__ __forceinline__ void at(int i, int &nrows, int &kpos0) const {
-    if (i < n_ctx) {
-      const int s = ctx_t0 + i * BN;
-      nrows = P - s;
-      kpos0 = s;
-    } else {
-      const int s = own_t0 + (i - n_ctx) * BN;
-      nrows = seqlen - s;
-      kpos0 = P + s;
-    }
+    KeyTiles<BN>::at(i, P, seqlen, nrows, kpos0);
   }
   // This wave's share of tile i into the LDS tile at st.
   __device__ __forceinline__ void fetch(char *st, int i) {
-    if (i < n_ctx) {
-      const int s = ctx_t0 + i * BN;
+    if (this->in_ctx(i)) {
+      const int s = this->ctx_start(i);
       dma.load(st, c_base + (long)s * kld, kld_b, P - s, w);
     } else {
-      const int s = own_t0 + (i - n_ctx) * BN;
+      const int s = this->own_start(i);
       dma.load(st, o_base + (long)s * kld, kld_b, seqlen - s, w);
-    }
-  }
-};
-
-// The query-row steps of a key work item: BM flattened (token, head) rows at a time,
-// walked from the item's last sequence and its last step backward, so that every key
-// tile of a sequence streams the same rows at the same time (L2 reuse).  A sequence's
-// visible rows are [fa, fb) in flattened units: for prompt keys (ctx) all of its rows,
-// for its own keys the rows from the tile's first key on, either cut at the window's
-// end.  The cursor keeps the sequence start and length of its seek, so a step's fetch
-// issues no scalar load.
-template <int BM> struct RowSteps {
-  const int32_t *cu;
-  int seq_lo, key_start, nk_tile, P, wl, G;
-  bool ctx;
-  int cs, cf, cfa, cfb, cs0, clen;
-  bool done;
-  __device__ __forceinline__ void seq_range(int sq, int &fa, int &fb, int &s0, int &len) const {
-    s0 = sload_i32(cu, sq);
-    len = sload_i32(cu, sq + 1) - s0;
-    int r_lo, r_hi;
-    if (ctx) {
-      r_lo = 0;
-      r_hi = len;
-      if (wl >= 0) r_hi = min(len, key_start + nk_tile - 1 + wl - P + 1);
-    } else {
-      r_lo = key_start;
-      r_hi = len;
-      if (wl >= 0) r_hi = min(len, key_start + nk_tile - 1 + wl + 1);
-    }
-    fa = r_lo * G;
-    fb = r_hi > r_lo ? r_hi * G : fa;
-  }
-  __device__ __forceinline__ void seek() {
-    while (cs >= seq_lo) {
-      int fa, fb, s0, len;
-      seq_range(cs, fa, fb, s0, len);
-      if (fb > fa) {
-        cfa = fa;
-        cfb = fb;
-        cs0 = s0;
-        clen = len;
-        cf = ((fb - 1) / BM) * BM;
-        return;
-      }
-      --cs;
-    }
-    done = true;
-  }
-  __device__ __forceinline__ void init(const int32_t *cu_, const KVItem &it, int nk_tile_, int P_,
-                                       int wl_, int G_, bool ctx_) {
-    cu = cu_;
-    seq_lo = it.seq_lo;
-    key_start = it.key_start;
-    nk_tile = nk_tile_;
-    P = P_;
-    wl = wl_;
-    G = G_;
-    ctx = ctx_;
-    cs = it.seq_hi - 1;
-    cf = cfa = cfb = cs0 = clen = 0;
-    done = false;
-    seek();
-  }
-  // The step at the cursor (first row f0, rows [flo, fend) inside the visible range),
-  // then the cursor moves on.
-  __device__ __forceinline__ void advance(int &f0, int &flo, int &fend) {
-    f0 = cf;
-    flo = max(cf, cfa);
-    fend = min(cf + BM, cfb);
-    cf -= BM;
-    if (cf + BM <= cfa) {
-      --cs;
-      seek();
     }
   }
 };
