@@ -430,8 +430,21 @@ def main():
                 "unit": un, "frac": round(achieved / pk, 4),
                 "traffic": traffic_for(dom, w.name), "avg_launch_ms": round(tot_ms / launches, 4),
                 "launches_per_step": launches // args.steps}
-    kernels = {k: {"ms_per_step": round(v[0] / args.steps, 4), "launches_per_step": v[1] // args.steps}
-               for k, v in ktimes.items()}
+    # Every kernel class's rate on its own algorithmic work (same live timings as the
+    # roofline above), so the dQ and forward kernels' fractions sit beside the dominant one.
+    kernels = {}
+    for k, v in ktimes.items():
+        rec = {"ms_per_step": round(v[0] / args.steps, 4), "launches_per_step": v[1] // args.steps}
+        if k in algo and v[0] > 0:
+            amount, unit, _ = algo[k]
+            per_s = amount * args.steps / (v[0] * 1e-3)
+            if unit == "flop":
+                rec["tflops"] = round(per_s / 1e12, 2)
+                rec["frac"] = round(per_s / 1e12 / peak, 4)
+            else:
+                rec["gbs"] = round(per_s / 1e9, 1)
+                rec["frac"] = round(per_s / 1e9 / PEAK_HBM_GBS, 4)
+        kernels[k] = rec
 
     # N-copy comparator: the same library's causal kernel over N sequences [P, R_i].
     ncopy_ms = None
