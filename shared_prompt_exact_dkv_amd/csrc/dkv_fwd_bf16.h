@@ -1,7 +1,7 @@
 // dkv_fwd_bf16.h -- the h16 forward kernel template ("DualKV", arXiv 2605.15422,
 // §3.1): one online softmax over the shared-prompt KV region then the sequence's own
-// region.  Instantiated for head dims 64 / 128 in dkv_fwd.hip and 512 in
-// dkv_d512.hip (built with different register-placement options).
+// region.  Instantiated for head dims 64, 96 and 128 in dkv_fwd.hip (head dims 192,
+// 256 and 512 have their own kernels in dkv_wide.hip).
 #pragma once
 
 #include "dkv_device.h"
