@@ -5,7 +5,7 @@
 //   dP = <dO_t, v_j>,   dS = p * (dP - D_t),    D_t = <dO_t, O_t>
 //   dQ_t += scale * dS * k_j,   dK_j += scale * dS * q_t,   dV_j += p * dO_t
 // Kernels (each h16 kernel has an fp32 counterpart for the 1e-5 parity workload;
-// head dim 512 is in dkv_wide.hip):
+// head dims 192, 256 and 512 are in dkv_wide.hip):
 //   bwd_pre   D = rowsum(dO * O) in fp32 (the auxiliary preprocessing launch), stored
 //             negated, and the LSE in units of the raw dot product, -LSE / scale;
 //             the fp32 path only: the h16 dQ kernel forms both for its rows

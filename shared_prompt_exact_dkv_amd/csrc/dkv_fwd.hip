@@ -1,7 +1,7 @@
 // dkv_fwd.hip -- forward kernels: online softmax over a shared-prompt KV region and a
 // per-sequence KV region in one pass ("DualKV", arXiv 2605.15422, §3.1).  h16 at head
-// dims 64 / 128 runs fwd_bf16_kernel (dkv_fwd_bf16.h), head dim 512 the kernels of
-// dkv_wide.hip; this file holds the fp32 kernel and the dispatch.
+// dims 64 / 96 / 128 runs fwd_h16_kernel (dkv_fwd_bf16.h), head dims 192 / 256 / 512
+// the kernels of dkv_wide.hip; this file holds the fp32 kernel and the dispatch.
 //
 // fp32 kernel: one workgroup (4 waves) owns 128 query rows = bm_tok tokens x G q-heads
 // of one kv head (grouped-query attention, §3.1 last paragraph), so every K/V tile
