@@ -92,7 +92,7 @@ typedef enum {
 enum {
     DKV_ACC_ZERO = 1,      /* clear acc_dk_p / acc_dv_p before adding this call's terms */
     DKV_ACC_FINALIZE = 2,  /* after adding, cast the accumulator into dk_p / dv_p once */
-    /* dkv_bwd only.  §3.2 Stage 1 resolves the N-way write to the shared dK_c / dV_c
+    /* dkv_bwd.  §3.2 Stage 1 resolves the N-way write to the shared dK_c / dV_c
        with fp32 atomic adds into a scratch buffer (the default here too).  This flag
        resolves it without atomics, still summing in fp32 and casting once:
        the responses are taken in S chunks of ceil(N / S) sequences
@@ -100,8 +100,13 @@ enum {
        into its own fp32 slice of the workspace (size it with DKV_CALL_BWD_SPLIT), and
        one kernel then adds the slices to the accumulator in slice order.  No atomics
        touch the accumulator, so for given inputs and call order dk_p / dv_p are
-       bitwise reproducible (the Call-1 term of dkv_ctx_bwd has one writer per
-       element).  Workspace: 2 * S * P * Hkv * d * 4 bytes more. */
+       bitwise reproducible when dkv_ctx_bwd gets the flag too.  Workspace:
+       2 * S * P * Hkv * d * 4 bytes more.
+       dkv_ctx_bwd (with an accumulator): without this flag, when the call's key tiles
+       are few (fewer than 2048 tiles times kv heads), the query rows of a long tile may
+       be split over several work items that each add their partial sums into the
+       accumulator (fp32 atomics), which fills the GPU; with it every element of the
+       Call-1 term has one writer. */
     DKV_ACC_SPLIT = 4
 };
 
@@ -194,8 +199,9 @@ dkv_status dkv_fwd(const dkv_params *p, const void *q_resp, const void *k_p,
  * Inputs as in dkv_ctx_fwd plus o, lse (from the forward) and dout [T, Hq, d].
  * Writes dq [T, Hq, d].  Key/value gradients:
  *   - acc_dk / acc_dv non-NULL (fp32 [T, Hkv, d]): added into the accumulator
- *     (cleared first with DKV_ACC_ZERO; cast into dk/dv with DKV_ACC_FINALIZE).
- *     With one sequence over the prompt this is the Call-1 term of eq. (6).
+ *     (cleared first with DKV_ACC_ZERO; cast into dk/dv with DKV_ACC_FINALIZE;
+ *     DKV_ACC_SPLIT keeps one writer per element, see the flags above).  With one
+ *     sequence over the prompt this is the Call-1 term of eq. (6).
  *   - acc_dk / acc_dv NULL: written directly to dk / dv [T, Hkv, d] (plain varlen
  *     causal backward, e.g. the N-copy packing).
  */

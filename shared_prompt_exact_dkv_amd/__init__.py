@@ -379,15 +379,16 @@ def dualkv_backward(q_p, k_p, v_p, q_r, k_r, v_r, o_p, lse_p, o_r, lse_r, do_p, 
                     kv_head_of_q=None):
     """The two calls of the backward sharing one fp32 accumulator for dK_P/dV_P
     (eq. (6)): Call 1 clears it and adds the prompt self-attention term, Call 2 adds
-    the N responses' terms and casts once (split=True: through per-chunk slices and a
-    fixed-order sum, bitwise reproducible).  -> dict of dq_p, dk_p, dv_p, dq_r, dk_r,
-    dv_r."""
+    the N responses' terms and casts once (split=True: Call 1 with one writer per
+    element, Call 2 through per-chunk slices and a fixed-order sum, bitwise
+    reproducible).  -> dict of dq_p, dk_p, dv_p, dq_r, dk_r, dv_r."""
     if acc is None:
         acc = torch.empty((2,) + tuple(k_p.shape), dtype=torch.float32, device=k_p.device)
     cu_p_host = _prompt_cu(q_p.shape[0], ctx_cu_host)
     dq_p, _, _ = dkv_ctx_bwd(q_p, k_p, v_p, o_p, lse_p, do_p, None, cu_host=cu_p_host,
                              window_left=window_left, softmax_scale=softmax_scale,
-                             acc_dk=acc[0], acc_dv=acc[1], acc_flags=DKV_ACC_ZERO,
+                             acc_dk=acc[0], acc_dv=acc[1],
+                             acc_flags=DKV_ACC_ZERO | (DKV_ACC_SPLIT if split else 0),
                              kv_head_of_q=kv_head_of_q)
     dq_r, dk_r, dv_r, dk_p, dv_p = dkv_bwd(q_r, k_p, v_p, k_r, v_r, o_r, lse_r, do_r,
                                            cu_seqlens, acc_dk_p=acc[0], acc_dv_p=acc[1],

@@ -639,6 +639,37 @@ long kv_rows_visible(const Shape &s, bool ctx, int key_start, int nk, int len, i
   return std::max<long>(0, hi - lo);
 }
 
+// Own-region key tiles of a call that adds them into the accumulator may be split into
+// row chunks (see KVItem::row_hi): when the call's key tiles alone would give fewer
+// workgroups than this, the causal walk's long first tiles leave most of the GPU idle.
+static constexpr long kChunkBelowItems = 2048;
+
+bool chunk_own_rows(const Shape &s) {
+  long tiles = 0;
+  for (int i = 0; i < s.N; ++i) tiles += (s.cu[i + 1] - s.cu[i] + s.kv_tile - 1) / s.kv_tile;
+  return tiles * s.Hkv < kChunkBelowItems;
+}
+
+// The work items of an own-region key tile (keys k0 .. k0 + nk - 1 of a sequence of len
+// rows): (row_hi, visible rows) each.  Unsplit, one item walks every row that sees the
+// tile (row_hi = 0); split, one item per kRowChunk-row chunk (on multiples of kRowChunk
+// flattened rows) of those rows, when they span more than one chunk's worth.
+std::vector<std::pair<int, long>> own_row_chunks(const Shape &s, int k0, int nk, int len,
+                                                 bool chunk) {
+  const long rows = kv_rows_visible(s, false, k0, nk, len, 0);
+  const long fa = (long)k0 * s.G, fb = fa + rows * s.G;   // flattened rows [fa, fb)
+  std::vector<std::pair<int, long>> out;
+  if (!chunk || fb - fa <= kRowChunk) {
+    out.push_back({0, rows});
+    return out;
+  }
+  for (long c = fa / kRowChunk; c * kRowChunk < fb; ++c) {
+    const long lo = std::max(fa, c * kRowChunk), hi = std::min(fb, (c + 1) * kRowChunk);
+    out.push_back({(int)((c + 1) * kRowChunk), (hi - lo + s.G - 1) / s.G});
+  }
+  return out;
+}
+
 // The chunks of sequences [lo, hi) of prompt group pg whose prompt-key tiles are
 // separate work items.  Split mode takes the global chunks of split_chunk() sequences
 // (chunk c fills slice c), clipped to the group; a chunk holding no sequence of the
@@ -662,11 +693,12 @@ std::vector<std::pair<int, int>> ctx_chunks(const Shape &s, int pg, bool split) 
   return out;
 }
 
-std::vector<KVItem> build_kv_items(const Shape &s, bool with_ctx, bool split) {
+std::vector<KVItem> build_kv_items(const Shape &s, bool with_ctx, bool split,
+                                   bool chunk_own = false) {
   // Per prompt group and chunk of its sequences: the prompt key tiles that add the
-  // chunk's terms to the shared accumulator, and the chunk's own response key tiles.
-  // All of them stream the chunk's query rows.
-  struct Rec { long work; int region, key_start, lo, hi, c0, Pg; };
+  // chunk's terms to the shared accumulator, and the chunk's own response key tiles
+  // (row chunks of them with chunk_own).  All of them stream the chunk's query rows.
+  struct Rec { long work; int region, key_start, lo, hi, c0, Pg, row_hi; };
   struct Group { long work; std::vector<Rec> recs; };
   std::vector<Group> groups;
   auto add = [&](Group &x) {
@@ -694,15 +726,15 @@ std::vector<KVItem> build_kv_items(const Shape &s, bool with_ctx, bool split) {
             w += kv_rows_visible(s, true, k0, nk, s.cu[i + 1] - s.cu[i], Pg);
           // Split mode keeps tiles no row of the chunk sees: they store the zeros of
           // their slice, so every slice element is written.
-          if (w > 0 || split) ctxg.recs.push_back({w, kRegionCtx, k0, lo, hi, c0, Pg});
+          if (w > 0 || split) ctxg.recs.push_back({w, kRegionCtx, k0, lo, hi, c0, Pg, 0});
         }
       }
       for (int i = lo; i < hi; ++i) {
         int len = s.cu[i + 1] - s.cu[i];
         for (int k0 = 0; k0 < len; k0 += s.kv_tile) {
           int nk = std::min(s.kv_tile, len - k0);
-          owng.recs.push_back(
-              {kv_rows_visible(s, false, k0, nk, len, Pg), kRegionOwn, k0, i, i + 1, c0, Pg});
+          for (const auto &ch : own_row_chunks(s, k0, nk, len, chunk_own))
+            owng.recs.push_back({ch.second, kRegionOwn, k0, i, i + 1, c0, Pg, ch.first});
         }
       }
       add(ctxg);
@@ -719,7 +751,7 @@ std::vector<KVItem> build_kv_items(const Shape &s, bool with_ctx, bool split) {
       for (size_t r = 0; r < groups[gi].recs.size(); ++r) {
         const Rec &x = groups[gi].recs[r];
         lists[hx.xcd(g, (int)(by_tile ? r : gi))].push_back(
-            {g, x.region, x.key_start, x.lo, x.hi, x.c0, x.Pg, 0});
+            {g, x.region, x.key_start, x.lo, x.hi, x.c0, x.Pg, x.row_hi});
       }
   return interleave_xcds(lists);
 }
@@ -730,12 +762,13 @@ struct BwdPlan {
   int slices = 0;
 };
 
-BwdPlan plan_bwd(const Shape &s, bool with_ctx, bool split) {
+BwdPlan plan_bwd(const Shape &s, bool with_ctx, bool split, bool chunk_own = false) {
   BwdPlan pl;
   size_t nkv = 0;
   for (int i = 0; i < s.N; ++i) {
     int len = s.cu[i + 1] - s.cu[i];
-    nkv += (size_t)((len + s.kv_tile - 1) / s.kv_tile);
+    for (int k0 = 0; k0 < len; k0 += s.kv_tile)
+      nkv += own_row_chunks(s, k0, std::min(s.kv_tile, len - k0), len, chunk_own).size();
   }
   if (with_ctx)
     for (int pg = 0; pg + 1 < (int)s.gseq.size(); ++pg) {
@@ -772,7 +805,10 @@ struct BwdIO {
 dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
                    hipStream_t stream, Staging how) {
   const bool split = (io.flags & DKV_ACC_SPLIT) && io.with_ctx && s.P > 0;
-  BwdPlan pl = plan_bwd(s, io.with_ctx, split);
+  // Own key tiles split into row chunks: a call that adds them into the accumulator
+  // (Call 1 with one), unless DKV_ACC_SPLIT asks for one writer per element.
+  const bool chunk = io.own_to_acc && !(io.flags & DKV_ACC_SPLIT) && chunk_own_rows(s);
+  BwdPlan pl = plan_bwd(s, io.with_ctx, split, chunk);
   dkv_status st = check_ws(ws, ws_bytes, pl.bytes);
   if (st != DKV_OK) return st;
   bool capturing = false;
@@ -799,7 +835,7 @@ dkv_status run_bwd(const Shape &s, const BwdIO &io, void *ws, size_t ws_bytes,
       if (e != hipSuccess) return hip_fail(e, "bwd preprocess launch");
     }
     std::vector<QItem> qi = build_q_items(s, s.bm_tok_dq, kFwdBN);
-    std::vector<KVItem> kv = build_kv_items(s, io.with_ctx, split);
+    std::vector<KVItem> kv = build_kv_items(s, io.with_ctx, split, chunk);
     if (qi.size() != pl.st.n_q || kv.size() > pl.st.n_kv)
       return fail(DKV_ERR_INVALID_ARG, "internal: work lists exceed their plan");
     char *stb = wsb + pl.st_off;
@@ -1102,7 +1138,9 @@ size_t dkv_workspace_size(const dkv_params *p, int which_call) {
   if (check_params(p, is_ctx, &s) != DKV_OK) return (size_t)-1;
   if (which_call == DKV_CALL_CTX_FWD || which_call == DKV_CALL_FWD) return plan_fwd(s).bytes;
   const bool with_ctx = which_call == DKV_CALL_BWD || which_call == DKV_CALL_BWD_SPLIT;
-  return plan_bwd(s, with_ctx, which_call == DKV_CALL_BWD_SPLIT).bytes;
+  // dkv_ctx_bwd may split its key tiles into row chunks (flags decide): size for them.
+  return plan_bwd(s, with_ctx, which_call == DKV_CALL_BWD_SPLIT,
+                  which_call == DKV_CALL_CTX_BWD && chunk_own_rows(s)).bytes;
 }
 
 dkv_status dkv_ctx_fwd(const dkv_params *p, const void *q, const void *k, const void *v,
@@ -1140,8 +1178,9 @@ dkv_status dkv_ctx_bwd(const dkv_params *p, const void *q, const void *k, const 
   Shape s;
   dkv_status st = check_params(p, true, &s);
   if (st != DKV_OK) return st;
-  if (acc_flags & ~(DKV_ACC_ZERO | DKV_ACC_FINALIZE))
-    return fail(DKV_ERR_INVALID_ARG, "dkv_ctx_bwd accepts DKV_ACC_ZERO | DKV_ACC_FINALIZE only");
+  if (acc_flags & ~(DKV_ACC_ZERO | DKV_ACC_FINALIZE | DKV_ACC_SPLIT))
+    return fail(DKV_ERR_INVALID_ARG,
+                "dkv_ctx_bwd accepts DKV_ACC_ZERO | DKV_ACC_FINALIZE | DKV_ACC_SPLIT only");
   if (s.T == 0) return DKV_OK;   // nothing to compute, clear or cast
   const bool use_acc = acc_dk != nullptr || acc_dv != nullptr;
   bool need = true;

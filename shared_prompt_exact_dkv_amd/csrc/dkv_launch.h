@@ -104,8 +104,15 @@ struct KVItem {
   // value tensors (and the accumulator) and its length P.
   int32_t ctx_start;
   int32_t ctx_len;
-  int32_t pad;
+  // 0: the item walks every query row that sees its keys.  Otherwise the item walks
+  // only flattened rows [row_hi - kRowChunk, row_hi) of its sequence: one chunk of a
+  // key tile whose rows are split over several items, each adding its partial sums
+  // into the fp32 accumulator (own-region keys of a call that accumulates).
+  int32_t row_hi;
 };
+// Flattened (token, head) query rows per chunk of a split key tile: a multiple of every
+// dK/dV kernel's row step, so chunks follow the step grid.
+static constexpr int kRowChunk = 4096;
 
 struct BwdKVArgs {
   const void *q, *dout, *k_ctx, *v_ctx, *k_own, *v_own;

@@ -371,11 +371,13 @@ template <int BN> struct KeyTiles {
 // tile of a sequence streams the same rows at the same time (L2 reuse).  A sequence's
 // visible rows are [fa, fb) in flattened units: for prompt keys (ctx) all of its rows,
 // for its own keys the rows from the tile's first key on, either cut at the window's
-// end.  The cursor keeps the sequence start and length of its seek, so a step's fetch
-// issues no scalar load.
+// end, and for an item that walks one chunk of them (row_hi > 0) cut to that chunk.
+// The cursor keeps the sequence start and length of its seek, so a step's fetch issues
+// no scalar load.
 template <int BM> struct RowSteps {
+  static_assert(kRowChunk % BM == 0, "row chunks follow the step grid");
   const int32_t *cu;
-  int seq_lo, key_start, nk_tile, P, wl, G;
+  int seq_lo, key_start, nk_tile, P, wl, G, row_hi;
   bool ctx;
   int cs, cf, cfa, cfb, cs0, clen;
   bool done;
@@ -394,6 +396,10 @@ template <int BM> struct RowSteps {
     }
     fa = r_lo * G;
     fb = r_hi > r_lo ? r_hi * G : fa;
+    if (row_hi > 0) {
+      fa = max(fa, row_hi - kRowChunk);
+      fb = max(fa, min(fb, row_hi));
+    }
   }
   // From sequence cs downward, the first one with visible rows; its last step.
   __device__ __forceinline__ void seek() {
@@ -422,6 +428,7 @@ template <int BM> struct RowSteps {
     wl = wl_;
     G = G_;
     ctx = ctx_;
+    row_hi = it.row_hi;
     cs = it.seq_hi - 1;
     cf = cfa = cfb = cs0 = clen = 0;
     done = false;

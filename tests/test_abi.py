@@ -174,10 +174,14 @@ def test_split_flag_validation():
     lib = L.lib()
     plain = lib.dkv_workspace_size(p, L.DKV_CALL_BWD)
     F = FAKE
-    # Call 1 has a single writer per element already: no split mode there
+    # Call 1 takes DKV_ACC_SPLIT (one writer per element: no row chunks), so validation
+    # passes it (here the call then fails at its first HIP call, without a GPU); an
+    # unknown flag is refused before anything is enqueued
     pc, keepc = _params(ctx_len=0)
     st = lib.dkv_ctx_bwd(pc, F, F, F, F, F, F, F, F, F, F, F, L.DKV_ACC_SPLIT, F, 1 << 20, None)
-    assert st == L.DKV_ERR_INVALID_ARG
+    assert st != L.DKV_ERR_INVALID_ARG
+    st = lib.dkv_ctx_bwd(pc, F, F, F, F, F, F, F, F, F, F, F, 8, F, 1 << 20, None)
+    assert st == L.DKV_ERR_INVALID_ARG and "DKV_ACC_SPLIT" in L.last_error()
     # a workspace sized for the atomic mode is too small for the slices
     st = lib.dkv_bwd(p, F, F, F, F, F, F, F, F, F, F, F, F, F, L.DKV_ACC_SPLIT, F, F, F, plain,
                      None)

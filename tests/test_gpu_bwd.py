@@ -220,3 +220,35 @@ def test_split_mode_matches_oracle_and_repeats_bitwise(P, lens, Hq, Hkv, d, wl, 
     for k in ("dk_p", "dv_p"):
         check(k + " (atomic vs split)", ga[k], g[k].detach().float().cpu().numpy().astype(np.float64),
               dtype)
+
+
+@pytest.mark.parametrize("P,lens,Hq,Hkv,d,wl,dtype", [
+    (1500, [40, 70], 8, 2, 128, -1, "bf16"),    # 6000 flattened prompt rows: two chunks
+    (1100, [30], 16, 2, 64, 700, "bf16"),       # G = 8 with a window: chunks of windowed rows
+    (1500, [20], 8, 2, 128, -1, "fp32"),        # the fp32 dK/dV kernel
+    (700, [50], 16, 2, 512, -1, "bf16"),        # the head-dim-split dK/dV kernel
+    (900, [60, 10], 12, 2, 256, -1, "bf16"),    # the pair dK/dV kernel
+])
+def test_call1_row_chunks(P, lens, Hq, Hkv, d, wl, dtype):
+    # Call 1 over a prompt whose first key tiles see more than 4096 flattened query rows:
+    # without DKV_ACC_SPLIT those tiles' rows are split over several work items that each
+    # add into the accumulator; with it each element keeps one writer.  Both match the
+    # oracle, and agree with each other up to the order of the fp32 additions.
+    print("call1 chunks: P=%d lens=%s Hq=%d Hkv=%d d=%d wl=%d %s" % (P, lens, Hq, Hkv, d, wl, dtype),
+          flush=True)
+    assert P * (Hq // Hkv) > 4096
+    x, t, ref, g, (o_p, lse_p, o_r, lse_r) = _run(P, lens, Hq, Hkv, d, wl, dtype, False,
+                                                  seed=P + d, split=False)
+    for k in GRADS:
+        check(k + " (row chunks)", g[k], ref[k], dtype)
+    g1 = dkv.dualkv_backward(t["q_p"], t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], o_p,
+                             lse_p, o_r, lse_r, t["do_p"], t["do_r"], t["cu"],
+                             cu_host=t["cu_host"], window_left=wl, split=True)
+    torch.cuda.synchronize()
+    for k in GRADS:
+        check(k + " (one writer)", g1[k], ref[k], dtype)
+    for k in ("dq_p", "dq_r", "dk_r", "dv_r"):
+        assert torch.equal(g[k], g1[k]), k
+    for k in ("dk_p", "dv_p"):
+        check(k + " (row chunks vs one writer)", g[k],
+              g1[k].detach().float().cpu().numpy().astype(np.float64), dtype)

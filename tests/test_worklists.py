@@ -6,7 +6,9 @@ windows, GQA ratios, head dims 64 / 128 / 512, atomic and split modes): every
 (kv head, sequence, query tile) of the forward and dQ lists exactly once; every own
 key tile exactly once; every (prompt key tile, sequence whose rows see it) exactly once
 in atomic mode and every (prompt key tile, slice) exactly once in split mode; every
-layout output row exactly once, all source rows in bounds.  It is built with hipcc
+own key tile split into row chunks (a call that accumulates them) covered chunk by chunk
+on the chunk grid, within the workspace plan's bound; every layout output row exactly
+once, all source rows in bounds.  It is built with hipcc
 (host code only) and linked against the built libdkv.so for the launch symbols.
 """
 import os

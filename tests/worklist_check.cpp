@@ -34,13 +34,15 @@ int main(int argc, char **argv) {
   long checked = 0;
   for (int trial = 0; trial < trials; ++trial) {
     const int ng = 1 + rng() % 4;
+    // one trial in four has long sequences, whose key tiles split into row chunks
+    const int maxlen = (rng() % 4 == 0) ? 3000 : 300;
     std::vector<int> ctx{0}, seq{0}, cu{0};
     for (int j = 0; j < ng; ++j) {
       const int P = (rng() % 4 == 0) ? 0 : rng() % 400;
       const int n = rng() % 5;
       ctx.push_back(ctx.back() + P);
       seq.push_back(seq.back() + n);
-      for (int i = 0; i < n; ++i) cu.push_back(cu.back() + ((rng() % 5 == 0) ? rng() % 2 : rng() % 300));
+      for (int i = 0; i < n; ++i) cu.push_back(cu.back() + ((rng() % 5 == 0) ? rng() % 2 : rng() % maxlen));
     }
     const int hds[6] = {64, 96, 128, 192, 256, 512};
     const int Gs[5] = {1, 2, 3, 4, 8};
@@ -144,6 +146,43 @@ int main(int argc, char **argv) {
             }
           }
       }
+    }
+
+    // ---- own key tiles split into row chunks (a call that adds them into the
+    // accumulator): a split tile's chunks sit on the kRowChunk grid and cover the
+    // flattened rows that see it exactly once; an unsplit tile is one item (row_hi 0)
+    for (int chunk = 0; chunk < 2; ++chunk) {
+      std::map<std::tuple<int, int, int>, std::vector<int>> tiles;
+      const std::vector<KVItem> items = build_kv_items(s, false, false, chunk);
+      for (const KVItem &it : items) {
+        REQUIRE(it.region == kRegionOwn && it.seq_hi == it.seq_lo + 1, "own item");
+        REQUIRE(it.row_hi >= 0 && it.row_hi % kRowChunk == 0, "row_hi %d", it.row_hi);
+        tiles[std::make_tuple(it.g, it.seq_lo, it.key_start)].push_back(it.row_hi);
+      }
+      long want = 0;
+      for (int i = 0; i < N; ++i) want += (long)((len(i) + s.kv_tile - 1) / s.kv_tile) * s.Hkv;
+      REQUIRE((long)tiles.size() == want, "chunked own tiles %zu of %ld", tiles.size(), want);
+      for (auto &t : tiles) {
+        const int i = std::get<1>(t.first), k0 = std::get<2>(t.first);
+        const int nk = std::min(s.kv_tile, len(i) - k0);
+        const long fa = (long)k0 * s.G, fb = fa + kv_rows_visible(s, false, k0, nk, len(i), 0) * s.G;
+        std::vector<int> &hs = t.second;
+        std::sort(hs.begin(), hs.end());
+        if (hs.size() == 1 && hs[0] == 0) {
+          REQUIRE(!(chunk && chunk_own_rows(s)) || fb - fa <= kRowChunk, "unsplit long tile");
+          continue;
+        }
+        REQUIRE(chunk && chunk_own_rows(s) && fb - fa > kRowChunk, "split tile");
+        long c = fa / kRowChunk;
+        for (int h : hs) {
+          REQUIRE(h == (c + 1) * kRowChunk, "chunk grid: row_hi %d, want %ld", h, (c + 1) * kRowChunk);
+          ++c;
+        }
+        REQUIRE((c - 1) * kRowChunk < fb && c * kRowChunk >= fb, "chunks end at the rows' end");
+      }
+      REQUIRE(plan_bwd(s, false, false, chunk).st.n_kv >= items.size(), "plan bound");
+      REQUIRE(plan_bwd(s, false, false, chunk_own_rows(s)).st.n_kv >= items.size(),
+              "workspace bound");
     }
 
     // ---- layout items
