@@ -103,7 +103,7 @@ enum {
        bitwise reproducible when dkv_ctx_bwd gets the flag too.  Workspace:
        2 * S * P * Hkv * d * 4 bytes more.
        dkv_ctx_bwd (with an accumulator): without this flag, when the call's key tiles
-       are few (fewer than 2048 tiles times kv heads), the query rows of a long tile may
+       are few (fewer than 1024 tiles times kv heads), the query rows of a long tile may
        be split over several work items that each add their partial sums into the
        accumulator (fp32 atomics), which fills the GPU; with it every element of the
        Call-1 term has one writer. */

@@ -641,8 +641,10 @@ long kv_rows_visible(const Shape &s, bool ctx, int key_start, int nk, int len, i
 
 // Own-region key tiles of a call that adds them into the accumulator may be split into
 // row chunks (see KVItem::row_hi): when the call's key tiles alone would give fewer
-// workgroups than this, the causal walk's long first tiles leave most of the GPU idle.
-static constexpr long kChunkBelowItems = 2048;
+// workgroups than this (two per slot of the GPU's 256 CUs x 2 resident workgroups), the
+// causal walk's long first tiles leave most of the GPU idle.  With more, the tiles
+// already fill the GPU and chunks would only add accumulator traffic.
+static constexpr long kChunkBelowItems = 1024;
 
 bool chunk_own_rows(const Shape &s) {
   long tiles = 0;
