@@ -94,6 +94,31 @@ def test_prompt_groups_split_mode(groups, Hq, Hkv, d, wl, dtype):
               g[k].detach().float().cpu().numpy().astype(np.float64), dtype)
 
 
+def test_prompt_groups_call1_row_chunks():
+    # Two prompts long enough (over 4096 flattened rows) that Call 1 splits their first
+    # key tiles' rows into chunks added into the accumulator, an empty prompt, and a group
+    # without responses: the chunked result and the one-writer (split mode) result both
+    # match the oracle, the latter bitwise on a second run, and they agree with each other
+    # up to the order of the fp32 additions.
+    groups = [(1500, [40]), (0, [30]), (1100, [30, 20]), (60, [])]
+    Hq, Hkv, d, wl, dtype = 8, 2, 128, -1, "bf16"
+    print("groups with call-1 row chunks: %s" % groups, flush=True)
+    t, ref, (o_p, lse_p, o_r, lse_r), g, kw = _run(groups, Hq, Hkv, d, wl, dtype, seed=21)
+    for k in GRADS:
+        check(k + " (row chunks)", g[k], ref[k], dtype)
+    args = (t["q_p"], t["k_p"], t["v_p"], t["q_r"], t["k_r"], t["v_r"], o_p, lse_p, o_r, lse_r,
+            t["do_p"], t["do_r"], t["cu"])
+    g1 = dkv.dualkv_backward(*args, split=True, **kw)
+    g2 = dkv.dualkv_backward(*args, split=True, **kw)
+    torch.cuda.synchronize()
+    for k in GRADS:
+        check(k + " (one writer)", g1[k], ref[k], dtype)
+        assert torch.equal(g1[k], g2[k]), k
+    for k in ("dk_p", "dv_p"):
+        check(k + " (row chunks vs one writer)", g[k],
+              g1[k].detach().float().cpu().numpy().astype(np.float64), dtype)
+
+
 def test_one_group_equals_no_groups():
     # One group spanning every response gives the bits of the call without groups.
     P, lens, Hq, Hkv, d = 130, [77, 64, 129], 8, 2, 128
