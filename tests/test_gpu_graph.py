@@ -23,6 +23,7 @@ CASES = [
     (90, [77, 40], 8, 2, 512, -1, True),
     (150, [160, 90], 6, 2, 256, 60, True),
     (61, [70, 5], 6, 2, 64, 30, True),
+    (1500, [40, 70], 8, 2, 128, -1, False),   # Call 1 with row chunks in the graph
 ]
 
 
