@@ -508,7 +508,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(BwdKVArgs a) {
   // Steps of BM flattened rows (RowSteps), walked from the last visible row of the last
   // sequence backward.
   RowSteps<BM> rs;
-  rs.init(a.cu, it, nk_tile, P, wl, G, ctx);
+  rs.init(a.cu, it, nk_tile, P, wl, G, ctx, 0);
 
   QStepRegs<HD> qregs, dregs;
   float lse_r = INFINITY, d_r = 0.f;
@@ -717,7 +717,7 @@ __global__ __launch_bounds__(256, WPE) void bwd_dkdv_h16_kernel(BwdKVArgs a) {
 
   // Steps of BM flattened rows, walked from the last one backward.
   RowSteps<BM> rs;
-  rs.init(a.cu, it, nk_tile, P, wl, G, ctx);
+  rs.init(a.cu, it, nk_tile, P, wl, G, ctx, 0);
 
   const int tl = lane / G, jl = lane - tl * G;   // this lane's row of the LSE / D fetch
   // ceil(2^24 / G): r * g_recip >> 24 is r / G exactly for r < 64 and G <= 128 (the

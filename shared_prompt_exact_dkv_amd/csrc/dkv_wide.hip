@@ -962,7 +962,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(BwdKVArgs a) {
 
   // Steps of BM flattened rows, walked from the last one backward.
   RowSteps<BM> rs;
-  rs.init(a.cu, it, nk_tile, P, wl, G, ctx);
+  rs.init(a.cu, it, nk_tile, P, wl, G, ctx, kBwdBNWide);
 
   const int qld_b = (int)(qld * 2);
   const int head0_b = g * G * HD * 2;
@@ -1244,7 +1244,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdKVArgs a) {
 
   // Steps of BM flattened rows, walked from the last one backward.
   RowSteps<BM> rs;
-  rs.init(a.cu, it, nk_tile, P, wl, G, ctx);
+  rs.init(a.cu, it, nk_tile, P, wl, G, ctx, 0);
 
   const int qld_b = (int)(qld * 2);
   const int head0_b = g * G * HD * 2;
