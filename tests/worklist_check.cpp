@@ -10,9 +10,12 @@
 //     tile) exactly once in atomic mode; in split mode every (kv head, prompt key tile,
 //     slice) exactly once, its sequence range inside both the slice's chunk and the
 //     tile's group;
-//   * layout items: every output row written exactly once, all rows in bounds.
+//   * layout items: every output row written exactly once, all rows in bounds;
+//   * the dK/dV kernels' row walk (RowSteps, the device code itself, compiled for the
+//     host) over every key item: the visible rows of each sequence exactly once.
 // Exit status 0 and "ok <n>" on success; the first violation is printed otherwise.
 #include "../shared_prompt_exact_dkv_amd/csrc/dkv_api.cpp"
+#include "../shared_prompt_exact_dkv_amd/csrc/dkv_walks.h"
 
 #include <map>
 #include <random>
@@ -27,6 +30,73 @@
       exit(1);                                   \
     }                                            \
   } while (0)
+
+
+// The device's row walk run on the host: sequence bounds read from host memory.
+struct HostCu {
+  static int32_t load(const int32_t *cu, int i) { return cu[i]; }
+};
+
+// A key item's row walk (RowSteps, as the dK/dV kernels run it, 32-row steps, with the
+// windowed own-key rotation for tiles of rot_bn keys or without it) visits, for each
+// sequence whose rows see the item's keys, exactly the flattened rows the scheduler
+// counts as visible (kv_rows_visible, cut to the item's row chunk): whole aligned steps
+// whose in-range parts tile those rows once, sequences from the last down; a rotated
+// walk over a whole band visits step r at position -r mod L.
+static void check_walk(const Shape &s, const KVItem &it, int rot_bn) {
+  constexpr int BM = 32;
+  const bool ctx = it.region == kRegionCtx;
+  const int P = it.ctx_len;
+  const int nkeys = ctx ? P - it.key_start : s.cu[it.seq_lo + 1] - s.cu[it.seq_lo] - it.key_start;
+  const int nk = std::min(s.kv_tile, nkeys);
+  dkv::RowSteps<BM, HostCu> rs;
+  rs.init(s.cu.data(), it, nk, P, s.wl, s.G, ctx, rot_bn);
+  std::map<int, std::vector<std::pair<int, int>>> runs;   // sequence -> (flo, fend) in visit order
+  std::map<int, std::vector<int>> steps;
+  int last_seq = it.seq_hi, guard = 0;
+  while (!rs.done) {
+    REQUIRE(++guard < 1 << 22, "walk does not end");
+    const int sq = rs.cs;
+    REQUIRE(sq >= it.seq_lo && sq < it.seq_hi && sq <= last_seq, "walk sequence %d", sq);
+    last_seq = sq;
+    REQUIRE(rs.cs0 == s.cu[sq] && rs.clen == s.cu[sq + 1] - s.cu[sq], "cursor bounds");
+    int f0, flo, fend;
+    rs.advance(f0, flo, fend);
+    REQUIRE(f0 % BM == 0 && f0 <= flo && flo < fend && fend <= f0 + BM, "step %d [%d, %d)", f0, flo, fend);
+    runs[sq].push_back({flo, fend});
+    steps[sq].push_back(f0 / BM);
+  }
+  for (int i = it.seq_lo; i < it.seq_hi; ++i) {
+    const int len = s.cu[i + 1] - s.cu[i];
+    long fa, fb;
+    if (ctx) {
+      fa = 0;
+      fb = kv_rows_visible(s, true, it.key_start, nk, len, P) * s.G;
+    } else {
+      fa = (long)it.key_start * s.G;
+      fb = fa + kv_rows_visible(s, false, it.key_start, nk, len, 0) * s.G;
+    }
+    if (it.row_hi > 0) {
+      fa = std::max<long>(fa, it.row_hi - kRowChunk);
+      fb = std::max<long>(fa, std::min<long>(fb, it.row_hi));
+    }
+    std::vector<std::pair<int, int>> r = runs.count(i) ? runs[i] : std::vector<std::pair<int, int>>{};
+    std::sort(r.begin(), r.end());
+    long at = fa;
+    for (auto &x : r) {
+      REQUIRE(x.first == at, "seq %d rows: run at %d, want %ld (rows [%ld, %ld))", i, x.first, at, fa, fb);
+      at = x.second;
+    }
+    REQUIRE(at == fb, "seq %d rows end at %ld, want %ld", i, at, fb);
+    if (rot_bn > 0 && !ctx && s.wl >= 0 && it.row_hi == 0 && !steps[i].empty()) {
+      const int L = ((rot_bn + s.wl) * s.G + BM - 1) / BM;
+      const std::vector<int> &v = steps[i];
+      if ((int)v.size() == L && fa % BM == 0)
+        for (int t = 0; t < L; ++t)
+          REQUIRE(((t + v[t]) % L) == 0, "rotated walk: step %d at position %d of %d", v[t], t, L);
+    }
+  }
+}
 
 int main(int argc, char **argv) {
   const int trials = argc > 1 ? atoi(argv[1]) : 400;
@@ -95,6 +165,8 @@ int main(int argc, char **argv) {
       const int cs = split ? split_chunk(s) : 1;
       for (const KVItem &it : build_kv_items(s, true, split)) {
         REQUIRE(it.g >= 0 && it.g < s.Hkv, "g");
+        check_walk(s, it, 0);
+        check_walk(s, it, s.kv_tile);
         REQUIRE(it.seq_lo >= 0 && it.seq_lo <= it.seq_hi && it.seq_hi <= N, "range");
         if (it.region == kRegionOwn) {
           REQUIRE(it.seq_hi == it.seq_lo + 1, "own item spans sequences");
@@ -156,6 +228,8 @@ int main(int argc, char **argv) {
       const std::vector<KVItem> items = build_kv_items(s, false, false, chunk);
       for (const KVItem &it : items) {
         REQUIRE(it.region == kRegionOwn && it.seq_hi == it.seq_lo + 1, "own item");
+        check_walk(s, it, 0);
+        check_walk(s, it, s.kv_tile);
         REQUIRE(it.row_hi >= 0 && it.row_hi % kRowChunk == 0, "row_hi %d", it.row_hi);
         tiles[std::make_tuple(it.g, it.seq_lo, it.key_start)].push_back(it.row_hi);
       }
