@@ -8,10 +8,11 @@ key tile exactly once; every (prompt key tile, sequence whose rows see it) exact
 in atomic mode and every (prompt key tile, slice) exactly once in split mode; every
 own key tile split into row chunks (a call that accumulates them) covered chunk by chunk
 on the chunk grid, within the workspace plan's bound; every layout output row exactly
-once, all source rows in bounds; and, run on the host, the dK/dV kernels' own row walk
-(RowSteps in dkv_walks.h, with and without the windowed rotation) over every key item
-visits exactly the rows the scheduler counts as visible, once each, in whole aligned
-steps.  It is built with hipcc
+once, all source rows in bounds; and, run on the host, the kernels' own walks
+(dkv_walks.h): every query item's key tiles (64 and 32 keys) cover the keys its rows
+see and none wholly outside them, and the dK/dV row walk (with and without the
+windowed rotation) over every key item visits exactly the rows the scheduler counts as
+visible, once each, in whole aligned steps.  It is built with hipcc
 (host code only) and linked against the built libdkv.so for the launch symbols.
 """
 import os

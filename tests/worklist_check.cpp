@@ -11,8 +11,9 @@
 //     slice) exactly once, its sequence range inside both the slice's chunk and the
 //     tile's group;
 //   * layout items: every output row written exactly once, all rows in bounds;
-//   * the dK/dV kernels' row walk (RowSteps, the device code itself, compiled for the
-//     host) over every key item: the visible rows of each sequence exactly once.
+//   * the kernels' own walks (dkv_walks.h, the device code itself compiled for the
+//     host): a query item's key tiles cover the keys its rows see (KeyTiles), and a key
+//     item's row walk visits each sequence's visible rows exactly once (RowSteps).
 // Exit status 0 and "ok <n>" on success; the first violation is printed otherwise.
 #include "../shared_prompt_exact_dkv_amd/csrc/dkv_api.cpp"
 #include "../shared_prompt_exact_dkv_amd/csrc/dkv_walks.h"
@@ -31,6 +32,34 @@
     }                                            \
   } while (0)
 
+
+// The key tiles a query item visits (KeyTiles, as the forward and dQ kernels walk them,
+// tiles of BN keys): within each region (prompt, then own keys) aligned tiles in order,
+// together covering every key some row of the item sees and none wholly outside them.
+template <int BN> static void check_key_tiles(int P, int wl, int t0, int nt, int seqlen) {
+  dkv::KeyTiles<BN> kt;
+  kt.init(P, wl, t0, nt);
+  const long c_lo = wl >= 0 ? std::max(0, P + t0 - wl) : 0, c_hi = P;   // prompt keys seen
+  const long o_lo = wl >= 0 ? std::max(0, t0 - wl) : 0, o_hi = t0 + nt;  // own keys seen
+  long c_at = c_lo < c_hi ? c_lo : -1, o_at = o_lo;
+  for (int i = 0; i < kt.n; ++i) {
+    int nrows, kpos0;
+    kt.at(i, P, seqlen, nrows, kpos0);
+    if (kt.in_ctx(i)) {
+      const int k0 = kt.ctx_start(i);
+      REQUIRE(k0 % BN == 0 && k0 <= c_at && k0 + BN > c_at && k0 < c_hi, "prompt tile %d at %d (want %ld)", i, k0, c_at);
+      REQUIRE(nrows == P - k0 && kpos0 == k0, "prompt tile rows");
+      c_at = std::min<long>(c_hi, k0 + BN);
+    } else {
+      const int k0 = kt.own_start(i);
+      REQUIRE(k0 % BN == 0 && k0 <= o_at && k0 + BN > o_at && k0 < o_hi, "own tile %d at %d (want %ld)", i, k0, o_at);
+      REQUIRE(nrows == seqlen - k0 && kpos0 == P + k0, "own tile rows");
+      o_at = std::min<long>(o_hi, k0 + BN);
+    }
+  }
+  REQUIRE(c_at == -1 || c_at == c_hi, "prompt keys end at %ld of %ld", c_at, c_hi);
+  REQUIRE(o_at == o_hi, "own keys end at %ld of %ld", o_at, o_hi);
+}
 
 // The device's row walk run on the host: sequence bounds read from host memory.
 struct HostCu {
@@ -153,6 +182,9 @@ int main(int argc, char **argv) {
         REQUIRE(it.ctx_start == s.gctx[j] && it.ctx_len == s.gctx[j + 1] - s.gctx[j],
                 "prompt of seq %d", i);
         REQUIRE(++seen[std::make_tuple(it.g, i, it.tile)] == 1, "q item repeated");
+        const int t0 = it.tile * bm, nt = std::min(bm, it.seq_len - t0);
+        check_key_tiles<64>(it.ctx_len, s.wl, t0, nt, it.seq_len);
+        check_key_tiles<32>(it.ctx_len, s.wl, t0, nt, it.seq_len);
       }
       long want = 0;
       for (int i = 0; i < N; ++i) want += (long)((len(i) + bm - 1) / bm) * s.Hkv;
