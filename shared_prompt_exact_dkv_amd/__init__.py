@@ -24,6 +24,7 @@ from ._lib import (DKV_FIRST_TOKEN_GATHER, DKV_FIRST_TOKEN_SCATTER, DKV_PACK,  #
 __all__ = ["dkv_workspace_size", "dkv_ctx_fwd", "dkv_fwd", "dkv_ctx_bwd", "dkv_bwd",
            "dkv_bwd_noalloc",
            "dkv_cast_acc", "dkv_layout", "layout_rows", "dualkv_forward", "dualkv_backward",
+           "DualKVAttention", "dualkv_attention",
            "DkvError", "DKV_ACC_ZERO", "DKV_ACC_FINALIZE", "DKV_ACC_SPLIT", "DKV_PACK",
            "DKV_UNPACK", "DKV_UNPACK_BWD", "DKV_FIRST_TOKEN_GATHER", "DKV_FIRST_TOKEN_SCATTER"]
 
@@ -400,3 +401,48 @@ def dualkv_backward(q_p, k_p, v_p, q_r, k_r, v_r, o_p, lse_p, o_r, lse_r, do_p, 
                                            group_seq_cu_host=group_seq_cu_host,
                                            kv_head_of_q=kv_head_of_q)
     return {"dq_p": dq_p, "dk_p": dk_p, "dv_p": dv_p, "dq_r": dq_r, "dk_r": dk_r, "dv_r": dv_r}
+
+
+class DualKVAttention(torch.autograd.Function):
+    """torch autograd over the two calls: the forward is dualkv_forward, the backward
+    dualkv_backward, so the prompt keys' gradient of eq. (6) (the Call-1 term plus every
+    response's Call-2 term) is summed in the library's fp32 accumulator and cast once.
+    Differentiable inputs: q_p, k_p, v_p, q_r, k_r, v_r; outputs (o_p, o_r).  The LSEs
+    are kept for the backward; an output the loss does not use gets a zero gradient."""
+
+    @staticmethod
+    def forward(ctx, q_p, k_p, v_p, q_r, k_r, v_r, cu_seqlens, opts):
+        o_p, lse_p, o_r, lse_r = dualkv_forward(
+            q_p, k_p, v_p, q_r, k_r, v_r, cu_seqlens, cu_host=opts["cu_host"],
+            window_left=opts["window_left"], softmax_scale=opts["softmax_scale"],
+            ctx_cu_host=opts["ctx_cu_host"], group_seq_cu_host=opts["group_seq_cu_host"],
+            kv_head_of_q=opts["kv_head_of_q"])
+        ctx.save_for_backward(q_p, k_p, v_p, q_r, k_r, v_r, o_p, lse_p, o_r, lse_r)
+        ctx.cu_seqlens = cu_seqlens
+        ctx.opts = opts
+        return o_p, o_r
+
+    @staticmethod
+    def backward(ctx, do_p, do_r):
+        q_p, k_p, v_p, q_r, k_r, v_r, o_p, lse_p, o_r, lse_r = ctx.saved_tensors
+        do_p = torch.zeros_like(o_p) if do_p is None else do_p.contiguous()
+        do_r = torch.zeros_like(o_r) if do_r is None else do_r.contiguous()
+        o = ctx.opts
+        g = dualkv_backward(q_p, k_p, v_p, q_r, k_r, v_r, o_p, lse_p, o_r, lse_r, do_p, do_r,
+                            ctx.cu_seqlens, cu_host=o["cu_host"], window_left=o["window_left"],
+                            softmax_scale=o["softmax_scale"], split=o["split"],
+                            ctx_cu_host=o["ctx_cu_host"],
+                            group_seq_cu_host=o["group_seq_cu_host"],
+                            kv_head_of_q=o["kv_head_of_q"])
+        return (g["dq_p"], g["dk_p"], g["dv_p"], g["dq_r"], g["dk_r"], g["dv_r"], None, None)
+
+
+def dualkv_attention(q_p, k_p, v_p, q_r, k_r, v_r, cu_seqlens, *, cu_host=None, window_left=-1,
+                     softmax_scale=0.0, split=False, ctx_cu_host=None, group_seq_cu_host=None,
+                     kv_head_of_q=None):
+    """DualKV attention as one differentiable op (DualKVAttention): -> (o_p, o_r).
+    split=True makes the backward's prompt-key gradient bitwise reproducible."""
+    opts = {"cu_host": cu_host, "window_left": window_left, "softmax_scale": softmax_scale,
+            "split": split, "ctx_cu_host": ctx_cu_host, "group_seq_cu_host": group_seq_cu_host,
+            "kv_head_of_q": kv_head_of_q}
+    return DualKVAttention.apply(q_p, k_p, v_p, q_r, k_r, v_r, cu_seqlens, opts)
