@@ -243,8 +243,11 @@ int main(int argc, char **argv) {
                 REQUIRE(slice.count(std::make_tuple(g, s.gctx[j] + k0, c)) == 1, "slice %d of tile missing", c);
             } else {
               for (int i = s.gseq[j]; i < s.gseq[j + 1]; ++i) {
+                // a chunk of sequences may include some that do not see the tile (their
+                // walk has no rows); every one that does is covered exactly once
                 const bool sees = kv_rows_visible(s, true, k0, nk, len(i), Pg) > 0;
-                REQUIRE(ctxc.count(std::make_tuple(g, s.gctx[j] + k0, i)) == (sees ? 1u : 0u),
+                const size_t c = ctxc.count(std::make_tuple(g, s.gctx[j] + k0, i));
+                REQUIRE(sees ? c == 1u : c <= 1u,
                         "ctx pair (g %d, key %d, seq %d) coverage", g, s.gctx[j] + k0, i);
               }
             }
