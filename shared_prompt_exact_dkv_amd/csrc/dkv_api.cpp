@@ -597,10 +597,13 @@ dkv_status run_fwd(const Shape &s, const void *q, const void *kc, const void *vc
 // Key-parallel work items (dK/dV): one per (kv head, key tile) of each sequence's own
 // keys, and per (kv head, prompt key tile, chunk of sequences) of the shared prompt.
 // The chunk size sets how many sequences' partial dK_P/dV_P a workgroup sums in
-// registers before one atomic add per element: 4 (fewer sequences when N < 4), which
-// quarters the accumulator's atomic traffic and measured 0.2-2.2 % faster per step than
-// 1 on every benchmarked workload; 8 was no better at d = 128 and 27 % slower on the
-// d = 512 global layer (N = 8: one chunk, too few and too long items).  DKV_CTX_CHUNK
+// registers before one atomic add per element.  Global layers: 4 (fewer sequences when
+// N < 4), which quarters the accumulator's atomic traffic and measured 0.2-2.2 % faster
+// per step than 1 on every global workload benchmarked; 8 was no better at d = 128 and
+// 27 % slower on the d = 512 global layer (N = 8: one chunk, too few and too long
+// items).  Windowed layers: 1.  There the responses see only the prompt's last window
+// of keys, so those items are few and short, and grouped by four they finish the launch
+// as a tail of long items (d = 256 and 512 windowed steps 4-6 % slower).  DKV_CTX_CHUNK
 // overrides it (tuning only).
 
 int ctx_chunk(const Shape &s) {
@@ -608,7 +611,8 @@ int ctx_chunk(const Shape &s) {
     const char *e = getenv("DKV_CTX_CHUNK");
     return e ? atoi(e) : 0;
   }();
-  return std::min(env > 0 ? env : 4, std::max(1, s.N));
+  const int c = env > 0 ? env : (s.wl >= 0 ? 1 : 4);
+  return std::min(c, std::max(1, s.N));
 }
 
 // Split mode: the prompt-key terms of the N responses go to S slices, one per chunk
