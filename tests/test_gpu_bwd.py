@@ -227,6 +227,7 @@ def test_split_mode_matches_oracle_and_repeats_bitwise(P, lens, Hq, Hkv, d, wl, 
     (1100, [30], 16, 2, 64, 700, "bf16"),       # G = 8 with a window: chunks of windowed rows
     (1500, [20], 8, 2, 128, -1, "fp32"),        # the fp32 dK/dV kernel
     (700, [50], 16, 2, 512, -1, "bf16"),        # the head-dim-split dK/dV kernel
+    (1200, [40], 16, 2, 512, 600, "bf16"),      # its windowed row walk, rotated, in chunks
     (900, [60, 10], 12, 2, 256, -1, "bf16"),    # the pair dK/dV kernel
 ])
 def test_call1_row_chunks(P, lens, Hq, Hkv, d, wl, dtype):
