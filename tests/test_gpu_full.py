@@ -55,6 +55,7 @@ def _check(name, got, ref, bound=None, rel=REL["bf16"], floor=0.0):
                                         ("large_rollout", False), ("d512_global", False),
                                         ("d512_swa", False), ("qwen3_8b", True),
                                         ("d512_swa", True), ("d256_swa", False),
+                                        ("hd96", False), ("hd192", True),
                                         ("table1_p4k", False),
                                         ("table1_p64k", True)])
 def test_full_size_parity(name, split):

@@ -36,7 +36,8 @@ def _close(name, got, ref):
 
 @pytest.mark.parametrize("name,keys_bitwise", [
     ("qwen3_8b", True), ("dapo_varlen", True), ("large_rollout", True),
-    ("d512_global", True), ("d512_swa", False), ("d256_swa", True)])
+    ("d512_global", True), ("d512_swa", False), ("d256_swa", True), ("hd96", True),
+    ("hd192", True)])
 def test_two_calls_equal_ncopy_causal_path_on_every_row(name, keys_bitwise):
     w = workloads.WORKLOADS[name]
     lens = w.resp_lens()

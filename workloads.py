@@ -87,6 +87,14 @@ WORKLOADS = {
     # d = 256.
     "d256_swa": Workload("d256_swa", P=57344, N=8, R=8192, R_range=None, Hq=16, Hkv=4,
                          d=256, dtype="bf16", window_left=1023, seed=15),
+    # Head dims 96 and 192 (App. E.1 "Numerical correctness" checks d in {64, 96, 128, 192,
+    # 256}; the pages time neither): the Qwen3-8B-shaped micro-batch at those head dims,
+    # timing the d = 96 path (rows staged 128 wide) and the d = 192 pair kernels (rows
+    # staged 256 wide).
+    "hd96": Workload("hd96", P=4096, N=32, R=4096, R_range=None, Hq=32, Hkv=8, d=96,
+                     dtype="bf16", seed=16),
+    "hd192": Workload("hd192", P=4096, N=32, R=4096, R_range=None, Hq=32, Hkv=8, d=192,
+                      dtype="bf16", seed=17),
     # The shapes of the paper's kernel benchmark (§4.1, Table 1): Qwen3-8B attention
     # dimensions, R = 2048 per response, fp16, global causal.
     "table1_p4k": Workload("table1_p4k", P=4096, N=28, R=2048, R_range=None, Hq=32, Hkv=8,
