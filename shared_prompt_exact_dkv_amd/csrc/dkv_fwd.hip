@@ -202,6 +202,14 @@ static hipError_t fwd_h16(const FwdArgs &a, int n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Head dim 192 at 32-key tiles of 256-wide rows: 64 KB of LDS and 246 registers, so two
+// workgroups per CU and two waves per SIMD.
+template <typename E>
+static hipError_t fwd_h16_192(const FwdArgs &a, int n, hipStream_t s) {
+  hipLaunchKernelGGL((fwd_h16_kernel<E, 192, 32, 2, 256>), dim3(n), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd(int dtype, int hd, const FwdArgs &a, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (dtype == 0 || dtype == 2) {   // bf16, fp16
@@ -210,7 +218,7 @@ hipError_t launch_fwd(int dtype, int hd, const FwdArgs &a, int n, hipStream_t s)
       case 64: return f ? fwd_h16<f16, 64>(a, n, s) : fwd_h16<h16, 64>(a, n, s);
       case 96: return f ? fwd_h16<f16, 96, 128>(a, n, s) : fwd_h16<h16, 96, 128>(a, n, s);
       case 128: return f ? fwd_h16<f16, 128>(a, n, s) : fwd_h16<h16, 128>(a, n, s);
-      case 192:
+      case 192: return f ? fwd_h16_192<f16>(a, n, s) : fwd_h16_192<h16>(a, n, s);
       case 256:
       case 512: return launch_fwd_wide(dtype, hd, a, n, s);
       default: break;

@@ -1,7 +1,8 @@
 // dkv_fwd_bf16.h -- the h16 forward kernel template ("DualKV", arXiv 2605.15422,
 // §3.1): one online softmax over the shared-prompt KV region then the sequence's own
-// region.  Instantiated for head dims 64, 96 and 128 in dkv_fwd.hip (head dims 192,
-// 256 and 512 have their own kernels in dkv_wide.hip).
+// region.  Instantiated in dkv_fwd.hip for head dims 64, 96 and 128 (64-key tiles) and
+// 192 (32-key tiles of 256-wide rows); head dims 256 and 512 have their own kernels in
+// dkv_wide.hip.
 #pragma once
 
 #include "dkv_device.h"
@@ -12,8 +13,8 @@ namespace dkv {
 
 // ------------------------------------------------------------- h16 kernel --
 //
-// The h16 path for head dims 64 and 128 (HD = 512 has its own kernels): 64-key
-// tiles at two waves per SIMD (WPE = 2, <= 256 registers).
+// The h16 path for head dims 64 to 192: BN-key tiles (64; 32 at head dim 192, where Q
+// and O take 144 registers) at two waves per SIMD (WPE = 2, <= 256 registers).
 //   - K and V tiles are dense swizzled tiles filled by LDS DMA, double-buffered with
 //     one barrier per tile: the next tile streams in while the current one is
 //     computed.

@@ -8,9 +8,10 @@
 // in rows of HDP elements (256 or 512, a power of two); head dim 192 is staged in
 // 256-wide rows whose last 64 elements read as zeros (its fragments past the head dim
 // are zero, its products there are skipped where whole blocks are padding, and its
-// outputs there are never stored), so it runs the d = 256 kernels.  Tiles are staged by
-// LDS DMA into swizzled dense rows (one 1 KB DMA block holds one 512-wide row or two
-// 256-wide rows).
+// outputs there are never stored), so its backward runs the d = 256 kernels (its
+// forward fits the whole-row kernel of dkv_fwd_bf16.h, which is faster there).  Tiles
+// are staged by LDS DMA into swizzled dense rows (one 1 KB DMA block holds one 512-wide
+// row or two 256-wide rows).
 //
 //   forward  (both widths) 128 query rows per workgroup of 8 waves; the two waves of
 //            a pair share 32 rows and each holds Q and O for one half of the head dim.
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(512, 1) void fwd_wide_kernel(FwdArgs a) {
   }
 }
 
-// Forward at HDP = 256 (head dims 192 and 256): 128 query rows per workgroup of 8
+// Forward at HDP = 256 (head dim 256; 192 also fits it): 128 query rows per workgroup of 8
 // waves, four pairs of 32 rows.  In pair p, wave p (role 0) holds Q of the pair's rows
 // over the whole head dim, forms Sᵀ = K Qᵀ, runs the online softmax and accumulates
 // the first half of O; wave p + 4 (role 1, on the same SIMD) accumulates the second
@@ -509,7 +510,6 @@ hipError_t launch_fwd_wide(int dtype, int hd, const FwdArgs &a, int n, hipStream
   if (n <= 0) return hipSuccess;
   const bool f = dtype == 2;
   switch (hd) {
-    case 192: return f ? fwd_wide<f16, 192, 256>(a, n, s) : fwd_wide<h16, 192, 256>(a, n, s);
     case 256: return f ? fwd_wide<f16, 256, 256>(a, n, s) : fwd_wide<h16, 256, 256>(a, n, s);
     case 512: return f ? fwd_wide<f16, 512, 512>(a, n, s) : fwd_wide<h16, 512, 512>(a, n, s);
     default: return hipErrorInvalidValue;
